@@ -1,0 +1,64 @@
+"""Builds libschnet_mi355x.so for gfx950 with hipcc, in the package directory.
+
+Usage: python -m schnet_continuous_filter_amd.build
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libschnet_mi355x.so")
+SOURCES = ["capi.hip", "nbr.hip", "cfconv.hip", "atomwise.hip", "md.hip"]
+
+FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    # packed fp32 instructions are kept out of the generated code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-result",
+]
+
+
+def build(verbose: bool = False) -> str:
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    objs = []
+    build_dir = os.path.join(PKG, "_build")
+    os.makedirs(build_dir, exist_ok=True)
+    procs = []
+    for src in SOURCES:
+        obj = os.path.join(build_dir, src.replace(".hip", ".o"))
+        objs.append(obj)
+        cmd = [hipcc, *[f for f in FLAGS if f != "-shared"], "-c", "-I", os.path.join(ROOT, "include"),
+               os.path.join(CSRC, src), "-o", obj]
+        procs.append((src, cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                                 stderr=subprocess.STDOUT, text=True)))
+    failed = False
+    for src, cmd, p in procs:
+        out, _ = p.communicate()
+        out = "\n".join(l for l in out.splitlines() if "unknown target feature" not in l
+                        and "packed-fp32-ops" not in l)
+        if p.returncode != 0:
+            failed = True
+            sys.stderr.write(f"--- {src} failed:\n{' '.join(cmd)}\n{out}\n")
+        elif verbose and out.strip():
+            sys.stderr.write(f"--- {src}:\n{out}\n")
+    if failed:
+        raise RuntimeError("hipcc compilation failed")
+    tmp = LIB + ".tmp"
+    link = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(link, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

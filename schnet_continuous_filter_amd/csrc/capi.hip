@@ -1,0 +1,578 @@
+// C ABI: argument validation, workspace carving and launch orchestration.
+// The calls and their contracts are documented in include/schnet_mi355x.h.
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <vector>
+
+#include "common.hpp"
+
+using namespace sn;
+
+struct sn_model {
+  sn_model_desc desc;
+  int KP = 0;
+  int n_cu = 0;
+  size_t n_w = 0;
+  float* w = nullptr;          // device copy of the flat fp32 weights
+  uint16_t* wbf = nullptr;     // bf16 filter copies, per block: W1t[D][KP], W2t[D][D], W2n[D][D]
+  float co2 = 0.f;             // readout output bias (host copy)
+  size_t off_emb = 0, off_o1 = 0, off_co1 = 0, off_o2 = 0;
+  std::vector<size_t> off_blk; // start of each interaction block
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t b) { return (b + kAlign - 1) / kAlign * kAlign; }
+
+bool desc_ok(const sn_model_desc* d) {
+  if (!d) return false;
+  return d->n_types >= 1 && (d->D == 64 || d->D == 128) && d->Dr >= 2 && d->Dr <= 64 && d->T >= 1 &&
+         d->T <= 8 && (d->H == 32 || d->H == 64) && d->H <= d->D && std::isfinite(d->rbf_min) &&
+         std::isfinite(d->rbf_max) && d->rbf_min >= 0.f && d->rbf_max > d->rbf_min &&
+         std::isfinite(d->r_cut) && d->r_cut > 0.f &&
+         (d->filter_dtype == SN_FILTER_F32 || d->filter_dtype == SN_FILTER_BF16);
+}
+
+size_t block_floats(const sn_model_desc* d) {
+  const size_t D = d->D, Dr = d->Dr;
+  return Dr * D + D + 3 * (D * D + D);
+}
+
+bool sys_ok(const sn_system* s) {
+  if (!s) return false;
+  if (s->n_replicas < 1 || s->atoms_per_replica < 1) return false;
+  if ((int64_t)s->n_replicas * s->atoms_per_replica > (int64_t)1 << 30) return false;
+  if (s->periodic && !(std::isfinite(s->box) && s->box > 0.f)) return false;
+  return true;
+}
+
+int64_t n_atoms(const sn_system* s) { return (int64_t)s->n_replicas * s->atoms_per_replica; }
+
+uint16_t bf16_bits(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  const uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7FFFu + lsb;
+  return (uint16_t)(u >> 16);
+}
+
+sn_status hip_fail(hipError_t e) { return e == hipSuccess ? SN_OK : SN_ERR_HIP; }
+
+// ---------------------------------------------------------------- profiling hook
+struct ProfRec { int kernel; hipEvent_t a, b; };
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof_recs;
+std::vector<hipEvent_t> g_prof_pool;
+
+hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+struct ProfScope {
+  int kernel;
+  hipStream_t s;
+  hipEvent_t a = nullptr, b = nullptr;
+  ProfScope(int k, hipStream_t st) : kernel(k), s(st) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!g_prof_on) return;
+    a = prof_event();
+    b = prof_event();
+    if (a && b) (void)hipEventRecord(a, s);
+  }
+  ~ProfScope() {
+    if (!(a && b)) return;
+    (void)hipEventRecord(b, s);
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_recs.push_back({kernel, a, b});
+  }
+};
+
+// ---------------------------------------------------------------- E+F orchestration
+int cf_grid(const sn_model* m, int64_t n) {
+  int64_t g = (n + 3) / 4;
+  if (g > m->n_cu) g = m->n_cu;
+  if (g > kMaxGrid) g = kMaxGrid;
+  return (int)(g < 1 ? 1 : g);
+}
+
+sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const float* pos,
+                             const int32_t* types, const int32_t* rowptr, const int32_t* col,
+                             float* energy, float* forces, char* ws, hipStream_t s) {
+  const sn_model_desc& d = m->desc;
+  const int64_t n = n_atoms(sys);
+  const int D = d.D, T = d.T, H = d.H;
+  const WsLayout L = ws_layout(n, D, T, H);
+  DevStatus* st = reinterpret_cast<DevStatus*>(ws + L.status);
+  int32_t* wg_start = reinterpret_cast<int32_t*>(ws + L.wg_start);
+  float* x = reinterpret_cast<float*>(ws + L.x);
+  float* au = reinterpret_cast<float*>(ws + L.au);
+  float* gbuf = reinterpret_cast<float*>(ws + L.gbuf);
+  float* tmp = reinterpret_cast<float*>(ws + L.tmp);
+  float* gx = reinterpret_cast<float*>(ws + L.gx);
+  float* eps = reinterpret_cast<float*>(ws + L.eps);
+  const size_t ND = (size_t)n * D;
+  const int bf16 = d.filter_dtype == SN_FILTER_BF16;
+  const int G = cf_grid(m, n);
+  hipError_t e;
+
+  if ((e = launch_partition(rowptr, (int)n, G, wg_start, s)) != hipSuccess) return hip_fail(e);
+  if ((e = launch_embed(types, m->w + m->off_emb, (int)n, D, d.n_types, x, st, s)) != hipSuccess)
+    return hip_fail(e);
+
+  CfParams p{};
+  p.rowptr = rowptr;
+  p.col = col;
+  p.pos = pos;
+  p.wg_start = wg_start;
+  p.periodic = sys->periodic;
+  p.box = sys->box;
+  p.half_box = 0.5f * sys->box;
+  const float step = (d.rbf_max - d.rbf_min) / (float)(d.Dr - 1);
+  p.rbf_min = d.rbf_min;
+  p.rbf_step = step;
+  p.rbf_coef = -0.5f / (step * step);
+  p.rbf_inv_s2 = 1.f / (step * step);
+  p.r_cut = d.r_cut;
+  p.pi_over_rc = (float)(M_PI / (double)d.r_cut);
+  p.Dr = d.Dr;
+  p.KP = m->KP;
+
+  auto set_block = [&](int t) {
+    const float* b = m->w + m->off_blk[t];
+    const size_t Dr = d.Dr, DD = (size_t)D * D;
+    p.Wf1 = b;
+    p.cf1 = b + Dr * D;
+    p.Wf2 = p.cf1 + D;
+    p.cf2 = p.Wf2 + DD;
+    if (bf16) {
+      const uint16_t* wb = m->wbf + (size_t)t * ((size_t)D * m->KP + 2 * DD);
+      p.W1t = wb;
+      p.W2t = wb + (size_t)D * m->KP;
+      p.W2n = p.W2t + DD;
+    }
+  };
+  auto Wu = [&](int t, int k) {  // k: 0 Wu1, 1 cu1, 2 Wu2, 3 cu2
+    const float* b = m->w + m->off_blk[t] + (size_t)d.Dr * D + D + (size_t)D * D + D;
+    const size_t DD = (size_t)D * D;
+    switch (k) {
+      case 0: return b;
+      case 1: return b + DD;
+      case 2: return b + DD + D;
+      default: return b + 2 * DD + D;
+    }
+  };
+
+  // forward
+  for (int t = 0; t < T; ++t) {
+    set_block(t);
+    p.x = x + t * ND;
+    p.h = gbuf;
+    {
+      ProfScope ps(0, s);
+      if ((e = launch_cf_forward(D, bf16, p, G, s)) != hipSuccess) return hip_fail(e);
+    }
+    GemmArgs g1{GEMM_BIAS, (int)n, D, D, gbuf, Wu(t, 0), Wu(t, 1), nullptr, nullptr, au + t * ND,
+                nullptr, 0.f, nullptr};
+    if ((e = launch_gemm(g1, m->n_cu, s)) != hipSuccess) return hip_fail(e);
+    GemmArgs g2{GEMM_SSP_RESID, (int)n, D, D, au + t * ND, Wu(t, 2), Wu(t, 3), x + t * ND, nullptr,
+                x + (t + 1) * ND, nullptr, 0.f, nullptr};
+    if ((e = launch_gemm(g2, m->n_cu, s)) != hipSuccess) return hip_fail(e);
+  }
+  // readout and its gradient
+  GemmArgs gr{GEMM_READOUT, (int)n, D, H, x + T * ND, m->w + m->off_o1, m->w + m->off_co1, nullptr,
+              nullptr, tmp, m->w + m->off_o2, m->co2, eps};
+  if ((e = launch_gemm(gr, m->n_cu, s)) != hipSuccess) return hip_fail(e);
+  GemmArgs grb{GEMM_T, (int)n, H, D, tmp, m->w + m->off_o1, nullptr, nullptr, nullptr, gx,
+               nullptr, 0.f, nullptr};
+  if ((e = launch_gemm(grb, m->n_cu, s)) != hipSuccess) return hip_fail(e);
+  if ((e = launch_energy(eps, sys->n_replicas, sys->atoms_per_replica, energy, st, s)) !=
+      hipSuccess)
+    return hip_fail(e);
+  // backward
+  int cur = 0;
+  for (int t = T - 1; t >= 0; --t) {
+    float* gx_cur = gx + cur * ND;
+    GemmArgs b1{GEMM_T_SIGMOID, (int)n, D, D, gx_cur, Wu(t, 2), nullptr, nullptr, au + t * ND, tmp,
+                nullptr, 0.f, nullptr};
+    if ((e = launch_gemm(b1, m->n_cu, s)) != hipSuccess) return hip_fail(e);
+    GemmArgs b2{GEMM_T, (int)n, D, D, tmp, Wu(t, 0), nullptr, nullptr, nullptr, gbuf, nullptr, 0.f,
+                nullptr};
+    if ((e = launch_gemm(b2, m->n_cu, s)) != hipSuccess) return hip_fail(e);
+    set_block(t);
+    p.x = x + t * ND;
+    p.gh = gbuf;
+    p.gx_in = gx_cur;
+    p.gx_out = t > 0 ? gx + (1 - cur) * ND : nullptr;
+    p.forces = forces;
+    p.force_accumulate = t != T - 1;
+    {
+      ProfScope ps(1, s);
+      if ((e = launch_cf_backward(D, bf16, p, G, s)) != hipSuccess) return hip_fail(e);
+    }
+    cur = 1 - cur;
+  }
+  return SN_OK;
+}
+
+sn_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (!ws) return SN_ERR_INVALID_ARG;
+  if (((uintptr_t)ws) % kAlign != 0) return SN_ERR_INVALID_ARG;
+  return ws_bytes >= need ? SN_OK : SN_ERR_WORKSPACE;
+}
+
+bool nbr_geom(const sn_system* sys, float r_list, NbrGeom& g) {
+  if (!(std::isfinite(r_list) && r_list > 0.f)) return false;
+  g.n_rep = sys->n_replicas;
+  g.n_per = sys->atoms_per_replica;
+  g.periodic = sys->periodic != 0;
+  g.box = sys->box;
+  g.L = g.periodic ? (double)sys->box : 0.0;
+  g.half = g.L / 2.0;
+  g.r2 = (double)r_list * (double)r_list;
+  g.cells_per_axis = 0;
+  g.inv_cell = 0.f;
+  if (g.periodic) {
+    if (!((double)sys->box >= 2.0 * (double)r_list)) return false;
+    int nc = (int)std::floor((double)sys->box / ((double)r_list * (1.0 + 1e-5)));
+    if (nc > kCellsPerAxisMax) nc = kCellsPerAxisMax;
+    if (sys->n_replicas == 1 && nc >= 3) {
+      g.cells_per_axis = nc;
+      g.inv_cell = (float)((double)nc / (double)sys->box);
+    }
+  }
+  return true;
+}
+
+struct MdSetup {
+  MdCoef c;
+  float r_list;
+};
+
+bool md_setup(const sn_model* m, const sn_system* sys, const sn_md_params* prm, MdSetup& out) {
+  if (!prm) return false;
+  if (!(prm->dt_fs > 0.f && std::isfinite(prm->dt_fs)) || !(prm->temperature_K >= 0.f) ||
+      !(prm->gamma_per_ps >= 0.f) || !(prm->mass_amu > 0.f) || !(prm->skin >= 0.f) ||
+      prm->rebuild_every < 1)
+    return false;
+  const double kappa = 4.184e-4, kB = 0.0019872043;
+  const double dt = prm->dt_fs, m_ = prm->mass_amu;
+  const double c1 = std::exp(-(double)prm->gamma_per_ps * 1e-3 * dt);
+  out.c.half_kick = (float)(0.5 * dt * kappa / m_);
+  out.c.half_dt = (float)(0.5 * dt);
+  out.c.c1 = (float)c1;
+  out.c.c2 = (float)std::sqrt((1.0 - c1 * c1) * kB * prm->temperature_K * kappa / m_);
+  out.c.sigma_v = (float)std::sqrt(kB * prm->temperature_K * kappa / m_);
+  out.c.half_skin2 = (float)(0.25 * (double)prm->skin * prm->skin);
+  out.c.seed = prm->seed;
+  out.c.periodic = sys->periodic != 0;
+  out.c.box = sys->box;
+  out.r_list = m->desc.r_cut + prm->skin;
+  return true;
+}
+
+bool state_ok(const sn_md_state* st) {
+  return st && st->pos && st->vel && st->forces && st->pos_at_build && st->rowptr && st->col &&
+         st->edge_capacity >= 0 && st->edge_capacity <= INT32_MAX;
+}
+
+} // namespace
+
+namespace sn {
+WsLayout ws_layout(int64_t n, int D, int T, int H) {
+  (void)H;
+  WsLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
+  const int64_t ncell = (int64_t)kCellsPerAxisMax * kCellsPerAxisMax * kCellsPerAxisMax;
+  const int64_t scan_n = (n > ncell ? n : ncell) + 1;
+  L.status = take(sizeof(DevStatus));
+  L.wg_start = take((size_t)(kMaxGrid + 1) * 4);
+  L.scan_blocks = take((size_t)(scan_n / kScanChunk + 2) * 8);
+  L.cell_count = take((size_t)(ncell + 1) * 4);
+  L.cell_start = take((size_t)ncell * 4);
+  L.cell_atoms = take((size_t)n * 4);
+  L.atom_cell = take((size_t)n * 4);
+  const size_t ND = (size_t)n * (size_t)D * 4;
+  L.x = take((size_t)(T + 1) * ND);
+  L.au = take((size_t)T * ND);
+  L.gbuf = take(ND);
+  L.tmp = take(ND);
+  L.gx = take(2 * ND);
+  L.eps = take((size_t)n * 4 + (size_t)n * 4);   // per-atom energies, then per-replica scratch
+  L.total = off;
+  return L;
+}
+} // namespace sn
+
+extern "C" {
+
+const char* sn_status_string(sn_status s) {
+  switch (s) {
+    case SN_OK: return "ok";
+    case SN_ERR_INVALID_ARG: return "invalid argument";
+    case SN_ERR_CAPACITY: return "neighbour list exceeds edge capacity";
+    case SN_ERR_NONFINITE: return "non-finite energy";
+    case SN_ERR_UNSUPPORTED: return "unsupported shape";
+    case SN_ERR_HIP: return "HIP runtime error";
+    case SN_ERR_WORKSPACE: return "workspace too small";
+  }
+  return "unknown status";
+}
+
+size_t sn_model_weight_count(const sn_model_desc* d) {
+  if (!desc_ok(d)) return 0;
+  const size_t D = d->D, H = d->H;
+  return (size_t)d->n_types * D + (size_t)d->T * block_floats(d) + D * H + H + H + 1;
+}
+
+sn_status sn_model_create(const sn_model_desc* d, const float* weights_host, size_t n_floats,
+                          sn_model** out) {
+  if (!d || !weights_host || !out) return SN_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (!desc_ok(d)) {
+    // distinguish malformed values from shapes this build does not cover
+    if (d->n_types < 1 || d->D < 1 || d->Dr < 2 || d->T < 1 || d->H < 1 ||
+        !(d->rbf_max > d->rbf_min) || !(d->r_cut > 0.f))
+      return SN_ERR_INVALID_ARG;
+    return SN_ERR_UNSUPPORTED;
+  }
+  const size_t nw = sn_model_weight_count(d);
+  if (n_floats != nw) return SN_ERR_INVALID_ARG;
+  for (size_t i = 0; i < nw; ++i)
+    if (!std::isfinite(weights_host[i])) return SN_ERR_INVALID_ARG;
+
+  sn_model* m = new (std::nothrow) sn_model();
+  if (!m) return SN_ERR_HIP;
+  m->desc = *d;
+  m->n_w = nw;
+  m->KP = cf_kp(d->Dr, d->filter_dtype == SN_FILTER_BF16);
+  const size_t D = d->D, H = d->H;
+  m->off_emb = 0;
+  size_t off = (size_t)d->n_types * D;
+  for (int t = 0; t < d->T; ++t) {
+    m->off_blk.push_back(off);
+    off += block_floats(d);
+  }
+  m->off_o1 = off;
+  m->off_co1 = off + D * H;
+  m->off_o2 = m->off_co1 + H;
+  m->co2 = weights_host[m->off_o2 + H];
+
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&m->n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = cf_prepare(d->D, d->filter_dtype == SN_FILTER_BF16);
+  if (e == hipSuccess) e = gemm_prepare();
+  if (e == hipSuccess) e = hipMalloc(&m->w, nw * sizeof(float));
+  if (e == hipSuccess) e = hipMemcpy(m->w, weights_host, nw * sizeof(float), hipMemcpyHostToDevice);
+  if (e == hipSuccess && d->filter_dtype == SN_FILTER_BF16) {
+    const size_t KP = m->KP, DD = D * D, per = D * KP + 2 * DD;
+    std::vector<uint16_t> hb(per * d->T, 0);
+    for (int t = 0; t < d->T; ++t) {
+      const float* Wf1 = weights_host + m->off_blk[t];
+      const float* Wf2 = Wf1 + (size_t)d->Dr * D + D;
+      uint16_t* W1t = hb.data() + t * per;
+      uint16_t* W2t = W1t + D * KP;
+      uint16_t* W2n = W2t + DD;
+      for (size_t n = 0; n < D; ++n)
+        for (size_t k = 0; k < (size_t)d->Dr; ++k) W1t[n * KP + k] = bf16_bits(Wf1[k * D + n]);
+      for (size_t k = 0; k < D; ++k)
+        for (size_t n = 0; n < D; ++n) {
+          W2t[n * D + k] = bf16_bits(Wf2[k * D + n]);
+          W2n[k * D + n] = bf16_bits(Wf2[k * D + n]);
+        }
+    }
+    e = hipMalloc(&m->wbf, hb.size() * sizeof(uint16_t));
+    if (e == hipSuccess)
+      e = hipMemcpy(m->wbf, hb.data(), hb.size() * sizeof(uint16_t), hipMemcpyHostToDevice);
+  }
+  if (e != hipSuccess) {
+    sn_model_destroy(m);
+    return SN_ERR_HIP;
+  }
+  *out = m;
+  return SN_OK;
+}
+
+void sn_model_destroy(sn_model* m) {
+  if (!m) return;
+  if (m->w) (void)hipFree(m->w);
+  if (m->wbf) (void)hipFree(m->wbf);
+  delete m;
+}
+
+sn_status sn_workspace_size(const sn_model_desc* d, const sn_system* sys, size_t* bytes) {
+  if (!sys || !bytes) return SN_ERR_INVALID_ARG;
+  if (!sys_ok(sys)) return SN_ERR_INVALID_ARG;
+  if (d && !desc_ok(d)) return SN_ERR_INVALID_ARG;
+  *bytes = ws_layout(n_atoms(sys), d ? d->D : 0, d ? d->T : 0, d ? d->H : 0).total;
+  return SN_OK;
+}
+
+sn_status sn_build_neighbors(const sn_system* sys, const float* pos, float r_list, int32_t* rowptr,
+                             int32_t* col, int64_t edge_capacity, int64_t* n_edges_host, void* ws,
+                             size_t ws_bytes, hipStream_t s) {
+  if (!sys_ok(sys) || !pos || !rowptr || (!col && edge_capacity > 0)) return SN_ERR_INVALID_ARG;
+  if (edge_capacity < 0 || edge_capacity > INT32_MAX) return SN_ERR_INVALID_ARG;
+  NbrGeom g;
+  if (!nbr_geom(sys, r_list, g)) return SN_ERR_INVALID_ARG;
+  const WsLayout L = ws_layout(n_atoms(sys), 0, 0, 0);
+  sn_status rc = check_ws(ws, ws_bytes, L.total);
+  if (rc != SN_OK) return rc;
+  char* w = static_cast<char*>(ws);
+  hipError_t e = launch_build_neighbors(g, pos, rowptr, col, edge_capacity, w, L, nullptr, 0, s);
+  if (e != hipSuccess) return SN_ERR_HIP;
+  if (n_edges_host) {
+    const DevStatus* st = reinterpret_cast<const DevStatus*>(w + L.status);
+    int64_t ne = 0;
+    e = hipMemcpyAsync(&ne, &st->last_n_edges, sizeof(int64_t), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return SN_ERR_HIP;
+    *n_edges_host = ne;
+  }
+  return SN_OK;
+}
+
+sn_status sn_energy_forces(const sn_model* m, const sn_system* sys, const float* pos,
+                           const int32_t* types, const int32_t* rowptr, const int32_t* col,
+                           float* energy, float* forces, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (!m || !sys_ok(sys) || !pos || !types || !rowptr || !col || !energy || !forces)
+    return SN_ERR_INVALID_ARG;
+  const WsLayout L = ws_layout(n_atoms(sys), m->desc.D, m->desc.T, m->desc.H);
+  sn_status rc = check_ws(ws, ws_bytes, L.total);
+  if (rc != SN_OK) return rc;
+  return energy_forces_impl(m, sys, pos, types, rowptr, col, energy, forces, static_cast<char*>(ws),
+                            s);
+}
+
+sn_status sn_md_init(const sn_model* m, const sn_system* sys, const int32_t* types,
+                     const sn_md_params* prm, sn_md_state* state, float* energy, void* ws,
+                     size_t ws_bytes, hipStream_t s) {
+  if (!m || !sys_ok(sys) || !types || !state_ok(state)) return SN_ERR_INVALID_ARG;
+  MdSetup su;
+  if (!md_setup(m, sys, prm, su)) return SN_ERR_INVALID_ARG;
+  NbrGeom g;
+  if (!nbr_geom(sys, su.r_list, g)) return SN_ERR_INVALID_ARG;
+  const int64_t n = n_atoms(sys);
+  const WsLayout L = ws_layout(n, m->desc.D, m->desc.T, m->desc.H);
+  sn_status rc = check_ws(ws, ws_bytes, L.total);
+  if (rc != SN_OK) return rc;
+  char* w = static_cast<char*>(ws);
+  DevStatus* st = reinterpret_cast<DevStatus*>(w + L.status);
+  float* e_out = energy ? energy : reinterpret_cast<float*>(w + L.eps) + n;
+  hipError_t e = hipSuccess;
+  if (sys->periodic) e = launch_md_wrap(su.c, n, state->pos, s);
+  if (e == hipSuccess) e = launch_md_init_vel(su.c, n, state->vel, s);
+  if (e == hipSuccess)
+    e = launch_build_neighbors(g, state->pos, state->rowptr, state->col, state->edge_capacity, w, L,
+                               nullptr, 0, s);
+  if (e == hipSuccess) e = launch_md_mark_build(n, state->pos, state->pos_at_build, st, nullptr, 0, s);
+  if (e != hipSuccess) return SN_ERR_HIP;
+  return energy_forces_impl(m, sys, state->pos, types, state->rowptr, state->col, e_out,
+                            state->forces, w, s);
+}
+
+sn_status sn_md_step(const sn_model* m, const sn_system* sys, const int32_t* types,
+                     const sn_md_params* prm, sn_md_state* state, int32_t n_steps, float* energy,
+                     void* ws, size_t ws_bytes, hipStream_t s) {
+  if (!m || !sys_ok(sys) || !types || !state_ok(state) || n_steps < 0) return SN_ERR_INVALID_ARG;
+  MdSetup su;
+  if (!md_setup(m, sys, prm, su)) return SN_ERR_INVALID_ARG;
+  NbrGeom g;
+  if (!nbr_geom(sys, su.r_list, g)) return SN_ERR_INVALID_ARG;
+  const int64_t n = n_atoms(sys);
+  const WsLayout L = ws_layout(n, m->desc.D, m->desc.T, m->desc.H);
+  sn_status rc = check_ws(ws, ws_bytes, L.total);
+  if (rc != SN_OK) return rc;
+  char* w = static_cast<char*>(ws);
+  DevStatus* st = reinterpret_cast<DevStatus*>(w + L.status);
+  float* e_out = energy ? energy : reinterpret_cast<float*>(w + L.eps) + n;
+  for (int32_t k = 0; k < n_steps; ++k) {
+    const uint64_t step = state->step;
+    hipError_t e = launch_md_baoa(su.c, n, step, state->pos, state->vel, state->forces,
+                                  state->pos_at_build, st, s);
+    if (e != hipSuccess) return SN_ERR_HIP;
+    const bool scheduled = ((step + 1) % (uint64_t)prm->rebuild_every) == 0;
+    const int64_t* gate = scheduled ? nullptr : &st->rebuild_req;
+    const int64_t gval = (int64_t)step + 1;
+    e = launch_build_neighbors(g, state->pos, state->rowptr, state->col, state->edge_capacity, w, L,
+                               gate, gval, s);
+    if (e == hipSuccess) e = launch_md_mark_build(n, state->pos, state->pos_at_build, st, gate, gval, s);
+    if (e != hipSuccess) return SN_ERR_HIP;
+    rc = energy_forces_impl(m, sys, state->pos, types, state->rowptr, state->col, e_out,
+                            state->forces, w, s);
+    if (rc != SN_OK) return rc;
+    e = launch_md_b(su.c, n, state->vel, state->forces, s);
+    if (e != hipSuccess) return SN_ERR_HIP;
+    state->step = step + 1;
+  }
+  return SN_OK;
+}
+
+sn_status sn_get_device_status(const void* ws, size_t ws_bytes, hipStream_t s, int32_t* status,
+                               int64_t* detail, int64_t* n_rebuilds) {
+  if (!ws || !status || ws_bytes < sizeof(DevStatus)) return SN_ERR_INVALID_ARG;
+  DevStatus h{};
+  hipError_t e = hipMemcpyAsync(&h, ws, sizeof(DevStatus), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return SN_ERR_HIP;
+  *status = h.status;
+  if (detail) *detail = h.detail;
+  if (n_rebuilds) *n_rebuilds = h.n_rebuilds;
+  return SN_OK;
+}
+
+sn_status sn_reset_device_status(void* ws, size_t ws_bytes, hipStream_t s) {
+  if (!ws || ws_bytes < sizeof(DevStatus)) return SN_ERR_INVALID_ARG;
+  return hip_fail(hipMemsetAsync(ws, 0, sizeof(DevStatus), s));
+}
+
+sn_status sn_philox4x64_10(const uint64_t* counters, uint64_t key0, uint64_t key1, uint64_t* out,
+                           int64_t n, hipStream_t s) {
+  if (n < 0 || (n > 0 && (!counters || !out))) return SN_ERR_INVALID_ARG;
+  return hip_fail(launch_philox(counters, key0, key1, out, n, s));
+}
+
+sn_status sn_profile_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = on != 0;
+  return SN_OK;
+}
+
+sn_status sn_profile_read(int32_t kernel, double* total_ms, int64_t* launches) {
+  if (!total_ms || !launches) return SN_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  double sum = 0.0;
+  int64_t cnt = 0;
+  std::vector<ProfRec> keep;
+  for (const ProfRec& r : g_prof_recs) {
+    if (r.kernel != kernel) {
+      keep.push_back(r);
+      continue;
+    }
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
+      return SN_ERR_HIP;
+    sum += ms;
+    ++cnt;
+    g_prof_pool.push_back(r.a);
+    g_prof_pool.push_back(r.b);
+  }
+  g_prof_recs.swap(keep);
+  *total_ms = sum;
+  *launches = cnt;
+  return SN_OK;
+}
+
+} // extern "C"

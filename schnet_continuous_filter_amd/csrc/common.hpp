@@ -1,0 +1,154 @@
+// Internal declarations shared by the HIP translation units of the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "schnet_mi355x.h"
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+namespace sn {
+
+constexpr int kThreads = 256;  // every kernel of the library runs 4 wave64 per block
+constexpr int kTileEdges = 64; // edges per CFConv tile (two 32-row MFMA blocks)
+constexpr int kTileAtoms = 64; // atoms per atom-wise GEMM tile
+constexpr int kMaxGrid = 4096; // upper bound on CFConv work-groups (partition table size)
+constexpr int kCellsPerAxisMax = 64;
+constexpr int kScanChunk = 1024; // elements per block of the device scan
+constexpr int kSortRowMax = 1024;
+
+// Device status block at offset 0 of every workspace.
+struct DevStatus {
+  int32_t status;        // sn_status; first error wins
+  int32_t overflow;      // 1 while the last neighbour build did not fit
+  int64_t detail;
+  int64_t n_rebuilds;    // neighbour builds done by the MD calls
+  int64_t last_n_edges;  // edge count of the last neighbour build
+  int64_t rebuild_req;   // MD: step+1 of the last step whose drift crossed skin/2
+  int64_t pad[3];
+};
+
+__device__ inline void dev_fail(DevStatus* st, int code, int64_t detail) {
+  if (atomicCAS(&st->status, 0, code) == 0) st->detail = detail;
+}
+
+// Offsets (bytes) of everything carved out of a workspace.
+struct WsLayout {
+  size_t status, wg_start, scan_blocks, cell_count, cell_start, cell_atoms, atom_cell;
+  size_t x, au, gbuf, tmp, gx, eps, total;
+};
+WsLayout ws_layout(int64_t n_atoms, int D, int T, int H);
+
+// ------------------------------------------------------------------ launchers
+// Neighbour list (nbr.hip). Returns hipSuccess or the first launch error.
+struct NbrGeom {
+  int n_rep, n_per, periodic;
+  float box;
+  double L, half, r2;   // IEEE double values used by the exact predicate
+  int cells_per_axis;   // 0 = all-pairs mode
+  float inv_cell;
+};
+hipError_t launch_build_neighbors(const NbrGeom& g, const float* pos, int32_t* rowptr,
+                                  int32_t* col, int64_t edge_capacity, char* ws,
+                                  const WsLayout& L, const int64_t* gate, int64_t gate_val,
+                                  hipStream_t s);
+
+// Scan (nbr.hip): in-place exclusive scan of a[0..n) into a[0..n], a[n] = total.
+hipError_t launch_exclusive_scan(int32_t* a, int64_t n, int32_t* blocks, DevStatus* st,
+                                 int64_t capacity, const int64_t* gate, int64_t gate_val,
+                                 hipStream_t s);
+
+// CFConv and atom-wise layers (cfconv.hip, atomwise.hip).
+struct CfParams {
+  const int32_t* rowptr;
+  const int32_t* col;
+  const float* pos;
+  const int32_t* wg_start;
+  int periodic;
+  float box, half_box;
+  float rbf_min, rbf_step, rbf_coef, rbf_inv_s2; // coef = -1/(2 sigma^2), inv_s2 = 1/sigma^2
+  float r_cut, pi_over_rc;
+  int Dr, KP;
+  // fp32 filter weights (row-major [fan_in][fan_out])
+  const float* Wf1;
+  const float* cf1;
+  const float* Wf2;
+  const float* cf2;
+  // bf16 filter weights: W1t[D][KP] (= Wf1 transposed, K zero-padded), W2t[D][D] (= Wf2
+  // transposed), W2n[D][D] (= Wf2)
+  const uint16_t* W1t;
+  const uint16_t* W2t;
+  const uint16_t* W2n;
+  const float* x;     // x^(t) [N][D]
+  float* h;           // forward output [N][D]
+  const float* gh;    // backward: dE/dh^(t) [N][D]
+  const float* gx_in; // backward: dE/dx^(t+1) [N][D]
+  float* gx_out;      // backward: dE/dx^(t) [N][D], or null for the first block
+  float* forces;      // backward: F [N][3]
+  int force_accumulate;
+};
+
+int cf_kp(int Dr, int bf16);               // padded basis length used by the kernels
+size_t cf_lds_bytes(int D, int KP, int bf16, int backward);
+hipError_t cf_prepare(int D, int bf16);    // raises the dynamic LDS limit of the kernels
+hipError_t launch_partition(const int32_t* rowptr, int n_atoms, int G, int32_t* wg_start,
+                            hipStream_t s);
+hipError_t launch_cf_forward(int D, int bf16, const CfParams& p, int G, hipStream_t s);
+hipError_t launch_cf_backward(int D, int bf16, const CfParams& p, int G, hipStream_t s);
+
+enum GemmMode {
+  GEMM_BIAS = 0,        // Y = A W + b
+  GEMM_SSP_RESID = 1,   // Y = R + ssp(A) W + b
+  GEMM_T_SIGMOID = 2,   // Y = (A W^T) * sigmoid(S)
+  GEMM_T = 3,           // Y = A W^T
+  GEMM_READOUT = 4,     // o = A W + b;  eps = ssp(o).w2 + b2;  Y = sigmoid(o) * w2
+};
+struct GemmArgs {
+  int mode;
+  int M, K, N;          // A [M][K]; output [M][N]
+  const float* A;
+  const float* W;       // [K][N] (plain modes) or [N][K] (transposed modes)
+  const float* bias;    // [N]
+  const float* R;       // residual [M][N]
+  const float* S;       // pre-activation [M][N] for the sigmoid gate
+  float* Y;
+  const float* w2;      // readout second layer [N]
+  float b2;
+  float* eps;           // readout per-atom energy [M]
+};
+size_t gemm_lds_bytes(int K, int N);
+hipError_t gemm_prepare();
+hipError_t launch_gemm(const GemmArgs& g, int n_cu, hipStream_t s);
+hipError_t launch_embed(const int32_t* types, const float* emb, int n_atoms, int D, int n_types,
+                        float* x, DevStatus* st, hipStream_t s);
+hipError_t launch_energy(const float* eps, int n_rep, int n_per, float* energy, DevStatus* st,
+                         hipStream_t s);
+
+// MD (md.hip).
+struct MdCoef {
+  float half_kick;   // dt/2 * kappa / m
+  float half_dt;     // dt/2
+  float c1, c2;      // O-step coefficients
+  float sigma_v;     // Maxwell-Boltzmann width
+  float half_skin2;  // (skin/2)^2
+  uint64_t seed;
+  int periodic;
+  float box;
+};
+hipError_t launch_md_init_vel(const MdCoef& c, int64_t n, float* vel, hipStream_t s);
+hipError_t launch_md_wrap(const MdCoef& c, int64_t n, float* pos, hipStream_t s);
+hipError_t launch_md_baoa(const MdCoef& c, int64_t n, uint64_t step, float* pos, float* vel,
+                          const float* forces, const float* pos_at_build, DevStatus* st,
+                          hipStream_t s);
+hipError_t launch_md_b(const MdCoef& c, int64_t n, float* vel, const float* forces,
+                       hipStream_t s);
+hipError_t launch_md_mark_build(int64_t n, const float* pos, float* pos_at_build, DevStatus* st,
+                                const int64_t* gate, int64_t gate_val, hipStream_t s);
+hipError_t launch_philox(const uint64_t* ctr, uint64_t k0, uint64_t k1, uint64_t* out, int64_t n,
+                         hipStream_t s);
+
+} // namespace sn

@@ -1,0 +1,346 @@
+// Neighbour list: directed edges within a radius, grouped by receiver (CSR).
+//
+// FlashSchNet, §3.2 "Building the neighbor list" defines the edge set (edge
+// j = src -> i = dst within the cutoff) and §4.3 "Index construction under
+// dynamic neighbor lists" groups edges into one contiguous segment per
+// destination by a bucket sort. Here the segments are produced directly:
+// count per receiver -> exclusive scan -> fill, with senders ascending.
+//
+// Membership is decided in IEEE double arithmetic without contraction on the
+// float inputs (see pair_in), so the list is identical to the one a host
+// computes with the same sequence of operations, and symmetric.
+//
+// Two search modes:
+//  * all pairs inside each replica, staged through LDS (chains and small
+//    boxes); the scan over senders is ascending, so rows come out sorted;
+//  * a cell list for one large periodic cube: cells of edge >= r_list,
+//    27-cell search, then a per-row rank sort in LDS.
+#include "common.hpp"
+
+namespace sn {
+
+// Exact membership test for the edge j -> i.
+__device__ __forceinline__ bool pair_in(float xi, float yi, float zi, float xj, float yj, float zj,
+                                        int periodic, double L, double half, double r2) {
+#pragma clang fp contract(off)
+  double dx = (double)xj - (double)xi;
+  double dy = (double)yj - (double)yi;
+  double dz = (double)zj - (double)zi;
+  if (periodic) {
+    if (dx > half) dx = dx - L; else if (dx < -half) dx = dx + L;
+    if (dy > half) dy = dy - L; else if (dy < -half) dy = dy + L;
+    if (dz > half) dz = dz - L; else if (dz < -half) dz = dz + L;
+  }
+  double sx = dx * dx;
+  double sy = dy * dy;
+  double sz = dz * dz;
+  double s = (sx + sy) + sz;
+  return s < r2;
+}
+
+#define SN_GATE                                   \
+  if (gate != nullptr && *gate != gate_val) return;
+
+// ------------------------------------------------------------------ scan
+// Exclusive scan of one value per thread over a 256-thread block.
+__device__ inline int64_t block_exclusive_scan(int64_t v, int64_t* smem, int64_t* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int64_t x = v;
+  for (int off = 1; off < 64; off <<= 1) {
+    int64_t y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) smem[wave] = x;
+  __syncthreads();
+  int64_t wave_off = 0, tot = 0;
+  for (int w = 0; w < kThreads / 64; ++w) {
+    if (w < wave) wave_off += smem[w];
+    tot += smem[w];
+  }
+  __syncthreads();
+  *total = tot;
+  return wave_off + x - v;
+}
+
+__global__ __launch_bounds__(kThreads) void k_scan_local(int32_t* a, int64_t n, int64_t* blocks,
+                                                         const int64_t* gate, int64_t gate_val) {
+  SN_GATE
+  __shared__ int64_t smem[kThreads / 64];
+  const int64_t base = (int64_t)blockIdx.x * kScanChunk + 4 * threadIdx.x;
+  int64_t v[4], s = 0;
+  for (int q = 0; q < 4; ++q) {
+    v[q] = (base + q < n) ? a[base + q] : 0;
+    s += v[q];
+  }
+  int64_t tot;
+  int64_t ex = block_exclusive_scan(s, smem, &tot);
+  for (int q = 0; q < 4; ++q) {
+    if (base + q < n) a[base + q] = (int32_t)ex;  // block-local prefix (block sums < 2^31)
+    ex += v[q];
+  }
+  if (threadIdx.x == 0) blocks[blockIdx.x] = tot;
+}
+
+__global__ __launch_bounds__(kThreads) void k_scan_top(int64_t* blocks, int64_t nblk, DevStatus* st,
+                                                       int64_t capacity, const int64_t* gate,
+                                                       int64_t gate_val) {
+  SN_GATE
+  __shared__ int64_t smem[kThreads / 64];
+  int64_t running = 0;
+  for (int64_t c0 = 0; c0 < nblk; c0 += 4 * kThreads) {
+    const int64_t base = c0 + 4 * threadIdx.x;
+    int64_t v[4], s = 0;
+    for (int q = 0; q < 4; ++q) {
+      v[q] = (base + q < nblk) ? blocks[base + q] : 0;
+      s += v[q];
+    }
+    int64_t tot;
+    int64_t ex = block_exclusive_scan(s, smem, &tot);
+    for (int q = 0; q < 4; ++q) {
+      if (base + q < nblk) blocks[base + q] = running + ex;
+      ex += v[q];
+    }
+    running += tot;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    blocks[nblk] = running;
+    if (capacity >= 0) {
+      const int ovf = running > capacity;
+      st->last_n_edges = running;
+      st->overflow = ovf;
+      if (ovf) dev_fail(st, SN_ERR_CAPACITY, running);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void k_scan_add(int32_t* a, int64_t n, const int64_t* blocks,
+                                                       int64_t nblk, int64_t capacity,
+                                                       const int64_t* gate, int64_t gate_val) {
+  SN_GATE
+  const int64_t total = blocks[nblk];
+  const bool ovf = capacity >= 0 && total > capacity;
+  const int64_t off = blocks[blockIdx.x];
+  const int64_t base = (int64_t)blockIdx.x * kScanChunk + 4 * threadIdx.x;
+  for (int q = 0; q < 4; ++q)
+    if (base + q < n) a[base + q] = ovf ? 0 : (int32_t)(a[base + q] + off);
+  if (blockIdx.x == 0 && threadIdx.x == 0) a[n] = ovf ? 0 : (int32_t)total;
+}
+
+hipError_t launch_exclusive_scan(int32_t* a, int64_t n, int32_t* blocks_i32, DevStatus* st,
+                                 int64_t capacity, const int64_t* gate, int64_t gate_val,
+                                 hipStream_t s) {
+  int64_t* blocks = reinterpret_cast<int64_t*>(blocks_i32);
+  const int64_t nblk = (n + kScanChunk - 1) / kScanChunk;
+  hipLaunchKernelGGL(k_scan_local, dim3((unsigned)nblk), dim3(kThreads), 0, s, a, n, blocks, gate,
+                     gate_val);
+  hipLaunchKernelGGL(k_scan_top, dim3(1), dim3(kThreads), 0, s, blocks, nblk, st, capacity, gate,
+                     gate_val);
+  hipLaunchKernelGGL(k_scan_add, dim3((unsigned)nblk), dim3(kThreads), 0, s, a, n, blocks, nblk,
+                     capacity, gate, gate_val);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ all pairs per replica
+template <bool FILL>
+__global__ __launch_bounds__(kThreads) void k_nbr_allpairs(const float* __restrict__ pos, int N,
+                                                           int periodic, double L, double half,
+                                                           double r2, int32_t* rowptr,
+                                                           int32_t* col, const DevStatus* st,
+                                                           const int64_t* gate, int64_t gate_val) {
+  SN_GATE
+  if (FILL && st->overflow) return;
+  __shared__ float sx[kThreads], sy[kThreads], sz[kThreads];
+  const int il = blockIdx.x * kThreads + threadIdx.x;
+  const int64_t base = (int64_t)blockIdx.y * N;
+  float xi = 0.f, yi = 0.f, zi = 0.f;
+  if (il < N) {
+    xi = pos[3 * (base + il) + 0];
+    yi = pos[3 * (base + il) + 1];
+    zi = pos[3 * (base + il) + 2];
+  }
+  int cnt = 0;
+  int64_t out = 0;
+  if (FILL && il < N) out = rowptr[base + il];
+  for (int j0 = 0; j0 < N; j0 += kThreads) {
+    __syncthreads();
+    const int jl = j0 + threadIdx.x;
+    if (jl < N) {
+      sx[threadIdx.x] = pos[3 * (base + jl) + 0];
+      sy[threadIdx.x] = pos[3 * (base + jl) + 1];
+      sz[threadIdx.x] = pos[3 * (base + jl) + 2];
+    }
+    __syncthreads();
+    const int jn = min(kThreads, N - j0);
+    if (il < N) {
+      for (int jj = 0; jj < jn; ++jj) {
+        const int j = j0 + jj;
+        if (j != il && pair_in(xi, yi, zi, sx[jj], sy[jj], sz[jj], periodic, L, half, r2)) {
+          if (FILL) col[out++] = (int32_t)(base + j);
+          else ++cnt;
+        }
+      }
+    }
+  }
+  if (!FILL && il < N) rowptr[base + il] = cnt;
+}
+
+// ------------------------------------------------------------------ cell list (one periodic cube)
+__global__ __launch_bounds__(kThreads) void k_fill_i32(int32_t* p, int64_t n, int32_t v,
+                                                       const int64_t* gate, int64_t gate_val) {
+  SN_GATE
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * kThreads)
+    p[i] = v;
+}
+
+__device__ __forceinline__ int cell_coord(float x, float inv_cell, int nc) {
+  int c = (int)(x * inv_cell);
+  return c < 0 ? 0 : (c >= nc ? nc - 1 : c);
+}
+
+__global__ __launch_bounds__(kThreads) void k_cell_assign(const float* __restrict__ pos, int N,
+                                                          float inv_cell, int nc, int32_t* atom_cell,
+                                                          int32_t* cell_count, const int64_t* gate,
+                                                          int64_t gate_val) {
+  SN_GATE
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  if (i >= N) return;
+  const int cx = cell_coord(pos[3 * i + 0], inv_cell, nc);
+  const int cy = cell_coord(pos[3 * i + 1], inv_cell, nc);
+  const int cz = cell_coord(pos[3 * i + 2], inv_cell, nc);
+  const int c = (cz * nc + cy) * nc + cx;
+  atom_cell[i] = c;
+  atomicAdd(&cell_count[c], 1);
+}
+
+__global__ __launch_bounds__(kThreads) void k_cell_scatter(int N, const int32_t* atom_cell,
+                                                           const int32_t* cell_start,
+                                                           int32_t* cell_cursor, int32_t* cell_atoms,
+                                                           const int64_t* gate, int64_t gate_val) {
+  SN_GATE
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  if (i >= N) return;
+  const int c = atom_cell[i];
+  const int slot = atomicAdd(&cell_cursor[c], 1);
+  cell_atoms[cell_start[c] + slot] = i;
+}
+
+template <bool FILL>
+__global__ __launch_bounds__(kThreads) void k_nbr_cells(const float* __restrict__ pos, int N, int nc,
+                                                        double L, double half, double r2,
+                                                        const int32_t* atom_cell,
+                                                        const int32_t* cell_start,
+                                                        const int32_t* cell_atoms, int32_t* rowptr,
+                                                        int32_t* col, const DevStatus* st,
+                                                        const int64_t* gate, int64_t gate_val) {
+  SN_GATE
+  if (FILL && st->overflow) return;
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  if (i >= N) return;
+  const float xi = pos[3 * i + 0], yi = pos[3 * i + 1], zi = pos[3 * i + 2];
+  const int c = atom_cell[i];
+  const int cx = c % nc, cy = (c / nc) % nc, cz = c / (nc * nc);
+  int cnt = 0;
+  int64_t out = FILL ? rowptr[i] : 0;
+  for (int dz = -1; dz <= 1; ++dz) {
+    const int zz = (cz + dz + nc) % nc;
+    for (int dy = -1; dy <= 1; ++dy) {
+      const int yy = (cy + dy + nc) % nc;
+      for (int dx = -1; dx <= 1; ++dx) {
+        const int xx = (cx + dx + nc) % nc;
+        const int cc = (zz * nc + yy) * nc + xx;
+        const int k1 = cell_start[cc + 1];
+        for (int k = cell_start[cc]; k < k1; ++k) {
+          const int j = cell_atoms[k];
+          if (j != i && pair_in(xi, yi, zi, pos[3 * j], pos[3 * j + 1], pos[3 * j + 2], 1, L,
+                                half, r2)) {
+            if (FILL) col[out++] = j;
+            else ++cnt;
+          }
+        }
+      }
+    }
+  }
+  if (!FILL) rowptr[i] = cnt;
+}
+
+// Rank sort of each row (distinct values), one wave per row, staged in LDS.
+__global__ __launch_bounds__(kThreads) void k_sort_rows(const int32_t* rowptr, int32_t* col, int N,
+                                                        DevStatus* st, const int64_t* gate,
+                                                        int64_t gate_val) {
+  SN_GATE
+  if (st->overflow) return;
+  __shared__ int32_t buf[kThreads / 64][kSortRowMax];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = blockIdx.x * (kThreads / 64) + wave;
+  int s = 0, n = 0;
+  if (row < N) {
+    s = rowptr[row];
+    n = rowptr[row + 1] - s;
+    if (n > kSortRowMax) {
+      if (lane == 0) dev_fail(st, SN_ERR_UNSUPPORTED, row);
+      n = 0;
+    }
+  }
+  for (int e = lane; e < n; e += 64) buf[wave][e] = col[s + e];
+  __syncthreads();
+  for (int e = lane; e < n; e += 64) {
+    const int v = buf[wave][e];
+    int rank = 0;
+    for (int k = 0; k < n; ++k) rank += buf[wave][k] < v;
+    col[s + rank] = v;
+  }
+}
+
+static unsigned blocks_for(int64_t n) { return (unsigned)((n + kThreads - 1) / kThreads); }
+
+hipError_t launch_build_neighbors(const NbrGeom& g, const float* pos, int32_t* rowptr, int32_t* col,
+                                  int64_t edge_capacity, char* ws, const WsLayout& L,
+                                  const int64_t* gate, int64_t gate_val, hipStream_t s) {
+  DevStatus* st = reinterpret_cast<DevStatus*>(ws + L.status);
+  int32_t* scan_blocks = reinterpret_cast<int32_t*>(ws + L.scan_blocks);
+  const int64_t n_tot = (int64_t)g.n_rep * g.n_per;
+  hipError_t e;
+  if (g.cells_per_axis == 0) {
+    dim3 grid(blocks_for(g.n_per), (unsigned)g.n_rep);
+    hipLaunchKernelGGL(k_nbr_allpairs<false>, grid, dim3(kThreads), 0, s, pos, g.n_per, g.periodic,
+                       g.L, g.half, g.r2, rowptr, col, st, gate, gate_val);
+    if ((e = launch_exclusive_scan(rowptr, n_tot, scan_blocks, st, edge_capacity, gate, gate_val,
+                                   s)) != hipSuccess)
+      return e;
+    hipLaunchKernelGGL(k_nbr_allpairs<true>, grid, dim3(kThreads), 0, s, pos, g.n_per, g.periodic,
+                       g.L, g.half, g.r2, rowptr, col, st, gate, gate_val);
+    return hipGetLastError();
+  }
+  const int nc = g.cells_per_axis;
+  const int64_t ncell = (int64_t)nc * nc * nc;
+  int32_t* cstart = reinterpret_cast<int32_t*>(ws + L.cell_count);   // counts, then starts
+  int32_t* ccur = reinterpret_cast<int32_t*>(ws + L.cell_start);     // scatter cursors
+  int32_t* catoms = reinterpret_cast<int32_t*>(ws + L.cell_atoms);
+  int32_t* acell = reinterpret_cast<int32_t*>(ws + L.atom_cell);
+  const int N = g.n_per;
+  hipLaunchKernelGGL(k_fill_i32, dim3(blocks_for(ncell + 1)), dim3(kThreads), 0, s, cstart,
+                     ncell + 1, 0, gate, gate_val);
+  hipLaunchKernelGGL(k_fill_i32, dim3(blocks_for(ncell)), dim3(kThreads), 0, s, ccur, ncell, 0,
+                     gate, gate_val);
+  hipLaunchKernelGGL(k_cell_assign, dim3(blocks_for(N)), dim3(kThreads), 0, s, pos, N, g.inv_cell,
+                     nc, acell, cstart, gate, gate_val);
+  if ((e = launch_exclusive_scan(cstart, ncell, scan_blocks, st, -1, gate, gate_val, s)) !=
+      hipSuccess)
+    return e;
+  hipLaunchKernelGGL(k_cell_scatter, dim3(blocks_for(N)), dim3(kThreads), 0, s, N, acell, cstart,
+                     ccur, catoms, gate, gate_val);
+  hipLaunchKernelGGL(k_nbr_cells<false>, dim3(blocks_for(N)), dim3(kThreads), 0, s, pos, N, nc,
+                     g.L, g.half, g.r2, acell, cstart, catoms, rowptr, col, st, gate, gate_val);
+  if ((e = launch_exclusive_scan(rowptr, N, scan_blocks, st, edge_capacity, gate, gate_val, s)) !=
+      hipSuccess)
+    return e;
+  hipLaunchKernelGGL(k_nbr_cells<true>, dim3(blocks_for(N)), dim3(kThreads), 0, s, pos, N, nc, g.L,
+                     g.half, g.r2, acell, cstart, catoms, rowptr, col, st, gate, gate_val);
+  hipLaunchKernelGGL(k_sort_rows, dim3((unsigned)((N + 3) / 4)), dim3(kThreads), 0, s, rowptr, col,
+                     N, st, gate, gate_val);
+  return hipGetLastError();
+}
+
+} // namespace sn

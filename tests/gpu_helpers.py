@@ -1,0 +1,57 @@
+"""Shared plumbing for the GPU parity tests (inputs, oracle calls, tolerances)."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from gen.configs import CONFIGS, make_config
+
+# Parity bars: energy within 1e-5 relative; forces within 1e-4 (max abs) of the
+# oracle's force RMS, for fp32 filters. bf16 filters: the oracle uses the same
+# bf16-rounded weights but exact activations, so the bars widen to 1e-3 on the
+# energy and 5e-2 (max) / 1e-2 (RMS) on the forces.
+E_TOL_F32, F_TOL_F32 = 1e-5, 1e-4
+E_TOL_BF16, F_TOL_BF16, F_RMS_TOL_BF16 = 1e-3, 5e-2, 1e-2
+
+
+def oracle_desc(m):
+    return oracle.ModelDesc(m.n_types, m.D, m.Dr, m.T, m.rbf_min, m.rbf_max, m.r_cut, m.H,
+                            m.filter_dtype)
+
+
+def lib_desc(lib, m):
+    return lib.make_desc(m.n_types, m.D, m.Dr, m.T, m.H, m.rbf_min, m.rbf_max, m.r_cut,
+                         m.filter_dtype)
+
+
+def lib_system(lib, s, n_replicas=None):
+    R = s.n_replicas if n_replicas is None else n_replicas
+    return lib.make_system(R, s.atoms_per_replica, s.periodic, s.box)
+
+
+def gpu_neighbors(lib, system, pos_np, r_list, capacity=None, ws=None):
+    import torch
+    n = system.n_replicas * system.atoms_per_replica
+    if ws is None:
+        ws = lib.Workspace(lib.sn_workspace_size(None, system))
+    p = torch.from_numpy(np.ascontiguousarray(pos_np, dtype=np.float32)).cuda().reshape(-1)
+    rowptr = torch.full((n + 1,), -7, dtype=torch.int32, device="cuda")
+    cap = capacity if capacity is not None else max(1, n * 200)
+    col = torch.full((max(cap, 1),), -7, dtype=torch.int32, device="cuda")
+    ne = lib.sn_build_neighbors(system, p, r_list, rowptr, col, cap, ws)
+    return p, rowptr, col, ne, ws
+
+
+def assert_energy_forces(E_gpu, F_gpu, E_ref, F_ref, bf16=False, what=""):
+    E_gpu = np.asarray(E_gpu, dtype=np.float64)
+    F_gpu = np.asarray(F_gpu, dtype=np.float64).reshape(-1, 3)
+    e_tol = E_TOL_BF16 if bf16 else E_TOL_F32
+    rel = np.abs(E_gpu - E_ref) / np.maximum(np.abs(E_ref), 1e-30)
+    assert np.all(rel <= e_tol), f"{what} energy rel err {rel.max():.3e} > {e_tol}"
+    rms = np.sqrt(np.mean(F_ref ** 2))
+    err = np.abs(F_gpu - F_ref)
+    f_tol = F_TOL_BF16 if bf16 else F_TOL_F32
+    assert err.max() <= f_tol * rms, f"{what} force max err {err.max() / rms:.3e} x rms > {f_tol}"
+    if bf16:
+        assert np.sqrt(np.mean(err ** 2)) <= F_RMS_TOL_BF16 * rms
+    return rel.max(), err.max() / rms
