@@ -1,0 +1,220 @@
+"""Throughput of the SchNet CFConv energy + force path on one MI355X.
+
+A step is one pass of the whole hot path over one batch: the Langevin (BAOAB)
+update of every replica, a neighbour-list rebuild (receiver-sorted CSR), the
+fused CFConv energy evaluation, and the analytic backward for the forces.
+The workload is 64 replicas of a 269-bead coarse-grained chain (D 128,
+50 Gaussians on 0-12 A, cosine cutoff 12 A, 3 interaction blocks, fp32), with
+synthetic seeded positions and random-init weights. The list is rebuilt every
+step at the cutoff radius, so every listed edge contributes.
+
+Prints one JSON line: directed edges through energy+forces per second (value),
+replica-steps per second, the roofline of the dominant kernel (backward
+CFConv, timed with HIP events around every launch inside the timed region)
+and the fp64 oracle timed on the host cores on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP32_MFMA_TFLOPS = 157.3     # MI355X dense fp32 matrix peak
+PEAK_BF16_MFMA_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cfconv_bwd_cg269x64_counters.txt")
+CFCONV_SRC = os.path.join(ROOT, "schnet_continuous_filter_amd", "csrc", "cfconv.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="cg269x64",
+                    choices=["cg269x64", "cg32", "bulk4k", "bulk64k", "md1024"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a device copy of known size (for counter scaling)")
+    return ap.parse_args()
+
+
+def kernel_hash() -> str:
+    return hashlib.sha256(open(CFCONV_SRC, "rb").read()).hexdigest()[:16]
+
+
+def copy_calibration():
+    import torch
+    n = 256 * 1024 * 1024 // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each_way": n * 4, "launches": 5}))
+
+
+def cpu_baseline(cfg, seconds: float):
+    """The oracle as it stands, on a bounded sample of the same workload:
+    8 replicas, MD steps (rebuild + energy/forces + BAOAB) until the budget."""
+    import numpy as np
+    import oracle
+    from gen.configs import make_config
+    from threadpoolctl import threadpool_info
+
+    R = 8
+    c, pos, types, w = make_config(cfg.name, n_replicas=R)
+    m = c.model
+    desc = oracle.ModelDesc(m.n_types, m.D, m.Dr, m.T, m.rbf_min, m.rbf_max, m.r_cut, m.H,
+                            m.filter_dtype)
+    W = oracle.unpack_weights(desc, w)
+    N = c.system.atoms_per_replica
+    per = c.system.periodic
+    box = c.system.box
+    state = {}
+
+    def rebuild(p):
+        state["nl"] = oracle.neighbor_list(np.asarray(p, np.float32), R, N, per, box, m.r_cut)
+
+    def forces(p):
+        return oracle.energy_forces(desc, None, p, types, *state["nl"], n_replicas=R,
+                                    periodic=per, box=box, weights=W)
+
+    rebuild(pos)
+    E0, F0 = forces(pos.astype(np.float64))
+    vel = oracle.init_velocities(0, len(pos), 300.0, 100.0)
+    p, v, F = pos.astype(np.float64), vel, F0
+    steps, edges = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        p, v, F, E, _ = oracle.baoab_run(forces, rebuild, p, v, F, dt_fs=2.0, temperature_K=300.0,
+                                         gamma_per_ps=1.0, mass_amu=100.0, skin=0.0,
+                                         rebuild_every=1, seed=0, step0=steps, n_steps=1,
+                                         periodic=per, box=box)
+        steps += 1
+        edges += len(state["nl"][1])
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": edges / dt, "unit": "edges/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{R} of {c.system.n_replicas} replicas x {N} beads, {steps} MD steps "
+                      f"(rebuild + fp64 energy/forces + BAOAB) in {dt:.1f} s; "
+                      f"{R * steps / dt:.3g} replica-steps/s",
+            "replica_steps_per_s": R * steps / dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    from gen.configs import CONFIGS, make_config
+    from schnet_continuous_filter_amd import _lib as L
+
+    cfg = CONFIGS[args.workload]
+    c, pos, types, w = make_config(cfg.name)
+    m, s = c.model, c.system
+    R, N = s.n_replicas, s.atoms_per_replica
+    desc = L.make_desc(m.n_types, m.D, m.Dr, m.T, m.H, m.rbf_min, m.rbf_max, m.r_cut,
+                       m.filter_dtype)
+    system = L.make_system(R, N, s.periodic, s.box)
+    model = L.sn_model_create(desc, w)
+    ws = L.Workspace(L.sn_workspace_size(desc, system))
+    dev = torch.device("cuda")
+    p = torch.from_numpy(pos).to(dev).reshape(-1)
+    t = torch.from_numpy(types).to(dev)
+    if c.md is not None:          # the MD workload keeps its own skin and cadence
+        md = L.make_md_params(c.md.dt_fs, c.md.temperature_K, c.md.gamma_per_ps, c.md.mass_amu,
+                              c.md.skin, c.md.rebuild_every, 0)
+        r_list = m.r_cut + c.md.skin
+    else:                         # rebuild every step at the cutoff
+        md = L.make_md_params(2.0, 300.0, 1.0, 100.0, 0.0, 1, 0)
+        r_list = m.r_cut
+    rowptr0 = torch.zeros(R * N + 1, dtype=torch.int32, device=dev)
+    ne0 = L.sn_build_neighbors(system, p, r_list, rowptr0, None, 0, ws)
+    L.sn_reset_device_status(ws)
+    capacity = int(ne0 * 1.5) + 1024
+    state = L.MdState(p, capacity)
+    energy = torch.empty(R, dtype=torch.float32, device=dev)
+    L.sn_md_init(model, system, t, md, state, energy, ws)
+    L.sn_md_step(model, system, t, md, state, args.warmup, energy, ws)
+    torch.cuda.synchronize()
+    L.sn_profile_read(0)
+    L.sn_profile_read(1)
+
+    L.sn_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    L.sn_md_step(model, system, t, md, state, args.steps, energy, ws)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    L.sn_profile_enable(False)
+    bwd_ms, bwd_n = L.sn_profile_read(1)
+    fwd_ms, fwd_n = L.sn_profile_read(0)
+    status, detail, n_rebuilds = L.sn_get_device_status(ws)
+    if status != 0:
+        print(f"device status {status} ({L.status_string(status)}), detail {detail}",
+              file=sys.stderr)
+        sys.exit(1)
+    # edge count on the final positions (untimed)
+    ne = L.sn_build_neighbors(system, state.pos, r_list, state.rowptr, state.col, capacity, ws)
+
+    ms_per_step = 1000.0 * elapsed / args.steps
+    edges_per_s = ne * args.steps / elapsed
+    bf16 = m.filter_dtype == 1
+    flops_bwd = 4.0 * m.D * (m.Dr + m.D) * ne          # recompute (2D(Dr+D)) + dgrad (2D(Dr+D))
+    avg_bwd_s = bwd_ms / 1000.0 / max(bwd_n, 1)
+    achieved = flops_bwd / avg_bwd_s / 1e12
+    peak = PEAK_BF16_MFMA_TFLOPS if bf16 else PEAK_FP32_MFMA_TFLOPS
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        rec = json.load(open(TRAFFIC_FILE))
+        if rec.get("kernel_hash") == kernel_hash() and rec.get("workload") == cfg.name:
+            traffic = rec.get("bytes_per_launch")
+    line = {
+        "metric": "CFConv energy+force edges/sec and replica-MD-steps/sec at 1 GPU; % HBM roofline",
+        "value": edges_per_s,
+        "unit": "edges/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16-filter/f32" if bf16 else "f32",
+        "data": "synthetic (seeded chains/boxes, random-init weights)",
+        "config": {"workload": cfg.name, "replicas": R, "atoms_per_replica": N,
+                   "directed_edges": ne, "list_radius_A": r_list, "D": m.D, "Dr": m.Dr, "T": m.T,
+                   "r_cut_A": m.r_cut, "step": "BAOAB + neighbour rebuild + energy/forces"},
+        "replica_steps_per_s": R * args.steps / elapsed,
+        "roofline": {"kernel": "k_cf_bwd (fused CFConv backward, one interaction block)",
+                     "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": traffic,
+                     "flops_per_launch": flops_bwd, "avg_launch_us": avg_bwd_s * 1e6,
+                     "launches": bwd_n,
+                     "fwd_avg_launch_us": fwd_ms * 1000.0 / max(fwd_n, 1)},
+        "n_rebuilds": n_rebuilds,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    print(json.dumps(line))
+    L.sn_model_destroy(model)
+
+
+if __name__ == "__main__":
+    main()

@@ -498,6 +498,9 @@ sn_status sn_md_step(const sn_model* m, const sn_system* sys, const int32_t* typ
   char* w = static_cast<char*>(ws);
   DevStatus* st = reinterpret_cast<DevStatus*>(w + L.status);
   float* e_out = energy ? energy : reinterpret_cast<float*>(w + L.eps) + n;
+  // a displacement flag left by an earlier call (for instance before a restore) must not
+  // trigger a rebuild in this one
+  if (hipMemsetAsync(&st->rebuild_req, 0, sizeof(int64_t), s) != hipSuccess) return SN_ERR_HIP;
   for (int32_t k = 0; k < n_steps; ++k) {
     const uint64_t step = state->step;
     hipError_t e = launch_md_baoa(su.c, n, step, state->pos, state->vel, state->forces,

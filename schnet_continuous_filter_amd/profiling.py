@@ -1,0 +1,103 @@
+"""Summaries of rocprofv3 output for the kernels of this library.
+
+  python -m schnet_continuous_filter_amd.profiling stats KT_STATS_CSV OUT_TXT --cmd "..."
+  python -m schnet_continuous_filter_amd.profiling traffic FETCH_CSV WRITE_CSV \
+      COPY_FETCH_CSV COPY_WRITE_CSV OUT_TXT --kernel k_cf_bwd --workload cg269x64 --cmd "..."
+
+``traffic`` scales FETCH_SIZE and WRITE_SIZE (KiB per dispatch) by what the
+same counters read for a device copy of known size (bench.py
+--copy-calibration copies 256 MiB five times), and records the result with a
+hash of the kernel source so that bench.py reports it only while the kernel
+is unchanged.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import json
+import os
+
+CFCONV_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", "cfconv.hip")
+COPY_BYTES = 256 * 1024 * 1024
+
+
+def kernel_hash() -> str:
+    return hashlib.sha256(open(CFCONV_SRC, "rb").read()).hexdigest()[:16]
+
+
+def stats(csv_path: str, out_txt: str, cmd: str, top: int = 25) -> None:
+    rows = list(csv.DictReader(open(csv_path)))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    lines = [f"# rocprofv3 --kernel-trace --stats summary", f"# command: {cmd}",
+             f"# total kernel time {total / 1e6:.3f} ms over {sum(int(r['Calls']) for r in rows)} "
+             "dispatches", "",
+             f"{'kernel':72s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} "
+             f"{'share%':>7s}"]
+    for r in rows[:top]:
+        lines.append(f"{r['Name'][:72]:72s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.1f} "
+                     f"{float(r['MinNs']) / 1e3:10.1f} {float(r['MaxNs']) / 1e3:10.1f} "
+                     f"{float(r['Percentage']):7.2f}")
+    open(out_txt, "w").write("\n".join(lines) + "\n")
+
+
+def _per_kernel(csv_path):
+    d = collections.defaultdict(list)
+    for r in csv.DictReader(open(csv_path)):
+        d[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return d
+
+
+def _pick(d, substr):
+    keys = [k for k in d if substr in k]
+    if not keys:
+        raise KeyError(f"no kernel matching {substr!r}")
+    vals = sum((d[k] for k in keys), [])
+    return sum(vals) / len(vals), len(vals), keys
+
+
+def traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, out_txt, kernel, workload,
+            cmd) -> dict:
+    f_kib, nf, names = _pick(_per_kernel(fetch_csv), kernel)
+    w_kib, nw, _ = _pick(_per_kernel(write_csv), kernel)
+    cf_kib, _, _ = _pick(_per_kernel(copy_fetch_csv), "copyBuffer")
+    cw_kib, _, _ = _pick(_per_kernel(copy_write_csv), "copyBuffer")
+    f_scale = COPY_BYTES / (cf_kib * 1024.0)
+    w_scale = COPY_BYTES / (cw_kib * 1024.0)
+    rec = {
+        "kernel": names[0], "workload": workload, "kernel_hash": kernel_hash(),
+        "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib, "dispatches": nf,
+        "copy_fetch_kib": cf_kib, "copy_write_kib": cw_kib, "fetch_scale": f_scale,
+        "write_scale": w_scale,
+        "bytes_per_launch": f_kib * 1024.0 * f_scale + w_kib * 1024.0 * w_scale,
+        "command": cmd,
+    }
+    with open(out_txt, "w") as f:
+        f.write(json.dumps(rec) + "\n")
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("out")
+    s.add_argument("--cmd", required=True)
+    t = sub.add_parser("traffic")
+    for a in ("fetch", "write", "copy_fetch", "copy_write", "out"):
+        t.add_argument(a)
+    t.add_argument("--kernel", default="k_cf_bwd")
+    t.add_argument("--workload", default="cg269x64")
+    t.add_argument("--cmd", required=True)
+    a = ap.parse_args()
+    if a.what == "stats":
+        stats(a.csv, a.out, a.cmd)
+    else:
+        print(json.dumps(traffic(a.fetch, a.write, a.copy_fetch, a.copy_write, a.out, a.kernel,
+                                 a.workload, a.cmd)))
+
+
+if __name__ == "__main__":
+    main()

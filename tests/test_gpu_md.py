@@ -1,0 +1,176 @@
+"""GPU MD path: Philox words, noise, BAOAB trajectory vs the oracle, restore,
+rebuild guard."""
+import numpy as np
+import pytest
+
+import oracle
+from gen.configs import CONFIGS, make_config, make_weights
+from tests.gpu_helpers import lib_desc, lib_system, oracle_desc
+
+pytestmark = pytest.mark.gpu
+
+
+def test_philox_words_exact(gpu_lib):
+    import torch
+    rng = np.random.default_rng(0)
+    ctr = rng.integers(0, 2**63, size=(5000, 4), dtype=np.int64).view(np.uint64)
+    ctr[:10] = 0
+    ctr[10:20, 0] = np.uint64(2**64 - 1)
+    key = (0xDEADBEEFCAFEBABE, 12345)
+    out = torch.empty(5000 * 4, dtype=torch.int64, device="cuda")
+    gpu_lib.sn_philox4x64_10(torch.from_numpy(ctr.view(np.int64).ravel()).cuda(), key[0], key[1],
+                             out)
+    ref = oracle.philox4x64_10(ctr, key)
+    assert np.array_equal(out.cpu().numpy().view(np.uint64).reshape(-1, 4), ref)
+
+
+def _md_setup(lib, name, R, seed=0, gamma=1.0, skin=1.0, rebuild_every=10, filter_f32=True):
+    import torch
+    cfg, pos, types, w = make_config(name, seed=seed, n_replicas=R)
+    m = cfg.model
+    if filter_f32 and m.filter_dtype != 0:
+        from dataclasses import replace
+        m = replace(m, filter_dtype=0)
+    desc = lib_desc(lib, m)
+    system = lib_system(lib, cfg.system, R)
+    model = lib.sn_model_create(desc, w)
+    ws = lib.Workspace(lib.sn_workspace_size(desc, system))
+    p = torch.from_numpy(pos).cuda().reshape(-1)
+    t = torch.from_numpy(types).cuda()
+    params = lib.make_md_params(2.0, 300.0, gamma, 100.0, skin, rebuild_every, 42)
+    state = lib.MdState(p, 400 * len(pos))
+    energy = torch.empty(R, dtype=torch.float32, device="cuda")
+    return cfg, m, pos, types, w, desc, system, model, ws, t, params, state, energy
+
+
+def test_short_trajectory_matches_oracle(gpu_lib):
+    """Ten BAOAB steps of 3 chain replicas with the same Philox stream: the
+    GPU (fp32) and the oracle (fp64) trajectories agree to fp32 accuracy."""
+    lib = gpu_lib
+    cfg, m, pos, types, w, desc, system, model, ws, t, params, state, energy = _md_setup(
+        lib, "cg269x64", 3)
+    try:
+        lib.sn_md_init(model, system, t, params, state, energy, ws)
+        v0 = state.vel.cpu().double().numpy().reshape(-1, 3)
+        F0 = state.forces.cpu().double().numpy().reshape(-1, 3)
+        lib.sn_md_step(model, system, t, params, state, 10, energy, ws)
+        import torch
+        torch.cuda.synchronize()
+        st = lib.sn_get_device_status(ws)
+        assert st[0] == 0, st
+        p_gpu = state.pos.cpu().double().numpy().reshape(-1, 3)
+        v_gpu = state.vel.cpu().double().numpy().reshape(-1, 3)
+        E_gpu = energy.cpu().double().numpy()
+        assert state.step == 10
+    finally:
+        lib.sn_model_destroy(model)
+
+    d = oracle_desc(m)
+    W = oracle.unpack_weights(d, w)
+    v_init = oracle.init_velocities(42, len(pos), 300.0, 100.0)
+    assert np.max(np.abs(v0 - v_init)) < 1e-6 * np.max(np.abs(v_init))
+    nl = {}
+
+    def rebuild(p):
+        nl["l"] = oracle.neighbor_list(np.asarray(p, np.float32), 3, 269, False, 0.0, m.r_cut + 1.0)
+
+    def forces(p):
+        return oracle.energy_forces(d, None, p, types, *nl["l"], n_replicas=3, weights=W)
+
+    rebuild(pos)
+    E0, F0o = forces(pos.astype(np.float64))
+    assert np.max(np.abs(F0 - F0o)) < 1e-4 * np.sqrt(np.mean(F0o ** 2))
+    p_o, v_o, F_o, E_o, _ = oracle.baoab_run(forces, rebuild, pos, v_init, F0o, dt_fs=2.0,
+                                             temperature_K=300.0, gamma_per_ps=1.0,
+                                             mass_amu=100.0, skin=1.0, rebuild_every=10, seed=42,
+                                             step0=0, n_steps=10)
+    # displacement over 10 steps is ~ 0.03 A; compare against it
+    # fp32 positions of up to ~200 A carry ~1e-5 A rounding per update; the
+    # displacement over 10 steps is ~0.03 A
+    disp = np.max(np.abs(p_o - pos))
+    assert np.max(np.abs(p_gpu - p_o)) < 1e-2 * disp + 2e-4
+    assert np.max(np.abs(v_gpu - v_o)) < 1e-3 * np.sqrt(np.mean(v_o ** 2))
+    assert np.all(np.abs(E_gpu - E_o) <= 1e-4 * np.abs(E_o) + 1e-4)
+
+
+def test_restore_replays_bitwise(gpu_lib):
+    import torch
+    lib = gpu_lib
+    cfg, m, pos, types, w, desc, system, model, ws, t, params, state, energy = _md_setup(
+        lib, "cg269x64", 2, rebuild_every=5)
+    try:
+        lib.sn_md_init(model, system, t, params, state, energy, ws)
+        lib.sn_md_step(model, system, t, params, state, 7, energy, ws)
+        snap = {k: getattr(state, k).clone() for k in
+                ("pos", "vel", "forces", "pos_at_build", "rowptr", "col")}
+        step = state.step
+        lib.sn_md_step(model, system, t, params, state, 9, energy, ws)
+        a = (state.pos.clone(), state.vel.clone(), energy.clone())
+        for k, v in snap.items():
+            getattr(state, k).copy_(v)
+        state.step = step
+        lib.sn_md_step(model, system, t, params, state, 9, energy, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(a[0], state.pos) and torch.equal(a[1], state.vel)
+        assert torch.equal(a[2], energy)
+    finally:
+        lib.sn_model_destroy(model)
+
+
+def test_skin_guard_forces_rebuild(gpu_lib):
+    """With a tiny skin the displacement guard must rebuild between scheduled
+    rebuilds; with a huge cadence only the guard rebuilds."""
+    import torch
+    lib = gpu_lib
+    cfg, m, pos, types, w, desc, system, model, ws, t, params, state, energy = _md_setup(
+        lib, "cg269x64", 2, skin=0.02, rebuild_every=1000)
+    try:
+        lib.sn_md_init(model, system, t, params, state, energy, ws)
+        lib.sn_md_step(model, system, t, params, state, 20, energy, ws)
+        st, det, nrb = lib.sn_get_device_status(ws)
+        assert st == 0
+        assert nrb >= 3, f"only {nrb} builds"
+        # the list in the state is the exact list of the current positions at r_cut + skin
+        # whenever a rebuild just happened; check the forces against a fresh evaluation
+        p = state.pos.clone()
+        rowptr = torch.zeros_like(state.rowptr)
+        col = torch.zeros_like(state.col)
+        lib.sn_build_neighbors(system, p, m.r_cut + 0.02, rowptr, col, col.numel(), ws)
+        e2 = torch.empty_like(energy)
+        f2 = torch.empty_like(state.forces)
+        lib.sn_energy_forces(model, system, p, t, rowptr, col, e2, f2, ws)
+        torch.cuda.synchronize()
+        assert torch.allclose(e2, energy, rtol=1e-6, atol=0)
+    finally:
+        lib.sn_model_destroy(model)
+
+
+def test_zero_model_keeps_temperature(gpu_lib):
+    """Zero weights give zero forces: the O step is then the exact OU process
+    and the kinetic temperature stays at 300 K."""
+    import torch
+    lib = gpu_lib
+    cfg = CONFIGS["cg269x64"]
+    m = cfg.model
+    R = 64
+    from gen.configs import make_system
+    pos, types = make_system(cfg.system, m.n_types, 0, R)
+    w = np.zeros(lib.sn_model_weight_count(lib_desc(lib, m)), np.float32)
+    desc = lib_desc(lib, m)
+    system = lib_system(lib, cfg.system, R)
+    model = lib.sn_model_create(desc, w)
+    try:
+        ws = lib.Workspace(lib.sn_workspace_size(desc, system))
+        params = lib.make_md_params(2.0, 300.0, 20.0, 100.0, 2.0, 10, 7)
+        state = lib.MdState(torch.from_numpy(pos).cuda().reshape(-1), 400 * len(pos))
+        energy = torch.empty(R, dtype=torch.float32, device="cuda")
+        t = torch.from_numpy(types).cuda()
+        lib.sn_md_init(model, system, t, params, state, energy, ws)
+        lib.sn_md_step(model, system, t, params, state, 30, energy, ws)
+        torch.cuda.synchronize()
+        assert torch.all(state.forces == 0)
+        v = state.vel.cpu().double().numpy().reshape(-1, 3)
+        ke = 0.5 * 100.0 * np.sum(v ** 2, axis=1) / oracle.md.KAPPA
+        assert abs(ke.mean() / (1.5 * oracle.md.KB * 300.0) - 1) < 0.03
+    finally:
+        lib.sn_model_destroy(model)
