@@ -8,9 +8,8 @@
 // or better (the replica sum here accumulates in double).
 //
 // The dense layers are [atoms x K] x [K x N] products on fp32 MFMA
-// (v_mfma_f32_32x32x2_f32). A work-group stages the weight matrix in LDS once
-// and loops over 64-atom tiles; each wave owns 32x32 output blocks and the
-// elementwise prologue/epilogue of each mode is fused into the product.
+// (v_mfma_f32_32x32x2_f32); each kernel chains the two layers of one network
+// with its activation (or gate) in between.
 #include "common.hpp"
 
 namespace sn {
@@ -27,164 +26,121 @@ __device__ __forceinline__ float sigmoid_f(float a) {
   return a >= 0.f ? inv : t * inv;
 }
 
-size_t gemm_lds_bytes(int K, int N) {
-  // weight region (max of plain [K][N+4] and transposed [N][K+4]) + A tile [64][K+4]
-  const size_t w = (size_t)K * (N + 4) > (size_t)N * (K + 4) ? (size_t)K * (N + 4) : (size_t)N * (K + 4);
-  const size_t a = (size_t)kTileAtoms * ((K > N ? K : N) + 4);
-  return (w + a) * 4;
+// ------------------------------------------------------------------ fused atom-wise pairs
+// A work-group takes 32 atoms at a time. The A tile sits in LDS (fp32, K
+// permuted per lane so one 16-byte load feeds four MFMAs); B operands come
+// straight from the weight matrices in global memory (row-major [K][N], so a
+// wave's 32 lanes read 128 contiguous bytes per row; the matrices stay in L2).
+// Each kernel chains two products with the elementwise step between them in
+// registers and the intermediate back in the same LDS tile.
+constexpr int kRows = 32;
+
+template <int K>
+__device__ __forceinline__ f32x16 mma_lds_glb(const float* Ap, const float* __restrict__ W,
+                                              int ldw, int c, int h) {
+  f32x16 acc = f32x16{};
+#pragma unroll 4
+  for (int k0 = 0; k0 < K; k0 += 8) {
+    const float* wp = W + (size_t)(k0 + 4 * h) * ldw + c;
+    const float b0 = wp[0], b1 = wp[ldw], b2 = wp[2 * ldw], b3 = wp[3 * ldw];
+    const f32x4 av = *reinterpret_cast<const f32x4*>(Ap + k0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.x, b0, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.y, b1, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.z, b2, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.w, b3, acc, 0, 0, 0);
+  }
+  return acc;
 }
 
-template <int K, int N, int MODE>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
-  constexpr bool TR = (MODE == GEMM_T_SIGMOID || MODE == GEMM_T);
-  constexpr int SWP = N + 4;           // plain weights [K][N+4]
-  constexpr int SWT = K + 4;           // transposed weights [N][K+4]
-  constexpr int SW = TR ? SWT : SWP;
-  constexpr int SA = (K > N ? K : N) + 4;
-  constexpr int NCB = N / 32, NBLK = 2 * NCB, NBW = (NBLK + 3) / 4;
-  constexpr int WSZ = (K * SWP > N * SWT) ? K * SWP : N * SWT;
-  extern __shared__ __align__(16) unsigned char lds_raw[];
-  float* Ws = reinterpret_cast<float*>(lds_raw);
-  float* At = Ws + WSZ;
+__device__ __forceinline__ int blk_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
+// MODE: ATOM_UPDATE_FWD  a = h W1 + b1 (stored);  x' = x + ssp(a) W2 + b2
+//       ATOM_UPDATE_BWD  g_a = (g_x W2^T) * sigmoid(a);  g_h = g_a W1^T   (W1, W2 given transposed)
+//       ATOM_READOUT     o = x W1 + b1;  eps = ssp(o).w2 + b2;  g_x = (sigmoid(o) * w2) W1^T
+template <int D, int N1, int MODE>
+__global__ __launch_bounds__(kThreads) void k_atom(AtomArgs g) {
+  constexpr int SA = D + 4;
+  __shared__ __align__(16) float At[kRows * SA];
+  __shared__ float Sh[MODE == ATOM_READOUT ? kRows * (N1 + 1) : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, li = lane & 31;
-  if constexpr (TR) {
-    for (int idx = tid; idx < N * K; idx += kThreads) {
-      const int n = idx / K, k = idx - n * K;
-      Ws[n * SWT + k] = g.W[idx];
-    }
-  } else {
-    for (int idx = tid; idx < K * N; idx += kThreads) {
-      const int k = idx / N, n = idx - k * N;
-      Ws[k * SWP + n] = g.W[idx];
-    }
-  }
-  __syncthreads();
-
-  for (int m0 = blockIdx.x * kTileAtoms; m0 < g.M; m0 += gridDim.x * kTileAtoms) {
-    for (int idx = tid; idx < kTileAtoms * K; idx += kThreads) {
-      const int r = idx / K, k = idx - r * K;
-      const int m = m0 + r;
-      float v = m < g.M ? g.A[(size_t)m * K + k] : 0.f;
-      if constexpr (MODE == GEMM_SSP_RESID) v = ssp_f(v);
-      At[r * SA + k] = v;
+  const float* Ap = At + li * SA + 4 * h;
+  for (int m0 = blockIdx.x * kRows; m0 < g.M; m0 += gridDim.x * kRows) {
+    // A tile: rows m0.., D columns, float4 loads
+    for (int idx = tid; idx < kRows * D / 4; idx += kThreads) {
+      const int r = idx / (D / 4), k4 = idx - r * (D / 4);
+      f32x4 v = f32x4{};
+      if (m0 + r < g.M) v = *reinterpret_cast<const f32x4*>(g.A + (size_t)(m0 + r) * D + 4 * k4);
+      *reinterpret_cast<f32x4*>(At + r * SA + 4 * k4) = v;
     }
     __syncthreads();
-    f32x16 accs[NBW];
-#pragma unroll
-    for (int q = 0; q < NBW; ++q) {
-      const int blk = wave + 4 * q;
-      accs[q] = f32x16{};
-      if (blk >= NBLK) continue;
-      const int rb = blk / NCB, cb = blk % NCB;
-      const int c = cb * 32 + li;
-      f32x16 acc = f32x16{};
-      const float* ap = At + (rb * 32 + li) * SA + 4 * h;
-      for (int k0 = 0; k0 < K; k0 += 8) {
-        float b0, b1, b2, b3;
-        if constexpr (TR) {
-          const f32x4 bv = *reinterpret_cast<const f32x4*>(Ws + c * SWT + k0 + 4 * h);
-          b0 = bv.x; b1 = bv.y; b2 = bv.z; b3 = bv.w;
-        } else {
-          const float* wp = Ws + (k0 + 4 * h) * SWP + c;
-          b0 = wp[0]; b1 = wp[SWP]; b2 = wp[2 * SWP]; b3 = wp[3 * SWP];
-        }
-        const f32x4 av = *reinterpret_cast<const f32x4*>(ap + k0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.x, b0, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.y, b1, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.z, b2, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.w, b3, acc, 0, 0, 0);
-      }
-      const float bias = (MODE == GEMM_BIAS || MODE == GEMM_SSP_RESID || MODE == GEMM_READOUT)
-                             ? g.bias[c] : 0.f;
-      const float w2 = (MODE == GEMM_READOUT) ? g.w2[c] : 0.f;
+    f32x16 v1 = f32x16{};
+    const int c1 = wave * 32 + li;
+    if (wave < N1 / 32) {
+      const f32x16 acc = mma_lds_glb<D>(Ap, g.W1, N1, c1, h);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = rb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        const int m = m0 + row;
-        float y = acc[r];
-        if constexpr (MODE == GEMM_READOUT) {
-          const float z = y + bias;
-          y = sigmoid_f(z) * w2;                 // d eps / d o
-          accs[q][r] = ssp_f(z) * w2;            // this feature's share of eps
+        const int m = m0 + blk_row(r, h);
+        const bool ok = m < g.M;
+        const size_t o = (size_t)m * N1 + c1;
+        if constexpr (MODE == ATOM_UPDATE_FWD) {
+          const float a = acc[r] + g.b1[c1];
+          if (ok) g.Aout[o] = a;
+          v1[r] = ssp_f(a);
+        } else if constexpr (MODE == ATOM_UPDATE_BWD) {
+          v1[r] = ok ? acc[r] * sigmoid_f(g.S[o]) : 0.f;
+        } else {
+          const float z = acc[r] + g.b1[c1];
+          const float w2 = g.w2[c1];
+          Sh[blk_row(r, h) * (N1 + 1) + c1] = ssp_f(z) * w2;
+          v1[r] = sigmoid_f(z) * w2;
         }
-        if (m >= g.M) continue;
-        const size_t o = (size_t)m * N + c;
-        if constexpr (MODE == GEMM_BIAS) y += bias;
-        if constexpr (MODE == GEMM_SSP_RESID) y += bias + g.R[o];
-        if constexpr (MODE == GEMM_T_SIGMOID) y *= sigmoid_f(g.S[o]);
-        g.Y[o] = y;
       }
     }
-    if constexpr (MODE == GEMM_READOUT) {
-      // stage the shares after every wave finished reading the A tile
-      __syncthreads();
+    __syncthreads();
+    if (wave < N1 / 32) {
 #pragma unroll
-      for (int q = 0; q < NBW; ++q) {
-        const int blk = wave + 4 * q;
-        if (blk >= NBLK) continue;
-        const int rb = blk / NCB, c = (blk % NCB) * 32 + li;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) At[(rb * 32 + 8 * (r >> 2) + 4 * h + (r & 3)) * SA + c] = accs[q][r];
-      }
+      for (int r = 0; r < 16; ++r) At[blk_row(r, h) * SA + c1] = v1[r];
     }
-    if constexpr (MODE == GEMM_READOUT) {
-      __syncthreads();
-      const int r = tid >> 2, part = tid & 3;
+    __syncthreads();
+    if constexpr (MODE == ATOM_READOUT) {
+      const int r = tid >> 3, part = tid & 7;
       float s = 0.f;
-      for (int k = part * (N / 4); k < (part + 1) * (N / 4); ++k) s += At[r * SA + k];
+      for (int k = part * (N1 / 8); k < (part + 1) * (N1 / 8); ++k) s += Sh[r * (N1 + 1) + k];
       s += __shfl_xor(s, 1, 64);
       s += __shfl_xor(s, 2, 64);
-      if (part == 0 && m0 + r < g.M) g.eps[m0 + r] = s + g.b2;
+      s += __shfl_xor(s, 4, 64);
+      if (part == 0 && m0 + r < g.M) g.eps[m0 + r] = s + g.b2s;
+    }
+    if (wave < D / 32) {
+      const int c2 = wave * 32 + li;
+      const f32x16 acc = mma_lds_glb<N1>(Ap, g.W2, D, c2, h);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + blk_row(r, h);
+        if (m >= g.M) continue;
+        const size_t o = (size_t)m * D + c2;
+        if constexpr (MODE == ATOM_UPDATE_FWD) g.Y[o] = g.R[o] + acc[r] + g.b2[c2];
+        else g.Y[o] = acc[r];
+      }
     }
     __syncthreads();
   }
 }
 
-template <int K, int N>
-static void gemm_dispatch_mode(const GemmArgs& g, dim3 grid, size_t lds, hipStream_t s) {
-  switch (g.mode) {
-    case GEMM_BIAS: hipLaunchKernelGGL((k_gemm<K, N, GEMM_BIAS>), grid, dim3(kThreads), lds, s, g); break;
-    case GEMM_SSP_RESID: hipLaunchKernelGGL((k_gemm<K, N, GEMM_SSP_RESID>), grid, dim3(kThreads), lds, s, g); break;
-    case GEMM_T_SIGMOID: hipLaunchKernelGGL((k_gemm<K, N, GEMM_T_SIGMOID>), grid, dim3(kThreads), lds, s, g); break;
-    case GEMM_T: hipLaunchKernelGGL((k_gemm<K, N, GEMM_T>), grid, dim3(kThreads), lds, s, g); break;
-    case GEMM_READOUT: hipLaunchKernelGGL((k_gemm<K, N, GEMM_READOUT>), grid, dim3(kThreads), lds, s, g); break;
+hipError_t launch_atom(const AtomArgs& g, int D, int N1, int n_cu, hipStream_t s) {
+  const int tiles = (g.M + kRows - 1) / kRows;
+  const int cap = 8 * n_cu;
+  const dim3 grid(tiles < cap ? (tiles > 0 ? tiles : 1) : cap);
+#define SN_ATOM(DD, NN, MM)                                                             \
+  if (D == DD && N1 == NN && g.mode == MM) {                                            \
+    hipLaunchKernelGGL((k_atom<DD, NN, MM>), grid, dim3(kThreads), 0, s, g);            \
+    return hipGetLastError();                                                           \
   }
-}
-
-template <int K, int N>
-static hipError_t gemm_raise_limit() {
-  const void* fns[] = {
-      reinterpret_cast<const void*>(&k_gemm<K, N, GEMM_BIAS>),
-      reinterpret_cast<const void*>(&k_gemm<K, N, GEMM_SSP_RESID>),
-      reinterpret_cast<const void*>(&k_gemm<K, N, GEMM_T_SIGMOID>),
-      reinterpret_cast<const void*>(&k_gemm<K, N, GEMM_T>),
-      reinterpret_cast<const void*>(&k_gemm<K, N, GEMM_READOUT>)};
-  for (const void* f : fns) {
-    hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
-}
-
-hipError_t gemm_prepare() {
-  hipError_t e;
-#define SN_RAISE(K, N) if ((e = gemm_raise_limit<K, N>()) != hipSuccess) return e;
-  SN_RAISE(64, 64) SN_RAISE(128, 128) SN_RAISE(64, 32) SN_RAISE(128, 64) SN_RAISE(32, 64)
-  SN_RAISE(64, 128) SN_RAISE(128, 32) SN_RAISE(32, 128)
-#undef SN_RAISE
-  return hipSuccess;
-}
-
-hipError_t launch_gemm(const GemmArgs& g, int n_cu, hipStream_t s) {
-  const int tiles = (g.M + kTileAtoms - 1) / kTileAtoms;
-  const int grid = tiles < n_cu ? (tiles > 0 ? tiles : 1) : n_cu;
-  const size_t lds = gemm_lds_bytes(g.K, g.N);
-  const dim3 gd(grid);
-#define SN_CASE(KK, NN) if (g.K == KK && g.N == NN) { gemm_dispatch_mode<KK, NN>(g, gd, lds, s); return hipGetLastError(); }
-  SN_CASE(64, 64) SN_CASE(128, 128) SN_CASE(64, 32) SN_CASE(128, 64) SN_CASE(32, 64)
-  SN_CASE(64, 128) SN_CASE(128, 32) SN_CASE(32, 128)
-#undef SN_CASE
+  SN_ATOM(64, 64, ATOM_UPDATE_FWD) SN_ATOM(64, 64, ATOM_UPDATE_BWD)
+  SN_ATOM(128, 128, ATOM_UPDATE_FWD) SN_ATOM(128, 128, ATOM_UPDATE_BWD)
+  SN_ATOM(64, 32, ATOM_READOUT) SN_ATOM(64, 64, ATOM_READOUT)
+  SN_ATOM(128, 32, ATOM_READOUT) SN_ATOM(128, 64, ATOM_READOUT)
+#undef SN_ATOM
   return hipErrorInvalidValue;
 }
 

@@ -17,6 +17,7 @@ struct sn_model {
   size_t n_w = 0;
   float* w = nullptr;          // device copy of the flat fp32 weights
   uint16_t* wbf = nullptr;     // bf16 filter copies, per block: W1t[D][KP], W2t[D][D], W2n[D][D]
+  float* wt = nullptr;         // transposed copies: per block Wu2^T, Wu1^T [D][D]; then Wo1^T [H][D]
   float co2 = 0.f;             // readout output bias (host copy)
   size_t off_emb = 0, off_o1 = 0, off_co1 = 0, off_o2 = 0;
   std::vector<size_t> off_blk; // start of each interaction block
@@ -44,7 +45,8 @@ size_t block_floats(const sn_model_desc* d) {
 bool sys_ok(const sn_system* s) {
   if (!s) return false;
   if (s->n_replicas < 1 || s->atoms_per_replica < 1) return false;
-  if ((int64_t)s->n_replicas * s->atoms_per_replica > (int64_t)1 << 30) return false;
+  // the kernels address per-atom feature rows with 32-bit byte offsets (N * 128 * 4 < 2^31)
+  if ((int64_t)s->n_replicas * s->atoms_per_replica > ((int64_t)1 << 22)) return false;
   if (s->periodic && !(std::isfinite(s->box) && s->box > 0.f)) return false;
   return true;
 }
@@ -135,13 +137,14 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
   p.col = col;
   p.pos = pos;
   p.wg_start = wg_start;
+  p.n_atoms = (int)n;
   p.periodic = sys->periodic;
   p.box = sys->box;
   p.half_box = 0.5f * sys->box;
   const float step = (d.rbf_max - d.rbf_min) / (float)(d.Dr - 1);
   p.rbf_min = d.rbf_min;
   p.rbf_step = step;
-  p.rbf_coef = -0.5f / (step * step);
+  p.rbf_coef2 = (float)(-0.5 / ((double)step * step) * 1.4426950408889634);
   p.rbf_inv_s2 = 1.f / (step * step);
   p.r_cut = d.r_cut;
   p.pi_over_rc = (float)(M_PI / (double)d.r_cut);
@@ -173,6 +176,10 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
     }
   };
 
+  const size_t DD = (size_t)D * D;
+  auto WuT = [&](int t, int k) { return m->wt + (size_t)t * 2 * DD + (size_t)k * DD; };  // 0: Wu2^T, 1: Wu1^T
+  const float* Wo1T = m->wt + (size_t)T * 2 * DD;
+
   // forward
   for (int t = 0; t < T; ++t) {
     set_block(t);
@@ -182,20 +189,14 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
       ProfScope ps(0, s);
       if ((e = launch_cf_forward(D, bf16, p, G, s)) != hipSuccess) return hip_fail(e);
     }
-    GemmArgs g1{GEMM_BIAS, (int)n, D, D, gbuf, Wu(t, 0), Wu(t, 1), nullptr, nullptr, au + t * ND,
-                nullptr, 0.f, nullptr};
-    if ((e = launch_gemm(g1, m->n_cu, s)) != hipSuccess) return hip_fail(e);
-    GemmArgs g2{GEMM_SSP_RESID, (int)n, D, D, au + t * ND, Wu(t, 2), Wu(t, 3), x + t * ND, nullptr,
-                x + (t + 1) * ND, nullptr, 0.f, nullptr};
-    if ((e = launch_gemm(g2, m->n_cu, s)) != hipSuccess) return hip_fail(e);
+    AtomArgs u{ATOM_UPDATE_FWD, (int)n, gbuf, Wu(t, 0), Wu(t, 1), Wu(t, 2), Wu(t, 3), x + t * ND,
+               nullptr, au + t * ND, x + (t + 1) * ND, nullptr, 0.f, nullptr};
+    if ((e = launch_atom(u, D, D, m->n_cu, s)) != hipSuccess) return hip_fail(e);
   }
   // readout and its gradient
-  GemmArgs gr{GEMM_READOUT, (int)n, D, H, x + T * ND, m->w + m->off_o1, m->w + m->off_co1, nullptr,
-              nullptr, tmp, m->w + m->off_o2, m->co2, eps};
-  if ((e = launch_gemm(gr, m->n_cu, s)) != hipSuccess) return hip_fail(e);
-  GemmArgs grb{GEMM_T, (int)n, H, D, tmp, m->w + m->off_o1, nullptr, nullptr, nullptr, gx,
-               nullptr, 0.f, nullptr};
-  if ((e = launch_gemm(grb, m->n_cu, s)) != hipSuccess) return hip_fail(e);
+  AtomArgs r{ATOM_READOUT, (int)n, x + T * ND, m->w + m->off_o1, m->w + m->off_co1, Wo1T, nullptr,
+             nullptr, nullptr, nullptr, gx, m->w + m->off_o2, m->co2, eps};
+  if ((e = launch_atom(r, D, H, m->n_cu, s)) != hipSuccess) return hip_fail(e);
   if ((e = launch_energy(eps, sys->n_replicas, sys->atoms_per_replica, energy, st, s)) !=
       hipSuccess)
     return hip_fail(e);
@@ -203,12 +204,9 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
   int cur = 0;
   for (int t = T - 1; t >= 0; --t) {
     float* gx_cur = gx + cur * ND;
-    GemmArgs b1{GEMM_T_SIGMOID, (int)n, D, D, gx_cur, Wu(t, 2), nullptr, nullptr, au + t * ND, tmp,
-                nullptr, 0.f, nullptr};
-    if ((e = launch_gemm(b1, m->n_cu, s)) != hipSuccess) return hip_fail(e);
-    GemmArgs b2{GEMM_T, (int)n, D, D, tmp, Wu(t, 0), nullptr, nullptr, nullptr, gbuf, nullptr, 0.f,
-                nullptr};
-    if ((e = launch_gemm(b2, m->n_cu, s)) != hipSuccess) return hip_fail(e);
+    AtomArgs b{ATOM_UPDATE_BWD, (int)n, gx_cur, WuT(t, 0), nullptr, WuT(t, 1), nullptr, nullptr,
+               au + t * ND, nullptr, gbuf, nullptr, 0.f, nullptr};
+    if ((e = launch_atom(b, D, D, m->n_cu, s)) != hipSuccess) return hip_fail(e);
     set_block(t);
     p.x = x + t * ND;
     p.gh = gbuf;
@@ -372,8 +370,7 @@ sn_status sn_model_create(const sn_model_desc* d, const float* weights_host, siz
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&m->n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e == hipSuccess) e = cf_prepare(d->D, d->filter_dtype == SN_FILTER_BF16);
-  if (e == hipSuccess) e = gemm_prepare();
+  if (e == hipSuccess) e = cf_prepare(d->D, m->KP, d->filter_dtype == SN_FILTER_BF16);
   if (e == hipSuccess) e = hipMalloc(&m->w, nw * sizeof(float));
   if (e == hipSuccess) e = hipMemcpy(m->w, weights_host, nw * sizeof(float), hipMemcpyHostToDevice);
   if (e == hipSuccess && d->filter_dtype == SN_FILTER_BF16) {
@@ -397,6 +394,29 @@ sn_status sn_model_create(const sn_model_desc* d, const float* weights_host, siz
     if (e == hipSuccess)
       e = hipMemcpy(m->wbf, hb.data(), hb.size() * sizeof(uint16_t), hipMemcpyHostToDevice);
   }
+  if (e == hipSuccess) {
+    // transposed copies for the backward products: Wu2^T and Wu1^T per block, Wo1^T
+    const size_t DD = D * D;
+    std::vector<float> ht(2 * DD * d->T + H * D);
+    for (int t = 0; t < d->T; ++t) {
+      const float* Wu1 = weights_host + m->off_blk[t] + (size_t)d->Dr * D + D + DD + D;
+      const float* Wu2 = Wu1 + DD + D;
+      float* o2 = ht.data() + 2 * DD * t;
+      float* o1 = o2 + DD;
+      for (size_t k = 0; k < D; ++k)
+        for (size_t c = 0; c < D; ++c) {
+          o2[c * D + k] = Wu2[k * D + c];
+          o1[c * D + k] = Wu1[k * D + c];
+        }
+    }
+    const float* Wo1 = weights_host + m->off_o1;
+    float* ot = ht.data() + 2 * DD * d->T;
+    for (size_t k = 0; k < D; ++k)
+      for (size_t c = 0; c < H; ++c) ot[c * D + k] = Wo1[k * H + c];
+    e = hipMalloc(&m->wt, ht.size() * sizeof(float));
+    if (e == hipSuccess)
+      e = hipMemcpy(m->wt, ht.data(), ht.size() * sizeof(float), hipMemcpyHostToDevice);
+  }
   if (e != hipSuccess) {
     sn_model_destroy(m);
     return SN_ERR_HIP;
@@ -409,6 +429,7 @@ void sn_model_destroy(sn_model* m) {
   if (!m) return;
   if (m->w) (void)hipFree(m->w);
   if (m->wbf) (void)hipFree(m->wbf);
+  if (m->wt) (void)hipFree(m->wt);
   delete m;
 }
 

@@ -68,9 +68,10 @@ struct CfParams {
   const int32_t* col;
   const float* pos;
   const int32_t* wg_start;
+  int n_atoms;
   int periodic;
   float box, half_box;
-  float rbf_min, rbf_step, rbf_coef, rbf_inv_s2; // coef = -1/(2 sigma^2), inv_s2 = 1/sigma^2
+  float rbf_min, rbf_step, rbf_coef2, rbf_inv_s2; // coef2 = -log2(e)/(2 sigma^2), inv_s2 = 1/sigma^2
   float r_cut, pi_over_rc;
   int Dr, KP;
   // fp32 filter weights (row-major [fan_in][fan_out])
@@ -94,35 +95,30 @@ struct CfParams {
 
 int cf_kp(int Dr, int bf16);               // padded basis length used by the kernels
 size_t cf_lds_bytes(int D, int KP, int bf16, int backward);
-hipError_t cf_prepare(int D, int bf16);    // raises the dynamic LDS limit of the kernels
+hipError_t cf_prepare(int D, int KP, int bf16);  // raises the dynamic LDS limit of the kernels
 hipError_t launch_partition(const int32_t* rowptr, int n_atoms, int G, int32_t* wg_start,
                             hipStream_t s);
 hipError_t launch_cf_forward(int D, int bf16, const CfParams& p, int G, hipStream_t s);
 hipError_t launch_cf_backward(int D, int bf16, const CfParams& p, int G, hipStream_t s);
 
-enum GemmMode {
-  GEMM_BIAS = 0,        // Y = A W + b
-  GEMM_SSP_RESID = 1,   // Y = R + ssp(A) W + b
-  GEMM_T_SIGMOID = 2,   // Y = (A W^T) * sigmoid(S)
-  GEMM_T = 3,           // Y = A W^T
-  GEMM_READOUT = 4,     // o = A W + b;  eps = ssp(o).w2 + b2;  Y = sigmoid(o) * w2
-};
-struct GemmArgs {
+enum AtomMode { ATOM_UPDATE_FWD = 0, ATOM_UPDATE_BWD = 1, ATOM_READOUT = 2 };
+struct AtomArgs {
   int mode;
-  int M, K, N;          // A [M][K]; output [M][N]
-  const float* A;
-  const float* W;       // [K][N] (plain modes) or [N][K] (transposed modes)
-  const float* bias;    // [N]
-  const float* R;       // residual [M][N]
-  const float* S;       // pre-activation [M][N] for the sigmoid gate
-  float* Y;
-  const float* w2;      // readout second layer [N]
-  float b2;
-  float* eps;           // readout per-atom energy [M]
+  int M;              // atoms
+  const float* A;     // [M][D]: h (update fwd), dE/dx' (update bwd), x^(T) (readout)
+  const float* W1;    // first product, row-major [D][N1]
+  const float* b1;    // [N1] (update fwd, readout)
+  const float* W2;    // second product, row-major [N1][D]
+  const float* b2;    // [D] (update fwd)
+  const float* R;     // residual x [M][D] (update fwd)
+  const float* S;     // pre-activation a [M][D] (update bwd)
+  float* Aout;        // pre-activation a [M][D] (update fwd)
+  float* Y;           // [M][D]: x', dE/dh, or dE/dx^(T)
+  const float* w2;    // readout output weights [N1]
+  float b2s;          // readout output bias
+  float* eps;         // per-atom energies [M] (readout)
 };
-size_t gemm_lds_bytes(int K, int N);
-hipError_t gemm_prepare();
-hipError_t launch_gemm(const GemmArgs& g, int n_cu, hipStream_t s);
+hipError_t launch_atom(const AtomArgs& g, int D, int N1, int n_cu, hipStream_t s);
 hipError_t launch_embed(const int32_t* types, const float* emb, int n_atoms, int D, int n_types,
                         float* x, DevStatus* st, hipStream_t s);
 hipError_t launch_energy(const float* eps, int n_rep, int n_per, float* energy, DevStatus* st,
