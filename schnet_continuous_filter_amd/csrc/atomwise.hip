@@ -39,7 +39,7 @@ template <int K>
 __device__ __forceinline__ f32x16 mma_lds_glb(const float* Ap, const float* __restrict__ W,
                                               int ldw, int c, int h) {
   f32x16 acc = f32x16{};
-#pragma unroll 4
+#pragma unroll
   for (int k0 = 0; k0 < K; k0 += 8) {
     const float* wp = W + (size_t)(k0 + 4 * h) * ldw + c;
     const float b0 = wp[0], b1 = wp[ldw], b2 = wp[2 * ldw], b3 = wp[3 * ldw];

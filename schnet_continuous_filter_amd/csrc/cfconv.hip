@@ -41,6 +41,8 @@
 // reads its A operand with one 16-byte LDS load (k = k0 + 4h + s for fp32,
 // k = k0 + 8h + s for bf16, h = lane / 32); A and B use the same permutation.
 // Gathers use buffer loads with 32-bit byte offsets.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace sn {
@@ -224,36 +226,85 @@ __device__ __forceinline__ void stage_weights(const CfParams& p, unsigned char* 
   }
 }
 
-// rowptr access through the LDS slice when the index falls inside it.
+// rowptr access: FULL when the work-group's whole slice sits in LDS (the
+// common case; no global loads, so the compiler need not drain in-flight
+// prefetches), else through the slice when the index falls inside it.
+template <bool FULL>
 struct RowPtr {
   const int32_t* g;
   const int32_t* s;
   int base, len;
   __device__ __forceinline__ int operator()(int i) const {
     const int k = i - base;
+    if constexpr (FULL) return s[k];
     return k < len ? s[k] : g[i];
   }
 };
 
-// Geometry of the tile's edges (threads 0..TM-1): receiver, sender, u = r_i - r_j,
-// d, envelope and its derivative, and the inside-cutoff flag.
+// Geometry loads run one tile ahead of the arithmetic: while tile k computes,
+// the positions of tile k+1 and the sender indices of tile k+2 are in flight
+// (threads 0..TM-1, one edge each).
+struct GeoPrefetch {
+  int i, j, jn;                 // receiver and sender of the next tile's edge; sender a tile later
+  float xi, yi, zi, xj, yj, zj; // their positions
+};
+
+__device__ __forceinline__ void pf_positions(GeoPrefetch& f, __amdgpu_buffer_rsrc_t rpos) {
+  const uint32_t oi = (uint32_t)f.i * 12u, oj = (uint32_t)f.j * 12u;
+  f.xi = bload(rpos, oi);
+  f.yi = bload(rpos, oi + 4);
+  f.zi = bload(rpos, oi + 8);
+  f.xj = bload(rpos, oj);
+  f.yj = bload(rpos, oj + 4);
+  f.zj = bload(rpos, oj + 8);
+}
+
+template <int TM, class RPT>
+__device__ __forceinline__ void pf_start(GeoPrefetch& f, const RPT& RP, int ia, int ts, int e_end,
+                                         __amdgpu_buffer_rsrc_t rcol, __amdgpu_buffer_rsrc_t rpos) {
+  const int e = ts + (int)threadIdx.x, e2 = e + TM;
+  // reads past the last edge return 0 (the buffer descriptor bounds them)
+  f.j = bload_i(rcol, (uint32_t)e * 4u);
+  f.jn = bload_i(rcol, (uint32_t)e2 * 4u);
+  int i = ia;
+  if (e < e_end)
+    while (RP(i + 1) <= e) ++i;
+  f.i = i;
+  pf_positions(f, rpos);
+}
+
+// Move the prefetch on to the tile starting at ts (the previous tile's values
+// have been consumed).
+template <int TM, class RPT>
+__device__ __forceinline__ void pf_advance(GeoPrefetch& f, const RPT& RP, int ts, int e_end,
+                                           __amdgpu_buffer_rsrc_t rcol,
+                                           __amdgpu_buffer_rsrc_t rpos) {
+  const int e = ts + (int)threadIdx.x, e2 = e + TM;
+  int i = f.i;
+  if (e < e_end)
+    while (RP(i + 1) <= e) ++i;
+  f.i = i;
+  f.j = f.jn;
+  f.jn = bload_i(rcol, (uint32_t)e2 * 4u);
+  pf_positions(f, rpos);
+}
+
+// Geometry of the tile's edges from the prefetched values (threads 0..TM-1):
+// receiver, sender, u = r_i - r_j, d, envelope and its derivative, and the
+// inside-cutoff flag. Rows past the tile end get receiver `cur`, sender 0.
 template <int TM, bool BWD>
-__device__ __forceinline__ void tile_geometry(const CfParams& p, const RowPtr& RP, float* geo,
-                                              int ts, int te, int cur,
-                                              __amdgpu_buffer_rsrc_t rcol,
-                                              __amdgpu_buffer_rsrc_t rpos) {
+__device__ __forceinline__ void tile_geometry(const CfParams& p, const GeoPrefetch& f, float* geo,
+                                              int ts, int te, int cur) {
   const int r = threadIdx.x;
-  if (r >= TM) return;
   const int e = ts + r;
   float d = 0.f, C = 0.f, Cp = 0.f, ux = 0.f, uy = 0.f, uz = 0.f, invd = 0.f;
   int j = 0, i = cur, inside = 0;
   if (e < te) {
-    while (RP(i + 1) <= e) ++i;
-    j = bload_i(rcol, (uint32_t)e * 4u);
-    const uint32_t oi = (uint32_t)i * 12u, oj = (uint32_t)j * 12u;
-    ux = bload(rpos, oi) - bload(rpos, oj);
-    uy = bload(rpos, oi + 4) - bload(rpos, oj + 4);
-    uz = bload(rpos, oi + 8) - bload(rpos, oj + 8);
+    i = f.i;
+    j = f.j;
+    ux = f.xi - f.xj;
+    uy = f.yi - f.yj;
+    uz = f.zi - f.zj;
     if (p.periodic) {
       ux = min_image(ux, p.box, p.half_box);
       uy = min_image(uy, p.box, p.half_box);
@@ -290,8 +341,8 @@ struct TileSegs {
   int first, last, nseg;
   bool last_open;
 };
-template <int TM>
-__device__ __forceinline__ TileSegs tile_segs(const RowPtr& RP, const int* geoi, int ts, int te,
+template <int TM, class RPT>
+__device__ __forceinline__ TileSegs tile_segs(const RPT& RP, const int* geoi, int ts, int te,
                                               int cur) {
   TileSegs t;
   t.first = cur;
@@ -305,8 +356,8 @@ __device__ __forceinline__ TileSegs tile_segs(const RowPtr& RP, const int* geoi,
 // receiver of the tile gets one thread per column; the first receiver adds the
 // carried partial sum, the last one either stores its partial (still open) or
 // clears the carry. flush(i, c, value) writes a completed receiver.
-template <int D, int SQ, class Flush>
-__device__ __forceinline__ void seg_sum_cols(const RowPtr& RP, const TileSegs& t, int ts, int te,
+template <int D, int SQ, class RPT, class Flush>
+__device__ __forceinline__ void seg_sum_cols(const RPT& RP, const TileSegs& t, int ts, int te,
                                              const float* buf, const float* carry_in,
                                              float* carry_out, Flush flush) {
   constexpr int NG = kCfThreads / D;
@@ -346,7 +397,7 @@ __global__ __launch_bounds__(kCfThreads, 1) void k_cf_fwd(CfParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, li = lane & 31;
   const int cb = wave % NCB, r0 = 32 * (wave / NCB), c = cb * 32 + li;
   const uint32_t N = (uint32_t)p.n_atoms;
-  const __amdgpu_buffer_rsrc_t rcol = rsrc(p.col, 0x7fffffffu);
+  const __amdgpu_buffer_rsrc_t rcol = rsrc(p.col, (uint32_t)p.rowptr[p.n_atoms] * 4u);
   const __amdgpu_buffer_rsrc_t rpos = rsrc(p.pos, N * 12u);
   const __amdgpu_buffer_rsrc_t rx = rsrc(p.x, N * (uint32_t)D * 4u);
 
@@ -356,15 +407,26 @@ __global__ __launch_bounds__(kCfThreads, 1) void k_cf_fwd(CfParams p) {
   const int rpl = min(ib - ia + 1, kRpMax);
   for (int k = tid; k < rpl; k += kCfThreads) rps[k] = p.rowptr[ia + k];
   for (int k = tid; k < 2 * D; k += kCfThreads) carry[k] = 0.f;
-  const RowPtr RP{p.rowptr, rps, ia, rpl};
   __syncthreads();
+  auto tiles = [&](auto full) {
+  const RowPtr<decltype(full)::value> RP{p.rowptr, rps, ia, rpl};
   const int e_begin = RP(ia), e_end = RP(ib);
   int cur = ia, par = 0;
+  GeoPrefetch pf{};
+  if (tid < TM) pf_start<TM>(pf, RP, ia, e_begin, e_end, rcol, rpos);
 
   for (int ts = e_begin; ts < e_end; ts += TM) {
     const int te = min(ts + TM, e_end);
-    tile_geometry<TM, false>(p, RP, geo, ts, te, cur, rcol, rpos);
+    if (tid < TM) {
+      tile_geometry<TM, false>(p, pf, geo, ts, te, cur);
+      pf_advance<TM>(pf, RP, ts + TM, e_end, rcol, rpos);
+    }
     __syncthreads();
+    // sender features, needed after the filter: issue the gathers now
+    float xg[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      xg[r] = bload(rx, ((uint32_t)geoi[G_J * TM + out_row(r0, r, h)] * D + c) * 4u);
     // basis b~ = exp(-(d - mu_k)^2 / (2 sigma^2)) C(d), zero for padding and masked edges
     for (int idx = tid; idx < TM * KP; idx += kCfThreads) {
       const int r = idx / KP, k = idx - r * KP;
@@ -403,13 +465,13 @@ __global__ __launch_bounds__(kCfThreads, 1) void k_cf_fwd(CfParams p) {
       const float* Ap[1] = {abuf + (r0 + li) * SQ + 4 * h};
       mma_f32<1, false, D>(acc, Ap, reinterpret_cast<const float*>(lds + L.w2), SW, cb * 32, lane);
     }
-    // m = x_src * w, gathered in the MFMA output layout
+    // m = x_src * w in the MFMA output layout
     float m[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = out_row(r0, r, h);
-      const float xj = bload(rx, ((uint32_t)geoi[G_J * TM + row] * D + c) * 4u);
-      m[r] = geoi[G_IN * TM + row] ? (acc[0][r] + bias2) * xj : 0.f;
+      const float mk = geoi[G_IN * TM + row] ? 1.f : 0.f;
+      m[r] = mk * ((acc[0][r] + bias2) * xg[r]);
     }
     __syncthreads();
 #pragma unroll
@@ -424,6 +486,9 @@ __global__ __launch_bounds__(kCfThreads, 1) void k_cf_fwd(CfParams p) {
   }
   for (int idx = tid; idx < (ib - cur) * D; idx += kCfThreads)
     p.h[(size_t)cur * D + idx] = 0.f;
+  };
+  if (rpl == ib - ia + 1) tiles(std::true_type{});
+  else tiles(std::false_type{});
 }
 
 // ------------------------------------------------------------------ backward
@@ -445,7 +510,7 @@ __global__ __launch_bounds__(kCfThreads, 1) void k_cf_bwd(CfParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, li = lane & 31;
   const int cb = wave % NCB, r0 = 32 * (wave / NCB), c = cb * 32 + li;
   const uint32_t N = (uint32_t)p.n_atoms;
-  const __amdgpu_buffer_rsrc_t rcol = rsrc(p.col, 0x7fffffffu);
+  const __amdgpu_buffer_rsrc_t rcol = rsrc(p.col, (uint32_t)p.rowptr[p.n_atoms] * 4u);
   const __amdgpu_buffer_rsrc_t rpos = rsrc(p.pos, N * 12u);
   const __amdgpu_buffer_rsrc_t rx = rsrc(p.x, N * (uint32_t)D * 4u);
   const __amdgpu_buffer_rsrc_t rgh = rsrc(p.gh, N * (uint32_t)D * 4u);
@@ -456,16 +521,30 @@ __global__ __launch_bounds__(kCfThreads, 1) void k_cf_bwd(CfParams p) {
   const int rpl = min(ib - ia + 1, kRpMax);
   for (int k = tid; k < rpl; k += kCfThreads) rps[k] = p.rowptr[ia + k];
   for (int k = tid; k < 2 * D + 8; k += kCfThreads) qcarry[k] = 0.f;
-  const RowPtr RP{p.rowptr, rps, ia, rpl};
   const bool want_gx = p.gx_out != nullptr;
   __syncthreads();
+  auto tiles = [&](auto full) {
+  const RowPtr<decltype(full)::value> RP{p.rowptr, rps, ia, rpl};
   const int e_begin = RP(ia), e_end = RP(ib);
   int cur = ia, par = 0;
+  GeoPrefetch pf{};
+  if (tid < TM) pf_start<TM>(pf, RP, ia, e_begin, e_end, rcol, rpos);
 
   for (int ts = e_begin; ts < e_end; ts += TM) {
     const int te = min(ts + TM, e_end);
-    tile_geometry<TM, true>(p, RP, geo, ts, te, cur, rcol, rpos);
+    if (tid < TM) {
+      tile_geometry<TM, true>(p, pf, geo, ts, te, cur);
+      pf_advance<TM>(pf, RP, ts + TM, e_end, rcol, rpos);
+    }
     __syncthreads();
+    // sender rows, needed after the filter: issue the gathers now
+    float xg[16], gg[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const uint32_t oj = ((uint32_t)geoi[G_J * TM + out_row(r0, r, h)] * D + c) * 4u;
+      xg[r] = bload(rx, oj);
+      gg[r] = bload(rgh, oj);
+    }
     // b~ and d b~ / dd
     for (int idx = tid; idx < TM * KP; idx += kCfThreads) {
       const int r = idx / KP, k = idx - r * KP;
@@ -516,18 +595,21 @@ __global__ __launch_bounds__(kCfThreads, 1) void k_cf_bwd(CfParams p) {
       mma_f32<1, false, D>(accw, Ap, reinterpret_cast<const float*>(lds + L.w2), SW, cb * 32, lane);
     }
     // gathers; q = dE/dh_j * w (source sum), g_w = dE/dh_i * x_j + dE/dh_j * x_i (both directions)
-    float gw[16];
+    // receiver rows: all 32 loads are issued before any is used (masks are
+    // arithmetic, so no load sits behind a branch)
+    float gw[16], xr[16], gr[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row = out_row(r0, r, h);
-      const bool in = geoi[G_IN * TM + row] != 0;
-      const uint32_t oj = ((uint32_t)geoi[G_J * TM + row] * D + c) * 4u;
-      const uint32_t oi = ((uint32_t)geoi[G_I * TM + row] * D + c) * 4u;
-      const float xj = bload(rx, oj), ghj = bload(rgh, oj);
-      const float xi = bload(rx, oi), ghi = bload(rgh, oi);
-      const float w = in ? accw[0][r] + bias2 : 0.f;
-      accw[0][r] = ghj * w;
-      gw[r] = in ? ghi * xj + ghj * xi : 0.f;
+      const uint32_t oi = ((uint32_t)geoi[G_I * TM + out_row(r0, r, h)] * D + c) * 4u;
+      xr[r] = bload(rx, oi);
+      gr[r] = bload(rgh, oi);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float mk = geoi[G_IN * TM + out_row(r0, r, h)] ? 1.f : 0.f;
+      const float w = mk * (accw[0][r] + bias2);
+      accw[0][r] = gg[r] * w;
+      gw[r] = mk * (gr[r] * xg[r] + gg[r] * xr[r]);
     }
     __syncthreads();
     const TileSegs t = tile_segs<TM>(RP, geoi, ts, te, cur);
@@ -613,6 +695,9 @@ __global__ __launch_bounds__(kCfThreads, 1) void k_cf_bwd(CfParams p) {
   }
   if (!p.force_accumulate)
     for (int idx = tid; idx < (ib - cur) * 3; idx += kCfThreads) p.forces[(size_t)cur * 3 + idx] = 0.f;
+  };
+  if (rpl == ib - ia + 1) tiles(std::true_type{});
+  else tiles(std::false_type{});
 }
 
 // ------------------------------------------------------------------ partition

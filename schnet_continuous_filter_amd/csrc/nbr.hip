@@ -142,16 +142,18 @@ hipError_t launch_exclusive_scan(int32_t* a, int64_t n, int32_t* blocks_i32, Dev
 }
 
 // ------------------------------------------------------------------ all pairs per replica
+constexpr int kPairThreads = 64;   // one wave per block: many small blocks fill the chip
+
 template <bool FILL>
-__global__ __launch_bounds__(kThreads) void k_nbr_allpairs(const float* __restrict__ pos, int N,
+__global__ __launch_bounds__(kPairThreads) void k_nbr_allpairs(const float* __restrict__ pos, int N,
                                                            int periodic, double L, double half,
                                                            double r2, int32_t* rowptr,
                                                            int32_t* col, const DevStatus* st,
                                                            const int64_t* gate, int64_t gate_val) {
   SN_GATE
   if (FILL && st->overflow) return;
-  __shared__ float sx[kThreads], sy[kThreads], sz[kThreads];
-  const int il = blockIdx.x * kThreads + threadIdx.x;
+  __shared__ float sx[kPairThreads], sy[kPairThreads], sz[kPairThreads];
+  const int il = blockIdx.x * kPairThreads + threadIdx.x;
   const int64_t base = (int64_t)blockIdx.y * N;
   float xi = 0.f, yi = 0.f, zi = 0.f;
   if (il < N) {
@@ -162,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void k_nbr_allpairs(const float* __restri
   int cnt = 0;
   int64_t out = 0;
   if (FILL && il < N) out = rowptr[base + il];
-  for (int j0 = 0; j0 < N; j0 += kThreads) {
+  for (int j0 = 0; j0 < N; j0 += kPairThreads) {
     __syncthreads();
     const int jl = j0 + threadIdx.x;
     if (jl < N) {
@@ -171,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void k_nbr_allpairs(const float* __restri
       sz[threadIdx.x] = pos[3 * (base + jl) + 2];
     }
     __syncthreads();
-    const int jn = min(kThreads, N - j0);
+    const int jn = min(kPairThreads, N - j0);
     if (il < N) {
       for (int jj = 0; jj < jn; ++jj) {
         const int j = j0 + jj;
@@ -303,13 +305,13 @@ hipError_t launch_build_neighbors(const NbrGeom& g, const float* pos, int32_t* r
   const int64_t n_tot = (int64_t)g.n_rep * g.n_per;
   hipError_t e;
   if (g.cells_per_axis == 0) {
-    dim3 grid(blocks_for(g.n_per), (unsigned)g.n_rep);
-    hipLaunchKernelGGL(k_nbr_allpairs<false>, grid, dim3(kThreads), 0, s, pos, g.n_per, g.periodic,
+    dim3 grid((unsigned)((g.n_per + kPairThreads - 1) / kPairThreads), (unsigned)g.n_rep);
+    hipLaunchKernelGGL(k_nbr_allpairs<false>, grid, dim3(kPairThreads), 0, s, pos, g.n_per, g.periodic,
                        g.L, g.half, g.r2, rowptr, col, st, gate, gate_val);
     if ((e = launch_exclusive_scan(rowptr, n_tot, scan_blocks, st, edge_capacity, gate, gate_val,
                                    s)) != hipSuccess)
       return e;
-    hipLaunchKernelGGL(k_nbr_allpairs<true>, grid, dim3(kThreads), 0, s, pos, g.n_per, g.periodic,
+    hipLaunchKernelGGL(k_nbr_allpairs<true>, grid, dim3(kPairThreads), 0, s, pos, g.n_per, g.periodic,
                        g.L, g.half, g.r2, rowptr, col, st, gate, gate_val);
     return hipGetLastError();
   }
