@@ -69,7 +69,14 @@ __global__ __launch_bounds__(kThreads) void k_atom(AtomArgs g) {
     for (int idx = tid; idx < kRows * D / 4; idx += kThreads) {
       const int r = idx / (D / 4), k4 = idx - r * (D / 4);
       f32x4 v = f32x4{};
-      if (m0 + r < g.M) v = *reinterpret_cast<const f32x4*>(g.A + (size_t)(m0 + r) * D + 4 * k4);
+      if (m0 + r < g.M) {
+        const size_t o = (size_t)(m0 + r) * D + 4 * k4;
+        v = *reinterpret_cast<const f32x4*>(g.A + o);
+        if constexpr (MODE == ATOM_UPDATE_BWD) {
+          if (g.A2) v += *reinterpret_cast<const f32x4*>(g.A2 + o);
+          if (g.Asum) *reinterpret_cast<f32x4*>(g.Asum + o) = v;
+        }
+      }
       *reinterpret_cast<f32x4*>(At + r * SA + 4 * k4) = v;
     }
     __syncthreads();

@@ -16,7 +16,8 @@ struct sn_model {
   int n_cu = 0;
   size_t n_w = 0;
   float* w = nullptr;          // device copy of the flat fp32 weights
-  uint16_t* wbf = nullptr;     // bf16 filter copies, per block: W1t[D][KP], W2t[D][D], W2n[D][D]
+  unsigned char* cfimg = nullptr;  // per block: the CFConv weight image (cf_fill_image)
+  size_t img_bytes = 0;
   float* wt = nullptr;         // transposed copies: per block Wu2^T, Wu1^T [D][D]; then Wo1^T [H][D]
   float co2 = 0.f;             // readout output bias (host copy)
   size_t off_emb = 0, off_o1 = 0, off_co1 = 0, off_o2 = 0;
@@ -52,14 +53,6 @@ bool sys_ok(const sn_system* s) {
 }
 
 int64_t n_atoms(const sn_system* s) { return (int64_t)s->n_replicas * s->atoms_per_replica; }
-
-uint16_t bf16_bits(float f) {
-  uint32_t u;
-  std::memcpy(&u, &f, 4);
-  const uint32_t lsb = (u >> 16) & 1u;
-  u += 0x7FFFu + lsb;
-  return (uint16_t)(u >> 16);
-}
 
 sn_status hip_fail(hipError_t e) { return e == hipSuccess ? SN_OK : SN_ERR_HIP; }
 
@@ -101,10 +94,13 @@ struct ProfScope {
 };
 
 // ---------------------------------------------------------------- E+F orchestration
-int cf_grid(const sn_model* m, int64_t n) {
-  int64_t g = (n + 3) / 4;
+// Work-groups for the CFConv kernels: one per CU for large systems (their LDS
+// plan allows one resident group), fewer for small ones so that every worker
+// (wave) gets a few receivers.
+int cf_grid(const sn_model* m, int64_t n, int workers) {
+  int64_t g = (n + 4 * workers - 1) / (4 * workers);
   if (g > m->n_cu) g = m->n_cu;
-  if (g > kMaxGrid) g = kMaxGrid;
+  if (g * workers > kMaxGrid) g = kMaxGrid / workers;
   return (int)(g < 1 ? 1 : g);
 }
 
@@ -123,12 +119,15 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
   float* tmp = reinterpret_cast<float*>(ws + L.tmp);
   float* gx = reinterpret_cast<float*>(ws + L.gx);
   float* eps = reinterpret_cast<float*>(ws + L.eps);
+  float* fblk = reinterpret_cast<float*>(ws + L.fblk);
   const size_t ND = (size_t)n * D;
   const int bf16 = d.filter_dtype == SN_FILTER_BF16;
-  const int G = cf_grid(m, n);
+  const int workers = cf_workers(bf16);
+  const int G = cf_grid(m, n, workers);
   hipError_t e;
 
-  if ((e = launch_partition(rowptr, (int)n, G, wg_start, s)) != hipSuccess) return hip_fail(e);
+  if ((e = launch_partition(rowptr, (int)n, G * workers, wg_start, s)) != hipSuccess)
+    return hip_fail(e);
   if ((e = launch_embed(types, m->w + m->off_emb, (int)n, D, d.n_types, x, st, s)) != hipSuccess)
     return hip_fail(e);
 
@@ -148,23 +147,9 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
   p.rbf_inv_s2 = 1.f / (step * step);
   p.r_cut = d.r_cut;
   p.pi_over_rc = (float)(M_PI / (double)d.r_cut);
-  p.Dr = d.Dr;
-  p.KP = m->KP;
+  p.KC = cf_chunks(d.Dr, bf16);
 
-  auto set_block = [&](int t) {
-    const float* b = m->w + m->off_blk[t];
-    const size_t Dr = d.Dr, DD = (size_t)D * D;
-    p.Wf1 = b;
-    p.cf1 = b + Dr * D;
-    p.Wf2 = p.cf1 + D;
-    p.cf2 = p.Wf2 + DD;
-    if (bf16) {
-      const uint16_t* wb = m->wbf + (size_t)t * ((size_t)D * m->KP + 2 * DD);
-      p.W1t = wb;
-      p.W2t = wb + (size_t)D * m->KP;
-      p.W2n = p.W2t + DD;
-    }
-  };
+  auto block_img = [&](int t) -> const void* { return m->cfimg + (size_t)t * m->img_bytes; };
   auto Wu = [&](int t, int k) {  // k: 0 Wu1, 1 cu1, 2 Wu2, 3 cu2
     const float* b = m->w + m->off_blk[t] + (size_t)d.Dr * D + D + (size_t)D * D + D;
     const size_t DD = (size_t)D * D;
@@ -182,44 +167,44 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
 
   // forward
   for (int t = 0; t < T; ++t) {
-    set_block(t);
+    p.img = block_img(t);
     p.x = x + t * ND;
     p.h = gbuf;
     {
       ProfScope ps(0, s);
-      if ((e = launch_cf_forward(D, bf16, p, G, s)) != hipSuccess) return hip_fail(e);
+      if ((e = launch_cf_forward(D, m->KP, bf16, p, G, s)) != hipSuccess) return hip_fail(e);
     }
-    AtomArgs u{ATOM_UPDATE_FWD, (int)n, gbuf, Wu(t, 0), Wu(t, 1), Wu(t, 2), Wu(t, 3), x + t * ND,
-               nullptr, au + t * ND, x + (t + 1) * ND, nullptr, 0.f, nullptr};
+    AtomArgs u{ATOM_UPDATE_FWD, (int)n, gbuf, nullptr, nullptr, Wu(t, 0), Wu(t, 1), Wu(t, 2),
+               Wu(t, 3), x + t * ND, nullptr, au + t * ND, x + (t + 1) * ND, nullptr, 0.f, nullptr};
     if ((e = launch_atom(u, D, D, m->n_cu, s)) != hipSuccess) return hip_fail(e);
   }
   // readout and its gradient
-  AtomArgs r{ATOM_READOUT, (int)n, x + T * ND, m->w + m->off_o1, m->w + m->off_co1, Wo1T, nullptr,
-             nullptr, nullptr, nullptr, gx, m->w + m->off_o2, m->co2, eps};
+  AtomArgs r{ATOM_READOUT, (int)n, x + T * ND, nullptr, nullptr, m->w + m->off_o1,
+             m->w + m->off_co1, Wo1T, nullptr, nullptr, nullptr, nullptr, gx,
+             m->w + m->off_o2, m->co2, eps};
   if ((e = launch_atom(r, D, H, m->n_cu, s)) != hipSuccess) return hip_fail(e);
   if ((e = launch_energy(eps, sys->n_replicas, sys->atoms_per_replica, energy, st, s)) !=
       hipSuccess)
     return hip_fail(e);
-  // backward
-  int cur = 0;
+  // backward: gx holds dE/dx^(t+1) without the newest source sum q, which the
+  // update-backward kernel adds (and stores back while an older block needs it)
   for (int t = T - 1; t >= 0; --t) {
-    float* gx_cur = gx + cur * ND;
-    AtomArgs b{ATOM_UPDATE_BWD, (int)n, gx_cur, WuT(t, 0), nullptr, WuT(t, 1), nullptr, nullptr,
-               au + t * ND, nullptr, gbuf, nullptr, 0.f, nullptr};
+    const bool has_q = t < T - 1;
+    AtomArgs b{ATOM_UPDATE_BWD, (int)n, gx, has_q ? tmp : nullptr, (has_q && t > 0) ? gx : nullptr,
+               WuT(t, 0), nullptr, WuT(t, 1), nullptr, nullptr, au + t * ND, nullptr, gbuf,
+               nullptr, 0.f, nullptr};
     if ((e = launch_atom(b, D, D, m->n_cu, s)) != hipSuccess) return hip_fail(e);
-    set_block(t);
+    p.img = block_img(t);
     p.x = x + t * ND;
     p.gh = gbuf;
-    p.gx_in = gx_cur;
-    p.gx_out = t > 0 ? gx + (1 - cur) * ND : nullptr;
-    p.forces = forces;
-    p.force_accumulate = t != T - 1;
+    p.q_out = t > 0 ? tmp : nullptr;
+    p.forces = fblk + (size_t)t * n * 3;
     {
       ProfScope ps(1, s);
-      if ((e = launch_cf_backward(D, bf16, p, G, s)) != hipSuccess) return hip_fail(e);
+      if ((e = launch_cf_backward(D, m->KP, bf16, p, G, s)) != hipSuccess) return hip_fail(e);
     }
-    cur = 1 - cur;
   }
+  if ((e = launch_force_sum(fblk, T, n, forces, s)) != hipSuccess) return hip_fail(e);
   return SN_OK;
 }
 
@@ -306,7 +291,8 @@ WsLayout ws_layout(int64_t n, int D, int T, int H) {
   L.au = take((size_t)T * ND);
   L.gbuf = take(ND);
   L.tmp = take(ND);
-  L.gx = take(2 * ND);
+  L.gx = take(ND);
+  L.fblk = take((size_t)T * n * 3 * 4);          // per-block dE/dr
   L.eps = take((size_t)n * 4 + (size_t)n * 4);   // per-atom energies, then per-replica scratch
   L.total = off;
   return L;
@@ -373,26 +359,21 @@ sn_status sn_model_create(const sn_model_desc* d, const float* weights_host, siz
   if (e == hipSuccess) e = cf_prepare(d->D, m->KP, d->filter_dtype == SN_FILTER_BF16);
   if (e == hipSuccess) e = hipMalloc(&m->w, nw * sizeof(float));
   if (e == hipSuccess) e = hipMemcpy(m->w, weights_host, nw * sizeof(float), hipMemcpyHostToDevice);
-  if (e == hipSuccess && d->filter_dtype == SN_FILTER_BF16) {
-    const size_t KP = m->KP, DD = D * D, per = D * KP + 2 * DD;
-    std::vector<uint16_t> hb(per * d->T, 0);
+  if (e == hipSuccess) {
+    // CFConv weight images, laid out as the kernels hold them in LDS
+    const int bf16 = d->filter_dtype == SN_FILTER_BF16;
+    m->img_bytes = cf_image_bytes(d->D, m->KP, bf16);
+    const size_t per = m->img_bytes;
+    std::vector<unsigned char> hi(per * d->T);
     for (int t = 0; t < d->T; ++t) {
       const float* Wf1 = weights_host + m->off_blk[t];
-      const float* Wf2 = Wf1 + (size_t)d->Dr * D + D;
-      uint16_t* W1t = hb.data() + t * per;
-      uint16_t* W2t = W1t + D * KP;
-      uint16_t* W2n = W2t + DD;
-      for (size_t n = 0; n < D; ++n)
-        for (size_t k = 0; k < (size_t)d->Dr; ++k) W1t[n * KP + k] = bf16_bits(Wf1[k * D + n]);
-      for (size_t k = 0; k < D; ++k)
-        for (size_t n = 0; n < D; ++n) {
-          W2t[n * D + k] = bf16_bits(Wf2[k * D + n]);
-          W2n[k * D + n] = bf16_bits(Wf2[k * D + n]);
-        }
+      const float* cf1 = Wf1 + (size_t)d->Dr * D;
+      const float* Wf2 = cf1 + D;
+      const float* cf2 = Wf2 + D * D;
+      cf_fill_image(d->D, m->KP, bf16, d->Dr, Wf1, cf1, Wf2, cf2, hi.data() + t * per);
     }
-    e = hipMalloc(&m->wbf, hb.size() * sizeof(uint16_t));
-    if (e == hipSuccess)
-      e = hipMemcpy(m->wbf, hb.data(), hb.size() * sizeof(uint16_t), hipMemcpyHostToDevice);
+    e = (per == 0) ? hipErrorInvalidValue : hipMalloc(&m->cfimg, hi.size());
+    if (e == hipSuccess) e = hipMemcpy(m->cfimg, hi.data(), hi.size(), hipMemcpyHostToDevice);
   }
   if (e == hipSuccess) {
     // transposed copies for the backward products: Wu2^T and Wu1^T per block, Wo1^T
@@ -428,7 +409,7 @@ sn_status sn_model_create(const sn_model_desc* d, const float* weights_host, siz
 void sn_model_destroy(sn_model* m) {
   if (!m) return;
   if (m->w) (void)hipFree(m->w);
-  if (m->wbf) (void)hipFree(m->wbf);
+  if (m->cfimg) (void)hipFree(m->cfimg);
   if (m->wt) (void)hipFree(m->wt);
   delete m;
 }

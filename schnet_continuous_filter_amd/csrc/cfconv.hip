@@ -9,39 +9,50 @@
 // source features, and §3.2 "Forces via autodiff" the force as the negative
 // position gradient.
 //
-// Work decomposition (one work-group = 8 wave64, two per SIMD, so one wave's
-// elementwise work overlaps the other's matrix work):
-//  * a work-group owns a contiguous range of receivers, chosen so that all
-//    groups get about the same number of edges + receivers (k_partition); its
-//    slice of rowptr is staged in LDS;
-//  * it walks its edge range in tiles of TM edges (TM = 64 for D = 128,
-//    128 for D = 64, so a tile is always eight 32x32 output blocks, one per
-//    wave); tiles may straddle receivers;
-//  * per tile: geometry -> basis into LDS -> GEMM1 (basis x Wf1, MFMA) ->
-//    shifted softplus into LDS -> GEMM2 (x Wf2, MFMA) -> gather of the sender
-//    features in the MFMA output layout -> messages into LDS -> segmented sum:
-//    every receiver of the tile is summed by its own thread group in
-//    parallel; the receiver open at the tile's end leaves its partial sum in a
-//    double-buffered carry row for the next tile;
-//  * the filter weights stay in LDS for the whole launch; no edge-sized
-//    tensor ever reaches HBM.
+// Work decomposition. Every wave is an independent worker: a work-group of
+// eight waves (two per SIMD) copies the filter weights into LDS once, which is
+// its only barrier; then each wave walks its own contiguous range of receivers
+// (k_partition balances edges + receivers over the workers) in tiles of 32
+// edges.
 //
-// Backward (forces): the neighbour list is symmetric and w_ij = w_ji, so the
-// owner of receiver i can produce, from its own row alone,
-//   dE/dx_i   = dE/dx'_i + sum_j dE/dh_j * w_ij                (source sum)
-//   dE/dd_ij  = filter-backward of (dE/dh_i * x_j + dE/dh_j * x_i)
+// Edge-on-lane products. Every product is computed transposed,
+// OUT^T[n][e] = sum_k W^T[n][k] IN^T[k][e]: the weights (rows n) are the MFMA A
+// operand, read from LDS, and the per-edge activations are the B operand, one
+// edge per lane column. The accumulator layout of one product (rows = features
+// in registers, lane = edge) is then exactly the B-operand layout of the next,
+// so basis -> GEMM1 -> shifted softplus -> GEMM2 (-> GEMM3 in the backward)
+// never leaves registers; the k index inside each MFMA is permuted to match the
+// accumulator rows a lane holds, and the weight images in LDS are laid out
+// (XOR-swizzled, permuted for bf16) so that every A operand is one 16-byte
+// read. Each lane also computes its own edge's geometry and basis and gathers
+// its own sender/receiver feature rows with 16-byte loads.
+//
+// Aggregation. The per-receiver sum runs over edges, i.e. across lanes: each
+// 32-column block of messages is transposed through a small per-wave LDS tile,
+// after which every lane holds one column for 16 edges, and the contiguous
+// CSR segments of the tile are summed in registers. A receiver still open at
+// the tile's end carries its partial sum into the next tile. The segment ends
+// of the next 64 receivers come from one lane-parallel load per tile. Nothing
+// edge-sized reaches HBM and every output row has exactly one writer.
+//
+// Backward (forces). The neighbour list is symmetric and w_ij = w_ji, so the
+// owner of receiver i produces, from its own row alone,
+//   q_i       = sum_j dE/dh_j * w_ij         (source sum; the residual
+//                                            dE/dx' is added by the next
+//                                            atom-wise kernel)
+//   dE/dd_ij  = <dE/dw_ij, dw_ij/dd>,  dE/dw_ij = dE/dh_i * x_j + dE/dh_j * x_i
 //   dE/dr_i   = sum_j dE/dd_ij (r_i - r_j) / d_ij
-// which needs no atomics: every output row has one owner. The forward filter
-// is recomputed (nothing edge-sized was stored); dE/dd uses
-// v = (d b~/dd) Wf1, computed with the same B operand as GEMM1, so
-// dE/dd = sum_n (g_w Wf2^T)_n sigmoid(a)_n v_n.
+// dw/dd is carried forward through the recomputed filter (forward-mode along
+// the single scalar d): a' = (d b~/dd) Wf1, s' = sigmoid(a) a', w' = s' Wf2.
+// The tangents ride in the same products as the values (second B operand,
+// same weight reads), so the backward needs no transposed product and lands
+// dE/dd on the edge's own lane. Each interaction block writes its own force
+// rows; a small kernel sums the blocks.
 //
-// MFMA use: v_mfma_f32_32x32x2_f32 for fp32 filters, v_mfma_f32_32x32x16_bf16
-// for bfloat16 filters. The k index inside each MFMA is permuted so every lane
-// reads its A operand with one 16-byte LDS load (k = k0 + 4h + s for fp32,
-// k = k0 + 8h + s for bf16, h = lane / 32); A and B use the same permutation.
-// Gathers use buffer loads with 32-bit byte offsets.
-#include <type_traits>
+// MFMA: v_mfma_f32_32x32x2_f32 (fp32 filters), v_mfma_f32_32x32x16_bf16
+// (bfloat16 filters, fp32 accumulation).
+#include <climits>
+#include <cstring>
 
 #include "common.hpp"
 
@@ -50,27 +61,49 @@ namespace sn {
 #define LN2F 0.69314718055994530942f
 #define LOG2EF 1.44269504088896340736f
 
-constexpr int kCfThreads = 512;
-constexpr int kRpMax = 2048;    // rowptr entries of a work-group staged in LDS
-
-template <int D> struct CfShape { static constexpr int TM = D == 128 ? 64 : 128; };
+constexpr int kEdges = 32;  // edges per wave tile: the MFMA column dimension
 
 // ------------------------------------------------------------------ small helpers
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
+// Bounded loads: an offset past the resource's size reads 0.
 __device__ __forceinline__ float bload(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
 }
 __device__ __forceinline__ int bload_i(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return (int)__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0);
 }
+__device__ __forceinline__ f32x4 bload4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Wave-uniform read of a read-only int array through the scalar cache.
+__device__ __forceinline__ int cload(const int32_t* p, int i) {
+  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
+
+// A copy of v the compiler cannot see through. Addresses derived from it are
+// recomputed where they are used instead of being hoisted out of the tile loop
+// and held in registers for the whole kernel.
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// Orders this wave's LDS writes before its later LDS reads (wave-private data).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 // e^x for x <= 0 and ln(y) for y in [1, 2], on the hardware exp2 / log2.
 __device__ __forceinline__ float exp_neg(float x) { return __builtin_amdgcn_exp2f(x * LOG2EF); }
 __device__ __forceinline__ float ln_1_2(float y) { return __builtin_amdgcn_logf(y) * LN2F; }
 
-// Shifted softplus and its derivative from t = exp(-|a|).
+// Shifted softplus and its derivative (the logistic sigmoid) from t = exp(-|a|).
 __device__ __forceinline__ void ssp_sig(float a, float& s, float& sg) {
   const float t = exp_neg(-fabsf(a));
   const float inv = __builtin_amdgcn_rcpf(1.f + t);
@@ -88,621 +121,653 @@ __device__ __forceinline__ float min_image(float u, float box, float half) {
   return u;
 }
 
-__device__ __forceinline__ int out_row(int r0, int r, int h) { return r0 + 8 * (r >> 2) + 4 * h + (r & 3); }
-
-// ------------------------------------------------------------------ MFMA helpers
-// acc[q] += A_q[32 x K] x B[K x 32] for NA A blocks sharing B.
-// Ap[q] points at A_q row (lane % 32), column 4*(lane / 32); rows 16-byte aligned.
-// B[k][c] = W[k*SW + c0 + c] (BT = false) or W[(c0 + c)*SW + k] (BT = true).
-template <int NA, bool BT, int K>
-__device__ __forceinline__ void mma_f32(f32x16* acc, const float* const* Ap, const float* W, int SW,
-                                        int c0, int lane) {
-  const int h = lane >> 5, li = lane & 31;
-#pragma unroll 2
-  for (int k0 = 0; k0 < K; k0 += 8) {
-    float b0, b1, b2, b3;
-    if constexpr (BT) {
-      const f32x4 bv = *reinterpret_cast<const f32x4*>(W + (c0 + li) * SW + k0 + 4 * h);
-      b0 = bv.x; b1 = bv.y; b2 = bv.z; b3 = bv.w;
-    } else {
-      const float* wp = W + (k0 + 4 * h) * SW + c0 + li;
-      b0 = wp[0]; b1 = wp[SW]; b2 = wp[2 * SW]; b3 = wp[3 * SW];
-    }
-#pragma unroll
-    for (int q = 0; q < NA; ++q) {
-      const f32x4 av = *reinterpret_cast<const f32x4*>(Ap[q] + k0);
-      acc[q] = __builtin_amdgcn_mfma_f32_32x32x2f32(av.x, b0, acc[q], 0, 0, 0);
-      acc[q] = __builtin_amdgcn_mfma_f32_32x32x2f32(av.y, b1, acc[q], 0, 0, 0);
-      acc[q] = __builtin_amdgcn_mfma_f32_32x32x2f32(av.z, b2, acc[q], 0, 0, 0);
-      acc[q] = __builtin_amdgcn_mfma_f32_32x32x2f32(av.w, b3, acc[q], 0, 0, 0);
-    }
-  }
+// XOR-swizzled offset of element (row, col) of a row-major array with RL
+// elements per row: 16-byte chunks (4 fp32 or 8 bf16) trade places by row, so
+// 16-byte reads down a column and 4-byte reads along a row are conflict-free.
+template <int RL>
+__host__ __device__ __forceinline__ int sw4(int row, int col) {
+  constexpr int M = (RL / 4 >= 8) ? 7 : RL / 4 - 1;
+  return row * RL + ((((col >> 2) ^ (row & M)) << 2) | (col & 3));
 }
-
-// bf16 operands: Ap[q] points at A_q row (lane % 32), column 8*(lane / 32);
-// B[k][c] = Wt[(c0 + c)*SWt + k] (B stored transposed, k contiguous).
-template <int NA, int K>
-__device__ __forceinline__ void mma_bf16(f32x16* acc, const __bf16* const* Ap, const __bf16* Wt,
-                                         int SWt, int c0, int lane) {
-  const int h = lane >> 5, li = lane & 31;
-  const __bf16* wp = Wt + (c0 + li) * SWt + 8 * h;
-#pragma unroll 2
-  for (int k0 = 0; k0 < K; k0 += 16) {
-    const bf16x8 b = *reinterpret_cast<const bf16x8*>(wp + k0);
-#pragma unroll
-    for (int q = 0; q < NA; ++q) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ap[q] + k0);
-      acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[q], 0, 0, 0);
-    }
-  }
+template <int RL>
+__host__ __device__ __forceinline__ int sw8(int row, int col) {
+  constexpr int M = (RL / 8 >= 8) ? 7 : RL / 8 - 1;
+  return row * RL + ((((col >> 3) ^ (row & M)) << 3) | (col & 7));
+}
+// bf16 images: position of contraction index k inside its group of 16 (bits 2
+// and 3 swapped), so that lane half h finds the 8 k values its accumulator
+// rows hold (4h..4h+3, 8+4h..8+4h+3) in one 16-byte run.
+__host__ __device__ constexpr int perm16(int k) {
+  return (k & ~15) | (k & 3) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
 
 // ------------------------------------------------------------------ LDS plan
-struct CfLds {
-  int w1, w2, w2n;    // weight regions (bytes)
-  int abuf;           // fp32 operand / staging region
-  int hbuf;           // bf16 operand region
-  int geo;            // per-edge geometry
-  int rp;             // rowptr slice
-  int carry;          // carry rows of the segmented sums
-  int total;
+// Weight image (built on the host, copied verbatim) then one transpose tile per wave.
+//   W1  : Wf1^T [D][KP] (k zero-padded past Dr)
+//   W2  : Wf2^T [D][D]
+//   BIAS: cf1[D], cf2[D] (fp32); staged only where LDS has room, else read
+//         from the image in global memory
+// Rows are output-major: the A operand of a lane is a run of its row.
+template <int D, int KP, bool BF16>
+struct Plan {
+  static constexpr int NW = 8;                 // workers (waves) per work-group
+  static constexpr int NT = NW * 64;
+  static constexpr int ES = BF16 ? 2 : 4;
+  static constexpr int W1 = 0;
+  static constexpr int W2 = W1 + D * KP * ES;
+  static constexpr int BIAS = W2 + D * D * ES;
+  static constexpr int IMG = BIAS + 2 * D * 4;
+  static constexpr int TB = kEdges * 64 * 4;   // transpose tile: 64 columns of 32 rows
+  static constexpr int LDS_MAX = 160 * 1024;
+  static constexpr bool BIAS_LDS = IMG + NW * TB <= LDS_MAX;
+  static constexpr int STAGE = BIAS_LDS ? IMG : BIAS;   // bytes copied into LDS
+  static constexpr int TOTAL = STAGE + NW * TB;
+  static_assert(IMG % 16 == 0 && STAGE % 16 == 0, "image is copied in 16-byte pieces");
+  static_assert(TOTAL <= LDS_MAX, "LDS plan exceeds 160 KiB");
 };
-
-enum { G_D = 0, G_C, G_CP, G_IN, G_J, G_I, G_UX, G_UY, G_UZ, G_INVD, G_FX, G_FY, G_FZ, G_SLOTS };
-
-__host__ __device__ inline int align16(int b) { return (b + 15) & ~15; }
-
-__host__ __device__ inline CfLds cf_plan(int D, int KP, bool bf16, bool bwd) {
-  const int TM = D == 128 ? 64 : 128;
-  CfLds L{};
-  int off = 0;
-  if (bf16) {
-    L.w1 = off; off += align16(D * (KP + 8) * 2);          // W1t [D][KP+8]
-    L.w2 = off; off += align16(D * (D + 8) * 2);           // W2t [D][D+8]
-    L.w2n = off; if (bwd) off += align16(D * (D + 8) * 2); // W2n [D][D+8]
-    L.abuf = off; off += align16(TM * (D + 4) * 4);        // fp32 staging [TM][D+4]
-    const int hb = (bwd ? 2 : 1) * TM * (KP + 8);
-    L.hbuf = off; off += align16((hb > TM * (D + 8) ? hb : TM * (D + 8)) * 2);
-  } else {
-    L.w1 = off; off += align16(KP * (D + 4) * 4);          // W1s [KP][D+4]
-    L.w2 = off; off += align16(D * (D + 4) * 4);           // W2s [D][D+4]
-    L.w2n = L.w2;
-    const int ab = (bwd ? 2 : 1) * TM * (KP + 4);
-    L.abuf = off; off += align16((ab > TM * (D + 4) ? ab : TM * (D + 4)) * 4);
-    L.hbuf = off;
-  }
-  L.geo = off; off += align16(TM * G_SLOTS * 4);
-  L.rp = off; off += align16(kRpMax * 4);
-  L.carry = off; off += align16((bwd ? 2 * D + 8 : 2 * D) * 4);
-  L.total = off;
-  return L;
-}
 
 int cf_kp(int Dr, int bf16) {
-  if (Dr <= 32) return 32;
-  if (!bf16 && Dr <= 56) return 56;
-  return 64;
+  (void)bf16;
+  return Dr <= 32 ? 32 : 64;
 }
-size_t cf_lds_bytes(int D, int KP, int bf16, int backward) {
-  return (size_t)cf_plan(D, KP, bf16 != 0, backward != 0).total;
+int cf_workers(int bf16) {
+  (void)bf16;
+  return 8;
+}
+int cf_chunks(int Dr, int bf16) { return bf16 ? (Dr + 15) / 16 : (Dr + 7) / 8; }
+
+template <int D, int KP, bool BF16>
+static void fill_image(int Dr, const float* Wf1, const float* cf1, const float* Wf2,
+                       const float* cf2, unsigned char* out) {
+  using P = Plan<D, KP, BF16>;
+  std::memset(out, 0, P::IMG);
+  if constexpr (BF16) {
+    uint16_t* w1 = reinterpret_cast<uint16_t*>(out + P::W1);
+    uint16_t* w2 = reinterpret_cast<uint16_t*>(out + P::W2);
+    for (int n = 0; n < D; ++n)
+      for (int k = 0; k < Dr; ++k) w1[sw8<KP>(n, k)] = bf16_rne_bits(Wf1[(size_t)k * D + n]);
+    for (int k = 0; k < D; ++k)
+      for (int n = 0; n < D; ++n) w2[sw8<D>(n, perm16(k))] = bf16_rne_bits(Wf2[(size_t)k * D + n]);
+  } else {
+    float* w1 = reinterpret_cast<float*>(out + P::W1);
+    float* w2 = reinterpret_cast<float*>(out + P::W2);
+    for (int n = 0; n < D; ++n)
+      for (int k = 0; k < Dr; ++k) w1[sw4<KP>(n, k)] = Wf1[(size_t)k * D + n];
+    for (int k = 0; k < D; ++k)
+      for (int n = 0; n < D; ++n) w2[sw4<D>(n, k)] = Wf2[(size_t)k * D + n];
+  }
+  float* bias = reinterpret_cast<float*>(out + P::BIAS);
+  std::memcpy(bias, cf1, D * sizeof(float));
+  std::memcpy(bias + D, cf2, D * sizeof(float));
 }
 
-// ------------------------------------------------------------------ shared pieces
-template <int D, int KP, bool BF16, bool BWD>
-__device__ __forceinline__ void stage_weights(const CfParams& p, unsigned char* lds, const CfLds& L) {
-  if constexpr (BF16) {
-    // global copies are compact [D][KP] and [D][D]; 8 bf16 (16 bytes) per move
-    const f32x4* g1 = reinterpret_cast<const f32x4*>(p.W1t);
-    const f32x4* g2 = reinterpret_cast<const f32x4*>(p.W2t);
-    for (int idx = threadIdx.x; idx < D * KP / 8; idx += kCfThreads) {
-      const int n = idx / (KP / 8), k8 = idx - n * (KP / 8);
-      *reinterpret_cast<f32x4*>(lds + L.w1 + (n * (KP + 8) + 8 * k8) * 2) = g1[idx];
+template <class P>
+__device__ __forceinline__ void stage_image(const void* img, unsigned char* lds) {
+  const f32x4* g = reinterpret_cast<const f32x4*>(img);
+  f32x4* l = reinterpret_cast<f32x4*>(lds);
+  for (int i = threadIdx.x; i < P::STAGE / 16; i += P::NT) l[i] = g[i];
+}
+
+// cf1 (idx < D) or cf2 (idx - D) values idx .. idx + 3 with idx = lo + k: lo
+// is this lane's part (computed inside the tile loop), k a compile-time
+// constant folded into the load's offset.
+template <class P>
+__device__ __forceinline__ f32x4 bias4(const CfParams& p, const unsigned char* lds, int lo, int k) {
+  const unsigned char* base =
+      P::BIAS_LDS ? lds + P::BIAS : reinterpret_cast<const unsigned char*>(p.img) + P::BIAS;
+  return *reinterpret_cast<const f32x4*>(base + 4 * lo + 4 * k);
+}
+
+// ------------------------------------------------------------------ per-edge geometry
+struct Geo {
+  float d0;            // d - rbf_min
+  float C, Cp, in;     // envelope, its d-derivative, 1 inside the cutoff (0 also for padding lanes)
+  float invd, ux, uy, uz;
+};
+
+__device__ __forceinline__ Geo geometry(const CfParams& p, __amdgpu_buffer_rsrc_t rpos, int recv,
+                                        float xj, float yj, float zj, bool valid) {
+  const uint32_t oi = (uint32_t)recv * 12u;
+  float ux = bload(rpos, oi) - xj;
+  float uy = bload(rpos, oi + 4) - yj;
+  float uz = bload(rpos, oi + 8) - zj;
+  if (p.periodic) {
+    ux = min_image(ux, p.box, p.half_box);
+    uy = min_image(uy, p.box, p.half_box);
+    uz = min_image(uz, p.box, p.half_box);
+  }
+  const float d = sqrtf(ux * ux + uy * uy + uz * uz);
+  float sn, cs;
+  sincosf(p.pi_over_rc * d, &sn, &cs);
+  Geo g;
+  g.d0 = d - p.rbf_min;
+  g.in = (valid && d < p.r_cut) ? 1.f : 0.f;
+  g.C = 0.5f * (cs + 1.f);
+  g.Cp = -0.5f * p.pi_over_rc * sn;
+  g.invd = d > 0.f ? 1.f / d : 0.f;
+  g.ux = ux; g.uy = uy; g.uz = uz;
+  return g;
+}
+
+// ------------------------------------------------------------------ products
+// Accumulator element r of block nb (lane half h) is feature 32 nb + 8 (r/4) +
+// 4 h + r%4 of edge lane%32.
+
+// GEMM1: acc[q][nb] += sum_k Wf1[k][32 nb + li] * basis_q(k) for k < 8 KC (fp32)
+// or 16 KC (bf16); basis_0 = b~ (Gaussian x envelope), basis_1 = d b~ / dd.
+// Each lane evaluates the basis of its own edge for the k slots it feeds.
+template <int D, int KP, bool BF16, int NA>
+__device__ __forceinline__ void gemm1(f32x16 (&acc)[NA][D / 32], const unsigned char* lds,
+                                      const CfParams& p, const Geo& g, int lane_) {
+  const int lane = opaque(lane_), h = lane >> 5, li = lane & 31;
+  constexpr int CH = BF16 ? 16 : 8;    // k per chunk
+  constexpr int PL = CH / 2;           // k per lane half per chunk
+  float step = p.rbf_step;
+  asm volatile("" : "+v"(step));
+  const float dh = g.d0 - (float)(PL * h) * step;
+  const float coef2 = p.rbf_coef2, inv_s2 = p.rbf_inv_s2;
+#pragma unroll 1
+  for (int c = 0; c < p.KC; ++c) {
+    float b[NA][PL];
+#pragma unroll
+    for (int t = 0; t < PL; ++t) {
+      const float z = dh - (float)(CH * c + t) * step;
+      const float gs = g.in * __builtin_amdgcn_exp2f(coef2 * z * z);
+      b[0][t] = gs * g.C;
+      if constexpr (NA == 2) b[1][t] = gs * (g.Cp - z * inv_s2 * g.C);
     }
-    for (int idx = threadIdx.x; idx < D * D / 8; idx += kCfThreads) {
-      const int n = idx / (D / 8), k8 = idx - n * (D / 8);
-      *reinterpret_cast<f32x4*>(lds + L.w2 + (n * (D + 8) + 8 * k8) * 2) = g2[idx];
-    }
-    if constexpr (BWD) {
-      const f32x4* g3 = reinterpret_cast<const f32x4*>(p.W2n);
-      for (int idx = threadIdx.x; idx < D * D / 8; idx += kCfThreads) {
-        const int n = idx / (D / 8), k8 = idx - n * (D / 8);
-        *reinterpret_cast<f32x4*>(lds + L.w2n + (n * (D + 8) + 8 * k8) * 2) = g3[idx];
+    if constexpr (BF16) {
+      const __bf16* W1 = reinterpret_cast<const __bf16*>(lds);
+      bf16x8 bq[NA];
+#pragma unroll
+      for (int q = 0; q < NA; ++q)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) bq[q][t] = (__bf16)b[q][t];
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb) {
+        const bf16x8 w = *reinterpret_cast<const bf16x8*>(W1 + sw8<KP>(32 * nb + li, CH * c + PL * h));
+#pragma unroll
+        for (int q = 0; q < NA; ++q)
+          acc[q][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w, bq[q], acc[q][nb], 0, 0, 0);
+      }
+    } else {
+      const float* W1 = reinterpret_cast<const float*>(lds);
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb) {
+        const f32x4 w = *reinterpret_cast<const f32x4*>(W1 + sw4<KP>(32 * nb + li, CH * c + PL * h));
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int q = 0; q < NA; ++q)
+            acc[q][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(w[t], b[q][t], acc[q][nb], 0, 0, 0);
       }
     }
+  }
+}
+
+// B operands of a chained product from an accumulator-layout input: fp32 uses
+// the accumulator registers directly; bf16 packs them once (k slot 8 h + t of
+// step (kb, u) is register 8 u + t of block kb).
+template <int D, bool BF16>
+struct Operand;
+template <int D>
+struct Operand<D, false> {
+  const f32x16 (&S)[D / 32];
+  __device__ __forceinline__ explicit Operand(const f32x16 (&s)[D / 32]) : S(s) {}
+};
+template <int D>
+struct Operand<D, true> {
+  bf16x8 S[D / 32][2];
+  __device__ __forceinline__ explicit Operand(const f32x16 (&s)[D / 32]) {
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) S[kb][u][t] = (__bf16)s[kb][8 * u + t];
+  }
+};
+
+// acc[q] += sum_k M[32 nb + li][k] S_q[k] for one output block nb and NA
+// inputs sharing each weight read; M is an output-major image (fp32: sw4
+// rows; bf16: sw8 rows with perm16 positions).
+template <int D, bool BF16, int NA>
+__device__ __forceinline__ void gemm_om_block(f32x16 (&acc)[NA],
+                                              const Operand<D, BF16>* const (&op)[NA],
+                                              const void* img, int nb, int h, int li) {
+  if constexpr (BF16) {
+    const __bf16* M = reinterpret_cast<const __bf16*>(img);
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const bf16x8 w =
+            *reinterpret_cast<const bf16x8*>(M + sw8<D>(32 * nb + li, 32 * kb + 16 * u + 8 * h));
+#pragma unroll
+        for (int q = 0; q < NA; ++q)
+          acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w, op[q]->S[kb][u], acc[q], 0, 0, 0);
+      }
   } else {
-    float* W1s = reinterpret_cast<float*>(lds + L.w1);
-    float* W2s = reinterpret_cast<float*>(lds + L.w2);
-    const f32x4* g1 = reinterpret_cast<const f32x4*>(p.Wf1);
-    const f32x4* g2 = reinterpret_cast<const f32x4*>(p.Wf2);
-    for (int idx = threadIdx.x; idx < KP * D / 4; idx += kCfThreads) {
-      const int k = idx / (D / 4), n4 = idx - k * (D / 4);
-      const f32x4 v = k < p.Dr ? g1[idx] : f32x4{};
-      *reinterpret_cast<f32x4*>(W1s + k * (D + 4) + 4 * n4) = v;
-    }
-    for (int idx = threadIdx.x; idx < D * D / 4; idx += kCfThreads) {
-      const int k = idx / (D / 4), n4 = idx - k * (D / 4);
-      *reinterpret_cast<f32x4*>(W2s + k * (D + 4) + 4 * n4) = g2[idx];
-    }
+    const float* M = reinterpret_cast<const float*>(img);
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f32x4 w =
+            *reinterpret_cast<const f32x4*>(M + sw4<D>(32 * nb + li, 32 * kb + 8 * c + 4 * h));
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int q = 0; q < NA; ++q)
+            acc[q] = __builtin_amdgcn_mfma_f32_32x32x2f32(w[t], op[q]->S[kb][4 * c + t], acc[q],
+                                                          0, 0, 0);
+      }
   }
 }
 
-// rowptr access: FULL when the work-group's whole slice sits in LDS (the
-// common case; no global loads, so the compiler need not drain in-flight
-// prefetches), else through the slice when the index falls inside it.
-template <bool FULL>
-struct RowPtr {
-  const int32_t* g;
-  const int32_t* s;
-  int base, len;
-  __device__ __forceinline__ int operator()(int i) const {
-    const int k = i - base;
-    if constexpr (FULL) return s[k];
-    return k < len ? s[k] : g[i];
+// ------------------------------------------------------------------ receiver segments
+// Lane l of a window holds rowptr[cur + 1 + l], the end of receiver cur + l's
+// segment; INT_MAX past the worker's last receiver ib - 1.
+__device__ __forceinline__ int load_window(__amdgpu_buffer_rsrc_t rrow, int cur, int ib, int lane) {
+  const int i = cur + lane;
+  const int v = bload_i(rrow, (uint32_t)((i < ib ? i : ib - 1) + 1) * 4u);
+  return i < ib ? v : INT_MAX;
+}
+// End of receiver cur + l (l wave-uniform).
+__device__ __forceinline__ int seg_end(const CfParams& p, int win, int cur, int ib, int l) {
+  if (l < 64) return __builtin_amdgcn_readlane(win, l);
+  return cur + l < ib ? cload(p.rowptr, cur + l + 1) : INT_MAX;
+}
+// Number of receivers from cur on whose segment ends at or before `bound`.
+__device__ __forceinline__ int count_ends(const CfParams& p, int win, int cur, int ib, int bound) {
+  int n = __builtin_popcountll(__ballot(win <= bound));
+  if (n == 64)
+    while (seg_end(p, win, cur, ib, n) <= bound) ++n;
+  return n;
+}
+
+// Sum of x over lanes li in [lo, hi) of the lower half (upper-half lanes pass 0).
+__device__ __forceinline__ float lane_range_sum(float x, int li, int lo, int hi) {
+  float s = (li >= lo && li < hi) ? x : 0.f;
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) s += __shfl_xor(s, o, 64);
+  return s;
+}
+
+// Transpose tile of a wave: 64 columns (two 32-feature blocks) of the 32 tile
+// rows, column-major, 16-byte chunks XOR-swizzled by column so that the
+// accumulator-layout writes (one column, 32 consecutive rows per half-wave)
+// and the per-lane column reads are both conflict-free.
+__device__ __forceinline__ int tpos(int c, int row) {
+  return c * kEdges + ((((row >> 2) ^ (c & 7)) << 2) | (row & 3));
+}
+// Writes block b (0/1) of the tile from accumulator layout.
+__device__ __forceinline__ void tile_put(float* Tb, int b, const float (&m)[16], int lane_) {
+  const int lane = opaque(lane_), h = lane >> 5, li = lane & 31;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) Tb[tpos(32 * b + 8 * (r >> 2) + 4 * h + (r & 3), li)] = m[r];
+}
+// Per-receiver sums of this lane's column of the tile (rows past the tile's
+// length hold zeros). Receivers cur .. cur + nfin - 1 end in this tile and are
+// written through out(i, total); the open receiver's partial sum is carried.
+// A segmented inclusive scan runs down the column (one FMA per row with a
+// wave-uniform keep factor that is 0 where a receiver's rows begin), is
+// written back over the column, and each receiver's total is then one read
+// at its last row; the summation order is the plain sequential one.
+template <class Out>
+__device__ __forceinline__ void column_segments(const CfParams& p, float* Tb, int win, int cur,
+                                                int ib, int nfin, int ts, int len, bool open,
+                                                float& carry, int lane_, Out out) {
+  const int lane = opaque(lane_);
+  uint32_t starts = 0;
+  for (int l = 0; l < nfin; ++l) {
+    const int b = seg_end(p, win, cur, ib, l) - ts;
+    if (b < kEdges) starts |= 1u << b;
   }
+  float* col = Tb + lane * kEdges;
+  float run = carry;
+#pragma unroll
+  for (int u = 0; u < kEdges / 4; ++u) {
+    float* q = col + ((u ^ (lane & 7)) << 2);
+    f32x4 t = *reinterpret_cast<const f32x4*>(q);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float keep = ((starts >> (4 * u + e)) & 1u) ? 0.f : 1.f;
+      run = fmaf(run, keep, t[e]);
+      t[e] = run;
+    }
+    *reinterpret_cast<f32x4*>(q) = t;
+  }
+  wave_sync();
+  int prev = 0;
+  for (int l = 0; l < nfin; ++l) {
+    const int b = seg_end(p, win, cur, ib, l) - ts;
+    const int r = b - 1;
+    const float tot = b > prev ? col[(((r >> 2) ^ (lane & 7)) << 2) | (r & 3)] : 0.f;
+    out(cur + l, tot);
+    prev = b;
+  }
+  carry = (open && prev < len) ? run : 0.f;
+}
+
+// ------------------------------------------------------------------ kernels
+// Per-worker state shared by the forward and backward walks.
+struct Walk {
+  int ia, ib, E0, E1;
+  __amdgpu_buffer_rsrc_t rrow, rcol, rpos;
 };
 
-// Geometry loads run one tile ahead of the arithmetic: while tile k computes,
-// the positions of tile k+1 and the sender indices of tile k+2 are in flight
-// (threads 0..TM-1, one edge each).
-struct GeoPrefetch {
-  int i, j, jn;                 // receiver and sender of the next tile's edge; sender a tile later
-  float xi, yi, zi, xj, yj, zj; // their positions
+template <class P>
+__device__ __forceinline__ bool worker_range(const CfParams& p, int wave, Walk& w) {
+  const uint32_t N = (uint32_t)p.n_atoms;
+  const int wid = (int)blockIdx.x * P::NW + wave;
+  w.ia = cload(p.wg_start, wid);
+  w.ib = cload(p.wg_start, wid + 1);
+  if (w.ia >= w.ib) return false;
+  w.E0 = cload(p.rowptr, w.ia);
+  w.E1 = cload(p.rowptr, w.ib);
+  w.rrow = rsrc(p.rowptr, (N + 1) * 4u);
+  w.rcol = rsrc(p.col, (uint32_t)cload(p.rowptr, (int)N) * 4u);
+  w.rpos = rsrc(p.pos, N * 12u);
+  return true;
+}
+
+// Receiver of this lane's edge ts + li: cur + the number of receivers whose
+// segment ends at or before it.
+__device__ __forceinline__ int edge_receiver(const CfParams& p, int win, int cur, int ib, int nin,
+                                             int e) {
+  int recv = cur;
+  for (int l = 0; l < nin; ++l) recv += (e >= seg_end(p, win, cur, ib, l)) ? 1 : 0;
+  return recv;
+}
+
+// Per-tile receiver bookkeeping and edge geometry (both kernels).
+struct TileHead {
+  int te, len, nfin, ncur, recv, j, win_next;
+  Geo g;
 };
 
-__device__ __forceinline__ void pf_positions(GeoPrefetch& f, __amdgpu_buffer_rsrc_t rpos) {
-  const uint32_t oi = (uint32_t)f.i * 12u, oj = (uint32_t)f.j * 12u;
-  f.xi = bload(rpos, oi);
-  f.yi = bload(rpos, oi + 4);
-  f.zi = bload(rpos, oi + 8);
-  f.xj = bload(rpos, oj);
-  f.yj = bload(rpos, oj + 4);
-  f.zj = bload(rpos, oj + 8);
-}
-
-template <int TM, class RPT>
-__device__ __forceinline__ void pf_start(GeoPrefetch& f, const RPT& RP, int ia, int ts, int e_end,
-                                         __amdgpu_buffer_rsrc_t rcol, __amdgpu_buffer_rsrc_t rpos) {
-  const int e = ts + (int)threadIdx.x, e2 = e + TM;
-  // reads past the last edge return 0 (the buffer descriptor bounds them)
-  f.j = bload_i(rcol, (uint32_t)e * 4u);
-  f.jn = bload_i(rcol, (uint32_t)e2 * 4u);
-  int i = ia;
-  if (e < e_end)
-    while (RP(i + 1) <= e) ++i;
-  f.i = i;
-  pf_positions(f, rpos);
-}
-
-// Move the prefetch on to the tile starting at ts (the previous tile's values
-// have been consumed).
-template <int TM, class RPT>
-__device__ __forceinline__ void pf_advance(GeoPrefetch& f, const RPT& RP, int ts, int e_end,
-                                           __amdgpu_buffer_rsrc_t rcol,
-                                           __amdgpu_buffer_rsrc_t rpos) {
-  const int e = ts + (int)threadIdx.x, e2 = e + TM;
-  int i = f.i;
-  if (e < e_end)
-    while (RP(i + 1) <= e) ++i;
-  f.i = i;
-  f.j = f.jn;
-  f.jn = bload_i(rcol, (uint32_t)e2 * 4u);
-  pf_positions(f, rpos);
-}
-
-// Geometry of the tile's edges from the prefetched values (threads 0..TM-1):
-// receiver, sender, u = r_i - r_j, d, envelope and its derivative, and the
-// inside-cutoff flag. Rows past the tile end get receiver `cur`, sender 0.
-template <int TM, bool BWD>
-__device__ __forceinline__ void tile_geometry(const CfParams& p, const GeoPrefetch& f, float* geo,
-                                              int ts, int te, int cur) {
-  const int r = threadIdx.x;
-  const int e = ts + r;
-  float d = 0.f, C = 0.f, Cp = 0.f, ux = 0.f, uy = 0.f, uz = 0.f, invd = 0.f;
-  int j = 0, i = cur, inside = 0;
-  if (e < te) {
-    i = f.i;
-    j = f.j;
-    ux = f.xi - f.xj;
-    uy = f.yi - f.yj;
-    uz = f.zi - f.zj;
-    if (p.periodic) {
-      ux = min_image(ux, p.box, p.half_box);
-      uy = min_image(uy, p.box, p.half_box);
-      uz = min_image(uz, p.box, p.half_box);
-    }
-    d = sqrtf(ux * ux + uy * uy + uz * uz);
-    inside = d < p.r_cut;
-    if (inside) {
-      float sn, cs;
-      sincosf(p.pi_over_rc * d, &sn, &cs);
-      C = 0.5f * (cs + 1.f);
-      Cp = -0.5f * p.pi_over_rc * sn;
-    }
-    invd = d > 0.f ? 1.f / d : 0.f;
-  }
-  int* geoi = reinterpret_cast<int*>(geo);
-  geo[G_D * TM + r] = d;
-  geo[G_C * TM + r] = C;
-  geoi[G_IN * TM + r] = inside;
-  geoi[G_J * TM + r] = j;
-  geoi[G_I * TM + r] = i;
-  if constexpr (BWD) {
-    geo[G_CP * TM + r] = Cp;
-    geo[G_UX * TM + r] = ux;
-    geo[G_UY * TM + r] = uy;
-    geo[G_UZ * TM + r] = uz;
-    geo[G_INVD * TM + r] = invd;
-  }
-}
-
-// The receivers [first, last] of a tile; `last_open` when the last one's
-// segment continues into the next tile.
-struct TileSegs {
-  int first, last, nseg;
-  bool last_open;
-};
-template <int TM, class RPT>
-__device__ __forceinline__ TileSegs tile_segs(const RPT& RP, const int* geoi, int ts, int te,
-                                              int cur) {
-  TileSegs t;
-  t.first = cur;
-  t.last = geoi[G_I * TM + (te - ts - 1)];
-  t.nseg = t.last - t.first + 1;
-  t.last_open = RP(t.last + 1) > te;
+__device__ __forceinline__ TileHead tile_head(const CfParams& p, const Walk& wk, int ts, int cur,
+                                              int win, int& jn, float pjx, float pjy, float pjz,
+                                              int lane, int li) {
+  TileHead t;
+  t.te = min(ts + kEdges, wk.E1);
+  t.len = t.te - ts;
+  t.nfin = count_ends(p, win, cur, wk.ib, t.te);
+  const int nin = count_ends(p, win, cur, wk.ib, t.te - 1);
+  t.recv = edge_receiver(p, win, cur, wk.ib, nin, ts + li);
+  t.j = jn;
+  t.g = geometry(p, wk.rpos, t.recv, pjx, pjy, pjz, li < t.len);
+  t.ncur = cur + t.nfin;
+  t.win_next = load_window(wk.rrow, t.ncur, wk.ib, lane);
+  jn = bload_i(wk.rcol, (uint32_t)(ts + kEdges + li) * 4u);
   return t;
 }
 
-// Column-parallel segmented sum of the tile rows in `buf` (stride SQ): every
-// receiver of the tile gets one thread per column; the first receiver adds the
-// carried partial sum, the last one either stores its partial (still open) or
-// clears the carry. flush(i, c, value) writes a completed receiver.
-template <int D, int SQ, class RPT, class Flush>
-__device__ __forceinline__ void seg_sum_cols(const RPT& RP, const TileSegs& t, int ts, int te,
-                                             const float* buf, const float* carry_in,
-                                             float* carry_out, Flush flush) {
-  constexpr int NG = kCfThreads / D;
-  const int g = threadIdx.x / D, c = threadIdx.x - g * D;
-  for (int k = g; k < t.nseg; k += NG) {
-    const int i = t.first + k;
-    const int rs = RP(i), re = RP(i + 1);
-    const int lo = (rs > ts ? rs : ts) - ts, hi = (re < te ? re : te) - ts;
-    float s = 0.f;
-    for (int r = lo; r < hi; ++r) s += buf[r * SQ + c];
-    if (k == 0) s += carry_in[c];
-    if (k == t.nseg - 1) {
-      if (t.last_open) {
-        carry_out[c] = s;
-        continue;
-      }
-      carry_out[c] = 0.f;
-    }
-    flush(i, c, s);
-  }
-}
-
-// ------------------------------------------------------------------ forward
 template <int D, int KP, bool BF16>
-__global__ __launch_bounds__(kCfThreads, 1) void k_cf_fwd(CfParams p) {
-  constexpr int TM = CfShape<D>::TM, NCB = D / 32, SQ = D + 4, SW = D + 4, SH = D + 8;
-  constexpr int SA = BF16 ? KP + 8 : KP + 4;
+__global__ __launch_bounds__(512, 1) void k_cf_fwd(CfParams p) {
+  using P = Plan<D, KP, BF16>;
+  constexpr int NB = D / 32;
   extern __shared__ __align__(16) unsigned char lds[];
-  const CfLds L = cf_plan(D, KP, BF16, false);
-  float* abuf = reinterpret_cast<float*>(lds + L.abuf);
-  __bf16* hbuf = reinterpret_cast<__bf16*>(lds + L.hbuf);
-  float* geo = reinterpret_cast<float*>(lds + L.geo);
-  const int* geoi = reinterpret_cast<const int*>(geo);
-  int32_t* rps = reinterpret_cast<int32_t*>(lds + L.rp);
-  float* carry = reinterpret_cast<float*>(lds + L.carry);
+  stage_image<P>(p.img, lds);
+  __syncthreads();
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, li = lane & 31;
-  const int cb = wave % NCB, r0 = 32 * (wave / NCB), c = cb * 32 + li;
+  const int lane = threadIdx.x & 63, h = lane >> 5, li = lane & 31;
+  const int wave = uni((int)threadIdx.x >> 6);
+  Walk wk;
+  if (!worker_range<P>(p, wave, wk)) return;
+  const int ib = wk.ib;
+  float* Tb = reinterpret_cast<float*>(lds + P::STAGE + wave * P::TB);
   const uint32_t N = (uint32_t)p.n_atoms;
-  const __amdgpu_buffer_rsrc_t rcol = rsrc(p.col, (uint32_t)p.rowptr[p.n_atoms] * 4u);
-  const __amdgpu_buffer_rsrc_t rpos = rsrc(p.pos, N * 12u);
   const __amdgpu_buffer_rsrc_t rx = rsrc(p.x, N * (uint32_t)D * 4u);
 
-  stage_weights<D, KP, BF16, false>(p, lds, L);
-  const float bias1 = p.cf1[c], bias2 = p.cf2[c];
-  const int ia = p.wg_start[blockIdx.x], ib = p.wg_start[blockIdx.x + 1];
-  const int rpl = min(ib - ia + 1, kRpMax);
-  for (int k = tid; k < rpl; k += kCfThreads) rps[k] = p.rowptr[ia + k];
-  for (int k = tid; k < 2 * D; k += kCfThreads) carry[k] = 0.f;
-  __syncthreads();
-  auto tiles = [&](auto full) {
-  const RowPtr<decltype(full)::value> RP{p.rowptr, rps, ia, rpl};
-  const int e_begin = RP(ia), e_end = RP(ib);
-  int cur = ia, par = 0;
-  GeoPrefetch pf{};
-  if (tid < TM) pf_start<TM>(pf, RP, ia, e_begin, e_end, rcol, rpos);
+  float carry[NB / 2];
+#pragma unroll
+  for (int pr = 0; pr < NB / 2; ++pr) carry[pr] = 0.f;
+  int cur = wk.ia;
+  int win = load_window(wk.rrow, cur, ib, lane);
+  int jn = bload_i(wk.rcol, (uint32_t)(wk.E0 + li) * 4u);
+  float pjx = bload(wk.rpos, (uint32_t)jn * 12u), pjy = bload(wk.rpos, (uint32_t)jn * 12u + 4),
+        pjz = bload(wk.rpos, (uint32_t)jn * 12u + 8);
 
-  for (int ts = e_begin; ts < e_end; ts += TM) {
-    const int te = min(ts + TM, e_end);
-    if (tid < TM) {
-      tile_geometry<TM, false>(p, pf, geo, ts, te, cur);
-      pf_advance<TM>(pf, RP, ts + TM, e_end, rcol, rpos);
-    }
-    __syncthreads();
-    // sender features, needed after the filter: issue the gathers now
-    float xg[16];
+  for (int ts = wk.E0; ts < wk.E1; ts += kEdges) {
+    const TileHead th = tile_head(p, wk, ts, cur, win, jn, pjx, pjy, pjz, lane, li);
+    const Geo& g = th.g;
+    const int h4 = 4 * (opaque(lane) >> 5);   // this lane's column offset in a block
+
+    // s = ssp(b~ Wf1 + cf1)
+    f32x16 s[1][NB];
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      xg[r] = bload(rx, ((uint32_t)geoi[G_J * TM + out_row(r0, r, h)] * D + c) * 4u);
-    // basis b~ = exp(-(d - mu_k)^2 / (2 sigma^2)) C(d), zero for padding and masked edges
-    for (int idx = tid; idx < TM * KP; idx += kCfThreads) {
-      const int r = idx / KP, k = idx - r * KP;
-      float v = 0.f;
-      if (k < p.Dr && geoi[G_IN * TM + r]) {
-        const float z = geo[G_D * TM + r] - (p.rbf_min + (float)k * p.rbf_step);
-        v = __builtin_amdgcn_exp2f(p.rbf_coef2 * z * z) * geo[G_C * TM + r];
+    for (int nb = 0; nb < NB; ++nb) s[0][nb] = f32x16{};
+    gemm1<D, KP, BF16, 1>(s, lds, p, g, lane);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 c1 = bias4<P>(p, lds, h4, 32 * nb + 8 * q);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) s[0][nb][4 * q + t] = ssp(s[0][nb][4 * q + t] + c1[t]);
       }
-      if constexpr (BF16) hbuf[r * SA + k] = (__bf16)v;
-      else abuf[r * SA + k] = v;
-    }
-    __syncthreads();
-    f32x16 acc[1] = {f32x16{}};
-    if constexpr (BF16) {
-      const __bf16* Ap[1] = {hbuf + (r0 + li) * SA + 8 * h};
-      mma_bf16<1, KP>(acc, Ap, reinterpret_cast<const __bf16*>(lds + L.w1), SA, cb * 32, lane);
-    } else {
-      const float* Ap[1] = {abuf + (r0 + li) * SA + 4 * h};
-      mma_f32<1, false, KP>(acc, Ap, reinterpret_cast<const float*>(lds + L.w1), SW, cb * 32, lane);
-    }
-    __syncthreads();
-    // s = ssp(a), the A operand of the second filter layer
+    pjx = bload(wk.rpos, (uint32_t)jn * 12u);
+    pjy = bload(wk.rpos, (uint32_t)jn * 12u + 4);
+    pjz = bload(wk.rpos, (uint32_t)jn * 12u + 8);
+    const Operand<D, BF16> os(s[0]);
+    const Operand<D, BF16>* const ops[1] = {&os};
+
+    // per output block: w = s Wf2 + cf2 (masked beyond the cutoff), message
+    // x_j * w, summed per receiver two blocks at a time
+    const uint32_t xo = ((uint32_t)th.j * (uint32_t)D + (uint32_t)h4) * 4u;
+    const int lane_o = opaque(lane), ho = lane_o >> 5, lio = lane_o & 31;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = out_row(r0, r, h);
-      const float s = ssp(acc[0][r] + bias1);
-      if constexpr (BF16) hbuf[row * SH + c] = (__bf16)s;
-      else abuf[row * SQ + c] = s;
-      acc[0][r] = 0.f;
-    }
-    __syncthreads();
-    if constexpr (BF16) {
-      const __bf16* Ap[1] = {hbuf + (r0 + li) * SH + 8 * h};
-      mma_bf16<1, D>(acc, Ap, reinterpret_cast<const __bf16*>(lds + L.w2), SH, cb * 32, lane);
-    } else {
-      const float* Ap[1] = {abuf + (r0 + li) * SQ + 4 * h};
-      mma_f32<1, false, D>(acc, Ap, reinterpret_cast<const float*>(lds + L.w2), SW, cb * 32, lane);
-    }
-    // m = x_src * w in the MFMA output layout
-    float m[16];
+    for (int pr = 0; pr < NB / 2; ++pr) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = out_row(r0, r, h);
-      const float mk = geoi[G_IN * TM + row] ? 1.f : 0.f;
-      m[r] = mk * ((acc[0][r] + bias2) * xg[r]);
-    }
-    __syncthreads();
+      for (int b = 0; b < 2; ++b) {
+        const int nb = 2 * pr + b;
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16 w[1] = {f32x16{}};
+        gemm_om_block<D, BF16, 1>(w, ops, lds + P::W2, nb, ho, lio);
+        float m[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) abuf[out_row(r0, r, h) * SQ + c] = m[r];
-    __syncthreads();
-    const TileSegs t = tile_segs<TM>(RP, geoi, ts, te, cur);
-    seg_sum_cols<D, SQ>(RP, t, ts, te, abuf, carry + par * D, carry + (1 - par) * D,
-                        [&](int i, int cc, float v) { p.h[(size_t)i * D + cc] = v; });
-    cur = t.last_open ? t.last : t.last + 1;
-    par = 1 - par;
-    __syncthreads();
+        for (int q = 0; q < 4; ++q) {
+          const int col = 32 * nb + 8 * q;   // + h4
+          const f32x4 xg = bload4(rx, xo + (uint32_t)col * 4u);
+          const f32x4 c2 = bias4<P>(p, lds, h4, D + col);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) m[4 * q + t] = xg[t] * (g.in * (w[0][4 * q + t] + c2[t]));
+        }
+        tile_put(Tb, b, m, lane);
+      }
+      wave_sync();
+      float* hout = p.h + 64 * pr + lane;
+      column_segments(p, Tb, win, cur, ib, th.nfin, ts, th.len, th.ncur < ib, carry[pr], lane,
+                      [&](int i, float tot) { hout[(size_t)i * D] = tot; });
+      wave_sync();
+    }
+    cur = th.ncur;
+    win = th.win_next;
   }
-  for (int idx = tid; idx < (ib - cur) * D; idx += kCfThreads)
-    p.h[(size_t)cur * D + idx] = 0.f;
-  };
-  if (rpl == ib - ia + 1) tiles(std::true_type{});
-  else tiles(std::false_type{});
+  // receivers of a worker without edges
+  for (int i = cur; i < ib; ++i)
+    for (int c = lane; c < D; c += 64) p.h[(size_t)i * D + c] = 0.f;
 }
 
-// ------------------------------------------------------------------ backward
 template <int D, int KP, bool BF16>
-__global__ __launch_bounds__(kCfThreads, 1) void k_cf_bwd(CfParams p) {
-  constexpr int TM = CfShape<D>::TM, NCB = D / 32, SQ = D + 4, SW = D + 4, SH = D + 8;
-  constexpr int SA = BF16 ? KP + 8 : KP + 4;
-  constexpr int TPR = kCfThreads / TM;   // threads per row in the feature sums
+__global__ __launch_bounds__(512, 1) void k_cf_bwd(CfParams p) {
+  using P = Plan<D, KP, BF16>;
+  constexpr int NB = D / 32;
   extern __shared__ __align__(16) unsigned char lds[];
-  const CfLds L = cf_plan(D, KP, BF16, true);
-  float* abuf = reinterpret_cast<float*>(lds + L.abuf);
-  __bf16* hbuf = reinterpret_cast<__bf16*>(lds + L.hbuf);
-  float* geo = reinterpret_cast<float*>(lds + L.geo);
-  const int* geoi = reinterpret_cast<const int*>(geo);
-  int32_t* rps = reinterpret_cast<int32_t*>(lds + L.rp);
-  float* qcarry = reinterpret_cast<float*>(lds + L.carry);   // [2][D]
-  float* fcarry = qcarry + 2 * D;                            // [2][4]
+  stage_image<P>(p.img, lds);
+  __syncthreads();
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, li = lane & 31;
-  const int cb = wave % NCB, r0 = 32 * (wave / NCB), c = cb * 32 + li;
+  const int lane = threadIdx.x & 63, h = lane >> 5, li = lane & 31;
+  const bool upper = h != 0;
+  const int wave = uni((int)threadIdx.x >> 6);
+  Walk wk;
+  if (!worker_range<P>(p, wave, wk)) return;
+  const int ib = wk.ib;
+  float* Tb = reinterpret_cast<float*>(lds + P::STAGE + wave * P::TB);
   const uint32_t N = (uint32_t)p.n_atoms;
-  const __amdgpu_buffer_rsrc_t rcol = rsrc(p.col, (uint32_t)p.rowptr[p.n_atoms] * 4u);
-  const __amdgpu_buffer_rsrc_t rpos = rsrc(p.pos, N * 12u);
   const __amdgpu_buffer_rsrc_t rx = rsrc(p.x, N * (uint32_t)D * 4u);
   const __amdgpu_buffer_rsrc_t rgh = rsrc(p.gh, N * (uint32_t)D * 4u);
+  const bool want_q = p.q_out != nullptr;
 
-  stage_weights<D, KP, BF16, true>(p, lds, L);
-  const float bias1 = p.cf1[c], bias2 = p.cf2[c];
-  const int ia = p.wg_start[blockIdx.x], ib = p.wg_start[blockIdx.x + 1];
-  const int rpl = min(ib - ia + 1, kRpMax);
-  for (int k = tid; k < rpl; k += kCfThreads) rps[k] = p.rowptr[ia + k];
-  for (int k = tid; k < 2 * D + 8; k += kCfThreads) qcarry[k] = 0.f;
-  const bool want_gx = p.gx_out != nullptr;
-  __syncthreads();
-  auto tiles = [&](auto full) {
-  const RowPtr<decltype(full)::value> RP{p.rowptr, rps, ia, rpl};
-  const int e_begin = RP(ia), e_end = RP(ib);
-  int cur = ia, par = 0;
-  GeoPrefetch pf{};
-  if (tid < TM) pf_start<TM>(pf, RP, ia, e_begin, e_end, rcol, rpos);
+  float carry[NB / 2];
+#pragma unroll
+  for (int pr = 0; pr < NB / 2; ++pr) carry[pr] = 0.f;
+  float fcx = 0.f, fcy = 0.f, fcz = 0.f;
+  int cur = wk.ia, ss = wk.E0;
+  int win = load_window(wk.rrow, cur, ib, lane);
+  int jn = bload_i(wk.rcol, (uint32_t)(wk.E0 + li) * 4u);
+  float pjx = bload(wk.rpos, (uint32_t)jn * 12u), pjy = bload(wk.rpos, (uint32_t)jn * 12u + 4),
+        pjz = bload(wk.rpos, (uint32_t)jn * 12u + 8);
 
-  for (int ts = e_begin; ts < e_end; ts += TM) {
-    const int te = min(ts + TM, e_end);
-    if (tid < TM) {
-      tile_geometry<TM, true>(p, pf, geo, ts, te, cur);
-      pf_advance<TM>(pf, RP, ts + TM, e_end, rcol, rpos);
-    }
-    __syncthreads();
-    // sender rows, needed after the filter: issue the gathers now
-    float xg[16], gg[16];
+  for (int ts = wk.E0; ts < wk.E1; ts += kEdges) {
+    const TileHead th = tile_head(p, wk, ts, cur, win, jn, pjx, pjy, pjz, lane, li);
+    const Geo& g = th.g;
+    const int h4 = 4 * (opaque(lane) >> 5);   // this lane's column offset in a block
+
+    // GEMM1: a = b~ Wf1 + cf1 and its tangent a' = (d b~/dd) Wf1;
+    // s = ssp(a), s' = sigmoid(a) a'
+    f32x16 av[2][NB];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const uint32_t oj = ((uint32_t)geoi[G_J * TM + out_row(r0, r, h)] * D + c) * 4u;
-      xg[r] = bload(rx, oj);
-      gg[r] = bload(rgh, oj);
-    }
-    // b~ and d b~ / dd
-    for (int idx = tid; idx < TM * KP; idx += kCfThreads) {
-      const int r = idx / KP, k = idx - r * KP;
-      float bt = 0.f, btp = 0.f;
-      if (k < p.Dr && geoi[G_IN * TM + r]) {
-        const float z = geo[G_D * TM + r] - (p.rbf_min + (float)k * p.rbf_step);
-        const float g = __builtin_amdgcn_exp2f(p.rbf_coef2 * z * z);
-        const float C = geo[G_C * TM + r], Cp = geo[G_CP * TM + r];
-        bt = g * C;
-        btp = g * (Cp - z * p.rbf_inv_s2 * C);
-      }
-      if constexpr (BF16) {
-        hbuf[r * SA + k] = (__bf16)bt;
-        hbuf[(TM + r) * SA + k] = (__bf16)btp;
-      } else {
-        abuf[r * SA + k] = bt;
-        abuf[(TM + r) * SA + k] = btp;
-      }
-    }
-    __syncthreads();
-    // GEMM1 on both operands: a = b~ Wf1, v = (d b~/dd) Wf1
-    f32x16 acc[2] = {f32x16{}, f32x16{}};
-    if constexpr (BF16) {
-      const __bf16* Ap[2] = {hbuf + (r0 + li) * SA + 8 * h, hbuf + (TM + r0 + li) * SA + 8 * h};
-      mma_bf16<2, KP>(acc, Ap, reinterpret_cast<const __bf16*>(lds + L.w1), SA, cb * 32, lane);
-    } else {
-      const float* Ap[2] = {abuf + (r0 + li) * SA + 4 * h, abuf + (TM + r0 + li) * SA + 4 * h};
-      mma_f32<2, false, KP>(acc, Ap, reinterpret_cast<const float*>(lds + L.w1), SW, cb * 32, lane);
-    }
-    __syncthreads();
-    // s = ssp(a) -> LDS; keep sigmoid(a) in acc[0] and v in acc[1]
+    for (int q = 0; q < 2; ++q)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = out_row(r0, r, h);
-      float s, sg;
-      ssp_sig(acc[0][r] + bias1, s, sg);
-      acc[0][r] = sg;
-      if constexpr (BF16) hbuf[row * SH + c] = (__bf16)s;
-      else abuf[row * SQ + c] = s;
-    }
-    __syncthreads();
-    f32x16 accw[1] = {f32x16{}};
-    if constexpr (BF16) {
-      const __bf16* Ap[1] = {hbuf + (r0 + li) * SH + 8 * h};
-      mma_bf16<1, D>(accw, Ap, reinterpret_cast<const __bf16*>(lds + L.w2), SH, cb * 32, lane);
-    } else {
-      const float* Ap[1] = {abuf + (r0 + li) * SQ + 4 * h};
-      mma_f32<1, false, D>(accw, Ap, reinterpret_cast<const float*>(lds + L.w2), SW, cb * 32, lane);
-    }
-    // gathers; q = dE/dh_j * w (source sum), g_w = dE/dh_i * x_j + dE/dh_j * x_i (both directions)
-    // receiver rows: all 32 loads are issued before any is used (masks are
-    // arithmetic, so no load sits behind a branch)
-    float gw[16], xr[16], gr[16];
+      for (int nb = 0; nb < NB; ++nb) av[q][nb] = f32x16{};
+    gemm1<D, KP, BF16, 2>(av, lds, p, g, lane);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const uint32_t oi = ((uint32_t)geoi[G_I * TM + out_row(r0, r, h)] * D + c) * 4u;
-      xr[r] = bload(rx, oi);
-      gr[r] = bload(rgh, oi);
-    }
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float mk = geoi[G_IN * TM + out_row(r0, r, h)] ? 1.f : 0.f;
-      const float w = mk * (accw[0][r] + bias2);
-      accw[0][r] = gg[r] * w;
-      gw[r] = mk * (gr[r] * xg[r] + gg[r] * xr[r]);
-    }
-    __syncthreads();
-    const TileSegs t = tile_segs<TM>(RP, geoi, ts, te, cur);
-    if (want_gx) {
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 c1 = bias4<P>(p, lds, h4, 32 * nb + 8 * q);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) abuf[out_row(r0, r, h) * SQ + c] = accw[0][r];
-      __syncthreads();
-      seg_sum_cols<D, SQ>(RP, t, ts, te, abuf, qcarry + par * D, qcarry + (1 - par) * D,
-                          [&](int i, int cc, float v) {
-                            const size_t o = (size_t)i * D + cc;
-                            p.gx_out[o] = p.gx_in[o] + v;
-                          });
-      __syncthreads();
-    }
-    // g_w -> LDS, GEMM3: g_s = g_w Wf2^T
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = out_row(r0, r, h);
-      if constexpr (BF16) hbuf[row * SH + c] = (__bf16)gw[r];
-      else abuf[row * SQ + c] = gw[r];
-    }
-    __syncthreads();
-    f32x16 accg[1] = {f32x16{}};
-    if constexpr (BF16) {
-      const __bf16* Ap[1] = {hbuf + (r0 + li) * SH + 8 * h};
-      mma_bf16<1, D>(accg, Ap, reinterpret_cast<const __bf16*>(lds + L.w2n), SH, cb * 32, lane);
-    } else {
-      const float* Ap[1] = {abuf + (r0 + li) * SQ + 4 * h};
-      mma_f32<1, true, D>(accg, Ap, reinterpret_cast<const float*>(lds + L.w2), SW, cb * 32, lane);
-    }
-    __syncthreads();
-    // p = g_s * sigmoid(a) * v, summed over features per edge -> dE/dd
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      abuf[out_row(r0, r, h) * SQ + c] = accg[0][r] * acc[0][r] * acc[1][r];
-    __syncthreads();
-    {
-      const int r = tid / TPR, part = tid - r * TPR;
-      float s = 0.f;
-      const float* rowp = abuf + r * SQ + part * (D / TPR);
-#pragma unroll
-      for (int k = 0; k < D / TPR; ++k) s += rowp[k];
-#pragma unroll
-      for (int o = 1; o < TPR; o <<= 1) s += __shfl_xor(s, o, 64);
-      if (part == 0) {
-        const float gd = geoi[G_IN * TM + r] ? s * geo[G_INVD * TM + r] : 0.f;
-        geo[G_FX * TM + r] = gd * geo[G_UX * TM + r];
-        geo[G_FY * TM + r] = gd * geo[G_UY * TM + r];
-        geo[G_FZ * TM + r] = gd * geo[G_UZ * TM + r];
-      }
-    }
-    __syncthreads();
-    // force rows: one thread per (receiver, component)
-    {
-      float* fin = fcarry + par * 4;
-      float* fout = fcarry + (1 - par) * 4;
-      const int comp = tid & 3;
-      for (int k = tid >> 2; k < t.nseg && comp < 3; k += kCfThreads / 4) {
-        const int i = t.first + k;
-        const int rs = RP(i), re = RP(i + 1);
-        const int lo = (rs > ts ? rs : ts) - ts, hi = (re < te ? re : te) - ts;
-        float s = 0.f;
-        for (int r = lo; r < hi; ++r) s += geo[(G_FX + comp) * TM + r];
-        if (k == 0) s += fin[comp];
-        if (k == t.nseg - 1) {
-          if (t.last_open) {
-            fout[comp] = s;
-            continue;
-          }
-          fout[comp] = 0.f;
+        for (int t = 0; t < 4; ++t) {
+          const int r = 4 * q + t;
+          float sv, sg;
+          ssp_sig(av[0][nb][r] + c1[t], sv, sg);
+          av[0][nb][r] = sv;
+          // materialised here: sunk towards its use in the tangent product,
+          // the gate's temporaries would stay live through the value product
+          float gv = sg * av[1][nb][r];
+          asm volatile("" : "+v"(gv));
+          av[1][nb][r] = gv;
         }
-        float* f = p.forces + (size_t)i * 3 + comp;
-        *f = (p.force_accumulate ? *f : 0.f) - s;
+      }
+    pjx = bload(wk.rpos, (uint32_t)jn * 12u);
+    pjy = bload(wk.rpos, (uint32_t)jn * 12u + 4);
+    pjz = bload(wk.rpos, (uint32_t)jn * 12u + 8);
+    // GEMM2 for the values, all output blocks (frees s): w = s Wf2
+    f32x16 wv[NB];
+    {
+      const Operand<D, BF16> os(av[0]);
+      const Operand<D, BF16>* const ops[1] = {&os};
+      const int lane_o = opaque(lane), ho = lane_o >> 5, lio = lane_o & 31;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        f32x16 acc[1] = {f32x16{}};
+        gemm_om_block<D, BF16, 1>(acc, ops, lds + P::W2, nb, ho, lio);
+        wv[nb] = acc[0];
       }
     }
-    cur = t.last_open ? t.last : t.last + 1;
-    par = 1 - par;
-    __syncthreads();
+    const Operand<D, BF16> ot(av[1]);
+    const Operand<D, BF16>* const opt[1] = {&ot};
+
+    // per output block: tangent w' = s' Wf2 (GEMM2 again, one block live);
+    // q = dE/dh_j w summed per receiver (two blocks at a time);
+    // dE/dd += <dE/dh_i x_j + dE/dh_j x_i, w'>
+    const uint32_t jo = ((uint32_t)th.j * (uint32_t)D + (uint32_t)h4) * 4u;
+    const uint32_t io = ((uint32_t)th.recv * (uint32_t)D + (uint32_t)h4) * 4u;
+    float gdd = 0.f;
+#pragma unroll
+    for (int pr = 0; pr < NB / 2; ++pr) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int nb = 2 * pr + b;
+        // one output block in flight: hoisted, the gathers of every block
+        // would be live at once
+        __builtin_amdgcn_sched_barrier(0);
+        const int lane_o = opaque(lane), ho = lane_o >> 5, lio = lane_o & 31;
+        f32x16 wt[1] = {f32x16{}};
+        gemm_om_block<D, BF16, 1>(wt, opt, lds + P::W2, nb, ho, lio);
+        float qv[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          // gathers in two halves of 32 registers (the first may run ahead
+          // of the block's product)
+          if (q == 2) __builtin_amdgcn_sched_barrier(0);
+          const int col = 32 * nb + 8 * q;   // + h4
+          const f32x4 xj = bload4(rx, jo + (uint32_t)col * 4u);
+          const f32x4 gj = bload4(rgh, jo + (uint32_t)col * 4u);
+          const f32x4 xi = bload4(rx, io + (uint32_t)col * 4u);
+          const f32x4 gi = bload4(rgh, io + (uint32_t)col * 4u);
+          const f32x4 c2 = bias4<P>(p, lds, h4, D + col);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int r = 4 * q + t;
+            qv[r] = gj[t] * (g.in * (wv[nb][r] + c2[t]));
+            gdd = fmaf(gi[t] * xj[t] + gj[t] * xi[t], wt[0][r], gdd);
+          }
+        }
+        if (want_q) tile_put(Tb, b, qv, lane);
+      }
+      if (want_q) {
+        wave_sync();
+        float* qout = p.q_out + 64 * pr + lane;
+        column_segments(p, Tb, win, cur, ib, th.nfin, ts, th.len, th.ncur < ib, carry[pr], lane,
+                        [&](int i, float tot) { qout[(size_t)i * D] = tot; });
+        wave_sync();
+      }
+    }
+    gdd += __shfl_xor(gdd, 32, 64);
+    const float gd = upper ? 0.f : gdd * g.invd * g.in;
+    const float fx = gd * g.ux, fy = gd * g.uy, fz = gd * g.uz;
+
+    // this block's dE/dr rows, one per receiver of the tile
+    {
+      int s0 = ss;
+      for (int l = 0; l < th.nfin; ++l) {
+        const int be = seg_end(p, win, cur, ib, l);
+        const int lo = (s0 > ts ? s0 : ts) - ts, hi = be - ts;
+        float sx = lane_range_sum(fx, li, lo, hi);
+        float sy = lane_range_sum(fy, li, lo, hi);
+        float sz = lane_range_sum(fz, li, lo, hi);
+        if (l == 0) {
+          sx += fcx; sy += fcy; sz += fcz;
+        }
+        if (lane == 0) {
+          float* f = p.forces + (size_t)(cur + l) * 3;
+          f[0] = sx; f[1] = sy; f[2] = sz;
+        }
+        s0 = be;
+      }
+      if (th.ncur < ib) {
+        const int lo = (s0 > ts ? s0 : ts) - ts;
+        const float sx = lane_range_sum(fx, li, lo, th.len);
+        const float sy = lane_range_sum(fy, li, lo, th.len);
+        const float sz = lane_range_sum(fz, li, lo, th.len);
+        if (th.nfin == 0) {
+          fcx += sx; fcy += sy; fcz += sz;
+        } else {
+          fcx = sx; fcy = sy; fcz = sz;
+        }
+      } else {
+        fcx = fcy = fcz = 0.f;
+      }
+      ss = s0;
+    }
+    cur = th.ncur;
+    win = th.win_next;
   }
-  for (int idx = tid; idx < (ib - cur) * D; idx += kCfThreads) {
-    const size_t o = (size_t)cur * D + idx;
-    if (want_gx) p.gx_out[o] = p.gx_in[o];
+  // receivers of a worker without edges
+  for (int i = cur; i < ib; ++i) {
+    if (want_q)
+      for (int c = lane; c < D; c += 64) p.q_out[(size_t)i * D + c] = 0.f;
+    if (lane < 3) p.forces[(size_t)i * 3 + lane] = 0.f;
   }
-  if (!p.force_accumulate)
-    for (int idx = tid; idx < (ib - cur) * 3; idx += kCfThreads) p.forces[(size_t)cur * 3 + idx] = 0.f;
-  };
-  if (rpl == ib - ia + 1) tiles(std::true_type{});
-  else tiles(std::false_type{});
 }
 
-// ------------------------------------------------------------------ partition
-// Work-group w owns receivers [wg_start[w], wg_start[w+1]); boundaries split
-// the monotone key rowptr[i] + i (edges plus one unit per receiver) evenly.
+// ------------------------------------------------------------------ small kernels
+// Worker w owns receivers [wg_start[w], wg_start[w+1]); boundaries split the
+// monotone key rowptr[i] + i (edges plus one unit per receiver) evenly.
 __global__ void k_partition(const int32_t* rowptr, int N, int G, int32_t* wg_start) {
   const int w = blockIdx.x * blockDim.x + threadIdx.x;
   if (w > G) return;
@@ -726,56 +791,80 @@ hipError_t launch_partition(const int32_t* rowptr, int n_atoms, int G, int32_t* 
   return hipGetLastError();
 }
 
+// F_i = -(sum over blocks of dE/dr_i)
+__global__ __launch_bounds__(kThreads) void k_force_sum(const float* fb, int T, int64_t n3,
+                                                        float* forces) {
+  const int64_t k = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (k >= n3) return;
+  float s = 0.f;
+  for (int t = 0; t < T; ++t) s += fb[(int64_t)t * n3 + k];
+  forces[k] = -s;
+}
+
+hipError_t launch_force_sum(const float* fb, int T, int64_t n_atoms, float* forces, hipStream_t s) {
+  const int64_t n3 = 3 * n_atoms;
+  hipLaunchKernelGGL(k_force_sum, dim3((unsigned)((n3 + kThreads - 1) / kThreads)), dim3(kThreads),
+                     0, s, fb, T, n3, forces);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ dispatch
 template <int D, int KP, bool BF16>
-static hipError_t set_lds_limit_one() {
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_cf_fwd<D, KP, BF16>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-  if (e != hipSuccess) return e;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_cf_bwd<D, KP, BF16>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-}
+struct CfKernels {
+  using P = Plan<D, KP, BF16>;
+  static hipError_t prepare() {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_cf_fwd<D, KP, BF16>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, P::TOTAL);
+    if (e != hipSuccess) return e;
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_cf_bwd<D, KP, BF16>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, P::TOTAL);
+  }
+  static size_t image_bytes() { return P::IMG; }
+  static void fill(int Dr, const float* Wf1, const float* cf1, const float* Wf2, const float* cf2,
+                   unsigned char* out) {
+    fill_image<D, KP, BF16>(Dr, Wf1, cf1, Wf2, cf2, out);
+  }
+  static hipError_t fwd(const CfParams& p, int G, hipStream_t s) {
+    hipLaunchKernelGGL((k_cf_fwd<D, KP, BF16>), dim3(G), dim3(P::NT), P::TOTAL, s, p);
+    return hipGetLastError();
+  }
+  static hipError_t bwd(const CfParams& p, int G, hipStream_t s) {
+    hipLaunchKernelGGL((k_cf_bwd<D, KP, BF16>), dim3(G), dim3(P::NT), P::TOTAL, s, p);
+    return hipGetLastError();
+  }
+};
 
-template <template <int, int, bool> class Fn>
-static hipError_t cf_dispatch(int D, int KP, int bf16, typename Fn<64, 32, false>::Arg a) {
-#define SN_CF(DD, KK, BB) if (D == DD && KP == KK && (bf16 != 0) == BB) return Fn<DD, KK, BB>::run(a);
-  SN_CF(64, 32, false) SN_CF(64, 56, false) SN_CF(64, 64, false)
-  SN_CF(128, 32, false) SN_CF(128, 56, false) SN_CF(128, 64, false)
+template <class R, class F>
+static R cf_dispatch(int D, int KP, int bf16, R fail, F f) {
+#define SN_CF(DD, KK, BB) \
+  if (D == DD && KP == KK && (bf16 != 0) == BB) return f(CfKernels<DD, KK, BB>{});
+  SN_CF(64, 32, false) SN_CF(64, 64, false) SN_CF(128, 32, false) SN_CF(128, 64, false)
   SN_CF(64, 32, true) SN_CF(64, 64, true) SN_CF(128, 32, true) SN_CF(128, 64, true)
 #undef SN_CF
-  return hipErrorInvalidValue;
+  return fail;
 }
 
-struct LaunchArg { const CfParams* p; int G; hipStream_t s; };
-template <int D, int KP, bool BF16> struct PrepFn {
-  using Arg = int;
-  static hipError_t run(int) { return set_lds_limit_one<D, KP, BF16>(); }
-};
-template <int D, int KP, bool BF16> struct FwdFn {
-  using Arg = LaunchArg;
-  static hipError_t run(LaunchArg a) {
-    hipLaunchKernelGGL((k_cf_fwd<D, KP, BF16>), dim3(a.G), dim3(kCfThreads),
-                       cf_lds_bytes(D, KP, BF16, 0), a.s, *a.p);
-    return hipGetLastError();
-  }
-};
-template <int D, int KP, bool BF16> struct BwdFn {
-  using Arg = LaunchArg;
-  static hipError_t run(LaunchArg a) {
-    hipLaunchKernelGGL((k_cf_bwd<D, KP, BF16>), dim3(a.G), dim3(kCfThreads),
-                       cf_lds_bytes(D, KP, BF16, 1), a.s, *a.p);
-    return hipGetLastError();
-  }
-};
-
-hipError_t cf_prepare(int D, int KP, int bf16) { return cf_dispatch<PrepFn>(D, KP, bf16, 0); }
-
-hipError_t launch_cf_forward(int D, int bf16, const CfParams& p, int G, hipStream_t s) {
-  return cf_dispatch<FwdFn>(D, p.KP, bf16, LaunchArg{&p, G, s});
+hipError_t cf_prepare(int D, int KP, int bf16) {
+  return cf_dispatch(D, KP, bf16, hipErrorInvalidValue,
+                     [](auto k) { return decltype(k)::prepare(); });
 }
-
-hipError_t launch_cf_backward(int D, int bf16, const CfParams& p, int G, hipStream_t s) {
-  return cf_dispatch<BwdFn>(D, p.KP, bf16, LaunchArg{&p, G, s});
+size_t cf_image_bytes(int D, int KP, int bf16) {
+  return cf_dispatch(D, KP, bf16, (size_t)0, [](auto k) { return decltype(k)::image_bytes(); });
+}
+void cf_fill_image(int D, int KP, int bf16, int Dr, const float* Wf1, const float* cf1,
+                   const float* Wf2, const float* cf2, unsigned char* out) {
+  cf_dispatch(D, KP, bf16, 0, [&](auto k) {
+    decltype(k)::fill(Dr, Wf1, cf1, Wf2, cf2, out);
+    return 0;
+  });
+}
+hipError_t launch_cf_forward(int D, int KP, int bf16, const CfParams& p, int G, hipStream_t s) {
+  return cf_dispatch(D, KP, bf16, hipErrorInvalidValue,
+                     [&](auto k) { return decltype(k)::fwd(p, G, s); });
+}
+hipError_t launch_cf_backward(int D, int KP, int bf16, const CfParams& p, int G, hipStream_t s) {
+  return cf_dispatch(D, KP, bf16, hipErrorInvalidValue,
+                     [&](auto k) { return decltype(k)::bwd(p, G, s); });
 }
 
 } // namespace sn

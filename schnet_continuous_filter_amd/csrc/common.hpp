@@ -14,8 +14,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 namespace sn {
 
 constexpr int kThreads = 256;  // every kernel of the library runs 4 wave64 per block
-constexpr int kTileEdges = 64; // edges per CFConv tile (two 32-row MFMA blocks)
-constexpr int kTileAtoms = 64; // atoms per atom-wise GEMM tile
 constexpr int kMaxGrid = 4096; // upper bound on CFConv work-groups (partition table size)
 constexpr int kCellsPerAxisMax = 64;
 constexpr int kScanChunk = 1024; // elements per block of the device scan
@@ -32,6 +30,14 @@ struct DevStatus {
   int64_t pad[3];
 };
 
+// Round-to-nearest-even bfloat16 bits of a finite float (host side).
+inline uint16_t bf16_rne_bits(float f) {
+  uint32_t u;
+  __builtin_memcpy(&u, &f, 4);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
 __device__ inline void dev_fail(DevStatus* st, int code, int64_t detail) {
   if (atomicCAS(&st->status, 0, code) == 0) st->detail = detail;
 }
@@ -39,7 +45,7 @@ __device__ inline void dev_fail(DevStatus* st, int code, int64_t detail) {
 // Offsets (bytes) of everything carved out of a workspace.
 struct WsLayout {
   size_t status, wg_start, scan_blocks, cell_count, cell_start, cell_atoms, atom_cell;
-  size_t x, au, gbuf, tmp, gx, eps, total;
+  size_t x, au, gbuf, tmp, gx, fblk, eps, total;
 };
 WsLayout ws_layout(int64_t n_atoms, int D, int T, int H);
 
@@ -73,39 +79,37 @@ struct CfParams {
   float box, half_box;
   float rbf_min, rbf_step, rbf_coef2, rbf_inv_s2; // coef2 = -log2(e)/(2 sigma^2), inv_s2 = 1/sigma^2
   float r_cut, pi_over_rc;
-  int Dr, KP;
-  // fp32 filter weights (row-major [fan_in][fan_out])
-  const float* Wf1;
-  const float* cf1;
-  const float* Wf2;
-  const float* cf2;
-  // bf16 filter weights: W1t[D][KP] (= Wf1 transposed, K zero-padded), W2t[D][D] (= Wf2
-  // transposed), W2n[D][D] (= Wf2)
-  const uint16_t* W1t;
-  const uint16_t* W2t;
-  const uint16_t* W2n;
+  int KC;             // basis chunks the first filter product runs over (cf_chunks)
+  const void* img;    // this block's filter weights and biases as laid out in LDS (cf_fill_image)
   const float* x;     // x^(t) [N][D]
   float* h;           // forward output [N][D]
   const float* gh;    // backward: dE/dh^(t) [N][D]
-  const float* gx_in; // backward: dE/dx^(t+1) [N][D]
-  float* gx_out;      // backward: dE/dx^(t) [N][D], or null for the first block
-  float* forces;      // backward: F [N][3]
-  int force_accumulate;
+  float* q_out;       // backward: sum_j dE/dh_j w_ij [N][D], or null for the first block
+  float* forces;      // backward: this block's dE/dr [N][3]
 };
 
-int cf_kp(int Dr, int bf16);               // padded basis length used by the kernels
-size_t cf_lds_bytes(int D, int KP, int bf16, int backward);
+int cf_kp(int Dr, int bf16);               // basis length the LDS images are padded to
+int cf_chunks(int Dr, int bf16);           // basis chunks (8 fp32 / 16 bf16 basis functions each)
+int cf_workers(int bf16);                  // waves (independent workers) per work-group
 hipError_t cf_prepare(int D, int KP, int bf16);  // raises the dynamic LDS limit of the kernels
+// Filter-weight image of one interaction block as the CFConv kernels hold it
+// in LDS: cf_image_bytes bytes, filled on the host.
+size_t cf_image_bytes(int D, int KP, int bf16);
+void cf_fill_image(int D, int KP, int bf16, int Dr, const float* Wf1, const float* cf1,
+                   const float* Wf2, const float* cf2, unsigned char* out);
+hipError_t launch_force_sum(const float* fb, int T, int64_t n_atoms, float* forces, hipStream_t s);
 hipError_t launch_partition(const int32_t* rowptr, int n_atoms, int G, int32_t* wg_start,
                             hipStream_t s);
-hipError_t launch_cf_forward(int D, int bf16, const CfParams& p, int G, hipStream_t s);
-hipError_t launch_cf_backward(int D, int bf16, const CfParams& p, int G, hipStream_t s);
+hipError_t launch_cf_forward(int D, int KP, int bf16, const CfParams& p, int G, hipStream_t s);
+hipError_t launch_cf_backward(int D, int KP, int bf16, const CfParams& p, int G, hipStream_t s);
 
 enum AtomMode { ATOM_UPDATE_FWD = 0, ATOM_UPDATE_BWD = 1, ATOM_READOUT = 2 };
 struct AtomArgs {
   int mode;
   int M;              // atoms
   const float* A;     // [M][D]: h (update fwd), dE/dx' (update bwd), x^(T) (readout)
+  const float* A2;    // update bwd: added to A when not null (the CFConv source sum)
+  float* Asum;        // update bwd: A + A2 is stored here when not null
   const float* W1;    // first product, row-major [D][N1]
   const float* b1;    // [N1] (update fwd, readout)
   const float* W2;    // second product, row-major [N1][D]
