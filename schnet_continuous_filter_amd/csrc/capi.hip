@@ -94,13 +94,13 @@ struct ProfScope {
 };
 
 // ---------------------------------------------------------------- E+F orchestration
-// Work-groups for the CFConv kernels: one per CU for large systems (their LDS
-// plan allows one resident group), fewer for small ones so that every worker
+// Work-groups for a CFConv kernel: one per CU for large systems (its LDS plan
+// allows one resident group), fewer for small ones so that every worker
 // (wave) gets a few receivers.
 int cf_grid(const sn_model* m, int64_t n, int workers) {
   int64_t g = (n + 4 * workers - 1) / (4 * workers);
   if (g > m->n_cu) g = m->n_cu;
-  if (g * workers > kMaxGrid) g = kMaxGrid / workers;
+  if (g * workers > kMaxWorkers) g = kMaxWorkers / workers;
   return (int)(g < 1 ? 1 : g);
 }
 
@@ -113,6 +113,7 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
   const WsLayout L = ws_layout(n, D, T, H);
   DevStatus* st = reinterpret_cast<DevStatus*>(ws + L.status);
   int32_t* wg_start = reinterpret_cast<int32_t*>(ws + L.wg_start);
+  int32_t* wg_start_b = reinterpret_cast<int32_t*>(ws + L.wg_start_b);
   float* x = reinterpret_cast<float*>(ws + L.x);
   float* au = reinterpret_cast<float*>(ws + L.au);
   float* gbuf = reinterpret_cast<float*>(ws + L.gbuf);
@@ -122,11 +123,13 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
   float* fblk = reinterpret_cast<float*>(ws + L.fblk);
   const size_t ND = (size_t)n * D;
   const int bf16 = d.filter_dtype == SN_FILTER_BF16;
-  const int workers = cf_workers(bf16);
-  const int G = cf_grid(m, n, workers);
+  const int wf = cf_workers(D, m->KP, bf16, 0), wb = cf_workers(D, m->KP, bf16, 1);
+  const int Gf = cf_grid(m, n, wf), Gb = cf_grid(m, n, wb);
   hipError_t e;
 
-  if ((e = launch_partition(rowptr, (int)n, G * workers, wg_start, s)) != hipSuccess)
+  if ((e = launch_partition(rowptr, (int)n, Gf * wf, wg_start, s)) != hipSuccess)
+    return hip_fail(e);
+  if ((e = launch_partition(rowptr, (int)n, Gb * wb, wg_start_b, s)) != hipSuccess)
     return hip_fail(e);
   if ((e = launch_embed(types, m->w + m->off_emb, (int)n, D, d.n_types, x, st, s)) != hipSuccess)
     return hip_fail(e);
@@ -168,11 +171,12 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
   // forward
   for (int t = 0; t < T; ++t) {
     p.img = block_img(t);
+    p.wg_start = wg_start;
     p.x = x + t * ND;
     p.h = gbuf;
     {
       ProfScope ps(0, s);
-      if ((e = launch_cf_forward(D, m->KP, bf16, p, G, s)) != hipSuccess) return hip_fail(e);
+      if ((e = launch_cf_forward(D, m->KP, bf16, p, Gf, s)) != hipSuccess) return hip_fail(e);
     }
     AtomArgs u{ATOM_UPDATE_FWD, (int)n, gbuf, nullptr, nullptr, Wu(t, 0), Wu(t, 1), Wu(t, 2),
                Wu(t, 3), x + t * ND, nullptr, au + t * ND, x + (t + 1) * ND, nullptr, 0.f, nullptr};
@@ -195,13 +199,14 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
                nullptr, 0.f, nullptr};
     if ((e = launch_atom(b, D, D, m->n_cu, s)) != hipSuccess) return hip_fail(e);
     p.img = block_img(t);
+    p.wg_start = wg_start_b;
     p.x = x + t * ND;
     p.gh = gbuf;
     p.q_out = t > 0 ? tmp : nullptr;
     p.forces = fblk + (size_t)t * n * 3;
     {
       ProfScope ps(1, s);
-      if ((e = launch_cf_backward(D, m->KP, bf16, p, G, s)) != hipSuccess) return hip_fail(e);
+      if ((e = launch_cf_backward(D, m->KP, bf16, p, Gb, s)) != hipSuccess) return hip_fail(e);
     }
   }
   if ((e = launch_force_sum(fblk, T, n, forces, s)) != hipSuccess) return hip_fail(e);
@@ -280,7 +285,8 @@ WsLayout ws_layout(int64_t n, int D, int T, int H) {
   const int64_t ncell = (int64_t)kCellsPerAxisMax * kCellsPerAxisMax * kCellsPerAxisMax;
   const int64_t scan_n = (n > ncell ? n : ncell) + 1;
   L.status = take(sizeof(DevStatus));
-  L.wg_start = take((size_t)(kMaxGrid + 1) * 4);
+  L.wg_start = take((size_t)(kMaxWorkers + 1) * 4);
+  L.wg_start_b = take((size_t)(kMaxWorkers + 1) * 4);
   L.scan_blocks = take((size_t)(scan_n / kScanChunk + 2) * 8);
   L.cell_count = take((size_t)(ncell + 1) * 4);
   L.cell_start = take((size_t)ncell * 4);

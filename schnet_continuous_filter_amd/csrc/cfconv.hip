@@ -9,31 +9,31 @@
 // source features, and §3.2 "Forces via autodiff" the force as the negative
 // position gradient.
 //
-// Work decomposition. Every wave is an independent worker: a work-group of
-// eight waves (two per SIMD) copies the filter weights into LDS once, which is
-// its only barrier; then each wave walks its own contiguous range of receivers
-// (k_partition balances edges + receivers over the workers) in tiles of 32
-// edges.
+// Work decomposition. Every wave is an independent worker: a work-group
+// copies the filter weights into LDS once, which is its only barrier; then
+// each of its waves walks its own contiguous range of receivers (k_partition
+// balances edges + receivers over the workers) in tiles of 16 edges.
 //
 // Edge-on-lane products. Every product is computed transposed,
-// OUT^T[n][e] = sum_k W^T[n][k] IN^T[k][e]: the weights (rows n) are the MFMA A
-// operand, read from LDS, and the per-edge activations are the B operand, one
-// edge per lane column. The accumulator layout of one product (rows = features
-// in registers, lane = edge) is then exactly the B-operand layout of the next,
-// so basis -> GEMM1 -> shifted softplus -> GEMM2 (-> GEMM3 in the backward)
-// never leaves registers; the k index inside each MFMA is permuted to match the
-// accumulator rows a lane holds, and the weight images in LDS are laid out
-// (XOR-swizzled, permuted for bf16) so that every A operand is one 16-byte
-// read. Each lane also computes its own edge's geometry and basis and gathers
-// its own sender/receiver feature rows with 16-byte loads.
+// OUT^T[n][e] = sum_k W^T[n][k] IN^T[k][e], on 16x16 MFMA blocks: the weights
+// (rows n) are the A operand, read from LDS, and the per-edge activations the
+// B operand, one edge per lane column (lane = e + 16 g; the four lane groups g
+// hold different feature rows). The accumulator layout of one product (lane
+// group g holds features 4g..4g+3 of each 16-feature block) is then exactly
+// the B-operand layout of the next, so basis -> GEMM1 -> shifted softplus ->
+// GEMM2 never leaves registers. The k index inside each MFMA is permuted to
+// match the rows a lane holds, and the weight images in LDS are laid out
+// (XOR-swizzled, permuted for bf16) so that every A operand is one 8- or
+// 16-byte read. Each lane computes its own edge's geometry and basis and
+// gathers its own sender/receiver feature rows with 16-byte loads.
 //
-// Aggregation. The per-receiver sum runs over edges, i.e. across lanes: each
-// 32-column block of messages is transposed through a small per-wave LDS tile,
-// after which every lane holds one column for 16 edges, and the contiguous
-// CSR segments of the tile are summed in registers. A receiver still open at
-// the tile's end carries its partial sum into the next tile. The segment ends
-// of the next 64 receivers come from one lane-parallel load per tile. Nothing
-// edge-sized reaches HBM and every output row has exactly one writer.
+// Aggregation. The per-receiver sum runs over edges, i.e. across lanes: 64
+// features of messages at a time are transposed through a 4 KiB per-wave LDS
+// tile so that every lane holds one feature for the tile's 16 edges, and a
+// segmented scan down that column yields each receiver's sum. A receiver still
+// open at the tile's end carries its partial sum into the next tile. The
+// segment ends of the next 64 receivers come from one lane-parallel load per
+// tile. Nothing edge-sized reaches HBM and every output row has one writer.
 //
 // Backward (forces). The neighbour list is symmetric and w_ij = w_ji, so the
 // owner of receiver i produces, from its own row alone,
@@ -44,12 +44,12 @@
 //   dE/dr_i   = sum_j dE/dd_ij (r_i - r_j) / d_ij
 // dw/dd is carried forward through the recomputed filter (forward-mode along
 // the single scalar d): a' = (d b~/dd) Wf1, s' = sigmoid(a) a', w' = s' Wf2.
-// The tangents ride in the same products as the values (second B operand,
-// same weight reads), so the backward needs no transposed product and lands
-// dE/dd on the edge's own lane. Each interaction block writes its own force
-// rows; a small kernel sums the blocks.
+// The tangents go through the same products as the values (same weight
+// images), so the backward needs no transposed product and lands dE/dd on the
+// edge's own lanes. Each interaction block writes its own force rows; a small
+// kernel sums the blocks.
 //
-// MFMA: v_mfma_f32_32x32x2_f32 (fp32 filters), v_mfma_f32_32x32x16_bf16
+// MFMA: v_mfma_f32_16x16x4_f32 (fp32 filters), v_mfma_f32_16x16x32_bf16
 // (bfloat16 filters, fp32 accumulation).
 #include <climits>
 #include <cstring>
@@ -61,7 +61,7 @@ namespace sn {
 #define LN2F 0.69314718055994530942f
 #define LOG2EF 1.44269504088896340736f
 
-constexpr int kEdges = 32;  // edges per wave tile: the MFMA column dimension
+constexpr int kEdges = 16;  // edges per wave tile: the MFMA column dimension
 
 // ------------------------------------------------------------------ small helpers
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
@@ -121,43 +121,50 @@ __device__ __forceinline__ float min_image(float u, float box, float half) {
   return u;
 }
 
+__device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 // XOR-swizzled offset of element (row, col) of a row-major array with RL
 // elements per row: 16-byte chunks (4 fp32 or 8 bf16) trade places by row, so
-// 16-byte reads down a column and 4-byte reads along a row are conflict-free.
+// that the 16 rows one lane group reads at a common column hit distinct banks.
 template <int RL>
 __host__ __device__ __forceinline__ int sw4(int row, int col) {
-  constexpr int M = (RL / 4 >= 8) ? 7 : RL / 4 - 1;
+  constexpr int M = (RL / 4 >= 16) ? 15 : RL / 4 - 1;
   return row * RL + ((((col >> 2) ^ (row & M)) << 2) | (col & 3));
 }
 template <int RL>
 __host__ __device__ __forceinline__ int sw8(int row, int col) {
-  constexpr int M = (RL / 8 >= 8) ? 7 : RL / 8 - 1;
+  constexpr int M = (RL / 8 >= 16) ? 15 : RL / 8 - 1;
   return row * RL + ((((col >> 3) ^ (row & M)) << 3) | (col & 7));
 }
-// bf16 images: position of contraction index k inside its group of 16 (bits 2
-// and 3 swapped), so that lane half h finds the 8 k values its accumulator
-// rows hold (4h..4h+3, 8+4h..8+4h+3) in one 16-byte run.
-__host__ __device__ constexpr int perm16(int k) {
-  return (k & ~15) | (k & 3) | ((k & 4) << 1) | ((k & 8) >> 1);
+// bf16 chained products: position of contraction index k in its group of 32,
+// so that lane group g finds the 8 k values its accumulator rows hold
+// (4g..4g+3 of two consecutive 16-feature blocks) in one 16-byte run.
+__host__ __device__ constexpr int perm32(int k) {
+  return (k & ~31) | (((k >> 2) & 3) << 3) | (((k >> 4) & 1) << 2) | (k & 3);
 }
 
 // ------------------------------------------------------------------ LDS plan
 // Weight image (built on the host, copied verbatim) then one transpose tile per wave.
 //   W1  : Wf1^T [D][KP] (k zero-padded past Dr)
-//   W2  : Wf2^T [D][D]
+//   W2  : Wf2^T [D][D] (bf16: positions permuted by perm32)
 //   BIAS: cf1[D], cf2[D] (fp32); staged only where LDS has room, else read
 //         from the image in global memory
 // Rows are output-major: the A operand of a lane is a run of its row.
-template <int D, int KP, bool BF16>
+template <int D, int KP, bool BF16, int NW_>
 struct Plan {
-  static constexpr int NW = 8;                 // workers (waves) per work-group
+  static constexpr int NW = NW_;               // workers (waves) per work-group
   static constexpr int NT = NW * 64;
   static constexpr int ES = BF16 ? 2 : 4;
   static constexpr int W1 = 0;
   static constexpr int W2 = W1 + D * KP * ES;
   static constexpr int BIAS = W2 + D * D * ES;
   static constexpr int IMG = BIAS + 2 * D * 4;
-  static constexpr int TB = kEdges * 64 * 4;   // transpose tile: 64 columns of 32 rows
+  static constexpr int TB = kEdges * 64 * 4;   // transpose tile: 64 columns of 16 rows
   static constexpr int LDS_MAX = 160 * 1024;
   static constexpr bool BIAS_LDS = IMG + NW * TB <= LDS_MAX;
   static constexpr int STAGE = BIAS_LDS ? IMG : BIAS;   // bytes copied into LDS
@@ -166,20 +173,24 @@ struct Plan {
   static_assert(TOTAL <= LDS_MAX, "LDS plan exceeds 160 KiB");
 };
 
+// Waves per work-group of each kernel at one work-group per CU: the forward
+// fits 128 registers (four waves per SIMD); the backward needs up to 256 at
+// D = 128 (two per SIMD; at three it spills and runs slower).
+template <int D, bool BF16, bool BWD>
+constexpr int cf_nw() {
+  return BWD ? 8 : 16;
+}
+
 int cf_kp(int Dr, int bf16) {
   (void)bf16;
   return Dr <= 32 ? 32 : 64;
 }
-int cf_workers(int bf16) {
-  (void)bf16;
-  return 8;
-}
-int cf_chunks(int Dr, int bf16) { return bf16 ? (Dr + 15) / 16 : (Dr + 7) / 8; }
+int cf_chunks(int Dr, int bf16) { return bf16 ? (Dr + 31) / 32 : (Dr + 7) / 8; }
 
 template <int D, int KP, bool BF16>
 static void fill_image(int Dr, const float* Wf1, const float* cf1, const float* Wf2,
                        const float* cf2, unsigned char* out) {
-  using P = Plan<D, KP, BF16>;
+  using P = Plan<D, KP, BF16, 1>;
   std::memset(out, 0, P::IMG);
   if constexpr (BF16) {
     uint16_t* w1 = reinterpret_cast<uint16_t*>(out + P::W1);
@@ -187,7 +198,7 @@ static void fill_image(int Dr, const float* Wf1, const float* cf1, const float* 
     for (int n = 0; n < D; ++n)
       for (int k = 0; k < Dr; ++k) w1[sw8<KP>(n, k)] = bf16_rne_bits(Wf1[(size_t)k * D + n]);
     for (int k = 0; k < D; ++k)
-      for (int n = 0; n < D; ++n) w2[sw8<D>(n, perm16(k))] = bf16_rne_bits(Wf2[(size_t)k * D + n]);
+      for (int n = 0; n < D; ++n) w2[sw8<D>(n, perm32(k))] = bf16_rne_bits(Wf2[(size_t)k * D + n]);
   } else {
     float* w1 = reinterpret_cast<float*>(out + P::W1);
     float* w2 = reinterpret_cast<float*>(out + P::W2);
@@ -250,21 +261,22 @@ __device__ __forceinline__ Geo geometry(const CfParams& p, __amdgpu_buffer_rsrc_
 }
 
 // ------------------------------------------------------------------ products
-// Accumulator element r of block nb (lane half h) is feature 32 nb + 8 (r/4) +
-// 4 h + r%4 of edge lane%32.
+// Accumulator element r of block nb (lane group g) is feature 16 nb + 4 g + r
+// of edge lane % 16.
 
-// GEMM1: acc[q][nb] += sum_k Wf1[k][32 nb + li] * basis_q(k) for k < 8 KC (fp32)
-// or 16 KC (bf16); basis_0 = b~ (Gaussian x envelope), basis_1 = d b~ / dd.
-// Each lane evaluates the basis of its own edge for the k slots it feeds.
+// GEMM1: acc[q][nb] += sum_k Wf1[k][16 nb + e] * basis_q(k) for k < 8 KC (fp32)
+// or 32 KC (bf16); basis_0 = b~ (Gaussian x envelope), basis_1 = d b~ / dd.
+// Each lane evaluates the basis of its own edge for the k slots it feeds
+// (fp32: k = 8c + 2g + u for the MFMA pair u; bf16: k = 32c + 8g + t).
 template <int D, int KP, bool BF16, int NA>
-__device__ __forceinline__ void gemm1(f32x16 (&acc)[NA][D / 32], const unsigned char* lds,
+__device__ __forceinline__ void gemm1(f32x4 (&acc)[NA][D / 16], const unsigned char* lds,
                                       const CfParams& p, const Geo& g, int lane_) {
-  const int lane = opaque(lane_), h = lane >> 5, li = lane & 31;
-  constexpr int CH = BF16 ? 16 : 8;    // k per chunk
-  constexpr int PL = CH / 2;           // k per lane half per chunk
+  const int lane = opaque(lane_), grp = lane >> 4, e = lane & 15;
+  constexpr int CH = BF16 ? 32 : 8;    // k per chunk
+  constexpr int PL = CH / 4;           // k per lane group per chunk
   float step = p.rbf_step;
   asm volatile("" : "+v"(step));
-  const float dh = g.d0 - (float)(PL * h) * step;
+  const float dh = g.d0 - (float)(PL * grp) * step;
   const float coef2 = p.rbf_coef2, inv_s2 = p.rbf_inv_s2;
 #pragma unroll 1
   for (int c = 0; c < p.KC; ++c) {
@@ -284,84 +296,80 @@ __device__ __forceinline__ void gemm1(f32x16 (&acc)[NA][D / 32], const unsigned 
 #pragma unroll
         for (int t = 0; t < 8; ++t) bq[q][t] = (__bf16)b[q][t];
 #pragma unroll
-      for (int nb = 0; nb < D / 32; ++nb) {
-        const bf16x8 w = *reinterpret_cast<const bf16x8*>(W1 + sw8<KP>(32 * nb + li, CH * c + PL * h));
+      for (int nb = 0; nb < D / 16; ++nb) {
+        const bf16x8 w = *reinterpret_cast<const bf16x8*>(W1 + sw8<KP>(16 * nb + e, CH * c + PL * grp));
 #pragma unroll
-        for (int q = 0; q < NA; ++q)
-          acc[q][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w, bq[q], acc[q][nb], 0, 0, 0);
+        for (int q = 0; q < NA; ++q) acc[q][nb] = mfma16(w, bq[q], acc[q][nb]);
       }
     } else {
       const float* W1 = reinterpret_cast<const float*>(lds);
 #pragma unroll
-      for (int nb = 0; nb < D / 32; ++nb) {
-        const f32x4 w = *reinterpret_cast<const f32x4*>(W1 + sw4<KP>(32 * nb + li, CH * c + PL * h));
+      for (int nb = 0; nb < D / 16; ++nb) {
+        const f32x2 w = *reinterpret_cast<const f32x2*>(W1 + sw4<KP>(16 * nb + e, CH * c + PL * grp));
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int q = 0; q < NA; ++q)
-            acc[q][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(w[t], b[q][t], acc[q][nb], 0, 0, 0);
+          for (int q = 0; q < NA; ++q) acc[q][nb] = mfma16(w[u], b[q][u], acc[q][nb]);
       }
     }
   }
 }
 
 // B operands of a chained product from an accumulator-layout input: fp32 uses
-// the accumulator registers directly; bf16 packs them once (k slot 8 h + t of
-// step (kb, u) is register 8 u + t of block kb).
+// the accumulator registers directly; bf16 packs them once (k slot 8 g + t of
+// step kk is register t % 4 of block 2 kk + t / 4).
 template <int D, bool BF16>
 struct Operand;
 template <int D>
 struct Operand<D, false> {
-  const f32x16 (&S)[D / 32];
-  __device__ __forceinline__ explicit Operand(const f32x16 (&s)[D / 32]) : S(s) {}
+  const f32x4 (&S)[D / 16];
+  __device__ __forceinline__ explicit Operand(const f32x4 (&s)[D / 16]) : S(s) {}
 };
 template <int D>
 struct Operand<D, true> {
-  bf16x8 S[D / 32][2];
-  __device__ __forceinline__ explicit Operand(const f32x16 (&s)[D / 32]) {
+  bf16x8 S[D / 32];
+  __device__ __forceinline__ explicit Operand(const f32x4 (&s)[D / 16]) {
 #pragma unroll
-    for (int kb = 0; kb < D / 32; ++kb)
+    for (int kk = 0; kk < D / 32; ++kk)
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int t = 0; t < 8; ++t) S[kb][u][t] = (__bf16)s[kb][8 * u + t];
+      for (int t = 0; t < 8; ++t) S[kk][t] = (__bf16)s[2 * kk + (t >> 2)][t & 3];
   }
 };
 
-// acc[q] += sum_k M[32 nb + li][k] S_q[k] for one output block nb and NA
-// inputs sharing each weight read; M is an output-major image (fp32: sw4
-// rows; bf16: sw8 rows with perm16 positions).
-template <int D, bool BF16, int NA>
-__device__ __forceinline__ void gemm_om_block(f32x16 (&acc)[NA],
-                                              const Operand<D, BF16>* const (&op)[NA],
-                                              const void* img, int nb, int h, int li) {
+// acc += sum_k M[16 nb + e][k] S[k] for one output block nb; M is an
+// output-major image (fp32: sw4 rows; bf16: sw8 rows with perm32 positions).
+template <int D, bool BF16>
+__device__ __forceinline__ void gemm_om_block(f32x4& acc, const Operand<D, BF16>& op,
+                                              const void* img, int nb, int grp, int e) {
   if constexpr (BF16) {
     const __bf16* M = reinterpret_cast<const __bf16*>(img);
 #pragma unroll
-    for (int kb = 0; kb < D / 32; ++kb)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const bf16x8 w =
-            *reinterpret_cast<const bf16x8*>(M + sw8<D>(32 * nb + li, 32 * kb + 16 * u + 8 * h));
-#pragma unroll
-        for (int q = 0; q < NA; ++q)
-          acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w, op[q]->S[kb][u], acc[q], 0, 0, 0);
-      }
+    for (int kk = 0; kk < D / 32; ++kk) {
+      const bf16x8 w = *reinterpret_cast<const bf16x8*>(M + sw8<D>(16 * nb + e, 32 * kk + 8 * grp));
+      acc = mfma16(w, op.S[kk], acc);
+    }
   } else {
     const float* M = reinterpret_cast<const float*>(img);
 #pragma unroll
-    for (int kb = 0; kb < D / 32; ++kb)
+    for (int kb = 0; kb < D / 16; ++kb) {
+      const f32x4 w = *reinterpret_cast<const f32x4*>(M + sw4<D>(16 * nb + e, 16 * kb + 4 * grp));
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const f32x4 w =
-            *reinterpret_cast<const f32x4*>(M + sw4<D>(32 * nb + li, 32 * kb + 8 * c + 4 * h));
+      for (int r = 0; r < 4; ++r) acc = mfma16(w[r], op.S[kb][r], acc);
+    }
+  }
+}
+
+// All output blocks: out[nb] = sum_k M[16 nb + e][k] S[k].
+template <int D, bool BF16>
+__device__ __forceinline__ void gemm_om(f32x4 (&out)[D / 16], const f32x4 (&S)[D / 16],
+                                        const void* img, int lane_) {
+  const int lane = opaque(lane_), grp = lane >> 4, e = lane & 15;
+  const Operand<D, BF16> op(S);
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int q = 0; q < NA; ++q)
-            acc[q] = __builtin_amdgcn_mfma_f32_32x32x2f32(w[t], op[q]->S[kb][4 * c + t], acc[q],
-                                                          0, 0, 0);
-      }
+  for (int nb = 0; nb < D / 16; ++nb) {
+    f32x4 acc = f32x4{};
+    gemm_om_block<D, BF16>(acc, op, img, nb, grp, e);
+    out[nb] = acc;
   }
 }
 
@@ -386,27 +394,25 @@ __device__ __forceinline__ int count_ends(const CfParams& p, int win, int cur, i
   return n;
 }
 
-// Sum of x over lanes li in [lo, hi) of the lower half (upper-half lanes pass 0).
-__device__ __forceinline__ float lane_range_sum(float x, int li, int lo, int hi) {
-  float s = (li >= lo && li < hi) ? x : 0.f;
+// Transpose tile of a wave: 64 columns of the tile's 16 rows, column-major.
+// Accumulator element r of block b (0..3) of lane group g goes to column
+// 16 b + 4 r + g, so that the four lane groups write neighbouring columns;
+// reader lane L then holds feature col_feature(L) of the 64. 16-byte chunks
+// are XOR-swizzled by column so that 8 neighbouring column reads hit distinct
+// banks.
+__device__ __forceinline__ int tpos(int col, int row) {
+  return col * kEdges + ((((row >> 2) ^ ((col >> 1) & 3)) << 2) | (row & 3));
+}
+__host__ __device__ __forceinline__ int col_feature(int L) {
+  return 16 * (L >> 4) + 4 * (L & 3) + ((L >> 2) & 3);
+}
+// Writes accumulator block b (0..3) of the current 64 features.
+__device__ __forceinline__ void tile_put(float* Tb, int b, const f32x4& m, int lane_) {
+  const int lane = opaque(lane_), grp = lane >> 4, e = lane & 15;
 #pragma unroll
-  for (int o = 1; o < 32; o <<= 1) s += __shfl_xor(s, o, 64);
-  return s;
+  for (int r = 0; r < 4; ++r) Tb[tpos(16 * b + 4 * r + grp, e)] = m[r];
 }
 
-// Transpose tile of a wave: 64 columns (two 32-feature blocks) of the 32 tile
-// rows, column-major, 16-byte chunks XOR-swizzled by column so that the
-// accumulator-layout writes (one column, 32 consecutive rows per half-wave)
-// and the per-lane column reads are both conflict-free.
-__device__ __forceinline__ int tpos(int c, int row) {
-  return c * kEdges + ((((row >> 2) ^ (c & 7)) << 2) | (row & 3));
-}
-// Writes block b (0/1) of the tile from accumulator layout.
-__device__ __forceinline__ void tile_put(float* Tb, int b, const float (&m)[16], int lane_) {
-  const int lane = opaque(lane_), h = lane >> 5, li = lane & 31;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) Tb[tpos(32 * b + 8 * (r >> 2) + 4 * h + (r & 3), li)] = m[r];
-}
 // Per-receiver sums of this lane's column of the tile (rows past the tile's
 // length hold zeros). Receivers cur .. cur + nfin - 1 end in this tile and are
 // written through out(i, total); the open receiver's partial sum is carried.
@@ -425,16 +431,17 @@ __device__ __forceinline__ void column_segments(const CfParams& p, float* Tb, in
     if (b < kEdges) starts |= 1u << b;
   }
   float* col = Tb + lane * kEdges;
+  const int sw = (lane >> 1) & 3;
   float run = carry;
 #pragma unroll
   for (int u = 0; u < kEdges / 4; ++u) {
-    float* q = col + ((u ^ (lane & 7)) << 2);
+    float* q = col + ((u ^ sw) << 2);
     f32x4 t = *reinterpret_cast<const f32x4*>(q);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float keep = ((starts >> (4 * u + e)) & 1u) ? 0.f : 1.f;
-      run = fmaf(run, keep, t[e]);
-      t[e] = run;
+    for (int r = 0; r < 4; ++r) {
+      const float keep = ((starts >> (4 * u + r)) & 1u) ? 0.f : 1.f;
+      run = fmaf(run, keep, t[r]);
+      t[r] = run;
     }
     *reinterpret_cast<f32x4*>(q) = t;
   }
@@ -443,7 +450,7 @@ __device__ __forceinline__ void column_segments(const CfParams& p, float* Tb, in
   for (int l = 0; l < nfin; ++l) {
     const int b = seg_end(p, win, cur, ib, l) - ts;
     const int r = b - 1;
-    const float tot = b > prev ? col[(((r >> 2) ^ (lane & 7)) << 2) | (r & 3)] : 0.f;
+    const float tot = b > prev ? col[(((r >> 2) ^ sw) << 2) | (r & 3)] : 0.f;
     out(cur + l, tot);
     prev = b;
   }
@@ -472,15 +479,6 @@ __device__ __forceinline__ bool worker_range(const CfParams& p, int wave, Walk& 
   return true;
 }
 
-// Receiver of this lane's edge ts + li: cur + the number of receivers whose
-// segment ends at or before it.
-__device__ __forceinline__ int edge_receiver(const CfParams& p, int win, int cur, int ib, int nin,
-                                             int e) {
-  int recv = cur;
-  for (int l = 0; l < nin; ++l) recv += (e >= seg_end(p, win, cur, ib, l)) ? 1 : 0;
-  return recv;
-}
-
 // Per-tile receiver bookkeeping and edge geometry (both kernels).
 struct TileHead {
   int te, len, nfin, ncur, recv, j, win_next;
@@ -489,30 +487,32 @@ struct TileHead {
 
 __device__ __forceinline__ TileHead tile_head(const CfParams& p, const Walk& wk, int ts, int cur,
                                               int win, int& jn, float pjx, float pjy, float pjz,
-                                              int lane, int li) {
+                                              int lane, int e) {
   TileHead t;
   t.te = min(ts + kEdges, wk.E1);
   t.len = t.te - ts;
   t.nfin = count_ends(p, win, cur, wk.ib, t.te);
   const int nin = count_ends(p, win, cur, wk.ib, t.te - 1);
-  t.recv = edge_receiver(p, win, cur, wk.ib, nin, ts + li);
+  int recv = cur;
+  for (int l = 0; l < nin; ++l) recv += (ts + e >= seg_end(p, win, cur, wk.ib, l)) ? 1 : 0;
+  t.recv = recv;
   t.j = jn;
-  t.g = geometry(p, wk.rpos, t.recv, pjx, pjy, pjz, li < t.len);
+  t.g = geometry(p, wk.rpos, recv, pjx, pjy, pjz, e < t.len);
   t.ncur = cur + t.nfin;
   t.win_next = load_window(wk.rrow, t.ncur, wk.ib, lane);
-  jn = bload_i(wk.rcol, (uint32_t)(ts + kEdges + li) * 4u);
+  jn = bload_i(wk.rcol, (uint32_t)(ts + kEdges + e) * 4u);
   return t;
 }
 
 template <int D, int KP, bool BF16>
-__global__ __launch_bounds__(512, 1) void k_cf_fwd(CfParams p) {
-  using P = Plan<D, KP, BF16>;
-  constexpr int NB = D / 32;
+__global__ __launch_bounds__((64 * cf_nw<D, BF16, false>()), 1) void k_cf_fwd(CfParams p) {
+  using P = Plan<D, KP, BF16, cf_nw<D, BF16, false>()>;
+  constexpr int NB = D / 16;
   extern __shared__ __align__(16) unsigned char lds[];
   stage_image<P>(p.img, lds);
   __syncthreads();
 
-  const int lane = threadIdx.x & 63, h = lane >> 5, li = lane & 31;
+  const int lane = threadIdx.x & 63, e = lane & 15;
   const int wave = uni((int)threadIdx.x >> 6);
   Walk wk;
   if (!worker_range<P>(p, wave, wk)) return;
@@ -520,66 +520,57 @@ __global__ __launch_bounds__(512, 1) void k_cf_fwd(CfParams p) {
   float* Tb = reinterpret_cast<float*>(lds + P::STAGE + wave * P::TB);
   const uint32_t N = (uint32_t)p.n_atoms;
   const __amdgpu_buffer_rsrc_t rx = rsrc(p.x, N * (uint32_t)D * 4u);
+  const int fcol = col_feature(lane);
 
-  float carry[NB / 2];
+  float carry[NB / 4];
 #pragma unroll
-  for (int pr = 0; pr < NB / 2; ++pr) carry[pr] = 0.f;
+  for (int pss = 0; pss < NB / 4; ++pss) carry[pss] = 0.f;
   int cur = wk.ia;
   int win = load_window(wk.rrow, cur, ib, lane);
-  int jn = bload_i(wk.rcol, (uint32_t)(wk.E0 + li) * 4u);
+  int jn = bload_i(wk.rcol, (uint32_t)(wk.E0 + e) * 4u);
   float pjx = bload(wk.rpos, (uint32_t)jn * 12u), pjy = bload(wk.rpos, (uint32_t)jn * 12u + 4),
         pjz = bload(wk.rpos, (uint32_t)jn * 12u + 8);
 
   for (int ts = wk.E0; ts < wk.E1; ts += kEdges) {
-    const TileHead th = tile_head(p, wk, ts, cur, win, jn, pjx, pjy, pjz, lane, li);
+    const TileHead th = tile_head(p, wk, ts, cur, win, jn, pjx, pjy, pjz, lane, e);
     const Geo& g = th.g;
-    const int h4 = 4 * (opaque(lane) >> 5);   // this lane's column offset in a block
+    const int g4 = 4 * (opaque(lane) >> 4);   // this lane's feature offset in a block
 
     // s = ssp(b~ Wf1 + cf1)
-    f32x16 s[1][NB];
+    f32x4 s[1][NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) s[0][nb] = f32x16{};
+    for (int nb = 0; nb < NB; ++nb) s[0][nb] = f32x4{};
     gemm1<D, KP, BF16, 1>(s, lds, p, g, lane);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+    for (int nb = 0; nb < NB; ++nb) {
+      const f32x4 c1 = bias4<P>(p, lds, g4, 16 * nb);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 c1 = bias4<P>(p, lds, h4, 32 * nb + 8 * q);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) s[0][nb][4 * q + t] = ssp(s[0][nb][4 * q + t] + c1[t]);
-      }
+      for (int r = 0; r < 4; ++r) s[0][nb][r] = ssp(s[0][nb][r] + c1[r]);
+    }
     pjx = bload(wk.rpos, (uint32_t)jn * 12u);
     pjy = bload(wk.rpos, (uint32_t)jn * 12u + 4);
     pjz = bload(wk.rpos, (uint32_t)jn * 12u + 8);
-    const Operand<D, BF16> os(s[0]);
-    const Operand<D, BF16>* const ops[1] = {&os};
 
-    // per output block: w = s Wf2 + cf2 (masked beyond the cutoff), message
-    // x_j * w, summed per receiver two blocks at a time
-    const uint32_t xo = ((uint32_t)th.j * (uint32_t)D + (uint32_t)h4) * 4u;
-    const int lane_o = opaque(lane), ho = lane_o >> 5, lio = lane_o & 31;
+    // w = s Wf2 + cf2 (masked beyond the cutoff); messages x_j * w summed per
+    // receiver, 64 features at a time
+    f32x4 w[NB];
+    gemm_om<D, BF16>(w, s[0], lds + P::W2, lane);
+    const uint32_t xo = ((uint32_t)th.j * (uint32_t)D + (uint32_t)g4) * 4u;
 #pragma unroll
-    for (int pr = 0; pr < NB / 2; ++pr) {
+    for (int pss = 0; pss < NB / 4; ++pss) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int nb = 2 * pr + b;
-        __builtin_amdgcn_sched_barrier(0);
-        f32x16 w[1] = {f32x16{}};
-        gemm_om_block<D, BF16, 1>(w, ops, lds + P::W2, nb, ho, lio);
-        float m[16];
+      for (int b = 0; b < 4; ++b) {
+        const int nb = 4 * pss + b;
+        const f32x4 xg = bload4(rx, xo + (uint32_t)(64 * nb));
+        const f32x4 c2 = bias4<P>(p, lds, g4, D + 16 * nb);
+        f32x4 m;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = 32 * nb + 8 * q;   // + h4
-          const f32x4 xg = bload4(rx, xo + (uint32_t)col * 4u);
-          const f32x4 c2 = bias4<P>(p, lds, h4, D + col);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) m[4 * q + t] = xg[t] * (g.in * (w[0][4 * q + t] + c2[t]));
-        }
+        for (int r = 0; r < 4; ++r) m[r] = xg[r] * (g.in * (w[nb][r] + c2[r]));
         tile_put(Tb, b, m, lane);
       }
       wave_sync();
-      float* hout = p.h + 64 * pr + lane;
-      column_segments(p, Tb, win, cur, ib, th.nfin, ts, th.len, th.ncur < ib, carry[pr], lane,
+      float* hout = p.h + 64 * pss + fcol;
+      column_segments(p, Tb, win, cur, ib, th.nfin, ts, th.len, th.ncur < ib, carry[pss], lane,
                       [&](int i, float tot) { hout[(size_t)i * D] = tot; });
       wave_sync();
     }
@@ -592,15 +583,14 @@ __global__ __launch_bounds__(512, 1) void k_cf_fwd(CfParams p) {
 }
 
 template <int D, int KP, bool BF16>
-__global__ __launch_bounds__(512, 1) void k_cf_bwd(CfParams p) {
-  using P = Plan<D, KP, BF16>;
-  constexpr int NB = D / 32;
+__global__ __launch_bounds__((64 * cf_nw<D, BF16, true>()), 1) void k_cf_bwd(CfParams p) {
+  using P = Plan<D, KP, BF16, cf_nw<D, BF16, true>()>;
+  constexpr int NB = D / 16;
   extern __shared__ __align__(16) unsigned char lds[];
   stage_image<P>(p.img, lds);
   __syncthreads();
 
-  const int lane = threadIdx.x & 63, h = lane >> 5, li = lane & 31;
-  const bool upper = h != 0;
+  const int lane = threadIdx.x & 63, e = lane & 15;
   const int wave = uni((int)threadIdx.x >> 6);
   Walk wk;
   if (!worker_range<P>(p, wave, wk)) return;
@@ -610,150 +600,98 @@ __global__ __launch_bounds__(512, 1) void k_cf_bwd(CfParams p) {
   const __amdgpu_buffer_rsrc_t rx = rsrc(p.x, N * (uint32_t)D * 4u);
   const __amdgpu_buffer_rsrc_t rgh = rsrc(p.gh, N * (uint32_t)D * 4u);
   const bool want_q = p.q_out != nullptr;
+  const int fcol = col_feature(lane);
 
-  float carry[NB / 2];
+  float carry[NB / 4];
 #pragma unroll
-  for (int pr = 0; pr < NB / 2; ++pr) carry[pr] = 0.f;
-  float fcx = 0.f, fcy = 0.f, fcz = 0.f;
-  int cur = wk.ia, ss = wk.E0;
+  for (int pss = 0; pss < NB / 4; ++pss) carry[pss] = 0.f;
+  float fcarry = 0.f;   // lanes 0..2: open receiver's force component
+  int cur = wk.ia;
   int win = load_window(wk.rrow, cur, ib, lane);
-  int jn = bload_i(wk.rcol, (uint32_t)(wk.E0 + li) * 4u);
+  int jn = bload_i(wk.rcol, (uint32_t)(wk.E0 + e) * 4u);
   float pjx = bload(wk.rpos, (uint32_t)jn * 12u), pjy = bload(wk.rpos, (uint32_t)jn * 12u + 4),
         pjz = bload(wk.rpos, (uint32_t)jn * 12u + 8);
 
   for (int ts = wk.E0; ts < wk.E1; ts += kEdges) {
-    const TileHead th = tile_head(p, wk, ts, cur, win, jn, pjx, pjy, pjz, lane, li);
+    const TileHead th = tile_head(p, wk, ts, cur, win, jn, pjx, pjy, pjz, lane, e);
     const Geo& g = th.g;
-    const int h4 = 4 * (opaque(lane) >> 5);   // this lane's column offset in a block
+    const int g4 = 4 * (opaque(lane) >> 4);   // this lane's feature offset in a block
 
     // GEMM1: a = b~ Wf1 + cf1 and its tangent a' = (d b~/dd) Wf1;
     // s = ssp(a), s' = sigmoid(a) a'
-    f32x16 av[2][NB];
+    f32x4 av[2][NB];
 #pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) av[q][nb] = f32x16{};
+      for (int nb = 0; nb < NB; ++nb) av[q][nb] = f32x4{};
     gemm1<D, KP, BF16, 2>(av, lds, p, g, lane);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+    for (int nb = 0; nb < NB; ++nb) {
+      const f32x4 c1 = bias4<P>(p, lds, g4, 16 * nb);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 c1 = bias4<P>(p, lds, h4, 32 * nb + 8 * q);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int r = 4 * q + t;
-          float sv, sg;
-          ssp_sig(av[0][nb][r] + c1[t], sv, sg);
-          av[0][nb][r] = sv;
-          // materialised here: sunk towards its use in the tangent product,
-          // the gate's temporaries would stay live through the value product
-          float gv = sg * av[1][nb][r];
-          asm volatile("" : "+v"(gv));
-          av[1][nb][r] = gv;
-        }
+      for (int r = 0; r < 4; ++r) {
+        float sv, sg;
+        ssp_sig(av[0][nb][r] + c1[r], sv, sg);
+        av[0][nb][r] = sv;
+        av[1][nb][r] = sg * av[1][nb][r];
       }
+    }
     pjx = bload(wk.rpos, (uint32_t)jn * 12u);
     pjy = bload(wk.rpos, (uint32_t)jn * 12u + 4);
     pjz = bload(wk.rpos, (uint32_t)jn * 12u + 8);
-    // GEMM2 for the values, all output blocks (frees s): w = s Wf2
-    f32x16 wv[NB];
-    {
-      const Operand<D, BF16> os(av[0]);
-      const Operand<D, BF16>* const ops[1] = {&os};
-      const int lane_o = opaque(lane), ho = lane_o >> 5, lio = lane_o & 31;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        f32x16 acc[1] = {f32x16{}};
-        gemm_om_block<D, BF16, 1>(acc, ops, lds + P::W2, nb, ho, lio);
-        wv[nb] = acc[0];
-      }
-    }
-    const Operand<D, BF16> ot(av[1]);
-    const Operand<D, BF16>* const opt[1] = {&ot};
 
-    // per output block: tangent w' = s' Wf2 (GEMM2 again, one block live);
-    // q = dE/dh_j w summed per receiver (two blocks at a time);
+    // GEMM2 for the tangents, then the values: w' = s' Wf2, w = s Wf2
+    f32x4 wt[NB], wv[NB];
+    gemm_om<D, BF16>(wt, av[1], lds + P::W2, lane);
+    gemm_om<D, BF16>(wv, av[0], lds + P::W2, lane);
+
+    // per 64 features: q = dE/dh_j w summed per receiver;
     // dE/dd += <dE/dh_i x_j + dE/dh_j x_i, w'>
-    const uint32_t jo = ((uint32_t)th.j * (uint32_t)D + (uint32_t)h4) * 4u;
-    const uint32_t io = ((uint32_t)th.recv * (uint32_t)D + (uint32_t)h4) * 4u;
+    const uint32_t jo = ((uint32_t)th.j * (uint32_t)D + (uint32_t)g4) * 4u;
+    const uint32_t io = ((uint32_t)th.recv * (uint32_t)D + (uint32_t)g4) * 4u;
     float gdd = 0.f;
 #pragma unroll
-    for (int pr = 0; pr < NB / 2; ++pr) {
+    for (int pss = 0; pss < NB / 4; ++pss) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int nb = 2 * pr + b;
-        // one output block in flight: hoisted, the gathers of every block
-        // would be live at once
-        __builtin_amdgcn_sched_barrier(0);
-        const int lane_o = opaque(lane), ho = lane_o >> 5, lio = lane_o & 31;
-        f32x16 wt[1] = {f32x16{}};
-        gemm_om_block<D, BF16, 1>(wt, opt, lds + P::W2, nb, ho, lio);
-        float qv[16];
+      for (int b = 0; b < 4; ++b) {
+        const int nb = 4 * pss + b;
+        const uint32_t co = (uint32_t)(64 * nb);
+        const f32x4 xj = bload4(rx, jo + co), gj = bload4(rgh, jo + co);
+        const f32x4 xi = bload4(rx, io + co), gi = bload4(rgh, io + co);
+        const f32x4 c2 = bias4<P>(p, lds, g4, D + 16 * nb);
+        f32x4 qv;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          // gathers in two halves of 32 registers (the first may run ahead
-          // of the block's product)
-          if (q == 2) __builtin_amdgcn_sched_barrier(0);
-          const int col = 32 * nb + 8 * q;   // + h4
-          const f32x4 xj = bload4(rx, jo + (uint32_t)col * 4u);
-          const f32x4 gj = bload4(rgh, jo + (uint32_t)col * 4u);
-          const f32x4 xi = bload4(rx, io + (uint32_t)col * 4u);
-          const f32x4 gi = bload4(rgh, io + (uint32_t)col * 4u);
-          const f32x4 c2 = bias4<P>(p, lds, h4, D + col);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int r = 4 * q + t;
-            qv[r] = gj[t] * (g.in * (wv[nb][r] + c2[t]));
-            gdd = fmaf(gi[t] * xj[t] + gj[t] * xi[t], wt[0][r], gdd);
-          }
+        for (int r = 0; r < 4; ++r) {
+          qv[r] = gj[r] * (g.in * (wv[nb][r] + c2[r]));
+          gdd = fmaf(gi[r] * xj[r] + gj[r] * xi[r], wt[nb][r], gdd);
         }
         if (want_q) tile_put(Tb, b, qv, lane);
       }
       if (want_q) {
         wave_sync();
-        float* qout = p.q_out + 64 * pr + lane;
-        column_segments(p, Tb, win, cur, ib, th.nfin, ts, th.len, th.ncur < ib, carry[pr], lane,
+        float* qout = p.q_out + 64 * pss + fcol;
+        column_segments(p, Tb, win, cur, ib, th.nfin, ts, th.len, th.ncur < ib, carry[pss], lane,
                         [&](int i, float tot) { qout[(size_t)i * D] = tot; });
         wave_sync();
       }
     }
+    gdd += __shfl_xor(gdd, 16, 64);
     gdd += __shfl_xor(gdd, 32, 64);
-    const float gd = upper ? 0.f : gdd * g.invd * g.in;
-    const float fx = gd * g.ux, fy = gd * g.uy, fz = gd * g.uz;
+    const float gd = gdd * g.invd * g.in;
 
-    // this block's dE/dr rows, one per receiver of the tile
-    {
-      int s0 = ss;
-      for (int l = 0; l < th.nfin; ++l) {
-        const int be = seg_end(p, win, cur, ib, l);
-        const int lo = (s0 > ts ? s0 : ts) - ts, hi = be - ts;
-        float sx = lane_range_sum(fx, li, lo, hi);
-        float sy = lane_range_sum(fy, li, lo, hi);
-        float sz = lane_range_sum(fz, li, lo, hi);
-        if (l == 0) {
-          sx += fcx; sy += fcy; sz += fcz;
-        }
-        if (lane == 0) {
-          float* f = p.forces + (size_t)(cur + l) * 3;
-          f[0] = sx; f[1] = sy; f[2] = sz;
-        }
-        s0 = be;
-      }
-      if (th.ncur < ib) {
-        const int lo = (s0 > ts ? s0 : ts) - ts;
-        const float sx = lane_range_sum(fx, li, lo, th.len);
-        const float sy = lane_range_sum(fy, li, lo, th.len);
-        const float sz = lane_range_sum(fz, li, lo, th.len);
-        if (th.nfin == 0) {
-          fcx += sx; fcy += sy; fcz += sz;
-        } else {
-          fcx = sx; fcy = sy; fcz = sz;
-        }
-      } else {
-        fcx = fcy = fcz = 0.f;
-      }
-      ss = s0;
+    // this block's dE/dr rows: the edge contributions gd u as three columns of
+    // the tile, summed per receiver like the features
+    if (lane < 16) {
+      Tb[tpos(0, e)] = gd * g.ux;
+      Tb[tpos(1, e)] = gd * g.uy;
+      Tb[tpos(2, e)] = gd * g.uz;
     }
+    wave_sync();
+    column_segments(p, Tb, win, cur, ib, th.nfin, ts, th.len, th.ncur < ib, fcarry, lane,
+                    [&](int i, float tot) {
+                      if (lane < 3) p.forces[(size_t)i * 3 + lane] = tot;
+                    });
+    wave_sync();
     cur = th.ncur;
     win = th.win_next;
   }
@@ -811,25 +749,27 @@ hipError_t launch_force_sum(const float* fb, int T, int64_t n_atoms, float* forc
 // ------------------------------------------------------------------ dispatch
 template <int D, int KP, bool BF16>
 struct CfKernels {
-  using P = Plan<D, KP, BF16>;
+  using PF = Plan<D, KP, BF16, cf_nw<D, BF16, false>()>;
+  using PB = Plan<D, KP, BF16, cf_nw<D, BF16, true>()>;
   static hipError_t prepare() {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_cf_fwd<D, KP, BF16>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, P::TOTAL);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, PF::TOTAL);
     if (e != hipSuccess) return e;
     return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_cf_bwd<D, KP, BF16>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, P::TOTAL);
+                               hipFuncAttributeMaxDynamicSharedMemorySize, PB::TOTAL);
   }
-  static size_t image_bytes() { return P::IMG; }
+  static size_t image_bytes() { return PF::IMG; }
+  static int workers(int bwd) { return bwd ? PB::NW : PF::NW; }
   static void fill(int Dr, const float* Wf1, const float* cf1, const float* Wf2, const float* cf2,
                    unsigned char* out) {
     fill_image<D, KP, BF16>(Dr, Wf1, cf1, Wf2, cf2, out);
   }
   static hipError_t fwd(const CfParams& p, int G, hipStream_t s) {
-    hipLaunchKernelGGL((k_cf_fwd<D, KP, BF16>), dim3(G), dim3(P::NT), P::TOTAL, s, p);
+    hipLaunchKernelGGL((k_cf_fwd<D, KP, BF16>), dim3(G), dim3(PF::NT), PF::TOTAL, s, p);
     return hipGetLastError();
   }
   static hipError_t bwd(const CfParams& p, int G, hipStream_t s) {
-    hipLaunchKernelGGL((k_cf_bwd<D, KP, BF16>), dim3(G), dim3(P::NT), P::TOTAL, s, p);
+    hipLaunchKernelGGL((k_cf_bwd<D, KP, BF16>), dim3(G), dim3(PB::NT), PB::TOTAL, s, p);
     return hipGetLastError();
   }
 };
@@ -847,6 +787,9 @@ static R cf_dispatch(int D, int KP, int bf16, R fail, F f) {
 hipError_t cf_prepare(int D, int KP, int bf16) {
   return cf_dispatch(D, KP, bf16, hipErrorInvalidValue,
                      [](auto k) { return decltype(k)::prepare(); });
+}
+int cf_workers(int D, int KP, int bf16, int bwd) {
+  return cf_dispatch(D, KP, bf16, 0, [&](auto k) { return decltype(k)::workers(bwd); });
 }
 size_t cf_image_bytes(int D, int KP, int bf16) {
   return cf_dispatch(D, KP, bf16, (size_t)0, [](auto k) { return decltype(k)::image_bytes(); });

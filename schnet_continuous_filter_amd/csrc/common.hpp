@@ -9,12 +9,13 @@
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 namespace sn {
 
 constexpr int kThreads = 256;  // every kernel of the library runs 4 wave64 per block
-constexpr int kMaxGrid = 4096; // upper bound on CFConv work-groups (partition table size)
+constexpr int kMaxWorkers = 8192; // upper bound on CFConv workers (partition table size)
 constexpr int kCellsPerAxisMax = 64;
 constexpr int kScanChunk = 1024; // elements per block of the device scan
 constexpr int kSortRowMax = 1024;
@@ -44,7 +45,7 @@ __device__ inline void dev_fail(DevStatus* st, int code, int64_t detail) {
 
 // Offsets (bytes) of everything carved out of a workspace.
 struct WsLayout {
-  size_t status, wg_start, scan_blocks, cell_count, cell_start, cell_atoms, atom_cell;
+  size_t status, wg_start, wg_start_b, scan_blocks, cell_count, cell_start, cell_atoms, atom_cell;
   size_t x, au, gbuf, tmp, gx, fblk, eps, total;
 };
 WsLayout ws_layout(int64_t n_atoms, int D, int T, int H);
@@ -90,7 +91,7 @@ struct CfParams {
 
 int cf_kp(int Dr, int bf16);               // basis length the LDS images are padded to
 int cf_chunks(int Dr, int bf16);           // basis chunks (8 fp32 / 16 bf16 basis functions each)
-int cf_workers(int bf16);                  // waves (independent workers) per work-group
+int cf_workers(int D, int KP, int bf16, int bwd);  // waves (workers) per work-group of a kernel
 hipError_t cf_prepare(int D, int KP, int bf16);  // raises the dynamic LDS limit of the kernels
 // Filter-weight image of one interaction block as the CFConv kernels hold it
 // in LDS: cf_image_bytes bytes, filled on the host.
