@@ -7,157 +7,256 @@
 // network then a sum. §4.1 "Precision contract": energy accumulation in fp32
 // or better (the replica sum here accumulates in double).
 //
-// The dense layers are [atoms x K] x [K x N] products on fp32 MFMA
-// (v_mfma_f32_32x32x2_f32); each kernel chains the two layers of one network
-// with its activation (or gate) in between.
-#include "common.hpp"
+// Each network is two dense products chained through an activation (or gate).
+// A work-group copies both weight matrices into LDS once; its waves then take
+// 16-atom tiles in turn. Products are computed transposed on 16x16 MFMA blocks
+// (v_mfma_f32_16x16x4_f32), one atom per lane column: the weights are the A
+// operand (output-major images built on the host), the atom features the B
+// operand, loaded from HBM straight into the accumulator layout (lane group g
+// holds features 4g..4g+3 of every 16-feature block) and stored back from it.
+// The intermediate activation never leaves registers.
+#include <cstring>
+
+#include "tile16.hpp"
 
 namespace sn {
 
-#define LN2F 0.69314718055994530942f
+constexpr int kAtomNW = 16;   // waves per work-group (four per SIMD)
+constexpr int kAtoms = 16;    // atoms per wave tile
 
-__device__ __forceinline__ float ssp_f(float a) {
-  const float t = __expf(-fabsf(a));
-  return fmaxf(a, 0.f) + __logf(1.f + t) - LN2F;
-}
-__device__ __forceinline__ float sigmoid_f(float a) {
-  const float t = __expf(-fabsf(a));
-  const float inv = __builtin_amdgcn_rcpf(1.f + t);
-  return a >= 0.f ? inv : t * inv;
-}
+// LDS image of one network: M1 [N1][D] (first product, output-major), M2
+// [D][N1] (second product), V1 [N1], V2 [D] (vectors of the mode).
+template <int D, int N1>
+struct AtomPlan {
+  static constexpr int M1 = 0;
+  static constexpr int M2 = M1 + N1 * D * 4;
+  static constexpr int V1 = M2 + D * N1 * 4;
+  static constexpr int V2 = V1 + N1 * 4;
+  static constexpr int IMG = V2 + D * 4;
+  static_assert(IMG <= 160 * 1024, "atom-wise image exceeds LDS");
+  static_assert(IMG % 16 == 0, "image is copied in 16-byte pieces");
+};
 
-// ------------------------------------------------------------------ fused atom-wise pairs
-// A work-group takes 32 atoms at a time. The A tile sits in LDS (fp32, K
-// permuted per lane so one 16-byte load feeds four MFMAs); B operands come
-// straight from the weight matrices in global memory (row-major [K][N], so a
-// wave's 32 lanes read 128 contiguous bytes per row; the matrices stay in L2).
-// Each kernel chains two products with the elementwise step between them in
-// registers and the intermediate back in the same LDS tile.
-constexpr int kRows = 32;
-
-template <int K>
-__device__ __forceinline__ f32x16 mma_lds_glb(const float* Ap, const float* __restrict__ W,
-                                              int ldw, int c, int h) {
-  f32x16 acc = f32x16{};
-#pragma unroll
-  for (int k0 = 0; k0 < K; k0 += 8) {
-    const float* wp = W + (size_t)(k0 + 4 * h) * ldw + c;
-    const float b0 = wp[0], b1 = wp[ldw], b2 = wp[2 * ldw], b3 = wp[3 * ldw];
-    const f32x4 av = *reinterpret_cast<const f32x4*>(Ap + k0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.x, b0, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.y, b1, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.z, b2, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.w, b3, acc, 0, 0, 0);
+// Products and vectors of each mode (weights row-major [fan_in][fan_out]):
+//   ATOM_UPDATE_FWD  a = h Wu1 + cu1 (stored);  x' = x + ssp(a) Wu2 + cu2
+//                    M1 = Wu1^T, M2 = Wu2^T, V1 = cu1, V2 = cu2
+//   ATOM_UPDATE_BWD  g_a = (g_x Wu2^T) sigmoid(a);  g_h = g_a Wu1^T
+//                    M1 = Wu2, M2 = Wu1
+//   ATOM_READOUT     o = x Wo1 + co1;  eps = ssp(o).wo2 + co2;
+//                    g_x = (sigmoid(o) wo2) Wo1^T
+//                    M1 = Wo1^T, M2 = Wo1, V1 = co1, V2[:N1] = wo2
+template <int D, int N1>
+static void fill_atom_image(int mode, const float* W1, const float* b1, const float* W2,
+                            const float* b2, unsigned char* out) {
+  using P = AtomPlan<D, N1>;
+  std::memset(out, 0, P::IMG);
+  float* m1 = reinterpret_cast<float*>(out + P::M1);
+  float* m2 = reinterpret_cast<float*>(out + P::M2);
+  float* v1 = reinterpret_cast<float*>(out + P::V1);
+  float* v2 = reinterpret_cast<float*>(out + P::V2);
+  if (mode == ATOM_UPDATE_FWD || mode == ATOM_READOUT) {
+    // W1 [D][N1]: M1[n][k] = W1[k][n]
+    for (int k = 0; k < D; ++k)
+      for (int n = 0; n < N1; ++n) m1[sw4<D>(n, k)] = W1[(size_t)k * N1 + n];
   }
-  return acc;
+  if (mode == ATOM_UPDATE_FWD) {
+    // W2 [N1][D]: M2[m][n] = W2[n][m]
+    for (int n = 0; n < N1; ++n)
+      for (int m = 0; m < D; ++m) m2[sw4<N1>(m, n)] = W2[(size_t)n * D + m];
+    std::memcpy(v1, b1, N1 * sizeof(float));
+    std::memcpy(v2, b2, D * sizeof(float));
+  } else if (mode == ATOM_UPDATE_BWD) {
+    // W1 = Wu1 [D][N1], W2 = Wu2 [N1][D]: M1[n][m] = Wu2[n][m], M2[k][n] = Wu1[k][n]
+    for (int n = 0; n < N1; ++n)
+      for (int m = 0; m < D; ++m) m1[sw4<D>(n, m)] = W2[(size_t)n * D + m];
+    for (int k = 0; k < D; ++k)
+      for (int n = 0; n < N1; ++n) m2[sw4<N1>(k, n)] = W1[(size_t)k * N1 + n];
+  } else {
+    // W1 = Wo1 [D][N1]: M2[k][n] = Wo1[k][n]; W2 = wo2 [N1]
+    for (int k = 0; k < D; ++k)
+      for (int n = 0; n < N1; ++n) m2[sw4<N1>(k, n)] = W1[(size_t)k * N1 + n];
+    std::memcpy(v1, b1, N1 * sizeof(float));
+    std::memcpy(v2, W2, N1 * sizeof(float));
+  }
 }
 
-__device__ __forceinline__ int blk_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
-
-// MODE: ATOM_UPDATE_FWD  a = h W1 + b1 (stored);  x' = x + ssp(a) W2 + b2
-//       ATOM_UPDATE_BWD  g_a = (g_x W2^T) * sigmoid(a);  g_h = g_a W1^T   (W1, W2 given transposed)
-//       ATOM_READOUT     o = x W1 + b1;  eps = ssp(o).w2 + b2;  g_x = (sigmoid(o) * w2) W1^T
 template <int D, int N1, int MODE>
-__global__ __launch_bounds__(kThreads) void k_atom(AtomArgs g) {
-  constexpr int SA = D + 4;
-  __shared__ __align__(16) float At[kRows * SA];
-  __shared__ float Sh[MODE == ATOM_READOUT ? kRows * (N1 + 1) : 1];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, li = lane & 31;
-  const float* Ap = At + li * SA + 4 * h;
-  for (int m0 = blockIdx.x * kRows; m0 < g.M; m0 += gridDim.x * kRows) {
-    // A tile: rows m0.., D columns, float4 loads
-    for (int idx = tid; idx < kRows * D / 4; idx += kThreads) {
-      const int r = idx / (D / 4), k4 = idx - r * (D / 4);
-      f32x4 v = f32x4{};
-      if (m0 + r < g.M) {
-        const size_t o = (size_t)(m0 + r) * D + 4 * k4;
-        v = *reinterpret_cast<const f32x4*>(g.A + o);
-        if constexpr (MODE == ATOM_UPDATE_BWD) {
-          if (g.A2) v += *reinterpret_cast<const f32x4*>(g.A2 + o);
-          if (g.Asum) *reinterpret_cast<f32x4*>(g.Asum + o) = v;
-        }
-      }
-      *reinterpret_cast<f32x4*>(At + r * SA + 4 * k4) = v;
-    }
-    __syncthreads();
-    f32x16 v1 = f32x16{};
-    const int c1 = wave * 32 + li;
-    if (wave < N1 / 32) {
-      const f32x16 acc = mma_lds_glb<D>(Ap, g.W1, N1, c1, h);
+__global__ __launch_bounds__(64 * kAtomNW, 1) void k_atom(AtomArgs g) {
+  using P = AtomPlan<D, N1>;
+  extern __shared__ __align__(16) unsigned char lds[];
+  {
+    const f32x4* src = reinterpret_cast<const f32x4*>(g.img);
+    f32x4* dst = reinterpret_cast<f32x4*>(lds);
+    for (int i = threadIdx.x; i < P::IMG / 16; i += 64 * kAtomNW) dst[i] = src[i];
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, e = lane & 15;
+  const int wave = uni((int)threadIdx.x >> 6);
+  const int ntiles = (g.M + kAtoms - 1) / kAtoms;
+  const uint32_t rows = (uint32_t)g.M;
+  const __amdgpu_buffer_rsrc_t rA = rsrc(g.A, rows * D * 4u);
+  const __amdgpu_buffer_rsrc_t rA2 = rsrc(g.A2, g.A2 ? rows * D * 4u : 0u);
+  const __amdgpu_buffer_rsrc_t rR = rsrc(g.R, g.R ? rows * D * 4u : 0u);
+  const __amdgpu_buffer_rsrc_t rS = rsrc(g.S, g.S ? rows * N1 * 4u : 0u);
+  const float* V1 = reinterpret_cast<const float*>(lds + P::V1);
+  const float* V2 = reinterpret_cast<const float*>(lds + P::V2);
+
+  for (int t = (int)blockIdx.x * kAtomNW + wave; t < ntiles; t += (int)gridDim.x * kAtomNW) {
+    const int g4 = 4 * (opaque(lane) >> 4);   // this lane's feature offset in a block
+    const int atom = t * kAtoms + e;
+    const bool ok = atom < g.M;
+    const uint32_t ro = ((uint32_t)atom * D + (uint32_t)g4) * 4u;    // D-wide rows
+    const uint32_t ro1 = ((uint32_t)atom * N1 + (uint32_t)g4) * 4u;  // N1-wide rows
+
+    f32x4 in[D / 16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + blk_row(r, h);
-        const bool ok = m < g.M;
-        const size_t o = (size_t)m * N1 + c1;
-        if constexpr (MODE == ATOM_UPDATE_FWD) {
-          const float a = acc[r] + g.b1[c1];
-          if (ok) g.Aout[o] = a;
-          v1[r] = ssp_f(a);
-        } else if constexpr (MODE == ATOM_UPDATE_BWD) {
-          v1[r] = ok ? acc[r] * sigmoid_f(g.S[o]) : 0.f;
-        } else {
-          const float z = acc[r] + g.b1[c1];
-          const float w2 = g.w2[c1];
-          Sh[blk_row(r, h) * (N1 + 1) + c1] = ssp_f(z) * w2;
-          v1[r] = sigmoid_f(z) * w2;
-        }
+    for (int kb = 0; kb < D / 16; ++kb) {
+      in[kb] = bload4(rA, ro + 64u * kb);
+      if constexpr (MODE == ATOM_UPDATE_BWD) {
+        if (g.A2) in[kb] += bload4(rA2, ro + 64u * kb);
       }
     }
-    __syncthreads();
-    if (wave < N1 / 32) {
+    if constexpr (MODE == ATOM_UPDATE_BWD) {
+      if (g.Asum && ok) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) At[blk_row(r, h) * SA + c1] = v1[r];
+        for (int kb = 0; kb < D / 16; ++kb)
+          *reinterpret_cast<f32x4*>(g.Asum + (size_t)atom * D + g4 + 16 * kb) = in[kb];
+      }
     }
-    __syncthreads();
+
+    f32x4 u[N1 / 16];
+    gemm_om<D, N1, false>(u, in, lds + P::M1, lane);
+    float ep = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < N1 / 16; ++nb) {
+      if constexpr (MODE == ATOM_UPDATE_FWD) {
+        const f32x4 b = *reinterpret_cast<const f32x4*>(V1 + g4 + 16 * nb);
+        const f32x4 a = u[nb] + b;
+        if (ok) *reinterpret_cast<f32x4*>(g.Aout + (size_t)atom * N1 + g4 + 16 * nb) = a;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) u[nb][r] = ssp(a[r]);
+      } else if constexpr (MODE == ATOM_UPDATE_BWD) {
+        const f32x4 a = bload4(rS, ro1 + 64u * nb);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float s, sg;
+          ssp_sig(a[r], s, sg);
+          u[nb][r] *= sg;
+        }
+      } else {
+        const f32x4 b = *reinterpret_cast<const f32x4*>(V1 + g4 + 16 * nb);
+        const f32x4 w2 = *reinterpret_cast<const f32x4*>(V2 + g4 + 16 * nb);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float s, sg;
+          ssp_sig(u[nb][r] + b[r], s, sg);
+          ep = fmaf(s, w2[r], ep);
+          u[nb][r] = sg * w2[r];
+        }
+      }
+    }
     if constexpr (MODE == ATOM_READOUT) {
-      const int r = tid >> 3, part = tid & 7;
-      float s = 0.f;
-      for (int k = part * (N1 / 8); k < (part + 1) * (N1 / 8); ++k) s += Sh[r * (N1 + 1) + k];
-      s += __shfl_xor(s, 1, 64);
-      s += __shfl_xor(s, 2, 64);
-      s += __shfl_xor(s, 4, 64);
-      if (part == 0 && m0 + r < g.M) g.eps[m0 + r] = s + g.b2s;
+      ep += __shfl_xor(ep, 16, 64);
+      ep += __shfl_xor(ep, 32, 64);
+      if (lane < kAtoms && ok) g.eps[atom] = ep + g.b2s;
     }
-    if (wave < D / 32) {
-      const int c2 = wave * 32 + li;
-      const f32x16 acc = mma_lds_glb<N1>(Ap, g.W2, D, c2, h);
+
+    f32x4 y[D / 16];
+    gemm_om<N1, D, false>(y, u, lds + P::M2, lane);
+    if (ok) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + blk_row(r, h);
-        if (m >= g.M) continue;
-        const size_t o = (size_t)m * D + c2;
-        if constexpr (MODE == ATOM_UPDATE_FWD) g.Y[o] = g.R[o] + acc[r] + g.b2[c2];
-        else g.Y[o] = acc[r];
+      for (int kb = 0; kb < D / 16; ++kb) {
+        f32x4 v = y[kb];
+        if constexpr (MODE == ATOM_UPDATE_FWD)
+          v += bload4(rR, ro + 64u * kb) + *reinterpret_cast<const f32x4*>(V2 + g4 + 16 * kb);
+        *reinterpret_cast<f32x4*>(g.Y + (size_t)atom * D + g4 + 16 * kb) = v;
       }
     }
-    __syncthreads();
   }
 }
 
-hipError_t launch_atom(const AtomArgs& g, int D, int N1, int n_cu, hipStream_t s) {
-  const int tiles = (g.M + kRows - 1) / kRows;
-  const int cap = 8 * n_cu;
-  const dim3 grid(tiles < cap ? (tiles > 0 ? tiles : 1) : cap);
-#define SN_ATOM(DD, NN, MM)                                                             \
-  if (D == DD && N1 == NN && g.mode == MM) {                                            \
-    hipLaunchKernelGGL((k_atom<DD, NN, MM>), grid, dim3(kThreads), 0, s, g);            \
-    return hipGetLastError();                                                           \
+template <int D, int N1>
+struct AtomKernels {
+  static constexpr int kD = D, kN1 = N1;
+  using P = AtomPlan<D, N1>;
+  static hipError_t prepare() {
+    hipError_t e = hipSuccess;
+    if (D == N1) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_atom<D, N1, ATOM_UPDATE_FWD>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, P::IMG);
+      if (e == hipSuccess)
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_atom<D, N1, ATOM_UPDATE_BWD>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, P::IMG);
+    } else {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_atom<D, N1, ATOM_READOUT>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, P::IMG);
+    }
+    return e;
   }
-  SN_ATOM(64, 64, ATOM_UPDATE_FWD) SN_ATOM(64, 64, ATOM_UPDATE_BWD)
-  SN_ATOM(128, 128, ATOM_UPDATE_FWD) SN_ATOM(128, 128, ATOM_UPDATE_BWD)
-  SN_ATOM(64, 32, ATOM_READOUT) SN_ATOM(64, 64, ATOM_READOUT)
-  SN_ATOM(128, 32, ATOM_READOUT) SN_ATOM(128, 64, ATOM_READOUT)
-#undef SN_ATOM
-  return hipErrorInvalidValue;
+  static hipError_t launch(const AtomArgs& g, int n_cu, hipStream_t s) {
+    const int ntiles = (g.M + kAtoms - 1) / kAtoms;
+    int G = (ntiles + kAtomNW - 1) / kAtomNW;
+    if (G > n_cu) G = n_cu;
+    if (G < 1) G = 1;
+    const dim3 grid(G), block(64 * kAtomNW);
+    switch (g.mode) {
+      case ATOM_UPDATE_FWD:
+        if (D != N1) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((k_atom<D, N1, ATOM_UPDATE_FWD>), grid, block, P::IMG, s, g);
+        break;
+      case ATOM_UPDATE_BWD:
+        if (D != N1) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((k_atom<D, N1, ATOM_UPDATE_BWD>), grid, block, P::IMG, s, g);
+        break;
+      default:
+        if (D == N1) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((k_atom<D, N1, ATOM_READOUT>), grid, block, P::IMG, s, g);
+    }
+    return hipGetLastError();
+  }
+};
+
+template <class R, class F>
+static R atom_dispatch(int D, int N1, R fail, F f) {
+#define SN_AT(DD, NN) \
+  if (D == DD && N1 == NN) return f(AtomKernels<DD, NN>{});
+  SN_AT(64, 64) SN_AT(128, 128) SN_AT(64, 32) SN_AT(128, 32) SN_AT(128, 64)
+#undef SN_AT
+  return fail;
+}
+
+hipError_t atom_prepare(int D, int H) {
+  hipError_t e = atom_dispatch(D, D, hipErrorInvalidValue,
+                               [](auto k) { return decltype(k)::prepare(); });
+  if (e != hipSuccess) return e;
+  return atom_dispatch(D, H, hipErrorInvalidValue, [](auto k) { return decltype(k)::prepare(); });
+}
+size_t atom_image_bytes(int D, int N1) {
+  return atom_dispatch(D, N1, (size_t)0, [](auto k) { return (size_t)decltype(k)::P::IMG; });
+}
+void atom_fill_image(int mode, int D, int N1, const float* W1, const float* b1, const float* W2,
+                     const float* b2, unsigned char* out) {
+  atom_dispatch(D, N1, 0, [&](auto k) {
+    using K = decltype(k);
+    fill_atom_image<K::kD, K::kN1>(mode, W1, b1, W2, b2, out);
+    return 0;
+  });
+}
+hipError_t launch_atom(const AtomArgs& g, int D, int N1, int n_cu, hipStream_t s) {
+  return atom_dispatch(D, N1, hipErrorInvalidValue,
+                       [&](auto k) { return decltype(k)::launch(g, n_cu, s); });
 }
 
 // x[i][:] = Emb[types[i]][:]
 __global__ __launch_bounds__(kThreads) void k_embed(const int32_t* types, const float* emb, int n,
-                                                    int D, int n_types, float* x, DevStatus* st) {
+                                                    int log2D, int n_types, float* x,
+                                                    DevStatus* st) {
   const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (idx >= (int64_t)n * D) return;
-  const int64_t i = idx / D;
-  const int c = (int)(idx - i * D);
+  const int D = 1 << log2D;
+  if (idx >= ((int64_t)n << log2D)) return;
+  const int64_t i = idx >> log2D;
+  const int c = (int)(idx & (D - 1));
   int t = types[i];
   if (t < 0 || t >= n_types) {
     if (c == 0) dev_fail(st, SN_ERR_INVALID_ARG, i);
@@ -168,22 +267,32 @@ __global__ __launch_bounds__(kThreads) void k_embed(const int32_t* types, const 
 
 hipError_t launch_embed(const int32_t* types, const float* emb, int n_atoms, int D, int n_types,
                         float* x, DevStatus* st, hipStream_t s) {
+  const int log2D = D == 128 ? 7 : 6;
   const int64_t n = (int64_t)n_atoms * D;
   hipLaunchKernelGGL(k_embed, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
-                     types, emb, n_atoms, D, n_types, x, st);
+                     types, emb, n_atoms, log2D, n_types, x, st);
   return hipGetLastError();
 }
 
-// E_r = sum over the replica's atoms of eps_i, accumulated in double in a fixed order.
-__global__ __launch_bounds__(kThreads) void k_energy(const float* eps, int n_per, float* energy,
-                                                     DevStatus* st) {
-  __shared__ double sm[kThreads];
+// E_r = sum over the replica's atoms of eps_i, accumulated in double in a
+// fixed order: thread t keeps four partial sums over the atoms t + 1024 q
+// (q mod 4 selecting the sum), then a fixed tree over the block.
+constexpr int kEnergyThreads = 1024;
+__global__ __launch_bounds__(kEnergyThreads) void k_energy(const float* eps, int n_per,
+                                                           float* energy, DevStatus* st) {
+  __shared__ double sm[kEnergyThreads];
   const int r = blockIdx.x;
-  double s = 0.0;
-  for (int i = threadIdx.x; i < n_per; i += kThreads) s += (double)eps[(int64_t)r * n_per + i];
-  sm[threadIdx.x] = s;
+  const float* e = eps + (int64_t)r * n_per;
+  double s[4] = {0.0, 0.0, 0.0, 0.0};
+  int i = threadIdx.x;
+  for (; i + 3 * kEnergyThreads < n_per; i += 4 * kEnergyThreads) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s[q] += (double)e[i + q * kEnergyThreads];
+  }
+  for (int q = 0; i < n_per; i += kEnergyThreads, ++q) s[q] += (double)e[i];
+  sm[threadIdx.x] = (s[0] + s[1]) + (s[2] + s[3]);
   __syncthreads();
-  for (int w = kThreads / 2; w > 0; w >>= 1) {
+  for (int w = kEnergyThreads / 2; w > 0; w >>= 1) {
     if (threadIdx.x < w) sm[threadIdx.x] += sm[threadIdx.x + w];
     __syncthreads();
   }
@@ -196,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void k_energy(const float* eps, int n_per
 
 hipError_t launch_energy(const float* eps, int n_rep, int n_per, float* energy, DevStatus* st,
                          hipStream_t s) {
-  hipLaunchKernelGGL(k_energy, dim3(n_rep), dim3(kThreads), 0, s, eps, n_per, energy, st);
+  hipLaunchKernelGGL(k_energy, dim3(n_rep), dim3(kEnergyThreads), 0, s, eps, n_per, energy, st);
   return hipGetLastError();
 }
 

@@ -18,7 +18,8 @@ struct sn_model {
   float* w = nullptr;          // device copy of the flat fp32 weights
   unsigned char* cfimg = nullptr;  // per block: the CFConv weight image (cf_fill_image)
   size_t img_bytes = 0;
-  float* wt = nullptr;         // transposed copies: per block Wu2^T, Wu1^T [D][D]; then Wo1^T [H][D]
+  unsigned char* atimg = nullptr;  // per block: update-forward then update-backward image; readout
+  size_t at_upd = 0, at_ro = 0;     // image sizes (bytes)
   float co2 = 0.f;             // readout output bias (host copy)
   size_t off_emb = 0, off_o1 = 0, off_co1 = 0, off_o2 = 0;
   std::vector<size_t> off_blk; // start of each interaction block
@@ -94,11 +95,11 @@ struct ProfScope {
 };
 
 // ---------------------------------------------------------------- E+F orchestration
-// Work-groups for a CFConv kernel: one per CU for large systems (its LDS plan
-// allows one resident group), fewer for small ones so that every worker
-// (wave) gets a few receivers.
+// Work-groups for a CFConv kernel: one per CU (its LDS plan allows one
+// resident group), fewer only when there are not enough receivers to give
+// every worker (wave) one.
 int cf_grid(const sn_model* m, int64_t n, int workers) {
-  int64_t g = (n + 4 * workers - 1) / (4 * workers);
+  int64_t g = (n + workers - 1) / workers;
   if (g > m->n_cu) g = m->n_cu;
   if (g * workers > kMaxWorkers) g = kMaxWorkers / workers;
   return (int)(g < 1 ? 1 : g);
@@ -164,9 +165,10 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
     }
   };
 
-  const size_t DD = (size_t)D * D;
-  auto WuT = [&](int t, int k) { return m->wt + (size_t)t * 2 * DD + (size_t)k * DD; };  // 0: Wu2^T, 1: Wu1^T
-  const float* Wo1T = m->wt + (size_t)T * 2 * DD;
+  auto atom_img = [&](int t, int bwd) -> const void* {
+    return m->atimg + (size_t)t * 2 * m->at_upd + (bwd ? m->at_upd : 0);
+  };
+  const void* ro_img = m->atimg + (size_t)T * 2 * m->at_upd;
 
   // forward
   for (int t = 0; t < T; ++t) {
@@ -178,14 +180,13 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
       ProfScope ps(0, s);
       if ((e = launch_cf_forward(D, m->KP, bf16, p, Gf, s)) != hipSuccess) return hip_fail(e);
     }
-    AtomArgs u{ATOM_UPDATE_FWD, (int)n, gbuf, nullptr, nullptr, Wu(t, 0), Wu(t, 1), Wu(t, 2),
-               Wu(t, 3), x + t * ND, nullptr, au + t * ND, x + (t + 1) * ND, nullptr, 0.f, nullptr};
+    AtomArgs u{ATOM_UPDATE_FWD, (int)n, gbuf, nullptr, nullptr, x + t * ND, nullptr, au + t * ND,
+               x + (t + 1) * ND, 0.f, nullptr, atom_img(t, 0)};
     if ((e = launch_atom(u, D, D, m->n_cu, s)) != hipSuccess) return hip_fail(e);
   }
   // readout and its gradient
-  AtomArgs r{ATOM_READOUT, (int)n, x + T * ND, nullptr, nullptr, m->w + m->off_o1,
-             m->w + m->off_co1, Wo1T, nullptr, nullptr, nullptr, nullptr, gx,
-             m->w + m->off_o2, m->co2, eps};
+  AtomArgs r{ATOM_READOUT, (int)n, x + T * ND, nullptr, nullptr, nullptr, nullptr, nullptr, gx,
+             m->co2, eps, ro_img};
   if ((e = launch_atom(r, D, H, m->n_cu, s)) != hipSuccess) return hip_fail(e);
   if ((e = launch_energy(eps, sys->n_replicas, sys->atoms_per_replica, energy, st, s)) !=
       hipSuccess)
@@ -195,8 +196,7 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
   for (int t = T - 1; t >= 0; --t) {
     const bool has_q = t < T - 1;
     AtomArgs b{ATOM_UPDATE_BWD, (int)n, gx, has_q ? tmp : nullptr, (has_q && t > 0) ? gx : nullptr,
-               WuT(t, 0), nullptr, WuT(t, 1), nullptr, nullptr, au + t * ND, nullptr, gbuf,
-               nullptr, 0.f, nullptr};
+               nullptr, au + t * ND, nullptr, gbuf, 0.f, nullptr, atom_img(t, 1)};
     if ((e = launch_atom(b, D, D, m->n_cu, s)) != hipSuccess) return hip_fail(e);
     p.img = block_img(t);
     p.wg_start = wg_start_b;
@@ -381,28 +381,26 @@ sn_status sn_model_create(const sn_model_desc* d, const float* weights_host, siz
     e = (per == 0) ? hipErrorInvalidValue : hipMalloc(&m->cfimg, hi.size());
     if (e == hipSuccess) e = hipMemcpy(m->cfimg, hi.data(), hi.size(), hipMemcpyHostToDevice);
   }
+  if (e == hipSuccess) e = atom_prepare(d->D, d->H);
   if (e == hipSuccess) {
-    // transposed copies for the backward products: Wu2^T and Wu1^T per block, Wo1^T
+    // atom-wise weight images, laid out as the kernels hold them in LDS
+    m->at_upd = atom_image_bytes(d->D, d->D);
+    m->at_ro = atom_image_bytes(d->D, d->H);
+    std::vector<unsigned char> ha(2 * m->at_upd * d->T + m->at_ro);
     const size_t DD = D * D;
-    std::vector<float> ht(2 * DD * d->T + H * D);
     for (int t = 0; t < d->T; ++t) {
       const float* Wu1 = weights_host + m->off_blk[t] + (size_t)d->Dr * D + D + DD + D;
-      const float* Wu2 = Wu1 + DD + D;
-      float* o2 = ht.data() + 2 * DD * t;
-      float* o1 = o2 + DD;
-      for (size_t k = 0; k < D; ++k)
-        for (size_t c = 0; c < D; ++c) {
-          o2[c * D + k] = Wu2[k * D + c];
-          o1[c * D + k] = Wu1[k * D + c];
-        }
+      const float* cu1 = Wu1 + DD;
+      const float* Wu2 = cu1 + D;
+      const float* cu2 = Wu2 + DD;
+      unsigned char* o = ha.data() + (size_t)t * 2 * m->at_upd;
+      atom_fill_image(ATOM_UPDATE_FWD, d->D, d->D, Wu1, cu1, Wu2, cu2, o);
+      atom_fill_image(ATOM_UPDATE_BWD, d->D, d->D, Wu1, cu1, Wu2, cu2, o + m->at_upd);
     }
-    const float* Wo1 = weights_host + m->off_o1;
-    float* ot = ht.data() + 2 * DD * d->T;
-    for (size_t k = 0; k < D; ++k)
-      for (size_t c = 0; c < H; ++c) ot[c * D + k] = Wo1[k * H + c];
-    e = hipMalloc(&m->wt, ht.size() * sizeof(float));
-    if (e == hipSuccess)
-      e = hipMemcpy(m->wt, ht.data(), ht.size() * sizeof(float), hipMemcpyHostToDevice);
+    atom_fill_image(ATOM_READOUT, d->D, d->H, weights_host + m->off_o1, weights_host + m->off_co1,
+                    weights_host + m->off_o2, nullptr, ha.data() + (size_t)d->T * 2 * m->at_upd);
+    e = (m->at_upd == 0 || m->at_ro == 0) ? hipErrorInvalidValue : hipMalloc(&m->atimg, ha.size());
+    if (e == hipSuccess) e = hipMemcpy(m->atimg, ha.data(), ha.size(), hipMemcpyHostToDevice);
   }
   if (e != hipSuccess) {
     sn_model_destroy(m);
@@ -416,7 +414,7 @@ void sn_model_destroy(sn_model* m) {
   if (!m) return;
   if (m->w) (void)hipFree(m->w);
   if (m->cfimg) (void)hipFree(m->cfimg);
-  if (m->wt) (void)hipFree(m->wt);
+  if (m->atimg) (void)hipFree(m->atimg);
   delete m;
 }
 

@@ -54,98 +54,16 @@
 #include <climits>
 #include <cstring>
 
-#include "common.hpp"
+#include "tile16.hpp"
 
 namespace sn {
 
-#define LN2F 0.69314718055994530942f
-#define LOG2EF 1.44269504088896340736f
-
 constexpr int kEdges = 16;  // edges per wave tile: the MFMA column dimension
-
-// ------------------------------------------------------------------ small helpers
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
-// Bounded loads: an offset past the resource's size reads 0.
-__device__ __forceinline__ float bload(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
-}
-__device__ __forceinline__ int bload_i(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
-  return (int)__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0);
-}
-__device__ __forceinline__ f32x4 bload4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
-  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
-}
-__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
-
-// Wave-uniform read of a read-only int array through the scalar cache.
-__device__ __forceinline__ int cload(const int32_t* p, int i) {
-  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
-}
-
-// A copy of v the compiler cannot see through. Addresses derived from it are
-// recomputed where they are used instead of being hoisted out of the tile loop
-// and held in registers for the whole kernel.
-__device__ __forceinline__ int opaque(int v) {
-  asm volatile("" : "+v"(v));
-  return v;
-}
-
-// Orders this wave's LDS writes before its later LDS reads (wave-private data).
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// e^x for x <= 0 and ln(y) for y in [1, 2], on the hardware exp2 / log2.
-__device__ __forceinline__ float exp_neg(float x) { return __builtin_amdgcn_exp2f(x * LOG2EF); }
-__device__ __forceinline__ float ln_1_2(float y) { return __builtin_amdgcn_logf(y) * LN2F; }
-
-// Shifted softplus and its derivative (the logistic sigmoid) from t = exp(-|a|).
-__device__ __forceinline__ void ssp_sig(float a, float& s, float& sg) {
-  const float t = exp_neg(-fabsf(a));
-  const float inv = __builtin_amdgcn_rcpf(1.f + t);
-  s = fmaxf(a, 0.f) + ln_1_2(1.f + t) - LN2F;
-  sg = a >= 0.f ? inv : t * inv;
-}
-__device__ __forceinline__ float ssp(float a) {
-  const float t = exp_neg(-fabsf(a));
-  return fmaxf(a, 0.f) + ln_1_2(1.f + t) - LN2F;
-}
 
 __device__ __forceinline__ float min_image(float u, float box, float half) {
   if (u > half) return u - box;
   if (u < -half) return u + box;
   return u;
-}
-
-__device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// XOR-swizzled offset of element (row, col) of a row-major array with RL
-// elements per row: 16-byte chunks (4 fp32 or 8 bf16) trade places by row, so
-// that the 16 rows one lane group reads at a common column hit distinct banks.
-template <int RL>
-__host__ __device__ __forceinline__ int sw4(int row, int col) {
-  constexpr int M = (RL / 4 >= 16) ? 15 : RL / 4 - 1;
-  return row * RL + ((((col >> 2) ^ (row & M)) << 2) | (col & 3));
-}
-template <int RL>
-__host__ __device__ __forceinline__ int sw8(int row, int col) {
-  constexpr int M = (RL / 8 >= 16) ? 15 : RL / 8 - 1;
-  return row * RL + ((((col >> 3) ^ (row & M)) << 3) | (col & 7));
-}
-// bf16 chained products: position of contraction index k in its group of 32,
-// so that lane group g finds the 8 k values its accumulator rows hold
-// (4g..4g+3 of two consecutive 16-feature blocks) in one 16-byte run.
-__host__ __device__ constexpr int perm32(int k) {
-  return (k & ~31) | (((k >> 2) & 3) << 3) | (((k >> 4) & 1) << 2) | (k & 3);
 }
 
 // ------------------------------------------------------------------ LDS plan
@@ -312,64 +230,6 @@ __device__ __forceinline__ void gemm1(f32x4 (&acc)[NA][D / 16], const unsigned c
           for (int q = 0; q < NA; ++q) acc[q][nb] = mfma16(w[u], b[q][u], acc[q][nb]);
       }
     }
-  }
-}
-
-// B operands of a chained product from an accumulator-layout input: fp32 uses
-// the accumulator registers directly; bf16 packs them once (k slot 8 g + t of
-// step kk is register t % 4 of block 2 kk + t / 4).
-template <int D, bool BF16>
-struct Operand;
-template <int D>
-struct Operand<D, false> {
-  const f32x4 (&S)[D / 16];
-  __device__ __forceinline__ explicit Operand(const f32x4 (&s)[D / 16]) : S(s) {}
-};
-template <int D>
-struct Operand<D, true> {
-  bf16x8 S[D / 32];
-  __device__ __forceinline__ explicit Operand(const f32x4 (&s)[D / 16]) {
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk)
-#pragma unroll
-      for (int t = 0; t < 8; ++t) S[kk][t] = (__bf16)s[2 * kk + (t >> 2)][t & 3];
-  }
-};
-
-// acc += sum_k M[16 nb + e][k] S[k] for one output block nb; M is an
-// output-major image (fp32: sw4 rows; bf16: sw8 rows with perm32 positions).
-template <int D, bool BF16>
-__device__ __forceinline__ void gemm_om_block(f32x4& acc, const Operand<D, BF16>& op,
-                                              const void* img, int nb, int grp, int e) {
-  if constexpr (BF16) {
-    const __bf16* M = reinterpret_cast<const __bf16*>(img);
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {
-      const bf16x8 w = *reinterpret_cast<const bf16x8*>(M + sw8<D>(16 * nb + e, 32 * kk + 8 * grp));
-      acc = mfma16(w, op.S[kk], acc);
-    }
-  } else {
-    const float* M = reinterpret_cast<const float*>(img);
-#pragma unroll
-    for (int kb = 0; kb < D / 16; ++kb) {
-      const f32x4 w = *reinterpret_cast<const f32x4*>(M + sw4<D>(16 * nb + e, 16 * kb + 4 * grp));
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc = mfma16(w[r], op.S[kb][r], acc);
-    }
-  }
-}
-
-// All output blocks: out[nb] = sum_k M[16 nb + e][k] S[k].
-template <int D, bool BF16>
-__device__ __forceinline__ void gemm_om(f32x4 (&out)[D / 16], const f32x4 (&S)[D / 16],
-                                        const void* img, int lane_) {
-  const int lane = opaque(lane_), grp = lane >> 4, e = lane & 15;
-  const Operand<D, BF16> op(S);
-#pragma unroll
-  for (int nb = 0; nb < D / 16; ++nb) {
-    f32x4 acc = f32x4{};
-    gemm_om_block<D, BF16>(acc, op, img, nb, grp, e);
-    out[nb] = acc;
   }
 }
 
@@ -554,7 +414,7 @@ __global__ __launch_bounds__((64 * cf_nw<D, BF16, false>()), 1) void k_cf_fwd(Cf
     // w = s Wf2 + cf2 (masked beyond the cutoff); messages x_j * w summed per
     // receiver, 64 features at a time
     f32x4 w[NB];
-    gemm_om<D, BF16>(w, s[0], lds + P::W2, lane);
+    gemm_om<D, D, BF16>(w, s[0], lds + P::W2, lane);
     const uint32_t xo = ((uint32_t)th.j * (uint32_t)D + (uint32_t)g4) * 4u;
 #pragma unroll
     for (int pss = 0; pss < NB / 4; ++pss) {
@@ -642,8 +502,8 @@ __global__ __launch_bounds__((64 * cf_nw<D, BF16, true>()), 1) void k_cf_bwd(CfP
 
     // GEMM2 for the tangents, then the values: w' = s' Wf2, w = s Wf2
     f32x4 wt[NB], wv[NB];
-    gemm_om<D, BF16>(wt, av[1], lds + P::W2, lane);
-    gemm_om<D, BF16>(wv, av[0], lds + P::W2, lane);
+    gemm_om<D, D, BF16>(wt, av[1], lds + P::W2, lane);
+    gemm_om<D, D, BF16>(wv, av[0], lds + P::W2, lane);
 
     // per 64 features: q = dE/dh_j w summed per receiver;
     // dE/dd += <dE/dh_i x_j + dE/dh_j x_i, w'>

@@ -111,18 +111,20 @@ struct AtomArgs {
   const float* A;     // [M][D]: h (update fwd), dE/dx' (update bwd), x^(T) (readout)
   const float* A2;    // update bwd: added to A when not null (the CFConv source sum)
   float* Asum;        // update bwd: A + A2 is stored here when not null
-  const float* W1;    // first product, row-major [D][N1]
-  const float* b1;    // [N1] (update fwd, readout)
-  const float* W2;    // second product, row-major [N1][D]
-  const float* b2;    // [D] (update fwd)
   const float* R;     // residual x [M][D] (update fwd)
-  const float* S;     // pre-activation a [M][D] (update bwd)
-  float* Aout;        // pre-activation a [M][D] (update fwd)
+  const float* S;     // pre-activation a [M][N1] (update bwd)
+  float* Aout;        // pre-activation a [M][N1] (update fwd)
   float* Y;           // [M][D]: x', dE/dh, or dE/dx^(T)
-  const float* w2;    // readout output weights [N1]
   float b2s;          // readout output bias
   float* eps;         // per-atom energies [M] (readout)
+  const void* img;    // the network's weight image (atom_fill_image)
 };
+// Weight image of one atom-wise network for `mode`: W1 [D][N1], b1 [N1],
+// W2 [N1][D] (readout: wo2 [N1]), b2 [D]; built on the host.
+size_t atom_image_bytes(int D, int N1);
+void atom_fill_image(int mode, int D, int N1, const float* W1, const float* b1, const float* W2,
+                     const float* b2, unsigned char* out);
+hipError_t atom_prepare(int D, int H);   // raises the dynamic LDS limit of the kernels
 hipError_t launch_atom(const AtomArgs& g, int D, int N1, int n_cu, hipStream_t s);
 hipError_t launch_embed(const int32_t* types, const float* emb, int n_atoms, int D, int n_types,
                         float* x, DevStatus* st, hipStream_t s);
