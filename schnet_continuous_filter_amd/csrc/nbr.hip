@@ -228,6 +228,11 @@ __global__ __launch_bounds__(kThreads) void k_cell_scatter(int N, const int32_t*
   cell_atoms[cell_start[c] + slot] = i;
 }
 
+// One wave per receiver i. The members of the 27 cells around i's cell form
+// one candidate list (cell order, then slot order); lanes take 64 candidates
+// at a time, each finding its cell by a binary search over the cells'
+// offsets, so the loads of a round are independent. Hits are compacted with a
+// ballot; k_sort_rows orders each row afterwards.
 template <bool FILL>
 __global__ __launch_bounds__(kThreads) void k_nbr_cells(const float* __restrict__ pos, int N, int nc,
                                                         double L, double half, double r2,
@@ -238,33 +243,54 @@ __global__ __launch_bounds__(kThreads) void k_nbr_cells(const float* __restrict_
                                                         const int64_t* gate, int64_t gate_val) {
   SN_GATE
   if (FILL && st->overflow) return;
-  const int i = blockIdx.x * kThreads + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int i = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   if (i >= N) return;
   const float xi = pos[3 * i + 0], yi = pos[3 * i + 1], zi = pos[3 * i + 2];
   const int c = atom_cell[i];
   const int cx = c % nc, cy = (c / nc) % nc, cz = c / (nc * nc);
-  int cnt = 0;
-  int64_t out = FILL ? rowptr[i] : 0;
-  for (int dz = -1; dz <= 1; ++dz) {
-    const int zz = (cz + dz + nc) % nc;
-    for (int dy = -1; dy <= 1; ++dy) {
-      const int yy = (cy + dy + nc) % nc;
-      for (int dx = -1; dx <= 1; ++dx) {
-        const int xx = (cx + dx + nc) % nc;
-        const int cc = (zz * nc + yy) * nc + xx;
-        const int k1 = cell_start[cc + 1];
-        for (int k = cell_start[cc]; k < k1; ++k) {
-          const int j = cell_atoms[k];
-          if (j != i && pair_in(xi, yi, zi, pos[3 * j], pos[3 * j + 1], pos[3 * j + 2], 1, L,
-                                half, r2)) {
-            if (FILL) col[out++] = j;
-            else ++cnt;
-          }
-        }
-      }
-    }
+  // lanes 0..26: start and size of one neighbouring cell (27 distinct cells, nc >= 3)
+  int cs = 0, cn = 0;
+  if (lane < 27) {
+    const int dz = lane / 9 - 1, dy = (lane / 3) % 3 - 1, dx = lane % 3 - 1;
+    const int cc = (((cz + dz + nc) % nc) * nc + (cy + dy + nc) % nc) * nc + (cx + dx + nc) % nc;
+    cs = cell_start[cc];
+    cn = cell_start[cc + 1] - cs;
   }
-  if (!FILL) rowptr[i] = cnt;
+  int incl = cn;
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  const int excl = incl - cn;
+  const int total = __shfl(incl, 26, 64);
+  int64_t out = FILL ? rowptr[i] : 0;
+  int cnt = 0;
+  for (int f0 = 0; f0 < total; f0 += 64) {
+    const int f = f0 + lane;
+    // the last cell whose offset is <= f (empty cells share the next cell's offset)
+    int lo = 0, hi = 26;
+#pragma unroll
+    for (int step = 0; step < 5; ++step) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (__shfl(excl, mid, 64) <= f) lo = mid;
+      else hi = mid - 1;
+    }
+    const int k = __shfl(cs, lo, 64) + (f - __shfl(excl, lo, 64));
+    bool in = false;
+    int j = 0;
+    if (f < total) {
+      j = cell_atoms[k];
+      in = j != i && pair_in(xi, yi, zi, pos[3 * j], pos[3 * j + 1], pos[3 * j + 2], 1, L, half, r2);
+    }
+    const uint64_t m = __ballot(in);
+    if (FILL && in) col[out + __popcll(m & ((1ull << lane) - 1))] = j;
+    const int nh = __popcll(m);
+    out += nh;
+    cnt += nh;
+  }
+  if (!FILL && lane == 0) rowptr[i] = cnt;
 }
 
 // Rank sort of each row (distinct values), one wave per row, staged in LDS.
@@ -333,12 +359,13 @@ hipError_t launch_build_neighbors(const NbrGeom& g, const float* pos, int32_t* r
     return e;
   hipLaunchKernelGGL(k_cell_scatter, dim3(blocks_for(N)), dim3(kThreads), 0, s, N, acell, cstart,
                      ccur, catoms, gate, gate_val);
-  hipLaunchKernelGGL(k_nbr_cells<false>, dim3(blocks_for(N)), dim3(kThreads), 0, s, pos, N, nc,
+  const dim3 wave_grid((unsigned)((N + kThreads / 64 - 1) / (kThreads / 64)));
+  hipLaunchKernelGGL(k_nbr_cells<false>, wave_grid, dim3(kThreads), 0, s, pos, N, nc,
                      g.L, g.half, g.r2, acell, cstart, catoms, rowptr, col, st, gate, gate_val);
   if ((e = launch_exclusive_scan(rowptr, N, scan_blocks, st, edge_capacity, gate, gate_val, s)) !=
       hipSuccess)
     return e;
-  hipLaunchKernelGGL(k_nbr_cells<true>, dim3(blocks_for(N)), dim3(kThreads), 0, s, pos, N, nc, g.L,
+  hipLaunchKernelGGL(k_nbr_cells<true>, wave_grid, dim3(kThreads), 0, s, pos, N, nc, g.L,
                      g.half, g.r2, acell, cstart, catoms, rowptr, col, st, gate, gate_val);
   hipLaunchKernelGGL(k_sort_rows, dim3((unsigned)((N + 3) / 4)), dim3(kThreads), 0, s, rowptr, col,
                      N, st, gate, gate_val);
