@@ -16,7 +16,6 @@ and the fp64 oracle timed on the host cores on a bounded sample.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -25,11 +24,12 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+from schnet_continuous_filter_amd import profiling  # noqa: E402  (no GPU work at import)
+
 PEAK_FP32_MFMA_TFLOPS = 157.3     # MI355X dense fp32 matrix peak
 PEAK_BF16_MFMA_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cfconv_bwd_cg269x64_counters.txt")
-CFCONV_SRC = os.path.join(ROOT, "schnet_continuous_filter_amd", "csrc", "cfconv.hip")
 
 
 def parse():
@@ -44,10 +44,6 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a device copy of known size (for counter scaling)")
     return ap.parse_args()
-
-
-def kernel_hash() -> str:
-    return hashlib.sha256(open(CFCONV_SRC, "rb").read()).hexdigest()[:16]
 
 
 def copy_calibration():
@@ -183,7 +179,7 @@ def main():
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         rec = json.load(open(TRAFFIC_FILE))
-        if rec.get("kernel_hash") == kernel_hash() and rec.get("workload") == cfg.name:
+        if rec.get("kernel_hash") == profiling.kernel_hash() and rec.get("workload") == cfg.name:
             traffic = rec.get("bytes_per_launch")
     line = {
         "metric": "CFConv energy+force edges/sec and replica-MD-steps/sec at 1 GPU; % HBM roofline",

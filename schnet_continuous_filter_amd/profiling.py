@@ -19,12 +19,17 @@ import hashlib
 import json
 import os
 
-CFCONV_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", "cfconv.hip")
+_CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+CFCONV_SRCS = [os.path.join(_CSRC, f) for f in ("cfconv.hip", "tile16.hpp", "common.hpp")]
 COPY_BYTES = 256 * 1024 * 1024
 
 
 def kernel_hash() -> str:
-    return hashlib.sha256(open(CFCONV_SRC, "rb").read()).hexdigest()[:16]
+    """Hash of the sources the CFConv kernels are compiled from."""
+    h = hashlib.sha256()
+    for f in CFCONV_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def stats(csv_path: str, out_txt: str, cmd: str, top: int = 25) -> None:
