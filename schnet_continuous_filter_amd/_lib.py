@@ -83,6 +83,9 @@ _SIGNATURES = {
 
 
 def _load():
+    # torch first: the library must bind to the HIP runtime torch brings, or
+    # two runtimes end up in the process and torch finds no device
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                            "`python -c 'import __graft_entry__ as g; g.build()'`")

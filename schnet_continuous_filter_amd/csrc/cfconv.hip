@@ -412,21 +412,27 @@ __global__ __launch_bounds__((64 * cf_nw<D, BF16, false>()), 1) void k_cf_fwd(Cf
     pjz = bload(wk.rpos, (uint32_t)jn * 12u + 8);
 
     // w = s Wf2 + cf2 (masked beyond the cutoff); messages x_j * w summed per
-    // receiver, 64 features at a time
+    // receiver, 64 features at a time. The sender rows of the first 64
+    // features are requested ahead of the product; a block's registers are
+    // refilled with the next 64 features' as soon as they are used.
+    const uint32_t xo = ((uint32_t)th.j * (uint32_t)D + (uint32_t)g4) * 4u;
+    f32x4 xg[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) xg[b] = bload4(rx, xo + (uint32_t)(64 * b));
+    __builtin_amdgcn_sched_barrier(0);
     f32x4 w[NB];
     gemm_om<D, D, BF16>(w, s[0], lds + P::W2, lane);
-    const uint32_t xo = ((uint32_t)th.j * (uint32_t)D + (uint32_t)g4) * 4u;
 #pragma unroll
     for (int pss = 0; pss < NB / 4; ++pss) {
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int nb = 4 * pss + b;
-        const f32x4 xg = bload4(rx, xo + (uint32_t)(64 * nb));
         const f32x4 c2 = bias4<P>(p, lds, g4, D + 16 * nb);
         f32x4 m;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) m[r] = xg[r] * (g.in * (w[nb][r] + c2[r]));
+        for (int r = 0; r < 4; ++r) m[r] = xg[b][r] * (g.in * (w[nb][r] + c2[r]));
         tile_put(Tb, b, m, lane);
+        if (pss + 1 < NB / 4) xg[b] = bload4(rx, xo + (uint32_t)(64 * (nb + 4)));
       }
       wave_sync();
       float* hout = p.h + 64 * pss + fcol;
@@ -500,32 +506,56 @@ __global__ __launch_bounds__((64 * cf_nw<D, BF16, true>()), 1) void k_cf_bwd(CfP
     pjy = bload(wk.rpos, (uint32_t)jn * 12u + 4);
     pjz = bload(wk.rpos, (uint32_t)jn * 12u + 8);
 
-    // GEMM2 for the tangents, then the values: w' = s' Wf2, w = s Wf2
-    f32x4 wt[NB], wv[NB];
-    gemm_om<D, D, BF16>(wt, av[1], lds + P::W2, lane);
-    gemm_om<D, D, BF16>(wv, av[0], lds + P::W2, lane);
-
-    // per 64 features: q = dE/dh_j w summed per receiver;
-    // dE/dd += <dE/dh_i x_j + dE/dh_j x_i, w'>
+    // gathers of the first 64 features (x_j, dE/dh_j, x_i, dE/dh_i), issued
+    // ahead of the tangent product so that their latency is covered
     const uint32_t jo = ((uint32_t)th.j * (uint32_t)D + (uint32_t)g4) * 4u;
     const uint32_t io = ((uint32_t)th.recv * (uint32_t)D + (uint32_t)g4) * 4u;
+    f32x4 G[4][4];
+    auto gather = [&](int nb, f32x4 (&Gb)[4]) {
+      const uint32_t co = (uint32_t)(64 * nb);
+      Gb[0] = bload4(rx, jo + co);
+      Gb[1] = bload4(rgh, jo + co);
+      Gb[2] = bload4(rx, io + co);
+      Gb[3] = bload4(rgh, io + co);
+    };
+#pragma unroll
+    for (int b = 0; b < 4; ++b) gather(b, G[b]);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // GEMM2 for the tangents, all blocks (frees s'): w' = s' Wf2; the values
+    // w = s Wf2 follow one output block at a time
+    f32x4 wt[NB];
+    gemm_om<D, D, BF16>(wt, av[1], lds + P::W2, lane);
+    const Operand<D, BF16> os(av[0]);
+
+    // per 64 features: q = dE/dh_j w summed per receiver;
+    // dE/dd += <dE/dh_i x_j + dE/dh_j x_i, w'>. A block's gather registers
+    // are refilled with the next 64 features' as soon as they are used.
     float gdd = 0.f;
 #pragma unroll
     for (int pss = 0; pss < NB / 4; ++pss) {
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int nb = 4 * pss + b;
-        const uint32_t co = (uint32_t)(64 * nb);
-        const f32x4 xj = bload4(rx, jo + co), gj = bload4(rgh, jo + co);
-        const f32x4 xi = bload4(rx, io + co), gi = bload4(rgh, io + co);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 wv = f32x4{};
+        {
+          const int lane_o = opaque(lane);
+          gemm_om_block<D, BF16>(wv, os, lds + P::W2, nb, lane_o >> 4, lane_o & 15);
+        }
+        const f32x4 xj = G[b][0], gj = G[b][1], xi = G[b][2], gi = G[b][3];
         const f32x4 c2 = bias4<P>(p, lds, g4, D + 16 * nb);
         f32x4 qv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          qv[r] = gj[r] * (g.in * (wv[nb][r] + c2[r]));
+          qv[r] = gj[r] * (g.in * (wv[r] + c2[r]));
           gdd = fmaf(gi[r] * xj[r] + gj[r] * xi[r], wt[nb][r], gdd);
         }
         if (want_q) tile_put(Tb, b, qv, lane);
+        if (pss + 1 < NB / 4) {
+          gather(nb + 4, G[b]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       if (want_q) {
         wave_sync();
