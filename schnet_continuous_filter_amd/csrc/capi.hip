@@ -151,6 +151,7 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
   p.rbf_inv_s2 = 1.f / (step * step);
   p.r_cut = d.r_cut;
   p.pi_over_rc = (float)(M_PI / (double)d.r_cut);
+  p.half_over_rc = (float)(0.5 / (double)d.r_cut);
   p.KC = cf_chunks(d.Dr, bf16);
 
   auto block_img = [&](int t) -> const void* { return m->cfimg + (size_t)t * m->img_bytes; };

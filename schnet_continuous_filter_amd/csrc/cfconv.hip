@@ -165,15 +165,17 @@ __device__ __forceinline__ Geo geometry(const CfParams& p, __amdgpu_buffer_rsrc_
     uy = min_image(uy, p.box, p.half_box);
     uz = min_image(uz, p.box, p.half_box);
   }
-  const float d = sqrtf(ux * ux + uy * uy + uz * uz);
-  float sn, cs;
-  sincosf(p.pi_over_rc * d, &sn, &cs);
+  // hardware sqrt / rcp (1 ulp) and sin / cos of an angle given in turns,
+  // d / (2 r_c) in [0, 1/2] (about 1e-7 absolute)
+  const float d = __builtin_amdgcn_sqrtf(ux * ux + uy * uy + uz * uz);
+  const float turns = fminf(d, p.r_cut) * p.half_over_rc;
+  const float cs = __builtin_amdgcn_cosf(turns), sn = __builtin_amdgcn_sinf(turns);
   Geo g;
   g.d0 = d - p.rbf_min;
   g.in = (valid && d < p.r_cut) ? 1.f : 0.f;
   g.C = 0.5f * (cs + 1.f);
   g.Cp = -0.5f * p.pi_over_rc * sn;
-  g.invd = d > 0.f ? 1.f / d : 0.f;
+  g.invd = d > 0.f ? __builtin_amdgcn_rcpf(d) : 0.f;
   g.ux = ux; g.uy = uy; g.uz = uz;
   return g;
 }
@@ -266,11 +268,21 @@ __device__ __forceinline__ int tpos(int col, int row) {
 __host__ __device__ __forceinline__ int col_feature(int L) {
   return 16 * (L >> 4) + 4 * (L & 3) + ((L >> 2) & 3);
 }
-// Writes accumulator block b (0..3) of the current 64 features.
-__device__ __forceinline__ void tile_put(float* Tb, int b, const f32x4& m, int lane_) {
-  const int lane = opaque(lane_), grp = lane >> 4, e = lane & 15;
+// Element offsets, in the transpose tile, of this lane's accumulator
+// elements r = 0..3 of block 0; block b adds 256 b (tpos(16 b + c, row) =
+// 256 b + tpos(c, row) for c < 16). Built once per tile.
+struct TileLanes {
+  int off[4];
+  __device__ __forceinline__ explicit TileLanes(int lane) {
+    const int grp = lane >> 4, e = lane & 15;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) Tb[tpos(16 * b + 4 * r + grp, e)] = m[r];
+    for (int r = 0; r < 4; ++r) off[r] = tpos(4 * r + grp, e);
+  }
+};
+// Writes accumulator block b (0..3) of the current 64 features.
+__device__ __forceinline__ void tile_put(float* Tb, int b, const f32x4& m, const TileLanes& tl) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) Tb[256 * b + tl.off[r]] = m[r];
 }
 
 // Per-receiver sums of this lane's column of the tile (rows past the tile's
@@ -394,7 +406,12 @@ __global__ __launch_bounds__((64 * cf_nw<D, BF16, false>()), 1) void k_cf_fwd(Cf
   for (int ts = wk.E0; ts < wk.E1; ts += kEdges) {
     const TileHead th = tile_head(p, wk, ts, cur, win, jn, pjx, pjy, pjz, lane, e);
     const Geo& g = th.g;
-    const int g4 = 4 * (opaque(lane) >> 4);   // this lane's feature offset in a block
+    // per-lane offsets, rebuilt each tile (kept for the whole kernel they would
+    // only occupy registers)
+    const int lane_t = opaque(lane);
+    const int g4 = 4 * (lane_t >> 4);   // this lane's feature offset in a block
+    const ImgLanes<D, BF16> wl(lane_t);
+    const TileLanes tl(lane_t);
 
     // s = ssp(b~ Wf1 + cf1)
     f32x4 s[1][NB];
@@ -421,7 +438,7 @@ __global__ __launch_bounds__((64 * cf_nw<D, BF16, false>()), 1) void k_cf_fwd(Cf
     for (int b = 0; b < 4; ++b) xg[b] = bload4(rx, xo + (uint32_t)(64 * b));
     __builtin_amdgcn_sched_barrier(0);
     f32x4 w[NB];
-    gemm_om<D, D, BF16>(w, s[0], lds + P::W2, lane);
+    gemm_om<D, D, BF16>(w, s[0], lds + P::W2, wl);
 #pragma unroll
     for (int pss = 0; pss < NB / 4; ++pss) {
 #pragma unroll
@@ -431,7 +448,7 @@ __global__ __launch_bounds__((64 * cf_nw<D, BF16, false>()), 1) void k_cf_fwd(Cf
         f32x4 m;
 #pragma unroll
         for (int r = 0; r < 4; ++r) m[r] = xg[b][r] * (g.in * (w[nb][r] + c2[r]));
-        tile_put(Tb, b, m, lane);
+        tile_put(Tb, b, m, tl);
         if (pss + 1 < NB / 4) xg[b] = bload4(rx, xo + (uint32_t)(64 * (nb + 4)));
       }
       wave_sync();
@@ -481,7 +498,12 @@ __global__ __launch_bounds__((64 * cf_nw<D, BF16, true>()), 1) void k_cf_bwd(CfP
   for (int ts = wk.E0; ts < wk.E1; ts += kEdges) {
     const TileHead th = tile_head(p, wk, ts, cur, win, jn, pjx, pjy, pjz, lane, e);
     const Geo& g = th.g;
-    const int g4 = 4 * (opaque(lane) >> 4);   // this lane's feature offset in a block
+    // per-lane offsets, rebuilt each tile (kept for the whole kernel they would
+    // only occupy registers)
+    const int lane_t = opaque(lane);
+    const int g4 = 4 * (lane_t >> 4);   // this lane's feature offset in a block
+    const ImgLanes<D, BF16> wl(lane_t);
+    const TileLanes tl(lane_t);
 
     // GEMM1: a = b~ Wf1 + cf1 and its tangent a' = (d b~/dd) Wf1;
     // s = ssp(a), s' = sigmoid(a) a'
@@ -525,7 +547,7 @@ __global__ __launch_bounds__((64 * cf_nw<D, BF16, true>()), 1) void k_cf_bwd(CfP
     // GEMM2 for the tangents, all blocks (frees s'): w' = s' Wf2; the values
     // w = s Wf2 follow one output block at a time
     f32x4 wt[NB];
-    gemm_om<D, D, BF16>(wt, av[1], lds + P::W2, lane);
+    gemm_om<D, D, BF16>(wt, av[1], lds + P::W2, wl);
     const Operand<D, BF16> os(av[0]);
 
     // per 64 features: q = dE/dh_j w summed per receiver;
@@ -539,10 +561,7 @@ __global__ __launch_bounds__((64 * cf_nw<D, BF16, true>()), 1) void k_cf_bwd(CfP
         const int nb = 4 * pss + b;
         __builtin_amdgcn_sched_barrier(0);
         f32x4 wv = f32x4{};
-        {
-          const int lane_o = opaque(lane);
-          gemm_om_block<D, BF16>(wv, os, lds + P::W2, nb, lane_o >> 4, lane_o & 15);
-        }
+        gemm_om_block<D, BF16>(wv, os, lds + P::W2, nb, wl);
         const f32x4 xj = G[b][0], gj = G[b][1], xi = G[b][2], gi = G[b][3];
         const f32x4 c2 = bias4<P>(p, lds, g4, D + 16 * nb);
         f32x4 qv;
@@ -551,7 +570,7 @@ __global__ __launch_bounds__((64 * cf_nw<D, BF16, true>()), 1) void k_cf_bwd(CfP
           qv[r] = gj[r] * (g.in * (wv[r] + c2[r]));
           gdd = fmaf(gi[r] * xj[r] + gj[r] * xi[r], wt[nb][r], gdd);
         }
-        if (want_q) tile_put(Tb, b, qv, lane);
+        if (want_q) tile_put(Tb, b, qv, tl);
         if (pss + 1 < NB / 4) {
           gather(nb + 4, G[b]);
           __builtin_amdgcn_sched_barrier(0);

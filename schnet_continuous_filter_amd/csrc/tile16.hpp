@@ -111,24 +111,45 @@ struct Operand<K, true> {
   }
 };
 
+// Per-lane element offsets of the A-operand reads of an output-major image
+// with K elements per row. The swizzle XORs the 16-byte chunk index with the
+// row's low 4 bits, so only the low 4 bits of the chunk vary per lane: four
+// offsets (chunk group q) plus compile-time constants address every read.
+// Build once per tile from the lane index.
+template <int K, bool BF16>
+struct ImgLanes {
+  int off[4];
+  __device__ __forceinline__ explicit ImgLanes(int lane) {
+    const int grp = lane >> 4, e = lane & 15;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (BF16) off[q] = sw8<K>(e, 32 * q + 8 * grp);
+      else off[q] = sw4<K>(e, 16 * q + 4 * grp);
+    }
+  }
+};
+
 // acc += sum_k M[16 nb + e][k] S[k] for one output block nb; M is an
 // output-major image with K elements per row (fp32: sw4 rows; bf16: sw8 rows
 // with perm32 positions).
 template <int K, bool BF16>
 __device__ __forceinline__ void gemm_om_block(f32x4& acc, const Operand<K, BF16>& op,
-                                              const void* img, int nb, int grp, int e) {
+                                              const void* img, int nb,
+                                              const ImgLanes<K, BF16>& ln) {
   if constexpr (BF16) {
-    const __bf16* M = reinterpret_cast<const __bf16*>(img);
+    static_assert(K / 32 <= 4, "chunk groups");
+    const __bf16* M = reinterpret_cast<const __bf16*>(img) + 16 * nb * K;
 #pragma unroll
     for (int kk = 0; kk < K / 32; ++kk) {
-      const bf16x8 w = *reinterpret_cast<const bf16x8*>(M + sw8<K>(16 * nb + e, 32 * kk + 8 * grp));
+      const bf16x8 w = *reinterpret_cast<const bf16x8*>(M + ln.off[kk]);
       acc = mfma16(w, op.S[kk], acc);
     }
   } else {
-    const float* M = reinterpret_cast<const float*>(img);
+    const float* M = reinterpret_cast<const float*>(img) + 16 * nb * K;
 #pragma unroll
     for (int kb = 0; kb < K / 16; ++kb) {
-      const f32x4 w = *reinterpret_cast<const f32x4*>(M + sw4<K>(16 * nb + e, 16 * kb + 4 * grp));
+      // chunk 4 kb + g: bit 4 (kb >= 4) is untouched by the swizzle
+      const f32x4 w = *reinterpret_cast<const f32x4*>(M + ln.off[kb & 3] + 64 * (kb >> 2));
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc = mfma16(w[r], op.S[kb][r], acc);
     }
@@ -138,15 +159,21 @@ __device__ __forceinline__ void gemm_om_block(f32x4& acc, const Operand<K, BF16>
 // All NOUT / 16 output blocks: out[nb] = sum_k M[16 nb + e][k] S[k] (k < K).
 template <int K, int NOUT, bool BF16>
 __device__ __forceinline__ void gemm_om(f32x4 (&out)[NOUT / 16], const f32x4 (&S)[K / 16],
-                                        const void* img, int lane_) {
-  const int lane = opaque(lane_), grp = lane >> 4, e = lane & 15;
+                                        const void* img, const ImgLanes<K, BF16>& ln) {
   const Operand<K, BF16> op(S);
 #pragma unroll
   for (int nb = 0; nb < NOUT / 16; ++nb) {
     f32x4 acc = f32x4{};
-    gemm_om_block<K, BF16>(acc, op, img, nb, grp, e);
+    gemm_om_block<K, BF16>(acc, op, img, nb, ln);
     out[nb] = acc;
   }
+}
+// The same, with the lane offsets built from the lane index here.
+template <int K, int NOUT, bool BF16>
+__device__ __forceinline__ void gemm_om(f32x4 (&out)[NOUT / 16], const f32x4 (&S)[K / 16],
+                                        const void* img, int lane_) {
+  const ImgLanes<K, BF16> ln(opaque(lane_));
+  gemm_om<K, NOUT, BF16>(out, S, img, ln);
 }
 
 } // namespace sn
