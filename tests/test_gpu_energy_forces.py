@@ -125,3 +125,77 @@ def test_net_force_and_translation(gpu_lib):
     E, F, _, _ = run_gpu(gpu_lib, m, system, pos, types, w, m.r_cut)
     rms = np.sqrt(np.mean(F ** 2))
     assert np.max(np.abs(F.sum(axis=0))) < 1e-3 * rms * np.sqrt(len(F))
+
+
+def test_md1024_full_sampled_replicas(gpu_lib):
+    """All 1024 replicas of the bf16 MD workload on the GPU; replicas are
+    independent, so sampled ones are checked exactly against the oracle run
+    on that replica alone."""
+    cfg, pos, types, w = make_config("md1024")
+    m = cfg.model
+    system = lib_system(gpu_lib, cfg.system)
+    E, F, _, _ = run_gpu(gpu_lib, m, system, pos, types, w, m.r_cut)
+    n = cfg.system.atoms_per_replica
+    for r in (0, 377, 1023):
+        sl = slice(r * n, (r + 1) * n)
+        rp, col = oracle.neighbor_list(pos[sl], 1, n, False, 0.0, m.r_cut)
+        Eo, Fo = oracle.energy_forces(oracle_desc(m), w, pos[sl], types[sl], rp, col,
+                                      n_replicas=1, periodic=False, box=0.0)
+        re, rf = assert_energy_forces(E[r:r + 1], F[sl], Eo, Fo, bf16=True, what=f"md1024 r{r}")
+        print(f"md1024 replica {r}: E rel {re:.2e}, F max/rms {rf:.2e}")
+
+
+def test_bulk4k_tiled_2x2x2(gpu_lib):
+    """The bulk4k system repeated 2 x 2 x 2 in a box of twice the side (32,768
+    atoms, the large-system cell-list path): with r_c below half the small box
+    every copy sees the same environment, so the energy is 8x and the forces
+    repeat those of the oracle on the small box. Positions sit on a 2^-12 A
+    grid and the side is 40.625 A, so every shifted coordinate is exact in
+    fp32 and all copies have the same geometry."""
+    cfg, pos, types, w = make_config("bulk4k")
+    m = cfg.model
+    L = np.float32(40.625)
+    q = np.float32(2.0 ** -12)
+    pos = (np.floor(pos.astype(np.float64) * (float(L) / cfg.system.box) / float(q)) * float(q))
+    pos = np.mod(pos, float(L)).astype(np.float32)
+    shifts = np.array([(a, b, c) for a in (0, 1) for b in (0, 1) for c in (0, 1)], np.float32) * L
+    big = np.concatenate([pos + s for s in shifts]).astype(np.float32)
+    assert np.array_equal(big[4096:8192] - shifts[1], pos)      # shifts are exact
+    big_types = np.tile(types, 8)
+    from gen.configs import Config, SystemSpec
+    c2 = Config("bulk4k_x8", SystemSpec("bulk", 1, len(big), True, float(2 * L)), m)
+    system = lib_system(gpu_lib, c2.system)
+    E, F, _, col = run_gpu(gpu_lib, m, system, big, big_types, w, m.r_cut)
+    rp, c4 = oracle.neighbor_list(pos, 1, len(pos), True, float(L), m.r_cut)
+    assert len(col) == 8 * len(c4)
+    Eo, Fo = oracle.energy_forces(oracle_desc(m), w, pos, types, rp, c4, n_replicas=1,
+                                  periodic=True, box=float(L))
+    re, rf = assert_energy_forces(E, F, 8 * Eo, np.tile(Fo, (8, 1)), what="bulk4k x8")
+    print(f"bulk4k x8: E rel {re:.2e}, F max/rms {rf:.2e}")
+
+
+def test_bulk64k_full_invariances(gpu_lib):
+    """The 65,536-atom box at full size: a periodic translation leaves energy
+    and forces unchanged and the net force vanishes. Positions sit on a
+    2^-10 A grid, the side (102.25 A) and the shift on a 1/4 A grid, so the
+    translated and wrapped coordinates are exact in fp32 and only the
+    kernels' own rounding (their order of summation over receivers and
+    tiles changes with the atom order in space) separates the two runs."""
+    cfg, pos, types, w = make_config("bulk64k")
+    m = cfg.model
+    L = 102.25
+    q = 2.0 ** -10
+    pos = np.mod(np.floor(pos.astype(np.float64) * (L / cfg.system.box) / q) * q, L)
+    pos = pos.astype(np.float32)
+    from gen.configs import Config, SystemSpec
+    c2 = Config("bulk64k_grid", SystemSpec("bulk", 1, len(pos), True, L), m)
+    system = lib_system(gpu_lib, c2.system)
+    E, F, _, _ = run_gpu(gpu_lib, m, system, pos, types, w, m.r_cut)
+    shift = np.array([16.25, -5.0, 40.75])
+    moved = np.mod(pos.astype(np.float64) + shift, L)
+    assert np.all(moved == moved.astype(np.float32))               # exact in fp32
+    E2, F2, _, _ = run_gpu(gpu_lib, m, system, moved.astype(np.float32), types, w, m.r_cut)
+    rms = np.sqrt(np.mean(F ** 2))
+    assert abs(E2[0] - E[0]) <= 1e-5 * abs(E[0]), (E, E2)
+    assert np.max(np.abs(F2 - F)) <= 1e-4 * rms, np.max(np.abs(F2 - F)) / rms
+    assert np.max(np.abs(F.sum(axis=0))) < 1e-3 * rms * np.sqrt(len(F))
