@@ -102,7 +102,10 @@ __global__ __launch_bounds__(64 * kAtomNW, 1) void k_atom(AtomArgs g) {
   const float* V1 = reinterpret_cast<const float*>(lds + P::V1);
   const float* V2 = reinterpret_cast<const float*>(lds + P::V2);
 
-  for (int t = (int)blockIdx.x * kAtomNW + wave; t < ntiles; t += (int)gridDim.x * kAtomNW) {
+  // tiles interleaved over the work-groups first, so that small systems
+  // spread one tile per SIMD over all CUs before any SIMD gets a second
+  for (int t = (int)blockIdx.x + (int)gridDim.x * wave; t < ntiles;
+       t += (int)gridDim.x * kAtomNW) {
     const int g4 = 4 * (opaque(lane) >> 4);   // this lane's feature offset in a block
     const int atom = t * kAtoms + e;
     const bool ok = atom < g.M;
@@ -196,7 +199,7 @@ struct AtomKernels {
   }
   static hipError_t launch(const AtomArgs& g, int n_cu, hipStream_t s) {
     const int ntiles = (g.M + kAtoms - 1) / kAtoms;
-    int G = (ntiles + kAtomNW - 1) / kAtomNW;
+    int G = ntiles;
     if (G > n_cu) G = n_cu;
     if (G < 1) G = 1;
     const dim3 grid(G), block(64 * kAtomNW);
@@ -248,29 +251,30 @@ hipError_t launch_atom(const AtomArgs& g, int D, int N1, int n_cu, hipStream_t s
                        [&](auto k) { return decltype(k)::launch(g, n_cu, s); });
 }
 
-// x[i][:] = Emb[types[i]][:]
+// x[i][:] = Emb[types[i]][:], four features per thread
 __global__ __launch_bounds__(kThreads) void k_embed(const int32_t* types, const float* emb, int n,
                                                     int log2D, int n_types, float* x,
                                                     DevStatus* st) {
-  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const int D = 1 << log2D;
-  if (idx >= ((int64_t)n << log2D)) return;
-  const int64_t i = idx >> log2D;
-  const int c = (int)(idx & (D - 1));
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;   // float4 index
+  const int log2q = log2D - 2;
+  if (idx >= ((int64_t)n << log2q)) return;
+  const int64_t i = idx >> log2q;
+  const int c4 = (int)(idx & ((1 << log2q) - 1));
   int t = types[i];
   if (t < 0 || t >= n_types) {
-    if (c == 0) dev_fail(st, SN_ERR_INVALID_ARG, i);
+    if (c4 == 0) dev_fail(st, SN_ERR_INVALID_ARG, i);
     t = 0;
   }
-  x[idx] = emb[(int64_t)t * D + c];
+  reinterpret_cast<f32x4*>(x)[idx] =
+      reinterpret_cast<const f32x4*>(emb)[((int64_t)t << log2q) + c4];
 }
 
 hipError_t launch_embed(const int32_t* types, const float* emb, int n_atoms, int D, int n_types,
                         float* x, DevStatus* st, hipStream_t s) {
   const int log2D = D == 128 ? 7 : 6;
-  const int64_t n = (int64_t)n_atoms * D;
-  hipLaunchKernelGGL(k_embed, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
-                     types, emb, n_atoms, log2D, n_types, x, st);
+  const int64_t n4 = (int64_t)n_atoms * D / 4;
+  hipLaunchKernelGGL(k_embed, dim3((unsigned)((n4 + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                     s, types, emb, n_atoms, log2D, n_types, x, st);
   return hipGetLastError();
 }
 

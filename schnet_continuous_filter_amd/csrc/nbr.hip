@@ -11,8 +11,8 @@
 // computes with the same sequence of operations, and symmetric.
 //
 // Two search modes:
-//  * all pairs inside each replica, staged through LDS (chains and small
-//    boxes); the scan over senders is ascending, so rows come out sorted;
+//  * all pairs inside each replica (chains and small boxes), one wave per
+//    receiver with ballot compaction; senders ascend, so rows come out sorted;
 //  * a cell list for one large periodic cube: cells of edge >= r_list,
 //    27-cell search, then a per-row rank sort in LDS.
 #include "common.hpp"
@@ -142,49 +142,44 @@ hipError_t launch_exclusive_scan(int32_t* a, int64_t n, int32_t* blocks_i32, Dev
 }
 
 // ------------------------------------------------------------------ all pairs per replica
-constexpr int kPairThreads = 64;   // one wave per block: many small blocks fill the chip
-
+// One wave per receiver: the lanes test 64 senders of the same replica at a
+// time and a ballot compacts the hits in sender order, so each row is written
+// sorted, with contiguous stores, and small replicas still give one wave per
+// atom of the whole batch.
 template <bool FILL>
-__global__ __launch_bounds__(kPairThreads) void k_nbr_allpairs(const float* __restrict__ pos, int N,
-                                                           int periodic, double L, double half,
-                                                           double r2, int32_t* rowptr,
-                                                           int32_t* col, const DevStatus* st,
+__global__ __launch_bounds__(kThreads) void k_nbr_allpairs(const float* __restrict__ pos, int N,
+                                                           int64_t n_tot, int periodic, double L,
+                                                           double half, double r2,
+                                                           int32_t* rowptr, int32_t* col,
+                                                           const DevStatus* st,
                                                            const int64_t* gate, int64_t gate_val) {
   SN_GATE
   if (FILL && st->overflow) return;
-  __shared__ float sx[kPairThreads], sy[kPairThreads], sz[kPairThreads];
-  const int il = blockIdx.x * kPairThreads + threadIdx.x;
-  const int64_t base = (int64_t)blockIdx.y * N;
-  float xi = 0.f, yi = 0.f, zi = 0.f;
-  if (il < N) {
-    xi = pos[3 * (base + il) + 0];
-    yi = pos[3 * (base + il) + 1];
-    zi = pos[3 * (base + il) + 2];
-  }
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (r >= n_tot) return;
+  const int il = (int)(r % N);
+  const int64_t base = r - il;
+  const float xi = pos[3 * r + 0], yi = pos[3 * r + 1], zi = pos[3 * r + 2];
+  const uint64_t below = (1ull << lane) - 1ull;
+  int64_t out = FILL ? (int64_t)rowptr[r] : 0;
   int cnt = 0;
-  int64_t out = 0;
-  if (FILL && il < N) out = rowptr[base + il];
-  for (int j0 = 0; j0 < N; j0 += kPairThreads) {
-    __syncthreads();
-    const int jl = j0 + threadIdx.x;
-    if (jl < N) {
-      sx[threadIdx.x] = pos[3 * (base + jl) + 0];
-      sy[threadIdx.x] = pos[3 * (base + jl) + 1];
-      sz[threadIdx.x] = pos[3 * (base + jl) + 2];
+  for (int j0 = 0; j0 < N; j0 += 64) {
+    const int j = j0 + lane;
+    bool in = false;
+    if (j < N && j != il) {
+      const float* pj = pos + 3 * (base + j);
+      in = pair_in(xi, yi, zi, pj[0], pj[1], pj[2], periodic, L, half, r2);
     }
-    __syncthreads();
-    const int jn = min(kPairThreads, N - j0);
-    if (il < N) {
-      for (int jj = 0; jj < jn; ++jj) {
-        const int j = j0 + jj;
-        if (j != il && pair_in(xi, yi, zi, sx[jj], sy[jj], sz[jj], periodic, L, half, r2)) {
-          if (FILL) col[out++] = (int32_t)(base + j);
-          else ++cnt;
-        }
-      }
+    const uint64_t m = __ballot(in);
+    if (FILL) {
+      if (in) col[out + __popcll(m & below)] = (int32_t)(base + j);
+      out += __popcll(m);
+    } else {
+      cnt += __popcll(m);
     }
   }
-  if (!FILL && il < N) rowptr[base + il] = cnt;
+  if (!FILL && lane == 0) rowptr[r] = cnt;
 }
 
 // ------------------------------------------------------------------ cell list (one periodic cube)
@@ -331,14 +326,14 @@ hipError_t launch_build_neighbors(const NbrGeom& g, const float* pos, int32_t* r
   const int64_t n_tot = (int64_t)g.n_rep * g.n_per;
   hipError_t e;
   if (g.cells_per_axis == 0) {
-    dim3 grid((unsigned)((g.n_per + kPairThreads - 1) / kPairThreads), (unsigned)g.n_rep);
-    hipLaunchKernelGGL(k_nbr_allpairs<false>, grid, dim3(kPairThreads), 0, s, pos, g.n_per, g.periodic,
-                       g.L, g.half, g.r2, rowptr, col, st, gate, gate_val);
+    const dim3 grid((unsigned)((n_tot + kThreads / 64 - 1) / (kThreads / 64)));
+    hipLaunchKernelGGL(k_nbr_allpairs<false>, grid, dim3(kThreads), 0, s, pos, g.n_per, n_tot,
+                       g.periodic, g.L, g.half, g.r2, rowptr, col, st, gate, gate_val);
     if ((e = launch_exclusive_scan(rowptr, n_tot, scan_blocks, st, edge_capacity, gate, gate_val,
                                    s)) != hipSuccess)
       return e;
-    hipLaunchKernelGGL(k_nbr_allpairs<true>, grid, dim3(kPairThreads), 0, s, pos, g.n_per, g.periodic,
-                       g.L, g.half, g.r2, rowptr, col, st, gate, gate_val);
+    hipLaunchKernelGGL(k_nbr_allpairs<true>, grid, dim3(kThreads), 0, s, pos, g.n_per, n_tot,
+                       g.periodic, g.L, g.half, g.r2, rowptr, col, st, gate, gate_val);
     return hipGetLastError();
   }
   const int nc = g.cells_per_axis;
