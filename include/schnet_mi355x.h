@@ -139,6 +139,37 @@ sn_status sn_energy_forces(const sn_model* model, const sn_system* sys, const fl
                            float* energy, float* forces, void* ws, size_t ws_bytes,
                            hipStream_t stream);
 
+/* The same energies and forces by the unfused pipeline that FlashSchNet
+ * measures its techniques against (§3.3 bottlenecks, Fig. 2(b) lower
+ * pipeline; §4.5 "End-to-end integration" names fusion and segmented
+ * reduction as ablation switches), so that both can be timed on one GPU.
+ * Each step of the edge path is a separate kernel whose output is an edge
+ * tensor in the workspace: distances, Gaussians, envelope, basis B[E][Dr],
+ * filter pre-activation, activation and filter W[E][D], gathered sender rows
+ * X_src[E][D] and messages M[E][D]; the backward applies the chain rule
+ * through the same tensors. Aggregation (messages into receivers, feature
+ * gradients into senders, dE/dr into both ends of each edge) is a segment sum
+ * over the receiver rows, the sender side through the reverse-edge index of
+ * the symmetric list, or with flags = SN_UNFUSED_ATOMIC atomic adds; atomic
+ * results are not bitwise reproducible. The embedding, update and readout
+ * layers are the ones sn_energy_forces runs.
+ * edge_capacity (>= 1) bounds the list's edge count rowptr[R*N]: every edge
+ * tensor has that many rows. A larger list sets the device status to
+ * SN_ERR_CAPACITY and leaves the outputs invalid. Other arguments as for
+ * sn_energy_forces; the list must come from sn_build_neighbors (symmetric,
+ * senders ascending). */
+enum { SN_UNFUSED_ATOMIC = 1 };
+
+/* Workspace bytes for sn_energy_forces_unfused: the sn_workspace_size amount
+ * plus about 4 (3T + 4) D + 8 Dr edge-tensor bytes per edge of capacity. */
+sn_status sn_unfused_workspace_size(const sn_model_desc* desc, const sn_system* sys,
+                                    int64_t edge_capacity, size_t* bytes_host);
+sn_status sn_energy_forces_unfused(const sn_model* model, const sn_system* sys, const float* pos,
+                                   const int32_t* types, const int32_t* rowptr,
+                                   const int32_t* col, int64_t edge_capacity, int32_t flags,
+                                   float* energy, float* forces, void* ws, size_t ws_bytes,
+                                   hipStream_t stream);
+
 /* Langevin dynamics by BAOAB splitting:
  *   v += dt/2 k F/m;  r += dt/2 v;  v = c1 v + c2 xi;  r += dt/2 v;
  *   (rebuild list if due);  F = F(r);  v += dt/2 k F/m

@@ -23,6 +23,7 @@ SN_ERR_HIP = 5
 SN_ERR_WORKSPACE = 6
 SN_FILTER_F32 = 0
 SN_FILTER_BF16 = 1
+SN_UNFUSED_ATOMIC = 1
 
 c_int32, c_int64, c_uint64, c_float, c_double = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,
                                                  ctypes.c_float, ctypes.c_double)
@@ -69,6 +70,11 @@ _SIGNATURES = {
                                      _P(c_int64), c_void_p, c_size_t, c_void_p]),
     "sn_energy_forces": (c_int32, [c_void_p, _P(SnSystem), c_void_p, c_void_p, c_void_p, c_void_p,
                                    c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "sn_unfused_workspace_size": (c_int32, [_P(SnModelDesc), _P(SnSystem), c_int64,
+                                            _P(c_size_t)]),
+    "sn_energy_forces_unfused": (c_int32, [c_void_p, _P(SnSystem), c_void_p, c_void_p, c_void_p,
+                                           c_void_p, c_int64, c_int32, c_void_p, c_void_p,
+                                           c_void_p, c_size_t, c_void_p]),
     "sn_md_init": (c_int32, [c_void_p, _P(SnSystem), c_void_p, _P(SnMdParams), _P(SnMdState),
                              c_void_p, c_void_p, c_size_t, c_void_p]),
     "sn_md_step": (c_int32, [c_void_p, _P(SnSystem), c_void_p, _P(SnMdParams), _P(SnMdState),
@@ -211,6 +217,30 @@ def sn_energy_forces(model, system: SnSystem, pos, types, rowptr, col, energy, f
     _check(LIB.sn_energy_forces(model, ctypes.byref(system), _ptr(pos), _ptr(types), _ptr(rowptr),
                                 _ptr(col), _ptr(energy), _ptr(forces), ws.ptr, ws.nbytes,
                                 _stream()), "sn_energy_forces")
+
+
+def sn_unfused_workspace_size(desc: SnModelDesc, system: SnSystem, edge_capacity: int) -> int:
+    n = c_size_t()
+    _check(LIB.sn_unfused_workspace_size(ctypes.byref(desc), ctypes.byref(system),
+                                         int(edge_capacity), ctypes.byref(n)),
+           "sn_unfused_workspace_size")
+    return n.value
+
+
+def sn_energy_forces_unfused(model, system: SnSystem, pos, types, rowptr, col, edge_capacity: int,
+                             flags: int, energy, forces, ws: Workspace) -> None:
+    import torch
+    n = system.n_replicas * system.atoms_per_replica
+    _check_tensor(pos, torch.float32, 3 * n, "pos")
+    _check_tensor(types, torch.int32, n, "types")
+    _check_tensor(rowptr, torch.int32, n + 1, "rowptr")
+    _check_tensor(col, torch.int32, edge_capacity, "col")
+    _check_tensor(energy, torch.float32, system.n_replicas, "energy")
+    _check_tensor(forces, torch.float32, 3 * n, "forces")
+    _check(LIB.sn_energy_forces_unfused(model, ctypes.byref(system), _ptr(pos), _ptr(types),
+                                        _ptr(rowptr), _ptr(col), int(edge_capacity), int(flags),
+                                        _ptr(energy), _ptr(forces), ws.ptr, ws.nbytes, _stream()),
+           "sn_energy_forces_unfused")
 
 
 def make_md_params(dt_fs=2.0, temperature_K=300.0, gamma_per_ps=1.0, mass_amu=100.0, skin=1.0,

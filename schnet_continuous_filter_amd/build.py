@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libschnet_mi355x.so")
-SOURCES = ["capi.hip", "nbr.hip", "cfconv.hip", "atomwise.hip", "md.hip"]
+SOURCES = ["capi.hip", "nbr.hip", "cfconv.hip", "atomwise.hip", "md.hip", "unfused.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",

@@ -20,6 +20,8 @@ struct sn_model {
   size_t img_bytes = 0;
   unsigned char* atimg = nullptr;  // per block: update-forward then update-backward image; readout
   size_t at_upd = 0, at_ro = 0;     // image sizes (bytes)
+  unsigned char* ufimg = nullptr;  // per block: the unfused pipeline's product images
+  size_t uf_bytes = 0;
   float co2 = 0.f;             // readout output bias (host copy)
   size_t off_emb = 0, off_o1 = 0, off_co1 = 0, off_o2 = 0;
   std::vector<size_t> off_blk; // start of each interaction block
@@ -105,9 +107,38 @@ int cf_grid(const sn_model* m, int64_t n, int workers) {
   return (int)(g < 1 ? 1 : g);
 }
 
+// Edge tensors of the unfused pipeline, carved after the common workspace.
+struct UfLayout {
+  size_t dst, rev, geo, C, mask, gd, B, gB, keep, buf, total;
+};
+UfLayout uf_layout(size_t base, int64_t cap, int D, int KP, int T) {
+  UfLayout U{};
+  size_t off = base;
+  auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
+  const size_t c = (size_t)cap;
+  U.dst = take(c * 4);
+  U.rev = take(c * 4);
+  U.geo = take(c * 16);
+  U.C = take(c * 4);
+  U.mask = take(c * 4);
+  U.gd = take(c * 4);
+  U.B = take(c * KP * 4);
+  U.gB = take(c * KP * 4);
+  U.keep = take((size_t)3 * T * c * D * 4);   // per block: A, W, X_src
+  U.buf = take((size_t)3 * c * D * 4);
+  U.total = off;
+  return U;
+}
+
+struct UfMode {
+  int64_t cap;
+  int atomic;
+};
+
 sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const float* pos,
                              const int32_t* types, const int32_t* rowptr, const int32_t* col,
-                             float* energy, float* forces, char* ws, hipStream_t s) {
+                             float* energy, float* forces, char* ws, hipStream_t s,
+                             const UfMode* uf = nullptr) {
   const sn_model_desc& d = m->desc;
   const int64_t n = n_atoms(sys);
   const int D = d.D, T = d.T, H = d.H;
@@ -128,10 +159,12 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
   const int Gf = cf_grid(m, n, wf), Gb = cf_grid(m, n, wb);
   hipError_t e;
 
-  if ((e = launch_partition(rowptr, (int)n, Gf * wf, wg_start, s)) != hipSuccess)
-    return hip_fail(e);
-  if ((e = launch_partition(rowptr, (int)n, Gb * wb, wg_start_b, s)) != hipSuccess)
-    return hip_fail(e);
+  if (!uf) {
+    if ((e = launch_partition(rowptr, (int)n, Gf * wf, wg_start, s)) != hipSuccess)
+      return hip_fail(e);
+    if ((e = launch_partition(rowptr, (int)n, Gb * wb, wg_start_b, s)) != hipSuccess)
+      return hip_fail(e);
+  }
   if ((e = launch_embed(types, m->w + m->off_emb, (int)n, D, d.n_types, x, st, s)) != hipSuccess)
     return hip_fail(e);
 
@@ -171,13 +204,68 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
   };
   const void* ro_img = m->atimg + (size_t)T * 2 * m->at_upd;
 
+  UfArgs ua{};
+  float* uf_keep = nullptr;
+  if (uf) {
+    const UfLayout U = uf_layout(L.total, uf->cap, D, m->KP, T);
+    uf_keep = reinterpret_cast<float*>(ws + U.keep);
+    ua.atomic = uf->atomic;
+    ua.D = D;
+    ua.KP = m->KP;
+    ua.Dr = d.Dr;
+    ua.bf16 = bf16;
+    ua.n_cu = m->n_cu;
+    ua.n_atoms = (int)n;
+    ua.periodic = sys->periodic;
+    ua.cap = uf->cap;
+    ua.box = sys->box;
+    ua.rbf_min = d.rbf_min;
+    ua.rbf_step = step;
+    ua.r_cut = d.r_cut;
+    ua.rowptr = rowptr;
+    ua.col = col;
+    ua.pos = pos;
+    ua.st = st;
+    ua.dst = reinterpret_cast<int32_t*>(ws + U.dst);
+    ua.rev = reinterpret_cast<int32_t*>(ws + U.rev);
+    ua.geo = reinterpret_cast<f32x4*>(ws + U.geo);
+    ua.B = reinterpret_cast<float*>(ws + U.B);
+    ua.C = reinterpret_cast<float*>(ws + U.C);
+    ua.mask = reinterpret_cast<float*>(ws + U.mask);
+    ua.gd = reinterpret_cast<float*>(ws + U.gd);
+    ua.gB = reinterpret_cast<float*>(ws + U.gB);
+    ua.dEdr = fblk;
+    const size_t ED = (size_t)uf->cap * D;
+    ua.buf0 = reinterpret_cast<float*>(ws + U.buf);
+    ua.buf1 = ua.buf0 + ED;
+    ua.buf2 = ua.buf1 + ED;
+    ua.phase = UF_EDGES;
+    if ((e = launch_unfused(ua, s)) != hipSuccess) return hip_fail(e);
+  }
+  auto uf_block = [&](int t, int phase) {
+    const size_t ED = (size_t)uf->cap * D;
+    ua.phase = phase;
+    ua.img = m->ufimg + (size_t)t * m->uf_bytes;
+    const float* Wf1 = m->w + m->off_blk[t];
+    ua.cf1 = Wf1 + (size_t)d.Dr * D;
+    ua.cf2 = ua.cf1 + D + (size_t)D * D;
+    ua.A = uf_keep + (size_t)3 * t * ED;
+    ua.W = ua.A + ED;
+    ua.Xs = ua.W + ED;
+    ua.x = x + t * ND;
+    return launch_unfused(ua, s);
+  };
+
   // forward
   for (int t = 0; t < T; ++t) {
     p.img = block_img(t);
     p.wg_start = wg_start;
     p.x = x + t * ND;
     p.h = gbuf;
-    {
+    if (uf) {
+      ua.h = gbuf;
+      if ((e = uf_block(t, UF_FORWARD)) != hipSuccess) return hip_fail(e);
+    } else {
       ProfScope ps(0, s);
       if ((e = launch_cf_forward(D, m->KP, bf16, p, Gf, s)) != hipSuccess) return hip_fail(e);
     }
@@ -205,12 +293,17 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
     p.gh = gbuf;
     p.q_out = t > 0 ? tmp : nullptr;
     p.forces = fblk + (size_t)t * n * 3;
-    {
+    if (uf) {
+      ua.gh = gbuf;
+      ua.q = t > 0 ? tmp : nullptr;
+      if ((e = uf_block(t, UF_BACKWARD)) != hipSuccess) return hip_fail(e);
+    } else {
       ProfScope ps(1, s);
       if ((e = launch_cf_backward(D, m->KP, bf16, p, Gb, s)) != hipSuccess) return hip_fail(e);
     }
   }
-  if ((e = launch_force_sum(fblk, T, n, forces, s)) != hipSuccess) return hip_fail(e);
+  // the unfused pipeline accumulates dE/dr of every block into one array
+  if ((e = launch_force_sum(fblk, uf ? 1 : T, n, forces, s)) != hipSuccess) return hip_fail(e);
   return SN_OK;
 }
 
@@ -382,6 +475,20 @@ sn_status sn_model_create(const sn_model_desc* d, const float* weights_host, siz
     e = (per == 0) ? hipErrorInvalidValue : hipMalloc(&m->cfimg, hi.size());
     if (e == hipSuccess) e = hipMemcpy(m->cfimg, hi.data(), hi.size(), hipMemcpyHostToDevice);
   }
+  if (e == hipSuccess) e = uf_prepare(d->D, m->KP, d->filter_dtype == SN_FILTER_BF16);
+  if (e == hipSuccess) {
+    // product images of the unfused pipeline
+    const int bf16 = d->filter_dtype == SN_FILTER_BF16;
+    m->uf_bytes = uf_images(d->D, m->KP, bf16).total;
+    std::vector<unsigned char> hu(m->uf_bytes * d->T);
+    for (int t = 0; t < d->T; ++t) {
+      const float* Wf1 = weights_host + m->off_blk[t];
+      const float* Wf2 = Wf1 + (size_t)d->Dr * D + D;
+      uf_fill_images(d->D, m->KP, bf16, d->Dr, Wf1, Wf2, hu.data() + t * m->uf_bytes);
+    }
+    e = hipMalloc(&m->ufimg, hu.size());
+    if (e == hipSuccess) e = hipMemcpy(m->ufimg, hu.data(), hu.size(), hipMemcpyHostToDevice);
+  }
   if (e == hipSuccess) e = atom_prepare(d->D, d->H);
   if (e == hipSuccess) {
     // atom-wise weight images, laid out as the kernels hold them in LDS
@@ -416,6 +523,7 @@ void sn_model_destroy(sn_model* m) {
   if (m->w) (void)hipFree(m->w);
   if (m->cfimg) (void)hipFree(m->cfimg);
   if (m->atimg) (void)hipFree(m->atimg);
+  if (m->ufimg) (void)hipFree(m->ufimg);
   delete m;
 }
 
@@ -461,6 +569,35 @@ sn_status sn_energy_forces(const sn_model* m, const sn_system* sys, const float*
   if (rc != SN_OK) return rc;
   return energy_forces_impl(m, sys, pos, types, rowptr, col, energy, forces, static_cast<char*>(ws),
                             s);
+}
+
+sn_status sn_unfused_workspace_size(const sn_model_desc* d, const sn_system* sys,
+                                    int64_t edge_capacity, size_t* bytes) {
+  if (!d || !sys || !bytes || !desc_ok(d) || !sys_ok(sys)) return SN_ERR_INVALID_ARG;
+  if (edge_capacity < 0 || edge_capacity > INT32_MAX) return SN_ERR_INVALID_ARG;
+  const size_t base = ws_layout(n_atoms(sys), d->D, d->T, d->H).total;
+  *bytes = uf_layout(base, edge_capacity, d->D, cf_kp(d->Dr, d->filter_dtype == SN_FILTER_BF16),
+                     d->T).total;
+  return SN_OK;
+}
+
+sn_status sn_energy_forces_unfused(const sn_model* m, const sn_system* sys, const float* pos,
+                                   const int32_t* types, const int32_t* rowptr,
+                                   const int32_t* col, int64_t edge_capacity, int32_t flags,
+                                   float* energy, float* forces, void* ws, size_t ws_bytes,
+                                   hipStream_t s) {
+  if (!m || !sys_ok(sys) || !pos || !types || !rowptr || !col || !energy || !forces)
+    return SN_ERR_INVALID_ARG;
+  if (edge_capacity < 1 || edge_capacity > INT32_MAX) return SN_ERR_INVALID_ARG;
+  if ((flags & ~SN_UNFUSED_ATOMIC) != 0) return SN_ERR_INVALID_ARG;
+  size_t need = 0;
+  sn_status rc = sn_unfused_workspace_size(&m->desc, sys, edge_capacity, &need);
+  if (rc != SN_OK) return rc;
+  rc = check_ws(ws, ws_bytes, need);
+  if (rc != SN_OK) return rc;
+  const UfMode mode{edge_capacity, (flags & SN_UNFUSED_ATOMIC) ? 1 : 0};
+  return energy_forces_impl(m, sys, pos, types, rowptr, col, energy, forces, static_cast<char*>(ws),
+                            s, &mode);
 }
 
 sn_status sn_md_init(const sn_model* m, const sn_system* sys, const int32_t* types,

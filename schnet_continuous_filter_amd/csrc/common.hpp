@@ -131,6 +131,50 @@ hipError_t launch_embed(const int32_t* types, const float* emb, int n_atoms, int
 hipError_t launch_energy(const float* eps, int n_rep, int n_per, float* energy, DevStatus* st,
                          hipStream_t s);
 
+// Unfused edge pipeline (unfused.hip): one kernel per step, edge tensors in
+// the workspace, atomic or segmented aggregation.
+enum UfPhase { UF_EDGES = 0, UF_FORWARD = 1, UF_BACKWARD = 2 };
+struct UfImages { size_t g1, g2, g3, g4, total; };  // byte offsets of the four product images
+struct UfArgs {
+  int phase, atomic;
+  int D, KP, Dr, bf16, n_cu, n_atoms, periodic;
+  int64_t cap;                 // edge capacity (rows of every edge tensor)
+  float box, rbf_min, rbf_step, r_cut;
+  const int32_t* rowptr;
+  const int32_t* col;
+  const float* pos;
+  DevStatus* st;
+  // per call: indices, geometry, basis, dE/dr
+  int32_t* dst;                // [cap] receiver of each edge
+  int32_t* rev;                // [cap] reverse edge (segmented mode)
+  f32x4* geo;                  // [cap] (u, d)
+  float* B;                    // [cap][KP] basis
+  float* C;                    // [cap] envelope
+  float* mask;                 // [cap] 1 inside the cutoff
+  float* gd;                   // [cap] dE/dd
+  float* gB;                   // [cap][KP] dE/dB
+  float* dEdr;                 // [N][3] accumulated over blocks
+  // per block
+  const void* img;             // uf_fill_images of this block
+  const float* cf1;
+  const float* cf2;
+  const float* x;              // x^(t) [N][D]
+  float* h;                    // forward output [N][D]
+  const float* gh;             // backward input dE/dh [N][D]
+  float* q;                    // backward sender sums [N][D], or null
+  float* A;                    // [cap][D] filter pre-activation (kept for the backward)
+  float* W;                    // [cap][D] masked filter (kept)
+  float* Xs;                   // [cap][D] gathered sender rows (kept)
+  float* buf0;                 // [cap][D] scratch
+  float* buf1;
+  float* buf2;
+};
+UfImages uf_images(int D, int KP, int bf16);
+void uf_fill_images(int D, int KP, int bf16, int Dr, const float* Wf1, const float* Wf2,
+                    unsigned char* out);
+hipError_t uf_prepare(int D, int KP, int bf16);
+hipError_t launch_unfused(const UfArgs& a, hipStream_t s);
+
 // MD (md.hip).
 struct MdCoef {
   float half_kick;   // dt/2 * kappa / m
