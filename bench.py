@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a device copy of known size (for counter scaling)")
+    ap.add_argument("--ablation", action="store_true",
+                    help="time one energy+force evaluation on a prebuilt list: fused vs the "
+                         "unfused pipeline (segment sums, atomic scatter), fp32 vs bf16 filters")
     return ap.parse_args()
 
 
@@ -107,6 +110,100 @@ def cpu_baseline(cfg, seconds: float):
             "replica_steps_per_s": R * steps / dt}
 
 
+def ablation(args):
+    """The switches FlashSchNet ablates (fusion, segmented reduction, 16-bit
+    filters; §4.5 "End-to-end integration") on one MI355X: one energy+force
+    evaluation on a prebuilt list, per variant, with the workspace it needs."""
+    import numpy as np
+    import torch
+    from gen.configs import CONFIGS, make_config
+    from schnet_continuous_filter_amd import _lib as L
+
+    cfg = CONFIGS[args.workload]
+    c, pos, types, w = make_config(cfg.name)
+    m, s = c.model, c.system
+    R, N = s.n_replicas, s.atoms_per_replica
+    system = L.make_system(R, N, s.periodic, s.box)
+    dev = torch.device("cuda")
+    p = torch.from_numpy(pos).to(dev).reshape(-1)
+    t = torch.from_numpy(types).to(dev)
+    n = R * N
+    ws_nbr = L.Workspace(L.sn_workspace_size(None, system))
+    rowptr = torch.zeros(n + 1, dtype=torch.int32, device=dev)
+    ne = L.sn_build_neighbors(system, p, m.r_cut, rowptr, None, 0, ws_nbr)
+    col = torch.empty(max(ne, 1), dtype=torch.int32, device=dev)
+    L.sn_reset_device_status(ws_nbr)
+    L.sn_build_neighbors(system, p, m.r_cut, rowptr, col, ne, ws_nbr)
+    energy = torch.empty(R, dtype=torch.float32, device=dev)
+    forces = torch.empty(3 * n, dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    variants = {}
+    energies = {}
+    dtypes = [m.filter_dtype, 1 - m.filter_dtype]
+    for fd in dtypes:
+        tag = "bf16" if fd == 1 else "f32"
+        desc = L.make_desc(m.n_types, m.D, m.Dr, m.T, m.H, m.rbf_min, m.rbf_max, m.r_cut, fd)
+        model = L.sn_model_create(desc, w)
+        runs = [("fused", L.sn_workspace_size(desc, system), None)]
+        if fd == m.filter_dtype:
+            ub = L.sn_unfused_workspace_size(desc, system, ne)
+            runs += [("unfused_segmented", ub, 0), ("unfused_atomic", ub, L.SN_UNFUSED_ATOMIC)]
+        for name, nbytes, flags in runs:
+            ws = L.Workspace(nbytes)
+            if flags is None:
+                fn = lambda: L.sn_energy_forces(model, system, p, t, rowptr, col, energy, forces,
+                                                ws)
+            else:
+                fn = lambda: L.sn_energy_forces_unfused(model, system, p, t, rowptr, col, ne,
+                                                        flags, energy, forces, ws)
+            ms = timed(fn)
+            st = L.sn_get_device_status(ws)
+            if st[0] != 0:
+                print(f"{name} {tag}: device status {st}", file=sys.stderr)
+                sys.exit(1)
+            key = f"{name}_{tag}"
+            variants[key] = {"ms": ms, "edges_per_s": ne / (ms * 1e-3),
+                             "workspace_bytes": nbytes}
+            energies[key] = energy.double().cpu().numpy().copy()
+            del ws
+            torch.cuda.empty_cache()
+        L.sn_model_destroy(model)
+    base = f"_{'bf16' if m.filter_dtype == 1 else 'f32'}"
+    ref = energies["fused" + base]
+    for k, e in energies.items():
+        variants[k]["energy_rel_diff_vs_fused"] = float(np.max(np.abs(e - ref) / np.abs(ref)))
+    ms = {k: v["ms"] for k, v in variants.items()}
+    line = {
+        "metric": "energy+force evaluation time per variant (same GPU, prebuilt list)",
+        "unit": "ms",
+        "higher_is_better": False,
+        "config": {"workload": cfg.name, "replicas": R, "atoms_per_replica": N,
+                   "directed_edges": ne, "D": m.D, "Dr": m.Dr, "T": m.T,
+                   "filter": "bf16" if m.filter_dtype == 1 else "f32"},
+        "steps": args.steps, "warmup": args.warmup,
+        "variants": variants,
+        "speedup": {
+            "segmented_vs_atomic (unfused)": ms["unfused_atomic" + base] / ms["unfused_segmented" + base],
+            "fusion (fused vs unfused, segmented)": ms["unfused_segmented" + base] / ms["fused" + base],
+            "fused vs unfused_atomic": ms["unfused_atomic" + base] / ms["fused" + base],
+            "bf16 vs f32 filter (fused)": ms["fused_f32"] / ms["fused_bf16"],
+        },
+    }
+    print(json.dumps(line))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -115,6 +212,9 @@ def main():
         sys.exit(2)
     import numpy as np
     import torch
+    if args.ablation:
+        ablation(args)
+        return
     if args.copy_calibration:
         copy_calibration()
         return
