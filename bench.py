@@ -43,6 +43,12 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a device copy of known size (for counter scaling)")
+    ap.add_argument("--sweep-replicas", default="",
+                    help="comma-separated replica counts: MD throughput and memory of the "
+                         "269-bead chain model (bf16 filter, 1 A skin, rebuild every 10) per count")
+    ap.add_argument("--topology", default="",
+                    help="comma-separated compaction factors: energy+force time of the fused and "
+                         "unfused pipelines on 64 chains rescaled about their centroids")
     ap.add_argument("--ablation", action="store_true",
                     help="time one energy+force evaluation on a prebuilt list: fused vs the "
                          "unfused pipeline (segment sums, atomic scatter), fp32 vs bf16 filters")
@@ -204,6 +210,132 @@ def ablation(args):
     print(json.dumps(line))
 
 
+def sweep_replicas(args):
+    """Replica-count scaling (§5.2 "Memory reduction enables better
+    scalability", Figure 7): MD replica-steps/s and device memory per count,
+    with the workspace the unfused pipeline would need for the same list."""
+    import torch
+    from gen.configs import make_config
+    from schnet_continuous_filter_amd import _lib as L
+
+    rows = []
+    for R in [int(v) for v in args.sweep_replicas.split(",")]:
+        c, pos, types, w = make_config("md1024", n_replicas=R)
+        m, s, md = c.model, c.system, c.md
+        N = s.atoms_per_replica
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        desc = L.make_desc(m.n_types, m.D, m.Dr, m.T, m.H, m.rbf_min, m.rbf_max, m.r_cut,
+                           m.filter_dtype)
+        system = L.make_system(R, N, s.periodic, s.box)
+        model = L.sn_model_create(desc, w)
+        wsb = L.sn_workspace_size(desc, system)
+        ws = L.Workspace(wsb)
+        p = torch.from_numpy(pos).cuda().reshape(-1)
+        t = torch.from_numpy(types).cuda()
+        prm = L.make_md_params(md.dt_fs, md.temperature_K, md.gamma_per_ps, md.mass_amu, md.skin,
+                               md.rebuild_every, 0)
+        rowptr0 = torch.zeros(R * N + 1, dtype=torch.int32, device="cuda")
+        ne0 = L.sn_build_neighbors(system, p, m.r_cut + md.skin, rowptr0, None, 0, ws)
+        L.sn_reset_device_status(ws)
+        cap = int(ne0 * 1.5) + 1024
+        state = L.MdState(p, cap)
+        energy = torch.empty(R, dtype=torch.float32, device="cuda")
+        L.sn_md_init(model, system, t, prm, state, energy, ws)
+        L.sn_md_step(model, system, t, prm, state, args.warmup, energy, ws)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        L.sn_md_step(model, system, t, prm, state, args.steps, energy, ws)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        st = L.sn_get_device_status(ws)
+        if st[0] != 0:
+            print(f"R={R}: device status {st}", file=sys.stderr)
+            sys.exit(1)
+        rows.append({"replicas": R, "edges_at_start": ne0, "ms_per_step": 1000 * dt / args.steps,
+                     "replica_steps_per_s": R * args.steps / dt,
+                     "peak_device_bytes": torch.cuda.max_memory_allocated(),
+                     "workspace_bytes": wsb,
+                     "unfused_workspace_bytes": L.sn_unfused_workspace_size(desc, system, cap)})
+        del state, ws
+        L.sn_model_destroy(model)
+    print(json.dumps({"metric": "replica-steps/s vs replica count (269-bead chain, bf16 filter)",
+                      "unit": "replica-steps/s", "higher_is_better": True, "steps": args.steps,
+                      "warmup": args.warmup, "rows": rows}))
+
+
+def topology(args):
+    """Dynamic-topology robustness (§5.2 "Robustness to dynamic graph
+    topology", Figures 5 and 6): the same 64 chains rescaled about their
+    centroids, so that the edge count and the share of long-range
+    (sequence-distant) contacts change; one energy+force evaluation per
+    pipeline on each list."""
+    import numpy as np
+    import torch
+    from gen.configs import make_config
+    from gen.systems import rescale_replicas
+    from schnet_continuous_filter_amd import _lib as L
+
+    c, pos0, types, w = make_config("cg269x64")
+    m, s = c.model, c.system
+    R, N = s.n_replicas, s.atoms_per_replica
+    n = R * N
+    system = L.make_system(R, N, s.periodic, s.box)
+    desc = L.make_desc(m.n_types, m.D, m.Dr, m.T, m.H, m.rbf_min, m.rbf_max, m.r_cut,
+                       m.filter_dtype)
+    model = L.sn_model_create(desc, w)
+    t = torch.from_numpy(types).cuda()
+    energy = torch.empty(R, dtype=torch.float32, device="cuda")
+    forces = torch.empty(3 * n, dtype=torch.float32, device="cuda")
+    rows = []
+    for f in [float(v) for v in args.topology.split(",")]:
+        p = torch.from_numpy(rescale_replicas(pos0, N, f)).cuda().reshape(-1)
+        ws_nbr = L.Workspace(L.sn_workspace_size(desc, system))
+        rowptr = torch.zeros(n + 1, dtype=torch.int32, device="cuda")
+        ne = L.sn_build_neighbors(system, p, m.r_cut, rowptr, None, 0, ws_nbr)
+        col = torch.empty(max(ne, 1), dtype=torch.int32, device="cuda")
+        L.sn_reset_device_status(ws_nbr)
+        L.sn_build_neighbors(system, p, m.r_cut, rowptr, col, ne, ws_nbr)
+        rp = rowptr.cpu().numpy()
+        cl = col[:ne].cpu().numpy()
+        recv = np.repeat(np.arange(n), np.diff(rp))
+        long_range = float(np.mean(np.abs(recv - cl) > 16)) if ne else 0.0
+        row = {"factor": f, "edges": ne, "edges_per_bead": ne / n,
+               "max_row": int(np.diff(rp).max()), "share_seq_sep_gt16": long_range}
+        uws = L.Workspace(L.sn_unfused_workspace_size(desc, system, ne))
+        for name, fn in (
+                ("fused", lambda: L.sn_energy_forces(model, system, p, t, rowptr, col, energy,
+                                                     forces, ws_nbr)),
+                ("unfused_segmented", lambda: L.sn_energy_forces_unfused(
+                    model, system, p, t, rowptr, col, ne, 0, energy, forces, uws)),
+                ("unfused_atomic", lambda: L.sn_energy_forces_unfused(
+                    model, system, p, t, rowptr, col, ne, L.SN_UNFUSED_ATOMIC, energy, forces,
+                    uws))):
+            for _ in range(args.warmup):
+                fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(args.steps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / args.steps
+            row[name] = {"ms": ms, "edges_per_s": ne / (ms * 1e-3)}
+        for wsx in (ws_nbr, uws):
+            st = L.sn_get_device_status(wsx)
+            if st[0] != 0:
+                print(f"factor {f}: device status {st}", file=sys.stderr)
+                sys.exit(1)
+        rows.append(row)
+        del uws
+        torch.cuda.empty_cache()
+    L.sn_model_destroy(model)
+    print(json.dumps({"metric": "energy+force edges/s vs conformation (64 x 269-bead chains)",
+                      "unit": "edges/s", "higher_is_better": True, "steps": args.steps,
+                      "warmup": args.warmup, "rows": rows}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -214,6 +346,12 @@ def main():
     import torch
     if args.ablation:
         ablation(args)
+        return
+    if args.sweep_replicas:
+        sweep_replicas(args)
+        return
+    if args.topology:
+        topology(args)
         return
     if args.copy_calibration:
         copy_calibration()

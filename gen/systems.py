@@ -56,6 +56,15 @@ def self_avoiding_chain(rng: np.random.Generator, n_beads: int, step: float = 3.
             return pos.astype(np.float32)
 
 
+def rescale_replicas(pos: np.ndarray, n_per: int, factor: float) -> np.ndarray:
+    """Each replica's positions scaled by ``factor`` about its own centroid
+    (below 1 a more compact conformation with more, and longer-range,
+    contacts; above 1 a more extended one). Returns float32 [R*N, 3]."""
+    p = np.asarray(pos, dtype=np.float64).reshape(-1, n_per, 3)
+    c = p.mean(axis=1, keepdims=True)
+    return np.ascontiguousarray((c + factor * (p - c)).reshape(-1, 3), dtype=np.float32)
+
+
 def bulk_uniform(rng: np.random.Generator, n_atoms: int, box: float) -> np.ndarray:
     """Uniform positions in the periodic cube [0, box)^3, float32. A coordinate
     that rounds up to ``box`` in float32 is set to 0 so that every value lies

@@ -196,14 +196,15 @@ __device__ __forceinline__ void gemm1(f32x4 (&acc)[NA][D / 16], const unsigned c
   constexpr int PL = CH / 4;           // k per lane group per chunk
   float step = p.rbf_step;
   asm volatile("" : "+v"(step));
-  const float dh = g.d0 - (float)(PL * grp) * step;
+  const int k0 = PL * grp;
   const float coef2 = p.rbf_coef2, inv_s2 = p.rbf_inv_s2;
 #pragma unroll 1
   for (int c = 0; c < p.KC; ++c) {
     float b[NA][PL];
 #pragma unroll
     for (int t = 0; t < PL; ++t) {
-      const float z = dh - (float)(CH * c + t) * step;
+      // d - mu_k with one rounding (the product k step is exact inside the fma)
+      const float z = __builtin_fmaf(-(float)(k0 + CH * c + t), step, g.d0);
       const float gs = g.in * __builtin_amdgcn_exp2f(coef2 * z * z);
       b[0][t] = gs * g.C;
       if constexpr (NA == 2) b[1][t] = gs * (g.Cp - z * inv_s2 * g.C);

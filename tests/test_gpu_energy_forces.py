@@ -72,6 +72,16 @@ def test_bulk4k_full(gpu_lib):
     check(gpu_lib, cfg, pos, types, w, what="bulk4k")
 
 
+@pytest.mark.parametrize("factor", [0.4, 0.6])
+def test_compact_chains_long_rows(gpu_lib, factor):
+    """Chains compacted about their centroids: receiver rows of up to ~170
+    edges span many tiles, and most contacts are sequence-distant."""
+    from gen.systems import rescale_replicas
+    cfg, pos, types, w = make_config("cg269x64", n_replicas=4, bias_scale=0.05)
+    pos = rescale_replicas(pos, 269, factor)
+    check(gpu_lib, cfg, pos, types, w, n_replicas=4, what=f"cg269x4 compacted x{factor}")
+
+
 def test_small_periodic_box_ragged(gpu_lib):
     """A periodic box whose atom count is not a multiple of any tile size."""
     cfg = CONFIGS["bulk4k"]

@@ -70,6 +70,14 @@ def test_cg269_four_replicas(gpu_lib, mode):
 
 
 @pytest.mark.parametrize("mode", list(MODES))
+def test_compact_chains_long_rows(gpu_lib, mode):
+    from gen.systems import rescale_replicas
+    cfg, pos, types, w = make_config("cg269x64", n_replicas=4, bias_scale=0.05)
+    pos = rescale_replicas(pos, 269, 0.4)
+    check(gpu_lib, cfg, pos, types, w, mode, n_replicas=4, what="cg269x4 compacted x0.4")
+
+
+@pytest.mark.parametrize("mode", list(MODES))
 def test_small_periodic_box_ragged(gpu_lib, mode):
     cfg = CONFIGS["bulk4k"]
     rng = np.random.default_rng(3)
