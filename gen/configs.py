@@ -22,6 +22,7 @@ from .systems import bulk_uniform, chain_walk, model_weights, self_avoiding_chai
 
 FILTER_F32 = 0
 FILTER_BF16 = 1
+W16A16 = 2
 
 
 @dataclass(frozen=True)

@@ -18,6 +18,7 @@ from .neighbors import neighbor_list, neighbor_list_bruteforce, neighbor_list_kd
 from .schnet import (  # noqa: F401
     ModelDesc,
     unpack_weights,
+    f16_channel_quantize,
     rbf,
     rbf_deriv,
     cutoff,

@@ -35,6 +35,7 @@ import scipy.sparse as sp
 LN2 = np.log(2.0)
 FILTER_F32 = 0
 FILTER_BF16 = 1
+W16A16 = 2
 
 
 @dataclass(frozen=True)
@@ -59,13 +60,33 @@ def _bf16_round(a: np.ndarray) -> np.ndarray:
     return u.astype(np.uint32).view(np.float32)
 
 
+def f16_channel_quantize(W: np.ndarray) -> np.ndarray:
+    """Per-output-channel 16-bit weights (§4.4 "Channel-wise quantization"),
+    with power-of-two scales as the reading of the page's per-channel scales.
+
+    Column n of W [fan_in][fan_out] (a vector is one column) gets the scale
+    s_n = 2^e where its largest magnitude is m 2^e with m in [0.5, 1) (s_n = 1
+    for an all-zero column); the column is divided by s_n (exact), rounded to
+    IEEE half precision (nearest, ties to even) and multiplied back. Returns
+    float32 of W's shape."""
+    W = np.asarray(W, dtype=np.float32)
+    col = W.reshape(W.shape[0], -1)
+    amax = np.max(np.abs(col), axis=0)
+    _, e = np.frexp(amax)
+    s = np.where(amax > 0, np.ldexp(np.float32(1.0), e), np.float32(1.0)).astype(np.float32)
+    q = (col / s).astype(np.float16).astype(np.float32) * s
+    return q.reshape(W.shape)
+
+
 def unpack_weights(desc: ModelDesc, flat) -> dict:
     """Split the flat fp32 vector into named fp64 arrays.
 
     Order: Emb[n_types][D]; per block Wf1[Dr][D], cf1[D], Wf2[D][D], cf2[D],
     Wu1[D][D], cu1[D], Wu2[D][D], cu2[D]; then Wo1[D][H], co1[H], Wo2[H],
     co2[1]. With a bf16 filter network the two filter weight matrices of every
-    block are first rounded to bfloat16 (their biases stay fp32)."""
+    block are first rounded to bfloat16 (their biases stay fp32); with
+    W16A16 every MLP weight (Wf1, Wf2, Wu1, Wu2, Wo1, Wo2) goes through
+    f16_channel_quantize (biases and the embedding stay fp32)."""
     flat = np.asarray(flat, dtype=np.float32)
     D, Dr, H = desc.D, desc.Dr, desc.H
     off = 0
@@ -86,11 +107,17 @@ def unpack_weights(desc: ModelDesc, flat) -> dict:
         if desc.filter_dtype == FILTER_BF16:
             for name in ("Wf1", "Wf2"):
                 blk[name] = _bf16_round(blk[name])
+        elif desc.filter_dtype == W16A16:
+            for name in ("Wf1", "Wf2", "Wu1", "Wu2"):
+                blk[name] = f16_channel_quantize(blk[name])
         W["blocks"].append(blk)
     W["Wo1"] = take(D, H)
     W["co1"] = take(H)
     W["Wo2"] = take(H)
     W["co2"] = take(1)
+    if desc.filter_dtype == W16A16:
+        W["Wo1"] = f16_channel_quantize(W["Wo1"])
+        W["Wo2"] = f16_channel_quantize(W["Wo2"])
     if off != flat.size:
         raise ValueError(f"weight vector has {flat.size} values, model needs {off}")
 
