@@ -29,6 +29,7 @@ from schnet_continuous_filter_amd import profiling  # noqa: E402  (no GPU work a
 PEAK_FP32_MFMA_TFLOPS = 157.3     # MI355X dense fp32 matrix peak
 PEAK_BF16_MFMA_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+PREC_TAGS = {0: "f32", 1: "bf16", 2: "w16a16"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cfconv_bwd_cg269x64_counters.txt")
 
 
@@ -40,6 +41,8 @@ def parse():
     ap.add_argument("--workload", default="cg269x64",
                     choices=["cg269x64", "cg32", "bulk4k", "bulk64k", "md1024"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--precision", choices=["f32", "bf16", "w16a16"], default=None,
+                    help="override the workload's network operand precision")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a device copy of known size (for counter scaling)")
@@ -157,9 +160,9 @@ def ablation(args):
 
     variants = {}
     energies = {}
-    dtypes = [m.filter_dtype, 1 - m.filter_dtype]
+    dtypes = [m.filter_dtype] + [fd for fd in (0, 1, 2) if fd != m.filter_dtype]
     for fd in dtypes:
-        tag = "bf16" if fd == 1 else "f32"
+        tag = PREC_TAGS[fd]
         desc = L.make_desc(m.n_types, m.D, m.Dr, m.T, m.H, m.rbf_min, m.rbf_max, m.r_cut, fd)
         model = L.sn_model_create(desc, w)
         runs = [("fused", L.sn_workspace_size(desc, system), None)]
@@ -186,7 +189,7 @@ def ablation(args):
             del ws
             torch.cuda.empty_cache()
         L.sn_model_destroy(model)
-    base = f"_{'bf16' if m.filter_dtype == 1 else 'f32'}"
+    base = f"_{PREC_TAGS[m.filter_dtype]}"
     ref = energies["fused" + base]
     for k, e in energies.items():
         variants[k]["energy_rel_diff_vs_fused"] = float(np.max(np.abs(e - ref) / np.abs(ref)))
@@ -197,7 +200,7 @@ def ablation(args):
         "higher_is_better": False,
         "config": {"workload": cfg.name, "replicas": R, "atoms_per_replica": N,
                    "directed_edges": ne, "D": m.D, "Dr": m.Dr, "T": m.T,
-                   "filter": "bf16" if m.filter_dtype == 1 else "f32"},
+                   "filter": PREC_TAGS[m.filter_dtype]},
         "steps": args.steps, "warmup": args.warmup,
         "variants": variants,
         "speedup": {
@@ -205,6 +208,7 @@ def ablation(args):
             "fusion (fused vs unfused, segmented)": ms["unfused_segmented" + base] / ms["fused" + base],
             "fused vs unfused_atomic": ms["unfused_atomic" + base] / ms["fused" + base],
             "bf16 vs f32 filter (fused)": ms["fused_f32"] / ms["fused_bf16"],
+            "w16a16 vs f32 (fused)": ms["fused_f32"] / ms["fused_w16a16"],
         },
     }
     print(json.dumps(line))
@@ -362,6 +366,9 @@ def main():
     cfg = CONFIGS[args.workload]
     c, pos, types, w = make_config(cfg.name)
     m, s = c.model, c.system
+    if args.precision is not None:
+        import dataclasses
+        m = dataclasses.replace(m, filter_dtype={v: k for k, v in PREC_TAGS.items()}[args.precision])
     R, N = s.n_replicas, s.atoms_per_replica
     desc = L.make_desc(m.n_types, m.D, m.Dr, m.T, m.H, m.rbf_min, m.rbf_max, m.r_cut,
                        m.filter_dtype)
@@ -409,11 +416,11 @@ def main():
 
     ms_per_step = 1000.0 * elapsed / args.steps
     edges_per_s = ne * args.steps / elapsed
-    bf16 = m.filter_dtype == 1
+    half = m.filter_dtype != 0          # bf16 or fp16 operands: the same dense MFMA peak
     flops_bwd = 4.0 * m.D * (m.Dr + m.D) * ne          # recompute (2D(Dr+D)) + dgrad (2D(Dr+D))
     avg_bwd_s = bwd_ms / 1000.0 / max(bwd_n, 1)
     achieved = flops_bwd / avg_bwd_s / 1e12
-    peak = PEAK_BF16_MFMA_TFLOPS if bf16 else PEAK_FP32_MFMA_TFLOPS
+    peak = PEAK_BF16_MFMA_TFLOPS if half else PEAK_FP32_MFMA_TFLOPS
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         rec = json.load(open(TRAFFIC_FILE))
@@ -430,7 +437,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16-filter/f32" if bf16 else "f32",
+        "dtype": {0: "f32", 1: "bf16-filter/f32", 2: "f16-mlps/f32"}[m.filter_dtype],
         "data": "synthetic (seeded chains/boxes, random-init weights)",
         "config": {"workload": cfg.name, "replicas": R, "atoms_per_replica": N,
                    "directed_edges": ne, "list_radius_A": r_list, "D": m.D, "Dr": m.Dr, "T": m.T,

@@ -51,12 +51,24 @@ typedef enum {
   SN_ERR_WORKSPACE = 6     /* the workspace is smaller than sn_workspace_size says */
 } sn_status;
 
-enum { SN_FILTER_F32 = 0, SN_FILTER_BF16 = 1 };
+/* Operand precision of the networks (sn_model_desc.filter_dtype):
+ *  SN_FILTER_F32   every product in fp32;
+ *  SN_FILTER_BF16  the filter network's products take bfloat16 operands
+ *                  (weights rounded to nearest even, activations rounded as
+ *                  they enter a product); the other layers stay fp32;
+ *  SN_W16A16       every MLP (filter, update, readout) takes fp16 operands,
+ *                  with per-output-channel scales (§4.4 "Channel-wise
+ *                  quantization"): each weight column n is stored as
+ *                  fp16(W[:, n] / s_n) with s_n the power of two at or above
+ *                  the column's largest magnitude (1 for a zero column), and
+ *                  the readout's output weights likewise as one column.
+ * Accumulation is fp32 in every case; positions, distances, basis
+ * functions, biases, energies and forces stay fp32. */
+enum { SN_FILTER_F32 = 0, SN_FILTER_BF16 = 1, SN_W16A16 = 2 };
 
 /* Model shape. Supported: D in {64, 128}; 2 <= Dr <= 64; 1 <= T <= 8;
- * H a multiple of 32 with H <= D; n_types >= 1; 0 <= rbf_min < rbf_max;
- * r_cut > 0. filter_dtype selects fp32 or bfloat16 operands (fp32
- * accumulation) for the filter network; all other layers are fp32. */
+ * H in {32, 64} with H <= D; n_types >= 1; 0 <= rbf_min < rbf_max;
+ * r_cut > 0; filter_dtype one of the precisions above. */
 typedef struct {
   int32_t n_types;   /* number of atom/bead types */
   int32_t D;         /* hidden feature width */
@@ -95,7 +107,7 @@ typedef struct sn_model sn_model;
 size_t sn_model_weight_count(const sn_model_desc* desc);
 
 /* Validates desc, copies `n_floats` host floats to the device (converting the
- * filter matrices to bfloat16 when filter_dtype is SN_FILTER_BF16) and returns
+ * network matrices to the 16-bit formats filter_dtype selects) and returns
  * a handle in *out. Synchronises the current device. Errors:
  * SN_ERR_INVALID_ARG (null pointers, n_floats mismatch), SN_ERR_UNSUPPORTED
  * (shape outside the supported set), SN_ERR_HIP. */
@@ -157,7 +169,8 @@ sn_status sn_energy_forces(const sn_model* model, const sn_system* sys, const fl
  * tensor has that many rows. A larger list sets the device status to
  * SN_ERR_CAPACITY and leaves the outputs invalid. Other arguments as for
  * sn_energy_forces; the list must come from sn_build_neighbors (symmetric,
- * senders ascending). */
+ * senders ascending). Models with filter_dtype SN_W16A16 return
+ * SN_ERR_UNSUPPORTED. */
 enum { SN_UNFUSED_ATOMIC = 1 };
 
 /* Workspace bytes for sn_energy_forces_unfused: the sn_workspace_size amount

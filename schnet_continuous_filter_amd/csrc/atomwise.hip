@@ -14,8 +14,14 @@
 // operand (output-major images built on the host), the atom features the B
 // operand, loaded from HBM straight into the accumulator layout (lane group g
 // holds features 4g..4g+3 of every 16-feature block) and stored back from it.
-// The intermediate activation never leaves registers.
+// The intermediate activation never leaves registers. With fp16 operands
+// (§4.4 "W16A16 mixed precision for MLP submodules") every weight column
+// carries a power-of-two scale: outputs of a product are multiplied by their
+// column's scale, and products with a transposed matrix (the gradients)
+// multiply their inputs by it instead.
+#include <cmath>
 #include <cstring>
+#include <vector>
 
 #include "tile16.hpp"
 
@@ -25,17 +31,33 @@ constexpr int kAtomNW = 16;   // waves per work-group (four per SIMD)
 constexpr int kAtoms = 16;    // atoms per wave tile
 
 // LDS image of one network: M1 [N1][D] (first product, output-major), M2
-// [D][N1] (second product), V1 [N1], V2 [D] (vectors of the mode).
-template <int D, int N1>
+// [D][N1] (second product), V1 [N1], V2 [D] (vectors of the mode), and for
+// fp16 operands the column scales S1 [N1] of the first network layer and S2
+// [D] of the second (readout: S1 only).
+template <int D, int N1, int PR>
 struct AtomPlan {
+  static constexpr int ES = PR != PREC_F32 ? 2 : 4;
   static constexpr int M1 = 0;
-  static constexpr int M2 = M1 + N1 * D * 4;
-  static constexpr int V1 = M2 + D * N1 * 4;
+  static constexpr int M2 = M1 + N1 * D * ES;
+  static constexpr int V1 = M2 + D * N1 * ES;
   static constexpr int V2 = V1 + N1 * 4;
-  static constexpr int IMG = V2 + D * 4;
+  static constexpr int S1 = V2 + D * 4;
+  static constexpr int S2 = S1 + N1 * 4;
+  static constexpr int IMG = PR == PREC_F16S ? S2 + D * 4 : S1;
   static_assert(IMG <= 160 * 1024, "atom-wise image exceeds LDS");
   static_assert(IMG % 16 == 0, "image is copied in 16-byte pieces");
 };
+
+// Power-of-two scales of the columns of a row-major [rows][cols] matrix.
+static std::vector<float> column_scales(const float* W, int rows, int cols) {
+  std::vector<float> s(cols);
+  for (int n = 0; n < cols; ++n) {
+    float amax = 0.f;
+    for (int k = 0; k < rows; ++k) amax = std::fmax(amax, std::fabs(W[(size_t)k * cols + n]));
+    s[n] = pow2_scale(amax);
+  }
+  return s;
+}
 
 // Products and vectors of each mode (weights row-major [fan_in][fan_out]):
 //   ATOM_UPDATE_FWD  a = h Wu1 + cu1 (stored);  x' = x + ssp(a) Wu2 + cu2
@@ -45,44 +67,53 @@ struct AtomPlan {
 //   ATOM_READOUT     o = x Wo1 + co1;  eps = ssp(o).wo2 + co2;
 //                    g_x = (sigmoid(o) wo2) Wo1^T
 //                    M1 = Wo1^T, M2 = Wo1, V1 = co1, V2[:N1] = wo2
-template <int D, int N1>
+// Weights are divided by their column scales (all 1 unless fp16) before
+// they are placed; the kernels multiply the scales back in.
+template <int D, int N1, int PR>
 static void fill_atom_image(int mode, const float* W1, const float* b1, const float* W2,
                             const float* b2, unsigned char* out) {
-  using P = AtomPlan<D, N1>;
+  using P = AtomPlan<D, N1, PR>;
+  constexpr bool SC = PR == PREC_F16S;
   std::memset(out, 0, P::IMG);
-  float* m1 = reinterpret_cast<float*>(out + P::M1);
-  float* m2 = reinterpret_cast<float*>(out + P::M2);
   float* v1 = reinterpret_cast<float*>(out + P::V1);
   float* v2 = reinterpret_cast<float*>(out + P::V2);
-  if (mode == ATOM_UPDATE_FWD || mode == ATOM_READOUT) {
-    // W1 [D][N1]: M1[n][k] = W1[k][n]
-    for (int k = 0; k < D; ++k)
-      for (int n = 0; n < N1; ++n) m1[sw4<D>(n, k)] = W1[(size_t)k * N1 + n];
+  // s1: columns of W1 [D][N1]; s2: columns of W2 [N1][D] (update) 
+  std::vector<float> s1(N1, 1.f), s2(D, 1.f);
+  if (SC) {
+    s1 = column_scales(W1, D, N1);
+    if (mode != ATOM_READOUT) s2 = column_scales(W2, N1, D);
+    std::memcpy(out + P::S1, s1.data(), N1 * sizeof(float));
+    if (mode != ATOM_READOUT) std::memcpy(out + P::S2, s2.data(), D * sizeof(float));
   }
-  if (mode == ATOM_UPDATE_FWD) {
-    // W2 [N1][D]: M2[m][n] = W2[n][m]
-    for (int n = 0; n < N1; ++n)
-      for (int m = 0; m < D; ++m) m2[sw4<N1>(m, n)] = W2[(size_t)n * D + m];
+  auto w1 = [&](int k, int n) { return W1[(size_t)k * N1 + n] / s1[n]; };   // k < D, n < N1
+  auto w2 = [&](int n, int m) { return W2[(size_t)n * D + m] / s2[m]; };    // n < N1, m < D
+  if (mode == ATOM_UPDATE_FWD || mode == ATOM_READOUT)   // M1[n][k] = W1[k][n]
+    om_image<D, PR>(N1, D, N1, w1, out + P::M1, nullptr);
+  if (mode == ATOM_UPDATE_FWD) {                         // M2[m][n] = W2[n][m]
+    om_image<N1, PR>(D, N1, D, [&](int n, int m) { return w2(n, m); }, out + P::M2, nullptr);
     std::memcpy(v1, b1, N1 * sizeof(float));
     std::memcpy(v2, b2, D * sizeof(float));
   } else if (mode == ATOM_UPDATE_BWD) {
-    // W1 = Wu1 [D][N1], W2 = Wu2 [N1][D]: M1[n][m] = Wu2[n][m], M2[k][n] = Wu1[k][n]
-    for (int n = 0; n < N1; ++n)
-      for (int m = 0; m < D; ++m) m1[sw4<D>(n, m)] = W2[(size_t)n * D + m];
-    for (int k = 0; k < D; ++k)
-      for (int n = 0; n < N1; ++n) m2[sw4<N1>(k, n)] = W1[(size_t)k * N1 + n];
+    // M1[n][m] = Wu2[n][m] (contraction over m), M2[k][n] = Wu1[k][n] (over n)
+    om_image<D, PR>(N1, D, N1, [&](int m, int n) { return w2(n, m); }, out + P::M1, nullptr);
+    om_image<N1, PR>(D, N1, D, [&](int n, int k) { return w1(k, n); }, out + P::M2, nullptr);
   } else {
-    // W1 = Wo1 [D][N1]: M2[k][n] = Wo1[k][n]; W2 = wo2 [N1]
-    for (int k = 0; k < D; ++k)
-      for (int n = 0; n < N1; ++n) m2[sw4<N1>(k, n)] = W1[(size_t)k * N1 + n];
+    // M2[k][n] = Wo1[k][n] (over n); V2 = wo2 [N1], on the fp16 grid of its
+    // own scale when the operands are fp16
+    om_image<N1, PR>(D, N1, D, [&](int n, int k) { return w1(k, n); }, out + P::M2, nullptr);
     std::memcpy(v1, b1, N1 * sizeof(float));
-    std::memcpy(v2, W2, N1 * sizeof(float));
+    for (int n = 0; n < N1; ++n) v2[n] = W2[n];
+    if (SC) {
+      const float so = column_scales(W2, N1, 1)[0];
+      for (int n = 0; n < N1; ++n) v2[n] = (float)(_Float16)(W2[n] / so) * so;
+    }
   }
 }
 
-template <int D, int N1, int MODE>
+template <int D, int N1, int MODE, int PR>
 __global__ __launch_bounds__(64 * kAtomNW, 1) void k_atom(AtomArgs g) {
-  using P = AtomPlan<D, N1>;
+  using P = AtomPlan<D, N1, PR>;
+  constexpr bool SC = PR == PREC_F16S;
   extern __shared__ __align__(16) unsigned char lds[];
   {
     const f32x4* src = reinterpret_cast<const f32x4*>(g.img);
@@ -101,6 +132,9 @@ __global__ __launch_bounds__(64 * kAtomNW, 1) void k_atom(AtomArgs g) {
   const __amdgpu_buffer_rsrc_t rS = rsrc(g.S, g.S ? rows * N1 * 4u : 0u);
   const float* V1 = reinterpret_cast<const float*>(lds + P::V1);
   const float* V2 = reinterpret_cast<const float*>(lds + P::V2);
+  const float* S1 = reinterpret_cast<const float*>(lds + P::S1);
+  const float* S2 = reinterpret_cast<const float*>(lds + P::S2);
+  auto v4 = [&](const float* v, int i) { return *reinterpret_cast<const f32x4*>(v + i); };
 
   // tiles interleaved over the work-groups first, so that small systems
   // spread one tile per SIMD over all CUs before any SIMD gets a second
@@ -128,11 +162,16 @@ __global__ __launch_bounds__(64 * kAtomNW, 1) void k_atom(AtomArgs g) {
       }
     }
 
+    if constexpr (SC && MODE == ATOM_UPDATE_BWD) {   // contraction over Wu2's columns
+#pragma unroll
+      for (int kb = 0; kb < D / 16; ++kb) in[kb] *= v4(S2, g4 + 16 * kb);
+    }
     f32x4 u[N1 / 16];
-    gemm_om<D, N1, false>(u, in, lds + P::M1, lane);
+    gemm_om<D, N1, PR>(u, in, lds + P::M1, lane);
     float ep = 0.f;
 #pragma unroll
     for (int nb = 0; nb < N1 / 16; ++nb) {
+      if constexpr (SC && MODE != ATOM_UPDATE_BWD) u[nb] *= v4(S1, g4 + 16 * nb);
       if constexpr (MODE == ATOM_UPDATE_FWD) {
         const f32x4 b = *reinterpret_cast<const f32x4*>(V1 + g4 + 16 * nb);
         const f32x4 a = u[nb] + b;
@@ -165,12 +204,17 @@ __global__ __launch_bounds__(64 * kAtomNW, 1) void k_atom(AtomArgs g) {
       if (lane < kAtoms && ok) g.eps[atom] = ep + g.b2s;
     }
 
+    if constexpr (SC && MODE != ATOM_UPDATE_FWD) {   // contraction over W1's columns
+#pragma unroll
+      for (int nb = 0; nb < N1 / 16; ++nb) u[nb] *= v4(S1, g4 + 16 * nb);
+    }
     f32x4 y[D / 16];
-    gemm_om<N1, D, false>(y, u, lds + P::M2, lane);
+    gemm_om<N1, D, PR>(y, u, lds + P::M2, lane);
     if (ok) {
 #pragma unroll
       for (int kb = 0; kb < D / 16; ++kb) {
         f32x4 v = y[kb];
+        if constexpr (SC && MODE == ATOM_UPDATE_FWD) v *= v4(S2, g4 + 16 * kb);
         if constexpr (MODE == ATOM_UPDATE_FWD)
           v += bload4(rR, ro + 64u * kb) + *reinterpret_cast<const f32x4*>(V2 + g4 + 16 * kb);
         *reinterpret_cast<f32x4*>(g.Y + (size_t)atom * D + g4 + 16 * kb) = v;
@@ -179,20 +223,21 @@ __global__ __launch_bounds__(64 * kAtomNW, 1) void k_atom(AtomArgs g) {
   }
 }
 
-template <int D, int N1>
+template <int D, int N1, int PR>
 struct AtomKernels {
-  static constexpr int kD = D, kN1 = N1;
-  using P = AtomPlan<D, N1>;
+  static constexpr int kD = D, kN1 = N1, kPR = PR;
+  using P = AtomPlan<D, N1, PR>;
   static hipError_t prepare() {
     hipError_t e = hipSuccess;
-    if (D == N1) {
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_atom<D, N1, ATOM_UPDATE_FWD>),
+    if constexpr (D == N1) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_atom<D, N1, ATOM_UPDATE_FWD, PR>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, P::IMG);
       if (e == hipSuccess)
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_atom<D, N1, ATOM_UPDATE_BWD>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, P::IMG);
+        e = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&k_atom<D, N1, ATOM_UPDATE_BWD, PR>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, P::IMG);
     } else {
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_atom<D, N1, ATOM_READOUT>),
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_atom<D, N1, ATOM_READOUT, PR>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, P::IMG);
     }
     return e;
@@ -203,51 +248,57 @@ struct AtomKernels {
     if (G > n_cu) G = n_cu;
     if (G < 1) G = 1;
     const dim3 grid(G), block(64 * kAtomNW);
-    switch (g.mode) {
-      case ATOM_UPDATE_FWD:
-        if (D != N1) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((k_atom<D, N1, ATOM_UPDATE_FWD>), grid, block, P::IMG, s, g);
-        break;
-      case ATOM_UPDATE_BWD:
-        if (D != N1) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((k_atom<D, N1, ATOM_UPDATE_BWD>), grid, block, P::IMG, s, g);
-        break;
-      default:
-        if (D == N1) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((k_atom<D, N1, ATOM_READOUT>), grid, block, P::IMG, s, g);
+    if constexpr (D == N1) {   // the update networks
+      if (g.mode == ATOM_UPDATE_FWD)
+        hipLaunchKernelGGL((k_atom<D, N1, ATOM_UPDATE_FWD, PR>), grid, block, P::IMG, s, g);
+      else if (g.mode == ATOM_UPDATE_BWD)
+        hipLaunchKernelGGL((k_atom<D, N1, ATOM_UPDATE_BWD, PR>), grid, block, P::IMG, s, g);
+      else
+        return hipErrorInvalidValue;
+    } else {                   // the readout
+      if (g.mode != ATOM_READOUT) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((k_atom<D, N1, ATOM_READOUT, PR>), grid, block, P::IMG, s, g);
     }
     return hipGetLastError();
   }
 };
 
+// Atom-wise layers run fp32 operands unless every MLP is 16-bit (PREC_F16S);
+// a bfloat16 filter network leaves them fp32.
 template <class R, class F>
-static R atom_dispatch(int D, int N1, R fail, F f) {
-#define SN_AT(DD, NN) \
-  if (D == DD && N1 == NN) return f(AtomKernels<DD, NN>{});
-  SN_AT(64, 64) SN_AT(128, 128) SN_AT(64, 32) SN_AT(128, 32) SN_AT(128, 64)
+static R atom_dispatch(int D, int N1, int prec, R fail, F f) {
+#define SN_AT(DD, NN, PP) \
+  if (D == DD && N1 == NN && ap == PP) return f(AtomKernels<DD, NN, PP>{});
+#define SN_AT_P(PP) \
+  SN_AT(64, 64, PP) SN_AT(128, 128, PP) SN_AT(64, 32, PP) SN_AT(128, 32, PP) SN_AT(128, 64, PP)
+  const int ap = prec == PREC_F16S ? PREC_F16S : PREC_F32;
+  SN_AT_P(PREC_F32) SN_AT_P(PREC_F16S)
+#undef SN_AT_P
 #undef SN_AT
   return fail;
 }
 
-hipError_t atom_prepare(int D, int H) {
-  hipError_t e = atom_dispatch(D, D, hipErrorInvalidValue,
+hipError_t atom_prepare(int D, int H, int prec) {
+  hipError_t e = atom_dispatch(D, D, prec, hipErrorInvalidValue,
                                [](auto k) { return decltype(k)::prepare(); });
   if (e != hipSuccess) return e;
-  return atom_dispatch(D, H, hipErrorInvalidValue, [](auto k) { return decltype(k)::prepare(); });
+  return atom_dispatch(D, H, prec, hipErrorInvalidValue,
+                       [](auto k) { return decltype(k)::prepare(); });
 }
-size_t atom_image_bytes(int D, int N1) {
-  return atom_dispatch(D, N1, (size_t)0, [](auto k) { return (size_t)decltype(k)::P::IMG; });
+size_t atom_image_bytes(int D, int N1, int prec) {
+  return atom_dispatch(D, N1, prec, (size_t)0,
+                       [](auto k) { return (size_t)decltype(k)::P::IMG; });
 }
-void atom_fill_image(int mode, int D, int N1, const float* W1, const float* b1, const float* W2,
-                     const float* b2, unsigned char* out) {
-  atom_dispatch(D, N1, 0, [&](auto k) {
+void atom_fill_image(int mode, int D, int N1, int prec, const float* W1, const float* b1,
+                     const float* W2, const float* b2, unsigned char* out) {
+  atom_dispatch(D, N1, prec, 0, [&](auto k) {
     using K = decltype(k);
-    fill_atom_image<K::kD, K::kN1>(mode, W1, b1, W2, b2, out);
+    fill_atom_image<K::kD, K::kN1, K::kPR>(mode, W1, b1, W2, b2, out);
     return 0;
   });
 }
-hipError_t launch_atom(const AtomArgs& g, int D, int N1, int n_cu, hipStream_t s) {
-  return atom_dispatch(D, N1, hipErrorInvalidValue,
+hipError_t launch_atom(const AtomArgs& g, int D, int N1, int prec, int n_cu, hipStream_t s) {
+  return atom_dispatch(D, N1, prec, hipErrorInvalidValue,
                        [&](auto k) { return decltype(k)::launch(g, n_cu, s); });
 }
 

@@ -38,7 +38,8 @@ bool desc_ok(const sn_model_desc* d) {
          d->T <= 8 && (d->H == 32 || d->H == 64) && d->H <= d->D && std::isfinite(d->rbf_min) &&
          std::isfinite(d->rbf_max) && d->rbf_min >= 0.f && d->rbf_max > d->rbf_min &&
          std::isfinite(d->r_cut) && d->r_cut > 0.f &&
-         (d->filter_dtype == SN_FILTER_F32 || d->filter_dtype == SN_FILTER_BF16);
+         (d->filter_dtype == SN_FILTER_F32 || d->filter_dtype == SN_FILTER_BF16 ||
+          d->filter_dtype == SN_W16A16);
 }
 
 size_t block_floats(const sn_model_desc* d) {
@@ -154,8 +155,9 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
   float* eps = reinterpret_cast<float*>(ws + L.eps);
   float* fblk = reinterpret_cast<float*>(ws + L.fblk);
   const size_t ND = (size_t)n * D;
-  const int bf16 = d.filter_dtype == SN_FILTER_BF16;
-  const int wf = cf_workers(D, m->KP, bf16, 0), wb = cf_workers(D, m->KP, bf16, 1);
+  const int prec = d.filter_dtype;
+  const int bf16 = prec == PREC_BF16;
+  const int wf = cf_workers(D, m->KP, prec, 0), wb = cf_workers(D, m->KP, prec, 1);
   const int Gf = cf_grid(m, n, wf), Gb = cf_grid(m, n, wb);
   hipError_t e;
 
@@ -185,7 +187,7 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
   p.r_cut = d.r_cut;
   p.pi_over_rc = (float)(M_PI / (double)d.r_cut);
   p.half_over_rc = (float)(0.5 / (double)d.r_cut);
-  p.KC = cf_chunks(d.Dr, bf16);
+  p.KC = cf_chunks(d.Dr, prec);
 
   auto block_img = [&](int t) -> const void* { return m->cfimg + (size_t)t * m->img_bytes; };
   auto Wu = [&](int t, int k) {  // k: 0 Wu1, 1 cu1, 2 Wu2, 3 cu2
@@ -267,16 +269,16 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
       if ((e = uf_block(t, UF_FORWARD)) != hipSuccess) return hip_fail(e);
     } else {
       ProfScope ps(0, s);
-      if ((e = launch_cf_forward(D, m->KP, bf16, p, Gf, s)) != hipSuccess) return hip_fail(e);
+      if ((e = launch_cf_forward(D, m->KP, prec, p, Gf, s)) != hipSuccess) return hip_fail(e);
     }
     AtomArgs u{ATOM_UPDATE_FWD, (int)n, gbuf, nullptr, nullptr, x + t * ND, nullptr, au + t * ND,
                x + (t + 1) * ND, 0.f, nullptr, atom_img(t, 0)};
-    if ((e = launch_atom(u, D, D, m->n_cu, s)) != hipSuccess) return hip_fail(e);
+    if ((e = launch_atom(u, D, D, prec, m->n_cu, s)) != hipSuccess) return hip_fail(e);
   }
   // readout and its gradient
   AtomArgs r{ATOM_READOUT, (int)n, x + T * ND, nullptr, nullptr, nullptr, nullptr, nullptr, gx,
              m->co2, eps, ro_img};
-  if ((e = launch_atom(r, D, H, m->n_cu, s)) != hipSuccess) return hip_fail(e);
+  if ((e = launch_atom(r, D, H, prec, m->n_cu, s)) != hipSuccess) return hip_fail(e);
   if ((e = launch_energy(eps, sys->n_replicas, sys->atoms_per_replica, energy, st, s)) !=
       hipSuccess)
     return hip_fail(e);
@@ -286,7 +288,7 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
     const bool has_q = t < T - 1;
     AtomArgs b{ATOM_UPDATE_BWD, (int)n, gx, has_q ? tmp : nullptr, (has_q && t > 0) ? gx : nullptr,
                nullptr, au + t * ND, nullptr, gbuf, 0.f, nullptr, atom_img(t, 1)};
-    if ((e = launch_atom(b, D, D, m->n_cu, s)) != hipSuccess) return hip_fail(e);
+    if ((e = launch_atom(b, D, D, prec, m->n_cu, s)) != hipSuccess) return hip_fail(e);
     p.img = block_img(t);
     p.wg_start = wg_start_b;
     p.x = x + t * ND;
@@ -299,7 +301,7 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
       if ((e = uf_block(t, UF_BACKWARD)) != hipSuccess) return hip_fail(e);
     } else {
       ProfScope ps(1, s);
-      if ((e = launch_cf_backward(D, m->KP, bf16, p, Gb, s)) != hipSuccess) return hip_fail(e);
+      if ((e = launch_cf_backward(D, m->KP, prec, p, Gb, s)) != hipSuccess) return hip_fail(e);
     }
   }
   // the unfused pipeline accumulates dE/dr of every block into one array
@@ -440,7 +442,7 @@ sn_status sn_model_create(const sn_model_desc* d, const float* weights_host, siz
   if (!m) return SN_ERR_HIP;
   m->desc = *d;
   m->n_w = nw;
-  m->KP = cf_kp(d->Dr, d->filter_dtype == SN_FILTER_BF16);
+  m->KP = cf_kp(d->Dr, d->filter_dtype);
   const size_t D = d->D, H = d->H;
   m->off_emb = 0;
   size_t off = (size_t)d->n_types * D;
@@ -456,13 +458,13 @@ sn_status sn_model_create(const sn_model_desc* d, const float* weights_host, siz
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&m->n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e == hipSuccess) e = cf_prepare(d->D, m->KP, d->filter_dtype == SN_FILTER_BF16);
+  if (e == hipSuccess) e = cf_prepare(d->D, m->KP, d->filter_dtype);
   if (e == hipSuccess) e = hipMalloc(&m->w, nw * sizeof(float));
   if (e == hipSuccess) e = hipMemcpy(m->w, weights_host, nw * sizeof(float), hipMemcpyHostToDevice);
   if (e == hipSuccess) {
     // CFConv weight images, laid out as the kernels hold them in LDS
-    const int bf16 = d->filter_dtype == SN_FILTER_BF16;
-    m->img_bytes = cf_image_bytes(d->D, m->KP, bf16);
+    const int prec = d->filter_dtype;
+    m->img_bytes = cf_image_bytes(d->D, m->KP, prec);
     const size_t per = m->img_bytes;
     std::vector<unsigned char> hi(per * d->T);
     for (int t = 0; t < d->T; ++t) {
@@ -470,7 +472,7 @@ sn_status sn_model_create(const sn_model_desc* d, const float* weights_host, siz
       const float* cf1 = Wf1 + (size_t)d->Dr * D;
       const float* Wf2 = cf1 + D;
       const float* cf2 = Wf2 + D * D;
-      cf_fill_image(d->D, m->KP, bf16, d->Dr, Wf1, cf1, Wf2, cf2, hi.data() + t * per);
+      cf_fill_image(d->D, m->KP, prec, d->Dr, Wf1, cf1, Wf2, cf2, hi.data() + t * per);
     }
     e = (per == 0) ? hipErrorInvalidValue : hipMalloc(&m->cfimg, hi.size());
     if (e == hipSuccess) e = hipMemcpy(m->cfimg, hi.data(), hi.size(), hipMemcpyHostToDevice);
@@ -489,11 +491,11 @@ sn_status sn_model_create(const sn_model_desc* d, const float* weights_host, siz
     e = hipMalloc(&m->ufimg, hu.size());
     if (e == hipSuccess) e = hipMemcpy(m->ufimg, hu.data(), hu.size(), hipMemcpyHostToDevice);
   }
-  if (e == hipSuccess) e = atom_prepare(d->D, d->H);
+  if (e == hipSuccess) e = atom_prepare(d->D, d->H, d->filter_dtype);
   if (e == hipSuccess) {
     // atom-wise weight images, laid out as the kernels hold them in LDS
-    m->at_upd = atom_image_bytes(d->D, d->D);
-    m->at_ro = atom_image_bytes(d->D, d->H);
+    m->at_upd = atom_image_bytes(d->D, d->D, d->filter_dtype);
+    m->at_ro = atom_image_bytes(d->D, d->H, d->filter_dtype);
     std::vector<unsigned char> ha(2 * m->at_upd * d->T + m->at_ro);
     const size_t DD = D * D;
     for (int t = 0; t < d->T; ++t) {
@@ -502,10 +504,12 @@ sn_status sn_model_create(const sn_model_desc* d, const float* weights_host, siz
       const float* Wu2 = cu1 + D;
       const float* cu2 = Wu2 + DD;
       unsigned char* o = ha.data() + (size_t)t * 2 * m->at_upd;
-      atom_fill_image(ATOM_UPDATE_FWD, d->D, d->D, Wu1, cu1, Wu2, cu2, o);
-      atom_fill_image(ATOM_UPDATE_BWD, d->D, d->D, Wu1, cu1, Wu2, cu2, o + m->at_upd);
+      atom_fill_image(ATOM_UPDATE_FWD, d->D, d->D, d->filter_dtype, Wu1, cu1, Wu2, cu2, o);
+      atom_fill_image(ATOM_UPDATE_BWD, d->D, d->D, d->filter_dtype, Wu1, cu1, Wu2, cu2,
+                      o + m->at_upd);
     }
-    atom_fill_image(ATOM_READOUT, d->D, d->H, weights_host + m->off_o1, weights_host + m->off_co1,
+    atom_fill_image(ATOM_READOUT, d->D, d->H, d->filter_dtype, weights_host + m->off_o1,
+                    weights_host + m->off_co1,
                     weights_host + m->off_o2, nullptr, ha.data() + (size_t)d->T * 2 * m->at_upd);
     e = (m->at_upd == 0 || m->at_ro == 0) ? hipErrorInvalidValue : hipMalloc(&m->atimg, ha.size());
     if (e == hipSuccess) e = hipMemcpy(m->atimg, ha.data(), ha.size(), hipMemcpyHostToDevice);
@@ -576,7 +580,7 @@ sn_status sn_unfused_workspace_size(const sn_model_desc* d, const sn_system* sys
   if (!d || !sys || !bytes || !desc_ok(d) || !sys_ok(sys)) return SN_ERR_INVALID_ARG;
   if (edge_capacity < 0 || edge_capacity > INT32_MAX) return SN_ERR_INVALID_ARG;
   const size_t base = ws_layout(n_atoms(sys), d->D, d->T, d->H).total;
-  *bytes = uf_layout(base, edge_capacity, d->D, cf_kp(d->Dr, d->filter_dtype == SN_FILTER_BF16),
+  *bytes = uf_layout(base, edge_capacity, d->D, cf_kp(d->Dr, d->filter_dtype),
                      d->T).total;
   return SN_OK;
 }
@@ -590,6 +594,7 @@ sn_status sn_energy_forces_unfused(const sn_model* m, const sn_system* sys, cons
     return SN_ERR_INVALID_ARG;
   if (edge_capacity < 1 || edge_capacity > INT32_MAX) return SN_ERR_INVALID_ARG;
   if ((flags & ~SN_UNFUSED_ATOMIC) != 0) return SN_ERR_INVALID_ARG;
+  if (m->desc.filter_dtype == SN_W16A16) return SN_ERR_UNSUPPORTED;
   size_t need = 0;
   sn_status rc = sn_unfused_workspace_size(&m->desc, sys, edge_capacity, &need);
   if (rc != SN_OK) return rc;

@@ -23,7 +23,7 @@
 // the B-operand layout of the next, so basis -> GEMM1 -> shifted softplus ->
 // GEMM2 never leaves registers. The k index inside each MFMA is permuted to
 // match the rows a lane holds, and the weight images in LDS are laid out
-// (XOR-swizzled, permuted for bf16) so that every A operand is one 8- or
+// (XOR-swizzled, permuted for 16-bit types) so that every A operand is one 8- or
 // 16-byte read. Each lane computes its own edge's geometry and basis and
 // gathers its own sender/receiver feature rows with 16-byte loads.
 //
@@ -50,7 +50,9 @@
 // kernel sums the blocks.
 //
 // MFMA: v_mfma_f32_16x16x4_f32 (fp32 filters), v_mfma_f32_16x16x32_bf16
-// (bfloat16 filters, fp32 accumulation).
+// (bfloat16 filters) or v_mfma_f32_16x16x32_f16 (fp16 filters whose weight
+// columns carry power-of-two scales, §4.4 "Channel-wise quantization"), fp32
+// accumulation throughout.
 #include <climits>
 #include <cstring>
 
@@ -69,19 +71,21 @@ __device__ __forceinline__ float min_image(float u, float box, float half) {
 // ------------------------------------------------------------------ LDS plan
 // Weight image (built on the host, copied verbatim) then one transpose tile per wave.
 //   W1  : Wf1^T [D][KP] (k zero-padded past Dr)
-//   W2  : Wf2^T [D][D] (bf16: positions permuted by perm32)
-//   BIAS: cf1[D], cf2[D] (fp32); staged only where LDS has room, else read
-//         from the image in global memory
+//   W2  : Wf2^T [D][D] (16-bit: positions permuted by perm32)
+//   BIAS: cf1[D], cf2[D] (fp32); then, for fp16 filters, the column scales
+//         s1[D], s2[D]; staged only where LDS has room, else read from the
+//         image in global memory
 // Rows are output-major: the A operand of a lane is a run of its row.
-template <int D, int KP, bool BF16, int NW_>
+template <int D, int KP, int PR, int NW_>
 struct Plan {
   static constexpr int NW = NW_;               // workers (waves) per work-group
   static constexpr int NT = NW * 64;
-  static constexpr int ES = BF16 ? 2 : 4;
+  static constexpr int ES = PR != PREC_F32 ? 2 : 4;
   static constexpr int W1 = 0;
   static constexpr int W2 = W1 + D * KP * ES;
   static constexpr int BIAS = W2 + D * D * ES;
-  static constexpr int IMG = BIAS + 2 * D * 4;
+  static constexpr int SC = BIAS + 2 * D * 4;
+  static constexpr int IMG = SC + (PR == PREC_F16S ? 2 * D * 4 : 0);
   static constexpr int TB = kEdges * 64 * 4;   // transpose tile: 64 columns of 16 rows
   static constexpr int LDS_MAX = 160 * 1024;
   static constexpr bool BIAS_LDS = IMG + NW * TB <= LDS_MAX;
@@ -94,37 +98,29 @@ struct Plan {
 // Waves per work-group of each kernel at one work-group per CU: the forward
 // fits 128 registers (four waves per SIMD); the backward needs up to 256 at
 // D = 128 (two per SIMD; at three it spills and runs slower).
-template <int D, bool BF16, bool BWD>
+template <int D, int PR, bool BWD>
 constexpr int cf_nw() {
   return BWD ? 8 : 16;
 }
 
-int cf_kp(int Dr, int bf16) {
-  (void)bf16;
+int cf_kp(int Dr, int prec) {
+  (void)prec;
   return Dr <= 32 ? 32 : 64;
 }
-int cf_chunks(int Dr, int bf16) { return bf16 ? (Dr + 31) / 32 : (Dr + 7) / 8; }
+int cf_chunks(int Dr, int prec) { return prec != PREC_F32 ? (Dr + 31) / 32 : (Dr + 7) / 8; }
 
-template <int D, int KP, bool BF16>
+// Wf1 without the perm32 placement: the first product's B operand (the
+// basis) is evaluated directly in the k order a lane feeds.
+template <int D, int KP, int PR>
 static void fill_image(int Dr, const float* Wf1, const float* cf1, const float* Wf2,
                        const float* cf2, unsigned char* out) {
-  using P = Plan<D, KP, BF16, 1>;
+  using P = Plan<D, KP, PR, 1>;
   std::memset(out, 0, P::IMG);
-  if constexpr (BF16) {
-    uint16_t* w1 = reinterpret_cast<uint16_t*>(out + P::W1);
-    uint16_t* w2 = reinterpret_cast<uint16_t*>(out + P::W2);
-    for (int n = 0; n < D; ++n)
-      for (int k = 0; k < Dr; ++k) w1[sw8<KP>(n, k)] = bf16_rne_bits(Wf1[(size_t)k * D + n]);
-    for (int k = 0; k < D; ++k)
-      for (int n = 0; n < D; ++n) w2[sw8<D>(n, perm32(k))] = bf16_rne_bits(Wf2[(size_t)k * D + n]);
-  } else {
-    float* w1 = reinterpret_cast<float*>(out + P::W1);
-    float* w2 = reinterpret_cast<float*>(out + P::W2);
-    for (int n = 0; n < D; ++n)
-      for (int k = 0; k < Dr; ++k) w1[sw4<KP>(n, k)] = Wf1[(size_t)k * D + n];
-    for (int k = 0; k < D; ++k)
-      for (int n = 0; n < D; ++n) w2[sw4<D>(n, k)] = Wf2[(size_t)k * D + n];
-  }
+  float* sc = reinterpret_cast<float*>(out + P::SC);
+  om_image<KP, PR, false>(D, Dr, D, [&](int k, int n) { return Wf1[(size_t)k * D + n]; },
+                          out + P::W1, sc);
+  om_image<D, PR, true>(D, D, D, [&](int k, int n) { return Wf2[(size_t)k * D + n]; },
+                        out + P::W2, sc + D);
   float* bias = reinterpret_cast<float*>(out + P::BIAS);
   std::memcpy(bias, cf1, D * sizeof(float));
   std::memcpy(bias + D, cf2, D * sizeof(float));
@@ -144,6 +140,13 @@ template <class P>
 __device__ __forceinline__ f32x4 bias4(const CfParams& p, const unsigned char* lds, int lo, int k) {
   const unsigned char* base =
       P::BIAS_LDS ? lds + P::BIAS : reinterpret_cast<const unsigned char*>(p.img) + P::BIAS;
+  return *reinterpret_cast<const f32x4*>(base + 4 * lo + 4 * k);
+}
+// Column scales s1 (idx < D) or s2 (idx - D), as bias4 (fp16 filters only).
+template <class P>
+__device__ __forceinline__ f32x4 scale4(const CfParams& p, const unsigned char* lds, int lo, int k) {
+  const unsigned char* base =
+      P::BIAS_LDS ? lds + P::SC : reinterpret_cast<const unsigned char*>(p.img) + P::SC;
   return *reinterpret_cast<const f32x4*>(base + 4 * lo + 4 * k);
 }
 
@@ -185,14 +188,15 @@ __device__ __forceinline__ Geo geometry(const CfParams& p, __amdgpu_buffer_rsrc_
 // of edge lane % 16.
 
 // GEMM1: acc[q][nb] += sum_k Wf1[k][16 nb + e] * basis_q(k) for k < 8 KC (fp32)
-// or 32 KC (bf16); basis_0 = b~ (Gaussian x envelope), basis_1 = d b~ / dd.
+// or 32 KC (16-bit); basis_0 = b~ (Gaussian x envelope), basis_1 = d b~ / dd.
 // Each lane evaluates the basis of its own edge for the k slots it feeds
-// (fp32: k = 8c + 2g + u for the MFMA pair u; bf16: k = 32c + 8g + t).
-template <int D, int KP, bool BF16, int NA>
+// (fp32: k = 8c + 2g + u for the MFMA pair u; 16-bit: k = 32c + 8g + t).
+template <int D, int KP, int PR, int NA>
 __device__ __forceinline__ void gemm1(f32x4 (&acc)[NA][D / 16], const unsigned char* lds,
                                       const CfParams& p, const Geo& g, int lane_) {
+  constexpr bool H16 = PR != PREC_F32;
   const int lane = opaque(lane_), grp = lane >> 4, e = lane & 15;
-  constexpr int CH = BF16 ? 32 : 8;    // k per chunk
+  constexpr int CH = H16 ? 32 : 8;     // k per chunk
   constexpr int PL = CH / 4;           // k per lane group per chunk
   float step = p.rbf_step;
   asm volatile("" : "+v"(step));
@@ -209,16 +213,18 @@ __device__ __forceinline__ void gemm1(f32x4 (&acc)[NA][D / 16], const unsigned c
       b[0][t] = gs * g.C;
       if constexpr (NA == 2) b[1][t] = gs * (g.Cp - z * inv_s2 * g.C);
     }
-    if constexpr (BF16) {
-      const __bf16* W1 = reinterpret_cast<const __bf16*>(lds);
-      bf16x8 bq[NA];
+    if constexpr (H16) {
+      using E = typename PrecT<PR>::E;
+      using V8 = typename PrecT<PR>::V8;
+      const E* W1 = reinterpret_cast<const E*>(lds);
+      V8 bq[NA];
 #pragma unroll
       for (int q = 0; q < NA; ++q)
 #pragma unroll
-        for (int t = 0; t < 8; ++t) bq[q][t] = (__bf16)b[q][t];
+        for (int t = 0; t < 8; ++t) bq[q][t] = (E)b[q][t];
 #pragma unroll
       for (int nb = 0; nb < D / 16; ++nb) {
-        const bf16x8 w = *reinterpret_cast<const bf16x8*>(W1 + sw8<KP>(16 * nb + e, CH * c + PL * grp));
+        const V8 w = *reinterpret_cast<const V8*>(W1 + sw8<KP>(16 * nb + e, CH * c + PL * grp));
 #pragma unroll
         for (int q = 0; q < NA; ++q) acc[q][nb] = mfma16(w, bq[q], acc[q][nb]);
       }
@@ -377,9 +383,9 @@ __device__ __forceinline__ TileHead tile_head(const CfParams& p, const Walk& wk,
   return t;
 }
 
-template <int D, int KP, bool BF16>
-__global__ __launch_bounds__((64 * cf_nw<D, BF16, false>()), 1) void k_cf_fwd(CfParams p) {
-  using P = Plan<D, KP, BF16, cf_nw<D, BF16, false>()>;
+template <int D, int KP, int PR>
+__global__ __launch_bounds__((64 * cf_nw<D, PR, false>()), 1) void k_cf_fwd(CfParams p) {
+  using P = Plan<D, KP, PR, cf_nw<D, PR, false>()>;
   constexpr int NB = D / 16;
   extern __shared__ __align__(16) unsigned char lds[];
   stage_image<P>(p.img, lds);
@@ -411,19 +417,25 @@ __global__ __launch_bounds__((64 * cf_nw<D, BF16, false>()), 1) void k_cf_fwd(Cf
     // only occupy registers)
     const int lane_t = opaque(lane);
     const int g4 = 4 * (lane_t >> 4);   // this lane's feature offset in a block
-    const ImgLanes<D, BF16> wl(lane_t);
+    const ImgLanes<D, PR> wl(lane_t);
     const TileLanes tl(lane_t);
 
     // s = ssp(b~ Wf1 + cf1)
     f32x4 s[1][NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) s[0][nb] = f32x4{};
-    gemm1<D, KP, BF16, 1>(s, lds, p, g, lane);
+    gemm1<D, KP, PR, 1>(s, lds, p, g, lane);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const f32x4 c1 = bias4<P>(p, lds, g4, 16 * nb);
+      if constexpr (PR == PREC_F16S) {
+        const f32x4 s1 = scale4<P>(p, lds, g4, 16 * nb);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s[0][nb][r] = ssp(s[0][nb][r] + c1[r]);
+        for (int r = 0; r < 4; ++r) s[0][nb][r] = ssp(fmaf(s[0][nb][r], s1[r], c1[r]));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[0][nb][r] = ssp(s[0][nb][r] + c1[r]);
+      }
     }
     pjx = bload(wk.rpos, (uint32_t)jn * 12u);
     pjy = bload(wk.rpos, (uint32_t)jn * 12u + 4);
@@ -439,13 +451,14 @@ __global__ __launch_bounds__((64 * cf_nw<D, BF16, false>()), 1) void k_cf_fwd(Cf
     for (int b = 0; b < 4; ++b) xg[b] = bload4(rx, xo + (uint32_t)(64 * b));
     __builtin_amdgcn_sched_barrier(0);
     f32x4 w[NB];
-    gemm_om<D, D, BF16>(w, s[0], lds + P::W2, wl);
+    gemm_om<D, D, PR>(w, s[0], lds + P::W2, wl);
 #pragma unroll
     for (int pss = 0; pss < NB / 4; ++pss) {
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int nb = 4 * pss + b;
         const f32x4 c2 = bias4<P>(p, lds, g4, D + 16 * nb);
+        if constexpr (PR == PREC_F16S) w[nb] *= scale4<P>(p, lds, g4, D + 16 * nb);
         f32x4 m;
 #pragma unroll
         for (int r = 0; r < 4; ++r) m[r] = xg[b][r] * (g.in * (w[nb][r] + c2[r]));
@@ -466,9 +479,9 @@ __global__ __launch_bounds__((64 * cf_nw<D, BF16, false>()), 1) void k_cf_fwd(Cf
     for (int c = lane; c < D; c += 64) p.h[(size_t)i * D + c] = 0.f;
 }
 
-template <int D, int KP, bool BF16>
-__global__ __launch_bounds__((64 * cf_nw<D, BF16, true>()), 1) void k_cf_bwd(CfParams p) {
-  using P = Plan<D, KP, BF16, cf_nw<D, BF16, true>()>;
+template <int D, int KP, int PR>
+__global__ __launch_bounds__((64 * cf_nw<D, PR, true>()), 1) void k_cf_bwd(CfParams p) {
+  using P = Plan<D, KP, PR, cf_nw<D, PR, true>()>;
   constexpr int NB = D / 16;
   extern __shared__ __align__(16) unsigned char lds[];
   stage_image<P>(p.img, lds);
@@ -503,7 +516,7 @@ __global__ __launch_bounds__((64 * cf_nw<D, BF16, true>()), 1) void k_cf_bwd(CfP
     // only occupy registers)
     const int lane_t = opaque(lane);
     const int g4 = 4 * (lane_t >> 4);   // this lane's feature offset in a block
-    const ImgLanes<D, BF16> wl(lane_t);
+    const ImgLanes<D, PR> wl(lane_t);
     const TileLanes tl(lane_t);
 
     // GEMM1: a = b~ Wf1 + cf1 and its tangent a' = (d b~/dd) Wf1;
@@ -513,10 +526,15 @@ __global__ __launch_bounds__((64 * cf_nw<D, BF16, true>()), 1) void k_cf_bwd(CfP
     for (int q = 0; q < 2; ++q)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) av[q][nb] = f32x4{};
-    gemm1<D, KP, BF16, 2>(av, lds, p, g, lane);
+    gemm1<D, KP, PR, 2>(av, lds, p, g, lane);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const f32x4 c1 = bias4<P>(p, lds, g4, 16 * nb);
+      if constexpr (PR == PREC_F16S) {
+        const f32x4 s1 = scale4<P>(p, lds, g4, 16 * nb);
+        av[0][nb] *= s1;
+        av[1][nb] *= s1;
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float sv, sg;
@@ -548,8 +566,8 @@ __global__ __launch_bounds__((64 * cf_nw<D, BF16, true>()), 1) void k_cf_bwd(CfP
     // GEMM2 for the tangents, all blocks (frees s'): w' = s' Wf2; the values
     // w = s Wf2 follow one output block at a time
     f32x4 wt[NB];
-    gemm_om<D, D, BF16>(wt, av[1], lds + P::W2, wl);
-    const Operand<D, BF16> os(av[0]);
+    gemm_om<D, D, PR>(wt, av[1], lds + P::W2, wl);
+    const Operand<D, PR> os(av[0]);
 
     // per 64 features: q = dE/dh_j w summed per receiver;
     // dE/dd += <dE/dh_i x_j + dE/dh_j x_i, w'>. A block's gather registers
@@ -562,9 +580,14 @@ __global__ __launch_bounds__((64 * cf_nw<D, BF16, true>()), 1) void k_cf_bwd(CfP
         const int nb = 4 * pss + b;
         __builtin_amdgcn_sched_barrier(0);
         f32x4 wv = f32x4{};
-        gemm_om_block<D, BF16>(wv, os, lds + P::W2, nb, wl);
+        gemm_om_block<D, PR>(wv, os, lds + P::W2, nb, wl);
         const f32x4 xj = G[b][0], gj = G[b][1], xi = G[b][2], gi = G[b][3];
         const f32x4 c2 = bias4<P>(p, lds, g4, D + 16 * nb);
+        if constexpr (PR == PREC_F16S) {
+          const f32x4 s2 = scale4<P>(p, lds, g4, D + 16 * nb);
+          wv *= s2;
+          wt[nb] *= s2;
+        }
         f32x4 qv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -657,66 +680,67 @@ hipError_t launch_force_sum(const float* fb, int T, int64_t n_atoms, float* forc
 }
 
 // ------------------------------------------------------------------ dispatch
-template <int D, int KP, bool BF16>
+template <int D, int KP, int PR>
 struct CfKernels {
-  using PF = Plan<D, KP, BF16, cf_nw<D, BF16, false>()>;
-  using PB = Plan<D, KP, BF16, cf_nw<D, BF16, true>()>;
+  using PF = Plan<D, KP, PR, cf_nw<D, PR, false>()>;
+  using PB = Plan<D, KP, PR, cf_nw<D, PR, true>()>;
   static hipError_t prepare() {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_cf_fwd<D, KP, BF16>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_cf_fwd<D, KP, PR>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, PF::TOTAL);
     if (e != hipSuccess) return e;
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_cf_bwd<D, KP, BF16>),
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_cf_bwd<D, KP, PR>),
                                hipFuncAttributeMaxDynamicSharedMemorySize, PB::TOTAL);
   }
   static size_t image_bytes() { return PF::IMG; }
   static int workers(int bwd) { return bwd ? PB::NW : PF::NW; }
   static void fill(int Dr, const float* Wf1, const float* cf1, const float* Wf2, const float* cf2,
                    unsigned char* out) {
-    fill_image<D, KP, BF16>(Dr, Wf1, cf1, Wf2, cf2, out);
+    fill_image<D, KP, PR>(Dr, Wf1, cf1, Wf2, cf2, out);
   }
   static hipError_t fwd(const CfParams& p, int G, hipStream_t s) {
-    hipLaunchKernelGGL((k_cf_fwd<D, KP, BF16>), dim3(G), dim3(PF::NT), PF::TOTAL, s, p);
+    hipLaunchKernelGGL((k_cf_fwd<D, KP, PR>), dim3(G), dim3(PF::NT), PF::TOTAL, s, p);
     return hipGetLastError();
   }
   static hipError_t bwd(const CfParams& p, int G, hipStream_t s) {
-    hipLaunchKernelGGL((k_cf_bwd<D, KP, BF16>), dim3(G), dim3(PB::NT), PB::TOTAL, s, p);
+    hipLaunchKernelGGL((k_cf_bwd<D, KP, PR>), dim3(G), dim3(PB::NT), PB::TOTAL, s, p);
     return hipGetLastError();
   }
 };
 
 template <class R, class F>
-static R cf_dispatch(int D, int KP, int bf16, R fail, F f) {
-#define SN_CF(DD, KK, BB) \
-  if (D == DD && KP == KK && (bf16 != 0) == BB) return f(CfKernels<DD, KK, BB>{});
-  SN_CF(64, 32, false) SN_CF(64, 64, false) SN_CF(128, 32, false) SN_CF(128, 64, false)
-  SN_CF(64, 32, true) SN_CF(64, 64, true) SN_CF(128, 32, true) SN_CF(128, 64, true)
+static R cf_dispatch(int D, int KP, int prec, R fail, F f) {
+#define SN_CF(DD, KK, PP) \
+  if (D == DD && KP == KK && prec == PP) return f(CfKernels<DD, KK, PP>{});
+#define SN_CF_P(PP) SN_CF(64, 32, PP) SN_CF(64, 64, PP) SN_CF(128, 32, PP) SN_CF(128, 64, PP)
+  SN_CF_P(PREC_F32) SN_CF_P(PREC_BF16) SN_CF_P(PREC_F16S)
+#undef SN_CF_P
 #undef SN_CF
   return fail;
 }
 
-hipError_t cf_prepare(int D, int KP, int bf16) {
-  return cf_dispatch(D, KP, bf16, hipErrorInvalidValue,
+hipError_t cf_prepare(int D, int KP, int prec) {
+  return cf_dispatch(D, KP, prec, hipErrorInvalidValue,
                      [](auto k) { return decltype(k)::prepare(); });
 }
-int cf_workers(int D, int KP, int bf16, int bwd) {
-  return cf_dispatch(D, KP, bf16, 0, [&](auto k) { return decltype(k)::workers(bwd); });
+int cf_workers(int D, int KP, int prec, int bwd) {
+  return cf_dispatch(D, KP, prec, 0, [&](auto k) { return decltype(k)::workers(bwd); });
 }
-size_t cf_image_bytes(int D, int KP, int bf16) {
-  return cf_dispatch(D, KP, bf16, (size_t)0, [](auto k) { return decltype(k)::image_bytes(); });
+size_t cf_image_bytes(int D, int KP, int prec) {
+  return cf_dispatch(D, KP, prec, (size_t)0, [](auto k) { return decltype(k)::image_bytes(); });
 }
-void cf_fill_image(int D, int KP, int bf16, int Dr, const float* Wf1, const float* cf1,
+void cf_fill_image(int D, int KP, int prec, int Dr, const float* Wf1, const float* cf1,
                    const float* Wf2, const float* cf2, unsigned char* out) {
-  cf_dispatch(D, KP, bf16, 0, [&](auto k) {
+  cf_dispatch(D, KP, prec, 0, [&](auto k) {
     decltype(k)::fill(Dr, Wf1, cf1, Wf2, cf2, out);
     return 0;
   });
 }
-hipError_t launch_cf_forward(int D, int KP, int bf16, const CfParams& p, int G, hipStream_t s) {
-  return cf_dispatch(D, KP, bf16, hipErrorInvalidValue,
+hipError_t launch_cf_forward(int D, int KP, int prec, const CfParams& p, int G, hipStream_t s) {
+  return cf_dispatch(D, KP, prec, hipErrorInvalidValue,
                      [&](auto k) { return decltype(k)::fwd(p, G, s); });
 }
-hipError_t launch_cf_backward(int D, int KP, int bf16, const CfParams& p, int G, hipStream_t s) {
-  return cf_dispatch(D, KP, bf16, hipErrorInvalidValue,
+hipError_t launch_cf_backward(int D, int KP, int prec, const CfParams& p, int G, hipStream_t s) {
+  return cf_dispatch(D, KP, prec, hipErrorInvalidValue,
                      [&](auto k) { return decltype(k)::bwd(p, G, s); });
 }
 

@@ -11,6 +11,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 namespace sn {
 
@@ -31,12 +32,36 @@ struct DevStatus {
   int64_t pad[3];
 };
 
+// MLP operand precisions (the filter_dtype values of sn_model_desc): fp32;
+// bfloat16 filter network; fp16 operands with per-output-channel power-of-two
+// scales in every MLP.
+enum Prec { PREC_F32 = 0, PREC_BF16 = 1, PREC_F16S = 2 };
+
 // Round-to-nearest-even bfloat16 bits of a finite float (host side).
 inline uint16_t bf16_rne_bits(float f) {
   uint32_t u;
   __builtin_memcpy(&u, &f, 4);
   u += 0x7FFFu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
+}
+
+// IEEE binary16 bits of a float, round to nearest even (host side).
+inline uint16_t f16_rne_bits(float f) {
+  const _Float16 h = (_Float16)f;
+  uint16_t u;
+  __builtin_memcpy(&u, &h, 2);
+  return u;
+}
+
+// Per-output-channel scale of a weight matrix for fp16 operands: the power of
+// two at or above the column's largest magnitude (1 for an all-zero column),
+// so that W / s lies in [-1, 1] and the division is exact.
+inline float pow2_scale(float absmax) {
+  if (!(absmax > 0.f)) return 1.f;
+  int e = 0;
+  const float m = __builtin_frexpf(absmax, &e);   // absmax = m 2^e, m in [0.5, 1)
+  (void)m;
+  return __builtin_ldexpf(1.f, e);
 }
 
 __device__ inline void dev_fail(DevStatus* st, int code, int64_t detail) {
@@ -89,20 +114,21 @@ struct CfParams {
   float* forces;      // backward: this block's dE/dr [N][3]
 };
 
-int cf_kp(int Dr, int bf16);               // basis length the LDS images are padded to
-int cf_chunks(int Dr, int bf16);           // basis chunks (8 fp32 / 16 bf16 basis functions each)
-int cf_workers(int D, int KP, int bf16, int bwd);  // waves (workers) per work-group of a kernel
-hipError_t cf_prepare(int D, int KP, int bf16);  // raises the dynamic LDS limit of the kernels
+// prec: the model's filter_dtype (Prec).
+int cf_kp(int Dr, int prec);               // basis length the LDS images are padded to
+int cf_chunks(int Dr, int prec);           // basis chunks (8 fp32 / 32 16-bit basis functions each)
+int cf_workers(int D, int KP, int prec, int bwd);  // waves (workers) per work-group of a kernel
+hipError_t cf_prepare(int D, int KP, int prec);  // raises the dynamic LDS limit of the kernels
 // Filter-weight image of one interaction block as the CFConv kernels hold it
 // in LDS: cf_image_bytes bytes, filled on the host.
-size_t cf_image_bytes(int D, int KP, int bf16);
-void cf_fill_image(int D, int KP, int bf16, int Dr, const float* Wf1, const float* cf1,
+size_t cf_image_bytes(int D, int KP, int prec);
+void cf_fill_image(int D, int KP, int prec, int Dr, const float* Wf1, const float* cf1,
                    const float* Wf2, const float* cf2, unsigned char* out);
 hipError_t launch_force_sum(const float* fb, int T, int64_t n_atoms, float* forces, hipStream_t s);
 hipError_t launch_partition(const int32_t* rowptr, int n_atoms, int G, int32_t* wg_start,
                             hipStream_t s);
-hipError_t launch_cf_forward(int D, int KP, int bf16, const CfParams& p, int G, hipStream_t s);
-hipError_t launch_cf_backward(int D, int KP, int bf16, const CfParams& p, int G, hipStream_t s);
+hipError_t launch_cf_forward(int D, int KP, int prec, const CfParams& p, int G, hipStream_t s);
+hipError_t launch_cf_backward(int D, int KP, int prec, const CfParams& p, int G, hipStream_t s);
 
 enum AtomMode { ATOM_UPDATE_FWD = 0, ATOM_UPDATE_BWD = 1, ATOM_READOUT = 2 };
 struct AtomArgs {
@@ -121,11 +147,13 @@ struct AtomArgs {
 };
 // Weight image of one atom-wise network for `mode`: W1 [D][N1], b1 [N1],
 // W2 [N1][D] (readout: wo2 [N1]), b2 [D]; built on the host.
-size_t atom_image_bytes(int D, int N1);
-void atom_fill_image(int mode, int D, int N1, const float* W1, const float* b1, const float* W2,
-                     const float* b2, unsigned char* out);
-hipError_t atom_prepare(int D, int H);   // raises the dynamic LDS limit of the kernels
-hipError_t launch_atom(const AtomArgs& g, int D, int N1, int n_cu, hipStream_t s);
+// prec: the model's filter_dtype (Prec); the atom-wise layers use fp16
+// operands only for PREC_F16S.
+size_t atom_image_bytes(int D, int N1, int prec);
+void atom_fill_image(int mode, int D, int N1, int prec, const float* W1, const float* b1,
+                     const float* W2, const float* b2, unsigned char* out);
+hipError_t atom_prepare(int D, int H, int prec);   // raises the dynamic LDS limit of the kernels
+hipError_t launch_atom(const AtomArgs& g, int D, int N1, int prec, int n_cu, hipStream_t s);
 hipError_t launch_embed(const int32_t* types, const float* emb, int n_atoms, int D, int n_types,
                         float* x, DevStatus* st, hipStream_t s);
 hipError_t launch_energy(const float* eps, int n_rep, int n_per, float* energy, DevStatus* st,

@@ -69,6 +69,14 @@ __device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Operand element type of each precision and its 8-wide vector.
+template <int PR> struct PrecT { using E = float; };
+template <> struct PrecT<PREC_BF16> { using E = __bf16; using V8 = bf16x8; };
+template <> struct PrecT<PREC_F16S> { using E = _Float16; using V8 = f16x8; };
 
 // XOR-swizzled offset of element (row, col) of a row-major array with RL
 // elements per row: 16-byte chunks (4 fp32 or 8 bf16) trade places by row, so
@@ -93,22 +101,22 @@ __host__ __device__ constexpr int perm32(int k) {
 // B operands of a chained product from an accumulator-layout input: fp32 uses
 // the accumulator registers directly; bf16 packs them once (k slot 8 g + t of
 // step kk is register t % 4 of block 2 kk + t / 4).
-template <int K, bool BF16>
-struct Operand;
-template <int K>
-struct Operand<K, false> {
-  const f32x4 (&S)[K / 16];
-  __device__ __forceinline__ explicit Operand(const f32x4 (&s)[K / 16]) : S(s) {}
-};
-template <int K>
-struct Operand<K, true> {
-  bf16x8 S[K / 32];
+template <int K, int PR>
+struct Operand {   // 16-bit operands
+  using V8 = typename PrecT<PR>::V8;
+  using E = typename PrecT<PR>::E;
+  V8 S[K / 32];
   __device__ __forceinline__ explicit Operand(const f32x4 (&s)[K / 16]) {
 #pragma unroll
     for (int kk = 0; kk < K / 32; ++kk)
 #pragma unroll
-      for (int t = 0; t < 8; ++t) S[kk][t] = (__bf16)s[2 * kk + (t >> 2)][t & 3];
+      for (int t = 0; t < 8; ++t) S[kk][t] = (E)s[2 * kk + (t >> 2)][t & 3];
   }
+};
+template <int K>
+struct Operand<K, PREC_F32> {
+  const f32x4 (&S)[K / 16];
+  __device__ __forceinline__ explicit Operand(const f32x4 (&s)[K / 16]) : S(s) {}
 };
 
 // Per-lane element offsets of the A-operand reads of an output-major image
@@ -116,32 +124,34 @@ struct Operand<K, true> {
 // row's low 4 bits, so only the low 4 bits of the chunk vary per lane: four
 // offsets (chunk group q) plus compile-time constants address every read.
 // Build once per tile from the lane index.
-template <int K, bool BF16>
+template <int K, int PR>
 struct ImgLanes {
   int off[4];
   __device__ __forceinline__ explicit ImgLanes(int lane) {
     const int grp = lane >> 4, e = lane & 15;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      if constexpr (BF16) off[q] = sw8<K>(e, 32 * q + 8 * grp);
+      if constexpr (PR != PREC_F32) off[q] = sw8<K>(e, 32 * q + 8 * grp);
       else off[q] = sw4<K>(e, 16 * q + 4 * grp);
     }
   }
 };
 
 // acc += sum_k M[16 nb + e][k] S[k] for one output block nb; M is an
-// output-major image with K elements per row (fp32: sw4 rows; bf16: sw8 rows
-// with perm32 positions).
-template <int K, bool BF16>
-__device__ __forceinline__ void gemm_om_block(f32x4& acc, const Operand<K, BF16>& op,
+// output-major image with K elements per row (fp32: sw4 rows; 16-bit: sw8
+// rows with perm32 positions).
+template <int K, int PR>
+__device__ __forceinline__ void gemm_om_block(f32x4& acc, const Operand<K, PR>& op,
                                               const void* img, int nb,
-                                              const ImgLanes<K, BF16>& ln) {
-  if constexpr (BF16) {
+                                              const ImgLanes<K, PR>& ln) {
+  if constexpr (PR != PREC_F32) {
     static_assert(K / 32 <= 4, "chunk groups");
-    const __bf16* M = reinterpret_cast<const __bf16*>(img) + 16 * nb * K;
+    using E = typename PrecT<PR>::E;
+    using V8 = typename PrecT<PR>::V8;
+    const E* M = reinterpret_cast<const E*>(img) + 16 * nb * K;
 #pragma unroll
     for (int kk = 0; kk < K / 32; ++kk) {
-      const bf16x8 w = *reinterpret_cast<const bf16x8*>(M + ln.off[kk]);
+      const V8 w = *reinterpret_cast<const V8*>(M + ln.off[kk]);
       acc = mfma16(w, op.S[kk], acc);
     }
   } else {
@@ -157,23 +167,55 @@ __device__ __forceinline__ void gemm_om_block(f32x4& acc, const Operand<K, BF16>
 }
 
 // All NOUT / 16 output blocks: out[nb] = sum_k M[16 nb + e][k] S[k] (k < K).
-template <int K, int NOUT, bool BF16>
+template <int K, int NOUT, int PR>
 __device__ __forceinline__ void gemm_om(f32x4 (&out)[NOUT / 16], const f32x4 (&S)[K / 16],
-                                        const void* img, const ImgLanes<K, BF16>& ln) {
-  const Operand<K, BF16> op(S);
+                                        const void* img, const ImgLanes<K, PR>& ln) {
+  const Operand<K, PR> op(S);
 #pragma unroll
   for (int nb = 0; nb < NOUT / 16; ++nb) {
     f32x4 acc = f32x4{};
-    gemm_om_block<K, BF16>(acc, op, img, nb, ln);
+    gemm_om_block<K, PR>(acc, op, img, nb, ln);
     out[nb] = acc;
   }
 }
 // The same, with the lane offsets built from the lane index here.
-template <int K, int NOUT, bool BF16>
+template <int K, int NOUT, int PR>
 __device__ __forceinline__ void gemm_om(f32x4 (&out)[NOUT / 16], const f32x4 (&S)[K / 16],
                                         const void* img, int lane_) {
-  const ImgLanes<K, BF16> ln(opaque(lane_));
-  gemm_om<K, NOUT, BF16>(out, S, img, ln);
+  const ImgLanes<K, PR> ln(opaque(lane_));
+  gemm_om<K, NOUT, PR>(out, S, img, ln);
+}
+
+// Host: output-major image of the K x N product matrix m(k, n) (zero for
+// k >= Kin or n >= Nin) for precision PR, with the per-output-channel scales
+// of PREC_F16S written to scale[N] (left alone otherwise). fp32: sw4 rows;
+// bf16: rounded values at sw8 positions; f16: m / s_n rounded. PERM places
+// 16-bit values at their perm32 positions (for chained-product operands).
+// With scale == nullptr, PREC_F16S rounds m itself (the caller has divided
+// by scales of its own).
+template <int K, int PR, bool PERM = true, class F>
+void om_image(int N, int Kin, int Nin, F m, unsigned char* out, float* scale) {
+  for (int n = 0; n < N; ++n) {
+    float s = 1.f;
+    if constexpr (PR == PREC_F16S) {
+      if (scale) {
+        float amax = 0.f;
+        for (int k = 0; k < Kin && n < Nin; ++k) amax = fmaxf(amax, fabsf(m(k, n)));
+        s = pow2_scale(amax);
+        scale[n] = s;
+      }
+    }
+    for (int k = 0; k < K; ++k) {
+      const float v = (k < Kin && n < Nin) ? m(k, n) : 0.f;
+      if constexpr (PR == PREC_F32) {
+        reinterpret_cast<float*>(out)[sw4<K>(n, k)] = v;
+      } else if constexpr (PR == PREC_BF16) {
+        reinterpret_cast<uint16_t*>(out)[sw8<K>(n, PERM ? perm32(k) : k)] = bf16_rne_bits(v);
+      } else {
+        reinterpret_cast<uint16_t*>(out)[sw8<K>(n, PERM ? perm32(k) : k)] = f16_rne_bits(v / s);
+      }
+    }
+  }
 }
 
 } // namespace sn

@@ -18,6 +18,7 @@
 // The dense products run on MFMA with the weights as the LDS-resident A
 // operand (tile16.hpp); everything else streams through HBM.
 #include <functional>
+#include <type_traits>
 
 #include "tile16.hpp"
 
@@ -163,11 +164,11 @@ __global__ __launch_bounds__(kThreads) void k_uf_rowscale(Edges r, float* X, con
 // ------------------------------------------------------------------ dense products
 // Y[e][:] = X[e][:] M (+ bias) for 16-edge tiles; M [K][N] is an output-major
 // image (uf_fill_images) staged once per work-group into LDS.
-template <int K, int N, bool BF16>
+template <int K, int N, int PR>
 __global__ __launch_bounds__(64 * kGemmWaves) void k_uf_gemm(Edges r, const float* X,
                                                             const void* img, const float* bias,
                                                             float* Y) {
-  constexpr int IMG = N * K * (BF16 ? 2 : 4);
+  constexpr int IMG = N * K * (PR != PREC_F32 ? 2 : 4);
   extern __shared__ __align__(16) unsigned char lds[];
   {
     const f32x4* src = reinterpret_cast<const f32x4*>(img);
@@ -189,7 +190,7 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_uf_gemm(Edges r, const floa
     for (int c = 0; c < K / 16; ++c)
       S[c] = ok ? *reinterpret_cast<const f32x4*>(xr + 16 * c) : f32x4{};
     f32x4 out[N / 16];
-    gemm_om<K, N, BF16>(out, S, lds, lane);
+    gemm_om<K, N, PR>(out, S, lds, lane);
     if (ok) {
       float* yr = Y + row * N + 4 * g;
 #pragma unroll
@@ -374,58 +375,46 @@ __global__ __launch_bounds__(kThreads) void k_uf_fill(float* p, int64_t n, float
 }
 
 // ------------------------------------------------------------------ host side
-// Image of the K x N matrix m(k, n) (zero for k >= Kin or n >= Nin) as the
-// products read it: output-major rows of K elements (fp32: sw4 chunks;
-// bf16: sw8 chunks at perm32 positions).
-template <int K>
-void om_image(int N, bool bf16, int Kin, int Nin, const std::function<float(int, int)>& m,
-              unsigned char* out) {
-  if (bf16) {
-    uint16_t* o = reinterpret_cast<uint16_t*>(out);
-    for (int n = 0; n < N; ++n)
-      for (int k = 0; k < K; ++k)
-        o[sw8<K>(n, perm32(k))] = bf16_rne_bits((k < Kin && n < Nin) ? m(k, n) : 0.f);
-  } else {
-    float* o = reinterpret_cast<float*>(out);
-    for (int n = 0; n < N; ++n)
-      for (int k = 0; k < K; ++k) o[sw4<K>(n, k)] = (k < Kin && n < Nin) ? m(k, n) : 0.f;
-  }
-}
-
-void om_image_k(int K, int N, bool bf16, int Kin, int Nin,
+void om_image_k(int K, int N, int bf16, int Kin, int Nin,
                 const std::function<float(int, int)>& m, unsigned char* out) {
+  auto go = [&](auto kk) {
+    constexpr int KK = decltype(kk)::value;
+    if (bf16) om_image<KK, PREC_BF16>(N, Kin, Nin, m, out, nullptr);
+    else om_image<KK, PREC_F32>(N, Kin, Nin, m, out, nullptr);
+  };
   switch (K) {
-    case 32: om_image<32>(N, bf16, Kin, Nin, m, out); break;
-    case 64: om_image<64>(N, bf16, Kin, Nin, m, out); break;
-    default: om_image<128>(N, bf16, Kin, Nin, m, out); break;
+    case 32: go(std::integral_constant<int, 32>{}); break;
+    case 64: go(std::integral_constant<int, 64>{}); break;
+    default: go(std::integral_constant<int, 128>{}); break;
   }
 }
 
 size_t img_bytes(int K, int N, int bf16) { return (size_t)K * N * (bf16 ? 2 : 4); }
 
-template <int K, int N, bool BF16>
+template <int K, int N, int PR>
 hipError_t gemm_prepare() {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_uf_gemm<K, N, BF16>),
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_uf_gemm<K, N, PR>),
                              hipFuncAttributeMaxDynamicSharedMemorySize,
-                             (int)img_bytes(K, N, BF16));
+                             (int)img_bytes(K, N, PR != PREC_F32));
 }
 
-template <int K, int N, bool BF16>
+template <int K, int N, int PR>
 hipError_t gemm_launch(Edges r, const float* X, const void* img, const float* bias, float* Y,
                        int n_cu, hipStream_t s) {
-  hipLaunchKernelGGL((k_uf_gemm<K, N, BF16>), dim3(n_cu * kGemmBlocksPerCu),
-                     dim3(64 * kGemmWaves), img_bytes(K, N, BF16), s, r, X, img, bias, Y);
+  hipLaunchKernelGGL((k_uf_gemm<K, N, PR>), dim3(n_cu * kGemmBlocksPerCu),
+                     dim3(64 * kGemmWaves), img_bytes(K, N, PR != PREC_F32), s, r, X, img, bias,
+                     Y);
   return hipGetLastError();
 }
 
 // The (K, N) shapes of the four products: (KP, D), (D, D), (D, D), (D, KP).
-template <bool BF16>
+template <int PR>
 hipError_t gemm_dispatch(int K, int N, Edges r, const float* X, const void* img,
                          const float* bias, float* Y, int n_cu, hipStream_t s, bool prepare) {
 #define SN_UF_CASE(KK, NN)                                                 \
   if (K == KK && N == NN)                                                  \
-    return prepare ? gemm_prepare<KK, NN, BF16>()                          \
-                   : gemm_launch<KK, NN, BF16>(r, X, img, bias, Y, n_cu, s);
+    return prepare ? gemm_prepare<KK, NN, PR>()                            \
+                   : gemm_launch<KK, NN, PR>(r, X, img, bias, Y, n_cu, s);
   SN_UF_CASE(32, 64) SN_UF_CASE(32, 128) SN_UF_CASE(64, 64) SN_UF_CASE(64, 128)
   SN_UF_CASE(128, 128) SN_UF_CASE(64, 32) SN_UF_CASE(128, 32) SN_UF_CASE(128, 64)
 #undef SN_UF_CASE
@@ -434,8 +423,8 @@ hipError_t gemm_dispatch(int K, int N, Edges r, const float* X, const void* img,
 
 hipError_t gemm(int K, int N, int bf16, Edges r, const float* X, const void* img,
                 const float* bias, float* Y, int n_cu, hipStream_t s) {
-  return bf16 ? gemm_dispatch<true>(K, N, r, X, img, bias, Y, n_cu, s, false)
-              : gemm_dispatch<false>(K, N, r, X, img, bias, Y, n_cu, s, false);
+  return bf16 ? gemm_dispatch<PREC_BF16>(K, N, r, X, img, bias, Y, n_cu, s, false)
+              : gemm_dispatch<PREC_F32>(K, N, r, X, img, bias, Y, n_cu, s, false);
 }
 
 } // namespace
@@ -470,9 +459,10 @@ hipError_t uf_prepare(int D, int KP, int bf16) {
   for (auto& sh : shapes) {
     const Edges r{nullptr, 0, 0};
     const hipError_t e =
-        bf16 ? gemm_dispatch<true>(sh[0], sh[1], r, nullptr, nullptr, nullptr, nullptr, 0, 0, true)
-             : gemm_dispatch<false>(sh[0], sh[1], r, nullptr, nullptr, nullptr, nullptr, 0, 0,
-                                    true);
+        bf16 ? gemm_dispatch<PREC_BF16>(sh[0], sh[1], r, nullptr, nullptr, nullptr, nullptr, 0, 0,
+                                        true)
+             : gemm_dispatch<PREC_F32>(sh[0], sh[1], r, nullptr, nullptr, nullptr, nullptr, 0, 0,
+                                       true);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

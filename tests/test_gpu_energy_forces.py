@@ -36,10 +36,15 @@ def check(lib, cfg, pos, types, w, r_list=None, n_replicas=None, what=""):
     system = lib_system(lib, cfg.system, n_replicas)
     r_list = m.r_cut if r_list is None else r_list
     E, F, rp, col = run_gpu(lib, m, system, pos, types, w, r_list)
-    Eo, Fo = oracle.energy_forces(oracle_desc(m), w, pos, types, rp, col,
-                                  n_replicas=system.n_replicas, periodic=bool(system.periodic),
-                                  box=system.box)
-    re, rf = assert_energy_forces(E, F, Eo, Fo, bf16=m.filter_dtype == 1, what=what)
+    Eo, Fo, eps = oracle.energy_forces(oracle_desc(m), w, pos, types, rp, col,
+                                       n_replicas=system.n_replicas,
+                                       periodic=bool(system.periodic), box=system.box,
+                                       return_eps=True)
+    eps_sum = np.abs(eps).reshape(system.n_replicas, -1).sum(axis=1) if m.filter_dtype == 2 else None
+    re, rf = assert_energy_forces(E, F, Eo, Fo, bf16=m.filter_dtype != 0, what=what,
+                                  eps_abs_sum=eps_sum)
+    if eps_sum is not None:
+        print(f"{what}: E err / sum|eps| {np.max(np.abs(E - Eo) / eps_sum):.2e}")
     print(f"{what}: E rel {re:.2e}, F max/rms {rf:.2e}, edges {len(col)}")
     return E, F
 
@@ -110,6 +115,32 @@ def test_isolated_atoms_and_single_atom(gpu_lib):
 def test_bf16_filter(gpu_lib):
     cfg, pos, types, w = make_config("md1024", n_replicas=4)
     check(gpu_lib, cfg, pos, types, w, n_replicas=4, what="bf16 filter, 4 x 269")
+
+
+def _w16a16(cfg):
+    import dataclasses
+    return dataclasses.replace(cfg, model=dataclasses.replace(cfg.model, filter_dtype=2))
+
+
+@pytest.mark.parametrize("name,nrep", [("md1024", 4), ("cg32", None)])
+def test_w16a16_chains(gpu_lib, name, nrep):
+    """fp16 operands with per-channel scales in every MLP (D 128 / H 64 and
+    D 64 / H 32 shapes) against the oracle with the same quantized weights."""
+    cfg, pos, types, w = make_config(name, n_replicas=nrep, bias_scale=0.05)
+    check(gpu_lib, _w16a16(cfg), pos, types, w, n_replicas=nrep, what=f"W16A16 {name}")
+
+
+def test_w16a16_periodic_box(gpu_lib):
+    cfg = CONFIGS["bulk4k"]
+    rng = np.random.default_rng(3)
+    n, box = 389, 17.9
+    pos = rng.uniform(0, box, (n, 3)).astype(np.float32)
+    pos[pos >= np.float32(box)] = 0
+    types = rng.integers(0, 4, n).astype(np.int32)
+    w = make_weights(cfg.model, 5, bias_scale=0.05)
+    from gen.configs import Config, SystemSpec
+    c2 = Config("box389", SystemSpec("bulk", 1, n, True, box), cfg.model)
+    check(gpu_lib, _w16a16(c2), pos, types, w, what="W16A16 box389")
 
 
 def test_deterministic_and_batched_equals_single(gpu_lib):

@@ -43,7 +43,7 @@ def check(lib, cfg, pos, types, w, mode, r_list=None, n_replicas=None, what=""):
     Eo, Fo = oracle.energy_forces(oracle_desc(m), w, pos, types, rp, col,
                                   n_replicas=system.n_replicas, periodic=bool(system.periodic),
                                   box=system.box)
-    re, rf = assert_energy_forces(E, F, Eo, Fo, bf16=m.filter_dtype == 1, what=f"{what} {mode}")
+    re, rf = assert_energy_forces(E, F, Eo, Fo, bf16=m.filter_dtype != 0, what=f"{what} {mode}")
     print(f"{what} {mode}: E rel {re:.2e}, F max/rms {rf:.2e}, edges {len(col)}")
     return E, F
 
@@ -149,6 +149,28 @@ def test_capacity_overflow_reported(gpu_lib):
                                            cap=100)
         assert len(col) > 100
         assert status[0] == gpu_lib.SN_ERR_CAPACITY and status[1] == len(col)
+
+
+def test_w16a16_model_is_rejected(gpu_lib):
+    import dataclasses
+    import torch
+    cfg, pos, types, w = make_config("cg32", seed=0)
+    m = dataclasses.replace(cfg.model, filter_dtype=2)
+    desc = lib_desc(gpu_lib, m)
+    system = lib_system(gpu_lib, cfg.system)
+    model = gpu_lib.sn_model_create(desc, w)
+    try:
+        p, rowptr, col, ne, _ = gpu_neighbors(gpu_lib, system, pos, m.r_cut)
+        ws = gpu_lib.Workspace(gpu_lib.sn_unfused_workspace_size(desc, system, ne))
+        t = torch.from_numpy(types).cuda()
+        energy = torch.empty(1, dtype=torch.float32, device="cuda")
+        forces = torch.empty(p.numel(), dtype=torch.float32, device="cuda")
+        with pytest.raises(gpu_lib.SnError) as ex:
+            gpu_lib.sn_energy_forces_unfused(model, system, p, t, rowptr, col, ne, 0, energy,
+                                             forces, ws)
+        assert ex.value.status == gpu_lib.SN_ERR_UNSUPPORTED
+    finally:
+        gpu_lib.sn_model_destroy(model)
 
 
 def test_host_validation(gpu_lib):
