@@ -296,43 +296,42 @@ __device__ __forceinline__ void tile_put(float* Tb, int b, const f32x4& m, const
 // length hold zeros). Receivers cur .. cur + nfin - 1 end in this tile and are
 // written through out(i, total); the open receiver's partial sum is carried.
 // A segmented inclusive scan runs down the column (one FMA per row with a
-// wave-uniform keep factor that is 0 where a receiver's rows begin), is
-// written back over the column, and each receiver's total is then one read
-// at its last row; the summation order is the plain sequential one.
+// wave-uniform keep factor that is 0 where a receiver's rows begin); at the
+// last row of each finished receiver the running value is its total and is
+// written out (receivers without rows in the tile get 0). The summation order
+// is the plain sequential one.
 template <class Out>
 __device__ __forceinline__ void column_segments(const CfParams& p, float* Tb, int win, int cur,
                                                 int ib, int nfin, int ts, int len, bool open,
                                                 float& carry, int lane_, Out out) {
   const int lane = opaque(lane_);
-  uint32_t starts = 0;
-  for (int l = 0; l < nfin; ++l) {
-    const int b = seg_end(p, win, cur, ib, l) - ts;
-    if (b < kEdges) starts |= 1u << b;
-  }
-  float* col = Tb + lane * kEdges;
-  const int sw = (lane >> 1) & 3;
-  float run = carry;
-#pragma unroll
-  for (int u = 0; u < kEdges / 4; ++u) {
-    float* q = col + ((u ^ sw) << 2);
-    f32x4 t = *reinterpret_cast<const f32x4*>(q);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float keep = ((starts >> (4 * u + r)) & 1u) ? 0.f : 1.f;
-      run = fmaf(run, keep, t[r]);
-      t[r] = run;
-    }
-    *reinterpret_cast<f32x4*>(q) = t;
-  }
-  wave_sync();
+  uint32_t starts = 0, lasts = 0;
   int prev = 0;
   for (int l = 0; l < nfin; ++l) {
     const int b = seg_end(p, win, cur, ib, l) - ts;
-    const int r = b - 1;
-    const float tot = b > prev ? col[(((r >> 2) ^ sw) << 2) | (r & 3)] : 0.f;
-    out(cur + l, tot);
+    if (b < kEdges) starts |= 1u << b;
+    if (b > prev) lasts |= 1u << (b - 1);
     prev = b;
   }
+  const float* col = Tb + lane * kEdges;
+  const int sw = (lane >> 1) & 3;
+  float run = carry;
+  int l = 0;   // next finished receiver (wave-uniform)
+#pragma unroll
+  for (int u = 0; u < kEdges / 4; ++u) {
+    const f32x4 t = *reinterpret_cast<const f32x4*>(col + ((u ^ sw) << 2));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * u + r;
+      const float keep = ((starts >> row) & 1u) ? 0.f : 1.f;
+      run = fmaf(run, keep, t[r]);
+      if ((lasts >> row) & 1u) {
+        while (seg_end(p, win, cur, ib, l) - ts <= row) out(cur + l++, 0.f);   // no rows here
+        out(cur + l++, run);
+      }
+    }
+  }
+  for (; l < nfin; ++l) out(cur + l, 0.f);
   carry = (open && prev < len) ? run : 0.f;
 }
 
