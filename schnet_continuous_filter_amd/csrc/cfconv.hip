@@ -33,7 +33,11 @@
 // segmented scan down that column yields each receiver's sum. A receiver still
 // open at the tile's end carries its partial sum into the next tile. The
 // segment ends of the next 64 receivers come from one lane-parallel load per
-// tile. Nothing edge-sized reaches HBM and every output row has one writer.
+// tile. The three force components of the backward are summed the same way
+// but without the transpose: each edge's lane already holds them, and a
+// segmented scan along the 16-lane rows (row shifts of the cross-lane data
+// path) leaves each receiver's total at its last edge's lane. Nothing
+// edge-sized reaches HBM and every output row has one writer.
 //
 // Backward (forces). The neighbour list is symmetric and w_ij = w_ji, so the
 // owner of receiver i produces, from its own row alone,
@@ -275,6 +279,20 @@ __device__ __forceinline__ int tpos(int col, int row) {
 __host__ __device__ __forceinline__ int col_feature(int L) {
   return 16 * (L >> 4) + 4 * (L & 3) + ((L >> 2) & 3);
 }
+// v of the lane k places lower in the same 16-lane row (0 for the row's
+// first k lanes).
+__device__ __forceinline__ float row_shr(float v, int k) {
+  const int x = __builtin_bit_cast(int, v);
+  int y;
+  switch (k) {
+    case 1: y = __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false); break;
+    case 2: y = __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false); break;
+    case 4: y = __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false); break;
+    default: y = __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false); break;
+  }
+  return __builtin_bit_cast(float, y);
+}
+
 // Element offsets, in the transpose tile, of this lane's accumulator
 // elements r = 0..3 of block 0; block b adds 256 b (tpos(16 b + c, row) =
 // 256 b + tpos(c, row) for c < 16). Built once per tile.
@@ -501,7 +519,7 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, true>()), 1) void k_cf_bwd(CfPar
   float carry[NB / 4];
 #pragma unroll
   for (int pss = 0; pss < NB / 4; ++pss) carry[pss] = 0.f;
-  float fcarry = 0.f;   // lanes 0..2: open receiver's force component
+  float fcarry[3] = {0.f, 0.f, 0.f};   // open receiver's dE/dr so far
   int cur = wk.ia;
   int win = load_window(wk.rrow, cur, ib, lane);
   int jn = bload_i(wk.rcol, (uint32_t)(wk.E0 + e) * 4u);
@@ -562,11 +580,23 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, true>()), 1) void k_cf_bwd(CfPar
     for (int b = 0; b < 4; ++b) gather(b, G[b]);
     __builtin_amdgcn_sched_barrier(0);
 
-    // GEMM2 for the tangents, all blocks (frees s'): w' = s' Wf2; the values
-    // w = s Wf2 follow one output block at a time
-    f32x4 wt[NB];
-    gemm_om<D, D, PR>(wt, av[1], lds + P::W2, wl);
+    // GEMM2: the tangents of all blocks, w' = s' Wf2, and the values w = s Wf2
+    // of the first 64 features, as independent product chains; the values of
+    // each further 64 features are formed once the previous ones are used
     const Operand<D, PR> os(av[0]);
+    f32x4 wt[NB], wv[4];
+    {
+      const Operand<D, PR> ot(av[1]);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        wt[nb] = f32x4{};
+        gemm_om_block<D, PR>(wt[nb], ot, lds + P::W2, nb, wl);
+        if (nb < 4) {
+          wv[nb] = f32x4{};
+          gemm_om_block<D, PR>(wv[nb], os, lds + P::W2, nb, wl);
+        }
+      }
+    }
 
     // per 64 features: q = dE/dh_j w summed per receiver;
     // dE/dd += <dE/dh_i x_j + dE/dh_j x_i, w'>. A block's gather registers
@@ -577,26 +607,28 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, true>()), 1) void k_cf_bwd(CfPar
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int nb = 4 * pss + b;
-        __builtin_amdgcn_sched_barrier(0);
-        f32x4 wv = f32x4{};
-        gemm_om_block<D, PR>(wv, os, lds + P::W2, nb, wl);
         const f32x4 xj = G[b][0], gj = G[b][1], xi = G[b][2], gi = G[b][3];
         const f32x4 c2 = bias4<P>(p, lds, g4, D + 16 * nb);
         if constexpr (PR == PREC_F16S) {
           const f32x4 s2 = scale4<P>(p, lds, g4, D + 16 * nb);
-          wv *= s2;
+          wv[b] *= s2;
           wt[nb] *= s2;
         }
         f32x4 qv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          qv[r] = gj[r] * (g.in * (wv[r] + c2[r]));
+          qv[r] = gj[r] * (g.in * (wv[b][r] + c2[r]));
           gdd = fmaf(gi[r] * xj[r] + gj[r] * xi[r], wt[nb][r], gdd);
         }
         if (want_q) tile_put(Tb, b, qv, tl);
-        if (pss + 1 < NB / 4) {
-          gather(nb + 4, G[b]);
-          __builtin_amdgcn_sched_barrier(0);
+        if (pss + 1 < NB / 4) gather(nb + 4, G[b]);
+      }
+      if (pss + 1 < NB / 4) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          wv[b] = f32x4{};
+          gemm_om_block<D, PR>(wv[b], os, lds + P::W2, 4 * (pss + 1) + b, wl);
         }
       }
       if (want_q) {
@@ -611,19 +643,43 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, true>()), 1) void k_cf_bwd(CfPar
     gdd += __shfl_xor(gdd, 32, 64);
     const float gd = gdd * g.invd * g.in;
 
-    // this block's dE/dr rows: the edge contributions gd u as three columns of
-    // the tile, summed per receiver like the features
-    if (lane < 16) {
-      Tb[tpos(0, e)] = gd * g.ux;
-      Tb[tpos(1, e)] = gd * g.uy;
-      Tb[tpos(2, e)] = gd * g.uz;
+    // this block's dE/dr rows: the edge contributions gd u summed per receiver
+    // by a segmented scan along the tile's 16 rows (one edge per lane of a
+    // 16-lane row); the lane at a finished receiver's last row holds its total
+    {
+      uint32_t starts = 0, lasts = 0;
+      int prev = 0;
+      for (int l = 0; l < th.nfin; ++l) {
+        const int b = seg_end(p, win, cur, ib, l) - ts;
+        if (b < kEdges) starts |= 1u << b;
+        if (b > prev) lasts |= 1u << (b - 1);
+        else if (lane < 3) p.forces[(size_t)(cur + l) * 3 + lane] = 0.f;   // no edges
+        prev = b;
+      }
+      float f[3] = {gd * g.ux, gd * g.uy, gd * g.uz};
+      if (e == 0) {
+#pragma unroll
+        for (int c = 0; c < 3; ++c) f[c] += fcarry[c];
+      }
+      const uint32_t sm = starts & ((2u << e) - 1u);          // receiver starts at rows <= e
+      const int dist = e - (sm ? 31 - __builtin_clz(sm) : 0);  // rows of this receiver before e
+#pragma unroll
+      for (int k = 1; k < kEdges; k <<= 1) {
+        const float keep = dist >= k ? 1.f : 0.f;
+#pragma unroll
+        for (int c = 0; c < 3; ++c) f[c] = fmaf(row_shr(f[c], k), keep, f[c]);
+      }
+      if (lane < kEdges && ((lasts >> e) & 1u)) {
+#pragma unroll
+        for (int c = 0; c < 3; ++c) p.forces[(size_t)th.recv * 3 + c] = f[c];
+      }
+      const bool open = th.ncur < ib && prev < th.len;
+#pragma unroll
+      for (int c = 0; c < 3; ++c)
+        fcarry[c] = open ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                        __builtin_bit_cast(int, f[c]), th.len - 1))
+                         : 0.f;
     }
-    wave_sync();
-    column_segments(p, Tb, win, cur, ib, th.nfin, ts, th.len, th.ncur < ib, fcarry, lane,
-                    [&](int i, float tot) {
-                      if (lane < 3) p.forces[(size_t)i * 3 + lane] = tot;
-                    });
-    wave_sync();
     cur = th.ncur;
     win = th.win_next;
   }

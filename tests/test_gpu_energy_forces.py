@@ -101,6 +101,39 @@ def test_small_periodic_box_ragged(gpu_lib):
     check(gpu_lib, c2, pos, types, w, what="box389")
 
 
+def sparse_clusters(n_iso=100, seed=11):
+    """Clusters of 10 atoms (index-contiguous, 4 A apart on a helix) separated
+    in index order by runs of isolated atoms 50 A apart: one 16-edge tile
+    then spans receivers more than 64 apart, most of them without edges."""
+    rng = np.random.default_rng(seed)
+    pos, types = [], []
+    for c in range(4):
+        base = np.array([0.0, 0.0, 400.0 * c])
+        for k in range(10):
+            ang = 1.7 * k
+            pos.append(base + [3.0 * np.cos(ang), 3.0 * np.sin(ang), 1.5 * k])
+            types.append(0)
+        for k in range(n_iso if c < 3 else 7):
+            pos.append(base + [60.0 + 50.0 * k, 0.0, 0.0])
+            types.append(0)
+    pos = np.asarray(pos, np.float32) + rng.normal(0, 0.05, (len(pos), 3)).astype(np.float32)
+    return pos, np.asarray(types, np.int32)
+
+
+def test_sparse_receivers_beyond_the_window(gpu_lib):
+    """1200 replicas of the sparse pattern: every worker owns ~100 receivers
+    or more, so tiles cross runs of >64 edgeless receivers (the segment-end
+    window's fallback path)."""
+    from gen.configs import Config, SystemSpec
+    cfg = CONFIGS["cg32"]
+    pos, types = sparse_clusters()
+    R = 1200
+    w = make_weights(cfg.model, 2, bias_scale=0.05)
+    c2 = Config("sparse", SystemSpec("chain_walk", R, len(pos), False), cfg.model)
+    check(gpu_lib, c2, np.tile(pos, (R, 1)), np.tile(types, R), w, n_replicas=R,
+          what="sparse clusters x1200")
+
+
 def test_isolated_atoms_and_single_atom(gpu_lib):
     cfg = CONFIGS["cg32"]
     w = make_weights(cfg.model, 0, bias_scale=0.1)

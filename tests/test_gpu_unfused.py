@@ -108,6 +108,16 @@ def test_bulk4k_full(gpu_lib, mode):
     check(gpu_lib, cfg, pos, types, w, mode, what="bulk4k")
 
 
+def test_sparse_receivers(gpu_lib):
+    from tests.test_gpu_energy_forces import sparse_clusters
+    cfg = CONFIGS["cg32"]
+    pos, types = sparse_clusters()
+    w = make_weights(cfg.model, 2, bias_scale=0.05)
+    c2 = Config("sparse", SystemSpec("chain_walk", 1, len(pos), False), cfg.model)
+    for mode in MODES:
+        check(gpu_lib, c2, pos, types, w, mode, what="sparse clusters")
+
+
 def test_isolated_atoms(gpu_lib):
     """No edges at all: every edge tensor is empty and the forces vanish."""
     cfg = CONFIGS["cg32"]
