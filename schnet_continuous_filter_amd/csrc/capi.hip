@@ -184,6 +184,13 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
   p.rbf_step = step;
   p.rbf_coef2 = (float)(-0.5 / ((double)step * step) * 1.4426950408889634);
   p.rbf_inv_s2 = 1.f / (step * step);
+  {
+    // sigma = step: g_{k+1} / g_k = exp((z_k step - step^2 / 2) / sigma^2)
+    const double st = step, is2 = 1.0 / ((double)step * step), l2e = 1.4426950408889634;
+    p.rbf_qa = (float)(l2e * st * is2);
+    p.rbf_qb = (float)(-0.5 * l2e * st * st * is2);
+    p.rbf_r = (float)std::exp(-st * st * is2);
+  }
   p.r_cut = d.r_cut;
   p.pi_over_rc = (float)(M_PI / (double)d.r_cut);
   p.half_over_rc = (float)(0.5 / (double)d.r_cut);

@@ -209,13 +209,35 @@ __device__ __forceinline__ void gemm1(f32x4 (&acc)[NA][D / 16], const unsigned c
 #pragma unroll 1
   for (int c = 0; c < p.KC; ++c) {
     float b[NA][PL];
+    if constexpr (H16) {
+      // the lane's 8 consecutive centres: one exp for the first Gaussian and
+      // one for the ratio of neighbours, g_{k+1} = g_k q_k with q_{k+1} = q_k r
+      // (centres one step apart), and the tangent factor
+      // C' - (d - mu_k) C / sigma^2, which grows by step C / sigma^2 per k
+      const float z = __builtin_fmaf(-(float)(k0 + CH * c), step, g.d0);
+      float gk = g.in * __builtin_amdgcn_exp2f(coef2 * z * z);
+      float q = __builtin_amdgcn_exp2f(__builtin_fmaf(p.rbf_qa, z, p.rbf_qb));
+      float tk = g.Cp - z * inv_s2 * g.C;
+      const float dt = step * inv_s2 * g.C;
 #pragma unroll
-    for (int t = 0; t < PL; ++t) {
-      // d - mu_k with one rounding (the product k step is exact inside the fma)
-      const float z = __builtin_fmaf(-(float)(k0 + CH * c + t), step, g.d0);
-      const float gs = g.in * __builtin_amdgcn_exp2f(coef2 * z * z);
-      b[0][t] = gs * g.C;
-      if constexpr (NA == 2) b[1][t] = gs * (g.Cp - z * inv_s2 * g.C);
+      for (int t = 0; t < PL; ++t) {
+        b[0][t] = gk * g.C;
+        if constexpr (NA == 2) {
+          b[1][t] = gk * tk;
+          tk += dt;
+        }
+        gk *= q;
+        q *= p.rbf_r;
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < PL; ++t) {
+        // d - mu_k with one rounding (the product k step is exact inside the fma)
+        const float z = __builtin_fmaf(-(float)(k0 + CH * c + t), step, g.d0);
+        const float gs = g.in * __builtin_amdgcn_exp2f(coef2 * z * z);
+        b[0][t] = gs * g.C;
+        if constexpr (NA == 2) b[1][t] = gs * (g.Cp - z * inv_s2 * g.C);
+      }
     }
     if constexpr (H16) {
       using E = typename PrecT<PR>::E;

@@ -104,6 +104,9 @@ struct CfParams {
   int periodic;
   float box, half_box;
   float rbf_min, rbf_step, rbf_coef2, rbf_inv_s2; // coef2 = -log2(e)/(2 sigma^2), inv_s2 = 1/sigma^2
+  // neighbouring Gaussians: g_{k+1} / g_k = 2^(qa z_k + qb) with z_k = d - mu_k,
+  // and that ratio shrinks by the factor r from one k to the next
+  float rbf_qa, rbf_qb, rbf_r;
   float r_cut, pi_over_rc, half_over_rc;   // half_over_rc = 1 / (2 r_cut)
   int KC;             // basis chunks the first filter product runs over (cf_chunks)
   const void* img;    // this block's filter weights and biases as laid out in LDS (cf_fill_image)
