@@ -162,9 +162,9 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
   hipError_t e;
 
   if (!uf) {
-    if ((e = launch_partition(rowptr, (int)n, Gf * wf, wg_start, s)) != hipSuccess)
+    if ((e = launch_partition(rowptr, (int)n, Gf * wf, wg_start, st, s)) != hipSuccess)
       return hip_fail(e);
-    if ((e = launch_partition(rowptr, (int)n, Gb * wb, wg_start_b, s)) != hipSuccess)
+    if ((e = launch_partition(rowptr, (int)n, Gb * wb, wg_start_b, st, s)) != hipSuccess)
       return hip_fail(e);
   }
   if ((e = launch_embed(types, m->w + m->off_emb, (int)n, D, d.n_types, x, st, s)) != hipSuccess)

@@ -716,10 +716,18 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, true>()), 1) void k_cf_bwd(CfPar
 // ------------------------------------------------------------------ small kernels
 // Worker w owns receivers [wg_start[w], wg_start[w+1]); boundaries split the
 // monotone key rowptr[i] + i (edges plus one unit per receiver) evenly.
-__global__ void k_partition(const int32_t* rowptr, int N, int G, int32_t* wg_start) {
+// The kernels address the edge list with 32-bit byte offsets: a list of
+// kMaxListEdges or more edges is refused through the status word.
+constexpr int64_t kMaxListEdges = (int64_t)1 << 30;
+__global__ void k_partition(const int32_t* rowptr, int N, int G, int32_t* wg_start,
+                            DevStatus* st) {
   const int w = blockIdx.x * blockDim.x + threadIdx.x;
   if (w > G) return;
-  if (w == 0) { wg_start[0] = 0; return; }
+  if (w == 0) {
+    if ((int64_t)rowptr[N] >= kMaxListEdges) dev_fail(st, SN_ERR_UNSUPPORTED, rowptr[N]);
+    wg_start[0] = 0;
+    return;
+  }
   if (w == G) { wg_start[G] = N; return; }
   const int64_t total = (int64_t)rowptr[N] + N;
   const int64_t target = (total * w + G - 1) / G;
@@ -733,9 +741,9 @@ __global__ void k_partition(const int32_t* rowptr, int N, int G, int32_t* wg_sta
 }
 
 hipError_t launch_partition(const int32_t* rowptr, int n_atoms, int G, int32_t* wg_start,
-                            hipStream_t s) {
+                            DevStatus* st, hipStream_t s) {
   hipLaunchKernelGGL(k_partition, dim3((G + 1 + kThreads - 1) / kThreads), dim3(kThreads), 0, s,
-                     rowptr, n_atoms, G, wg_start);
+                     rowptr, n_atoms, G, wg_start, st);
   return hipGetLastError();
 }
 

@@ -129,7 +129,7 @@ void cf_fill_image(int D, int KP, int prec, int Dr, const float* Wf1, const floa
                    const float* Wf2, const float* cf2, unsigned char* out);
 hipError_t launch_force_sum(const float* fb, int T, int64_t n_atoms, float* forces, hipStream_t s);
 hipError_t launch_partition(const int32_t* rowptr, int n_atoms, int G, int32_t* wg_start,
-                            hipStream_t s);
+                            DevStatus* st, hipStream_t s);
 hipError_t launch_cf_forward(int D, int KP, int prec, const CfParams& p, int G, hipStream_t s);
 hipError_t launch_cf_backward(int D, int KP, int prec, const CfParams& p, int G, hipStream_t s);
 
