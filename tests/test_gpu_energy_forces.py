@@ -155,6 +155,31 @@ def _w16a16(cfg):
     return dataclasses.replace(cfg, model=dataclasses.replace(cfg.model, filter_dtype=2))
 
 
+@pytest.mark.parametrize("dtype", [1, 2])
+def test_16bit_small_model(gpu_lib, dtype):
+    """The D 64 / Dr 32 / H 32 model with a bf16 filter (one 32-wide basis
+    chunk) or W16A16, on a chain with biases."""
+    import dataclasses
+    cfg, pos, types, w = make_config("cg32", seed=3, bias_scale=0.05)
+    c2 = dataclasses.replace(cfg, model=dataclasses.replace(cfg.model, filter_dtype=dtype))
+    check(gpu_lib, c2, pos, types, w, what=f"cg32 filter_dtype {dtype}")
+
+
+def test_bf16_periodic_box(gpu_lib):
+    import dataclasses
+    cfg = CONFIGS["bulk4k"]
+    rng = np.random.default_rng(4)
+    n, box = 389, 17.9
+    pos = rng.uniform(0, box, (n, 3)).astype(np.float32)
+    pos[pos >= np.float32(box)] = 0
+    types = rng.integers(0, 4, n).astype(np.int32)
+    w = make_weights(cfg.model, 6, bias_scale=0.05)
+    from gen.configs import Config, SystemSpec
+    c2 = Config("box389", SystemSpec("bulk", 1, n, True, box),
+                dataclasses.replace(cfg.model, filter_dtype=1))
+    check(gpu_lib, c2, pos, types, w, what="bf16 box389")
+
+
 @pytest.mark.parametrize("name,nrep", [("md1024", 4), ("cg32", None)])
 def test_w16a16_chains(gpu_lib, name, nrep):
     """fp16 operands with per-channel scales in every MLP (D 128 / H 64 and
