@@ -29,7 +29,7 @@ from schnet_continuous_filter_amd import profiling  # noqa: E402  (no GPU work a
 PEAK_FP32_MFMA_TFLOPS = 157.3     # MI355X dense fp32 matrix peak
 PEAK_BF16_MFMA_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
-PREC_TAGS = {0: "f32", 1: "bf16", 2: "w16a16"}
+PREC_TAGS = {0: "f32", 1: "bf16", 2: "w16a16", 3: "f16x2"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cfconv_bwd_cg269x64_counters.txt")
 
 
@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--workload", default="cg269x64",
                     choices=["cg269x64", "cg32", "bulk4k", "bulk64k", "md1024"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--precision", choices=["f32", "bf16", "w16a16"], default=None,
+    ap.add_argument("--precision", choices=["f32", "bf16", "w16a16", "f16x2"], default=None,
                     help="override the workload's network operand precision")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -160,13 +160,13 @@ def ablation(args):
 
     variants = {}
     energies = {}
-    dtypes = [m.filter_dtype] + [fd for fd in (0, 1, 2) if fd != m.filter_dtype]
+    dtypes = [m.filter_dtype] + [fd for fd in (0, 1, 2, 3) if fd != m.filter_dtype]
     for fd in dtypes:
         tag = PREC_TAGS[fd]
         desc = L.make_desc(m.n_types, m.D, m.Dr, m.T, m.H, m.rbf_min, m.rbf_max, m.r_cut, fd)
         model = L.sn_model_create(desc, w)
         runs = [("fused", L.sn_workspace_size(desc, system), None)]
-        if fd == m.filter_dtype:
+        if fd == m.filter_dtype and fd in (0, 1):
             ub = L.sn_unfused_workspace_size(desc, system, ne)
             runs += [("unfused_segmented", ub, 0), ("unfused_atomic", ub, L.SN_UNFUSED_ATOMIC)]
         for name, nbytes, flags in runs:
@@ -209,6 +209,7 @@ def ablation(args):
             "fused vs unfused_atomic": ms["unfused_atomic" + base] / ms["fused" + base],
             "bf16 vs f32 filter (fused)": ms["fused_f32"] / ms["fused_bf16"],
             "w16a16 vs f32 (fused)": ms["fused_f32"] / ms["fused_w16a16"],
+            "f16x2 vs f32 (fused)": ms["fused_f32"] / ms["fused_f16x2"],
         },
     }
     print(json.dumps(line))
@@ -437,7 +438,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {0: "f32", 1: "bf16-filter/f32", 2: "f16-mlps/f32"}[m.filter_dtype],
+        "dtype": {0: "f32", 1: "bf16-filter/f32", 2: "f16-mlps/f32",
+                  3: "f16x2-filter/f32"}[m.filter_dtype],
         "data": "synthetic (seeded chains/boxes, random-init weights)",
         "config": {"workload": cfg.name, "replicas": R, "atoms_per_replica": N,
                    "directed_edges": ne, "list_radius_A": r_list, "D": m.D, "Dr": m.Dr, "T": m.T,

@@ -23,6 +23,7 @@ from .systems import bulk_uniform, chain_walk, model_weights, self_avoiding_chai
 FILTER_F32 = 0
 FILTER_BF16 = 1
 W16A16 = 2
+FILTER_F16X2 = 3
 
 
 @dataclass(frozen=True)

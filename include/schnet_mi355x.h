@@ -61,10 +61,21 @@ typedef enum {
  *                  quantization"): each weight column n is stored as
  *                  fp16(W[:, n] / s_n) with s_n the power of two at or above
  *                  the column's largest magnitude (1 for a zero column), and
- *                  the readout's output weights likewise as one column.
+ *                  the readout's output weights likewise as one column;
+ *  SN_FILTER_F16X2 the filter network keeps fp32 weights and activations,
+ *                  each entering its products as a pair of fp16 numbers
+ *                  hi + lo (22 significant bits; whole matrices and
+ *                  activation vectors are first scaled by powers of two,
+ *                  derived on the host from the weights and the basis
+ *                  width, so that both parts stay in fp16's normal range),
+ *                  and each product is hi*hi + hi*lo + lo*hi on the fp16
+ *                  matrix units: about 1e-6 relative error per dot product,
+ *                  inside the fp32 tolerances; the other layers stay fp32.
+ *                  The energy+force calls accept it; the unfused pipeline
+ *                  returns SN_ERR_UNSUPPORTED.
  * Accumulation is fp32 in every case; positions, distances, basis
  * functions, biases, energies and forces stay fp32. */
-enum { SN_FILTER_F32 = 0, SN_FILTER_BF16 = 1, SN_W16A16 = 2 };
+enum { SN_FILTER_F32 = 0, SN_FILTER_BF16 = 1, SN_W16A16 = 2, SN_FILTER_F16X2 = 3 };
 
 /* Model shape. Supported: D in {64, 128}; 2 <= Dr <= 64; 1 <= T <= 8;
  * H in {32, 64} with H <= D; n_types >= 1; 0 <= rbf_min < rbf_max;
@@ -171,8 +182,8 @@ sn_status sn_energy_forces(const sn_model* model, const sn_system* sys, const fl
  * tensor has that many rows. A larger list sets the device status to
  * SN_ERR_CAPACITY and leaves the outputs invalid. Other arguments as for
  * sn_energy_forces; the list must come from sn_build_neighbors (symmetric,
- * senders ascending). Models with filter_dtype SN_W16A16 return
- * SN_ERR_UNSUPPORTED. */
+ * senders ascending). Models with filter_dtype SN_W16A16 or SN_FILTER_F16X2
+ * return SN_ERR_UNSUPPORTED. */
 enum { SN_UNFUSED_ATOMIC = 1 };
 
 /* Workspace bytes for sn_energy_forces_unfused: the sn_workspace_size amount

@@ -36,6 +36,9 @@ LN2 = np.log(2.0)
 FILTER_F32 = 0
 FILTER_BF16 = 1
 W16A16 = 2
+# fp32 filter whose products the kernels evaluate on fp16 hi/lo pairs: the
+# model itself is the fp32 one, so the oracle treats it as FILTER_F32
+FILTER_F16X2 = 3
 
 
 @dataclass(frozen=True)
@@ -86,7 +89,8 @@ def unpack_weights(desc: ModelDesc, flat) -> dict:
     co2[1]. With a bf16 filter network the two filter weight matrices of every
     block are first rounded to bfloat16 (their biases stay fp32); with
     W16A16 every MLP weight (Wf1, Wf2, Wu1, Wu2, Wo1, Wo2) goes through
-    f16_channel_quantize (biases and the embedding stay fp32)."""
+    f16_channel_quantize (biases and the embedding stay fp32). FILTER_F32 and
+    FILTER_F16X2 use the weights as given."""
     flat = np.asarray(flat, dtype=np.float32)
     D, Dr, H = desc.D, desc.Dr, desc.H
     off = 0

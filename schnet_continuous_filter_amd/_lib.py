@@ -24,6 +24,7 @@ SN_ERR_WORKSPACE = 6
 SN_FILTER_F32 = 0
 SN_FILTER_BF16 = 1
 SN_W16A16 = 2
+SN_FILTER_F16X2 = 3
 SN_UNFUSED_ATOMIC = 1
 
 c_int32, c_int64, c_uint64, c_float, c_double = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,

@@ -39,7 +39,7 @@ bool desc_ok(const sn_model_desc* d) {
          std::isfinite(d->rbf_max) && d->rbf_min >= 0.f && d->rbf_max > d->rbf_min &&
          std::isfinite(d->r_cut) && d->r_cut > 0.f &&
          (d->filter_dtype == SN_FILTER_F32 || d->filter_dtype == SN_FILTER_BF16 ||
-          d->filter_dtype == SN_W16A16);
+          d->filter_dtype == SN_W16A16 || d->filter_dtype == SN_FILTER_F16X2);
 }
 
 size_t block_floats(const sn_model_desc* d) {
@@ -479,7 +479,8 @@ sn_status sn_model_create(const sn_model_desc* d, const float* weights_host, siz
       const float* cf1 = Wf1 + (size_t)d->Dr * D;
       const float* Wf2 = cf1 + D;
       const float* cf2 = Wf2 + D * D;
-      cf_fill_image(d->D, m->KP, prec, d->Dr, Wf1, cf1, Wf2, cf2, hi.data() + t * per);
+      cf_fill_image(d->D, m->KP, prec, d->Dr, Wf1, cf1, Wf2, cf2,
+                    (d->rbf_max - d->rbf_min) / (float)(d->Dr - 1), d->r_cut, hi.data() + t * per);
     }
     e = (per == 0) ? hipErrorInvalidValue : hipMalloc(&m->cfimg, hi.size());
     if (e == hipSuccess) e = hipMemcpy(m->cfimg, hi.data(), hi.size(), hipMemcpyHostToDevice);
@@ -601,7 +602,8 @@ sn_status sn_energy_forces_unfused(const sn_model* m, const sn_system* sys, cons
     return SN_ERR_INVALID_ARG;
   if (edge_capacity < 1 || edge_capacity > INT32_MAX) return SN_ERR_INVALID_ARG;
   if ((flags & ~SN_UNFUSED_ATOMIC) != 0) return SN_ERR_INVALID_ARG;
-  if (m->desc.filter_dtype == SN_W16A16) return SN_ERR_UNSUPPORTED;
+  if (m->desc.filter_dtype == SN_W16A16 || m->desc.filter_dtype == SN_FILTER_F16X2)
+    return SN_ERR_UNSUPPORTED;
   size_t need = 0;
   sn_status rc = sn_unfused_workspace_size(&m->desc, sys, edge_capacity, &need);
   if (rc != SN_OK) return rc;

@@ -57,7 +57,9 @@
 // (bfloat16 filters) or v_mfma_f32_16x16x32_f16 (fp16 filters whose weight
 // columns carry power-of-two scales, §4.4 "Channel-wise quantization"), fp32
 // accumulation throughout.
+#include <algorithm>
 #include <climits>
+#include <cmath>
 #include <cstring>
 
 #include "tile16.hpp"
@@ -74,22 +76,28 @@ __device__ __forceinline__ float min_image(float u, float box, float half) {
 
 // ------------------------------------------------------------------ LDS plan
 // Weight image (built on the host, copied verbatim) then one transpose tile per wave.
-//   W1  : Wf1^T [D][KP] (k zero-padded past Dr)
-//   W2  : Wf2^T [D][D] (16-bit: positions permuted by perm32)
+//   W1  : Wf1^T [D][KP] (k zero-padded past Dr); fp16 pairs: the hi image,
+//         then the lo image (W1L)
+//   W2  : Wf2^T [D][D] (16-bit: positions permuted by perm32); fp16 pairs:
+//         hi, then lo (W2L)
 //   BIAS: cf1[D], cf2[D] (fp32); then, for fp16 filters, the column scales
-//         s1[D], s2[D]; staged only where LDS has room, else read from the
-//         image in global memory
+//         s1[D], s2[D], or for fp16 pairs the split scales (SplitScales);
+//         staged only where LDS has room, else read from the image in
+//         global memory
 // Rows are output-major: the A operand of a lane is a run of its row.
 template <int D, int KP, int PR, int NW_>
 struct Plan {
   static constexpr int NW = NW_;               // workers (waves) per work-group
   static constexpr int NT = NW * 64;
   static constexpr int ES = PR != PREC_F32 ? 2 : 4;
+  static constexpr int NS = PR == PREC_F16X2 ? 2 : 1;   // images per matrix
   static constexpr int W1 = 0;
-  static constexpr int W2 = W1 + D * KP * ES;
-  static constexpr int BIAS = W2 + D * D * ES;
+  static constexpr int W1L = W1 + D * KP * ES;
+  static constexpr int W2 = W1 + NS * D * KP * ES;
+  static constexpr int W2L = W2 + D * D * ES;
+  static constexpr int BIAS = W2 + NS * D * D * ES;
   static constexpr int SC = BIAS + 2 * D * 4;
-  static constexpr int IMG = SC + (PR == PREC_F16S ? 2 * D * 4 : 0);
+  static constexpr int IMG = SC + (PR == PREC_F16S ? 2 * D * 4 : PR == PREC_F16X2 ? 32 : 0);
   static constexpr int TB = kEdges * 64 * 4;   // transpose tile: 64 columns of 16 rows
   static constexpr int LDS_MAX = 160 * 1024;
   static constexpr bool BIAS_LDS = IMG + NW * TB <= LDS_MAX;
@@ -113,18 +121,92 @@ int cf_kp(int Dr, int prec) {
 }
 int cf_chunks(int Dr, int prec) { return prec != PREC_F32 ? (Dr + 31) / 32 : (Dr + 7) / 8; }
 
+// Scales of the fp16-pair filter (8 floats at Plan::SC). Product q's input
+// is multiplied by a[q] before it is split, its weights by a power of two
+// sw, and its output by u[q] = 1 / (sw a[q]); q = 0: basis into Wf1, 1: basis
+// derivative into Wf1, 2: softplus output into Wf2, 3: its tangent into Wf2.
+struct SplitScales {
+  float a[4], u[4];
+};
+
+// v = m 2^e with m in [0.5, 1): e (0 for v = 0)
+static int binade(double v) {
+  int e = 0;
+  if (v > 0) std::frexp(v, &e);
+  return e;
+}
+
+// fp16-pair images and scales. Each matrix is scaled by the power of two
+// that puts its largest magnitude in [2^13, 2^14), then stored as fp16 hi
+// and lo images. The product inputs get powers of two that map a bound of
+// their magnitude into [2^12, 2^13), far inside fp16's range (65504):
+//   basis          b~_k = g_k C <= 1
+//   its derivative |d b~_k/dd| <= e^(-1/2) / sigma + pi / (2 r_c)   (=: B1;
+//                  the Gaussian's slope peaks at d - mu_k = sigma, and
+//                  |C'| <= pi / (2 r_c), |C|, g_k <= 1)
+//   softplus out   |ssp(a_n)| <= max(|a_n|, ln 2), |a_n| <= A_n + |cf1_n|
+//                  with A_n = sum_k |Wf1[k][n]| (the basis is in [0, 1])
+//   its tangent    |sigmoid(a_n) a'_n| <= A_n B1
+// Exponents are clamped so that every scale and u stays a normal float.
+template <int D, int KP>
+static void fill_split(int Dr, const float* Wf1, const float* cf1, const float* Wf2,
+                       float rbf_step, float r_cut, unsigned char* w1h, unsigned char* w1l,
+                       unsigned char* w2h, unsigned char* w2l, SplitScales& sc) {
+  auto w1 = [&](int k, int n) { return Wf1[(size_t)k * D + n]; };
+  auto w2 = [&](int k, int n) { return Wf2[(size_t)k * D + n]; };
+  double m1 = 0, m2 = 0, Amax = 0, B2 = std::log(2.0);
+  for (int n = 0; n < D; ++n) {
+    double An = 0;
+    for (int k = 0; k < Dr; ++k) {
+      An += std::fabs((double)w1(k, n));
+      m1 = std::fmax(m1, std::fabs((double)w1(k, n)));
+    }
+    Amax = std::fmax(Amax, An);
+    B2 = std::fmax(B2, An + std::fabs((double)cf1[n]));
+    for (int k = 0; k < D; ++k) m2 = std::fmax(m2, std::fabs((double)w2(k, n)));
+  }
+  const double B1 = std::exp(-0.5) / (double)rbf_step + M_PI / (2.0 * (double)r_cut);
+  const double B[4] = {1.0, B1, B2, Amax * B1};
+  const int e1 = std::max(binade(m1), -100), e2 = std::max(binade(m2), -100);
+  const float s1 = std::ldexp(1.f, 14 - e1), s2 = std::ldexp(1.f, 14 - e2);
+  for (int q = 0; q < 4; ++q) {
+    const int ew = q < 2 ? e1 : e2;
+    const int eb = std::max(binade(B[q]), -99 - ew);   // u = 2^(ew + eb - 27) >= 2^-126
+    sc.a[q] = std::ldexp(1.f, 13 - eb);
+    sc.u[q] = std::ldexp(1.f, ew + eb - 27);
+  }
+  auto hi = [](float v) { return (float)(_Float16)v; };
+  om_image<KP, PREC_F16S, false>(D, Dr, D, [&](int k, int n) { return hi(w1(k, n) * s1); }, w1h,
+                                 nullptr);
+  om_image<KP, PREC_F16S, false>(
+      D, Dr, D, [&](int k, int n) { const float v = w1(k, n) * s1; return v - hi(v); }, w1l,
+      nullptr);
+  om_image<D, PREC_F16S, true>(D, D, D, [&](int k, int n) { return hi(w2(k, n) * s2); }, w2h,
+                               nullptr);
+  om_image<D, PREC_F16S, true>(
+      D, D, D, [&](int k, int n) { const float v = w2(k, n) * s2; return v - hi(v); }, w2l,
+      nullptr);
+}
+
 // Wf1 without the perm32 placement: the first product's B operand (the
 // basis) is evaluated directly in the k order a lane feeds.
 template <int D, int KP, int PR>
 static void fill_image(int Dr, const float* Wf1, const float* cf1, const float* Wf2,
-                       const float* cf2, unsigned char* out) {
+                       const float* cf2, float rbf_step, float r_cut, unsigned char* out) {
   using P = Plan<D, KP, PR, 1>;
   std::memset(out, 0, P::IMG);
   float* sc = reinterpret_cast<float*>(out + P::SC);
-  om_image<KP, PR, false>(D, Dr, D, [&](int k, int n) { return Wf1[(size_t)k * D + n]; },
-                          out + P::W1, sc);
-  om_image<D, PR, true>(D, D, D, [&](int k, int n) { return Wf2[(size_t)k * D + n]; },
-                        out + P::W2, sc + D);
+  if constexpr (PR == PREC_F16X2) {
+    SplitScales ss;
+    fill_split<D, KP>(Dr, Wf1, cf1, Wf2, rbf_step, r_cut, out + P::W1, out + P::W1L, out + P::W2,
+                      out + P::W2L, ss);
+    std::memcpy(sc, &ss, sizeof(ss));
+  } else {
+    om_image<KP, PR, false>(D, Dr, D, [&](int k, int n) { return Wf1[(size_t)k * D + n]; },
+                            out + P::W1, sc);
+    om_image<D, PR, true>(D, D, D, [&](int k, int n) { return Wf2[(size_t)k * D + n]; },
+                          out + P::W2, sc + D);
+  }
   float* bias = reinterpret_cast<float*>(out + P::BIAS);
   std::memcpy(bias, cf1, D * sizeof(float));
   std::memcpy(bias + D, cf2, D * sizeof(float));
@@ -152,6 +234,21 @@ __device__ __forceinline__ f32x4 scale4(const CfParams& p, const unsigned char* 
   const unsigned char* base =
       P::BIAS_LDS ? lds + P::SC : reinterpret_cast<const unsigned char*>(p.img) + P::SC;
   return *reinterpret_cast<const f32x4*>(base + 4 * lo + 4 * k);
+}
+
+// The fp16-pair scales, wave-uniform (scalar loads from the image in global memory).
+template <class P>
+__device__ __forceinline__ SplitScales split_scales(const CfParams& p) {
+  const __attribute__((address_space(4))) float* s =
+      (const __attribute__((address_space(4))) float*)(static_cast<const unsigned char*>(p.img) +
+                                                       P::SC);
+  SplitScales r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    r.a[q] = s[q];
+    r.u[q] = s[4 + q];
+  }
+  return r;
 }
 
 // ------------------------------------------------------------------ per-edge geometry
@@ -196,8 +293,8 @@ __device__ __forceinline__ Geo geometry(const CfParams& p, __amdgpu_buffer_rsrc_
 // Each lane evaluates the basis of its own edge for the k slots it feeds
 // (fp32: k = 8c + 2g + u for the MFMA pair u; 16-bit: k = 32c + 8g + t).
 template <int D, int KP, int PR, int NA>
-__device__ __forceinline__ void gemm1(f32x4 (&acc)[NA][D / 16], const unsigned char* lds,
-                                      const CfParams& p, const Geo& g, int lane_) {
+__device__ __forceinline__ void gemm1_plain(f32x4 (&acc)[NA][D / 16], const unsigned char* lds,
+                                            const CfParams& p, const Geo& g, int lane_) {
   constexpr bool H16 = PR != PREC_F32;
   const int lane = opaque(lane_), grp = lane >> 4, e = lane & 15;
   constexpr int CH = H16 ? 32 : 8;     // k per chunk
@@ -266,6 +363,92 @@ __device__ __forceinline__ void gemm1(f32x4 (&acc)[NA][D / 16], const unsigned c
       }
     }
   }
+}
+
+// All KP / 32 basis chunks at once (KC = KP / 32 for the 16-bit layouts):
+// the basis of the lane's 8 k per chunk, split into fp16 pairs, then, as in
+// gemm_split_block, every correction product before the hi*hi products.
+template <int D, int KP, int NA>
+__device__ __forceinline__ void gemm1_split(f32x4 (&acc)[NA][D / 16], const unsigned char* lds,
+                                            const CfParams& p, const Geo& g, int lane_, float sa0,
+                                            float sa1) {
+  constexpr int NC = KP / 32;
+  const int lane = opaque(lane_), grp = lane >> 4, e = lane & 15;
+  float step = p.rbf_step;
+  asm volatile("" : "+v"(step));
+  const float coef2 = p.rbf_coef2;
+  const float Ca = g.C * sa0, Cpa = g.Cp * sa1, Cia = p.rbf_inv_s2 * g.C * sa1;
+  f16x8 bh[NC][NA], bl[NC][NA];
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      // d - mu_k with one rounding, as the fp32 path
+      const float z = __builtin_fmaf(-(float)(32 * c + 8 * grp + t), step, g.d0);
+      const float gs = g.in * __builtin_amdgcn_exp2f(coef2 * z * z);
+      // each basis value is pinned before it is split: hi and lo must both
+      // come from the one rounded float (a product contracted into either
+      // conversion would be rounded differently for each part)
+      float b[NA];
+      b[0] = pinned(gs * Ca);
+      if constexpr (NA == 2) b[1] = pinned(gs * (Cpa - z * Cia));
+#pragma unroll
+      for (int q = 0; q < NA; ++q) {
+        const _Float16 h = (_Float16)b[q];
+        bh[c][q][t] = h;
+        bl[c][q][t] = (_Float16)(b[q] - (float)h);
+      }
+    }
+  const _Float16* W1H = reinterpret_cast<const _Float16*>(lds);
+  const _Float16* W1L = W1H + D * KP;
+#pragma unroll
+  for (int nb = 0; nb < D / 16; ++nb) {
+    f16x8 wh[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int o = sw8<KP>(16 * nb + e, 32 * c + 8 * grp);
+      wh[c] = *reinterpret_cast<const f16x8*>(W1H + o);
+      const f16x8 wl = *reinterpret_cast<const f16x8*>(W1L + o);
+#pragma unroll
+      for (int q = 0; q < NA; ++q) {
+        acc[q][nb] = mfma16(wl, bh[c][q], acc[q][nb]);
+        acc[q][nb] = mfma16(wh[c], bl[c][q], acc[q][nb]);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int q = 0; q < NA; ++q) acc[q][nb] = mfma16(wh[c], bh[c][q], acc[q][nb]);
+  }
+}
+
+// fp16 pairs: basis_q enters scaled by a[q] (sa0, sa1), in fp32 as the
+// fp32 path computes it, and is split into hi + lo.
+template <int D, int KP, int PR, int NA>
+__device__ __forceinline__ void gemm1(f32x4 (&acc)[NA][D / 16], const unsigned char* lds,
+                                      const CfParams& p, const Geo& g, int lane, float sa0 = 1.f,
+                                      float sa1 = 1.f) {
+  if constexpr (PR == PREC_F16X2) gemm1_split<D, KP, NA>(acc, lds, p, g, lane, sa0, sa1);
+  else gemm1_plain<D, KP, PR, NA>(acc, lds, p, g, lane);
+}
+
+// The second filter product (through Wf2), one output block: B operands in
+// the precision's own form, or as fp16 pairs of the inputs scaled by a.
+template <int D, int PR>
+struct W2Op {
+  using T = Operand<D, PR>;
+  __device__ __forceinline__ static T make(const f32x4 (&s)[D / 16], float) { return T(s); }
+};
+template <int D>
+struct W2Op<D, PREC_F16X2> {
+  using T = SplitOperand<D>;
+  __device__ __forceinline__ static T make(const f32x4 (&s)[D / 16], float a) { return T(s, a); }
+};
+template <class P, int D, int PR, class Op>
+__device__ __forceinline__ void gemm2_block(f32x4& acc, const Op& op, const unsigned char* lds,
+                                            int nb, const ImgLanes<D, PR>& wl) {
+  if constexpr (PR == PREC_F16X2) gemm_split_block<D>(acc, op, lds + P::W2, lds + P::W2L, nb, wl);
+  else gemm_om_block<D, PR>(acc, op, lds + P::W2, nb, wl);
 }
 
 // ------------------------------------------------------------------ receiver segments
@@ -439,6 +622,8 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, false>()), 1) void k_cf_fwd(CfPa
   const uint32_t N = (uint32_t)p.n_atoms;
   const __amdgpu_buffer_rsrc_t rx = rsrc(p.x, N * (uint32_t)D * 4u);
   const int fcol = col_feature(lane);
+  SplitScales ss{};
+  if constexpr (PR == PREC_F16X2) ss = split_scales<P>(p);
 
   float carry[NB / 4];
 #pragma unroll
@@ -463,7 +648,7 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, false>()), 1) void k_cf_fwd(CfPa
     f32x4 s[1][NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) s[0][nb] = f32x4{};
-    gemm1<D, KP, PR, 1>(s, lds, p, g, lane);
+    gemm1<D, KP, PR, 1>(s, lds, p, g, lane, ss.a[0], ss.a[1]);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const f32x4 c1 = bias4<P>(p, lds, g4, 16 * nb);
@@ -471,6 +656,9 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, false>()), 1) void k_cf_fwd(CfPa
         const f32x4 s1 = scale4<P>(p, lds, g4, 16 * nb);
 #pragma unroll
         for (int r = 0; r < 4; ++r) s[0][nb][r] = ssp(fmaf(s[0][nb][r], s1[r], c1[r]));
+      } else if constexpr (PR == PREC_F16X2) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[0][nb][r] = ssp(fmaf(s[0][nb][r], ss.u[0], c1[r]));
       } else {
 #pragma unroll
         for (int r = 0; r < 4; ++r) s[0][nb][r] = ssp(s[0][nb][r] + c1[r]);
@@ -490,7 +678,14 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, false>()), 1) void k_cf_fwd(CfPa
     for (int b = 0; b < 4; ++b) xg[b] = bload4(rx, xo + (uint32_t)(64 * b));
     __builtin_amdgcn_sched_barrier(0);
     f32x4 w[NB];
-    gemm_om<D, D, PR>(w, s[0], lds + P::W2, wl);
+    {
+      const auto os = W2Op<D, PR>::make(s[0], ss.a[2]);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        w[nb] = f32x4{};
+        gemm2_block<P>(w[nb], os, lds, nb, wl);
+      }
+    }
 #pragma unroll
     for (int pss = 0; pss < NB / 4; ++pss) {
 #pragma unroll
@@ -498,6 +693,7 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, false>()), 1) void k_cf_fwd(CfPa
         const int nb = 4 * pss + b;
         const f32x4 c2 = bias4<P>(p, lds, g4, D + 16 * nb);
         if constexpr (PR == PREC_F16S) w[nb] *= scale4<P>(p, lds, g4, D + 16 * nb);
+        if constexpr (PR == PREC_F16X2) w[nb] *= ss.u[2];
         f32x4 m;
 #pragma unroll
         for (int r = 0; r < 4; ++r) m[r] = xg[b][r] * (g.in * (w[nb][r] + c2[r]));
@@ -537,6 +733,8 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, true>()), 1) void k_cf_bwd(CfPar
   const __amdgpu_buffer_rsrc_t rgh = rsrc(p.gh, N * (uint32_t)D * 4u);
   const bool want_q = p.q_out != nullptr;
   const int fcol = col_feature(lane);
+  SplitScales ss{};
+  if constexpr (PR == PREC_F16X2) ss = split_scales<P>(p);
 
   float carry[NB / 4];
 #pragma unroll
@@ -565,7 +763,7 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, true>()), 1) void k_cf_bwd(CfPar
     for (int q = 0; q < 2; ++q)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) av[q][nb] = f32x4{};
-    gemm1<D, KP, PR, 2>(av, lds, p, g, lane);
+    gemm1<D, KP, PR, 2>(av, lds, p, g, lane, ss.a[0], ss.a[1]);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const f32x4 c1 = bias4<P>(p, lds, g4, 16 * nb);
@@ -573,6 +771,10 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, true>()), 1) void k_cf_bwd(CfPar
         const f32x4 s1 = scale4<P>(p, lds, g4, 16 * nb);
         av[0][nb] *= s1;
         av[1][nb] *= s1;
+      }
+      if constexpr (PR == PREC_F16X2) {
+        av[0][nb] *= ss.u[0];
+        av[1][nb] *= ss.u[1];
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -605,17 +807,17 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, true>()), 1) void k_cf_bwd(CfPar
     // GEMM2: the tangents of all blocks, w' = s' Wf2, and the values w = s Wf2
     // of the first 64 features, as independent product chains; the values of
     // each further 64 features are formed once the previous ones are used
-    const Operand<D, PR> os(av[0]);
+    const auto os = W2Op<D, PR>::make(av[0], ss.a[2]);
     f32x4 wt[NB], wv[4];
     {
-      const Operand<D, PR> ot(av[1]);
+      const auto ot = W2Op<D, PR>::make(av[1], ss.a[3]);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         wt[nb] = f32x4{};
-        gemm_om_block<D, PR>(wt[nb], ot, lds + P::W2, nb, wl);
+        gemm2_block<P>(wt[nb], ot, lds, nb, wl);
         if (nb < 4) {
           wv[nb] = f32x4{};
-          gemm_om_block<D, PR>(wv[nb], os, lds + P::W2, nb, wl);
+          gemm2_block<P>(wv[nb], os, lds, nb, wl);
         }
       }
     }
@@ -636,6 +838,10 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, true>()), 1) void k_cf_bwd(CfPar
           wv[b] *= s2;
           wt[nb] *= s2;
         }
+        if constexpr (PR == PREC_F16X2) {
+          wv[b] *= ss.u[2];
+          wt[nb] *= ss.u[3];
+        }
         f32x4 qv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -650,7 +856,7 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, true>()), 1) void k_cf_bwd(CfPar
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           wv[b] = f32x4{};
-          gemm_om_block<D, PR>(wv[b], os, lds + P::W2, 4 * (pss + 1) + b, wl);
+          gemm2_block<P>(wv[b], os, lds, 4 * (pss + 1) + b, wl);
         }
       }
       if (want_q) {
@@ -779,8 +985,8 @@ struct CfKernels {
   static size_t image_bytes() { return PF::IMG; }
   static int workers(int bwd) { return bwd ? PB::NW : PF::NW; }
   static void fill(int Dr, const float* Wf1, const float* cf1, const float* Wf2, const float* cf2,
-                   unsigned char* out) {
-    fill_image<D, KP, PR>(Dr, Wf1, cf1, Wf2, cf2, out);
+                   float rbf_step, float r_cut, unsigned char* out) {
+    fill_image<D, KP, PR>(Dr, Wf1, cf1, Wf2, cf2, rbf_step, r_cut, out);
   }
   static hipError_t fwd(const CfParams& p, int G, hipStream_t s) {
     hipLaunchKernelGGL((k_cf_fwd<D, KP, PR>), dim3(G), dim3(PF::NT), PF::TOTAL, s, p);
@@ -797,7 +1003,7 @@ static R cf_dispatch(int D, int KP, int prec, R fail, F f) {
 #define SN_CF(DD, KK, PP) \
   if (D == DD && KP == KK && prec == PP) return f(CfKernels<DD, KK, PP>{});
 #define SN_CF_P(PP) SN_CF(64, 32, PP) SN_CF(64, 64, PP) SN_CF(128, 32, PP) SN_CF(128, 64, PP)
-  SN_CF_P(PREC_F32) SN_CF_P(PREC_BF16) SN_CF_P(PREC_F16S)
+  SN_CF_P(PREC_F32) SN_CF_P(PREC_BF16) SN_CF_P(PREC_F16S) SN_CF_P(PREC_F16X2)
 #undef SN_CF_P
 #undef SN_CF
   return fail;
@@ -814,9 +1020,10 @@ size_t cf_image_bytes(int D, int KP, int prec) {
   return cf_dispatch(D, KP, prec, (size_t)0, [](auto k) { return decltype(k)::image_bytes(); });
 }
 void cf_fill_image(int D, int KP, int prec, int Dr, const float* Wf1, const float* cf1,
-                   const float* Wf2, const float* cf2, unsigned char* out) {
+                   const float* Wf2, const float* cf2, float rbf_step, float r_cut,
+                   unsigned char* out) {
   cf_dispatch(D, KP, prec, 0, [&](auto k) {
-    decltype(k)::fill(Dr, Wf1, cf1, Wf2, cf2, out);
+    decltype(k)::fill(Dr, Wf1, cf1, Wf2, cf2, rbf_step, r_cut, out);
     return 0;
   });
 }

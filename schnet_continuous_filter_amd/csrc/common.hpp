@@ -34,8 +34,8 @@ struct DevStatus {
 
 // MLP operand precisions (the filter_dtype values of sn_model_desc): fp32;
 // bfloat16 filter network; fp16 operands with per-output-channel power-of-two
-// scales in every MLP.
-enum Prec { PREC_F32 = 0, PREC_BF16 = 1, PREC_F16S = 2 };
+// scales in every MLP; fp32 filter network evaluated on fp16 hi/lo pairs.
+enum Prec { PREC_F32 = 0, PREC_BF16 = 1, PREC_F16S = 2, PREC_F16X2 = 3 };
 
 // Round-to-nearest-even bfloat16 bits of a finite float (host side).
 inline uint16_t bf16_rne_bits(float f) {
@@ -125,8 +125,11 @@ hipError_t cf_prepare(int D, int KP, int prec);  // raises the dynamic LDS limit
 // Filter-weight image of one interaction block as the CFConv kernels hold it
 // in LDS: cf_image_bytes bytes, filled on the host.
 size_t cf_image_bytes(int D, int KP, int prec);
+// rbf_step and r_cut bound the basis functions and their derivatives, from
+// which PREC_F16X2 sets the power-of-two scales of its product inputs.
 void cf_fill_image(int D, int KP, int prec, int Dr, const float* Wf1, const float* cf1,
-                   const float* Wf2, const float* cf2, unsigned char* out);
+                   const float* Wf2, const float* cf2, float rbf_step, float r_cut,
+                   unsigned char* out);
 hipError_t launch_force_sum(const float* fb, int T, int64_t n_atoms, float* forces, hipStream_t s);
 hipError_t launch_partition(const int32_t* rowptr, int n_atoms, int G, int32_t* wg_start,
                             DevStatus* st, hipStream_t s);

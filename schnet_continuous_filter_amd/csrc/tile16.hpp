@@ -40,6 +40,13 @@ __device__ __forceinline__ int opaque(int v) {
   return v;
 }
 
+// v rounded to a float in a register: every later use starts from this one
+// rounding, whatever the compiler contracts into those uses.
+__device__ __forceinline__ float pinned(float v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // Orders this wave's LDS writes before its later LDS reads (wave-private data).
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -77,6 +84,7 @@ __device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
 template <int PR> struct PrecT { using E = float; };
 template <> struct PrecT<PREC_BF16> { using E = __bf16; using V8 = bf16x8; };
 template <> struct PrecT<PREC_F16S> { using E = _Float16; using V8 = f16x8; };
+template <> struct PrecT<PREC_F16X2> { using E = _Float16; using V8 = f16x8; };
 
 // XOR-swizzled offset of element (row, col) of a row-major array with RL
 // elements per row: 16-byte chunks (4 fp32 or 8 bf16) trade places by row, so
@@ -117,6 +125,27 @@ template <int K>
 struct Operand<K, PREC_F32> {
   const f32x4 (&S)[K / 16];
   __device__ __forceinline__ explicit Operand(const f32x4 (&s)[K / 16]) : S(s) {}
+};
+
+// B operands of a chained product on fp16 pairs: each input value x is
+// scaled by the power of two a, then written as hi + lo with hi = fp16(a x)
+// and lo = fp16(a x - hi) (both rounded to nearest even; 22 significant bits
+// in all while a x stays in fp16's normal range). a x is exact, so the two
+// parts agree however the compiler forms them.
+template <int K>
+struct SplitOperand {
+  f16x8 H[K / 32], L[K / 32];
+  __device__ __forceinline__ SplitOperand(const f32x4 (&s)[K / 16], float a) {
+#pragma unroll
+    for (int kk = 0; kk < K / 32; ++kk)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const float v = s[2 * kk + (t >> 2)][t & 3] * a;
+        const _Float16 h = (_Float16)v;
+        H[kk][t] = h;
+        L[kk][t] = (_Float16)(v - (float)h);
+      }
+  }
 };
 
 // Per-lane element offsets of the A-operand reads of an output-major image
@@ -164,6 +193,34 @@ __device__ __forceinline__ void gemm_om_block(f32x4& acc, const Operand<K, PR>& 
       for (int r = 0; r < 4; ++r) acc = mfma16(w[r], op.S[kb][r], acc);
     }
   }
+}
+
+// acc = sum_k M[16 nb + e][k] S[k] with M = MH + ML and S = H + L given as
+// fp16 pairs: the three products MH H + MH L + ML H (the ML L term is below
+// the pairs' own rounding). MH and ML are 16-bit output-major images as in
+// gemm_om_block. The fp16 products enter the fp32 accumulator without a
+// correctly rounded sum: bits of a product far below the accumulator's
+// magnitude are lost. So every small correction product (one lo factor) is
+// summed first, while the accumulator is of its own size, and the hi*hi
+// products last; those are exact 22-bit numbers on the final sum's grid.
+template <int K>
+__device__ __forceinline__ void gemm_split_block(f32x4& acc, const SplitOperand<K>& op,
+                                                 const void* img_hi, const void* img_lo, int nb,
+                                                 const ImgLanes<K, PREC_F16X2>& ln) {
+  static_assert(K / 32 <= 4, "chunk groups");
+  const _Float16* MH = reinterpret_cast<const _Float16*>(img_hi) + 16 * nb * K;
+  const _Float16* ML = reinterpret_cast<const _Float16*>(img_lo) + 16 * nb * K;
+  f16x8 wh[K / 32];
+  acc = f32x4{};
+#pragma unroll
+  for (int kk = 0; kk < K / 32; ++kk) {
+    wh[kk] = *reinterpret_cast<const f16x8*>(MH + ln.off[kk]);
+    const f16x8 wl = *reinterpret_cast<const f16x8*>(ML + ln.off[kk]);
+    acc = mfma16(wl, op.H[kk], acc);
+    acc = mfma16(wh[kk], op.L[kk], acc);
+  }
+#pragma unroll
+  for (int kk = 0; kk < K / 32; ++kk) acc = mfma16(wh[kk], op.H[kk], acc);
 }
 
 // All NOUT / 16 output blocks: out[nb] = sum_k M[16 nb + e][k] S[k] (k < K).

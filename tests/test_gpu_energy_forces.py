@@ -41,7 +41,7 @@ def check(lib, cfg, pos, types, w, r_list=None, n_replicas=None, what=""):
                                        periodic=bool(system.periodic), box=system.box,
                                        return_eps=True)
     eps_sum = np.abs(eps).reshape(system.n_replicas, -1).sum(axis=1) if m.filter_dtype == 2 else None
-    re, rf = assert_energy_forces(E, F, Eo, Fo, bf16=m.filter_dtype != 0, what=what,
+    re, rf = assert_energy_forces(E, F, Eo, Fo, bf16=m.filter_dtype in (1, 2), what=what,
                                   eps_abs_sum=eps_sum)
     if eps_sum is not None:
         print(f"{what}: E err / sum|eps| {np.max(np.abs(E - Eo) / eps_sum):.2e}")

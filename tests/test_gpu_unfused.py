@@ -43,7 +43,7 @@ def check(lib, cfg, pos, types, w, mode, r_list=None, n_replicas=None, what=""):
     Eo, Fo = oracle.energy_forces(oracle_desc(m), w, pos, types, rp, col,
                                   n_replicas=system.n_replicas, periodic=bool(system.periodic),
                                   box=system.box)
-    re, rf = assert_energy_forces(E, F, Eo, Fo, bf16=m.filter_dtype != 0, what=f"{what} {mode}")
+    re, rf = assert_energy_forces(E, F, Eo, Fo, bf16=m.filter_dtype in (1, 2), what=f"{what} {mode}")
     print(f"{what} {mode}: E rel {re:.2e}, F max/rms {rf:.2e}, edges {len(col)}")
     return E, F
 
