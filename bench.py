@@ -30,6 +30,7 @@ PEAK_FP32_MFMA_TFLOPS = 157.3     # MI355X dense fp32 matrix peak
 PEAK_BF16_MFMA_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 PREC_TAGS = {0: "f32", 1: "bf16", 2: "w16a16", 3: "f16x2"}
+DTYPE_TAGS = {0: "f32", 1: "bf16-filter/f32", 2: "f16-mlps/f32", 3: "f16x2-filter/f32"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cfconv_bwd_cg269x64_counters.txt")
 
 
@@ -44,6 +45,8 @@ def parse():
     ap.add_argument("--precision", choices=["f32", "bf16", "w16a16", "f16x2"], default=None,
                     help="override the workload's network operand precision")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-alt", action="store_true",
+                    help="fp32 workloads: skip the extra timing with the filter on fp16 pairs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a device copy of known size (for counter scaling)")
     ap.add_argument("--sweep-replicas", default="",
@@ -347,8 +350,7 @@ def main():
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no "
               "multi-GPU path", file=sys.stderr)
         sys.exit(2)
-    import numpy as np
-    import torch
+    import torch  # noqa: F401  (initialises the device before any library call)
     if args.ablation:
         ablation(args)
         return
@@ -362,14 +364,76 @@ def main():
         copy_calibration()
         return
     from gen.configs import CONFIGS, make_config
-    from schnet_continuous_filter_amd import _lib as L
 
     cfg = CONFIGS[args.workload]
     c, pos, types, w = make_config(cfg.name)
-    m, s = c.model, c.system
+    m = c.model
     if args.precision is not None:
         import dataclasses
         m = dataclasses.replace(m, filter_dtype={v: k for k, v in PREC_TAGS.items()}[args.precision])
+    r = md_timing(cfg, c, m, pos, types, w, args.steps, args.warmup)
+    R = c.system.n_replicas
+    flops_bwd = 4.0 * m.D * (m.Dr + m.D) * r["ne"]    # recompute (2D(Dr+D)) + dgrad (2D(Dr+D))
+    avg_bwd_s = r["bwd_ms"] / 1000.0 / max(r["bwd_n"], 1)
+    achieved = flops_bwd / avg_bwd_s / 1e12
+    half = m.filter_dtype != 0          # 16-bit operands: the dense fp16/bf16 MFMA peak
+    peak = PEAK_BF16_MFMA_TFLOPS if half else PEAK_FP32_MFMA_TFLOPS
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        rec = json.load(open(TRAFFIC_FILE))
+        if (rec.get("kernel_hash") == profiling.kernel_hash() and rec.get("workload") == cfg.name
+                and m.filter_dtype == 0):
+            traffic = rec.get("bytes_per_launch")
+    line = {
+        "metric": "CFConv energy+force edges/sec and replica-MD-steps/sec at 1 GPU; % HBM roofline",
+        "value": r["edges_per_s"],
+        "unit": "edges/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE_TAGS[m.filter_dtype],
+        "data": "synthetic (seeded chains/boxes, random-init weights)",
+        "config": {"workload": cfg.name, "replicas": R,
+                   "atoms_per_replica": c.system.atoms_per_replica,
+                   "directed_edges": r["ne"], "list_radius_A": r["r_list"], "D": m.D, "Dr": m.Dr,
+                   "T": m.T, "r_cut_A": m.r_cut,
+                   "step": "BAOAB + neighbour rebuild + energy/forces"},
+        "replica_steps_per_s": r["replica_steps_per_s"],
+        "roofline": {"kernel": "k_cf_bwd (fused CFConv backward, one interaction block)",
+                     "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": traffic,
+                     "flops_per_launch": flops_bwd, "avg_launch_us": avg_bwd_s * 1e6,
+                     "launches": r["bwd_n"],
+                     "fwd_avg_launch_us": r["fwd_ms"] * 1000.0 / max(r["fwd_n"], 1)},
+        "n_rebuilds": r["n_rebuilds"],
+    }
+    if m.filter_dtype == 0 and args.precision is None and not args.no_alt:
+        # the same fp32 model with the filter products on fp16 pairs (held to
+        # the fp32 parity bars), timed the same way
+        import dataclasses
+        m2 = dataclasses.replace(m, filter_dtype=3)
+        r2 = md_timing(cfg, c, m2, pos, types, w, args.steps, args.warmup)
+        line["f16x2_filter"] = {
+            "value": r2["edges_per_s"], "unit": "edges/s", "ms_per_step": r2["ms_per_step"],
+            "replica_steps_per_s": r2["replica_steps_per_s"], "dtype": DTYPE_TAGS[3],
+            "bwd_avg_launch_us": r2["bwd_ms"] * 1000.0 / max(r2["bwd_n"], 1),
+            "fwd_avg_launch_us": r2["fwd_ms"] * 1000.0 / max(r2["fwd_n"], 1),
+            "parity": "fp32 bars (energy 1e-5 relative, forces 1e-4 of the force RMS)"}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    print(json.dumps(line))
+
+
+def md_timing(cfg, c, m, pos, types, w, steps, warmup):
+    """MD steps of one model on the workload: warm-up, then `steps` timed
+    steps with the CFConv kernels' launch times recorded by the library."""
+    import torch
+    from schnet_continuous_filter_amd import _lib as L
+    s = c.system
     R, N = s.n_replicas, s.atoms_per_replica
     desc = L.make_desc(m.n_types, m.D, m.Dr, m.T, m.H, m.rbf_min, m.rbf_max, m.r_cut,
                        m.filter_dtype)
@@ -393,7 +457,7 @@ def main():
     state = L.MdState(p, capacity)
     energy = torch.empty(R, dtype=torch.float32, device=dev)
     L.sn_md_init(model, system, t, md, state, energy, ws)
-    L.sn_md_step(model, system, t, md, state, args.warmup, energy, ws)
+    L.sn_md_step(model, system, t, md, state, warmup, energy, ws)
     torch.cuda.synchronize()
     L.sn_profile_read(0)
     L.sn_profile_read(1)
@@ -401,7 +465,7 @@ def main():
     L.sn_profile_enable(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    L.sn_md_step(model, system, t, md, state, args.steps, energy, ws)
+    L.sn_md_step(model, system, t, md, state, steps, energy, ws)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     L.sn_profile_enable(False)
@@ -414,49 +478,11 @@ def main():
         sys.exit(1)
     # edge count on the final positions (untimed)
     ne = L.sn_build_neighbors(system, state.pos, r_list, state.rowptr, state.col, capacity, ws)
-
-    ms_per_step = 1000.0 * elapsed / args.steps
-    edges_per_s = ne * args.steps / elapsed
-    half = m.filter_dtype != 0          # bf16 or fp16 operands: the same dense MFMA peak
-    flops_bwd = 4.0 * m.D * (m.Dr + m.D) * ne          # recompute (2D(Dr+D)) + dgrad (2D(Dr+D))
-    avg_bwd_s = bwd_ms / 1000.0 / max(bwd_n, 1)
-    achieved = flops_bwd / avg_bwd_s / 1e12
-    peak = PEAK_BF16_MFMA_TFLOPS if half else PEAK_FP32_MFMA_TFLOPS
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        rec = json.load(open(TRAFFIC_FILE))
-        if rec.get("kernel_hash") == profiling.kernel_hash() and rec.get("workload") == cfg.name:
-            traffic = rec.get("bytes_per_launch")
-    line = {
-        "metric": "CFConv energy+force edges/sec and replica-MD-steps/sec at 1 GPU; % HBM roofline",
-        "value": edges_per_s,
-        "unit": "edges/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": {0: "f32", 1: "bf16-filter/f32", 2: "f16-mlps/f32",
-                  3: "f16x2-filter/f32"}[m.filter_dtype],
-        "data": "synthetic (seeded chains/boxes, random-init weights)",
-        "config": {"workload": cfg.name, "replicas": R, "atoms_per_replica": N,
-                   "directed_edges": ne, "list_radius_A": r_list, "D": m.D, "Dr": m.Dr, "T": m.T,
-                   "r_cut_A": m.r_cut, "step": "BAOAB + neighbour rebuild + energy/forces"},
-        "replica_steps_per_s": R * args.steps / elapsed,
-        "roofline": {"kernel": "k_cf_bwd (fused CFConv backward, one interaction block)",
-                     "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": traffic,
-                     "flops_per_launch": flops_bwd, "avg_launch_us": avg_bwd_s * 1e6,
-                     "launches": bwd_n,
-                     "fwd_avg_launch_us": fwd_ms * 1000.0 / max(fwd_n, 1)},
-        "n_rebuilds": n_rebuilds,
-    }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
-    print(json.dumps(line))
     L.sn_model_destroy(model)
+    return {"edges_per_s": ne * steps / elapsed, "ms_per_step": 1000.0 * elapsed / steps,
+            "replica_steps_per_s": R * steps / elapsed, "ne": ne, "r_list": r_list,
+            "bwd_ms": bwd_ms, "bwd_n": bwd_n, "fwd_ms": fwd_ms, "fwd_n": fwd_n,
+            "n_rebuilds": n_rebuilds}
 
 
 if __name__ == "__main__":
