@@ -18,7 +18,12 @@
 // (§4.4 "W16A16 mixed precision for MLP submodules") every weight column
 // carries a power-of-two scale: outputs of a product are multiplied by their
 // column's scale, and products with a transposed matrix (the gradients)
-// multiply their inputs by it instead.
+// multiply their inputs by it instead. With an fp32 model whose products run
+// on fp16 pairs (PREC_F16X2) each matrix is stored as hi and lo fp16 images
+// of its values times one power of two, and each atom's input vector is
+// scaled by the power of two that puts its largest magnitude in
+// [2^12, 2^13) before it is split into hi + lo; the output is scaled back.
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <vector>
@@ -33,17 +38,21 @@ constexpr int kAtoms = 16;    // atoms per wave tile
 // LDS image of one network: M1 [N1][D] (first product, output-major), M2
 // [D][N1] (second product), V1 [N1], V2 [D] (vectors of the mode), and for
 // fp16 operands the column scales S1 [N1] of the first network layer and S2
-// [D] of the second (readout: S1 only).
+// [D] of the second (readout: S1 only). fp16 pairs: M1 and M2 hold the hi
+// images, M1L and M2L the lo images, and S1 the two matrices' inverse scales.
 template <int D, int N1, int PR>
 struct AtomPlan {
   static constexpr int ES = PR != PREC_F32 ? 2 : 4;
+  static constexpr int NS = PR == PREC_F16X2 ? 2 : 1;   // images per matrix
   static constexpr int M1 = 0;
-  static constexpr int M2 = M1 + N1 * D * ES;
-  static constexpr int V1 = M2 + D * N1 * ES;
+  static constexpr int M1L = M1 + N1 * D * ES;
+  static constexpr int M2 = M1 + NS * N1 * D * ES;
+  static constexpr int M2L = M2 + D * N1 * ES;
+  static constexpr int V1 = M2 + NS * D * N1 * ES;
   static constexpr int V2 = V1 + N1 * 4;
   static constexpr int S1 = V2 + D * 4;
   static constexpr int S2 = S1 + N1 * 4;
-  static constexpr int IMG = PR == PREC_F16S ? S2 + D * 4 : S1;
+  static constexpr int IMG = PR == PREC_F16S ? S2 + D * 4 : PR == PREC_F16X2 ? S1 + 16 : S1;
   static_assert(IMG <= 160 * 1024, "atom-wise image exceeds LDS");
   static_assert(IMG % 16 == 0, "image is copied in 16-byte pieces");
 };
@@ -69,12 +78,62 @@ static std::vector<float> column_scales(const float* W, int rows, int cols) {
 //                    M1 = Wo1^T, M2 = Wo1, V1 = co1, V2[:N1] = wo2
 // Weights are divided by their column scales (all 1 unless fp16) before
 // they are placed; the kernels multiply the scales back in.
+// fp16-pair images of one matrix: m scaled by the power of two that puts
+// its largest magnitude in [2^13, 2^14), as hi and lo images (PERM layout of
+// chained products); returns the inverse of that scale.
+template <int K, class F>
+static float pair_images(int N, F m, unsigned char* hi, unsigned char* lo) {
+  float amax = 0.f;
+  for (int n = 0; n < N; ++n)
+    for (int k = 0; k < K; ++k) amax = std::fmax(amax, std::fabs(m(k, n)));
+  int e = 0;
+  if (amax > 0.f) std::frexp(amax, &e);
+  e = std::max(e, -100);
+  const float sc = std::ldexp(1.f, 14 - e);
+  auto h = [](float v) { return (float)(_Float16)v; };
+  om_image<K, PREC_F16S>(N, K, N, [&](int k, int n) { return h(m(k, n) * sc); }, hi, nullptr);
+  om_image<K, PREC_F16S>(N, K, N, [&](int k, int n) { const float v = m(k, n) * sc; return v - h(v); },
+                         lo, nullptr);
+  return std::ldexp(1.f, e - 14);
+}
+
+// The products of each mode as in fill_atom_image, on fp16 pairs; S1 holds
+// the inverse scales of M1 and M2.
+template <int D, int N1>
+static void fill_atom_pairs(int mode, const float* W1, const float* b1, const float* W2,
+                            const float* b2, unsigned char* out) {
+  using P = AtomPlan<D, N1, PREC_F16X2>;
+  float* v1 = reinterpret_cast<float*>(out + P::V1);
+  float* v2 = reinterpret_cast<float*>(out + P::V2);
+  float* inv = reinterpret_cast<float*>(out + P::S1);
+  auto w1 = [&](int k, int n) { return W1[(size_t)k * N1 + n]; };   // k < D, n < N1
+  auto w2 = [&](int n, int m) { return W2[(size_t)n * D + m]; };    // n < N1, m < D
+  if (mode == ATOM_UPDATE_FWD) {
+    inv[0] = pair_images<D>(N1, w1, out + P::M1, out + P::M1L);
+    inv[1] = pair_images<N1>(D, w2, out + P::M2, out + P::M2L);
+    std::memcpy(v1, b1, N1 * sizeof(float));
+    std::memcpy(v2, b2, D * sizeof(float));
+  } else if (mode == ATOM_UPDATE_BWD) {
+    inv[0] = pair_images<D>(N1, [&](int m, int n) { return w2(n, m); }, out + P::M1, out + P::M1L);
+    inv[1] = pair_images<N1>(D, [&](int n, int k) { return w1(k, n); }, out + P::M2, out + P::M2L);
+  } else {
+    inv[0] = pair_images<D>(N1, w1, out + P::M1, out + P::M1L);
+    inv[1] = pair_images<N1>(D, [&](int n, int k) { return w1(k, n); }, out + P::M2, out + P::M2L);
+    std::memcpy(v1, b1, N1 * sizeof(float));
+    for (int n = 0; n < N1; ++n) v2[n] = W2[n];
+  }
+}
+
 template <int D, int N1, int PR>
 static void fill_atom_image(int mode, const float* W1, const float* b1, const float* W2,
                             const float* b2, unsigned char* out) {
   using P = AtomPlan<D, N1, PR>;
   constexpr bool SC = PR == PREC_F16S;
   std::memset(out, 0, P::IMG);
+  if constexpr (PR == PREC_F16X2) {
+    fill_atom_pairs<D, N1>(mode, W1, b1, W2, b2, out);
+    return;
+  }
   float* v1 = reinterpret_cast<float*>(out + P::V1);
   float* v2 = reinterpret_cast<float*>(out + P::V2);
   // s1: columns of W1 [D][N1]; s2: columns of W2 [N1][D] (update) 
@@ -107,6 +166,41 @@ static void fill_atom_image(int mode, const float* W1, const float* b1, const fl
       const float so = column_scales(W2, N1, 1)[0];
       for (int n = 0; n < N1; ++n) v2[n] = (float)(_Float16)(W2[n] / so) * so;
     }
+  }
+}
+
+// Binade of the largest magnitude of this lane's atom vector (its K values
+// are spread over the four lane groups of the atom's column): v = m 2^e with
+// m in [0.5, 1); e >= -100 so that 2^(13 - e) stays a normal float.
+template <int K>
+__device__ __forceinline__ int atom_binade(const f32x4 (&v)[K / 16]) {
+  float m = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < K / 16; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(v[kb][r]));
+  m = fmaxf(m, __shfl_xor(m, 16, 64));
+  m = fmaxf(m, __shfl_xor(m, 32, 64));
+  int e = 0;
+  (void)frexpf(m, &e);
+  return max(e, -100);
+}
+
+// out[nb] = sum_k M[16 nb + e][k] in[k] on fp16 pairs: the input scaled into
+// [2^12, 2^13) per atom, then the product scaled back by inv_m 2^(e - 13)
+// (inv_m: the inverse of the matrix's own scale).
+template <int K, int NOUT>
+__device__ __forceinline__ void atom_pair_product(f32x4 (&out)[NOUT / 16], const f32x4 (&in)[K / 16],
+                                                  const unsigned char* hi, const unsigned char* lo,
+                                                  float inv_m, int lane) {
+  const int e = atom_binade<K>(in);
+  const SplitOperand<K> op(in, ldexpf(1.f, 13 - e));
+  const ImgLanes<K, PREC_F16X2> ln(opaque(lane));
+  const float back = ldexpf(inv_m, e - 13);
+#pragma unroll
+  for (int nb = 0; nb < NOUT / 16; ++nb) {
+    gemm_split_block<K>(out[nb], op, hi, lo, nb, ln);
+    out[nb] *= back;
   }
 }
 
@@ -167,7 +261,10 @@ __global__ __launch_bounds__(64 * kAtomNW, 1) void k_atom(AtomArgs g) {
       for (int kb = 0; kb < D / 16; ++kb) in[kb] *= v4(S2, g4 + 16 * kb);
     }
     f32x4 u[N1 / 16];
-    gemm_om<D, N1, PR>(u, in, lds + P::M1, lane);
+    if constexpr (PR == PREC_F16X2)
+      atom_pair_product<D, N1>(u, in, lds + P::M1, lds + P::M1L, S1[0], lane);
+    else
+      gemm_om<D, N1, PR>(u, in, lds + P::M1, lane);
     float ep = 0.f;
 #pragma unroll
     for (int nb = 0; nb < N1 / 16; ++nb) {
@@ -209,7 +306,10 @@ __global__ __launch_bounds__(64 * kAtomNW, 1) void k_atom(AtomArgs g) {
       for (int nb = 0; nb < N1 / 16; ++nb) u[nb] *= v4(S1, g4 + 16 * nb);
     }
     f32x4 y[D / 16];
-    gemm_om<N1, D, PR>(y, u, lds + P::M2, lane);
+    if constexpr (PR == PREC_F16X2)
+      atom_pair_product<N1, D>(y, u, lds + P::M2, lds + P::M2L, S1[1], lane);
+    else
+      gemm_om<N1, D, PR>(y, u, lds + P::M2, lane);
     if (ok) {
 #pragma unroll
       for (int kb = 0; kb < D / 16; ++kb) {
@@ -263,16 +363,17 @@ struct AtomKernels {
   }
 };
 
-// Atom-wise layers run fp32 operands unless every MLP is 16-bit (PREC_F16S);
-// a bfloat16 filter network leaves them fp32.
+// Atom-wise layers run fp32 operands unless every MLP is 16-bit (PREC_F16S)
+// or the model's products run on fp16 pairs (PREC_F16X2); a bfloat16 filter
+// network leaves them fp32.
 template <class R, class F>
 static R atom_dispatch(int D, int N1, int prec, R fail, F f) {
 #define SN_AT(DD, NN, PP) \
   if (D == DD && N1 == NN && ap == PP) return f(AtomKernels<DD, NN, PP>{});
 #define SN_AT_P(PP) \
   SN_AT(64, 64, PP) SN_AT(128, 128, PP) SN_AT(64, 32, PP) SN_AT(128, 32, PP) SN_AT(128, 64, PP)
-  const int ap = prec == PREC_F16S ? PREC_F16S : PREC_F32;
-  SN_AT_P(PREC_F32) SN_AT_P(PREC_F16S)
+  const int ap = (prec == PREC_F16S || prec == PREC_F16X2) ? prec : PREC_F32;
+  SN_AT_P(PREC_F32) SN_AT_P(PREC_F16S) SN_AT_P(PREC_F16X2)
 #undef SN_AT_P
 #undef SN_AT
   return fail;
