@@ -62,17 +62,17 @@ typedef enum {
  *                  fp16(W[:, n] / s_n) with s_n the power of two at or above
  *                  the column's largest magnitude (1 for a zero column), and
  *                  the readout's output weights likewise as one column;
- *  SN_FILTER_F16X2 the filter network keeps fp32 weights and activations,
- *                  each entering its products as a pair of fp16 numbers
- *                  hi + lo (22 significant bits; whole matrices and
- *                  activation vectors are first scaled by powers of two,
- *                  derived on the host from the weights and the basis
- *                  width, so that both parts stay in fp16's normal range),
- *                  and each product is hi*hi + hi*lo + lo*hi on the fp16
- *                  matrix units: about 1e-6 relative error per dot product,
- *                  inside the fp32 tolerances; the other layers stay fp32.
- *                  The energy+force calls accept it; the unfused pipeline
- *                  returns SN_ERR_UNSUPPORTED.
+ *  SN_FILTER_F16X2 the fp32 model with every MLP product (filter, update,
+ *                  readout) on the fp16 matrix units: each fp32 weight and
+ *                  activation enters as a pair of fp16 numbers hi + lo (22
+ *                  significant bits) after a power-of-two scaling that keeps
+ *                  both parts in fp16's normal range (per matrix; per
+ *                  filter input from bounds derived on the host from the
+ *                  weights and the basis width; per atom for the update and
+ *                  readout inputs), and each product is hi*hi + hi*lo +
+ *                  lo*hi: about 1e-6 relative error per dot product, inside
+ *                  the fp32 tolerances. The energy+force and MD calls accept
+ *                  it; the unfused pipeline returns SN_ERR_UNSUPPORTED.
  * Accumulation is fp32 in every case; positions, distances, basis
  * functions, biases, energies and forces stay fp32. */
 enum { SN_FILTER_F32 = 0, SN_FILTER_BF16 = 1, SN_W16A16 = 2, SN_FILTER_F16X2 = 3 };
