@@ -24,13 +24,16 @@ def test_philox_words_exact(gpu_lib):
     assert np.array_equal(out.cpu().numpy().view(np.uint64).reshape(-1, 4), ref)
 
 
-def _md_setup(lib, name, R, seed=0, gamma=1.0, skin=1.0, rebuild_every=10, filter_f32=True):
+def _md_setup(lib, name, R, seed=0, gamma=1.0, skin=1.0, rebuild_every=10, filter_f32=True,
+              dtype=None):
     import torch
+    from dataclasses import replace
     cfg, pos, types, w = make_config(name, seed=seed, n_replicas=R)
     m = cfg.model
     if filter_f32 and m.filter_dtype != 0:
-        from dataclasses import replace
         m = replace(m, filter_dtype=0)
+    if dtype is not None:
+        m = replace(m, filter_dtype=dtype)
     desc = lib_desc(lib, m)
     system = lib_system(lib, cfg.system, R)
     model = lib.sn_model_create(desc, w)
@@ -43,12 +46,14 @@ def _md_setup(lib, name, R, seed=0, gamma=1.0, skin=1.0, rebuild_every=10, filte
     return cfg, m, pos, types, w, desc, system, model, ws, t, params, state, energy
 
 
-def test_short_trajectory_matches_oracle(gpu_lib):
+@pytest.mark.parametrize("dtype", [0, 3])
+def test_short_trajectory_matches_oracle(gpu_lib, dtype):
     """Ten BAOAB steps of 3 chain replicas with the same Philox stream: the
-    GPU (fp32) and the oracle (fp64) trajectories agree to fp32 accuracy."""
+    GPU (fp32, or the fp32 model on fp16 pairs) and the oracle (fp64)
+    trajectories agree to fp32 accuracy."""
     lib = gpu_lib
     cfg, m, pos, types, w, desc, system, model, ws, t, params, state, energy = _md_setup(
-        lib, "cg269x64", 3)
+        lib, "cg269x64", 3, dtype=dtype)
     try:
         lib.sn_md_init(model, system, t, params, state, energy, ws)
         v0 = state.vel.cpu().double().numpy().reshape(-1, 3)
