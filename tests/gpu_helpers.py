@@ -72,3 +72,37 @@ def assert_energy_forces(E_gpu, F_gpu, E_ref, F_ref, bf16=False, what="", eps_ab
     if bf16:
         assert np.sqrt(np.mean(err ** 2)) <= F_RMS_TOL_BF16 * rms
     return rel.max(), err.max() / rms
+
+
+def cutout_forces(cfg, pos, types, w, m, centre, radius, inner):
+    """Oracle forces of the atoms within `inner` of atom `centre` of a periodic
+    box, from a non-periodic cutout of every atom within `radius` of it.
+
+    An atom's energy depends on positions within T r_c of it, so the force on
+    atom i involves positions within 2 T r_c of i: with radius >= inner +
+    2 T r_c the cutout gives those forces exactly. Positions are unwrapped
+    about the centre by whole box lengths in fp64 (exact), and the cutout's
+    list is the oracle's periodic list restricted to pairs inside it (the
+    same pairs, since every such pair's minimum image is its unwrapped
+    difference)."""
+    L = float(np.float32(cfg.system.box))
+    p = pos.astype(np.float64)
+    u = p - p[centre]
+    shift = L * np.round(u / L)
+    r = np.linalg.norm(u - shift, axis=1)
+    sel = np.nonzero(r < radius)[0]
+    idx = -np.ones(len(pos), np.int64)
+    idx[sel] = np.arange(len(sel))
+    rp, col = oracle.neighbor_list(pos, 1, len(pos), True, cfg.system.box, m.r_cut)
+    rows, cols = [0], []
+    for a in sel:
+        nb = idx[col[rp[a]:rp[a + 1]]]
+        nb = np.sort(nb[nb >= 0])
+        cols.append(nb)
+        rows.append(rows[-1] + len(nb))
+    sub_rp = np.asarray(rows, np.int64)
+    sub_col = np.concatenate(cols)
+    _, Fo = oracle.energy_forces(oracle_desc(m), w, p[sel] - shift[sel], types[sel], sub_rp,
+                                 sub_col, n_replicas=1)
+    keep = r[sel] < inner
+    return sel[keep], Fo[keep]

@@ -4,8 +4,8 @@ import pytest
 
 import oracle
 from gen.configs import CONFIGS, ModelSpec, make_config, make_weights
-from tests.gpu_helpers import (assert_energy_forces, gpu_neighbors, lib_desc, lib_system,
-                               oracle_desc)
+from tests.gpu_helpers import (assert_energy_forces, cutout_forces, gpu_neighbors, lib_desc,
+                               lib_system, oracle_desc)
 
 pytestmark = pytest.mark.gpu
 
@@ -300,51 +300,17 @@ def test_bulk64k_full_invariances(gpu_lib):
     assert np.max(np.abs(F.sum(axis=0))) < 1e-3 * rms * np.sqrt(len(F))
 
 
-def _cutout_forces(cfg, pos, types, w, m, centre, radius, inner):
-    """Oracle forces of the atoms within `inner` of atom `centre` of a periodic
-    box, from a non-periodic cutout of every atom within `radius` of it.
-
-    An atom's energy depends on positions within T r_c of it, so the force on
-    atom i involves positions within 2 T r_c of i: with radius >= inner +
-    2 T r_c the cutout gives those forces exactly. Positions are unwrapped
-    about the centre by whole box lengths in fp64 (exact), and the cutout's
-    list is the oracle's periodic list restricted to pairs inside it (the
-    same pairs, since every such pair's minimum image is its unwrapped
-    difference)."""
-    L = float(np.float32(cfg.system.box))
-    p = pos.astype(np.float64)
-    u = p - p[centre]
-    shift = L * np.round(u / L)
-    r = np.linalg.norm(u - shift, axis=1)
-    sel = np.nonzero(r < radius)[0]
-    idx = -np.ones(len(pos), np.int64)
-    idx[sel] = np.arange(len(sel))
-    rp, col = oracle.neighbor_list(pos, 1, len(pos), True, cfg.system.box, m.r_cut)
-    rows, cols = [0], []
-    for a in sel:
-        nb = idx[col[rp[a]:rp[a + 1]]]
-        nb = np.sort(nb[nb >= 0])
-        cols.append(nb)
-        rows.append(rows[-1] + len(nb))
-    sub_rp = np.asarray(rows, np.int64)
-    sub_col = np.concatenate(cols)
-    _, Fo = oracle.energy_forces(oracle_desc(m), w, p[sel] - shift[sel], types[sel], sub_rp,
-                                 sub_col, n_replicas=1)
-    keep = r[sel] < inner
-    return sel[keep], Fo[keep]
-
-
 def test_bulk64k_sampled_forces_vs_oracle(gpu_lib):
     """The 65,536-atom box at full size, in the bench's launch configuration:
     the forces of the ~250 atoms within 10 A of atom 0, element by element
     against the oracle evaluated on a 40.5 A cutout around it (exact for
-    them, see _cutout_forces), for the fp32 filter and the fp32 model on
+    them, see cutout_forces), for the fp32 filter and the fp32 model on
     fp16 pairs."""
     import dataclasses
     cfg, pos, types, w = make_config("bulk64k")
     m = cfg.model
     assert 40.5 >= 10.0 + 2 * m.T * m.r_cut
-    atoms, Fo = _cutout_forces(cfg, pos, types, w, m, 0, 40.5, 10.0)
+    atoms, Fo = cutout_forces(cfg, pos, types, w, m, 0, 40.5, 10.0)
     assert len(atoms) > 150
     rms = np.sqrt(np.mean(Fo ** 2))
     system = lib_system(gpu_lib, cfg.system)
