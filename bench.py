@@ -399,7 +399,8 @@ def main():
         "data": "synthetic (seeded chains/boxes, random-init weights)",
         "config": {"workload": cfg.name, "replicas": R,
                    "atoms_per_replica": c.system.atoms_per_replica,
-                   "directed_edges": r["ne"], "list_radius_A": r["r_list"], "D": m.D, "Dr": m.Dr,
+                   "directed_edges": r["ne"], "list_radius_A": r["r_list"],
+                   "list_edges": r["ne_list"], "D": m.D, "Dr": m.Dr,
                    "T": m.T, "r_cut_A": m.r_cut,
                    "step": "BAOAB + neighbour rebuild + energy/forces"},
         "replica_steps_per_s": r["replica_steps_per_s"],
@@ -476,11 +477,15 @@ def md_timing(cfg, c, m, pos, types, w, steps, warmup):
         print(f"device status {status} ({L.status_string(status)}), detail {detail}",
               file=sys.stderr)
         sys.exit(1)
-    # edge count on the final positions (untimed)
-    ne = L.sn_build_neighbors(system, state.pos, r_list, state.rowptr, state.col, capacity, ws)
+    # edge counts on the final positions (untimed): the pairs inside the
+    # cutoff are the work (the MD evaluates only those); the list's own size
+    ne_list = L.sn_build_neighbors(system, state.pos, r_list, state.rowptr, state.col, capacity,
+                                   ws)
+    ne = L.sn_build_neighbors(system, state.pos, m.r_cut, state.rowptr, state.col, capacity, ws)
     L.sn_model_destroy(model)
     return {"edges_per_s": ne * steps / elapsed, "ms_per_step": 1000.0 * elapsed / steps,
-            "replica_steps_per_s": R * steps / elapsed, "ne": ne, "r_list": r_list,
+            "replica_steps_per_s": R * steps / elapsed, "ne": ne, "ne_list": ne_list,
+            "r_list": r_list,
             "bwd_ms": bwd_ms, "bwd_n": bwd_n, "fwd_ms": fwd_ms, "fwd_n": fwd_n,
             "n_rebuilds": n_rebuilds}
 

@@ -218,7 +218,15 @@ typedef struct {
 /* Caller-owned MD state; every pointer is a device buffer of R*N*3 floats,
  * except rowptr (R*N+1 int32) and col (edge_capacity int32). `step` counts the
  * steps taken so far and keys the noise: restoring (pos, vel, forces,
- * pos_at_build, rowptr, col, step) replays the same trajectory bit for bit. */
+ * pos_at_build, rowptr, col, step) replays the same trajectory bit for bit.
+ * rowptr_active (R*N+1 int32) and col_active (edge_capacity int32) are
+ * optional, both NULL or both set: when set, the MD calls copy from the skin
+ * list (rowptr, col), after every drift, the pairs closer than
+ * r_cut (1 + 2^-10) by the list's own membership test, and evaluate energies
+ * and forces on those. Listed pairs at or beyond r_cut contribute nothing,
+ * so the results are the skin list's (up to the order of the force sums)
+ * for less work; the active list is rebuilt from the state each step and
+ * needs no restoring. Skins below r_cut 2^-10 skip the copy. */
 typedef struct {
   float* pos;
   float* vel;
@@ -228,6 +236,8 @@ typedef struct {
   int32_t* col;
   int64_t edge_capacity;
   uint64_t step;
+  int32_t* rowptr_active;
+  int32_t* col_active;
 } sn_md_state;
 
 /* Draws Maxwell-Boltzmann velocities (Philox counter (atom, 0, 1, 0)), builds

@@ -52,7 +52,8 @@ class SnMdParams(ctypes.Structure):
 class SnMdState(ctypes.Structure):
     _fields_ = [("pos", c_void_p), ("vel", c_void_p), ("forces", c_void_p),
                 ("pos_at_build", c_void_p), ("rowptr", c_void_p), ("col", c_void_p),
-                ("edge_capacity", c_int64), ("step", c_uint64)]
+                ("edge_capacity", c_int64), ("step", c_uint64),
+                ("rowptr_active", c_void_p), ("col_active", c_void_p)]
 
 
 class SnError(RuntimeError):
@@ -251,9 +252,10 @@ def make_md_params(dt_fs=2.0, temperature_K=300.0, gamma_per_ps=1.0, mass_amu=10
 
 
 class MdState:
-    """Device tensors of the MD state plus the host step counter."""
+    """Device tensors of the MD state plus the host step counter; with
+    active=True also the buffers of the per-step active list."""
 
-    def __init__(self, pos, edge_capacity: int, step: int = 0):
+    def __init__(self, pos, edge_capacity: int, step: int = 0, active: bool = True):
         import torch
         n3 = pos.numel()
         dev = pos.device
@@ -265,11 +267,19 @@ class MdState:
         self.col = torch.zeros(max(int(edge_capacity), 1), dtype=torch.int32, device=dev)
         self.edge_capacity = int(edge_capacity)
         self.step = int(step)
+        self.rowptr_active = self.col_active = None
+        if active:
+            self.rowptr_active = torch.zeros(n3 // 3 + 1, dtype=torch.int32, device=dev)
+            self.col_active = torch.zeros(max(int(edge_capacity), 1), dtype=torch.int32,
+                                          device=dev)
 
     def as_c(self) -> SnMdState:
+        act = self.rowptr_active is not None
         return SnMdState(self.pos.data_ptr(), self.vel.data_ptr(), self.forces.data_ptr(),
                          self.pos_at_build.data_ptr(), self.rowptr.data_ptr(), self.col.data_ptr(),
-                         self.edge_capacity, self.step)
+                         self.edge_capacity, self.step,
+                         self.rowptr_active.data_ptr() if act else None,
+                         self.col_active.data_ptr() if act else None)
 
 
 def sn_md_init(model, system: SnSystem, types, params: SnMdParams, state: MdState, energy,

@@ -374,7 +374,26 @@ bool md_setup(const sn_model* m, const sn_system* sys, const sn_md_params* prm, 
 
 bool state_ok(const sn_md_state* st) {
   return st && st->pos && st->vel && st->forces && st->pos_at_build && st->rowptr && st->col &&
-         st->edge_capacity >= 0 && st->edge_capacity <= INT32_MAX;
+         st->edge_capacity >= 0 && st->edge_capacity <= INT32_MAX &&
+         (st->rowptr_active == nullptr) == (st->col_active == nullptr);
+}
+
+// The list the MD calls evaluate: the active list (pairs inside r_cut plus a
+// margin of 2^-10 r_cut, far above the rounding of the kernels' distances),
+// copied from the skin list after the drift when the state provides its
+// buffers and the skin is wider than the margin; the skin list otherwise.
+hipError_t md_eval_list(const sn_model* m, const sn_md_params* prm, const NbrGeom& g,
+                        const sn_md_state* state, char* w, const WsLayout& L, hipStream_t s,
+                        const int32_t*& rp, const int32_t*& cl) {
+  rp = state->rowptr;
+  cl = state->col;
+  const double margin = (double)m->desc.r_cut / 1024.0;
+  if (!state->rowptr_active || !((double)prm->skin > margin)) return hipSuccess;
+  const double rk = (double)(float)((double)m->desc.r_cut + margin);
+  rp = state->rowptr_active;
+  cl = state->col_active;
+  return launch_active_list(g, state->pos, state->rowptr, state->col, rk * rk,
+                            state->rowptr_active, state->col_active, w, L, s);
 }
 
 } // namespace
@@ -636,9 +655,10 @@ sn_status sn_md_init(const sn_model* m, const sn_system* sys, const int32_t* typ
     e = launch_build_neighbors(g, state->pos, state->rowptr, state->col, state->edge_capacity, w, L,
                                nullptr, 0, s);
   if (e == hipSuccess) e = launch_md_mark_build(n, state->pos, state->pos_at_build, st, nullptr, 0, s);
+  const int32_t *rp = nullptr, *cl = nullptr;
+  if (e == hipSuccess) e = md_eval_list(m, prm, g, state, w, L, s, rp, cl);
   if (e != hipSuccess) return SN_ERR_HIP;
-  return energy_forces_impl(m, sys, state->pos, types, state->rowptr, state->col, e_out,
-                            state->forces, w, s);
+  return energy_forces_impl(m, sys, state->pos, types, rp, cl, e_out, state->forces, w, s);
 }
 
 sn_status sn_md_step(const sn_model* m, const sn_system* sys, const int32_t* types,
@@ -670,9 +690,10 @@ sn_status sn_md_step(const sn_model* m, const sn_system* sys, const int32_t* typ
     e = launch_build_neighbors(g, state->pos, state->rowptr, state->col, state->edge_capacity, w, L,
                                gate, gval, s);
     if (e == hipSuccess) e = launch_md_mark_build(n, state->pos, state->pos_at_build, st, gate, gval, s);
+    const int32_t *rp = nullptr, *cl = nullptr;
+    if (e == hipSuccess) e = md_eval_list(m, prm, g, state, w, L, s, rp, cl);
     if (e != hipSuccess) return SN_ERR_HIP;
-    rc = energy_forces_impl(m, sys, state->pos, types, state->rowptr, state->col, e_out,
-                            state->forces, w, s);
+    rc = energy_forces_impl(m, sys, state->pos, types, rp, cl, e_out, state->forces, w, s);
     if (rc != SN_OK) return rc;
     e = launch_md_b(su.c, n, state->vel, state->forces, s);
     if (e != hipSuccess) return SN_ERR_HIP;

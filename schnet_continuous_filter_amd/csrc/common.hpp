@@ -89,6 +89,12 @@ hipError_t launch_build_neighbors(const NbrGeom& g, const float* pos, int32_t* r
                                   const WsLayout& L, const int64_t* gate, int64_t gate_val,
                                   hipStream_t s);
 
+// Rows of (rowptr, col) restricted to the pairs inside sqrt(r2) by the same
+// membership test, same order, into (out_rowptr [n+1], out_col) (nbr.hip).
+hipError_t launch_active_list(const NbrGeom& g, const float* pos, const int32_t* rowptr,
+                              const int32_t* col, double r2, int32_t* out_rowptr,
+                              int32_t* out_col, char* ws, const WsLayout& L, hipStream_t s);
+
 // Scan (nbr.hip): in-place exclusive scan of a[0..n) into a[0..n], a[n] = total.
 hipError_t launch_exclusive_scan(int32_t* a, int64_t n, int32_t* blocks, DevStatus* st,
                                  int64_t capacity, const int64_t* gate, int64_t gate_val,

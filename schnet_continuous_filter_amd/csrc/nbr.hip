@@ -316,6 +316,69 @@ __global__ __launch_bounds__(kThreads) void k_sort_rows(const int32_t* rowptr, i
   }
 }
 
+// ------------------------------------------------------------------ active list
+// The rows of a list restricted to the pairs that pass the membership test at
+// a smaller radius, in the same order. Each row is taken by LPR lanes (64 /
+// LPR rows per wave: rows are short) that test LPR listed senders at a time;
+// a ballot compacts the kept ones within the row's lane group. The count pass
+// (FILL false) writes row lengths into out_rowptr, the fill pass the senders
+// at the scanned offsets.
+template <bool FILL, int LPR>
+__global__ __launch_bounds__(kThreads) void k_active(const float* __restrict__ pos, int64_t n_tot,
+                                                     int periodic, double L, double half,
+                                                     double r2, const int32_t* __restrict__ rowptr,
+                                                     const int32_t* __restrict__ col,
+                                                     int32_t* out_rowptr, int32_t* out_col) {
+  const int lane = threadIdx.x & 63, sub = lane % LPR, grp = lane / LPR;
+  const int64_t r = ((int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) * (64 / LPR) + grp;
+  const bool row_ok = r < n_tot;
+  const int b = row_ok ? rowptr[r] : 0, e = row_ok ? rowptr[r + 1] : 0;
+  float xi = 0.f, yi = 0.f, zi = 0.f;
+  if (row_ok) {
+    xi = pos[3 * r + 0];
+    yi = pos[3 * r + 1];
+    zi = pos[3 * r + 2];
+  }
+  const uint64_t gmask = (LPR == 64 ? ~0ull : ((1ull << LPR) - 1ull)) << (grp * LPR);
+  const uint64_t below = ((1ull << lane) - 1ull) & gmask;
+  int64_t out = (FILL && row_ok) ? (int64_t)out_rowptr[r] : 0;
+  // every lane group of the wave loops as long as its longest row needs
+  int len = e - b;
+  for (int o = LPR; o < 64; o <<= 1) len = max(len, __shfl_xor(len, o, 64));
+  for (int k0 = 0; k0 < len; k0 += LPR) {
+    const int k = b + k0 + sub;
+    bool in = false;
+    int j = 0;
+    if (k < e) {
+      j = col[k];
+      const float* pj = pos + 3 * (int64_t)j;
+      in = pair_in(xi, yi, zi, pj[0], pj[1], pj[2], periodic, L, half, r2);
+    }
+    const uint64_t m = __ballot(in);
+    if (FILL && in) out_col[out + __popcll(m & below)] = j;
+    out += __popcll(m & gmask);
+  }
+  if (!FILL && row_ok && sub == 0) out_rowptr[r] = (int32_t)out;
+}
+
+hipError_t launch_active_list(const NbrGeom& g, const float* pos, const int32_t* rowptr,
+                              const int32_t* col, double r2, int32_t* out_rowptr,
+                              int32_t* out_col, char* ws, const WsLayout& L, hipStream_t s) {
+  constexpr int LPR = 16;
+  DevStatus* st = reinterpret_cast<DevStatus*>(ws + L.status);
+  int32_t* scan_blocks = reinterpret_cast<int32_t*>(ws + L.scan_blocks);
+  const int64_t n_tot = (int64_t)g.n_rep * g.n_per;
+  const int64_t rows_per_block = (kThreads / 64) * (64 / LPR);
+  const dim3 grid((unsigned)((n_tot + rows_per_block - 1) / rows_per_block));
+  hipLaunchKernelGGL((k_active<false, LPR>), grid, dim3(kThreads), 0, s, pos, n_tot, g.periodic,
+                     g.L, g.half, r2, rowptr, col, out_rowptr, out_col);
+  hipError_t e = launch_exclusive_scan(out_rowptr, n_tot, scan_blocks, st, -1, nullptr, 0, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_active<true, LPR>), grid, dim3(kThreads), 0, s, pos, n_tot, g.periodic,
+                     g.L, g.half, r2, rowptr, col, out_rowptr, out_col);
+  return hipGetLastError();
+}
+
 static unsigned blocks_for(int64_t n) { return (unsigned)((n + kThreads - 1) / kThreads); }
 
 hipError_t launch_build_neighbors(const NbrGeom& g, const float* pos, int32_t* rowptr, int32_t* col,

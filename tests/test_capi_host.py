@@ -90,6 +90,11 @@ def test_invalid_arguments_rejected_on_host(lib):
                 lib.make_md_params(rebuild_every=0)):
         assert L.sn_md_step(dummy, ctypes.byref(good), dummy, ctypes.byref(prm), ctypes.byref(st),
                             1, None, dummy, 10**9, None) == lib.SN_ERR_INVALID_ARG
+    # an active list needs both of its buffers
+    half = lib.SnMdState(256, 256, 256, 256, 256, 256, 10, 0, 256, None)
+    prm = lib.make_md_params()
+    assert L.sn_md_step(dummy, ctypes.byref(good), dummy, ctypes.byref(prm), ctypes.byref(half), 1,
+                        None, dummy, 10**9, None) == lib.SN_ERR_INVALID_ARG
     assert L.sn_philox4x64_10(None, 0, 0, None, -1, None) == lib.SN_ERR_INVALID_ARG
     assert L.sn_get_device_status(None, 0, None, None, None, None) == lib.SN_ERR_INVALID_ARG
     zero = ctypes.c_int64()

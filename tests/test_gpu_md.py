@@ -25,7 +25,7 @@ def test_philox_words_exact(gpu_lib):
 
 
 def _md_setup(lib, name, R, seed=0, gamma=1.0, skin=1.0, rebuild_every=10, filter_f32=True,
-              dtype=None):
+              dtype=None, active=True):
     import torch
     from dataclasses import replace
     cfg, pos, types, w = make_config(name, seed=seed, n_replicas=R)
@@ -41,7 +41,7 @@ def _md_setup(lib, name, R, seed=0, gamma=1.0, skin=1.0, rebuild_every=10, filte
     p = torch.from_numpy(pos).cuda().reshape(-1)
     t = torch.from_numpy(types).cuda()
     params = lib.make_md_params(2.0, 300.0, gamma, 100.0, skin, rebuild_every, 42)
-    state = lib.MdState(p, 400 * len(pos))
+    state = lib.MdState(p, 400 * len(pos), active=active)
     energy = torch.empty(R, dtype=torch.float32, device="cuda")
     return cfg, m, pos, types, w, desc, system, model, ws, t, params, state, energy
 
@@ -179,3 +179,58 @@ def test_zero_model_keeps_temperature(gpu_lib):
         assert abs(ke.mean() / (1.5 * oracle.md.KB * 300.0) - 1) < 0.03
     finally:
         lib.sn_model_destroy(model)
+
+
+def test_active_list(gpu_lib):
+    """The per-step active list: at initialisation it is exactly the oracle's
+    list at r_cut (1 + 2^-10); after 25 steps (with rebuilds and without) it
+    holds every pair inside r_cut and none beyond the keep radius, each row
+    in the skin list's order; and trajectories with and without it agree to
+    rounding (listed pairs beyond r_cut contribute nothing)."""
+    import torch
+    lib = gpu_lib
+    R = 4
+    cfg, m, pos, types, w, desc, system, model, ws, t, params, state, energy = _md_setup(
+        lib, "md1024", R, filter_f32=False, rebuild_every=10)
+    N = cfg.system.atoms_per_replica
+    r_keep = float(np.float32(m.r_cut + m.r_cut / 1024.0))
+    try:
+        lib.sn_md_init(model, system, t, params, state, energy, ws)
+        torch.cuda.synchronize()
+        rp_a = state.rowptr_active.cpu().numpy()
+        col_a = state.col_active[:rp_a[-1]].cpu().numpy()
+        rp_o, col_o = oracle.neighbor_list(state.pos.cpu().numpy().reshape(-1, 3), R, N, False,
+                                           0.0, r_keep)
+        assert np.array_equal(rp_a, rp_o) and np.array_equal(col_a, col_o)
+        lib.sn_md_step(model, system, t, params, state, 25, energy, ws)
+        torch.cuda.synchronize()
+        assert lib.sn_get_device_status(ws)[0] == 0
+        p_now = state.pos.cpu().numpy().reshape(-1, 3)
+        rp_a = state.rowptr_active.cpu().numpy()
+        col_a = state.col_active[:rp_a[-1]].cpu().numpy()
+        rp_s = state.rowptr.cpu().numpy()
+        col_s = state.col[:rp_s[-1]].cpu().numpy()
+        rp_c, col_c = oracle.neighbor_list(p_now, R, N, False, 0.0, m.r_cut)
+        rp_k, col_k = oracle.neighbor_list(p_now, R, N, False, 0.0, r_keep)
+        for i in range(R * N):
+            a = col_a[rp_a[i]:rp_a[i + 1]]
+            assert set(col_c[rp_c[i]:rp_c[i + 1]]) <= set(a) <= set(col_k[rp_k[i]:rp_k[i + 1]])
+            s = list(col_s[rp_s[i]:rp_s[i + 1]])
+            assert [s.index(j) for j in a] == sorted(s.index(j) for j in a)
+        E_act = energy.cpu().double().numpy()
+        P_act = p_now.astype(np.float64)
+    finally:
+        lib.sn_model_destroy(model)
+    cfg, m, pos, types, w, desc, system, model, ws, t, params, state, energy = _md_setup(
+        lib, "md1024", R, filter_f32=False, rebuild_every=10, active=False)
+    try:
+        lib.sn_md_init(model, system, t, params, state, energy, ws)
+        lib.sn_md_step(model, system, t, params, state, 25, energy, ws)
+        torch.cuda.synchronize()
+        E_full = energy.cpu().double().numpy()
+        P_full = state.pos.cpu().double().numpy().reshape(-1, 3)
+    finally:
+        lib.sn_model_destroy(model)
+    disp = np.max(np.abs(P_full - pos))
+    assert np.max(np.abs(P_act - P_full)) < 1e-3 * disp
+    assert np.all(np.abs(E_act - E_full) <= 1e-4 * np.abs(E_full))
