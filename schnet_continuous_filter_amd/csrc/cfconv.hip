@@ -303,8 +303,8 @@ __device__ __forceinline__ void gemm1_plain(f32x4 (&acc)[NA][D / 16], const unsi
   asm volatile("" : "+v"(step));
   const int k0 = PL * grp;
   const float coef2 = p.rbf_coef2, inv_s2 = p.rbf_inv_s2;
-#pragma unroll 1
-  for (int c = 0; c < p.KC; ++c) {
+  // one chunk of basis functions: evaluate, then accumulate its products
+  auto chunk = [&](int c) {
     float b[NA][PL];
     if constexpr (H16) {
       // the lane's 8 consecutive centres: one exp for the first Gaussian and
@@ -362,6 +362,16 @@ __device__ __forceinline__ void gemm1_plain(f32x4 (&acc)[NA][D / 16], const unsi
           for (int q = 0; q < NA; ++q) acc[q][nb] = mfma16(w[u], b[q][u], acc[q][nb]);
       }
     }
+  };
+  if constexpr (H16) {
+    // the 16-bit layouts always run KP / 32 chunks (p.KC): a compile-time
+    // count lets the first chunk's products start from a zero accumulator
+    // operand instead of zeroed registers
+#pragma unroll
+    for (int c = 0; c < KP / 32; ++c) chunk(c);
+  } else {
+#pragma unroll 1
+    for (int c = 0; c < p.KC; ++c) chunk(c);
   }
 }
 
