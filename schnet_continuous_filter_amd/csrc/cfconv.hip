@@ -370,8 +370,10 @@ __device__ __forceinline__ void gemm1_plain(f32x4 (&acc)[NA][D / 16], const unsi
 #pragma unroll
     for (int c = 0; c < KP / 32; ++c) chunk(c);
   } else {
+    // the first chunk peeled for the same reason (KC >= 1)
+    chunk(0);
 #pragma unroll 1
-    for (int c = 0; c < p.KC; ++c) chunk(c);
+    for (int c = 1; c < p.KC; ++c) chunk(c);
   }
 }
 
