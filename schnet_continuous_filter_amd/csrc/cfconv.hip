@@ -398,15 +398,15 @@ __device__ __forceinline__ void gemm1_split(f32x4 (&acc)[NA][D / 16], const unsi
       // d - mu_k with one rounding, as the fp32 path
       const float z = __builtin_fmaf(-(float)(32 * c + 8 * grp + t), step, g.d0);
       const float gs = g.in * __builtin_amdgcn_exp2f(coef2 * z * z);
-      // each basis value is pinned before it is split: hi and lo must both
-      // come from the one rounded float (a product contracted into either
-      // conversion would be rounded differently for each part)
+      // the hi part is pinned: the lo part must be taken against the very hi
+      // that is stored (the compiler may form either from the rounded or the
+      // exact product; with one hi, hi + lo represents the value either way)
       float b[NA];
-      b[0] = pinned(gs * Ca);
-      if constexpr (NA == 2) b[1] = pinned(gs * (Cpa - z * Cia));
+      b[0] = gs * Ca;
+      if constexpr (NA == 2) b[1] = gs * (Cpa - z * Cia);
 #pragma unroll
       for (int q = 0; q < NA; ++q) {
-        const _Float16 h = (_Float16)b[q];
+        const _Float16 h = pinned((_Float16)b[q]);
         bh[c][q][t] = h;
         bl[c][q][t] = (_Float16)(b[q] - (float)h);
       }

@@ -47,6 +47,11 @@ __device__ __forceinline__ float pinned(float v) {
   return v;
 }
 
+__device__ __forceinline__ _Float16 pinned(_Float16 v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // Orders this wave's LDS writes before its later LDS reads (wave-private data).
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
