@@ -689,26 +689,26 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, false>()), 1) void k_cf_fwd(CfPa
 #pragma unroll
     for (int b = 0; b < 4; ++b) xg[b] = bload4(rx, xo + (uint32_t)(64 * b));
     __builtin_amdgcn_sched_barrier(0);
-    f32x4 w[NB];
-    {
-      const auto os = W2Op<D, PR>::make(s[0], ss.a[2]);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        w[nb] = f32x4{};
-        gemm2_block<P>(w[nb], os, lds, nb, wl);
-      }
-    }
+    // the products of each 64 features are formed right before their
+    // messages (fewer live accumulators)
+    const auto os = W2Op<D, PR>::make(s[0], ss.a[2]);
 #pragma unroll
     for (int pss = 0; pss < NB / 4; ++pss) {
+      f32x4 w[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        w[b] = f32x4{};
+        gemm2_block<P>(w[b], os, lds, 4 * pss + b, wl);
+      }
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int nb = 4 * pss + b;
         const f32x4 c2 = bias4<P>(p, lds, g4, D + 16 * nb);
-        if constexpr (PR == PREC_F16S) w[nb] *= scale4<P>(p, lds, g4, D + 16 * nb);
-        if constexpr (PR == PREC_F16X2) w[nb] *= ss.u[2];
+        if constexpr (PR == PREC_F16S) w[b] *= scale4<P>(p, lds, g4, D + 16 * nb);
+        if constexpr (PR == PREC_F16X2) w[b] *= ss.u[2];
         f32x4 m;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) m[r] = xg[b][r] * (g.in * (w[nb][r] + c2[r]));
+        for (int r = 0; r < 4; ++r) m[r] = xg[b][r] * (g.in * (w[b][r] + c2[r]));
         tile_put(Tb, b, m, tl);
         if (pss + 1 < NB / 4) xg[b] = bload4(rx, xo + (uint32_t)(64 * (nb + 4)));
       }
