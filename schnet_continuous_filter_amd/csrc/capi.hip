@@ -147,6 +147,8 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
   DevStatus* st = reinterpret_cast<DevStatus*>(ws + L.status);
   int32_t* wg_start = reinterpret_cast<int32_t*>(ws + L.wg_start);
   int32_t* wg_start_b = reinterpret_cast<int32_t*>(ws + L.wg_start_b);
+  int32_t* wg_edge = reinterpret_cast<int32_t*>(ws + L.wg_edge);
+  int32_t* wg_edge_b = reinterpret_cast<int32_t*>(ws + L.wg_edge_b);
   float* x = reinterpret_cast<float*>(ws + L.x);
   float* au = reinterpret_cast<float*>(ws + L.au);
   float* gbuf = reinterpret_cast<float*>(ws + L.gbuf);
@@ -162,9 +164,10 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
   hipError_t e;
 
   if (!uf) {
-    if ((e = launch_partition(rowptr, (int)n, Gf * wf, wg_start, st, s)) != hipSuccess)
+    if ((e = launch_partition(rowptr, (int)n, Gf * wf, wg_start, wg_edge, st, s)) != hipSuccess)
       return hip_fail(e);
-    if ((e = launch_partition(rowptr, (int)n, Gb * wb, wg_start_b, st, s)) != hipSuccess)
+    if ((e = launch_partition(rowptr, (int)n, Gb * wb, wg_start_b, wg_edge_b, st, s)) !=
+        hipSuccess)
       return hip_fail(e);
   }
   if ((e = launch_embed(types, m->w + m->off_emb, (int)n, D, d.n_types, x, st, s)) != hipSuccess)
@@ -175,6 +178,10 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
   p.col = col;
   p.pos = pos;
   p.wg_start = wg_start;
+  p.wg_edge = wg_edge;
+  p.side_recv = reinterpret_cast<int32_t*>(ws + L.side_recv);
+  p.side_h = reinterpret_cast<float*>(ws + L.side_h);
+  p.side_f = reinterpret_cast<float*>(ws + L.side_f);
   p.n_atoms = (int)n;
   p.periodic = sys->periodic;
   p.box = sys->box;
@@ -269,14 +276,19 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
   for (int t = 0; t < T; ++t) {
     p.img = block_img(t);
     p.wg_start = wg_start;
+    p.wg_edge = wg_edge;
     p.x = x + t * ND;
     p.h = gbuf;
     if (uf) {
       ua.h = gbuf;
       if ((e = uf_block(t, UF_FORWARD)) != hipSuccess) return hip_fail(e);
     } else {
-      ProfScope ps(0, s);
-      if ((e = launch_cf_forward(D, m->KP, prec, p, Gf, s)) != hipSuccess) return hip_fail(e);
+      {
+        ProfScope ps(0, s);
+        if ((e = launch_cf_forward(D, m->KP, prec, p, Gf, s)) != hipSuccess) return hip_fail(e);
+      }
+      if ((e = launch_cf_fixup(p, Gf * wf, D, gbuf, nullptr, s)) != hipSuccess)
+        return hip_fail(e);
     }
     AtomArgs u{ATOM_UPDATE_FWD, (int)n, gbuf, nullptr, nullptr, x + t * ND, nullptr, au + t * ND,
                x + (t + 1) * ND, 0.f, nullptr, atom_img(t, 0)};
@@ -298,6 +310,7 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
     if ((e = launch_atom(b, D, D, prec, m->n_cu, s)) != hipSuccess) return hip_fail(e);
     p.img = block_img(t);
     p.wg_start = wg_start_b;
+    p.wg_edge = wg_edge_b;
     p.x = x + t * ND;
     p.gh = gbuf;
     p.q_out = t > 0 ? tmp : nullptr;
@@ -307,8 +320,13 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
       ua.q = t > 0 ? tmp : nullptr;
       if ((e = uf_block(t, UF_BACKWARD)) != hipSuccess) return hip_fail(e);
     } else {
-      ProfScope ps(1, s);
-      if ((e = launch_cf_backward(D, m->KP, prec, p, Gb, s)) != hipSuccess) return hip_fail(e);
+      {
+        ProfScope ps(1, s);
+        if ((e = launch_cf_backward(D, m->KP, prec, p, Gb, s)) != hipSuccess)
+          return hip_fail(e);
+      }
+      if ((e = launch_cf_fixup(p, Gb * wb, D, p.q_out, p.forces, s)) != hipSuccess)
+        return hip_fail(e);
     }
   }
   // the unfused pipeline accumulates dE/dr of every block into one array
@@ -409,6 +427,11 @@ WsLayout ws_layout(int64_t n, int D, int T, int H) {
   L.status = take(sizeof(DevStatus));
   L.wg_start = take((size_t)(kMaxWorkers + 1) * 4);
   L.wg_start_b = take((size_t)(kMaxWorkers + 1) * 4);
+  L.wg_edge = take((size_t)(kMaxWorkers + 1) * 4);
+  L.wg_edge_b = take((size_t)(kMaxWorkers + 1) * 4);
+  L.side_recv = take((size_t)kMaxWorkers * 4);
+  L.side_h = take((size_t)kMaxWorkers * (size_t)D * 4);
+  L.side_f = take((size_t)kMaxWorkers * 3 * 4);
   L.scan_blocks = take((size_t)(scan_n / kScanChunk + 2) * 8);
   L.cell_count = take((size_t)(ncell + 1) * 4);
   L.cell_start = take((size_t)ncell * 4);

@@ -11,8 +11,11 @@
 //
 // Work decomposition. Every wave is an independent worker: a work-group
 // copies the filter weights into LDS once, which is its only barrier; then
-// each of its waves walks its own contiguous range of receivers (k_partition
-// balances edges + receivers over the workers) in tiles of 16 edges.
+// each of its waves walks its own contiguous range of edges in tiles of 16
+// (k_partition gives every worker the same number of whole tiles, to one).
+// A receiver whose edges a worker boundary cuts is written by the worker
+// holding its last edge; the earlier workers leave their parts in side
+// buffers, which k_cf_fixup adds in worker order (no atomics; fixed order).
 //
 // Edge-on-lane products. Every product is computed transposed,
 // OUT^T[n][e] = sum_k W^T[n][k] IN^T[k][e], on 16x16 MFMA blocks: the weights
@@ -571,21 +574,34 @@ __device__ __forceinline__ void column_segments(const CfParams& p, float* Tb, in
 }
 
 // ------------------------------------------------------------------ kernels
-// Per-worker state shared by the forward and backward walks.
+// Per-worker state shared by the forward and backward walks: the worker's
+// range index, its edges [E0, E1) (whole tiles), its receivers [ia, ib) and
+// whether the last of them continues past E1 (tail: its part here goes to
+// the side buffers). The first receiver may have started before E0.
 struct Walk {
-  int ia, ib, E0, E1;
+  int rid, ia, ib, E0, E1;
+  bool tail;
   __amdgpu_buffer_rsrc_t rrow, rcol, rpos;
 };
 
+// The four waves a SIMD holds (waves w, w + 4, ... of a work-group; waves
+// are placed on the SIMDs in turn) take consecutive ranges, so that each
+// SIMD's share of tiles is balanced to one tile.
 template <class P>
 __device__ __forceinline__ bool worker_range(const CfParams& p, int wave, Walk& w) {
   const uint32_t N = (uint32_t)p.n_atoms;
-  const int wid = (int)blockIdx.x * P::NW + wave;
-  w.ia = cload(p.wg_start, wid);
-  w.ib = cload(p.wg_start, wid + 1);
-  if (w.ia >= w.ib) return false;
-  w.E0 = cload(p.rowptr, w.ia);
-  w.E1 = cload(p.rowptr, w.ib);
+  w.rid = (int)blockIdx.x * P::NW + (wave & 3) * (P::NW / 4) + (wave >> 2);
+  w.ia = cload(p.wg_start, w.rid);
+  const int ia1 = cload(p.wg_start, w.rid + 1);
+  w.E0 = cload(p.wg_edge, w.rid);
+  w.E1 = cload(p.wg_edge, w.rid + 1);
+  // the next worker's first receiver, if it started before E1, is ours too
+  w.tail = cload(p.rowptr, ia1) < w.E1;
+  w.ib = ia1 + (w.tail ? 1 : 0);
+  if (w.ia >= w.ib) {
+    if ((threadIdx.x & 63) == 0) p.side_recv[w.rid] = -1;
+    return false;
+  }
   w.rrow = rsrc(p.rowptr, (N + 1) * 4u);
   w.rcol = rsrc(p.col, (uint32_t)cload(p.rowptr, (int)N) * 4u);
   w.rpos = rsrc(p.pos, N * 12u);
@@ -721,9 +737,17 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, false>()), 1) void k_cf_fwd(CfPa
     cur = th.ncur;
     win = th.win_next;
   }
-  // receivers of a worker without edges
-  for (int i = cur; i < ib; ++i)
+  // receivers of the worker left without edges; an open tail receiver
+  // (cur = ib - 1) leaves its partial sums to the side buffer
+  const int zend = wk.tail ? ib - 1 : ib;
+  for (int i = cur; i < zend; ++i)
     for (int c = lane; c < D; c += 64) p.h[(size_t)i * D + c] = 0.f;
+  if (wk.tail) {
+#pragma unroll
+    for (int pss = 0; pss < NB / 4; ++pss)
+      p.side_h[(size_t)wk.rid * D + 64 * pss + fcol] = carry[pss];
+  }
+  if (lane == 0) p.side_recv[wk.rid] = wk.tail ? ib - 1 : -1;
 }
 
 template <int D, int KP, int PR>
@@ -923,45 +947,99 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, true>()), 1) void k_cf_bwd(CfPar
     cur = th.ncur;
     win = th.win_next;
   }
-  // receivers of a worker without edges
-  for (int i = cur; i < ib; ++i) {
+  // receivers of the worker left without edges; an open tail receiver
+  // (cur = ib - 1) leaves its partial sums to the side buffers
+  const int zend = wk.tail ? ib - 1 : ib;
+  for (int i = cur; i < zend; ++i) {
     if (want_q)
       for (int c = lane; c < D; c += 64) p.q_out[(size_t)i * D + c] = 0.f;
     if (lane < 3) p.forces[(size_t)i * 3 + lane] = 0.f;
   }
+  if (wk.tail) {
+    if (want_q) {
+#pragma unroll
+      for (int pss = 0; pss < NB / 4; ++pss)
+        p.side_h[(size_t)wk.rid * D + 64 * pss + fcol] = carry[pss];
+    }
+    if (lane < 3)
+      p.side_f[(size_t)wk.rid * 3 + lane] = lane == 0 ? fcarry[0] : (lane == 1 ? fcarry[1] : fcarry[2]);
+  }
+  if (lane == 0) p.side_recv[wk.rid] = wk.tail ? ib - 1 : -1;
 }
 
 // ------------------------------------------------------------------ small kernels
-// Worker w owns receivers [wg_start[w], wg_start[w+1]); boundaries split the
-// monotone key rowptr[i] + i (edges plus one unit per receiver) evenly.
-// The kernels address the edge list with 32-bit byte offsets: a list of
-// kMaxListEdges or more edges is refused through the status word.
+// Worker w takes the edges [wg_edge[w], wg_edge[w + 1]) in whole tiles:
+// wg_edge[w] = 16 floor(w T / G) with T = ceil(E / 16) tiles, so every
+// worker runs floor(T / G) or ceil(T / G) of them. Its receivers start at the
+// one holding edge wg_edge[w] (which may have started in an earlier worker),
+// or, where wg_edge[w] falls on a receiver boundary, at the first receiver
+// starting there (empty receivers at a boundary belong to the worker that
+// starts there). The kernels address the edge list with 32-bit byte offsets:
+// a list of kMaxListEdges or more edges is refused through the status word.
 constexpr int64_t kMaxListEdges = (int64_t)1 << 30;
 __global__ void k_partition(const int32_t* rowptr, int N, int G, int32_t* wg_start,
-                            DevStatus* st) {
+                            int32_t* wg_edge, DevStatus* st) {
   const int w = blockIdx.x * blockDim.x + threadIdx.x;
   if (w > G) return;
-  if (w == 0) {
-    if ((int64_t)rowptr[N] >= kMaxListEdges) dev_fail(st, SN_ERR_UNSUPPORTED, rowptr[N]);
-    wg_start[0] = 0;
+  const int64_t E = rowptr[N];
+  if (w == 0 && E >= kMaxListEdges) dev_fail(st, SN_ERR_UNSUPPORTED, E);
+  if (w == G) {
+    wg_start[G] = N;
+    wg_edge[G] = (int32_t)E;
     return;
   }
-  if (w == G) { wg_start[G] = N; return; }
-  const int64_t total = (int64_t)rowptr[N] + N;
-  const int64_t target = (total * w + G - 1) / G;
-  int lo = 0, hi = N;
+  const int64_t T = (E + 15) / 16;
+  const int64_t e0 = min((int64_t)16 * (((int64_t)w * T) / G), E);
+  int lo = 0, hi = N;   // first r with rowptr[r] >= e0 (rowptr[N] = E >= e0)
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
-    if ((int64_t)rowptr[mid] + mid >= target) hi = mid;
+    if ((int64_t)rowptr[mid] >= e0) hi = mid;
     else lo = mid + 1;
   }
-  wg_start[w] = lo;
+  wg_start[w] = ((int64_t)rowptr[lo] > e0) ? lo - 1 : lo;   // lo >= 1 there
+  wg_edge[w] = (int32_t)e0;
 }
 
 hipError_t launch_partition(const int32_t* rowptr, int n_atoms, int G, int32_t* wg_start,
-                            DevStatus* st, hipStream_t s) {
+                            int32_t* wg_edge, DevStatus* st, hipStream_t s) {
   hipLaunchKernelGGL(k_partition, dim3((G + 1 + kThreads - 1) / kThreads), dim3(kThreads), 0, s,
-                     rowptr, n_atoms, G, wg_start, st);
+                     rowptr, n_atoms, G, wg_start, wg_edge, st);
+  return hipGetLastError();
+}
+
+// Receivers cut by worker boundaries: the worker holding a receiver's last
+// edge wrote its own part to the output; the earlier workers' parts (side
+// buffers, consecutive workers) are summed in worker order and added once,
+// by the last of those workers. One wave per worker.
+__global__ __launch_bounds__(kThreads) void k_cf_fixup(const int32_t* __restrict__ side_recv,
+                                                       const float* __restrict__ side_h,
+                                                       const float* __restrict__ side_f, int G,
+                                                       int D, float* out_h, float* out_f) {
+  const int w = (int)blockIdx.x * (kThreads / 64) + ((int)threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (w >= G) return;
+  const int r = side_recv[w];
+  if (r < 0 || (w + 1 < G && side_recv[w + 1] == r)) return;
+  int f = w;
+  while (f > 0 && side_recv[f - 1] == r) --f;
+  if (out_h) {
+    for (int c = lane; c < D; c += 64) {
+      float acc = 0.f;
+      for (int k = f; k <= w; ++k) acc += side_h[(size_t)k * D + c];
+      out_h[(size_t)r * D + c] += acc;
+    }
+  }
+  if (out_f && lane < 3) {
+    float acc = 0.f;
+    for (int k = f; k <= w; ++k) acc += side_f[(size_t)k * 3 + lane];
+    out_f[(size_t)r * 3 + lane] += acc;
+  }
+}
+
+hipError_t launch_cf_fixup(const CfParams& p, int G, int D, float* out_h, float* out_f,
+                           hipStream_t s) {
+  hipLaunchKernelGGL(k_cf_fixup, dim3((unsigned)((G + kThreads / 64 - 1) / (kThreads / 64))),
+                     dim3(kThreads), 0, s, p.side_recv, p.side_h, p.side_f, G, D, out_h, out_f);
   return hipGetLastError();
 }
 

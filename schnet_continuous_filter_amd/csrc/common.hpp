@@ -70,7 +70,8 @@ __device__ inline void dev_fail(DevStatus* st, int code, int64_t detail) {
 
 // Offsets (bytes) of everything carved out of a workspace.
 struct WsLayout {
-  size_t status, wg_start, wg_start_b, scan_blocks, cell_count, cell_start, cell_atoms, atom_cell;
+  size_t status, wg_start, wg_start_b, wg_edge, wg_edge_b, side_recv, side_h, side_f;
+  size_t scan_blocks, cell_count, cell_start, cell_atoms, atom_cell;
   size_t x, au, gbuf, tmp, gx, fblk, eps, total;
 };
 WsLayout ws_layout(int64_t n_atoms, int D, int T, int H);
@@ -105,7 +106,15 @@ struct CfParams {
   const int32_t* rowptr;
   const int32_t* col;
   const float* pos;
-  const int32_t* wg_start;
+  const int32_t* wg_start;  // per worker: first receiver (launch_partition)
+  const int32_t* wg_edge;   // per worker: first edge (a multiple of 16)
+  // receivers cut by worker boundaries: the part a worker holds of its last,
+  // unfinished receiver (side_h [workers][D] features, side_f [workers][3]
+  // force rows) and that receiver (side_recv, -1 for none); k_cf_fixup adds
+  // them to the finishing worker's output
+  int32_t* side_recv;
+  float* side_h;
+  float* side_f;
   int n_atoms;
   int periodic;
   float box, half_box;
@@ -138,7 +147,11 @@ void cf_fill_image(int D, int KP, int prec, int Dr, const float* Wf1, const floa
                    unsigned char* out);
 hipError_t launch_force_sum(const float* fb, int T, int64_t n_atoms, float* forces, hipStream_t s);
 hipError_t launch_partition(const int32_t* rowptr, int n_atoms, int G, int32_t* wg_start,
-                            DevStatus* st, hipStream_t s);
+                            int32_t* wg_edge, DevStatus* st, hipStream_t s);
+// Adds the side partials of the G workers of the last CFConv launch to out_h
+// [N][D] and out_f [N][3] (either may be null).
+hipError_t launch_cf_fixup(const CfParams& p, int G, int D, float* out_h, float* out_f,
+                           hipStream_t s);
 hipError_t launch_cf_forward(int D, int KP, int prec, const CfParams& p, int G, hipStream_t s);
 hipError_t launch_cf_backward(int D, int KP, int prec, const CfParams& p, int G, hipStream_t s);
 
