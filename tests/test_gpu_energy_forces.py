@@ -320,3 +320,25 @@ def test_bulk64k_sampled_forces_vs_oracle(gpu_lib):
         err = np.max(np.abs(F[atoms] - Fo)) / rms
         print(f"bulk64k dtype {dtype}: {len(atoms)} atoms, F max/rms {err:.2e}")
         assert err <= 1e-4
+
+
+@pytest.mark.parametrize("dtype", [0, 3])
+def test_rows_cut_by_worker_boundaries(gpu_lib, dtype):
+    """Workers take whole 16-edge tiles, so receiver rows are cut between
+    workers and finished by the fix-up: 16 mutually neighbouring atoms (rows
+    of 15 against tiles of 16, one tile per worker) and 200 atoms in a 9 A
+    ball at about bulk density (rows of ~120-199 edges spanning several
+    workers), with biases."""
+    import dataclasses
+    from gen.configs import Config, SystemSpec
+    cfg = CONFIGS["cg32"]
+    m = dataclasses.replace(cfg.model, filter_dtype=dtype)
+    rng = np.random.default_rng(21)
+    w = make_weights(cfg.model, 8, bias_scale=0.05)
+    for n, radius in ((16, 4.5), (200, 9.0)):
+        d = rng.standard_normal((n, 3))
+        d /= np.linalg.norm(d, axis=1, keepdims=True)
+        pos = (d * radius * rng.uniform(0.2, 1.0, (n, 1)) ** (1 / 3)).astype(np.float32)
+        types = np.zeros(n, np.int32)
+        c2 = Config(f"ball{n}", SystemSpec("chain_walk", 1, n, False), m)
+        check(gpu_lib, c2, pos, types, w, what=f"ball of {n}, dtype {dtype}")
