@@ -209,11 +209,7 @@ __global__ __launch_bounds__(64 * kAtomNW, 1) void k_atom(AtomArgs g) {
   using P = AtomPlan<D, N1, PR>;
   constexpr bool SC = PR == PREC_F16S;
   extern __shared__ __align__(16) unsigned char lds[];
-  {
-    const f32x4* src = reinterpret_cast<const f32x4*>(g.img);
-    f32x4* dst = reinterpret_cast<f32x4*>(lds);
-    for (int i = threadIdx.x; i < P::IMG / 16; i += 64 * kAtomNW) dst[i] = src[i];
-  }
+  stage_lds<P::IMG, 64 * kAtomNW>(g.img, lds);
   __syncthreads();
 
   const int lane = threadIdx.x & 63, e = lane & 15;
@@ -240,13 +236,18 @@ __global__ __launch_bounds__(64 * kAtomNW, 1) void k_atom(AtomArgs g) {
     const uint32_t ro = ((uint32_t)atom * D + (uint32_t)g4) * 4u;    // D-wide rows
     const uint32_t ro1 = ((uint32_t)atom * N1 + (uint32_t)g4) * 4u;  // N1-wide rows
 
+    // Every load of a tile is issued before the first of them is waited for:
+    // a missing A2 and rows past M read 0 through their bounded resources.
     f32x4 in[D / 16];
 #pragma unroll
     for (int kb = 0; kb < D / 16; ++kb) {
       in[kb] = bload4(rA, ro + 64u * kb);
-      if constexpr (MODE == ATOM_UPDATE_BWD) {
-        if (g.A2) in[kb] += bload4(rA2, ro + 64u * kb);
-      }
+      if constexpr (MODE == ATOM_UPDATE_BWD) in[kb] += bload4(rA2, ro + 64u * kb);
+    }
+    f32x4 pre[MODE == ATOM_UPDATE_BWD ? N1 / 16 : 1];
+    if constexpr (MODE == ATOM_UPDATE_BWD) {
+#pragma unroll
+      for (int nb = 0; nb < N1 / 16; ++nb) pre[nb] = bload4(rS, ro1 + 64u * nb);
     }
     if constexpr (MODE == ATOM_UPDATE_BWD) {
       if (g.Asum && ok) {
@@ -276,11 +277,10 @@ __global__ __launch_bounds__(64 * kAtomNW, 1) void k_atom(AtomArgs g) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) u[nb][r] = ssp(a[r]);
       } else if constexpr (MODE == ATOM_UPDATE_BWD) {
-        const f32x4 a = bload4(rS, ro1 + 64u * nb);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           float s, sg;
-          ssp_sig(a[r], s, sg);
+          ssp_sig(pre[nb][r], s, sg);
           u[nb][r] *= sg;
         }
       } else {
@@ -305,6 +305,11 @@ __global__ __launch_bounds__(64 * kAtomNW, 1) void k_atom(AtomArgs g) {
 #pragma unroll
       for (int nb = 0; nb < N1 / 16; ++nb) u[nb] *= v4(S1, g4 + 16 * nb);
     }
+    f32x4 res[MODE == ATOM_UPDATE_FWD ? D / 16 : 1];
+    if constexpr (MODE == ATOM_UPDATE_FWD) {
+#pragma unroll
+      for (int kb = 0; kb < D / 16; ++kb) res[kb] = bload4(rR, ro + 64u * kb);
+    }
     f32x4 y[D / 16];
     if constexpr (PR == PREC_F16X2)
       atom_pair_product<N1, D>(y, u, lds + P::M2, lds + P::M2L, S1[1], lane);
@@ -316,7 +321,7 @@ __global__ __launch_bounds__(64 * kAtomNW, 1) void k_atom(AtomArgs g) {
         f32x4 v = y[kb];
         if constexpr (SC && MODE == ATOM_UPDATE_FWD) v *= v4(S2, g4 + 16 * kb);
         if constexpr (MODE == ATOM_UPDATE_FWD)
-          v += bload4(rR, ro + 64u * kb) + *reinterpret_cast<const f32x4*>(V2 + g4 + 16 * kb);
+          v += res[kb] + *reinterpret_cast<const f32x4*>(V2 + g4 + 16 * kb);
         *reinterpret_cast<f32x4*>(g.Y + (size_t)atom * D + g4 + 16 * kb) = v;
       }
     }

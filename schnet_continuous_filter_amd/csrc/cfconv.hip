@@ -217,9 +217,7 @@ static void fill_image(int Dr, const float* Wf1, const float* cf1, const float* 
 
 template <class P>
 __device__ __forceinline__ void stage_image(const void* img, unsigned char* lds) {
-  const f32x4* g = reinterpret_cast<const f32x4*>(img);
-  f32x4* l = reinterpret_cast<f32x4*>(lds);
-  for (int i = threadIdx.x; i < P::STAGE / 16; i += P::NT) l[i] = g[i];
+  stage_lds<P::STAGE, P::NT>(img, lds);
 }
 
 // cf1 (idx < D) or cf2 (idx - D) values idx .. idx + 3 with idx = lo + k: lo

@@ -52,6 +52,36 @@ __device__ __forceinline__ _Float16 pinned(_Float16 v) {
   return v;
 }
 
+// Copies BYTES (a multiple of 16) of a weight image from global memory into
+// LDS with the NT threads of a work-group. Each thread issues up to sixteen
+// 16-byte loads before it writes any of them, so the copy waits for one memory
+// round trip per sixteen pieces, not one per piece. The caller synchronises the
+// work-group before the image is read.
+template <int BYTES, int NT>
+__device__ __forceinline__ void stage_lds(const void* src, unsigned char* lds) {
+  static_assert(BYTES % 16 == 0, "image is copied in 16-byte pieces");
+  constexpr int N = BYTES / 16;
+  constexpr int PER = (N + NT - 1) / NT;
+  constexpr int B = 16;
+  const f32x4* g = reinterpret_cast<const f32x4*>(src);
+  f32x4* l = reinterpret_cast<f32x4*>(lds);
+  const int t = (int)threadIdx.x;
+#pragma unroll
+  for (int j0 = 0; j0 < PER; j0 += B) {
+    f32x4 v[B];
+#pragma unroll
+    for (int j = 0; j < B && j0 + j < PER; ++j) {
+      const int i = t + (j0 + j) * NT;
+      if ((j0 + j + 1) * NT <= N || i < N) v[j] = g[i];
+    }
+#pragma unroll
+    for (int j = 0; j < B && j0 + j < PER; ++j) {
+      const int i = t + (j0 + j) * NT;
+      if ((j0 + j + 1) * NT <= N || i < N) l[i] = v[j];
+    }
+  }
+}
+
 // Orders this wave's LDS writes before its later LDS reads (wave-private data).
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

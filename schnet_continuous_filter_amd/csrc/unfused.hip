@@ -170,11 +170,7 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_uf_gemm(Edges r, const floa
                                                             float* Y) {
   constexpr int IMG = N * K * (PR != PREC_F32 ? 2 : 4);
   extern __shared__ __align__(16) unsigned char lds[];
-  {
-    const f32x4* src = reinterpret_cast<const f32x4*>(img);
-    f32x4* dstl = reinterpret_cast<f32x4*>(lds);
-    for (int i = threadIdx.x; i < IMG / 16; i += 64 * kGemmWaves) dstl[i] = src[i];
-  }
+  stage_lds<IMG, 64 * kGemmWaves>(img, lds);
   __syncthreads();
   const int lane = threadIdx.x & 63, e = lane & 15, g = lane >> 4;
   const int wave = uni((int)threadIdx.x >> 6);
