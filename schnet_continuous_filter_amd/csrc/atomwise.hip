@@ -408,39 +408,29 @@ hipError_t launch_atom(const AtomArgs& g, int D, int N1, int prec, int n_cu, hip
                        [&](auto k) { return decltype(k)::launch(g, n_cu, s); });
 }
 
-// x[i][:] = Emb[types[i]][:], four features per thread
-__global__ __launch_bounds__(kThreads) void k_embed(const int32_t* types, const float* emb, int n,
-                                                    int log2D, int n_types, float* x,
-                                                    DevStatus* st) {
-  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;   // float4 index
-  const int log2q = log2D - 2;
-  if (idx >= ((int64_t)n << log2q)) return;
-  const int64_t i = idx >> log2q;
-  const int c4 = (int)(idx & ((1 << log2q) - 1));
-  int t = types[i];
-  if (t < 0 || t >= n_types) {
-    if (c4 == 0) dev_fail(st, SN_ERR_INVALID_ARG, i);
-    t = 0;
-  }
-  reinterpret_cast<f32x4*>(x)[idx] =
-      reinterpret_cast<const f32x4*>(emb)[((int64_t)t << log2q) + c4];
-}
-
-hipError_t launch_embed(const int32_t* types, const float* emb, int n_atoms, int D, int n_types,
-                        float* x, DevStatus* st, hipStream_t s) {
-  const int log2D = D == 128 ? 7 : 6;
-  const int64_t n4 = (int64_t)n_atoms * D / 4;
-  hipLaunchKernelGGL(k_embed, dim3((unsigned)((n4 + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                     s, types, emb, n_atoms, log2D, n_types, x, st);
-  return hipGetLastError();
-}
-
 // E_r = sum over the replica's atoms of eps_i, accumulated in double in a
 // fixed order: thread t keeps four partial sums over the atoms t + 1024 q
 // (q mod 4 selecting the sum), then a fixed tree over the block.
 constexpr int kEnergyThreads = 1024;
-__global__ __launch_bounds__(kEnergyThreads) void k_energy(const float* eps, int n_per,
-                                                           float* energy, DevStatus* st) {
+
+// Blocks 0 .. n_rep - 1: one replica's energy each (a double sum of its
+// per-atom energies); the blocks after them: F = -(sum over the T blocks of
+// dE/dr), kEnergyThreads components per block, and, when vel is given, the
+// closing velocity half-kick of a BAOAB step, vel += half_kick F.
+__global__ __launch_bounds__(kEnergyThreads) void k_finish(const float* eps, int n_rep, int n_per,
+                                                           float* energy, const float* fb, int T,
+                                                           int64_t n3, float* forces, float* vel,
+                                                           float half_kick, DevStatus* st) {
+  if ((int)blockIdx.x >= n_rep) {
+    const int64_t k = (int64_t)(blockIdx.x - n_rep) * kEnergyThreads + threadIdx.x;
+    if (k >= n3) return;
+    float s = 0.f;
+    for (int t = 0; t < T; ++t) s += fb[(int64_t)t * n3 + k];
+    const float f = -s;
+    forces[k] = f;
+    if (vel) vel[k] += half_kick * f;
+    return;
+  }
   __shared__ double sm[kEnergyThreads];
   const int r = blockIdx.x;
   const float* e = eps + (int64_t)r * n_per;
@@ -464,9 +454,13 @@ __global__ __launch_bounds__(kEnergyThreads) void k_energy(const float* eps, int
   }
 }
 
-hipError_t launch_energy(const float* eps, int n_rep, int n_per, float* energy, DevStatus* st,
-                         hipStream_t s) {
-  hipLaunchKernelGGL(k_energy, dim3(n_rep), dim3(kEnergyThreads), 0, s, eps, n_per, energy, st);
+hipError_t launch_finish(const float* eps, int n_rep, int n_per, float* energy, const float* fb,
+                         int T, int64_t n_atoms, float* forces, float* vel, float half_kick,
+                         DevStatus* st, hipStream_t s) {
+  const int64_t n3 = 3 * n_atoms;
+  const int64_t nb = n_rep + (n3 + kEnergyThreads - 1) / kEnergyThreads;
+  hipLaunchKernelGGL(k_finish, dim3((unsigned)nb), dim3(kEnergyThreads), 0, s, eps, n_rep, n_per,
+                     energy, fb, T, n3, forces, vel, half_kick, st);
   return hipGetLastError();
 }
 

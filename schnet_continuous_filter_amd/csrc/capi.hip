@@ -139,7 +139,8 @@ struct UfMode {
 sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const float* pos,
                              const int32_t* types, const int32_t* rowptr, const int32_t* col,
                              float* energy, float* forces, char* ws, hipStream_t s,
-                             const UfMode* uf = nullptr) {
+                             const UfMode* uf = nullptr, float* vel_kick = nullptr,
+                             float half_kick = 0.f) {
   const sn_model_desc& d = m->desc;
   const int64_t n = n_atoms(sys);
   const int D = d.D, T = d.T, H = d.H;
@@ -163,14 +164,9 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
   const int Gf = cf_grid(m, n, wf), Gb = cf_grid(m, n, wb);
   hipError_t e;
 
-  if (!uf) {
-    if ((e = launch_partition(rowptr, (int)n, Gf * wf, wg_start, wg_edge, st, s)) != hipSuccess)
-      return hip_fail(e);
-    if ((e = launch_partition(rowptr, (int)n, Gb * wb, wg_start_b, wg_edge_b, st, s)) !=
-        hipSuccess)
-      return hip_fail(e);
-  }
-  if ((e = launch_embed(types, m->w + m->off_emb, (int)n, D, d.n_types, x, st, s)) != hipSuccess)
+  if ((e = launch_setup(uf ? nullptr : rowptr, (int)n, Gf * wf, wg_start, wg_edge, Gb * wb,
+                        wg_start_b, wg_edge_b, types, m->w + m->off_emb, D, d.n_types, x, st, s)) !=
+      hipSuccess)
     return hip_fail(e);
 
   CfParams p{};
@@ -298,9 +294,6 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
   AtomArgs r{ATOM_READOUT, (int)n, x + T * ND, nullptr, nullptr, nullptr, nullptr, nullptr, gx,
              m->co2, eps, ro_img};
   if ((e = launch_atom(r, D, H, prec, m->n_cu, s)) != hipSuccess) return hip_fail(e);
-  if ((e = launch_energy(eps, sys->n_replicas, sys->atoms_per_replica, energy, st, s)) !=
-      hipSuccess)
-    return hip_fail(e);
   // backward: gx holds dE/dx^(t+1) without the newest source sum q, which the
   // update-backward kernel adds (and stores back while an older block needs it)
   for (int t = T - 1; t >= 0; --t) {
@@ -329,8 +322,11 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
         return hip_fail(e);
     }
   }
-  // the unfused pipeline accumulates dE/dr of every block into one array
-  if ((e = launch_force_sum(fblk, uf ? 1 : T, n, forces, s)) != hipSuccess) return hip_fail(e);
+  // replica energies, and the forces (the unfused pipeline accumulates dE/dr
+  // of every block into one array)
+  if ((e = launch_finish(eps, sys->n_replicas, sys->atoms_per_replica, energy, fblk, uf ? 1 : T, n,
+                         forces, vel_kick, half_kick, st, s)) != hipSuccess)
+    return hip_fail(e);
   return SN_OK;
 }
 
@@ -716,10 +712,10 @@ sn_status sn_md_step(const sn_model* m, const sn_system* sys, const int32_t* typ
     const int32_t *rp = nullptr, *cl = nullptr;
     if (e == hipSuccess) e = md_eval_list(m, prm, g, state, w, L, s, rp, cl);
     if (e != hipSuccess) return SN_ERR_HIP;
-    rc = energy_forces_impl(m, sys, state->pos, types, rp, cl, e_out, state->forces, w, s);
+    // the closing half-kick B runs in the launch that sums the forces
+    rc = energy_forces_impl(m, sys, state->pos, types, rp, cl, e_out, state->forces, w, s, nullptr,
+                            state->vel, su.c.half_kick);
     if (rc != SN_OK) return rc;
-    e = launch_md_b(su.c, n, state->vel, state->forces, s);
-    if (e != hipSuccess) return SN_ERR_HIP;
     state->step = step + 1;
   }
   return SN_OK;

@@ -12,7 +12,7 @@
 // Work decomposition. Every wave is an independent worker: a work-group
 // copies the filter weights into LDS once, which is its only barrier; then
 // each of its waves walks its own contiguous range of edges in tiles of 16
-// (k_partition gives every worker the same number of whole tiles, to one).
+// (k_setup gives every worker the same number of whole tiles, to one).
 // A receiver whose edges a worker boundary cuts is written by the worker
 // holding its last edge; the earlier workers leave their parts in side
 // buffers, which k_cf_fixup adds in worker order (no atomics; fixed order).
@@ -975,12 +975,8 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, true>()), 1) void k_cf_bwd(CfPar
 // starts there). The kernels address the edge list with 32-bit byte offsets:
 // a list of kMaxListEdges or more edges is refused through the status word.
 constexpr int64_t kMaxListEdges = (int64_t)1 << 30;
-__global__ void k_partition(const int32_t* rowptr, int N, int G, int32_t* wg_start,
-                            int32_t* wg_edge, DevStatus* st) {
-  const int w = blockIdx.x * blockDim.x + threadIdx.x;
-  if (w > G) return;
-  const int64_t E = rowptr[N];
-  if (w == 0 && E >= kMaxListEdges) dev_fail(st, SN_ERR_UNSUPPORTED, E);
+__device__ __forceinline__ void partition_one(const int32_t* rowptr, int N, int64_t E, int G, int w,
+                                              int32_t* wg_start, int32_t* wg_edge) {
   if (w == G) {
     wg_start[G] = N;
     wg_edge[G] = (int32_t)E;
@@ -998,10 +994,51 @@ __global__ void k_partition(const int32_t* rowptr, int N, int G, int32_t* wg_sta
   wg_edge[w] = (int32_t)e0;
 }
 
-hipError_t launch_partition(const int32_t* rowptr, int n_atoms, int G, int32_t* wg_start,
-                            int32_t* wg_edge, DevStatus* st, hipStream_t s) {
-  hipLaunchKernelGGL(k_partition, dim3((G + 1 + kThreads - 1) / kThreads), dim3(kThreads), 0, s,
-                     rowptr, n_atoms, G, wg_start, wg_edge, st);
+// Set-up of one evaluation in one launch. The first nbp blocks write both
+// kernels' partitions (threads 0..G1 the first, the next G2 + 1 threads the
+// second; nbp = 0 when no partition is wanted); the blocks after them write
+// the initial features x[i][:] = Emb[types[i]][:] (FlashSchNet §3.2 "SchNet
+// model"), four features per thread.
+__global__ __launch_bounds__(kThreads) void k_setup(const int32_t* rowptr, int N, int G1,
+                                                    int32_t* wg_start1, int32_t* wg_edge1, int G2,
+                                                    int32_t* wg_start2, int32_t* wg_edge2, int nbp,
+                                                    const int32_t* types, const float* emb,
+                                                    int log2D, int n_types, float* x,
+                                                    DevStatus* st) {
+  if ((int)blockIdx.x < nbp) {
+    const int t = blockIdx.x * kThreads + threadIdx.x;
+    const int64_t E = rowptr[N];
+    if (t == 0 && E >= kMaxListEdges) dev_fail(st, SN_ERR_UNSUPPORTED, E);
+    if (t <= G1) partition_one(rowptr, N, E, G1, t, wg_start1, wg_edge1);
+    else if (t <= G1 + 1 + G2) partition_one(rowptr, N, E, G2, t - G1 - 1, wg_start2, wg_edge2);
+    return;
+  }
+  const int64_t idx = (int64_t)(blockIdx.x - nbp) * kThreads + threadIdx.x;   // float4 index
+  const int log2q = log2D - 2;
+  if (idx >= ((int64_t)N << log2q)) return;
+  const int64_t i = idx >> log2q;
+  const int c4 = (int)(idx & ((1 << log2q) - 1));
+  int ty = types[i];
+  if (ty < 0 || ty >= n_types) {
+    if (c4 == 0) dev_fail(st, SN_ERR_INVALID_ARG, i);
+    ty = 0;
+  }
+  reinterpret_cast<f32x4*>(x)[idx] =
+      reinterpret_cast<const f32x4*>(emb)[((int64_t)ty << log2q) + c4];
+}
+
+hipError_t launch_setup(const int32_t* rowptr, int n_atoms, int G1, int32_t* wg_start1,
+                        int32_t* wg_edge1, int G2, int32_t* wg_start2, int32_t* wg_edge2,
+                        const int32_t* types, const float* emb, int D, int n_types, float* x,
+                        DevStatus* st, hipStream_t s) {
+  const int nbp = rowptr ? (G1 + 1 + G2 + 1 + kThreads - 1) / kThreads : 0;
+  const int log2D = D == 128 ? 7 : 6;
+  const int64_t n4 = (int64_t)n_atoms * D / 4;
+  const int64_t nb = nbp + (n4 + kThreads - 1) / kThreads;
+  if (nb == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_setup, dim3((unsigned)nb), dim3(kThreads), 0, s, rowptr, n_atoms, G1,
+                     wg_start1, wg_edge1, G2, wg_start2, wg_edge2, nbp, types, emb, log2D, n_types,
+                     x, st);
   return hipGetLastError();
 }
 
@@ -1016,10 +1053,16 @@ __global__ __launch_bounds__(kThreads) void k_cf_fixup(const int32_t* __restrict
   const int w = (int)blockIdx.x * (kThreads / 64) + ((int)threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (w >= G) return;
+  // the worker's own entry and both neighbours' in one round trip
   const int r = side_recv[w];
-  if (r < 0 || (w + 1 < G && side_recv[w + 1] == r)) return;
+  const int rn = w + 1 < G ? side_recv[w + 1] : -1;
+  const int rp = w > 0 ? side_recv[w - 1] : -1;
+  if (r < 0 || rn == r) return;
   int f = w;
-  while (f > 0 && side_recv[f - 1] == r) --f;
+  if (rp == r) {
+    f = w - 1;
+    while (f > 0 && side_recv[f - 1] == r) --f;
+  }
   if (out_h) {
     for (int c = lane; c < D; c += 64) {
       float acc = 0.f;
@@ -1038,23 +1081,6 @@ hipError_t launch_cf_fixup(const CfParams& p, int G, int D, float* out_h, float*
                            hipStream_t s) {
   hipLaunchKernelGGL(k_cf_fixup, dim3((unsigned)((G + kThreads / 64 - 1) / (kThreads / 64))),
                      dim3(kThreads), 0, s, p.side_recv, p.side_h, p.side_f, G, D, out_h, out_f);
-  return hipGetLastError();
-}
-
-// F_i = -(sum over blocks of dE/dr_i)
-__global__ __launch_bounds__(kThreads) void k_force_sum(const float* fb, int T, int64_t n3,
-                                                        float* forces) {
-  const int64_t k = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (k >= n3) return;
-  float s = 0.f;
-  for (int t = 0; t < T; ++t) s += fb[(int64_t)t * n3 + k];
-  forces[k] = -s;
-}
-
-hipError_t launch_force_sum(const float* fb, int T, int64_t n_atoms, float* forces, hipStream_t s) {
-  const int64_t n3 = 3 * n_atoms;
-  hipLaunchKernelGGL(k_force_sum, dim3((unsigned)((n3 + kThreads - 1) / kThreads)), dim3(kThreads),
-                     0, s, fb, T, n3, forces);
   return hipGetLastError();
 }
 

@@ -145,9 +145,12 @@ size_t cf_image_bytes(int D, int KP, int prec);
 void cf_fill_image(int D, int KP, int prec, int Dr, const float* Wf1, const float* cf1,
                    const float* Wf2, const float* cf2, float rbf_step, float r_cut,
                    unsigned char* out);
-hipError_t launch_force_sum(const float* fb, int T, int64_t n_atoms, float* forces, hipStream_t s);
-hipError_t launch_partition(const int32_t* rowptr, int n_atoms, int G, int32_t* wg_start,
-                            int32_t* wg_edge, DevStatus* st, hipStream_t s);
+// Both CFConv kernels' worker partitions of the receiver CSR (skipped when
+// rowptr is null) and the initial features x = Emb[types], in one launch.
+hipError_t launch_setup(const int32_t* rowptr, int n_atoms, int G1, int32_t* wg_start1,
+                        int32_t* wg_edge1, int G2, int32_t* wg_start2, int32_t* wg_edge2,
+                        const int32_t* types, const float* emb, int D, int n_types, float* x,
+                        DevStatus* st, hipStream_t s);
 // Adds the side partials of the G workers of the last CFConv launch to out_h
 // [N][D] and out_f [N][3] (either may be null).
 hipError_t launch_cf_fixup(const CfParams& p, int G, int D, float* out_h, float* out_f,
@@ -179,10 +182,11 @@ void atom_fill_image(int mode, int D, int N1, int prec, const float* W1, const f
                      const float* W2, const float* b2, unsigned char* out);
 hipError_t atom_prepare(int D, int H, int prec);   // raises the dynamic LDS limit of the kernels
 hipError_t launch_atom(const AtomArgs& g, int D, int N1, int prec, int n_cu, hipStream_t s);
-hipError_t launch_embed(const int32_t* types, const float* emb, int n_atoms, int D, int n_types,
-                        float* x, DevStatus* st, hipStream_t s);
-hipError_t launch_energy(const float* eps, int n_rep, int n_per, float* energy, DevStatus* st,
-                         hipStream_t s);
+// Per-replica energies (double sums of eps) and F = -(sum over the T blocks
+// of fb), in one launch; with vel, also vel += half_kick F.
+hipError_t launch_finish(const float* eps, int n_rep, int n_per, float* energy, const float* fb,
+                         int T, int64_t n_atoms, float* forces, float* vel, float half_kick,
+                         DevStatus* st, hipStream_t s);
 
 // Unfused edge pipeline (unfused.hip): one kernel per step, edge tensors in
 // the workspace, atomic or segmented aggregation.
@@ -244,8 +248,6 @@ hipError_t launch_md_wrap(const MdCoef& c, int64_t n, float* pos, hipStream_t s)
 hipError_t launch_md_baoa(const MdCoef& c, int64_t n, uint64_t step, float* pos, float* vel,
                           const float* forces, const float* pos_at_build, DevStatus* st,
                           hipStream_t s);
-hipError_t launch_md_b(const MdCoef& c, int64_t n, float* vel, const float* forces,
-                       hipStream_t s);
 hipError_t launch_md_mark_build(int64_t n, const float* pos, float* pos_at_build, DevStatus* st,
                                 const int64_t* gate, int64_t gate_val, hipStream_t s);
 hipError_t launch_philox(const uint64_t* ctr, uint64_t k0, uint64_t k1, uint64_t* out, int64_t n,

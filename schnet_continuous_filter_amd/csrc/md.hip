@@ -102,13 +102,6 @@ __global__ __launch_bounds__(kThreads) void k_md_baoa(MdCoef c, int64_t n, uint6
   if (d2 > c.half_skin2) st->rebuild_req = (int64_t)step + 1;
 }
 
-__global__ __launch_bounds__(kThreads) void k_md_b(MdCoef c, int64_t n, float* vel,
-                                                   const float* forces) {
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i >= 3 * n) return;
-  vel[i] += c.half_kick * forces[i];
-}
-
 __global__ __launch_bounds__(kThreads) void k_md_mark_build(int64_t n, const float* pos,
                                                             float* pos_at_build, DevStatus* st,
                                                             const int64_t* gate, int64_t gate_val) {
@@ -143,11 +136,6 @@ hipError_t launch_md_baoa(const MdCoef& c, int64_t n, uint64_t step, float* pos,
                           hipStream_t s) {
   hipLaunchKernelGGL(k_md_baoa, grid_for(n), dim3(kThreads), 0, s, c, n, step, pos, vel, forces,
                      pos_at_build, st);
-  return hipGetLastError();
-}
-hipError_t launch_md_b(const MdCoef& c, int64_t n, float* vel, const float* forces,
-                       hipStream_t s) {
-  hipLaunchKernelGGL(k_md_b, grid_for(3 * n), dim3(kThreads), 0, s, c, n, vel, forces);
   return hipGetLastError();
 }
 hipError_t launch_md_mark_build(int64_t n, const float* pos, float* pos_at_build, DevStatus* st,

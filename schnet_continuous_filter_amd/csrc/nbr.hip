@@ -42,7 +42,8 @@ __device__ __forceinline__ bool pair_in(float xi, float yi, float zi, float xj, 
   if (gate != nullptr && *gate != gate_val) return;
 
 // ------------------------------------------------------------------ scan
-// Exclusive scan of one value per thread over a 256-thread block.
+// Exclusive scan of one value per thread over an NT-thread block.
+template <int NT = kThreads>
 __device__ inline int64_t block_exclusive_scan(int64_t v, int64_t* smem, int64_t* total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int64_t x = v;
@@ -53,7 +54,7 @@ __device__ inline int64_t block_exclusive_scan(int64_t v, int64_t* smem, int64_t
   if (lane == 63) smem[wave] = x;
   __syncthreads();
   int64_t wave_off = 0, tot = 0;
-  for (int w = 0; w < kThreads / 64; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     if (w < wave) wave_off += smem[w];
     tot += smem[w];
   }
@@ -127,9 +128,85 @@ __global__ __launch_bounds__(kThreads) void k_scan_add(int32_t* a, int64_t n, co
   if (blockIdx.x == 0 && threadIdx.x == 0) a[n] = ovf ? 0 : (int32_t)total;
 }
 
+// Inclusive scan over the 64 lanes of a wave on DPP lane moves: shifts by 1,
+// 2, 4 and 8 inside each row of 16 lanes (lanes without a source add 0),
+// then lane 15 of rows 0 and 2 added to rows 1 and 3, then lane 31 added to
+// rows 2 and 3.
+__device__ __forceinline__ int32_t wave_inclusive_scan(int32_t x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return x;
+}
+
+// Lists of up to 32,768 rows are scanned by one block of kScan1Threads
+// threads in one launch. Wave w owns the contiguous run [w 64 Q, (w + 1) 64 Q);
+// its Q loads of 64 consecutive counts (one per lane, bounded: reads past n
+// give 0) are all issued before the first is used; the wave scans them in
+// order, carrying its running total, and one block scan of the sixteen wave
+// totals gives each wave its offset.
+constexpr int kScan1Threads = 1024;
+constexpr int64_t kScan1Max = 32768;
+template <int Q>
+__global__ __launch_bounds__(kScan1Threads) void k_scan_single(int32_t* a, int64_t n,
+                                                              DevStatus* st, int64_t capacity,
+                                                              const int64_t* gate,
+                                                              int64_t gate_val) {
+  SN_GATE
+  __shared__ int64_t smem[kScan1Threads / 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc(a, (short)0, (int)(n * 4), 0x00020000);
+  const uint32_t base = (uint32_t)(wave * 64 * Q + lane);
+  int32_t v[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q)
+    v[q] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(ra, (base + 64u * q) * 4u, 0, 0);
+  // exclusive prefixes within each group of 64, chained over the groups in order
+  int64_t carry = 0;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int32_t x = wave_inclusive_scan(v[q]);
+    const int32_t wtot = __builtin_amdgcn_readlane(x, 63);
+    v[q] = (int32_t)(carry + (x - v[q]));
+    carry += wtot;
+  }
+  int64_t tot;
+  const int64_t off = block_exclusive_scan<kScan1Threads>(lane == 63 ? carry : 0, smem, &tot);
+  const bool ovf = capacity >= 0 && tot > capacity;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int64_t i = (int64_t)base + 64 * q;
+    if (i < n) a[i] = ovf ? 0 : (int32_t)(off + v[q]);
+  }
+  if (threadIdx.x == 0) {
+    a[n] = ovf ? 0 : (int32_t)tot;
+    if (capacity >= 0) {
+      st->last_n_edges = tot;
+      st->overflow = ovf;
+      if (ovf) dev_fail(st, SN_ERR_CAPACITY, tot);
+    }
+  }
+}
+
 hipError_t launch_exclusive_scan(int32_t* a, int64_t n, int32_t* blocks_i32, DevStatus* st,
                                  int64_t capacity, const int64_t* gate, int64_t gate_val,
                                  hipStream_t s) {
+  if (n <= kScan1Max) {
+    const int64_t q = (n + kScan1Threads - 1) / kScan1Threads;   // loads per lane needed
+    auto one = [&](auto kern) {
+      hipLaunchKernelGGL(kern, dim3(1), dim3(kScan1Threads), 0, s, a, n, st, capacity, gate,
+                         gate_val);
+      return hipGetLastError();
+    };
+    if (q <= 4) return one(k_scan_single<4>);
+    if (q <= 8) return one(k_scan_single<8>);
+    if (q <= 16) return one(k_scan_single<16>);
+    return one(k_scan_single<32>);
+  }
   int64_t* blocks = reinterpret_cast<int64_t*>(blocks_i32);
   const int64_t nblk = (n + kScanChunk - 1) / kScanChunk;
   hipLaunchKernelGGL(k_scan_local, dim3((unsigned)nblk), dim3(kThreads), 0, s, a, n, blocks, gate,

@@ -85,6 +85,24 @@ def test_capacity_overflow_reports_and_leaves_rows_empty(gpu_lib):
     assert np.array_equal(col[:ne].cpu().numpy(), col_ref)
 
 
+@pytest.mark.parametrize("n", [32768, 32769])
+def test_row_scan_either_side_of_one_launch(gpu_lib, n):
+    """Row counts of up to 32,768 receivers are scanned in one launch, more in
+    three: exact lists on both sides, and an overflow reported with empty rows
+    on both."""
+    import torch
+    rng = np.random.default_rng(n)
+    box = 48.0
+    pos = rng.uniform(0, box, (n, 3)).astype(np.float32)
+    pos[pos >= np.float32(box)] = 0
+    system = gpu_lib.make_system(1, n, True, box)
+    ne = _compare(gpu_lib, system, pos, 3.0)
+    p, rowptr, col, ne2, ws = gpu_neighbors(gpu_lib, system, pos, 3.0, capacity=ne - 1)
+    status, detail, _ = gpu_lib.sn_get_device_status(ws)
+    assert status == gpu_lib.SN_ERR_CAPACITY and detail == ne and ne2 == ne
+    assert torch.all(rowptr == 0)
+
+
 def test_host_validation(gpu_lib):
     import torch
     system = gpu_lib.make_system(1, 10, True, 9.0)
