@@ -204,6 +204,20 @@ __device__ __forceinline__ void atom_pair_product(f32x4 (&out)[NOUT / 16], const
   }
 }
 
+// out[j] = sum_k M[16 (nb0 + j) + e][k] S[k] for the NB output blocks from nb0.
+template <int K, int NB, int PR>
+__device__ __forceinline__ void gemm_om_blocks(f32x4 (&out)[NB], const f32x4 (&S)[K / 16],
+                                               const void* img, int lane, int nb0) {
+  const ImgLanes<K, PR> ln(opaque(lane));
+  const Operand<K, PR> op(S);
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    f32x4 acc = f32x4{};
+    gemm_om_block<K, PR>(acc, op, img, nb0 + j, ln);
+    out[j] = acc;
+  }
+}
+
 template <int D, int N1, int MODE, int PR>
 __global__ __launch_bounds__(64 * kAtomNW, 1) void k_atom(AtomArgs g) {
   using P = AtomPlan<D, N1, PR>;
@@ -328,41 +342,211 @@ __global__ __launch_bounds__(64 * kAtomNW, 1) void k_atom(AtomArgs g) {
   }
 }
 
+// The same networks for small systems, whose few tiles would leave most
+// SIMDs idle or give a few of them a second tile: a group of four waves, one
+// per SIMD, takes a 16-atom tile. Member m computes hidden blocks
+// [m N1/64, (m + 1) N1/64) of the first product and their activation,
+// writes them to the group's LDS exchange tile, and after a work-group
+// barrier computes output blocks [m D/64, (m + 1) D/64) of the second
+// product from all of them. Only the matrices are staged; the vectors are
+// read from the image in global memory. The readout's per-atom energy is
+// summed over the four members' parts in member order. fp32 operands only
+// (with 16-bit operands each member would still convert or split the whole
+// input, and the kernels are bound by that, not by the products).
+template <int D, int N1, int MODE, int PR>
+struct AtomSplitPlan {
+  using P = AtomPlan<D, N1, PR>;
+  static constexpr int MAT = P::V1;                  // matrices (staged)
+  static constexpr int XB = (N1 / 16) * 64 * 16;     // one group's activation tile
+  static constexpr int X = MAT;                      // four exchange tiles
+  static constexpr int EP = X + 4 * XB;              // readout: [group][member][atom] parts
+  static constexpr int TOTAL = EP + (MODE == ATOM_READOUT ? 4 * 4 * kAtoms * 4 : 0);
+  static_assert(MAT % 16 == 0, "image is copied in 16-byte pieces");
+  static_assert(TOTAL <= 160 * 1024, "split plan exceeds LDS");
+};
+
+template <int D, int N1, int MODE, int PR>
+__global__ __launch_bounds__(64 * kAtomNW, 1) void k_atom_split(AtomArgs g) {
+  using P = AtomPlan<D, N1, PR>;
+  using SP = AtomSplitPlan<D, N1, MODE, PR>;
+  static_assert(PR == PREC_F32, "fp32 operands only");
+  constexpr int NH = N1 / 64, NO = D / 64;   // blocks per member
+  static_assert(NH >= 1 && NO >= 1, "four members need 64-wide layers");
+  extern __shared__ __align__(16) unsigned char lds[];
+  stage_lds<SP::MAT, 64 * kAtomNW>(g.img, lds);
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, e = lane & 15;
+  const int wave = uni((int)threadIdx.x >> 6);
+  const int grp = wave >> 2, mem = wave & 3;
+  const int ntiles = (g.M + kAtoms - 1) / kAtoms;
+  const uint32_t rows = (uint32_t)g.M;
+  const __amdgpu_buffer_rsrc_t rA = rsrc(g.A, rows * D * 4u);
+  const __amdgpu_buffer_rsrc_t rA2 = rsrc(g.A2, g.A2 ? rows * D * 4u : 0u);
+  const __amdgpu_buffer_rsrc_t rR = rsrc(g.R, g.R ? rows * D * 4u : 0u);
+  const __amdgpu_buffer_rsrc_t rS = rsrc(g.S, g.S ? rows * N1 * 4u : 0u);
+  const unsigned char* gimg = reinterpret_cast<const unsigned char*>(g.img);
+  const float* V1 = reinterpret_cast<const float*>(gimg + P::V1);
+  const float* V2 = reinterpret_cast<const float*>(gimg + P::V2);
+  auto v4 = [&](const float* v, int i) { return *reinterpret_cast<const f32x4*>(v + i); };
+  f32x4* xch = reinterpret_cast<f32x4*>(lds + SP::X + grp * SP::XB);
+  float* epl = reinterpret_cast<float*>(lds + SP::EP) + grp * 4 * kAtoms;
+  const int h0 = mem * NH, o0 = mem * NO;   // first hidden / output block of this member
+
+  // every wave runs the same number of rounds (group 0's tiles); a group
+  // without a tile in a round still meets both barriers
+  for (int t0 = (int)blockIdx.x; t0 < ntiles; t0 += (int)gridDim.x * 4) {
+    const int t = t0 + (int)gridDim.x * grp;
+    const bool active = t < ntiles;
+    const int g4 = 4 * (opaque(lane) >> 4);
+    const int atom = t * kAtoms + e;
+    const bool ok = active && atom < g.M;
+    const uint32_t ro = ((uint32_t)atom * D + (uint32_t)g4) * 4u;
+    const uint32_t ro1 = ((uint32_t)atom * N1 + (uint32_t)g4) * 4u;
+    // update backward: this member's quarter of A + A2, stored to Asum only
+    // after the barrier (Asum may be A, which the other members still read)
+    f32x4 sum[MODE == ATOM_UPDATE_BWD ? NO : 1];
+    if (active) {
+      f32x4 in[D / 16];
+#pragma unroll
+      for (int kb = 0; kb < D / 16; ++kb) {
+        in[kb] = bload4(rA, ro + 64u * kb);
+        if constexpr (MODE == ATOM_UPDATE_BWD) in[kb] += bload4(rA2, ro + 64u * kb);
+      }
+      f32x4 pre[MODE == ATOM_UPDATE_BWD ? NH : 1];
+      if constexpr (MODE == ATOM_UPDATE_BWD) {
+#pragma unroll
+        for (int j = 0; j < NH; ++j) pre[j] = bload4(rS, ro1 + 64u * (h0 + j));
+#pragma unroll
+        for (int j = 0; j < NO; ++j) sum[j] = in[o0 + j];
+      }
+      f32x4 u[NH];
+      gemm_om_blocks<D, NH, PR>(u, in, lds + P::M1, lane, h0);
+      float ep = 0.f;
+#pragma unroll
+      for (int j = 0; j < NH; ++j) {
+        const int c = g4 + 16 * (h0 + j);   // this lane's hidden index of block j
+        if constexpr (MODE == ATOM_UPDATE_FWD) {
+          const f32x4 a = u[j] + v4(V1, c);
+          if (ok) *reinterpret_cast<f32x4*>(g.Aout + (size_t)atom * N1 + c) = a;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) u[j][r] = ssp(a[r]);
+        } else if constexpr (MODE == ATOM_UPDATE_BWD) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float sp, sg;
+            ssp_sig(pre[j][r], sp, sg);
+            u[j][r] *= sg;
+          }
+        } else {
+          const f32x4 b = v4(V1, c);
+          const f32x4 w2 = v4(V2, c);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float sp, sg;
+            ssp_sig(u[j][r] + b[r], sp, sg);
+            ep = fmaf(sp, w2[r], ep);
+            u[j][r] = sg * w2[r];
+          }
+        }
+        xch[(h0 + j) * 64 + lane] = u[j];
+      }
+      if constexpr (MODE == ATOM_READOUT) {
+        ep += __shfl_xor(ep, 16, 64);
+        ep += __shfl_xor(ep, 32, 64);
+        if (lane < kAtoms) epl[mem * kAtoms + lane] = ep;
+      }
+    }
+    __syncthreads();
+    if (active) {
+      if constexpr (MODE == ATOM_UPDATE_BWD) {
+        if (g.Asum && ok) {
+#pragma unroll
+          for (int j = 0; j < NO; ++j)
+            *reinterpret_cast<f32x4*>(g.Asum + (size_t)atom * D + g4 + 16 * (o0 + j)) = sum[j];
+        }
+      }
+      f32x4 uf[N1 / 16];
+#pragma unroll
+      for (int nb = 0; nb < N1 / 16; ++nb) uf[nb] = xch[nb * 64 + lane];
+      if constexpr (MODE == ATOM_READOUT) {
+        if (mem == 0 && lane < kAtoms && ok) {
+          const float* q = epl + lane;
+          g.eps[atom] = ((q[0] + q[kAtoms]) + q[2 * kAtoms]) + q[3 * kAtoms] + g.b2s;
+        }
+      }
+      f32x4 res[MODE == ATOM_UPDATE_FWD ? NO : 1];
+      if constexpr (MODE == ATOM_UPDATE_FWD) {
+#pragma unroll
+        for (int j = 0; j < NO; ++j) res[j] = bload4(rR, ro + 64u * (o0 + j));
+      }
+      f32x4 y[NO];
+      gemm_om_blocks<N1, NO, PR>(y, uf, lds + P::M2, lane, o0);
+      if (ok) {
+#pragma unroll
+        for (int j = 0; j < NO; ++j) {
+          const int c = g4 + 16 * (o0 + j);
+          f32x4 v = y[j];
+          if constexpr (MODE == ATOM_UPDATE_FWD) v += res[j] + v4(V2, c);
+          *reinterpret_cast<f32x4*>(g.Y + (size_t)atom * D + c) = v;
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
 template <int D, int N1, int PR>
 struct AtomKernels {
   static constexpr int kD = D, kN1 = N1, kPR = PR;
   using P = AtomPlan<D, N1, PR>;
-  static hipError_t prepare() {
-    hipError_t e = hipSuccess;
-    if constexpr (D == N1) {
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_atom<D, N1, ATOM_UPDATE_FWD, PR>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, P::IMG);
+  // the four-wave split: fp32 operands, both layers in 64-wide multiples
+  static constexpr bool kSplit = PR == PREC_F32 && N1 % 64 == 0 && D % 64 == 0;
+  template <int MODE>
+  static hipError_t allow() {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_atom<D, N1, MODE, PR>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, P::IMG);
+    if constexpr (kSplit) {
       if (e == hipSuccess)
-        e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&k_atom<D, N1, ATOM_UPDATE_BWD, PR>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, P::IMG);
-    } else {
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_atom<D, N1, ATOM_READOUT, PR>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, P::IMG);
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_atom_split<D, N1, MODE, PR>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                AtomSplitPlan<D, N1, MODE, PR>::TOTAL);
     }
     return e;
+  }
+  static hipError_t prepare() {
+    if constexpr (D == N1) {
+      hipError_t e = allow<ATOM_UPDATE_FWD>();
+      return e == hipSuccess ? allow<ATOM_UPDATE_BWD>() : e;
+    } else {
+      return allow<ATOM_READOUT>();
+    }
+  }
+  template <int MODE>
+  static void run(const AtomArgs& g, int G, int ntiles, int n_cu, hipStream_t s) {
+    const dim3 grid(G), block(64 * kAtomNW);
+    // at most two tiles per SIMD: the split kernel shortens the longest SIMD's work
+    if constexpr (kSplit) {
+      if (ntiles <= 2 * 4 * n_cu) {
+        constexpr int lds_bytes = AtomSplitPlan<D, N1, MODE, PR>::TOTAL;
+        hipLaunchKernelGGL((k_atom_split<D, N1, MODE, PR>), grid, block, lds_bytes, s, g);
+        return;
+      }
+    }
+    hipLaunchKernelGGL((k_atom<D, N1, MODE, PR>), grid, block, P::IMG, s, g);
   }
   static hipError_t launch(const AtomArgs& g, int n_cu, hipStream_t s) {
     const int ntiles = (g.M + kAtoms - 1) / kAtoms;
     int G = ntiles;
     if (G > n_cu) G = n_cu;
     if (G < 1) G = 1;
-    const dim3 grid(G), block(64 * kAtomNW);
     if constexpr (D == N1) {   // the update networks
-      if (g.mode == ATOM_UPDATE_FWD)
-        hipLaunchKernelGGL((k_atom<D, N1, ATOM_UPDATE_FWD, PR>), grid, block, P::IMG, s, g);
-      else if (g.mode == ATOM_UPDATE_BWD)
-        hipLaunchKernelGGL((k_atom<D, N1, ATOM_UPDATE_BWD, PR>), grid, block, P::IMG, s, g);
-      else
-        return hipErrorInvalidValue;
+      if (g.mode == ATOM_UPDATE_FWD) run<ATOM_UPDATE_FWD>(g, G, ntiles, n_cu, s);
+      else if (g.mode == ATOM_UPDATE_BWD) run<ATOM_UPDATE_BWD>(g, G, ntiles, n_cu, s);
+      else return hipErrorInvalidValue;
     } else {                   // the readout
       if (g.mode != ATOM_READOUT) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((k_atom<D, N1, ATOM_READOUT, PR>), grid, block, P::IMG, s, g);
+      run<ATOM_READOUT>(g, G, ntiles, n_cu, s);
     }
     return hipGetLastError();
   }

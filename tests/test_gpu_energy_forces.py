@@ -5,7 +5,7 @@ import pytest
 import oracle
 from gen.configs import CONFIGS, ModelSpec, make_config, make_weights
 from tests.gpu_helpers import (assert_energy_forces, cutout_forces, gpu_neighbors, lib_desc,
-                               lib_system, oracle_desc)
+                               lib_system, oracle_desc, F_TOL_BF16, F_TOL_F32)
 
 pytestmark = pytest.mark.gpu
 
@@ -305,7 +305,9 @@ def test_bulk64k_sampled_forces_vs_oracle(gpu_lib):
     the forces of the ~250 atoms within 10 A of atom 0, element by element
     against the oracle evaluated on a 40.5 A cutout around it (exact for
     them, see cutout_forces), for the fp32 filter and the fp32 model on
-    fp16 pairs."""
+    fp16 pairs at the fp32 bar, and for the bf16 filter and W16A16 at the
+    16-bit bar (the atom-wise kernels of 4,096 tiles take one wave per
+    tile)."""
     import dataclasses
     cfg, pos, types, w = make_config("bulk64k")
     m = cfg.model
@@ -314,12 +316,44 @@ def test_bulk64k_sampled_forces_vs_oracle(gpu_lib):
     assert len(atoms) > 150
     rms = np.sqrt(np.mean(Fo ** 2))
     system = lib_system(gpu_lib, cfg.system)
-    for dtype in (0, 3):
+    for dtype in (0, 3, 1, 2):
         _, F, _, _ = run_gpu(gpu_lib, dataclasses.replace(m, filter_dtype=dtype), system, pos,
                              types, w, m.r_cut)
         err = np.max(np.abs(F[atoms] - Fo)) / rms
         print(f"bulk64k dtype {dtype}: {len(atoms)} atoms, F max/rms {err:.2e}")
-        assert err <= 1e-4
+        assert err <= (F_TOL_F32 if dtype in (0, 3) else F_TOL_BF16)
+
+
+@pytest.mark.parametrize("dtype", [0, 1, 2, 3])
+def test_small_and_large_batches_agree(gpu_lib, dtype):
+    """With fp32 operands (the fp32 and the bf16 filter) and up to two 16-atom
+    tiles per SIMD, the atom-wise networks run with four waves per tile (each
+    a quarter of the hidden and output features), above that with one. The
+    first 8 replicas of a 160-replica batch of the MD model's chains (2,690
+    tiles) against the same 8 alone (135 tiles): same energies and forces
+    within the fp32 bars (1e-5 relative, 1e-4 of the force RMS); for W16A16
+    (within its own bars: an fp32 rounding difference in a feature can move
+    one of its fp16 roundings) and fp16 pairs, which take one wave per tile
+    at both sizes, a check of size invariance alone."""
+    import dataclasses
+    cfg, pos, types, w = make_config("md1024", n_replicas=160)
+    m = dataclasses.replace(cfg.model, filter_dtype=dtype)
+    nper = cfg.system.atoms_per_replica
+    E1, F1, _, _ = run_gpu(gpu_lib, m, lib_system(gpu_lib, cfg.system, 160), pos, types, w,
+                           m.r_cut)
+    k = 8 * nper
+    E2, F2, _, _ = run_gpu(gpu_lib, m, lib_system(gpu_lib, cfg.system, 8), pos[:k], types[:k], w,
+                           m.r_cut)
+    F1 = np.asarray(F1).reshape(-1, 3)[:k]
+    F2 = np.asarray(F2).reshape(-1, 3)
+    rms = np.sqrt(np.mean(F2 ** 2))
+    de = np.max(np.abs(E1[:8] - E2) / np.abs(E2))
+    df = np.max(np.abs(F1 - F2)) / rms
+    print(f"dtype {dtype}: E rel {de:.2e}, F max/rms {df:.2e}")
+    if dtype == 2:
+        assert de <= 1e-3 and df <= F_TOL_BF16
+    else:
+        assert de <= 1e-5 and df <= F_TOL_F32
 
 
 @pytest.mark.parametrize("dtype", [0, 3])
