@@ -218,14 +218,27 @@ __device__ __forceinline__ void gemm_om_blocks(f32x4 (&out)[NB], const f32x4 (&S
   }
 }
 
+// Adds to v, which holds the row of atom `atom` that a CFConv launch wrote
+// (plus, in the update backward, the row it is summed with), the parts of
+// that receiver held by other workers (cut_workers), in worker order.
+template <int D>
+__device__ __forceinline__ void add_cut_parts(f32x4 (&v)[D / 16], const AtomArgs& g, int atom,
+                                              bool ok, int g4) {
+  const int64_t E = g.cut_rowptr[g.M];
+  int w0 = 0, w1 = 0;
+  if (ok) cut_workers(g.cut_rowptr[atom], g.cut_rowptr[atom + 1], (E + 15) / 16, g.cut_G, w0, w1);
+  for (int w = w0; w < w1; ++w) {
+#pragma unroll
+    for (int kb = 0; kb < D / 16; ++kb)
+      v[kb] += *reinterpret_cast<const f32x4*>(g.cut_side + (size_t)w * D + g4 + 16 * kb);
+  }
+}
+
 template <int D, int N1, int MODE, int PR>
 __global__ __launch_bounds__(64 * kAtomNW, 1) void k_atom(AtomArgs g) {
   using P = AtomPlan<D, N1, PR>;
   constexpr bool SC = PR == PREC_F16S;
   extern __shared__ __align__(16) unsigned char lds[];
-  stage_lds<P::IMG, 64 * kAtomNW>(g.img, lds);
-  __syncthreads();
-
   const int lane = threadIdx.x & 63, e = lane & 15;
   const int wave = uni((int)threadIdx.x >> 6);
   const int ntiles = (g.M + kAtoms - 1) / kAtoms;
@@ -234,6 +247,27 @@ __global__ __launch_bounds__(64 * kAtomNW, 1) void k_atom(AtomArgs g) {
   const __amdgpu_buffer_rsrc_t rA2 = rsrc(g.A2, g.A2 ? rows * D * 4u : 0u);
   const __amdgpu_buffer_rsrc_t rR = rsrc(g.R, g.R ? rows * D * 4u : 0u);
   const __amdgpu_buffer_rsrc_t rS = rsrc(g.S, g.S ? rows * N1 * 4u : 0u);
+  // a tile's input rows: A (+ A2), every load issued before the first is
+  // waited for (a missing A2 and rows past M read 0 through their bounded
+  // resources), then the parts of receivers cut by the CFConv launch
+  auto fetch = [&](int t, f32x4 (&in)[D / 16]) {
+    const int g4 = 4 * (opaque(lane) >> 4);
+    const int atom = t * kAtoms + e;
+    const uint32_t ro = ((uint32_t)atom * D + (uint32_t)g4) * 4u;
+#pragma unroll
+    for (int kb = 0; kb < D / 16; ++kb) {
+      in[kb] = bload4(rA, ro + 64u * kb);
+      if constexpr (MODE == ATOM_UPDATE_BWD) in[kb] += bload4(rA2, ro + 64u * kb);
+    }
+    if (g.cut_side) add_cut_parts<D>(in, g, atom, atom < g.M, g4);
+  };
+  // the first tile's rows are fetched while the work-group stages the weights
+  int t = (int)blockIdx.x + (int)gridDim.x * wave;
+  f32x4 in[D / 16];
+  if (t < ntiles) fetch(t, in);
+  stage_lds<P::IMG, 64 * kAtomNW>(g.img, lds);
+  __syncthreads();
+
   const float* V1 = reinterpret_cast<const float*>(lds + P::V1);
   const float* V2 = reinterpret_cast<const float*>(lds + P::V2);
   const float* S1 = reinterpret_cast<const float*>(lds + P::S1);
@@ -242,27 +276,22 @@ __global__ __launch_bounds__(64 * kAtomNW, 1) void k_atom(AtomArgs g) {
 
   // tiles interleaved over the work-groups first, so that small systems
   // spread one tile per SIMD over all CUs before any SIMD gets a second
-  for (int t = (int)blockIdx.x + (int)gridDim.x * wave; t < ntiles;
-       t += (int)gridDim.x * kAtomNW) {
+  // (the next tile's rows are fetched at the end of each iteration)
+  while (t < ntiles) {
     const int g4 = 4 * (opaque(lane) >> 4);   // this lane's feature offset in a block
     const int atom = t * kAtoms + e;
     const bool ok = atom < g.M;
     const uint32_t ro = ((uint32_t)atom * D + (uint32_t)g4) * 4u;    // D-wide rows
     const uint32_t ro1 = ((uint32_t)atom * N1 + (uint32_t)g4) * 4u;  // N1-wide rows
-
-    // Every load of a tile is issued before the first of them is waited for:
-    // a missing A2 and rows past M read 0 through their bounded resources.
-    f32x4 in[D / 16];
-#pragma unroll
-    for (int kb = 0; kb < D / 16; ++kb) {
-      in[kb] = bload4(rA, ro + 64u * kb);
-      if constexpr (MODE == ATOM_UPDATE_BWD) in[kb] += bload4(rA2, ro + 64u * kb);
-    }
+    // the stored pre-activations, issued with the input rows (with fp16
+    // pairs, whose operand split needs those registers, after the product)
+    constexpr bool PRE_EARLY = PR != PREC_F16X2;
     f32x4 pre[MODE == ATOM_UPDATE_BWD ? N1 / 16 : 1];
-    if constexpr (MODE == ATOM_UPDATE_BWD) {
+    auto fetch_pre = [&]() {
 #pragma unroll
       for (int nb = 0; nb < N1 / 16; ++nb) pre[nb] = bload4(rS, ro1 + 64u * nb);
-    }
+    };
+    if constexpr (MODE == ATOM_UPDATE_BWD && PRE_EARLY) fetch_pre();
     if constexpr (MODE == ATOM_UPDATE_BWD) {
       if (g.Asum && ok) {
 #pragma unroll
@@ -280,6 +309,7 @@ __global__ __launch_bounds__(64 * kAtomNW, 1) void k_atom(AtomArgs g) {
       atom_pair_product<D, N1>(u, in, lds + P::M1, lds + P::M1L, S1[0], lane);
     else
       gemm_om<D, N1, PR>(u, in, lds + P::M1, lane);
+    if constexpr (MODE == ATOM_UPDATE_BWD && !PRE_EARLY) fetch_pre();
     float ep = 0.f;
 #pragma unroll
     for (int nb = 0; nb < N1 / 16; ++nb) {
@@ -339,6 +369,8 @@ __global__ __launch_bounds__(64 * kAtomNW, 1) void k_atom(AtomArgs g) {
         *reinterpret_cast<f32x4*>(g.Y + (size_t)atom * D + g4 + 16 * kb) = v;
       }
     }
+    t += (int)gridDim.x * kAtomNW;
+    if (t < ntiles) fetch(t, in);
   }
 }
 
@@ -373,9 +405,6 @@ __global__ __launch_bounds__(64 * kAtomNW, 1) void k_atom_split(AtomArgs g) {
   constexpr int NH = N1 / 64, NO = D / 64;   // blocks per member
   static_assert(NH >= 1 && NO >= 1, "four members need 64-wide layers");
   extern __shared__ __align__(16) unsigned char lds[];
-  stage_lds<SP::MAT, 64 * kAtomNW>(g.img, lds);
-  __syncthreads();
-
   const int lane = threadIdx.x & 63, e = lane & 15;
   const int wave = uni((int)threadIdx.x >> 6);
   const int grp = wave >> 2, mem = wave & 3;
@@ -385,6 +414,26 @@ __global__ __launch_bounds__(64 * kAtomNW, 1) void k_atom_split(AtomArgs g) {
   const __amdgpu_buffer_rsrc_t rA2 = rsrc(g.A2, g.A2 ? rows * D * 4u : 0u);
   const __amdgpu_buffer_rsrc_t rR = rsrc(g.R, g.R ? rows * D * 4u : 0u);
   const __amdgpu_buffer_rsrc_t rS = rsrc(g.S, g.S ? rows * N1 * 4u : 0u);
+  // a tile's input rows, as in k_atom (each member reads all of them)
+  auto fetch = [&](int t, f32x4 (&in)[D / 16]) {
+    const int g4 = 4 * (opaque(lane) >> 4);
+    const int atom = t * kAtoms + e;
+    const uint32_t ro = ((uint32_t)atom * D + (uint32_t)g4) * 4u;
+#pragma unroll
+    for (int kb = 0; kb < D / 16; ++kb) {
+      in[kb] = bload4(rA, ro + 64u * kb);
+      if constexpr (MODE == ATOM_UPDATE_BWD) in[kb] += bload4(rA2, ro + 64u * kb);
+    }
+    if (g.cut_side) add_cut_parts<D>(in, g, atom, atom < g.M, g4);
+  };
+  // the first round's rows are fetched while the work-group stages the weights
+  f32x4 in[D / 16];
+  {
+    const int t = (int)blockIdx.x + (int)gridDim.x * grp;
+    if (t < ntiles) fetch(t, in);
+  }
+  stage_lds<SP::MAT, 64 * kAtomNW>(g.img, lds);
+  __syncthreads();
   const unsigned char* gimg = reinterpret_cast<const unsigned char*>(g.img);
   const float* V1 = reinterpret_cast<const float*>(gimg + P::V1);
   const float* V2 = reinterpret_cast<const float*>(gimg + P::V2);
@@ -395,6 +444,7 @@ __global__ __launch_bounds__(64 * kAtomNW, 1) void k_atom_split(AtomArgs g) {
 
   // every wave runs the same number of rounds (group 0's tiles); a group
   // without a tile in a round still meets both barriers
+  // (the next round's rows are fetched at the end of each round)
   for (int t0 = (int)blockIdx.x; t0 < ntiles; t0 += (int)gridDim.x * 4) {
     const int t = t0 + (int)gridDim.x * grp;
     const bool active = t < ntiles;
@@ -407,12 +457,6 @@ __global__ __launch_bounds__(64 * kAtomNW, 1) void k_atom_split(AtomArgs g) {
     // after the barrier (Asum may be A, which the other members still read)
     f32x4 sum[MODE == ATOM_UPDATE_BWD ? NO : 1];
     if (active) {
-      f32x4 in[D / 16];
-#pragma unroll
-      for (int kb = 0; kb < D / 16; ++kb) {
-        in[kb] = bload4(rA, ro + 64u * kb);
-        if constexpr (MODE == ATOM_UPDATE_BWD) in[kb] += bload4(rA2, ro + 64u * kb);
-      }
       f32x4 pre[MODE == ATOM_UPDATE_BWD ? NH : 1];
       if constexpr (MODE == ATOM_UPDATE_BWD) {
 #pragma unroll
@@ -491,6 +535,10 @@ __global__ __launch_bounds__(64 * kAtomNW, 1) void k_atom_split(AtomArgs g) {
           *reinterpret_cast<f32x4*>(g.Y + (size_t)atom * D + c) = v;
         }
       }
+    }
+    {
+      const int tn = t + (int)gridDim.x * 4;
+      if (tn < ntiles) fetch(tn, in);
     }
     __syncthreads();
   }
@@ -604,12 +652,29 @@ constexpr int kEnergyThreads = 1024;
 __global__ __launch_bounds__(kEnergyThreads) void k_finish(const float* eps, int n_rep, int n_per,
                                                            float* energy, const float* fb, int T,
                                                            int64_t n3, float* forces, float* vel,
-                                                           float half_kick, DevStatus* st) {
+                                                           float half_kick, const int32_t* rowptr,
+                                                           int G, const float* side_f,
+                                                           int64_t side_stride, DevStatus* st) {
   if ((int)blockIdx.x >= n_rep) {
     const int64_t k = (int64_t)(blockIdx.x - n_rep) * kEnergyThreads + threadIdx.x;
     if (k >= n3) return;
+    const int64_t i = k / 3;
+    const int c = (int)(k - 3 * i);
+    int w0 = 0, w1 = 0;
+    if (side_f) {
+      const int64_t E = rowptr[n3 / 3];
+      cut_workers(rowptr[i], rowptr[i + 1], (E + 15) / 16, G, w0, w1);
+    }
     float s = 0.f;
-    for (int t = 0; t < T; ++t) s += fb[(int64_t)t * n3 + k];
+    for (int t = 0; t < T; ++t) {
+      float v = fb[(int64_t)t * n3 + k];
+      if (w0 < w1) {   // block t's row completed by the other workers' parts
+        float acc = 0.f;
+        for (int w = w0; w < w1; ++w) acc += side_f[t * side_stride + 3 * w + c];
+        v += acc;
+      }
+      s += v;
+    }
     const float f = -s;
     forces[k] = f;
     if (vel) vel[k] += half_kick * f;
@@ -640,11 +705,13 @@ __global__ __launch_bounds__(kEnergyThreads) void k_finish(const float* eps, int
 
 hipError_t launch_finish(const float* eps, int n_rep, int n_per, float* energy, const float* fb,
                          int T, int64_t n_atoms, float* forces, float* vel, float half_kick,
+                         const int32_t* rowptr, int G, const float* side_f, int64_t side_stride,
                          DevStatus* st, hipStream_t s) {
   const int64_t n3 = 3 * n_atoms;
   const int64_t nb = n_rep + (n3 + kEnergyThreads - 1) / kEnergyThreads;
   hipLaunchKernelGGL(k_finish, dim3((unsigned)nb), dim3(kEnergyThreads), 0, s, eps, n_rep, n_per,
-                     energy, fb, T, n3, forces, vel, half_kick, st);
+                     energy, fb, T, n3, forces, vel, half_kick, rowptr, G, side_f, side_stride,
+                     st);
   return hipGetLastError();
 }
 

@@ -175,9 +175,9 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
   p.pos = pos;
   p.wg_start = wg_start;
   p.wg_edge = wg_edge;
-  p.side_recv = reinterpret_cast<int32_t*>(ws + L.side_recv);
   p.side_h = reinterpret_cast<float*>(ws + L.side_h);
-  p.side_f = reinterpret_cast<float*>(ws + L.side_f);
+  float* side_f = reinterpret_cast<float*>(ws + L.side_f);   // one [workers][3] array per block
+  constexpr int64_t kSideF = (int64_t)kMaxWorkers * 3;
   p.n_atoms = (int)n;
   p.periodic = sys->periodic;
   p.box = sys->box;
@@ -279,15 +279,17 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
       ua.h = gbuf;
       if ((e = uf_block(t, UF_FORWARD)) != hipSuccess) return hip_fail(e);
     } else {
-      {
-        ProfScope ps(0, s);
-        if ((e = launch_cf_forward(D, m->KP, prec, p, Gf, s)) != hipSuccess) return hip_fail(e);
-      }
-      if ((e = launch_cf_fixup(p, Gf * wf, D, gbuf, nullptr, s)) != hipSuccess)
-        return hip_fail(e);
+      ProfScope ps(0, s);
+      if ((e = launch_cf_forward(D, m->KP, prec, p, Gf, s)) != hipSuccess) return hip_fail(e);
     }
+    // h of receivers cut by the forward's worker boundaries is completed as it is read
     AtomArgs u{ATOM_UPDATE_FWD, (int)n, gbuf, nullptr, nullptr, x + t * ND, nullptr, au + t * ND,
                x + (t + 1) * ND, 0.f, nullptr, atom_img(t, 0)};
+    if (!uf) {
+      u.cut_rowptr = rowptr;
+      u.cut_G = Gf * wf;
+      u.cut_side = p.side_h;
+    }
     if ((e = launch_atom(u, D, D, prec, m->n_cu, s)) != hipSuccess) return hip_fail(e);
   }
   // readout and its gradient
@@ -300,6 +302,11 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
     const bool has_q = t < T - 1;
     AtomArgs b{ATOM_UPDATE_BWD, (int)n, gx, has_q ? tmp : nullptr, (has_q && t > 0) ? gx : nullptr,
                nullptr, au + t * ND, nullptr, gbuf, 0.f, nullptr, atom_img(t, 1)};
+    if (!uf && has_q) {   // q of the previous backward launch, completed as it is read
+      b.cut_rowptr = rowptr;
+      b.cut_G = Gb * wb;
+      b.cut_side = p.side_h;
+    }
     if ((e = launch_atom(b, D, D, prec, m->n_cu, s)) != hipSuccess) return hip_fail(e);
     p.img = block_img(t);
     p.wg_start = wg_start_b;
@@ -308,24 +315,22 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
     p.gh = gbuf;
     p.q_out = t > 0 ? tmp : nullptr;
     p.forces = fblk + (size_t)t * n * 3;
+    p.side_f = side_f + t * kSideF;
     if (uf) {
       ua.gh = gbuf;
       ua.q = t > 0 ? tmp : nullptr;
       if ((e = uf_block(t, UF_BACKWARD)) != hipSuccess) return hip_fail(e);
     } else {
-      {
-        ProfScope ps(1, s);
-        if ((e = launch_cf_backward(D, m->KP, prec, p, Gb, s)) != hipSuccess)
-          return hip_fail(e);
-      }
-      if ((e = launch_cf_fixup(p, Gb * wb, D, p.q_out, p.forces, s)) != hipSuccess)
-        return hip_fail(e);
+      ProfScope ps(1, s);
+      if ((e = launch_cf_backward(D, m->KP, prec, p, Gb, s)) != hipSuccess) return hip_fail(e);
     }
   }
   // replica energies, and the forces (the unfused pipeline accumulates dE/dr
-  // of every block into one array)
+  // of every block into one array), each block's rows of cut receivers
+  // completed from its side parts
   if ((e = launch_finish(eps, sys->n_replicas, sys->atoms_per_replica, energy, fblk, uf ? 1 : T, n,
-                         forces, vel_kick, half_kick, st, s)) != hipSuccess)
+                         forces, vel_kick, half_kick, rowptr, Gb * wb, uf ? nullptr : side_f,
+                         kSideF, st, s)) != hipSuccess)
     return hip_fail(e);
   return SN_OK;
 }
@@ -425,9 +430,8 @@ WsLayout ws_layout(int64_t n, int D, int T, int H) {
   L.wg_start_b = take((size_t)(kMaxWorkers + 1) * 4);
   L.wg_edge = take((size_t)(kMaxWorkers + 1) * 4);
   L.wg_edge_b = take((size_t)(kMaxWorkers + 1) * 4);
-  L.side_recv = take((size_t)kMaxWorkers * 4);
   L.side_h = take((size_t)kMaxWorkers * (size_t)D * 4);
-  L.side_f = take((size_t)kMaxWorkers * 3 * 4);
+  L.side_f = take((size_t)T * kMaxWorkers * 3 * 4);
   L.scan_blocks = take((size_t)(scan_n / kScanChunk + 2) * 8);
   L.cell_count = take((size_t)(ncell + 1) * 4);
   L.cell_start = take((size_t)ncell * 4);

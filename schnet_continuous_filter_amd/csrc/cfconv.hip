@@ -15,7 +15,9 @@
 // (k_setup gives every worker the same number of whole tiles, to one).
 // A receiver whose edges a worker boundary cuts is written by the worker
 // holding its last edge; the earlier workers leave their parts in side
-// buffers, which k_cf_fixup adds in worker order (no atomics; fixed order).
+// buffers, which the kernels that next read the output add in worker order
+// (no atomics; fixed order; cut_workers names the workers from the row
+// pointers alone).
 //
 // Edge-on-lane products. Every product is computed transposed,
 // OUT^T[n][e] = sum_k W^T[n][k] IN^T[k][e], on 16x16 MFMA blocks: the weights
@@ -596,10 +598,7 @@ __device__ __forceinline__ bool worker_range(const CfParams& p, int wave, Walk& 
   // the next worker's first receiver, if it started before E1, is ours too
   w.tail = cload(p.rowptr, ia1) < w.E1;
   w.ib = ia1 + (w.tail ? 1 : 0);
-  if (w.ia >= w.ib) {
-    if ((threadIdx.x & 63) == 0) p.side_recv[w.rid] = -1;
-    return false;
-  }
+  if (w.ia >= w.ib) return false;
   w.rrow = rsrc(p.rowptr, (N + 1) * 4u);
   w.rcol = rsrc(p.col, (uint32_t)cload(p.rowptr, (int)N) * 4u);
   w.rpos = rsrc(p.pos, N * 12u);
@@ -745,7 +744,6 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, false>()), 1) void k_cf_fwd(CfPa
     for (int pss = 0; pss < NB / 4; ++pss)
       p.side_h[(size_t)wk.rid * D + 64 * pss + fcol] = carry[pss];
   }
-  if (lane == 0) p.side_recv[wk.rid] = wk.tail ? ib - 1 : -1;
 }
 
 template <int D, int KP, int PR>
@@ -962,7 +960,6 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, true>()), 1) void k_cf_bwd(CfPar
     if (lane < 3)
       p.side_f[(size_t)wk.rid * 3 + lane] = lane == 0 ? fcarry[0] : (lane == 1 ? fcarry[1] : fcarry[2]);
   }
-  if (lane == 0) p.side_recv[wk.rid] = wk.tail ? ib - 1 : -1;
 }
 
 // ------------------------------------------------------------------ small kernels
@@ -1039,48 +1036,6 @@ hipError_t launch_setup(const int32_t* rowptr, int n_atoms, int G1, int32_t* wg_
   hipLaunchKernelGGL(k_setup, dim3((unsigned)nb), dim3(kThreads), 0, s, rowptr, n_atoms, G1,
                      wg_start1, wg_edge1, G2, wg_start2, wg_edge2, nbp, types, emb, log2D, n_types,
                      x, st);
-  return hipGetLastError();
-}
-
-// Receivers cut by worker boundaries: the worker holding a receiver's last
-// edge wrote its own part to the output; the earlier workers' parts (side
-// buffers, consecutive workers) are summed in worker order and added once,
-// by the last of those workers. One wave per worker.
-__global__ __launch_bounds__(kThreads) void k_cf_fixup(const int32_t* __restrict__ side_recv,
-                                                       const float* __restrict__ side_h,
-                                                       const float* __restrict__ side_f, int G,
-                                                       int D, float* out_h, float* out_f) {
-  const int w = (int)blockIdx.x * (kThreads / 64) + ((int)threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (w >= G) return;
-  // the worker's own entry and both neighbours' in one round trip
-  const int r = side_recv[w];
-  const int rn = w + 1 < G ? side_recv[w + 1] : -1;
-  const int rp = w > 0 ? side_recv[w - 1] : -1;
-  if (r < 0 || rn == r) return;
-  int f = w;
-  if (rp == r) {
-    f = w - 1;
-    while (f > 0 && side_recv[f - 1] == r) --f;
-  }
-  if (out_h) {
-    for (int c = lane; c < D; c += 64) {
-      float acc = 0.f;
-      for (int k = f; k <= w; ++k) acc += side_h[(size_t)k * D + c];
-      out_h[(size_t)r * D + c] += acc;
-    }
-  }
-  if (out_f && lane < 3) {
-    float acc = 0.f;
-    for (int k = f; k <= w; ++k) acc += side_f[(size_t)k * 3 + lane];
-    out_f[(size_t)r * 3 + lane] += acc;
-  }
-}
-
-hipError_t launch_cf_fixup(const CfParams& p, int G, int D, float* out_h, float* out_f,
-                           hipStream_t s) {
-  hipLaunchKernelGGL(k_cf_fixup, dim3((unsigned)((G + kThreads / 64 - 1) / (kThreads / 64))),
-                     dim3(kThreads), 0, s, p.side_recv, p.side_h, p.side_f, G, D, out_h, out_f);
   return hipGetLastError();
 }
 

@@ -70,7 +70,7 @@ __device__ inline void dev_fail(DevStatus* st, int code, int64_t detail) {
 
 // Offsets (bytes) of everything carved out of a workspace.
 struct WsLayout {
-  size_t status, wg_start, wg_start_b, wg_edge, wg_edge_b, side_recv, side_h, side_f;
+  size_t status, wg_start, wg_start_b, wg_edge, wg_edge_b, side_h, side_f;
   size_t scan_blocks, cell_count, cell_start, cell_atoms, atom_cell;
   size_t x, au, gbuf, tmp, gx, fblk, eps, total;
 };
@@ -110,9 +110,9 @@ struct CfParams {
   const int32_t* wg_edge;   // per worker: first edge (a multiple of 16)
   // receivers cut by worker boundaries: the part a worker holds of its last,
   // unfinished receiver (side_h [workers][D] features, side_f [workers][3]
-  // force rows) and that receiver (side_recv, -1 for none); k_cf_fixup adds
-  // them to the finishing worker's output
-  int32_t* side_recv;
+  // force rows); the worker holding the receiver's last edge writes its own
+  // part to the output, and the kernels that next read that output add the
+  // other parts (cut_workers names the workers)
   float* side_h;
   float* side_f;
   int n_atoms;
@@ -151,10 +151,6 @@ hipError_t launch_setup(const int32_t* rowptr, int n_atoms, int G1, int32_t* wg_
                         int32_t* wg_edge1, int G2, int32_t* wg_start2, int32_t* wg_edge2,
                         const int32_t* types, const float* emb, int D, int n_types, float* x,
                         DevStatus* st, hipStream_t s);
-// Adds the side partials of the G workers of the last CFConv launch to out_h
-// [N][D] and out_f [N][3] (either may be null).
-hipError_t launch_cf_fixup(const CfParams& p, int G, int D, float* out_h, float* out_f,
-                           hipStream_t s);
 hipError_t launch_cf_forward(int D, int KP, int prec, const CfParams& p, int G, hipStream_t s);
 hipError_t launch_cf_backward(int D, int KP, int prec, const CfParams& p, int G, hipStream_t s);
 
@@ -172,6 +168,12 @@ struct AtomArgs {
   float b2s;          // readout output bias
   float* eps;         // per-atom energies [M] (readout)
   const void* img;    // the network's weight image (atom_fill_image)
+  // receivers of the CFConv launch (cut_G workers over the list cut_rowptr)
+  // that wrote A (update fwd) or A2 (update bwd) whose parts cut_side
+  // [workers][D] holds; null: none
+  const int32_t* cut_rowptr;
+  int cut_G;
+  const float* cut_side;
 };
 // Weight image of one atom-wise network for `mode`: W1 [D][N1], b1 [N1],
 // W2 [N1][D] (readout: wo2 [N1]), b2 [D]; built on the host.
@@ -183,9 +185,12 @@ void atom_fill_image(int mode, int D, int N1, int prec, const float* W1, const f
 hipError_t atom_prepare(int D, int H, int prec);   // raises the dynamic LDS limit of the kernels
 hipError_t launch_atom(const AtomArgs& g, int D, int N1, int prec, int n_cu, hipStream_t s);
 // Per-replica energies (double sums of eps) and F = -(sum over the T blocks
-// of fb), in one launch; with vel, also vel += half_kick F.
+// of fb), in one launch; with vel, also vel += half_kick F. With side_f,
+// block t's rows of receivers cut by the G workers of its CFConv launch
+// (over the list rowptr) gain their parts side_f[t * side_stride + 3 w].
 hipError_t launch_finish(const float* eps, int n_rep, int n_per, float* energy, const float* fb,
                          int T, int64_t n_atoms, float* forces, float* vel, float half_kick,
+                         const int32_t* rowptr, int G, const float* side_f, int64_t side_stride,
                          DevStatus* st, hipStream_t s);
 
 // Unfused edge pipeline (unfused.hip): one kernel per step, edge tensors in

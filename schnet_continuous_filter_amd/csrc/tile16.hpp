@@ -82,6 +82,22 @@ __device__ __forceinline__ void stage_lds(const void* src, unsigned char* lds) {
   }
 }
 
+// Receivers cut by worker boundaries. A CFConv launch with G workers over a
+// list of E edges (T = ceil(E / 16) tiles) starts worker v at edge
+// 16 floor(v T / G). Worker w holds a part of receiver r, whose edges are
+// [a, b), when its end (worker w + 1's start) falls strictly inside (a, b);
+// those workers form the range [w0, w1), empty when r is not cut.
+__device__ __forceinline__ void cut_workers(int64_t a, int64_t b, int64_t T, int G, int& w0,
+                                            int& w1) {
+  w0 = 0;
+  w1 = 0;
+  if (b - a < 2) return;
+  const int64_t j0 = a / 16 + 1, j1 = (b + 15) / 16;   // tile boundaries 16 j inside: j0 <= j < j1
+  if (j0 >= j1) return;
+  w0 = (int)((j0 * G + T - 1) / T) - 1;   // the first worker start past a, minus one
+  w1 = (int)((j1 * G + T - 1) / T) - 1;   // the first worker start at or past b, minus one
+}
+
 // Orders this wave's LDS writes before its later LDS reads (wave-private data).
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
