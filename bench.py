@@ -31,7 +31,23 @@ PEAK_BF16_MFMA_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 PREC_TAGS = {0: "f32", 1: "bf16", 2: "w16a16", 3: "f16x2"}
 DTYPE_TAGS = {0: "f32", 1: "bf16-filter/f32", 2: "f16-mlps/f32", 3: "f16x2-filter/f32"}
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cfconv_bwd_cg269x64_counters.txt")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def bwd_traffic(workload, m):
+    """Counter-measured bytes per k_cf_bwd launch for this workload and filter
+    precision (profiles/cfconv_bwd_<workload>[_f16x2]_counters.txt), or None
+    when no such record exists or the kernels changed since it was taken."""
+    for name in (f"cfconv_bwd_{workload}_counters.txt", f"cfconv_bwd_{workload}_f16x2_counters.txt"):
+        path = os.path.join(PROFILES, name)
+        if not os.path.exists(path):
+            continue
+        rec = json.load(open(path))
+        kern = rec.get("kernel", "")   # "void sn::k_cf_bwd<D, KP, precision>(sn::CfParams)"
+        if (rec.get("kernel_hash") == profiling.kernel_hash() and kern.startswith(f"void sn::k_cf_bwd<{m.D}, ")
+                and f", {m.filter_dtype}>(" in kern and rec.get("workload", "").split("_")[0] == workload):
+            return rec.get("bytes_per_launch")
+    return None
 
 
 def parse():
@@ -378,12 +394,7 @@ def main():
     achieved = flops_bwd / avg_bwd_s / 1e12
     half = m.filter_dtype != 0          # 16-bit operands: the dense fp16/bf16 MFMA peak
     peak = PEAK_BF16_MFMA_TFLOPS if half else PEAK_FP32_MFMA_TFLOPS
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        rec = json.load(open(TRAFFIC_FILE))
-        if (rec.get("kernel_hash") == profiling.kernel_hash() and rec.get("workload") == cfg.name
-                and m.filter_dtype == 0):
-            traffic = rec.get("bytes_per_launch")
+    traffic = bwd_traffic(cfg.name, m)
     line = {
         "metric": "CFConv energy+force edges/sec and replica-MD-steps/sec at 1 GPU; % HBM roofline",
         "value": r["edges_per_s"],
