@@ -106,7 +106,7 @@ struct CfParams {
   const int32_t* rowptr;
   const int32_t* col;
   const float* pos;
-  const int32_t* wg_start;  // per worker: first receiver (launch_partition)
+  const int32_t* wg_start;  // per worker: first receiver (launch_setup)
   const int32_t* wg_edge;   // per worker: first edge (a multiple of 16)
   // receivers cut by worker boundaries: the part a worker holds of its last,
   // unfinished receiver (side_h [workers][D] features, side_f [workers][3]

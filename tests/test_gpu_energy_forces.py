@@ -359,7 +359,8 @@ def test_small_and_large_batches_agree(gpu_lib, dtype):
 @pytest.mark.parametrize("dtype", [0, 3])
 def test_rows_cut_by_worker_boundaries(gpu_lib, dtype):
     """Workers take whole 16-edge tiles, so receiver rows are cut between
-    workers and finished by the fix-up: 16 mutually neighbouring atoms (rows
+    workers, the other workers' parts added where the rows are read (the
+    atom-wise kernels, the force sum): 16 mutually neighbouring atoms (rows
     of 15 against tiles of 16, one tile per worker) and 200 atoms in a 9 A
     ball at about bulk density (rows of ~120-199 edges spanning several
     workers), with biases."""
