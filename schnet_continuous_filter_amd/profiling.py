@@ -18,17 +18,26 @@ import csv
 import hashlib
 import json
 import os
+import re
 
 _CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 CFCONV_SRCS = [os.path.join(_CSRC, f) for f in ("cfconv.hip", "tile16.hpp", "common.hpp")]
 COPY_BYTES = 256 * 1024 * 1024
 
 
+def code_text(src: str) -> str:
+    """C++ source without its comments and blank or trailing space, so that an
+    edit of a comment does not change the hash of the code."""
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return "\n".join(line.rstrip() for line in src.splitlines() if line.strip())
+
+
 def kernel_hash() -> str:
-    """Hash of the sources the CFConv kernels are compiled from."""
+    """Hash of the code (comments removed) the CFConv kernels are compiled from."""
     h = hashlib.sha256()
     for f in CFCONV_SRCS:
-        h.update(open(f, "rb").read())
+        h.update(code_text(open(f, encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 
