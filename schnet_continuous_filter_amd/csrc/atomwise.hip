@@ -247,6 +247,10 @@ __global__ __launch_bounds__(64 * kAtomNW, 1) void k_atom(AtomArgs g) {
   const __amdgpu_buffer_rsrc_t rA2 = rsrc(g.A2, g.A2 ? rows * D * 4u : 0u);
   const __amdgpu_buffer_rsrc_t rR = rsrc(g.R, g.R ? rows * D * 4u : 0u);
   const __amdgpu_buffer_rsrc_t rS = rsrc(g.S, g.S ? rows * N1 * 4u : 0u);
+  // outputs through bounded stores: rows past M are dropped without a branch
+  const __amdgpu_buffer_rsrc_t rY = rsrc(g.Y, rows * D * 4u);
+  const __amdgpu_buffer_rsrc_t rAo = rsrc(g.Aout, g.Aout ? rows * N1 * 4u : 0u);
+  const __amdgpu_buffer_rsrc_t rAs = rsrc(g.Asum, g.Asum ? rows * D * 4u : 0u);
   // a tile's input rows: A (+ A2), every load issued before the first is
   // waited for (a missing A2 and rows past M read 0 through their bounded
   // resources), then the parts of receivers cut by the CFConv launch
@@ -293,11 +297,8 @@ __global__ __launch_bounds__(64 * kAtomNW, 1) void k_atom(AtomArgs g) {
     };
     if constexpr (MODE == ATOM_UPDATE_BWD && PRE_EARLY) fetch_pre();
     if constexpr (MODE == ATOM_UPDATE_BWD) {
-      if (g.Asum && ok) {
 #pragma unroll
-        for (int kb = 0; kb < D / 16; ++kb)
-          *reinterpret_cast<f32x4*>(g.Asum + (size_t)atom * D + g4 + 16 * kb) = in[kb];
-      }
+      for (int kb = 0; kb < D / 16; ++kb) bstore4(rAs, ro + 64u * kb, in[kb]);
     }
 
     if constexpr (SC && MODE == ATOM_UPDATE_BWD) {   // contraction over Wu2's columns
@@ -317,7 +318,7 @@ __global__ __launch_bounds__(64 * kAtomNW, 1) void k_atom(AtomArgs g) {
       if constexpr (MODE == ATOM_UPDATE_FWD) {
         const f32x4 b = *reinterpret_cast<const f32x4*>(V1 + g4 + 16 * nb);
         const f32x4 a = u[nb] + b;
-        if (ok) *reinterpret_cast<f32x4*>(g.Aout + (size_t)atom * N1 + g4 + 16 * nb) = a;
+        bstore4(rAo, ro1 + 64u * nb, a);
 #pragma unroll
         for (int r = 0; r < 4; ++r) u[nb][r] = ssp(a[r]);
       } else if constexpr (MODE == ATOM_UPDATE_BWD) {
@@ -359,15 +360,13 @@ __global__ __launch_bounds__(64 * kAtomNW, 1) void k_atom(AtomArgs g) {
       atom_pair_product<N1, D>(y, u, lds + P::M2, lds + P::M2L, S1[1], lane);
     else
       gemm_om<N1, D, PR>(y, u, lds + P::M2, lane);
-    if (ok) {
 #pragma unroll
-      for (int kb = 0; kb < D / 16; ++kb) {
-        f32x4 v = y[kb];
-        if constexpr (SC && MODE == ATOM_UPDATE_FWD) v *= v4(S2, g4 + 16 * kb);
-        if constexpr (MODE == ATOM_UPDATE_FWD)
-          v += res[kb] + *reinterpret_cast<const f32x4*>(V2 + g4 + 16 * kb);
-        *reinterpret_cast<f32x4*>(g.Y + (size_t)atom * D + g4 + 16 * kb) = v;
-      }
+    for (int kb = 0; kb < D / 16; ++kb) {
+      f32x4 v = y[kb];
+      if constexpr (SC && MODE == ATOM_UPDATE_FWD) v *= v4(S2, g4 + 16 * kb);
+      if constexpr (MODE == ATOM_UPDATE_FWD)
+        v += res[kb] + *reinterpret_cast<const f32x4*>(V2 + g4 + 16 * kb);
+      bstore4(rY, ro + 64u * kb, v);
     }
     t += (int)gridDim.x * kAtomNW;
     if (t < ntiles) fetch(t, in);
