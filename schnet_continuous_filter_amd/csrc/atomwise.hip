@@ -33,6 +33,12 @@
 namespace sn {
 
 constexpr int kAtomNW = 16;   // waves per work-group (four per SIMD)
+
+// Bounded store: an offset past the resource's size writes nothing.
+__device__ __forceinline__ void bstore4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f32x4 v) {
+  using u32x4 = __attribute__((ext_vector_type(4))) uint32_t;
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, byte_off, 0, 0);
+}
 constexpr int kAtoms = 16;    // atoms per wave tile
 
 // LDS image of one network: M1 [N1][D] (first product, output-major), M2

@@ -25,10 +25,6 @@ __device__ __forceinline__ int bload_i(__amdgpu_buffer_rsrc_t r, uint32_t byte_o
 __device__ __forceinline__ f32x4 bload4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
-// Bounded store: an offset past the resource's size writes nothing.
-__device__ __forceinline__ void bstore4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) uint32_t, v), r, byte_off, 0, 0);
-}
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // Wave-uniform read of a read-only int array through the scalar cache.
