@@ -140,7 +140,7 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
                              const int32_t* types, const int32_t* rowptr, const int32_t* col,
                              float* energy, float* forces, char* ws, hipStream_t s,
                              const UfMode* uf = nullptr, float* vel_kick = nullptr,
-                             float half_kick = 0.f) {
+                             float half_kick = 0.f, const BuildMark* mark = nullptr) {
   const sn_model_desc& d = m->desc;
   const int64_t n = n_atoms(sys);
   const int D = d.D, T = d.T, H = d.H;
@@ -165,7 +165,8 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
   hipError_t e;
 
   if ((e = launch_setup(uf ? nullptr : rowptr, (int)n, Gf * wf, wg_start, wg_edge, Gb * wb,
-                        wg_start_b, wg_edge_b, types, m->w + m->off_emb, D, d.n_types, x, st, s)) !=
+                        wg_start_b, wg_edge_b, types, m->w + m->off_emb, D, d.n_types, x, mark, st,
+                        s)) !=
       hipSuccess)
     return hip_fail(e);
 
@@ -677,11 +678,13 @@ sn_status sn_md_init(const sn_model* m, const sn_system* sys, const int32_t* typ
   if (e == hipSuccess)
     e = launch_build_neighbors(g, state->pos, state->rowptr, state->col, state->edge_capacity, w, L,
                                nullptr, 0, s);
-  if (e == hipSuccess) e = launch_md_mark_build(n, state->pos, state->pos_at_build, st, nullptr, 0, s);
   const int32_t *rp = nullptr, *cl = nullptr;
   if (e == hipSuccess) e = md_eval_list(m, prm, g, state, w, L, s, rp, cl);
   if (e != hipSuccess) return SN_ERR_HIP;
-  return energy_forces_impl(m, sys, state->pos, types, rp, cl, e_out, state->forces, w, s);
+  // the build's positions are kept by the evaluation's set-up launch
+  const BuildMark mark{state->pos, state->pos_at_build, nullptr, 0};
+  return energy_forces_impl(m, sys, state->pos, types, rp, cl, e_out, state->forces, w, s, nullptr,
+                            nullptr, 0.f, &mark);
 }
 
 sn_status sn_md_step(const sn_model* m, const sn_system* sys, const int32_t* types,
@@ -712,13 +715,14 @@ sn_status sn_md_step(const sn_model* m, const sn_system* sys, const int32_t* typ
     const int64_t gval = (int64_t)step + 1;
     e = launch_build_neighbors(g, state->pos, state->rowptr, state->col, state->edge_capacity, w, L,
                                gate, gval, s);
-    if (e == hipSuccess) e = launch_md_mark_build(n, state->pos, state->pos_at_build, st, gate, gval, s);
     const int32_t *rp = nullptr, *cl = nullptr;
     if (e == hipSuccess) e = md_eval_list(m, prm, g, state, w, L, s, rp, cl);
     if (e != hipSuccess) return SN_ERR_HIP;
-    // the closing half-kick B runs in the launch that sums the forces
+    // the build mark (when this step rebuilt) runs in the evaluation's set-up
+    // launch, the closing half-kick B in the launch that sums the forces
+    const BuildMark mark{state->pos, state->pos_at_build, gate, gval};
     rc = energy_forces_impl(m, sys, state->pos, types, rp, cl, e_out, state->forces, w, s, nullptr,
-                            state->vel, su.c.half_kick);
+                            state->vel, su.c.half_kick, &mark);
     if (rc != SN_OK) return rc;
     state->step = step + 1;
   }

@@ -993,21 +993,29 @@ __device__ __forceinline__ void partition_one(const int32_t* rowptr, int N, int6
 
 // Set-up of one evaluation in one launch. The first nbp blocks write both
 // kernels' partitions (threads 0..G1 the first, the next G2 + 1 threads the
-// second; nbp = 0 when no partition is wanted); the blocks after them write
+// second; nbp = 0 when no partition is wanted); the next nbe blocks write
 // the initial features x[i][:] = Emb[types[i]][:] (FlashSchNet §3.2 "SchNet
-// model"), four features per thread.
+// model"), four features per thread; any blocks after them apply the MD
+// build mark (BuildMark), one position component per thread.
 __global__ __launch_bounds__(kThreads) void k_setup(const int32_t* rowptr, int N, int G1,
                                                     int32_t* wg_start1, int32_t* wg_edge1, int G2,
                                                     int32_t* wg_start2, int32_t* wg_edge2, int nbp,
                                                     const int32_t* types, const float* emb,
-                                                    int log2D, int n_types, float* x,
-                                                    DevStatus* st) {
+                                                    int log2D, int n_types, float* x, int nbe,
+                                                    BuildMark mark, DevStatus* st) {
   if ((int)blockIdx.x < nbp) {
     const int t = blockIdx.x * kThreads + threadIdx.x;
     const int64_t E = rowptr[N];
     if (t == 0 && E >= kMaxListEdges) dev_fail(st, SN_ERR_UNSUPPORTED, E);
     if (t <= G1) partition_one(rowptr, N, E, G1, t, wg_start1, wg_edge1);
     else if (t <= G1 + 1 + G2) partition_one(rowptr, N, E, G2, t - G1 - 1, wg_start2, wg_edge2);
+    return;
+  }
+  if ((int)blockIdx.x >= nbp + nbe) {
+    if (mark.gate != nullptr && *mark.gate != mark.gate_val) return;
+    const int64_t k = (int64_t)(blockIdx.x - nbp - nbe) * kThreads + threadIdx.x;
+    if (k == 0) st->n_rebuilds += 1;
+    if (k < 3 * (int64_t)N) mark.pos_at_build[k] = mark.pos[k];
     return;
   }
   const int64_t idx = (int64_t)(blockIdx.x - nbp) * kThreads + threadIdx.x;   // float4 index
@@ -1027,15 +1035,18 @@ __global__ __launch_bounds__(kThreads) void k_setup(const int32_t* rowptr, int N
 hipError_t launch_setup(const int32_t* rowptr, int n_atoms, int G1, int32_t* wg_start1,
                         int32_t* wg_edge1, int G2, int32_t* wg_start2, int32_t* wg_edge2,
                         const int32_t* types, const float* emb, int D, int n_types, float* x,
-                        DevStatus* st, hipStream_t s) {
+                        const BuildMark* mark, DevStatus* st, hipStream_t s) {
   const int nbp = rowptr ? (G1 + 1 + G2 + 1 + kThreads - 1) / kThreads : 0;
   const int log2D = D == 128 ? 7 : 6;
   const int64_t n4 = (int64_t)n_atoms * D / 4;
-  const int64_t nb = nbp + (n4 + kThreads - 1) / kThreads;
+  const int nbe = (int)((n4 + kThreads - 1) / kThreads);
+  const int nbm = mark ? std::max(1, (int)((3 * (int64_t)n_atoms + kThreads - 1) / kThreads)) : 0;
+  const int64_t nb = (int64_t)nbp + nbe + nbm;
   if (nb == 0) return hipSuccess;
+  const BuildMark mk = mark ? *mark : BuildMark{};
   hipLaunchKernelGGL(k_setup, dim3((unsigned)nb), dim3(kThreads), 0, s, rowptr, n_atoms, G1,
                      wg_start1, wg_edge1, G2, wg_start2, wg_edge2, nbp, types, emb, log2D, n_types,
-                     x, st);
+                     x, nbe, mk, st);
   return hipGetLastError();
 }
 

@@ -145,12 +145,22 @@ size_t cf_image_bytes(int D, int KP, int prec);
 void cf_fill_image(int D, int KP, int prec, int Dr, const float* Wf1, const float* cf1,
                    const float* Wf2, const float* cf2, float rbf_step, float r_cut,
                    unsigned char* out);
+// MD bookkeeping that joins the set-up launch: when *gate == gate_val (or
+// gate is null), the positions of a list build are kept (pos_at_build =
+// pos) and the build is counted (DevStatus::n_rebuilds).
+struct BuildMark {
+  const float* pos;
+  float* pos_at_build;
+  const int64_t* gate;
+  int64_t gate_val;
+};
 // Both CFConv kernels' worker partitions of the receiver CSR (skipped when
-// rowptr is null) and the initial features x = Emb[types], in one launch.
+// rowptr is null), the initial features x = Emb[types] and, with mark, the
+// build mark, in one launch.
 hipError_t launch_setup(const int32_t* rowptr, int n_atoms, int G1, int32_t* wg_start1,
                         int32_t* wg_edge1, int G2, int32_t* wg_start2, int32_t* wg_edge2,
                         const int32_t* types, const float* emb, int D, int n_types, float* x,
-                        DevStatus* st, hipStream_t s);
+                        const BuildMark* mark, DevStatus* st, hipStream_t s);
 hipError_t launch_cf_forward(int D, int KP, int prec, const CfParams& p, int G, hipStream_t s);
 hipError_t launch_cf_backward(int D, int KP, int prec, const CfParams& p, int G, hipStream_t s);
 
@@ -253,8 +263,6 @@ hipError_t launch_md_wrap(const MdCoef& c, int64_t n, float* pos, hipStream_t s)
 hipError_t launch_md_baoa(const MdCoef& c, int64_t n, uint64_t step, float* pos, float* vel,
                           const float* forces, const float* pos_at_build, DevStatus* st,
                           hipStream_t s);
-hipError_t launch_md_mark_build(int64_t n, const float* pos, float* pos_at_build, DevStatus* st,
-                                const int64_t* gate, int64_t gate_val, hipStream_t s);
 hipError_t launch_philox(const uint64_t* ctr, uint64_t k0, uint64_t k1, uint64_t* out, int64_t n,
                          hipStream_t s);
 

@@ -102,16 +102,6 @@ __global__ __launch_bounds__(kThreads) void k_md_baoa(MdCoef c, int64_t n, uint6
   if (d2 > c.half_skin2) st->rebuild_req = (int64_t)step + 1;
 }
 
-__global__ __launch_bounds__(kThreads) void k_md_mark_build(int64_t n, const float* pos,
-                                                            float* pos_at_build, DevStatus* st,
-                                                            const int64_t* gate, int64_t gate_val) {
-  if (gate != nullptr && *gate != gate_val) return;
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i == 0) st->n_rebuilds += 1;
-  if (i >= 3 * n) return;
-  pos_at_build[i] = pos[i];
-}
-
 __global__ __launch_bounds__(kThreads) void k_philox(const uint64_t* ctr, uint64_t k0, uint64_t k1,
                                                      uint64_t* out, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -136,12 +126,6 @@ hipError_t launch_md_baoa(const MdCoef& c, int64_t n, uint64_t step, float* pos,
                           hipStream_t s) {
   hipLaunchKernelGGL(k_md_baoa, grid_for(n), dim3(kThreads), 0, s, c, n, step, pos, vel, forces,
                      pos_at_build, st);
-  return hipGetLastError();
-}
-hipError_t launch_md_mark_build(int64_t n, const float* pos, float* pos_at_build, DevStatus* st,
-                                const int64_t* gate, int64_t gate_val, hipStream_t s) {
-  hipLaunchKernelGGL(k_md_mark_build, grid_for(3 * n), dim3(kThreads), 0, s, n, pos, pos_at_build,
-                     st, gate, gate_val);
   return hipGetLastError();
 }
 hipError_t launch_philox(const uint64_t* ctr, uint64_t k0, uint64_t k1, uint64_t* out, int64_t n,
