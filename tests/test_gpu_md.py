@@ -150,6 +150,25 @@ def test_skin_guard_forces_rebuild(gpu_lib):
         lib.sn_model_destroy(model)
 
 
+def test_scheduled_rebuilds_counted_once_each(gpu_lib):
+    """With a 3 A skin the guard cannot trip in 20 steps of 2 fs (the beads
+    move ~0.1 A), so the builds are exactly the initial one and the scheduled
+    ones at steps 4, 9, 14 and 19 (every 5), each counted once, split over
+    two calls."""
+    lib = gpu_lib
+    cfg, m, pos, types, w, desc, system, model, ws, t, params, state, energy = _md_setup(
+        lib, "cg269x64", 2, skin=3.0, rebuild_every=5)
+    try:
+        lib.sn_md_init(model, system, t, params, state, energy, ws)
+        lib.sn_md_step(model, system, t, params, state, 7, energy, ws)
+        lib.sn_md_step(model, system, t, params, state, 13, energy, ws)
+        st, det, nrb = lib.sn_get_device_status(ws)
+        assert st == 0
+        assert nrb == 1 + 4, f"{nrb} builds"
+    finally:
+        lib.sn_model_destroy(model)
+
+
 def test_zero_model_keeps_temperature(gpu_lib):
     """Zero weights give zero forces: the O step is then the exact OU process
     and the kinetic temperature stays at 300 K."""
