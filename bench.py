@@ -434,6 +434,8 @@ def main():
             "replica_steps_per_s": r2["replica_steps_per_s"], "dtype": DTYPE_TAGS[3],
             "bwd_avg_launch_us": r2["bwd_ms"] * 1000.0 / max(r2["bwd_n"], 1),
             "fwd_avg_launch_us": r2["fwd_ms"] * 1000.0 / max(r2["fwd_n"], 1),
+            # counter-measured bytes per backward launch of this path (or None)
+            "bwd_traffic": bwd_traffic(cfg.name, m2),
             "parity": "fp32 bars (energy 1e-5 relative, forces 1e-4 of the force RMS)"}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
