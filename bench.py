@@ -30,7 +30,7 @@ PEAK_FP32_MFMA_TFLOPS = 157.3     # MI355X dense fp32 matrix peak
 PEAK_BF16_MFMA_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 PREC_TAGS = {0: "f32", 1: "bf16", 2: "w16a16", 3: "f16x2"}
-DTYPE_TAGS = {0: "f32", 1: "bf16-filter/f32", 2: "f16-mlps/f32", 3: "f16x2-filter/f32"}
+DTYPE_TAGS = {0: "f32", 1: "bf16-filter/f16x2-atomwise/f32", 2: "f16-mlps/f32", 3: "f16x2-filter/f32"}
 PROFILES = os.path.join(ROOT, "profiles")
 
 

@@ -55,7 +55,10 @@ typedef enum {
  *  SN_FILTER_F32   every product in fp32;
  *  SN_FILTER_BF16  the filter network's products take bfloat16 operands
  *                  (weights rounded to nearest even, activations rounded as
- *                  they enter a product); the other layers stay fp32;
+ *                  they enter a product); the update and readout layers
+ *                  keep fp32-grade products (in the fused calls on fp16
+ *                  pairs, as SN_FILTER_F16X2 describes; in the unfused
+ *                  pipeline in fp32);
  *  SN_W16A16       every MLP (filter, update, readout) takes fp16 operands,
  *                  with per-output-channel scales (§4.4 "Channel-wise
  *                  quantization"): each weight column n is stored as

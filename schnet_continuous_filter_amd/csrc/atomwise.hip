@@ -605,16 +605,19 @@ struct AtomKernels {
   }
 };
 
-// Atom-wise layers run fp32 operands unless every MLP is 16-bit (PREC_F16S)
-// or the model's products run on fp16 pairs (PREC_F16X2); a bfloat16 filter
-// network leaves them fp32.
+// Atom-wise operands: fp16 when every MLP is 16-bit (PREC_F16S); fp16 pairs,
+// which give fp32-grade products, when the model's products run on pairs
+// (PREC_F16X2) and also behind a bfloat16 filter (PREC_BF16), whose
+// atom-wise layers stay fp32-grade; fp32 otherwise.
 template <class R, class F>
 static R atom_dispatch(int D, int N1, int prec, R fail, F f) {
 #define SN_AT(DD, NN, PP) \
   if (D == DD && N1 == NN && ap == PP) return f(AtomKernels<DD, NN, PP>{});
 #define SN_AT_P(PP) \
   SN_AT(64, 64, PP) SN_AT(128, 128, PP) SN_AT(64, 32, PP) SN_AT(128, 32, PP) SN_AT(128, 64, PP)
-  const int ap = (prec == PREC_F16S || prec == PREC_F16X2) ? prec : PREC_F32;
+  const int ap = prec == PREC_F16S                          ? PREC_F16S
+                 : (prec == PREC_F16X2 || prec == PREC_BF16) ? PREC_F16X2
+                                                             : PREC_F32;
   SN_AT_P(PREC_F32) SN_AT_P(PREC_F16S) SN_AT_P(PREC_F16X2)
 #undef SN_AT_P
 #undef SN_AT

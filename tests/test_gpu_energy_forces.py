@@ -326,15 +326,16 @@ def test_bulk64k_sampled_forces_vs_oracle(gpu_lib):
 
 @pytest.mark.parametrize("dtype", [0, 1, 2, 3])
 def test_small_and_large_batches_agree(gpu_lib, dtype):
-    """With fp32 operands (the fp32 and the bf16 filter) and up to two 16-atom
+    """With fp32 atom-wise operands (the fp32 filter) and up to two 16-atom
     tiles per SIMD, the atom-wise networks run with four waves per tile (each
     a quarter of the hidden and output features), above that with one. The
     first 8 replicas of a 160-replica batch of the MD model's chains (2,690
     tiles) against the same 8 alone (135 tiles): same energies and forces
-    within the fp32 bars (1e-5 relative, 1e-4 of the force RMS); for W16A16
+    within the fp32 bars (1e-5 relative, 1e-4 of the force RMS); for the
+    bf16 filter and fp16 pairs (atom-wise layers on fp16 pairs) and W16A16
     (within its own bars: an fp32 rounding difference in a feature can move
-    one of its fp16 roundings) and fp16 pairs, which take one wave per tile
-    at both sizes, a check of size invariance alone."""
+    one of its fp16 roundings), which take one wave per tile at both sizes,
+    a check of size invariance alone."""
     import dataclasses
     cfg, pos, types, w = make_config("md1024", n_replicas=160)
     m = dataclasses.replace(cfg.model, filter_dtype=dtype)
