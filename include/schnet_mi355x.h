@@ -20,8 +20,8 @@
  *    except where a call says it synchronises.
  *  - Arguments are validated on the host before anything is launched; an
  *    invalid argument returns SN_ERR_INVALID_ARG and enqueues nothing.
- *  - Errors found on the device (list capacity, non-finite energy) are
- *    recorded in a status word inside the workspace; read it with
+ *  - Errors found on the device (list capacity, non-finite energies or
+ *    positions) are recorded in a status word inside the workspace; read it with
  *    sn_get_device_status. The first error wins until sn_reset_device_status.
  *  - Atoms are numbered replica-major: atom a of replica r is r*N + a, with
  *    N = atoms_per_replica. Positions and forces are float [R*N][3].
@@ -45,7 +45,8 @@ typedef enum {
   SN_OK = 0,
   SN_ERR_INVALID_ARG = 1,  /* bad pointer, size, shape or geometry */
   SN_ERR_CAPACITY = 2,     /* the neighbour list needs more than edge_capacity slots */
-  SN_ERR_NONFINITE = 3,    /* a replica energy came out NaN or infinite */
+  SN_ERR_NONFINITE = 3,    /* a replica energy, a position given to a neighbour
+                              build or an MD position or velocity is NaN or infinite */
   SN_ERR_UNSUPPORTED = 4,  /* a model or system shape this build does not handle */
   SN_ERR_HIP = 5,          /* a HIP runtime call failed */
   SN_ERR_WORKSPACE = 6     /* the workspace is smaller than sn_workspace_size says */
@@ -56,9 +57,9 @@ typedef enum {
  *  SN_FILTER_BF16  the filter network's products take bfloat16 operands
  *                  (weights rounded to nearest even, activations rounded as
  *                  they enter a product); the update and readout layers
- *                  keep fp32-grade products (in the fused calls on fp16
- *                  pairs, as SN_FILTER_F16X2 describes; in the unfused
- *                  pipeline in fp32);
+ *                  keep fp32-grade products on fp16 pairs, as
+ *                  SN_FILTER_F16X2 describes (in the fused calls and in the
+ *                  unfused pipeline alike);
  *  SN_W16A16       every MLP (filter, update, readout) takes fp16 operands,
  *                  with per-output-channel scales (§4.4 "Channel-wise
  *                  quantization"): each weight column n is stored as
@@ -150,7 +151,9 @@ sn_status sn_workspace_size(const sn_model_desc* desc, const sn_system* sys, siz
  * SN_ERR_CAPACITY with the needed count as detail, every row of rowptr is left
  * empty and col is not written. If n_edges_host is not NULL the call
  * synchronises the stream and stores the edge count there (also on overflow).
- * Positions must be finite. */
+ * Positions must be finite: a NaN or infinite coordinate of atom i sets the
+ * device status to SN_ERR_NONFINITE with detail -(1 + i) (such an atom
+ * would otherwise pass no membership test and silently lose its edges). */
 sn_status sn_build_neighbors(const sn_system* sys, const float* pos, float r_list, int32_t* rowptr,
                              int32_t* col, int64_t edge_capacity, int64_t* n_edges_host, void* ws,
                              size_t ws_bytes, hipStream_t stream);
@@ -255,14 +258,19 @@ sn_status sn_md_init(const sn_model* model, const sn_system* sys, const int32_t*
  * state->step. Besides the scheduled rebuilds, the list is rebuilt on the
  * device after any step in which some atom moved more than skin/2 since the
  * last build. energy[R] (optional) receives the potential energy after the
- * last step. Periodic positions are wrapped into [0, box) after each drift. */
+ * last step. Periodic positions are wrapped into [0, box) after each drift.
+ * An atom i whose position or velocity becomes NaN or infinite in a step sets
+ * the device status to SN_ERR_NONFINITE with detail -(1 + i); the state is
+ * then invalid (restore a checkpoint). */
 sn_status sn_md_step(const sn_model* model, const sn_system* sys, const int32_t* types,
                      const sn_md_params* params, sn_md_state* state, int32_t n_steps,
                      float* energy, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Reads the device status word and its detail (synchronises the stream):
  * status_host gets an sn_status value; detail_host the needed edge count for
- * SN_ERR_CAPACITY, the replica for SN_ERR_NONFINITE. n_rebuilds_host (may be
+ * SN_ERR_CAPACITY; for SN_ERR_NONFINITE the replica r >= 0 whose energy is
+ * not finite, or -(1 + i) for atom i whose position or velocity is not
+ * finite. n_rebuilds_host (may be
  * NULL) gets the number of neighbour-list builds done by the MD calls. */
 sn_status sn_get_device_status(const void* ws, size_t ws_bytes, hipStream_t stream,
                                int32_t* status_host, int64_t* detail_host,

@@ -567,13 +567,17 @@ struct AtomKernels {
     }
     return e;
   }
+  // the update networks exist for N1 == D; the readout for N1 = H in
+  // {32, 64}, H == D = 64 included
+  static constexpr bool kReadout = N1 <= 64;
   static hipError_t prepare() {
+    hipError_t e = hipSuccess;
+    if constexpr (kReadout) e = allow<ATOM_READOUT>();
     if constexpr (D == N1) {
-      hipError_t e = allow<ATOM_UPDATE_FWD>();
-      return e == hipSuccess ? allow<ATOM_UPDATE_BWD>() : e;
-    } else {
-      return allow<ATOM_READOUT>();
+      if (e == hipSuccess) e = allow<ATOM_UPDATE_FWD>();
+      if (e == hipSuccess) e = allow<ATOM_UPDATE_BWD>();
     }
+    return e;
   }
   template <int MODE>
   static void run(const AtomArgs& g, int G, int ntiles, int n_cu, hipStream_t s) {
@@ -593,13 +597,15 @@ struct AtomKernels {
     int G = ntiles;
     if (G > n_cu) G = n_cu;
     if (G < 1) G = 1;
-    if constexpr (D == N1) {   // the update networks
+    if (g.mode == ATOM_READOUT) {
+      if constexpr (kReadout) run<ATOM_READOUT>(g, G, ntiles, n_cu, s);
+      else return hipErrorInvalidValue;
+    } else if constexpr (D == N1) {   // the update networks
       if (g.mode == ATOM_UPDATE_FWD) run<ATOM_UPDATE_FWD>(g, G, ntiles, n_cu, s);
       else if (g.mode == ATOM_UPDATE_BWD) run<ATOM_UPDATE_BWD>(g, G, ntiles, n_cu, s);
       else return hipErrorInvalidValue;
-    } else {                   // the readout
-      if (g.mode != ATOM_READOUT) return hipErrorInvalidValue;
-      run<ATOM_READOUT>(g, G, ntiles, n_cu, s);
+    } else {
+      return hipErrorInvalidValue;
     }
     return hipGetLastError();
   }

@@ -458,7 +458,7 @@ const char* sn_status_string(sn_status s) {
     case SN_OK: return "ok";
     case SN_ERR_INVALID_ARG: return "invalid argument";
     case SN_ERR_CAPACITY: return "neighbour list exceeds edge capacity";
-    case SN_ERR_NONFINITE: return "non-finite energy";
+    case SN_ERR_NONFINITE: return "non-finite energy, position or velocity";
     case SN_ERR_UNSUPPORTED: return "unsupported shape";
     case SN_ERR_HIP: return "HIP runtime error";
     case SN_ERR_WORKSPACE: return "workspace too small";

@@ -187,8 +187,10 @@ struct AtomArgs {
 };
 // Weight image of one atom-wise network for `mode`: W1 [D][N1], b1 [N1],
 // W2 [N1][D] (readout: wo2 [N1]), b2 [D]; built on the host.
-// prec: the model's filter_dtype (Prec); the atom-wise layers use fp16
-// operands only for PREC_F16S.
+// prec: the model's filter_dtype (Prec). The atom-wise layers take fp16
+// operands for PREC_F16S, fp16 pairs for PREC_F16X2 and PREC_BF16 (behind a
+// bfloat16 filter they stay fp32-grade), fp32 operands for PREC_F32; the
+// fused and the unfused pipelines run the same atom-wise kernels.
 size_t atom_image_bytes(int D, int N1, int prec);
 void atom_fill_image(int mode, int D, int N1, int prec, const float* W1, const float* b1,
                      const float* W2, const float* b2, unsigned char* out);

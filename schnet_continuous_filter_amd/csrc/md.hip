@@ -72,7 +72,9 @@ __global__ __launch_bounds__(kThreads) void k_md_wrap(MdCoef c, int64_t n, float
 }
 
 // B A O A for step `step`; flags a rebuild when an atom moved more than skin/2
-// since the last build.
+// since the last build, and reports an atom whose new position or velocity is
+// not finite (detail -(1 + atom)): its edges would otherwise vanish from the
+// next list without a trace.
 __global__ __launch_bounds__(kThreads) void k_md_baoa(MdCoef c, int64_t n, uint64_t step,
                                                       float* pos, float* vel,
                                                       const float* forces,
@@ -82,6 +84,7 @@ __global__ __launch_bounds__(kThreads) void k_md_baoa(MdCoef c, int64_t n, uint6
   double z[3];
   normals3(c.seed, step, 0, (uint64_t)i, z);
   float d2 = 0.f;
+  bool finite = true;
   for (int k = 0; k < 3; ++k) {
     float v = vel[3 * i + k] + c.half_kick * forces[3 * i + k];
     float r = pos[3 * i + k] + c.half_dt * v;
@@ -96,9 +99,11 @@ __global__ __launch_bounds__(kThreads) void k_md_baoa(MdCoef c, int64_t n, uint6
       dd = r - pos_at_build[3 * i + k];
     }
     d2 += dd * dd;
+    finite = finite && isfinite(r) && isfinite(v);
     vel[3 * i + k] = v;
     pos[3 * i + k] = r;
   }
+  if (!finite) dev_fail(st, SN_ERR_NONFINITE, -1 - i);
   if (d2 > c.half_skin2) st->rebuild_req = (int64_t)step + 1;
 }
 

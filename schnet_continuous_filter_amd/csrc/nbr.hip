@@ -38,6 +38,13 @@ __device__ __forceinline__ bool pair_in(float xi, float yi, float zi, float xj, 
   return s < r2;
 }
 
+// A non-finite position fails every membership test, so its atom would
+// silently lose its edges: it is reported instead (detail -(1 + atom)).
+__device__ __forceinline__ void check_position(DevStatus* st, int64_t atom, float x, float y,
+                                               float z) {
+  if (!(isfinite(x) && isfinite(y) && isfinite(z))) dev_fail(st, SN_ERR_NONFINITE, -1 - atom);
+}
+
 #define SN_GATE                                   \
   if (gate != nullptr && *gate != gate_val) return;
 
@@ -228,7 +235,7 @@ __global__ __launch_bounds__(kThreads) void k_nbr_allpairs(const float* __restri
                                                            int64_t n_tot, int periodic, double L,
                                                            double half, double r2,
                                                            int32_t* rowptr, int32_t* col,
-                                                           const DevStatus* st,
+                                                           DevStatus* st,
                                                            const int64_t* gate, int64_t gate_val) {
   SN_GATE
   if (FILL && st->overflow) return;
@@ -238,6 +245,7 @@ __global__ __launch_bounds__(kThreads) void k_nbr_allpairs(const float* __restri
   const int il = (int)(r % N);
   const int64_t base = r - il;
   const float xi = pos[3 * r + 0], yi = pos[3 * r + 1], zi = pos[3 * r + 2];
+  if (!FILL && lane == 0) check_position(st, r, xi, yi, zi);
   const uint64_t below = (1ull << lane) - 1ull;
   int64_t out = FILL ? (int64_t)rowptr[r] : 0;
   int cnt = 0;
@@ -275,11 +283,12 @@ __device__ __forceinline__ int cell_coord(float x, float inv_cell, int nc) {
 
 __global__ __launch_bounds__(kThreads) void k_cell_assign(const float* __restrict__ pos, int N,
                                                           float inv_cell, int nc, int32_t* atom_cell,
-                                                          int32_t* cell_count, const int64_t* gate,
-                                                          int64_t gate_val) {
+                                                          int32_t* cell_count, DevStatus* st,
+                                                          const int64_t* gate, int64_t gate_val) {
   SN_GATE
   const int i = blockIdx.x * kThreads + threadIdx.x;
   if (i >= N) return;
+  check_position(st, i, pos[3 * i + 0], pos[3 * i + 1], pos[3 * i + 2]);
   const int cx = cell_coord(pos[3 * i + 0], inv_cell, nc);
   const int cy = cell_coord(pos[3 * i + 1], inv_cell, nc);
   const int cz = cell_coord(pos[3 * i + 2], inv_cell, nc);
@@ -488,7 +497,7 @@ hipError_t launch_build_neighbors(const NbrGeom& g, const float* pos, int32_t* r
   hipLaunchKernelGGL(k_fill_i32, dim3(blocks_for(ncell)), dim3(kThreads), 0, s, ccur, ncell, 0,
                      gate, gate_val);
   hipLaunchKernelGGL(k_cell_assign, dim3(blocks_for(N)), dim3(kThreads), 0, s, pos, N, g.inv_cell,
-                     nc, acell, cstart, gate, gate_val);
+                     nc, acell, cstart, st, gate, gate_val);
   if ((e = launch_exclusive_scan(cstart, ncell, scan_blocks, st, -1, gate, gate_val, s)) !=
       hipSuccess)
     return e;
