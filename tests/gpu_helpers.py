@@ -48,6 +48,18 @@ def gpu_neighbors(lib, system, pos_np, r_list, capacity=None, ws=None):
     return p, rowptr, col, ne, ws
 
 
+def oracle_list(system, pos_np, r_list, rp_gpu, col_gpu, what=""):
+    """The oracle's own list for the same positions and radius, after checking
+    that the GPU's list equals it entry for entry (the oracle is then
+    evaluated on a list the GPU did not build)."""
+    rp, col = oracle.neighbor_list(np.ascontiguousarray(pos_np, dtype=np.float32),
+                                   system.n_replicas, system.atoms_per_replica,
+                                   bool(system.periodic), system.box, r_list)
+    assert np.array_equal(np.asarray(rp_gpu), rp), f"{what}: GPU rowptr differs from the oracle's"
+    assert np.array_equal(np.asarray(col_gpu), col), f"{what}: GPU col differs from the oracle's"
+    return rp, col
+
+
 def assert_energy_forces(E_gpu, F_gpu, E_ref, F_ref, bf16=False, what="", eps_abs_sum=None):
     """bf16: the 16-bit bars; with eps_abs_sum (per replica sum of |eps_i|
     from the oracle) the energy bar is the W16A16 one."""

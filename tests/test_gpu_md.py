@@ -253,3 +253,116 @@ def test_active_list(gpu_lib):
     disp = np.max(np.abs(P_full - pos))
     assert np.max(np.abs(P_act - P_full)) < 1e-3 * disp
     assert np.all(np.abs(E_act - E_full) <= 1e-4 * np.abs(E_full))
+
+
+def test_nonfinite_position_is_reported(gpu_lib):
+    """A NaN written into one bead's position: the next step's B-A-O-A sees
+    it and the device status becomes SN_ERR_NONFINITE with detail -(1 + atom)
+    (before, the bead silently lost its edges and the status stayed SN_OK).
+    An infinite velocity of another bead is reported the same way."""
+    import torch
+    lib = gpu_lib
+    cfg, m, pos, types, w, desc, system, model, ws, t, params, state, energy = _md_setup(
+        lib, "cg269x64", 2)
+    try:
+        lib.sn_md_init(model, system, t, params, state, energy, ws)
+        assert lib.sn_get_device_status(ws)[0] == 0
+        state.pos[3 * 300 + 1] = float("nan")
+        lib.sn_md_step(model, system, t, params, state, 1, energy, ws)
+        st, det, _ = lib.sn_get_device_status(ws)
+        assert st == lib.SN_ERR_NONFINITE and det == -(1 + 300), (st, det)
+    finally:
+        lib.sn_model_destroy(model)
+    cfg, m, pos, types, w, desc, system, model, ws, t, params, state, energy = _md_setup(
+        lib, "cg269x64", 2)
+    try:
+        lib.sn_md_init(model, system, t, params, state, energy, ws)
+        state.vel[3 * 17 + 2] = float("inf")
+        lib.sn_md_step(model, system, t, params, state, 1, energy, ws)
+        st, det, _ = lib.sn_get_device_status(ws)
+        assert st == lib.SN_ERR_NONFINITE and det == -(1 + 17), (st, det)
+    finally:
+        lib.sn_model_destroy(model)
+
+
+@pytest.mark.parametrize("periodic", [False, True])
+def test_nonfinite_position_in_neighbour_build(gpu_lib, periodic):
+    """sn_build_neighbors on positions with one NaN coordinate (all-pairs
+    search, and the cell list of a periodic cube) reports the atom."""
+    import torch
+    lib = gpu_lib
+    rng = np.random.default_rng(5)
+    if periodic:
+        n, box = 4000, 40.0
+        pos = rng.uniform(0, box, (n, 3)).astype(np.float32)
+        system = lib.make_system(1, n, True, box)
+    else:
+        n, box = 300, 0.0
+        pos = rng.uniform(0, 30.0, (n, 3)).astype(np.float32)
+        system = lib.make_system(1, n, False, 0.0)
+    pos[123, 0] = np.nan
+    ws = lib.Workspace(lib.sn_workspace_size(None, system))
+    p = torch.from_numpy(pos).cuda().reshape(-1)
+    rowptr = torch.zeros(n + 1, dtype=torch.int32, device="cuda")
+    col = torch.zeros(n * 200, dtype=torch.int32, device="cuda")
+    lib.sn_build_neighbors(system, p, 5.0, rowptr, col, n * 200, ws)
+    st, det, _ = lib.sn_get_device_status(ws)
+    assert st == lib.SN_ERR_NONFINITE and det == -(1 + 123), (st, det)
+
+
+def test_short_trajectory_bf16_filter_active_list(gpu_lib):
+    """The MD workload's own precision and path: a bf16 filter, the update
+    and readout layers on fp16 pairs, the per-step active list, ten BAOAB
+    steps of 3 replicas against the oracle with the same bf16-rounded filter
+    weights and exact activations. Bars follow from the 16-bit force bar:
+    a force error of at most F_TOL_BF16 F_rms per step moves velocities by at
+    most that times dt kappa / m per step, and positions by dt times that."""
+    import torch
+    from tests.gpu_helpers import E_TOL_BF16, F_TOL_BF16
+    lib = gpu_lib
+    nsteps = 10
+    cfg, m, pos, types, w, desc, system, model, ws, t, params, state, energy = _md_setup(
+        lib, "md1024", 3, filter_f32=False, active=True)
+    assert m.filter_dtype == 1
+    try:
+        lib.sn_md_init(model, system, t, params, state, energy, ws)
+        F0 = state.forces.cpu().double().numpy().reshape(-1, 3)
+        lib.sn_md_step(model, system, t, params, state, nsteps, energy, ws)
+        torch.cuda.synchronize()
+        st = lib.sn_get_device_status(ws)
+        assert st[0] == 0, st
+        p_gpu = state.pos.cpu().double().numpy().reshape(-1, 3)
+        v_gpu = state.vel.cpu().double().numpy().reshape(-1, 3)
+        E_gpu = energy.cpu().double().numpy()
+    finally:
+        lib.sn_model_destroy(model)
+    d = oracle_desc(m)
+    W = oracle.unpack_weights(d, w)
+    v_init = oracle.init_velocities(42, len(pos), 300.0, 100.0)
+    nl = {}
+
+    def rebuild(p):
+        nl["l"] = oracle.neighbor_list(np.asarray(p, np.float32), 3, 269, False, 0.0, m.r_cut + 1.0)
+
+    def forces(p):
+        return oracle.energy_forces(d, None, p, types, *nl["l"], n_replicas=3, weights=W)
+
+    rebuild(pos)
+    E0, F0o = forces(pos.astype(np.float64))
+    f_rms = np.sqrt(np.mean(F0o ** 2))
+    assert np.max(np.abs(F0 - F0o)) <= F_TOL_BF16 * f_rms
+    p_o, v_o, F_o, E_o, _ = oracle.baoab_run(forces, rebuild, pos, v_init, F0o, dt_fs=2.0,
+                                             temperature_K=300.0, gamma_per_ps=1.0,
+                                             mass_amu=100.0, skin=1.0, rebuild_every=10, seed=42,
+                                             step0=0, n_steps=nsteps)
+    kick = 2.0 * oracle.md.KAPPA / 100.0                 # dt kappa / m per step
+    dv_bar = nsteps * kick * F_TOL_BF16 * f_rms + 1e-3 * np.sqrt(np.mean(v_o ** 2))
+    disp = np.max(np.abs(p_o - pos))
+    dp_bar = nsteps * 2.0 * dv_bar + 1e-2 * disp + 2e-4
+    dv = np.max(np.abs(v_gpu - v_o))
+    dp = np.max(np.abs(p_gpu - p_o))
+    de = np.max(np.abs(E_gpu - E_o) / np.abs(E_o))
+    print(f"bf16 trajectory: dv {dv:.2e} (bar {dv_bar:.2e}), dp {dp:.2e} (bar {dp_bar:.2e}), "
+          f"E rel {de:.2e}")
+    assert dv <= dv_bar and dp <= dp_bar
+    assert de <= E_TOL_BF16

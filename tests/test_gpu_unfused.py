@@ -6,7 +6,7 @@ import pytest
 import oracle
 from gen.configs import CONFIGS, Config, SystemSpec, make_config, make_weights
 from tests.gpu_helpers import (assert_energy_forces, gpu_neighbors, lib_desc, lib_system,
-                               oracle_desc)
+                               oracle_desc, oracle_list)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,8 +38,9 @@ def check(lib, cfg, pos, types, w, mode, r_list=None, n_replicas=None, what=""):
     m = cfg.model
     system = lib_system(lib, cfg.system, n_replicas)
     r_list = m.r_cut if r_list is None else r_list
-    E, F, rp, col, status = run_unfused(lib, m, system, pos, types, w, r_list, MODES[mode])
+    E, F, rp_gpu, col_gpu, status = run_unfused(lib, m, system, pos, types, w, r_list, MODES[mode])
     assert status[0] == 0, f"device status {status}"
+    rp, col = oracle_list(system, pos, r_list, rp_gpu, col_gpu, what)
     Eo, Fo = oracle.energy_forces(oracle_desc(m), w, pos, types, rp, col,
                                   n_replicas=system.n_replicas, periodic=bool(system.periodic),
                                   box=system.box)
