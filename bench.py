@@ -1,23 +1,31 @@
 """Throughput of the SchNet CFConv energy + force path on one MI355X.
 
-A step is one pass of the whole hot path over one batch: the Langevin (BAOAB)
-update of every replica, a neighbour-list rebuild (receiver-sorted CSR), the
-fused CFConv energy evaluation, and the analytic backward for the forces.
-The workload is 64 replicas of a 269-bead coarse-grained chain (D 128,
-50 Gaussians on 0-12 A, cosine cutoff 12 A, 3 interaction blocks, fp32), with
-synthetic seeded positions and random-init weights. The list is rebuilt every
-step at the cutoff radius, so every listed edge contributes.
+Headline (no flags): the 1024-replica MD workload. A step is one pass of the
+whole hot path over the batch: the Langevin (BAOAB) update of every bead, the
+neighbour-list rebuild every 10 steps at r_cut + 1 A (and on the skin guard),
+the per-step active list, the fused CFConv energy evaluation and the analytic
+backward for the forces. 1024 replicas of a 269-bead chain, D 128, 50
+Gaussians on 0-12 A, cosine cutoff 12 A, 3 interaction blocks, bf16 filter
+network with fp32 accumulation; synthetic seeded chains and random-init
+weights. `value` is replica-steps per second (the pages' timestep.mol/s),
+the median of `--repeats` runs of exactly `--steps` steps each.
 
-Prints one JSON line: directed edges through energy+forces per second (value),
-replica-steps per second, the roofline of the dominant kernel (backward
-CFConv, timed with HIP events around every launch inside the timed region)
-and the fp64 oracle timed on the host cores on a bounded sample.
+Beside it, the energy + force evaluation of the other workloads on a prebuilt
+list (median of 5 runs x N iterations after 20 warm-ups): the 32-bead chain
+(launch latency), 64 x 269-bead chains, and the 4096- and 65,536-atom
+periodic boxes (fp32), each with the roofline of its dominant kernel (the
+fused CFConv backward, timed with HIP events around every launch inside the
+timed region) and its counter-measured HBM traffic; and the fp64 oracle timed
+on the host cores on bounded samples.
+
+Prints one JSON line.
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -27,44 +35,71 @@ sys.path.insert(0, ROOT)
 from schnet_continuous_filter_amd import profiling  # noqa: E402  (no GPU work at import)
 
 PEAK_FP32_MFMA_TFLOPS = 157.3     # MI355X dense fp32 matrix peak
-PEAK_BF16_MFMA_TFLOPS = 2500.0
+PEAK_BF16_MFMA_TFLOPS = 2500.0    # dense bf16 / fp16 matrix peak
 PEAK_HBM_GBS = 8000.0
 PREC_TAGS = {0: "f32", 1: "bf16", 2: "w16a16", 3: "f16x2"}
 DTYPE_TAGS = {0: "f32", 1: "bf16-filter/f16x2-atomwise/f32", 2: "f16-mlps/f32", 3: "f16x2-filter/f32"}
 PROFILES = os.path.join(ROOT, "profiles")
+SUB_WORKLOADS = ("cg32", "cg269x64", "bulk4k", "bulk64k")
 
 
-def bwd_traffic(workload, m):
-    """Counter-measured bytes per k_cf_bwd launch for this workload and filter
-    precision (profiles/cfconv_bwd_<workload>[_f16x2]_counters.txt), or None
-    when no such record exists or the kernels changed since it was taken."""
-    for name in (f"cfconv_bwd_{workload}_counters.txt", f"cfconv_bwd_{workload}_f16x2_counters.txt"):
+def counter_record(kind, workload, m):
+    """The committed counter record (profiles/cfconv_<kind>_<workload>[_tag]_counters.txt)
+    of the kernel of this workload and precision, or None when there is none
+    or the kernels changed since it was taken. kind: 'bwd' or 'fwd'."""
+    for name in (f"cfconv_{kind}_{workload}_counters.txt",
+                 f"cfconv_{kind}_{workload}_{PREC_TAGS[m.filter_dtype]}_counters.txt"):
         path = os.path.join(PROFILES, name)
         if not os.path.exists(path):
             continue
         rec = json.load(open(path))
         kern = rec.get("kernel", "")   # "void sn::k_cf_bwd<D, KP, precision>(sn::CfParams)"
-        if (rec.get("kernel_hash") == profiling.kernel_hash() and kern.startswith(f"void sn::k_cf_bwd<{m.D}, ")
-                and f", {m.filter_dtype}>(" in kern and rec.get("workload", "").split("_")[0] == workload):
-            return rec.get("bytes_per_launch")
+        if (rec.get("kernel_hash") == profiling.kernel_hash()
+                and kern.startswith(f"void sn::k_cf_{kind}<{m.D}, ")
+                and f", {m.filter_dtype}>(" in kern
+                and rec.get("workload", "").split("_")[0] == workload):
+            return rec
     return None
+
+
+def utilisation_record(kind, workload, m):
+    """MFMA-busy and VALU-busy fractions of the kernel from the committed
+    counter record (profiles/cfconv_<kind>_<workload>_<prec>_util.txt), or
+    None (missing, or the kernels changed since)."""
+    path = os.path.join(PROFILES, f"cfconv_{kind}_{workload}_{PREC_TAGS[m.filter_dtype]}_util.txt")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_hash") != profiling.kernel_hash():
+        return None
+    return {k: rec[k] for k in ("mfma_busy", "valu_busy") if k in rec}
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="cg269x64",
+    ap.add_argument("--steps", type=int, default=1000,
+                    help="MD steps per timed run of the headline workload")
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--repeats", type=int, default=3,
+                    help="timed runs of the headline; value is their median")
+    ap.add_argument("--workload", default="md1024",
                     choices=["cg269x64", "cg32", "bulk4k", "bulk64k", "md1024"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-subs", action="store_true",
+                    help="skip the energy+force lines of the other workloads")
+    ap.add_argument("--subs", default=",".join(SUB_WORKLOADS),
+                    help="comma-separated workloads timed as energy+force evaluations")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="also time the oracle on the whole 65,536-atom box (about a minute "
+                         "or more of host time)")
     ap.add_argument("--precision", choices=["f32", "bf16", "w16a16", "f16x2"], default=None,
                     help="override the workload's network operand precision")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--no-alt", action="store_true",
-                    help="fp32 workloads: skip the extra timing with the filter on fp16 pairs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a device copy of known size (for counter scaling)")
+    ap.add_argument("--ef-only", default="",
+                    help="only time the energy+force evaluation of this workload (for "
+                         "profiler runs); with --precision")
     ap.add_argument("--sweep-replicas", default="",
                     help="comma-separated replica counts: MD throughput and memory of the "
                          "269-bead chain model (bf16 filter, 1 A skin, rebuild every 10) per count")
@@ -88,54 +123,109 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_each_way": n * 4, "launches": 5}))
 
 
-def cpu_baseline(cfg, seconds: float):
-    """The oracle as it stands, on a bounded sample of the same workload:
-    8 replicas, MD steps (rebuild + energy/forces + BAOAB) until the budget."""
+# ---------------------------------------------------------------- the oracle on the host
+def host_info():
+    cores = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return cores, model
+
+
+def _oracle_model(m):
+    import oracle
+    return oracle.ModelDesc(m.n_types, m.D, m.Dr, m.T, m.rbf_min, m.rbf_max, m.r_cut, m.H,
+                            m.filter_dtype)
+
+
+def cpu_md_subset(R=8, steps=10):
+    """The oracle as it stands on the MD workload's subset: R replicas of the
+    269-bead chain, `steps` BAOAB steps (list at r_cut + 1 A rebuilt every 10
+    steps, fp64 energy and forces with the bf16-rounded filter weights)."""
     import numpy as np
     import oracle
     from gen.configs import make_config
-    from threadpoolctl import threadpool_info
 
-    R = 8
-    c, pos, types, w = make_config(cfg.name, n_replicas=R)
-    m = c.model
-    desc = oracle.ModelDesc(m.n_types, m.D, m.Dr, m.T, m.rbf_min, m.rbf_max, m.r_cut, m.H,
-                            m.filter_dtype)
+    c, pos, types, w = make_config("md1024", n_replicas=R)
+    m, md = c.model, c.md
+    desc = _oracle_model(m)
     W = oracle.unpack_weights(desc, w)
     N = c.system.atoms_per_replica
-    per = c.system.periodic
-    box = c.system.box
     state = {}
 
     def rebuild(p):
-        state["nl"] = oracle.neighbor_list(np.asarray(p, np.float32), R, N, per, box, m.r_cut)
+        state["nl"] = oracle.neighbor_list(np.asarray(p, np.float32), R, N, False, 0.0,
+                                           m.r_cut + md.skin)
 
     def forces(p):
         return oracle.energy_forces(desc, None, p, types, *state["nl"], n_replicas=R,
-                                    periodic=per, box=box, weights=W)
+                                    weights=W)
 
+    t0 = time.perf_counter()
     rebuild(pos)
     E0, F0 = forces(pos.astype(np.float64))
-    vel = oracle.init_velocities(0, len(pos), 300.0, 100.0)
-    p, v, F = pos.astype(np.float64), vel, F0
-    steps, edges = 0, 0
-    t0 = time.perf_counter()
-    while True:
-        p, v, F, E, _ = oracle.baoab_run(forces, rebuild, p, v, F, dt_fs=2.0, temperature_K=300.0,
-                                         gamma_per_ps=1.0, mass_amu=100.0, skin=0.0,
-                                         rebuild_every=1, seed=0, step0=steps, n_steps=1,
-                                         periodic=per, box=box)
-        steps += 1
-        edges += len(state["nl"][1])
-        if time.perf_counter() - t0 >= seconds:
-            break
+    vel = oracle.init_velocities(0, len(pos), md.temperature_K, md.mass_amu)
+    oracle.baoab_run(forces, rebuild, pos, vel, F0, dt_fs=md.dt_fs,
+                     temperature_K=md.temperature_K, gamma_per_ps=md.gamma_per_ps,
+                     mass_amu=md.mass_amu, skin=md.skin, rebuild_every=md.rebuild_every,
+                     seed=0, step0=0, n_steps=steps)
     dt = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": edges / dt, "unit": "edges/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{R} of {c.system.n_replicas} replicas x {N} beads, {steps} MD steps "
-                      f"(rebuild + fp64 energy/forces + BAOAB) in {dt:.1f} s; "
-                      f"{R * steps / dt:.3g} replica-steps/s",
-            "replica_steps_per_s": R * steps / dt}
+    return R * steps / dt, dt
+
+
+def cpu_ef(name, reps):
+    """The oracle's energy + forces of a whole workload on its own list
+    (median of `reps` runs), in edges/s."""
+    import numpy as np
+    import oracle
+    from gen.configs import make_config
+
+    c, pos, types, w = make_config(name)
+    m, s = c.model, c.system
+    desc = _oracle_model(m)
+    W = oracle.unpack_weights(desc, w)
+    rp, col = oracle.neighbor_list(pos, s.n_replicas, s.atoms_per_replica, s.periodic, s.box,
+                                   m.r_cut)
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        oracle.energy_forces(desc, None, pos, types, rp, col, n_replicas=s.n_replicas,
+                             periodic=s.periodic, box=s.box, weights=W)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    return len(col) / t, t
+
+
+def cpu_baseline(subs, full):
+    """The oracle on the host cores: the MD subset for the headline (8 of the
+    1024 replicas, 10 steps), and whole energy + force evaluations of the
+    other workloads, with every core the process may use and with one."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    cores, model = host_info()
+    with threadpool_limits(limits=cores):
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        rs, dt = cpu_md_subset()
+        out = {"value": rs, "unit": "replica-steps/s", "cores": cores, "kind": "oracle",
+               "sample": f"8 of 1024 replicas x 269 beads, 10 BAOAB steps (list at 13 A, fp64 "
+                         f"energy/forces, bf16-rounded filter weights) in {dt:.1f} s",
+               "cpu_model": model, "blas_threads": blas, "workloads": {}}
+        for name in subs:
+            if name == "bulk64k" and not full:
+                continue
+            eps, t = cpu_ef(name, 1 if name in ("bulk64k", "cg269x64", "bulk4k") else 3)
+            out["workloads"][name] = {"edges_per_s": eps, "s_per_ef": t, "threads": blas}
+    with threadpool_limits(limits=1):
+        for name in ("cg32", "bulk4k"):
+            if name in subs:
+                eps, t = cpu_ef(name, 1 if name == "bulk4k" else 3)
+                out["workloads"][name]["edges_per_s_1thread"] = eps
+    return out
 
 
 def ablation(args):
@@ -360,13 +450,134 @@ def topology(args):
                       "warmup": args.warmup, "rows": rows}))
 
 
+def cf_flops(m, edges):
+    """Algorithmic work of the fused CFConv kernels per launch: the two filter
+    products per directed edge, 2 D (Dr + D) flops forward; the backward
+    recomputes them and runs their derivative through both, 4 D (Dr + D)."""
+    fwd = 2.0 * m.D * (m.Dr + m.D) * edges
+    return fwd, 2.0 * fwd
+
+
+def roofline(m, edges, bwd_us, fwd_us, workload):
+    """Roofline object of the dominant kernel (the fused backward): achieved
+    matrix throughput against the peak of its operand type, its
+    counter-measured traffic (bytes per launch, None when no record of the
+    current kernel exists) and the HBM fraction that traffic makes at the
+    launch time."""
+    _, fl_b = cf_flops(m, edges)
+    half = m.filter_dtype != 0
+    peak = PEAK_BF16_MFMA_TFLOPS if half else PEAK_FP32_MFMA_TFLOPS
+    achieved = fl_b / (bwd_us * 1e-6) / 1e12
+    rec = counter_record("bwd", workload, m)
+    traffic = rec["bytes_per_launch"] if rec else None
+    out = {"kernel": "k_cf_bwd (fused CFConv backward, one interaction block)",
+           "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+           "frac": achieved / peak, "traffic": traffic,
+           "flops_per_launch": fl_b, "avg_launch_us": bwd_us, "fwd_avg_launch_us": fwd_us,
+           "hbm_gbs_at_traffic": (traffic / (bwd_us * 1e-6) / 1e9) if traffic else None,
+           "hbm_frac_at_traffic": (traffic / (bwd_us * 1e-6) / 1e9 / PEAK_HBM_GBS)
+           if traffic else None}
+    util = utilisation_record("bwd", workload, m)
+    if util:
+        out["counters"] = util
+    return out
+
+
+def model_for(name, precision):
+    from gen.configs import make_config
+    c, pos, types, w = make_config(name)
+    m = c.model
+    if precision is not None:
+        import dataclasses
+        m = dataclasses.replace(m, filter_dtype={v: k for k, v in PREC_TAGS.items()}[precision])
+    return c, m, pos, types, w
+
+
+def ef_timing(name, precision=None, runs=5, warmup=20):
+    """One energy + force evaluation of a workload on a prebuilt list (the
+    list at r_cut, built and timed separately): median over `runs` runs of
+    `iters` evaluations after `warmup`, with the CFConv launches timed by the
+    library's event hook."""
+    import torch
+    from schnet_continuous_filter_amd import _lib as L
+    c, m, pos, types, w = model_for(name, precision)
+    s = c.system
+    R, N = s.n_replicas, s.atoms_per_replica
+    n = R * N
+    iters = 100 if n <= 20000 else 20
+    desc = L.make_desc(m.n_types, m.D, m.Dr, m.T, m.H, m.rbf_min, m.rbf_max, m.r_cut,
+                       m.filter_dtype)
+    system = L.make_system(R, N, s.periodic, s.box)
+    model = L.sn_model_create(desc, w)
+    ws = L.Workspace(L.sn_workspace_size(desc, system))
+    dev = torch.device("cuda")
+    p = torch.from_numpy(pos).to(dev).reshape(-1)
+    t = torch.from_numpy(types).to(dev)
+    rowptr = torch.zeros(n + 1, dtype=torch.int32, device=dev)
+    ne = L.sn_build_neighbors(system, p, m.r_cut, rowptr, None, 0, ws)
+    col = torch.empty(max(ne, 1), dtype=torch.int32, device=dev)
+    L.sn_reset_device_status(ws)
+    L.sn_build_neighbors(system, p, m.r_cut, rowptr, col, ne, ws)
+    energy = torch.empty(R, dtype=torch.float32, device=dev)
+    forces = torch.empty(3 * n, dtype=torch.float32, device=dev)
+
+    def timed(fn, k):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(k):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / k
+
+    build = lambda: L.sn_build_neighbors(system, p, m.r_cut, rowptr, col, ne, ws,
+                                         return_count=False)
+    ef = lambda: L.sn_energy_forces(model, system, p, t, rowptr, col, energy, forces, ws)
+    for _ in range(warmup):
+        build()
+        ef()
+    torch.cuda.synchronize()
+    build_ms = statistics.median(timed(build, iters) for _ in range(runs))
+    L.sn_profile_read(0)
+    L.sn_profile_read(1)
+    L.sn_profile_enable(True)
+    ms = [timed(ef, iters) for _ in range(runs)]
+    L.sn_profile_enable(False)
+    bwd_ms, bwd_n = L.sn_profile_read(1)
+    fwd_ms, fwd_n = L.sn_profile_read(0)
+    status, detail, _ = L.sn_get_device_status(ws)
+    L.sn_model_destroy(model)
+    if status != 0:
+        print(f"{name}: device status {status} ({L.status_string(status)}), detail {detail}",
+              file=sys.stderr)
+        sys.exit(1)
+    med = statistics.median(ms)
+    bwd_us = 1000.0 * bwd_ms / max(bwd_n, 1)
+    fwd_us = 1000.0 * fwd_ms / max(fwd_n, 1)
+    return {"workload": name, "replicas": R, "atoms_per_replica": N, "directed_edges": ne,
+            "dtype": DTYPE_TAGS[m.filter_dtype], "ms_per_ef": med,
+            "ms_per_ef_runs": ms, "runs": runs, "iters": iters, "warmup": warmup,
+            "edges_per_s": ne / (med * 1e-3),
+            "list_build_ms": build_ms,
+            "edges_per_s_build_and_ef": ne / ((med + build_ms) * 1e-3),
+            "roofline": roofline(m, ne, bwd_us, fwd_us, name)}
+
+
+def ef_only(args):
+    """Energy + force evaluations of one workload, nothing else (for profiler
+    runs whose kernel statistics must cover exactly those launches)."""
+    r = ef_timing(args.ef_only, args.precision, runs=max(1, args.repeats), warmup=args.warmup)
+    r.pop("ms_per_ef_runs")
+    print(json.dumps(r))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no "
               "multi-GPU path", file=sys.stderr)
         sys.exit(2)
-    import torch  # noqa: F401  (initialises the device before any library call)
+    import torch  # (initialises the device before any library call)
     if args.ablation:
         ablation(args)
         return
@@ -379,72 +590,58 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
-    from gen.configs import CONFIGS, make_config
-
-    cfg = CONFIGS[args.workload]
-    c, pos, types, w = make_config(cfg.name)
-    m = c.model
-    if args.precision is not None:
-        import dataclasses
-        m = dataclasses.replace(m, filter_dtype={v: k for k, v in PREC_TAGS.items()}[args.precision])
-    r = md_timing(cfg, c, m, pos, types, w, args.steps, args.warmup)
+    if args.ef_only:
+        ef_only(args)
+        return
+    name = args.workload
+    c, m, pos, types, w = model_for(name, args.precision)
+    torch.cuda.reset_peak_memory_stats()
+    r = md_timing(c, m, pos, types, w, args.steps, args.warmup, args.repeats)
+    peak_mem = torch.cuda.max_memory_allocated()
     R = c.system.n_replicas
-    flops_bwd = 4.0 * m.D * (m.Dr + m.D) * r["ne"]    # recompute (2D(Dr+D)) + dgrad (2D(Dr+D))
-    avg_bwd_s = r["bwd_ms"] / 1000.0 / max(r["bwd_n"], 1)
-    achieved = flops_bwd / avg_bwd_s / 1e12
-    half = m.filter_dtype != 0          # 16-bit operands: the dense fp16/bf16 MFMA peak
-    peak = PEAK_BF16_MFMA_TFLOPS if half else PEAK_FP32_MFMA_TFLOPS
-    traffic = bwd_traffic(cfg.name, m)
     line = {
         "metric": "CFConv energy+force edges/sec and replica-MD-steps/sec at 1 GPU; % HBM roofline",
-        "value": r["edges_per_s"],
-        "unit": "edges/s",
+        "value": r["replica_steps_per_s"],
+        "unit": "replica-steps/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "repeats": args.repeats,
         "ms_per_step": r["ms_per_step"],
+        "ms_per_step_runs": r["ms_per_step_runs"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": DTYPE_TAGS[m.filter_dtype],
         "data": "synthetic (seeded chains/boxes, random-init weights)",
-        "config": {"workload": cfg.name, "replicas": R,
+        "config": {"workload": name, "replicas": R,
                    "atoms_per_replica": c.system.atoms_per_replica,
                    "directed_edges": r["ne"], "list_radius_A": r["r_list"],
                    "list_edges": r["ne_list"], "D": m.D, "Dr": m.Dr,
                    "T": m.T, "r_cut_A": m.r_cut,
-                   "step": "BAOAB + neighbour rebuild + energy/forces"},
-        "replica_steps_per_s": r["replica_steps_per_s"],
-        "roofline": {"kernel": "k_cf_bwd (fused CFConv backward, one interaction block)",
-                     "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": traffic,
-                     "flops_per_launch": flops_bwd, "avg_launch_us": avg_bwd_s * 1e6,
-                     "launches": r["bwd_n"],
-                     "fwd_avg_launch_us": r["fwd_ms"] * 1000.0 / max(r["fwd_n"], 1)},
+                   "rebuild_every": r["rebuild_every"],
+                   "step": "BAOAB + scheduled neighbour rebuild + active list + energy/forces"},
+        "edges_per_s": r["edges_per_s"],
+        "peak_device_bytes": peak_mem,
+        "roofline": roofline(m, r["ne"], r["bwd_us"], r["fwd_us"], name),
         "n_rebuilds": r["n_rebuilds"],
     }
-    if m.filter_dtype == 0 and args.precision is None and not args.no_alt:
-        # the same fp32 model with the filter products on fp16 pairs (held to
-        # the fp32 parity bars), timed the same way
-        import dataclasses
-        m2 = dataclasses.replace(m, filter_dtype=3)
-        r2 = md_timing(cfg, c, m2, pos, types, w, args.steps, args.warmup)
-        line["f16x2_filter"] = {
-            "value": r2["edges_per_s"], "unit": "edges/s", "ms_per_step": r2["ms_per_step"],
-            "replica_steps_per_s": r2["replica_steps_per_s"], "dtype": DTYPE_TAGS[3],
-            "bwd_avg_launch_us": r2["bwd_ms"] * 1000.0 / max(r2["bwd_n"], 1),
-            "fwd_avg_launch_us": r2["fwd_ms"] * 1000.0 / max(r2["fwd_n"], 1),
-            # counter-measured bytes per backward launch of this path (or None)
-            "bwd_traffic": bwd_traffic(cfg.name, m2),
-            "parity": "fp32 bars (energy 1e-5 relative, forces 1e-4 of the force RMS)"}
+    subs = [] if args.no_subs else [v for v in args.subs.split(",") if v]
+    if subs:
+        line["energy_forces"] = {}
+        for sub in subs:
+            e = ef_timing(sub)
+            e.pop("ms_per_ef_runs")
+            line["energy_forces"][sub] = e
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(subs, args.cpu_full)
     print(json.dumps(line))
 
 
-def md_timing(cfg, c, m, pos, types, w, steps, warmup):
-    """MD steps of one model on the workload: warm-up, then `steps` timed
-    steps with the CFConv kernels' launch times recorded by the library."""
+def md_timing(c, m, pos, types, w, steps, warmup, repeats):
+    """MD steps of one model on the workload: warm-up, then `repeats` timed
+    runs of `steps` steps (each bracketed by device synchronisations), with
+    the CFConv kernels' launch times recorded by the library."""
     import torch
     from schnet_continuous_filter_amd import _lib as L
     s = c.system
@@ -461,9 +658,11 @@ def md_timing(cfg, c, m, pos, types, w, steps, warmup):
         md = L.make_md_params(c.md.dt_fs, c.md.temperature_K, c.md.gamma_per_ps, c.md.mass_amu,
                               c.md.skin, c.md.rebuild_every, 0)
         r_list = m.r_cut + c.md.skin
+        every = c.md.rebuild_every
     else:                         # rebuild every step at the cutoff
         md = L.make_md_params(2.0, 300.0, 1.0, 100.0, 0.0, 1, 0)
         r_list = m.r_cut
+        every = 1
     rowptr0 = torch.zeros(R * N + 1, dtype=torch.int32, device=dev)
     ne0 = L.sn_build_neighbors(system, p, r_list, rowptr0, None, 0, ws)
     L.sn_reset_device_status(ws)
@@ -477,11 +676,14 @@ def md_timing(cfg, c, m, pos, types, w, steps, warmup):
     L.sn_profile_read(1)
 
     L.sn_profile_enable(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    L.sn_md_step(model, system, t, md, state, steps, energy, ws)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    runs = []
+    for _ in range(repeats):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        L.sn_md_step(model, system, t, md, state, steps, energy, ws)
+        torch.cuda.synchronize()
+        runs.append(time.perf_counter() - t0)
+        print(f"timed run: {steps} steps in {runs[-1]:.3f} s", file=sys.stderr, flush=True)
     L.sn_profile_enable(False)
     bwd_ms, bwd_n = L.sn_profile_read(1)
     fwd_ms, fwd_n = L.sn_profile_read(0)
@@ -490,6 +692,7 @@ def md_timing(cfg, c, m, pos, types, w, steps, warmup):
         print(f"device status {status} ({L.status_string(status)}), detail {detail}",
               file=sys.stderr)
         sys.exit(1)
+    elapsed = statistics.median(runs)
     # edge counts on the final positions (untimed): the pairs inside the
     # cutoff are the work (the MD evaluates only those); the list's own size
     ne_list = L.sn_build_neighbors(system, state.pos, r_list, state.rowptr, state.col, capacity,
@@ -497,10 +700,11 @@ def md_timing(cfg, c, m, pos, types, w, steps, warmup):
     ne = L.sn_build_neighbors(system, state.pos, m.r_cut, state.rowptr, state.col, capacity, ws)
     L.sn_model_destroy(model)
     return {"edges_per_s": ne * steps / elapsed, "ms_per_step": 1000.0 * elapsed / steps,
+            "ms_per_step_runs": [1000.0 * v / steps for v in runs],
             "replica_steps_per_s": R * steps / elapsed, "ne": ne, "ne_list": ne_list,
-            "r_list": r_list,
-            "bwd_ms": bwd_ms, "bwd_n": bwd_n, "fwd_ms": fwd_ms, "fwd_n": fwd_n,
-            "n_rebuilds": n_rebuilds}
+            "r_list": r_list, "rebuild_every": every,
+            "bwd_us": 1000.0 * bwd_ms / max(bwd_n, 1), "fwd_us": 1000.0 * fwd_ms / max(fwd_n, 1),
+            "bwd_n": bwd_n, "fwd_n": fwd_n, "n_rebuilds": n_rebuilds}
 
 
 if __name__ == "__main__":

@@ -4,11 +4,21 @@
   python -m schnet_continuous_filter_amd.profiling traffic FETCH_CSV WRITE_CSV \
       COPY_FETCH_CSV COPY_WRITE_CSV OUT_TXT --kernel k_cf_bwd --workload cg269x64 --cmd "..."
 
+  python -m schnet_continuous_filter_amd.profiling util PMC_CSV OUT_TXT \
+      --kernel k_cf_bwd --workload md1024 --cmd "..."
+
 ``traffic`` scales FETCH_SIZE and WRITE_SIZE (KiB per dispatch) by what the
 same counters read for a device copy of known size (bench.py
 --copy-calibration copies 256 MiB five times), and records the result with a
 hash of the kernel source so that bench.py reports it only while the kernel
 is unchanged.
+
+``util`` averages the per-dispatch values of the derived counters MfmaUtil
+(percent of the cycles the SIMDs' matrix units were busy: summed
+SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE times the SIMD count) and
+VALUBusy (percent of the cycles the vector ALUs issued: SQ_ACTIVE_INST_VALU
+over the CU count times GRBM_GUI_ACTIVE), as rocprofv3 defines them, plus
+any raw counters of the same run, and records them the same way.
 """
 from __future__ import annotations
 
@@ -92,6 +102,30 @@ def traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, out_txt, kerne
     return rec
 
 
+def _per_kernel_counter(csv_path):
+    d = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(csv_path)):
+        d[r["Counter_Name"]][r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return d
+
+
+def util(pmc_csv, out_txt, kernel, workload, cmd) -> dict:
+    d = _per_kernel_counter(pmc_csv)
+    rec = {"workload": workload, "kernel_hash": kernel_hash(), "command": cmd, "counters": {}}
+    for name, per in d.items():
+        avg, n, keys = _pick(per, kernel)
+        rec["kernel"] = keys[0]
+        rec["dispatches"] = n
+        rec["counters"][name] = avg
+    if "MfmaUtil" in rec["counters"]:
+        rec["mfma_busy"] = rec["counters"]["MfmaUtil"] / 100.0
+    if "VALUBusy" in rec["counters"]:
+        rec["valu_busy"] = rec["counters"]["VALUBusy"] / 100.0
+    with open(out_txt, "w") as f:
+        f.write(json.dumps(rec) + "\n")
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -105,9 +139,17 @@ def main():
     t.add_argument("--kernel", default="k_cf_bwd")
     t.add_argument("--workload", default="cg269x64")
     t.add_argument("--cmd", required=True)
+    u = sub.add_parser("util")
+    u.add_argument("csv")
+    u.add_argument("out")
+    u.add_argument("--kernel", default="k_cf_bwd")
+    u.add_argument("--workload", default="md1024")
+    u.add_argument("--cmd", required=True)
     a = ap.parse_args()
     if a.what == "stats":
         stats(a.csv, a.out, a.cmd)
+    elif a.what == "util":
+        print(json.dumps(util(a.csv, a.out, a.kernel, a.workload, a.cmd)))
     else:
         print(json.dumps(traffic(a.fetch, a.write, a.copy_fetch, a.copy_write, a.out, a.kernel,
                                  a.workload, a.cmd)))
