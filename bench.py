@@ -616,8 +616,8 @@ def main():
         "data": "synthetic (seeded chains/boxes, random-init weights)",
         "config": {"workload": name, "replicas": R,
                    "atoms_per_replica": c.system.atoms_per_replica,
-                   "directed_edges": r["ne"], "list_radius_A": r["r_list"],
-                   "list_edges": r["ne_list"], "D": m.D, "Dr": m.Dr,
+                   "directed_edges_per_step": r["ne"], "list_radius_A": r["r_list"],
+                   "list_edges_at_end": r["ne_list"], "D": m.D, "Dr": m.Dr,
                    "T": m.T, "r_cut_A": m.r_cut,
                    "rebuild_every": r["rebuild_every"],
                    "step": "BAOAB + scheduled neighbour rebuild + active list + energy/forces"},
@@ -639,9 +639,12 @@ def main():
 
 
 def md_timing(c, m, pos, types, w, steps, warmup, repeats):
-    """MD steps of one model on the workload: warm-up, then `repeats` timed
-    runs of `steps` steps (each bracketed by device synchronisations), with
-    the CFConv kernels' launch times recorded by the library."""
+    """MD steps of one model on the workload. Every repeat starts the same
+    trajectory from the same state (initial velocities, list build and forces,
+    then `warmup` steps, untimed) and times `steps` steps bracketed by device
+    synchronisations, so that the repeats do the same work; the CFConv
+    kernels' launch times are recorded by the library and the edges each
+    evaluation ran on are counted on the device."""
     import torch
     from schnet_continuous_filter_amd import _lib as L
     s = c.system
@@ -652,7 +655,7 @@ def md_timing(c, m, pos, types, w, steps, warmup, repeats):
     model = L.sn_model_create(desc, w)
     ws = L.Workspace(L.sn_workspace_size(desc, system))
     dev = torch.device("cuda")
-    p = torch.from_numpy(pos).to(dev).reshape(-1)
+    p0 = torch.from_numpy(pos).to(dev).reshape(-1)
     t = torch.from_numpy(types).to(dev)
     if c.md is not None:          # the MD workload keeps its own skin and cadence
         md = L.make_md_params(c.md.dt_fs, c.md.temperature_K, c.md.gamma_per_ps, c.md.mass_amu,
@@ -664,47 +667,57 @@ def md_timing(c, m, pos, types, w, steps, warmup, repeats):
         r_list = m.r_cut
         every = 1
     rowptr0 = torch.zeros(R * N + 1, dtype=torch.int32, device=dev)
-    ne0 = L.sn_build_neighbors(system, p, r_list, rowptr0, None, 0, ws)
+    ne0 = L.sn_build_neighbors(system, p0, r_list, rowptr0, None, 0, ws)
     L.sn_reset_device_status(ws)
     capacity = int(ne0 * 1.5) + 1024
-    state = L.MdState(p, capacity)
+    state = L.MdState(p0, capacity)
     energy = torch.empty(R, dtype=torch.float32, device=dev)
-    L.sn_md_init(model, system, t, md, state, energy, ws)
-    L.sn_md_step(model, system, t, md, state, warmup, energy, ws)
-    torch.cuda.synchronize()
-    L.sn_profile_read(0)
-    L.sn_profile_read(1)
-
-    L.sn_profile_enable(True)
-    runs = []
+    runs, edges, rebuilds = [], [], []
+    bwd_ms = fwd_ms = 0.0
+    bwd_n = fwd_n = 0
     for _ in range(repeats):
+        state.pos.copy_(p0)
+        state.step = 0
+        L.sn_md_init(model, system, t, md, state, energy, ws)
+        L.sn_md_step(model, system, t, md, state, warmup, energy, ws)
+        torch.cuda.synchronize()
+        L.sn_reset_device_status(ws)
+        L.sn_profile_read(0)
+        L.sn_profile_read(1)
+        L.sn_profile_enable(True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         L.sn_md_step(model, system, t, md, state, steps, energy, ws)
         torch.cuda.synchronize()
         runs.append(time.perf_counter() - t0)
-        print(f"timed run: {steps} steps in {runs[-1]:.3f} s", file=sys.stderr, flush=True)
-    L.sn_profile_enable(False)
-    bwd_ms, bwd_n = L.sn_profile_read(1)
-    fwd_ms, fwd_n = L.sn_profile_read(0)
-    status, detail, n_rebuilds = L.sn_get_device_status(ws)
-    if status != 0:
-        print(f"device status {status} ({L.status_string(status)}), detail {detail}",
-              file=sys.stderr)
-        sys.exit(1)
-    elapsed = statistics.median(runs)
-    # edge counts on the final positions (untimed): the pairs inside the
-    # cutoff are the work (the MD evaluates only those); the list's own size
+        L.sn_profile_enable(False)
+        b = L.sn_profile_read(1)
+        f = L.sn_profile_read(0)
+        bwd_ms, bwd_n, fwd_ms, fwd_n = bwd_ms + b[0], bwd_n + b[1], fwd_ms + f[0], fwd_n + f[1]
+        status, detail, n_rebuilds = L.sn_get_device_status(ws)
+        if status != 0:
+            print(f"device status {status} ({L.status_string(status)}), detail {detail}",
+                  file=sys.stderr)
+            sys.exit(1)
+        n_eval, n_edges = L.sn_get_device_counters(ws)
+        assert n_eval == steps
+        edges.append(n_edges)
+        rebuilds.append(n_rebuilds)
+        print(f"timed run: {steps} steps in {runs[-1]:.3f} s, {n_edges / steps:.0f} edges "
+              f"per evaluation, {n_rebuilds} list builds", file=sys.stderr, flush=True)
+    k = sorted(range(repeats), key=lambda i: runs[i])[repeats // 2]   # the median run
+    elapsed = runs[k]
+    ne_mean = edges[k] / steps
+    # the list's size at the end of the last run (untimed)
     ne_list = L.sn_build_neighbors(system, state.pos, r_list, state.rowptr, state.col, capacity,
                                    ws)
-    ne = L.sn_build_neighbors(system, state.pos, m.r_cut, state.rowptr, state.col, capacity, ws)
     L.sn_model_destroy(model)
-    return {"edges_per_s": ne * steps / elapsed, "ms_per_step": 1000.0 * elapsed / steps,
+    return {"edges_per_s": edges[k] / elapsed, "ms_per_step": 1000.0 * elapsed / steps,
             "ms_per_step_runs": [1000.0 * v / steps for v in runs],
-            "replica_steps_per_s": R * steps / elapsed, "ne": ne, "ne_list": ne_list,
+            "replica_steps_per_s": R * steps / elapsed, "ne": ne_mean, "ne_list": ne_list,
             "r_list": r_list, "rebuild_every": every,
             "bwd_us": 1000.0 * bwd_ms / max(bwd_n, 1), "fwd_us": 1000.0 * fwd_ms / max(fwd_n, 1),
-            "bwd_n": bwd_n, "fwd_n": fwd_n, "n_rebuilds": n_rebuilds}
+            "bwd_n": bwd_n, "fwd_n": fwd_n, "n_rebuilds": rebuilds[k]}
 
 
 if __name__ == "__main__":

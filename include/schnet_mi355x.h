@@ -276,7 +276,15 @@ sn_status sn_get_device_status(const void* ws, size_t ws_bytes, hipStream_t stre
                                int32_t* status_host, int64_t* detail_host,
                                int64_t* n_rebuilds_host);
 
-/* Zeroes the status word and rebuild counter (enqueued on the stream). */
+/* Work counters of the workspace (synchronises the stream): the number of
+ * fused energy + force evaluations (sn_energy_forces, and those inside the
+ * MD calls) enqueued on it since the last sn_reset_device_status, and the
+ * sum of the edge counts rowptr[R*N] of the lists they ran on (the MD calls
+ * evaluate the active list when the state has one). */
+sn_status sn_get_device_counters(const void* ws, size_t ws_bytes, hipStream_t stream,
+                                 int64_t* evaluations_host, int64_t* edges_evaluated_host);
+
+/* Zeroes the status word and the counters (enqueued on the stream). */
 sn_status sn_reset_device_status(void* ws, size_t ws_bytes, hipStream_t stream);
 
 const char* sn_status_string(sn_status status);

@@ -84,6 +84,8 @@ _SIGNATURES = {
                              c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
     "sn_get_device_status": (c_int32, [c_void_p, c_size_t, c_void_p, _P(c_int32), _P(c_int64),
                                        _P(c_int64)]),
+    "sn_get_device_counters": (c_int32, [c_void_p, c_size_t, c_void_p, _P(c_int64),
+                                         _P(c_int64)]),
     "sn_reset_device_status": (c_int32, [c_void_p, c_size_t, c_void_p]),
     "sn_philox4x64_10": (c_int32, [c_void_p, c_uint64, c_uint64, c_void_p, c_int64, c_void_p]),
     "sn_profile_enable": (c_int32, [c_int32]),
@@ -305,6 +307,14 @@ def sn_get_device_status(ws: Workspace):
     _check(LIB.sn_get_device_status(ws.ptr, ws.nbytes, _stream(), ctypes.byref(st),
                                     ctypes.byref(det), ctypes.byref(nrb)), "sn_get_device_status")
     return st.value, det.value, nrb.value
+
+
+def sn_get_device_counters(ws: Workspace):
+    """(evaluations, edges evaluated) since the last reset; synchronises the stream."""
+    ev, ed = c_int64(), c_int64()
+    _check(LIB.sn_get_device_counters(ws.ptr, ws.nbytes, _stream(), ctypes.byref(ev),
+                                      ctypes.byref(ed)), "sn_get_device_counters")
+    return ev.value, ed.value
 
 
 def sn_reset_device_status(ws: Workspace) -> None:

@@ -742,6 +742,19 @@ sn_status sn_get_device_status(const void* ws, size_t ws_bytes, hipStream_t s, i
   return SN_OK;
 }
 
+sn_status sn_get_device_counters(const void* ws, size_t ws_bytes, hipStream_t s,
+                                 int64_t* evaluations, int64_t* edges_evaluated) {
+  if (!ws || !evaluations || !edges_evaluated || ws_bytes < sizeof(DevStatus))
+    return SN_ERR_INVALID_ARG;
+  DevStatus h{};
+  hipError_t e = hipMemcpyAsync(&h, ws, sizeof(DevStatus), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return SN_ERR_HIP;
+  *evaluations = h.evaluations;
+  *edges_evaluated = h.edges_evaluated;
+  return SN_OK;
+}
+
 sn_status sn_reset_device_status(void* ws, size_t ws_bytes, hipStream_t s) {
   if (!ws || ws_bytes < sizeof(DevStatus)) return SN_ERR_INVALID_ARG;
   return hip_fail(hipMemsetAsync(ws, 0, sizeof(DevStatus), s));

@@ -1006,7 +1006,11 @@ __global__ __launch_bounds__(kThreads) void k_setup(const int32_t* rowptr, int N
   if ((int)blockIdx.x < nbp) {
     const int t = blockIdx.x * kThreads + threadIdx.x;
     const int64_t E = rowptr[N];
-    if (t == 0 && E >= kMaxListEdges) dev_fail(st, SN_ERR_UNSUPPORTED, E);
+    if (t == 0) {
+      if (E >= kMaxListEdges) dev_fail(st, SN_ERR_UNSUPPORTED, E);
+      st->evaluations += 1;
+      st->edges_evaluated += E;
+    }
     if (t <= G1) partition_one(rowptr, N, E, G1, t, wg_start1, wg_edge1);
     else if (t <= G1 + 1 + G2) partition_one(rowptr, N, E, G2, t - G1 - 1, wg_start2, wg_edge2);
     return;

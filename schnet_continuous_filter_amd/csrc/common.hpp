@@ -29,7 +29,9 @@ struct DevStatus {
   int64_t n_rebuilds;    // neighbour builds done by the MD calls
   int64_t last_n_edges;  // edge count of the last neighbour build
   int64_t rebuild_req;   // MD: step+1 of the last step whose drift crossed skin/2
-  int64_t pad[3];
+  int64_t evaluations;   // fused energy + force evaluations enqueued since the last reset
+  int64_t edges_evaluated;   // the sum of their lists' edge counts
+  int64_t pad[1];
 };
 
 // MLP operand precisions (the filter_dtype values of sn_model_desc): fp32;
