@@ -8,16 +8,21 @@ from gen.configs import CONFIGS, make_config
 
 # Parity bars: energy within 1e-5 relative; forces within 1e-4 (max abs) of the
 # oracle's force RMS, for fp32 filters. bf16 filters: the oracle uses the same
-# bf16-rounded weights but exact activations, so the bars widen to 1e-3 on the
-# energy and 5e-2 (max) / 1e-2 (RMS) on the forces.
+# bf16-rounded weights but exact activations (every activation entering a
+# filter product is rounded to 8 significant bits on the GPU), so the bars
+# widen; they are set at about twice the largest errors measured over the
+# parity cases on MI355X (energy 1.3e-4 relative, forces 9.5e-3 max and
+# 2.6e-3 RMS of the force RMS).
 E_TOL_F32, F_TOL_F32 = 1e-5, 1e-4
-E_TOL_BF16, F_TOL_BF16, F_RMS_TOL_BF16 = 1e-3, 5e-2, 1e-2
+E_TOL_BF16, F_TOL_BF16, F_RMS_TOL_BF16 = 3e-4, 2e-2, 5e-3
 # fp16 operands in every MLP (W16A16): every activation entering a product is
 # rounded to 11 significant bits, so a replica's energy error grows with the
 # per-atom energies it sums, not with their (possibly cancelling) total: the
-# 16-bit energy bar (1e-3, about two fp16 unit roundoffs) is taken relative to
-# sum_i |eps_i|; the force bars are the bf16 ones.
-E_TOL_W16_ABS_SUM = 1e-3
+# energy bar is taken relative to sum_i |eps_i|. Bars at about twice the
+# largest measured errors (1.6e-4 of sum |eps_i|, forces 3.2e-3 max and
+# 4.8e-4 RMS of the force RMS).
+E_TOL_W16_ABS_SUM = 3.5e-4
+F_TOL_W16, F_RMS_TOL_W16 = 7e-3, 1e-3
 
 
 def oracle_desc(m):
@@ -79,10 +84,12 @@ def assert_energy_forces(E_gpu, F_gpu, E_ref, F_ref, bf16=False, what="", eps_ab
     if rms == 0.0:            # no forces at all (isolated atoms): demand exact zeros
         assert err.max() == 0.0, f"{what} forces should vanish"
         return rel.max(), 0.0
-    f_tol = F_TOL_BF16 if bf16 else F_TOL_F32
+    f_tol = (F_TOL_W16 if eps_abs_sum is not None else F_TOL_BF16) if bf16 else F_TOL_F32
     assert err.max() <= f_tol * rms, f"{what} force max err {err.max() / rms:.3e} x rms > {f_tol}"
     if bf16:
-        assert np.sqrt(np.mean(err ** 2)) <= F_RMS_TOL_BF16 * rms
+        e_rms = np.sqrt(np.mean(err ** 2)) / rms
+        print(f"{what}: F err rms/rms {e_rms:.2e}")
+        assert e_rms <= (F_RMS_TOL_W16 if eps_abs_sum is not None else F_RMS_TOL_BF16)
     return rel.max(), err.max() / rms
 
 
