@@ -170,6 +170,28 @@ sn_status sn_energy_forces(const sn_model* model, const sn_system* sys, const fl
                            float* energy, float* forces, void* ws, size_t ws_bytes,
                            hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the
+ * energies and forces of sn_energy_forces, same arguments and results, with
+ * the workspace taken from a static device array of the library instead of
+ * a caller's buffer. The call allocates nothing. The array holds
+ * SN_SCRATCH_BYTES (32 MiB) on each GPU the library runs on, until the
+ * process ends; a system whose workspace (sn_workspace_size) is larger is
+ * refused with SN_ERR_WORKSPACE before anything is enqueued (at D = 128,
+ * T = 3 that is above about 5,000 atoms; the 4096-atom box fits).
+ * The array's status block is cleared at the start of every call, and when
+ * the call's work completes its sn_status and detail (as
+ * sn_get_device_status reports them) are written to status_dev[0] and
+ * status_dev[1] (device memory, int64). Every call on a GPU shares that
+ * GPU's array, which keeps the last call's contents: calls on one stream are
+ * ordered and safe, calls that overlap on one GPU (other streams, other
+ * threads) race and give wrong results. No profiling events are recorded. */
+#define SN_SCRATCH_BYTES ((size_t)32 << 20)
+sn_status sn_energy_forces_noalloc(const sn_model* model, const sn_system* sys, const float* pos,
+                                   const int32_t* types, const int32_t* rowptr,
+                                   const int32_t* col, float* energy, float* forces,
+                                   int64_t* status_dev, hipStream_t stream);
+
 /* The same energies and forces by the unfused pipeline that FlashSchNet
  * measures its techniques against (§3.3 bottlenecks, Fig. 2(b) lower
  * pipeline; §4.5 "End-to-end integration" names fusion and segmented

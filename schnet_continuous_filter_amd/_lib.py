@@ -73,6 +73,9 @@ _SIGNATURES = {
                                      _P(c_int64), c_void_p, c_size_t, c_void_p]),
     "sn_energy_forces": (c_int32, [c_void_p, _P(SnSystem), c_void_p, c_void_p, c_void_p, c_void_p,
                                    c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "sn_energy_forces_noalloc": (c_int32, [c_void_p, _P(SnSystem), c_void_p, c_void_p,
+                                           c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                           c_void_p]),
     "sn_unfused_workspace_size": (c_int32, [_P(SnModelDesc), _P(SnSystem), c_int64,
                                             _P(c_size_t)]),
     "sn_energy_forces_unfused": (c_int32, [c_void_p, _P(SnSystem), c_void_p, c_void_p, c_void_p,
@@ -222,6 +225,26 @@ def sn_energy_forces(model, system: SnSystem, pos, types, rowptr, col, energy, f
     _check(LIB.sn_energy_forces(model, ctypes.byref(system), _ptr(pos), _ptr(types), _ptr(rowptr),
                                 _ptr(col), _ptr(energy), _ptr(forces), ws.ptr, ws.nbytes,
                                 _stream()), "sn_energy_forces")
+
+
+SN_SCRATCH_BYTES = 32 << 20
+
+
+def sn_energy_forces_noalloc(model, system: SnSystem, pos, types, rowptr, col, energy, forces,
+                             status_dev) -> None:
+    """sn_energy_forces on the library's static device workspace; status_dev:
+    int64 device tensor of 2 (status, detail), written when the work completes."""
+    import torch
+    n = system.n_replicas * system.atoms_per_replica
+    _check_tensor(pos, torch.float32, 3 * n, "pos")
+    _check_tensor(types, torch.int32, n, "types")
+    _check_tensor(rowptr, torch.int32, n + 1, "rowptr")
+    _check_tensor(energy, torch.float32, system.n_replicas, "energy")
+    _check_tensor(forces, torch.float32, 3 * n, "forces")
+    _check_tensor(status_dev, torch.int64, 2, "status_dev")
+    _check(LIB.sn_energy_forces_noalloc(model, ctypes.byref(system), _ptr(pos), _ptr(types),
+                                        _ptr(rowptr), _ptr(col), _ptr(energy), _ptr(forces),
+                                        _ptr(status_dev), _stream()), "sn_energy_forces_noalloc")
 
 
 def sn_unfused_workspace_size(desc: SnModelDesc, system: SnSystem, edge_capacity: int) -> int:

@@ -10,6 +10,22 @@
 
 using namespace sn;
 
+// Device memory of sn_energy_forces_noalloc (see scratch_for_current_device).
+static __device__ __align__(256) unsigned char scratch[SN_SCRATCH_BYTES];
+
+__global__ void k_status_clear(sn::DevStatus* st) {
+  int64_t* w = reinterpret_cast<int64_t*>(st);
+  constexpr int n = (int)(sizeof(sn::DevStatus) / sizeof(int64_t));
+  if ((int)threadIdx.x < n) w[threadIdx.x] = 0;
+}
+
+__global__ void k_status_copy(const sn::DevStatus* st, int64_t* out) {
+  if (threadIdx.x == 0) {
+    out[0] = st->status;
+    out[1] = st->detail;
+  }
+}
+
 struct sn_model {
   sn_model_desc desc;
   int KP = 0;
@@ -82,7 +98,9 @@ struct ProfScope {
   int kernel;
   hipStream_t s;
   hipEvent_t a = nullptr, b = nullptr;
+  // kernel < 0: never recorded (the allocation-free entry point)
   ProfScope(int k, hipStream_t st) : kernel(k), s(st) {
+    if (k < 0) return;
     std::lock_guard<std::mutex> lk(g_prof_mu);
     if (!g_prof_on) return;
     a = prof_event();
@@ -140,7 +158,8 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
                              const int32_t* types, const int32_t* rowptr, const int32_t* col,
                              float* energy, float* forces, char* ws, hipStream_t s,
                              const UfMode* uf = nullptr, float* vel_kick = nullptr,
-                             float half_kick = 0.f, const BuildMark* mark = nullptr) {
+                             float half_kick = 0.f, const BuildMark* mark = nullptr,
+                             bool profile = true) {
   const sn_model_desc& d = m->desc;
   const int64_t n = n_atoms(sys);
   const int D = d.D, T = d.T, H = d.H;
@@ -280,7 +299,7 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
       ua.h = gbuf;
       if ((e = uf_block(t, UF_FORWARD)) != hipSuccess) return hip_fail(e);
     } else {
-      ProfScope ps(0, s);
+      ProfScope ps(profile ? 0 : -1, s);
       if ((e = launch_cf_forward(D, m->KP, prec, p, Gf, s)) != hipSuccess) return hip_fail(e);
     }
     // h of receivers cut by the forward's worker boundaries is completed as it is read
@@ -322,7 +341,7 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
       ua.q = t > 0 ? tmp : nullptr;
       if ((e = uf_block(t, UF_BACKWARD)) != hipSuccess) return hip_fail(e);
     } else {
-      ProfScope ps(1, s);
+      ProfScope ps(profile ? 1 : -1, s);
       if ((e = launch_cf_backward(D, m->KP, prec, p, Gb, s)) != hipSuccess) return hip_fail(e);
     }
   }
@@ -333,6 +352,32 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
                          forces, vel_kick, half_kick, rowptr, Gb * wb, uf ? nullptr : side_f,
                          kSideF, st, s)) != hipSuccess)
     return hip_fail(e);
+  return SN_OK;
+}
+
+// ---------------------------------------------------------------- allocation-free workspace
+// The workspace of sn_energy_forces_noalloc: a static device array, one copy
+// per GPU (the loader places it when the library's code object is loaded on
+// that GPU; it is held until the process ends). Host code never uses the
+// array's name as an address: the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kScratchBytes = SN_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+sn_status scratch_for_current_device(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SN_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return SN_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return SN_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<char*>(g_scratch_ptr[dev]);
   return SN_OK;
 }
 
@@ -624,6 +669,30 @@ sn_status sn_energy_forces(const sn_model* m, const sn_system* sys, const float*
   if (rc != SN_OK) return rc;
   return energy_forces_impl(m, sys, pos, types, rowptr, col, energy, forces, static_cast<char*>(ws),
                             s);
+}
+
+sn_status sn_energy_forces_noalloc(const sn_model* m, const sn_system* sys, const float* pos,
+                                   const int32_t* types, const int32_t* rowptr,
+                                   const int32_t* col, float* energy, float* forces,
+                                   int64_t* status_dev, hipStream_t s) {
+  if (!m || !sys_ok(sys) || !pos || !types || !rowptr || !col || !energy || !forces ||
+      !status_dev)
+    return SN_ERR_INVALID_ARG;
+  const WsLayout L = ws_layout(n_atoms(sys), m->desc.D, m->desc.T, m->desc.H);
+  if (L.total > kScratchBytes) return SN_ERR_WORKSPACE;
+  char* w = nullptr;
+  sn_status rc = scratch_for_current_device(&w);
+  if (rc != SN_OK) return rc;
+  DevStatus* st = reinterpret_cast<DevStatus*>(w + L.status);
+  // the status block starts at zero on every call (a kernel, not a memset:
+  // the call may be captured into a graph)
+  hipLaunchKernelGGL(k_status_clear, dim3(1), dim3(64), 0, s, st);
+  if (hipGetLastError() != hipSuccess) return SN_ERR_HIP;
+  rc = energy_forces_impl(m, sys, pos, types, rowptr, col, energy, forces, w, s, nullptr, nullptr,
+                          0.f, nullptr, false);
+  if (rc != SN_OK) return rc;
+  hipLaunchKernelGGL(k_status_copy, dim3(1), dim3(64), 0, s, st, status_dev);
+  return hipGetLastError() == hipSuccess ? SN_OK : SN_ERR_HIP;
 }
 
 sn_status sn_unfused_workspace_size(const sn_model_desc* d, const sn_system* sys,
