@@ -72,6 +72,10 @@
 namespace sn {
 
 constexpr int kEdges = 16;  // edges per wave tile: the MFMA column dimension
+// Byte offset of a feature row that lies past the end of every per-atom array
+// (the library admits at most 2^22 atoms, so N D 4 <= 2^31, and the offsets
+// added to it stay below 2^31 + 512): bounded buffer loads from it read zeros.
+constexpr uint32_t kMaskedRow = 0x80000000u;
 
 __device__ __forceinline__ float min_image(float u, float box, float half) {
   if (u > half) return u - box;
@@ -697,7 +701,12 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, false>()), 1) void k_cf_fwd(CfPa
     // receiver, 64 features at a time. The sender rows of the first 64
     // features are requested ahead of the product; a block's registers are
     // refilled with the next 64 features' as soon as they are used.
-    const uint32_t xo = ((uint32_t)th.j * (uint32_t)D + (uint32_t)g4) * 4u;
+    // lanes of edges that contribute nothing (at or beyond the cutoff, or
+    // past the worker's last edge) gather from an offset past the end of x,
+    // which the bounded loads read as zeros: their messages vanish without a
+    // mask multiply
+    const uint32_t xo = g.in > 0.f ? ((uint32_t)th.j * (uint32_t)D + (uint32_t)g4) * 4u
+                                   : kMaskedRow;
     f32x4 xg[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) xg[b] = bload4(rx, xo + (uint32_t)(64 * b));
@@ -721,7 +730,7 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, false>()), 1) void k_cf_fwd(CfPa
         if constexpr (PR == PREC_F16X2) w[b] *= ss.u[2];
         f32x4 m;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) m[r] = xg[b][r] * (g.in * (w[b][r] + c2[r]));
+        for (int r = 0; r < 4; ++r) m[r] = xg[b][r] * (w[b][r] + c2[r]);
         tile_put(Tb, b, m, tl);
         if (pss + 1 < NB / 4) xg[b] = bload4(rx, xo + (uint32_t)(64 * (nb + 4)));
       }
@@ -822,8 +831,12 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, true>()), 1) void k_cf_bwd(CfPar
 
     // gathers of the first 64 features (x_j, dE/dh_j, x_i, dE/dh_i), issued
     // ahead of the tangent product so that their latency is covered
-    const uint32_t jo = ((uint32_t)th.j * (uint32_t)D + (uint32_t)g4) * 4u;
-    const uint32_t io = ((uint32_t)th.recv * (uint32_t)D + (uint32_t)g4) * 4u;
+    // (edges that contribute nothing read zeros, as in the forward: their
+    // source sums and dE/dd vanish)
+    const uint32_t jo = g.in > 0.f ? ((uint32_t)th.j * (uint32_t)D + (uint32_t)g4) * 4u
+                                   : kMaskedRow;
+    const uint32_t io = g.in > 0.f ? ((uint32_t)th.recv * (uint32_t)D + (uint32_t)g4) * 4u
+                                   : kMaskedRow;
     f32x4 G[4][4];
     auto gather = [&](int nb, f32x4 (&Gb)[4]) {
       const uint32_t co = (uint32_t)(64 * nb);
@@ -877,7 +890,7 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, true>()), 1) void k_cf_bwd(CfPar
         f32x4 qv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          qv[r] = gj[r] * (g.in * (wv[b][r] + c2[r]));
+          qv[r] = gj[r] * (wv[b][r] + c2[r]);
           gdd = fmaf(gi[r] * xj[r] + gj[r] * xi[r], wt[nb][r], gdd);
         }
         if (want_q) tile_put(Tb, b, qv, tl);
@@ -901,7 +914,7 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, true>()), 1) void k_cf_bwd(CfPar
     }
     gdd += __shfl_xor(gdd, 16, 64);
     gdd += __shfl_xor(gdd, 32, 64);
-    const float gd = gdd * g.invd * g.in;
+    const float gd = gdd * g.invd;
 
     // this block's dE/dr rows: the edge contributions gd u summed per receiver
     // by a segmented scan along the tile's 16 rows (one edge per lane of a

@@ -109,16 +109,21 @@ __device__ __forceinline__ void wave_sync() {
 __device__ __forceinline__ float exp_neg(float x) { return __builtin_amdgcn_exp2f(x * LOG2EF); }
 __device__ __forceinline__ float ln_1_2(float y) { return __builtin_amdgcn_logf(y) * LN2F; }
 
-// Shifted softplus and its derivative (the logistic sigmoid) from t = exp(-|a|).
+// Shifted softplus and its derivative (the logistic sigmoid) from
+// t = exp(-|a|) and h = (1 + t) / 2 in (1/2, 1]:
+//   ssp(a) = ln(1 + e^a) - ln 2 = max(a, 0) + ln 2 log2(h),
+//   sigmoid(a) = 1 / (1 + e^-a) = (a >= 0 ? 1 : t) / (2 h).
+// log2 of h near 1 needs no cancellation against ln 2.
 __device__ __forceinline__ void ssp_sig(float a, float& s, float& sg) {
   const float t = exp_neg(-fabsf(a));
-  const float inv = __builtin_amdgcn_rcpf(1.f + t);
-  s = fmaxf(a, 0.f) + ln_1_2(1.f + t) - LN2F;
-  sg = a >= 0.f ? inv : t * inv;
+  const float h = fmaf(t, 0.5f, 0.5f);
+  const float r = __builtin_amdgcn_rcpf(h);
+  s = fmaf(LN2F, __builtin_amdgcn_logf(h), fmaxf(a, 0.f));
+  sg = (a >= 0.f ? 0.5f : 0.5f * t) * r;
 }
 __device__ __forceinline__ float ssp(float a) {
   const float t = exp_neg(-fabsf(a));
-  return fmaxf(a, 0.f) + ln_1_2(1.f + t) - LN2F;
+  return fmaf(LN2F, __builtin_amdgcn_logf(fmaf(t, 0.5f, 0.5f)), fmaxf(a, 0.f));
 }
 
 __device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
