@@ -47,8 +47,7 @@ def counter_record(kind, workload, m):
     """The committed counter record (profiles/cfconv_<kind>_<workload>[_tag]_counters.txt)
     of the kernel of this workload and precision, or None when there is none
     or the kernels changed since it was taken. kind: 'bwd' or 'fwd'."""
-    for name in (f"cfconv_{kind}_{workload}_counters.txt",
-                 f"cfconv_{kind}_{workload}_{PREC_TAGS[m.filter_dtype]}_counters.txt"):
+    for name in (f"cfconv_{kind}_{workload}_{PREC_TAGS[m.filter_dtype]}_counters.txt",):
         path = os.path.join(PROFILES, name)
         if not os.path.exists(path):
             continue
@@ -99,7 +98,10 @@ def parse():
                     help="only run a device copy of known size (for counter scaling)")
     ap.add_argument("--ef-only", default="",
                     help="only time the energy+force evaluation of this workload (for "
-                         "profiler runs); with --precision")
+                         "profiler runs); with --precision and --order")
+    ap.add_argument("--order", choices=["given", "cell"], default="given",
+                    help="with --ef-only on a periodic box: atoms as generated, or relabelled "
+                         "in the order of 5 A cells (the same system)")
     ap.add_argument("--sweep-replicas", default="",
                     help="comma-separated replica counts: MD throughput and memory of the "
                          "269-bead chain model (bf16 filter, 1 A skin, rebuild every 10) per count")
@@ -483,9 +485,15 @@ def roofline(m, edges, bwd_us, fwd_us, workload):
     return out
 
 
-def model_for(name, precision):
+def model_for(name, precision, order="given"):
     from gen.configs import make_config
     c, pos, types, w = make_config(name)
+    if order == "cell":
+        from gen.systems import cell_order
+        if not c.system.periodic or c.system.n_replicas != 1:
+            raise SystemExit("--order cell applies to a single periodic box")
+        k = cell_order(pos, c.system.box)
+        pos, types = pos[k].copy(), types[k].copy()
     m = c.model
     if precision is not None:
         import dataclasses
@@ -493,14 +501,14 @@ def model_for(name, precision):
     return c, m, pos, types, w
 
 
-def ef_timing(name, precision=None, runs=5, warmup=20):
+def ef_timing(name, precision=None, runs=5, warmup=20, order="given"):
     """One energy + force evaluation of a workload on a prebuilt list (the
     list at r_cut, built and timed separately): median over `runs` runs of
     `iters` evaluations after `warmup`, with the CFConv launches timed by the
     library's event hook."""
     import torch
     from schnet_continuous_filter_amd import _lib as L
-    c, m, pos, types, w = model_for(name, precision)
+    c, m, pos, types, w = model_for(name, precision, order)
     s = c.system
     R, N = s.n_replicas, s.atoms_per_replica
     n = R * N
@@ -566,7 +574,9 @@ def ef_timing(name, precision=None, runs=5, warmup=20):
 def ef_only(args):
     """Energy + force evaluations of one workload, nothing else (for profiler
     runs whose kernel statistics must cover exactly those launches)."""
-    r = ef_timing(args.ef_only, args.precision, runs=max(1, args.repeats), warmup=args.warmup)
+    r = ef_timing(args.ef_only, args.precision, runs=max(1, args.repeats), warmup=args.warmup,
+                  order=args.order)
+    r["order"] = args.order
     r.pop("ms_per_ef_runs")
     print(json.dumps(r))
 

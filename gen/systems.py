@@ -108,3 +108,12 @@ def model_weights(rng: np.random.Generator, n_types: int, D: int, Dr: int, T: in
     flat = np.concatenate([p.ravel() for p in parts]).astype(np.float32)
     assert flat.size == n_model_weights(n_types, D, Dr, T, H)
     return flat
+
+
+def cell_order(pos, box, cell=5.0):
+    """A relabelling of the atoms of one periodic cube: their order by cell of
+    the grid of cells of side >= `cell` (z-major, then y, then x; stable
+    inside a cell), as an index array."""
+    nc = max(1, int(box // cell))
+    c = np.floor(pos.astype(np.float64) / (box / nc)).astype(np.int64).clip(0, nc - 1)
+    return np.argsort((c[:, 2] * nc + c[:, 1]) * nc + c[:, 0], kind="stable")

@@ -407,3 +407,63 @@ def test_readout_as_wide_as_the_features(gpu_lib):
         w = make_weights(m, 9, bias_scale=0.05)
         check(gpu_lib, dataclasses.replace(cfg, model=m), pos, types, w,
               what=f"cg32 D 64 H 64 dtype {dtype}")
+
+
+def test_bulk64k_relabelled_in_cell_order(gpu_lib):
+    """The same 65,536-atom box with its atoms relabelled in the order of 5 A
+    cells (the order a cell-sorted MD code keeps; bench.py --order cell):
+    the list, the tile partition and every summation order change, the
+    energy and the relabelled forces must not. Against the stored oracle
+    values, fp32 bars."""
+    import json
+    import os
+    from gen.systems import cell_order
+    from tests.gpu_helpers import E_TOL_F32
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                       "bulk64k_oracle.json")))
+    cfg, pos, types, w = make_config("bulk64k")
+    m = cfg.model
+    k = cell_order(pos, cfg.system.box)
+    inv = np.empty_like(k)
+    inv[k] = np.arange(len(k))
+    system = lib_system(gpu_lib, cfg.system)
+    E, F, _, col = run_gpu(gpu_lib, m, system, pos[k].copy(), types[k].copy(), w, m.r_cut)
+    assert len(col) == gold["edges"]
+    atoms = np.asarray(gold["forces"]["0"]["atoms"])
+    Fo = np.asarray(gold["forces"]["0"]["F"])
+    rms = np.sqrt(np.mean(Fo ** 2))
+    ferr = np.max(np.abs(F[inv[atoms]] - Fo)) / rms
+    eerr = abs(E[0] - gold["energy"]["0"]["E"]) / abs(gold["energy"]["0"]["E"])
+    print(f"bulk64k in cell order: E err {eerr:.2e}, F max/rms {ferr:.2e}")
+    assert eerr <= E_TOL_F32 and ferr <= F_TOL_F32
+
+
+def test_largest_admitted_system(gpu_lib):
+    """The largest batch the library admits (at most 2^22 atoms): 15,592
+    replicas of the 269-bead chain model, 4,194,248 atoms and about 68M
+    directed edges, where the per-atom feature arrays span 2^31 - 2^15 bytes
+    and the masked-gather offset sits just past their end. Replicas are
+    independent, so sampled replicas are checked exactly against the oracle
+    on that replica alone (the batch repeats the first 1024 conformations),
+    with the fp32 filter at the fp32 bars and the bf16 filter at its own."""
+    import dataclasses
+    cfg, pos0, types0, w = make_config("md1024")
+    N = cfg.system.atoms_per_replica
+    R = (1 << 22) // N
+    assert R * N <= (1 << 22) < (R + 1) * N
+    reps = np.arange(R) % 1024
+    pos = pos0.reshape(1024, N, 3)[reps].reshape(-1, 3)
+    types = types0.reshape(1024, N)[reps].reshape(-1)
+    system = lib_system(gpu_lib, cfg.system, R)
+    for dtype in (0, 1):
+        m = dataclasses.replace(cfg.model, filter_dtype=dtype)
+        E, F, _, col = run_gpu(gpu_lib, m, system, pos, types, w, m.r_cut)
+        for r in (0, 7777, R - 1):
+            sl = slice(r * N, (r + 1) * N)
+            rp, cl = oracle.neighbor_list(pos[sl], 1, N, False, 0.0, m.r_cut)
+            Eo, Fo = oracle.energy_forces(oracle_desc(m), w, pos[sl], types[sl], rp, cl,
+                                          n_replicas=1)
+            re, rf = assert_energy_forces(E[r:r + 1], F[sl], Eo, Fo, bf16=dtype == 1,
+                                          what=f"max size r{r} dtype {dtype}")
+            print(f"largest batch, dtype {dtype}, replica {r}: {len(col)} edges in all, "
+                  f"E rel {re:.2e}, F max/rms {rf:.2e}")
