@@ -58,6 +58,15 @@
 // edge's own lanes. Each interaction block writes its own force rows; a small
 // kernel sums the blocks.
 //
+// Base-2 units (every precision but the fp16 pairs): the basis enters the
+// first product multiplied by log2 e, and both biases are stored multiplied by
+// log2 e, so that the first product yields u = a log2 e, the shifted softplus
+// is taken as ssp(a) / ln 2 = max(u, 0) + log2((1 + 2^-|u|) / 2) (no multiply
+// by log2 e or ln 2 per value), and the second product, starting from its
+// bias, yields w log2 e. The sums over a receiver's edges (h, q) and dE/dd
+// are scaled back by ln 2 once each, where they leave the kernel; the biases
+// are the accumulators' starting values, so no per-value bias add remains.
+//
 // MFMA: v_mfma_f32_16x16x4_f32 (fp32 filters), v_mfma_f32_16x16x32_bf16
 // (bfloat16 filters) or v_mfma_f32_16x16x32_f16 (fp16 filters whose weight
 // columns carry power-of-two scales, §4.4 "Channel-wise quantization"), fp32
@@ -76,6 +85,24 @@ constexpr int kEdges = 16;  // edges per wave tile: the MFMA column dimension
 // (the library admits at most 2^22 atoms, so N D 4 <= 2^31, and the offsets
 // added to it stay below 2^31 + 512): bounded buffer loads from it read zeros.
 constexpr uint32_t kMaskedRow = 0x80000000u;
+
+// The filter runs in base-2 units (above) in every precision but the fp16
+// pairs, whose operand scales are bounds of the unscaled basis and softplus.
+template <int PR>
+constexpr bool kBase2 = PR != PREC_F16X2;
+// Accumulators start from the bias where no column scale follows the product.
+template <int PR>
+constexpr bool kBiasInit = PR == PREC_F32 || PR == PREC_BF16;
+// The kernels request their first gathers before the first product with the
+// 16-bit filters (faster there); at fp32 and on fp16 pairs the backward would
+// spill and the forward runs no faster, so they request them after it.
+template <int PR>
+constexpr bool kEarlyGather = PR == PREC_BF16 || PR == PREC_F16S;
+// A sum over messages (h, q) or a dE/dd leaving the kernel, back in natural units.
+template <int PR>
+__device__ __forceinline__ float out_scale(float v) {
+  return kBase2<PR> ? v * LN2F : v;
+}
 
 __device__ __forceinline__ float min_image(float u, float box, float half) {
   if (u > half) return u - box;
@@ -217,8 +244,11 @@ static void fill_image(int Dr, const float* Wf1, const float* cf1, const float* 
                           out + P::W2, sc + D);
   }
   float* bias = reinterpret_cast<float*>(out + P::BIAS);
-  std::memcpy(bias, cf1, D * sizeof(float));
-  std::memcpy(bias + D, cf2, D * sizeof(float));
+  const double k = kBase2<PR> ? 1.4426950408889634074 : 1.0;   // log2 e
+  for (int n = 0; n < D; ++n) {
+    bias[n] = (float)(k * (double)cf1[n]);
+    bias[D + n] = (float)(k * (double)cf2[n]);
+  }
 }
 
 template <class P>
@@ -310,6 +340,9 @@ __device__ __forceinline__ void gemm1_plain(f32x4 (&acc)[NA][D / 16], const unsi
   asm volatile("" : "+v"(step));
   const int k0 = PL * grp;
   const float coef2 = p.rbf_coef2, inv_s2 = p.rbf_inv_s2;
+  // the envelope and its derivative times log2 e (base-2 units)
+  static_assert(kBase2<PR>, "the fp16 pairs take gemm1_split");
+  const float gC = g.C * LOG2EF, gCp = g.Cp * LOG2EF;
   // one chunk of basis functions: evaluate, then accumulate its products
   auto chunk = [&](int c) {
     float b[NA][PL];
@@ -321,11 +354,11 @@ __device__ __forceinline__ void gemm1_plain(f32x4 (&acc)[NA][D / 16], const unsi
       const float z = __builtin_fmaf(-(float)(k0 + CH * c), step, g.d0);
       float gk = g.in * __builtin_amdgcn_exp2f(coef2 * z * z);
       float q = __builtin_amdgcn_exp2f(__builtin_fmaf(p.rbf_qa, z, p.rbf_qb));
-      float tk = g.Cp - z * inv_s2 * g.C;
-      const float dt = step * inv_s2 * g.C;
+      float tk = gCp - z * inv_s2 * gC;
+      const float dt = step * inv_s2 * gC;
 #pragma unroll
       for (int t = 0; t < PL; ++t) {
-        b[0][t] = gk * g.C;
+        b[0][t] = gk * gC;
         if constexpr (NA == 2) {
           b[1][t] = gk * tk;
           tk += dt;
@@ -339,8 +372,8 @@ __device__ __forceinline__ void gemm1_plain(f32x4 (&acc)[NA][D / 16], const unsi
         // d - mu_k with one rounding (the product k step is exact inside the fma)
         const float z = __builtin_fmaf(-(float)(k0 + CH * c + t), step, g.d0);
         const float gs = g.in * __builtin_amdgcn_exp2f(coef2 * z * z);
-        b[0][t] = gs * g.C;
-        if constexpr (NA == 2) b[1][t] = gs * (g.Cp - z * inv_s2 * g.C);
+        b[0][t] = gs * gC;
+        if constexpr (NA == 2) b[1][t] = gs * (gCp - z * inv_s2 * gC);
       }
     }
     if constexpr (H16) {
@@ -673,43 +706,52 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, false>()), 1) void k_cf_fwd(CfPa
     const ImgLanes<D, PR> wl(lane_t);
     const TileLanes tl(lane_t);
 
-    // s = ssp(b~ Wf1 + cf1)
+    // the sender rows of the first 64 features, requested before the first
+    // product (16-bit filters) or the second. Lanes of edges that contribute
+    // nothing (at or beyond the cutoff, or past the worker's last edge)
+    // gather from an offset past the end of x, which the bounded loads read
+    // as zeros: their messages vanish without a mask multiply
+    const uint32_t xo = g.in > 0.f ? ((uint32_t)th.j * (uint32_t)D + (uint32_t)g4) * 4u
+                                   : kMaskedRow;
+    f32x4 xg[4];
+    if constexpr (kEarlyGather<PR>) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) xg[b] = bload4(rx, xo + (uint32_t)(64 * b));
+    }
+
+    // s = ssp(b~ Wf1 + cf1) (base-2 units: s / ln 2 from u = a log2 e)
     f32x4 s[1][NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) s[0][nb] = f32x4{};
+    for (int nb = 0; nb < NB; ++nb)
+      s[0][nb] = kBiasInit<PR> ? bias4<P>(p, lds, g4, 16 * nb) : f32x4{};
     gemm1<D, KP, PR, 1>(s, lds, p, g, lane, ss.a[0], ss.a[1]);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const f32x4 c1 = bias4<P>(p, lds, g4, 16 * nb);
       if constexpr (PR == PREC_F16S) {
+        const f32x4 c1 = bias4<P>(p, lds, g4, 16 * nb);
         const f32x4 s1 = scale4<P>(p, lds, g4, 16 * nb);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s[0][nb][r] = ssp(fmaf(s[0][nb][r], s1[r], c1[r]));
+        for (int r = 0; r < 4; ++r) s[0][nb][r] = ssp2(fmaf(s[0][nb][r], s1[r], c1[r]));
       } else if constexpr (PR == PREC_F16X2) {
+        const f32x4 c1 = bias4<P>(p, lds, g4, 16 * nb);
 #pragma unroll
         for (int r = 0; r < 4; ++r) s[0][nb][r] = ssp(fmaf(s[0][nb][r], ss.u[0], c1[r]));
       } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s[0][nb][r] = ssp(s[0][nb][r] + c1[r]);
+        for (int r = 0; r < 4; ++r) s[0][nb][r] = ssp2(s[0][nb][r]);
       }
     }
     pjx = bload(wk.rpos, (uint32_t)jn * 12u);
     pjy = bload(wk.rpos, (uint32_t)jn * 12u + 4);
     pjz = bload(wk.rpos, (uint32_t)jn * 12u + 8);
 
-    // w = s Wf2 + cf2 (masked beyond the cutoff); messages x_j * w summed per
-    // receiver, 64 features at a time. The sender rows of the first 64
-    // features are requested ahead of the product; a block's registers are
-    // refilled with the next 64 features' as soon as they are used.
-    // lanes of edges that contribute nothing (at or beyond the cutoff, or
-    // past the worker's last edge) gather from an offset past the end of x,
-    // which the bounded loads read as zeros: their messages vanish without a
-    // mask multiply
-    const uint32_t xo = g.in > 0.f ? ((uint32_t)th.j * (uint32_t)D + (uint32_t)g4) * 4u
-                                   : kMaskedRow;
-    f32x4 xg[4];
+    if constexpr (!kEarlyGather<PR>) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) xg[b] = bload4(rx, xo + (uint32_t)(64 * b));
+      for (int b = 0; b < 4; ++b) xg[b] = bload4(rx, xo + (uint32_t)(64 * b));
+    }
+    // w = s Wf2 + cf2 (masked beyond the cutoff); messages x_j * w summed per
+    // receiver, 64 features at a time; a block's gather registers are
+    // refilled with the next 64 features' as soon as they are used
     __builtin_amdgcn_sched_barrier(0);
     // the products of each 64 features are formed right before their
     // messages (fewer live accumulators)
@@ -719,25 +761,29 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, false>()), 1) void k_cf_fwd(CfPa
       f32x4 w[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        w[b] = f32x4{};
+        w[b] = kBiasInit<PR> ? bias4<P>(p, lds, g4, D + 16 * (4 * pss + b)) : f32x4{};
         gemm2_block<P>(w[b], os, lds, 4 * pss + b, wl);
       }
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int nb = 4 * pss + b;
-        const f32x4 c2 = bias4<P>(p, lds, g4, D + 16 * nb);
-        if constexpr (PR == PREC_F16S) w[b] *= scale4<P>(p, lds, g4, D + 16 * nb);
-        if constexpr (PR == PREC_F16X2) w[b] *= ss.u[2];
+        if constexpr (!kBiasInit<PR>) {
+          const f32x4 c2 = bias4<P>(p, lds, g4, D + 16 * nb);
+          const f32x4 s2 = PR == PREC_F16S ? scale4<P>(p, lds, g4, D + 16 * nb)
+                                           : f32x4{ss.u[2], ss.u[2], ss.u[2], ss.u[2]};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) w[b][r] = fmaf(w[b][r], s2[r], c2[r]);
+        }
         f32x4 m;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) m[r] = xg[b][r] * (w[b][r] + c2[r]);
+        for (int r = 0; r < 4; ++r) m[r] = xg[b][r] * w[b][r];
         tile_put(Tb, b, m, tl);
         if (pss + 1 < NB / 4) xg[b] = bload4(rx, xo + (uint32_t)(64 * (nb + 4)));
       }
       wave_sync();
       float* hout = p.h + 64 * pss + fcol;
       column_segments(p, Tb, win, cur, ib, th.nfin, ts, th.len, th.ncur < ib, carry[pss], lane,
-                      [&](int i, float tot) { hout[(size_t)i * D] = tot; });
+                      [&](int i, float tot) { hout[(size_t)i * D] = out_scale<PR>(tot); });
       wave_sync();
     }
     cur = th.ncur;
@@ -751,7 +797,7 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, false>()), 1) void k_cf_fwd(CfPa
   if (wk.tail) {
 #pragma unroll
     for (int pss = 0; pss < NB / 4; ++pss)
-      p.side_h[(size_t)wk.rid * D + 64 * pss + fcol] = carry[pss];
+      p.side_h[(size_t)wk.rid * D + 64 * pss + fcol] = out_scale<PR>(carry[pss]);
   }
 }
 
@@ -797,42 +843,10 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, true>()), 1) void k_cf_bwd(CfPar
     const ImgLanes<D, PR> wl(lane_t);
     const TileLanes tl(lane_t);
 
-    // GEMM1: a = b~ Wf1 + cf1 and its tangent a' = (d b~/dd) Wf1;
-    // s = ssp(a), s' = sigmoid(a) a'
-    f32x4 av[2][NB];
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) av[q][nb] = f32x4{};
-    gemm1<D, KP, PR, 2>(av, lds, p, g, lane, ss.a[0], ss.a[1]);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const f32x4 c1 = bias4<P>(p, lds, g4, 16 * nb);
-      if constexpr (PR == PREC_F16S) {
-        const f32x4 s1 = scale4<P>(p, lds, g4, 16 * nb);
-        av[0][nb] *= s1;
-        av[1][nb] *= s1;
-      }
-      if constexpr (PR == PREC_F16X2) {
-        av[0][nb] *= ss.u[0];
-        av[1][nb] *= ss.u[1];
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float sv, sg;
-        ssp_sig(av[0][nb][r] + c1[r], sv, sg);
-        av[0][nb][r] = sv;
-        av[1][nb][r] = sg * av[1][nb][r];
-      }
-    }
-    pjx = bload(wk.rpos, (uint32_t)jn * 12u);
-    pjy = bload(wk.rpos, (uint32_t)jn * 12u + 4);
-    pjz = bload(wk.rpos, (uint32_t)jn * 12u + 8);
-
-    // gathers of the first 64 features (x_j, dE/dh_j, x_i, dE/dh_i), issued
-    // ahead of the tangent product so that their latency is covered
-    // (edges that contribute nothing read zeros, as in the forward: their
-    // source sums and dE/dd vanish)
+    // gathers of the first 64 features (x_j, dE/dh_j, x_i, dE/dh_i); edges
+    // that contribute nothing read zeros, as in the forward (their source
+    // sums and dE/dd vanish). Issued before the first product where the
+    // registers allow (16-bit filters), else before the second.
     const uint32_t jo = g.in > 0.f ? ((uint32_t)th.j * (uint32_t)D + (uint32_t)g4) * 4u
                                    : kMaskedRow;
     const uint32_t io = g.in > 0.f ? ((uint32_t)th.recv * (uint32_t)D + (uint32_t)g4) * 4u
@@ -845,8 +859,52 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, true>()), 1) void k_cf_bwd(CfPar
       Gb[2] = bload4(rx, io + co);
       Gb[3] = bload4(rgh, io + co);
     };
+    if constexpr (kEarlyGather<PR>) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) gather(b, G[b]);
+      for (int b = 0; b < 4; ++b) gather(b, G[b]);
+    }
+
+    // GEMM1: a = b~ Wf1 + cf1 and its tangent a' = (d b~/dd) Wf1;
+    // s = ssp(a), s' = sigmoid(a) a' (base-2 units: all three times log2 e)
+    f32x4 av[2][NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      av[0][nb] = kBiasInit<PR> ? bias4<P>(p, lds, g4, 16 * nb) : f32x4{};
+      av[1][nb] = f32x4{};
+    }
+    gemm1<D, KP, PR, 2>(av, lds, p, g, lane, ss.a[0], ss.a[1]);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      if constexpr (PR == PREC_F16S) {
+        const f32x4 c1 = bias4<P>(p, lds, g4, 16 * nb);
+        const f32x4 s1 = scale4<P>(p, lds, g4, 16 * nb);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) av[0][nb][r] = fmaf(av[0][nb][r], s1[r], c1[r]);
+        av[1][nb] *= s1;
+      }
+      if constexpr (PR == PREC_F16X2) {
+        const f32x4 c1 = bias4<P>(p, lds, g4, 16 * nb);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) av[0][nb][r] = fmaf(av[0][nb][r], ss.u[0], c1[r]);
+        av[1][nb] *= ss.u[1];
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float sv, sg;
+        if constexpr (kBase2<PR>) ssp2_sig(av[0][nb][r], sv, sg);
+        else ssp_sig(av[0][nb][r], sv, sg);
+        av[0][nb][r] = sv;
+        av[1][nb][r] = sg * av[1][nb][r];
+      }
+    }
+    pjx = bload(wk.rpos, (uint32_t)jn * 12u);
+    pjy = bload(wk.rpos, (uint32_t)jn * 12u + 4);
+    pjz = bload(wk.rpos, (uint32_t)jn * 12u + 8);
+
+    if constexpr (!kEarlyGather<PR>) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) gather(b, G[b]);
+    }
     __builtin_amdgcn_sched_barrier(0);
 
     // GEMM2: the tangents of all blocks, w' = s' Wf2, and the values w = s Wf2
@@ -861,7 +919,7 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, true>()), 1) void k_cf_bwd(CfPar
         wt[nb] = f32x4{};
         gemm2_block<P>(wt[nb], ot, lds, nb, wl);
         if (nb < 4) {
-          wv[nb] = f32x4{};
+          wv[nb] = kBiasInit<PR> ? bias4<P>(p, lds, g4, D + 16 * nb) : f32x4{};
           gemm2_block<P>(wv[nb], os, lds, nb, wl);
         }
       }
@@ -877,20 +935,23 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, true>()), 1) void k_cf_bwd(CfPar
       for (int b = 0; b < 4; ++b) {
         const int nb = 4 * pss + b;
         const f32x4 xj = G[b][0], gj = G[b][1], xi = G[b][2], gi = G[b][3];
-        const f32x4 c2 = bias4<P>(p, lds, g4, D + 16 * nb);
         if constexpr (PR == PREC_F16S) {
+          const f32x4 c2 = bias4<P>(p, lds, g4, D + 16 * nb);
           const f32x4 s2 = scale4<P>(p, lds, g4, D + 16 * nb);
-          wv[b] *= s2;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) wv[b][r] = fmaf(wv[b][r], s2[r], c2[r]);
           wt[nb] *= s2;
         }
         if constexpr (PR == PREC_F16X2) {
-          wv[b] *= ss.u[2];
+          const f32x4 c2 = bias4<P>(p, lds, g4, D + 16 * nb);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) wv[b][r] = fmaf(wv[b][r], ss.u[2], c2[r]);
           wt[nb] *= ss.u[3];
         }
         f32x4 qv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          qv[r] = gj[r] * (wv[b][r] + c2[r]);
+          qv[r] = gj[r] * wv[b][r];
           gdd = fmaf(gi[r] * xj[r] + gj[r] * xi[r], wt[nb][r], gdd);
         }
         if (want_q) tile_put(Tb, b, qv, tl);
@@ -900,7 +961,7 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, true>()), 1) void k_cf_bwd(CfPar
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          wv[b] = f32x4{};
+          wv[b] = kBiasInit<PR> ? bias4<P>(p, lds, g4, D + 16 * (4 * (pss + 1) + b)) : f32x4{};
           gemm2_block<P>(wv[b], os, lds, 4 * (pss + 1) + b, wl);
         }
       }
@@ -908,13 +969,13 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, true>()), 1) void k_cf_bwd(CfPar
         wave_sync();
         float* qout = p.q_out + 64 * pss + fcol;
         column_segments(p, Tb, win, cur, ib, th.nfin, ts, th.len, th.ncur < ib, carry[pss], lane,
-                        [&](int i, float tot) { qout[(size_t)i * D] = tot; });
+                        [&](int i, float tot) { qout[(size_t)i * D] = out_scale<PR>(tot); });
         wave_sync();
       }
     }
     gdd += __shfl_xor(gdd, 16, 64);
     gdd += __shfl_xor(gdd, 32, 64);
-    const float gd = gdd * g.invd;
+    const float gd = gdd * (kBase2<PR> ? g.invd * LN2F : g.invd);
 
     // this block's dE/dr rows: the edge contributions gd u summed per receiver
     // by a segmented scan along the tile's 16 rows (one edge per lane of a
@@ -968,7 +1029,7 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, true>()), 1) void k_cf_bwd(CfPar
     if (want_q) {
 #pragma unroll
       for (int pss = 0; pss < NB / 4; ++pss)
-        p.side_h[(size_t)wk.rid * D + 64 * pss + fcol] = carry[pss];
+        p.side_h[(size_t)wk.rid * D + 64 * pss + fcol] = out_scale<PR>(carry[pss]);
     }
     if (lane < 3)
       p.side_f[(size_t)wk.rid * 3 + lane] = lane == 0 ? fcarry[0] : (lane == 1 ? fcarry[1] : fcarry[2]);

@@ -126,6 +126,30 @@ __device__ __forceinline__ float ssp(float a) {
   return fmaf(LN2F, __builtin_amdgcn_logf(fmaf(t, 0.5f, 0.5f)), fmaxf(a, 0.f));
 }
 
+// max(u, 0) for finite u as the median of (u, 0, FLT_MAX): one instruction
+// on a product's output, which fmaxf would first canonicalise (+inf maps to
+// FLT_MAX; a NaN u yields a NaN through the other terms of the softplus).
+__device__ __forceinline__ float pos_part(float u) {
+  return __builtin_amdgcn_fmed3f(u, 0.f, 3.40282347e38f);
+}
+
+// The same in base-2 units: for a pre-activation given as u = a log2 e,
+//   ssp(a) / ln 2 = max(u, 0) + log2(h),  h = (1 + 2^-|u|) / 2,
+//   sigmoid(a)    = (u >= 0 ? 1 : 2^-|u|) / (2 h),
+// one multiply fewer per value than from a (the factors log2 e and ln 2
+// are carried by the inputs and outputs of the products around it).
+__device__ __forceinline__ void ssp2_sig(float u, float& s, float& sg) {
+  const float t = __builtin_amdgcn_exp2f(-fabsf(u));
+  const float h = fmaf(t, 0.5f, 0.5f);
+  const float r = __builtin_amdgcn_rcpf(h);
+  s = __builtin_amdgcn_logf(h) + pos_part(u);
+  sg = (u >= 0.f ? 0.5f : 0.5f * t) * r;
+}
+__device__ __forceinline__ float ssp2(float u) {
+  const float t = __builtin_amdgcn_exp2f(-fabsf(u));
+  return __builtin_amdgcn_logf(fmaf(t, 0.5f, 0.5f)) + pos_part(u);
+}
+
 __device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
