@@ -621,13 +621,24 @@ struct Walk {
   __amdgpu_buffer_rsrc_t rrow, rcol, rpos;
 };
 
+// Work-groups are dealt to the chip's 8 XCDs in turn (work-group b to XCD
+// b mod 8), and each XCD has its own L2. The group that runs on XCD x as its
+// k-th takes the range index (x's first) + k, so that every XCD walks one
+// contiguous part of the list and its L2 holds the rows that part gathers.
+// Only which group runs which range changes: the results do not.
+__device__ __forceinline__ int xcd_range_index() {
+  const int G = (int)gridDim.x, b = (int)blockIdx.x;
+  const int q = G >> 3, r = G & 7, x = b & 7;
+  return x * q + min(x, r) + (b >> 3);
+}
+
 // The four waves a SIMD holds (waves w, w + 4, ... of a work-group; waves
 // are placed on the SIMDs in turn) take consecutive ranges, so that each
 // SIMD's share of tiles is balanced to one tile.
 template <class P>
 __device__ __forceinline__ bool worker_range(const CfParams& p, int wave, Walk& w) {
   const uint32_t N = (uint32_t)p.n_atoms;
-  w.rid = (int)blockIdx.x * P::NW + (wave & 3) * (P::NW / 4) + (wave >> 2);
+  w.rid = xcd_range_index() * P::NW + (wave & 3) * (P::NW / 4) + (wave >> 2);
   w.ia = cload(p.wg_start, w.rid);
   const int ia1 = cload(p.wg_start, w.rid + 1);
   w.E0 = cload(p.wg_edge, w.rid);
