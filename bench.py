@@ -454,10 +454,17 @@ def topology(args):
 
 def cf_flops(m, edges):
     """Algorithmic work of the fused CFConv kernels per launch: the two filter
-    products per directed edge, 2 D (Dr + D) flops forward; the backward
-    recomputes them and runs their derivative through both, 4 D (Dr + D)."""
+    products per directed edge, 2 D (Dr + D) flops forward. The backward of a
+    block whose source sums are wanted recomputes both products and runs
+    their derivative along d through both, 4 D (Dr + D); the first block's
+    backward (no source sums: its input is the embedding) needs the first
+    product's values and tangents and the second's tangents only,
+    2 D (2 Dr + D). Returned: forward, and the backward averaged over the T
+    launches of one evaluation (what the mean launch time is taken over)."""
     fwd = 2.0 * m.D * (m.Dr + m.D) * edges
-    return fwd, 2.0 * fwd
+    bwd_q = 4.0 * m.D * (m.Dr + m.D) * edges
+    bwd_0 = 2.0 * m.D * (2 * m.Dr + m.D) * edges
+    return fwd, ((m.T - 1) * bwd_q + bwd_0) / m.T
 
 
 def roofline(m, edges, bwd_us, fwd_us, workload):
@@ -472,7 +479,7 @@ def roofline(m, edges, bwd_us, fwd_us, workload):
     achieved = fl_b / (bwd_us * 1e-6) / 1e12
     rec = counter_record("bwd", workload, m)
     traffic = rec["bytes_per_launch"] if rec else None
-    out = {"kernel": "k_cf_bwd (fused CFConv backward, one interaction block)",
+    out = {"kernel": "k_cf_bwd (fused CFConv backward; mean over the T launches of an evaluation)",
            "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
            "frac": achieved / peak, "traffic": traffic,
            "flops_per_launch": fl_b, "avg_launch_us": bwd_us, "fwd_avg_launch_us": fwd_us,

@@ -667,24 +667,26 @@ __global__ __launch_bounds__(kEnergyThreads) void k_finish(const float* eps, int
                                                            float* energy, const float* fb, int T,
                                                            int64_t n3, float* forces, float* vel,
                                                            float half_kick, const int32_t* rowptr,
-                                                           int G, const float* side_f,
+                                                           int G0, int G, const float* side_f,
                                                            int64_t side_stride, DevStatus* st) {
   if ((int)blockIdx.x >= n_rep) {
     const int64_t k = (int64_t)(blockIdx.x - n_rep) * kEnergyThreads + threadIdx.x;
     if (k >= n3) return;
     const int64_t i = k / 3;
     const int c = (int)(k - 3 * i);
-    int w0 = 0, w1 = 0;
+    int w0 = 0, w1 = 0, v0 = 0, v1 = 0;   // cut parts of blocks t > 0 and of block 0
     if (side_f) {
       const int64_t E = rowptr[n3 / 3];
       cut_workers(rowptr[i], rowptr[i + 1], (E + 15) / 16, G, w0, w1);
+      cut_workers(rowptr[i], rowptr[i + 1], (E + 15) / 16, G0, v0, v1);
     }
     float s = 0.f;
     for (int t = 0; t < T; ++t) {
       float v = fb[(int64_t)t * n3 + k];
-      if (w0 < w1) {   // block t's row completed by the other workers' parts
+      const int a = t == 0 ? v0 : w0, b = t == 0 ? v1 : w1;
+      if (a < b) {   // block t's row completed by the other workers' parts
         float acc = 0.f;
-        for (int w = w0; w < w1; ++w) acc += side_f[t * side_stride + 3 * w + c];
+        for (int w = a; w < b; ++w) acc += side_f[t * side_stride + 3 * w + c];
         v += acc;
       }
       s += v;
@@ -719,13 +721,13 @@ __global__ __launch_bounds__(kEnergyThreads) void k_finish(const float* eps, int
 
 hipError_t launch_finish(const float* eps, int n_rep, int n_per, float* energy, const float* fb,
                          int T, int64_t n_atoms, float* forces, float* vel, float half_kick,
-                         const int32_t* rowptr, int G, const float* side_f, int64_t side_stride,
-                         DevStatus* st, hipStream_t s) {
+                         const int32_t* rowptr, int G0, int G, const float* side_f,
+                         int64_t side_stride, DevStatus* st, hipStream_t s) {
   const int64_t n3 = 3 * n_atoms;
   const int64_t nb = n_rep + (n3 + kEnergyThreads - 1) / kEnergyThreads;
   hipLaunchKernelGGL(k_finish, dim3((unsigned)nb), dim3(kEnergyThreads), 0, s, eps, n_rep, n_per,
-                     energy, fb, T, n3, forces, vel, half_kick, rowptr, G, side_f, side_stride,
-                     st);
+                     energy, fb, T, n3, forces, vel, half_kick, rowptr, G0, G, side_f,
+                     side_stride, st);
   return hipGetLastError();
 }
 

@@ -169,6 +169,8 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
   int32_t* wg_start_b = reinterpret_cast<int32_t*>(ws + L.wg_start_b);
   int32_t* wg_edge = reinterpret_cast<int32_t*>(ws + L.wg_edge);
   int32_t* wg_edge_b = reinterpret_cast<int32_t*>(ws + L.wg_edge_b);
+  int32_t* wg_start_b0 = reinterpret_cast<int32_t*>(ws + L.wg_start_b0);
+  int32_t* wg_edge_b0 = reinterpret_cast<int32_t*>(ws + L.wg_edge_b0);
   float* x = reinterpret_cast<float*>(ws + L.x);
   float* au = reinterpret_cast<float*>(ws + L.au);
   float* gbuf = reinterpret_cast<float*>(ws + L.gbuf);
@@ -179,14 +181,15 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
   const size_t ND = (size_t)n * D;
   const int prec = d.filter_dtype;
   const int bf16 = prec == PREC_BF16;
-  const int wf = cf_workers(D, m->KP, prec, 0), wb = cf_workers(D, m->KP, prec, 1);
-  const int Gf = cf_grid(m, n, wf), Gb = cf_grid(m, n, wb);
+  // workers of the forward, the backward and the first block's backward
+  const int wf = cf_workers(D, m->KP, prec, 0), wb = cf_workers(D, m->KP, prec, 1),
+            wb0 = cf_workers(D, m->KP, prec, 2);
+  const int Gf = cf_grid(m, n, wf), Gb = cf_grid(m, n, wb), Gb0 = cf_grid(m, n, wb0);
   hipError_t e;
 
   if ((e = launch_setup(uf ? nullptr : rowptr, (int)n, Gf * wf, wg_start, wg_edge, Gb * wb,
-                        wg_start_b, wg_edge_b, types, m->w + m->off_emb, D, d.n_types, x, mark, st,
-                        s)) !=
-      hipSuccess)
+                        wg_start_b, wg_edge_b, Gb0 * wb0, wg_start_b0, wg_edge_b0, types,
+                        m->w + m->off_emb, D, d.n_types, x, mark, st, s)) != hipSuccess)
     return hip_fail(e);
 
   CfParams p{};
@@ -328,9 +331,10 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
       b.cut_side = p.side_h;
     }
     if ((e = launch_atom(b, D, D, prec, m->n_cu, s)) != hipSuccess) return hip_fail(e);
+    // the first block (no source sums) runs its own kernel and partition
     p.img = block_img(t);
-    p.wg_start = wg_start_b;
-    p.wg_edge = wg_edge_b;
+    p.wg_start = t > 0 ? wg_start_b : wg_start_b0;
+    p.wg_edge = t > 0 ? wg_edge_b : wg_edge_b0;
     p.x = x + t * ND;
     p.gh = gbuf;
     p.q_out = t > 0 ? tmp : nullptr;
@@ -342,15 +346,16 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
       if ((e = uf_block(t, UF_BACKWARD)) != hipSuccess) return hip_fail(e);
     } else {
       ProfScope ps(profile ? 1 : -1, s);
-      if ((e = launch_cf_backward(D, m->KP, prec, p, Gb, s)) != hipSuccess) return hip_fail(e);
+      if ((e = launch_cf_backward(D, m->KP, prec, p, t > 0 ? Gb : Gb0, s)) != hipSuccess)
+        return hip_fail(e);
     }
   }
   // replica energies, and the forces (the unfused pipeline accumulates dE/dr
   // of every block into one array), each block's rows of cut receivers
   // completed from its side parts
   if ((e = launch_finish(eps, sys->n_replicas, sys->atoms_per_replica, energy, fblk, uf ? 1 : T, n,
-                         forces, vel_kick, half_kick, rowptr, Gb * wb, uf ? nullptr : side_f,
-                         kSideF, st, s)) != hipSuccess)
+                         forces, vel_kick, half_kick, rowptr, Gb0 * wb0, Gb * wb,
+                         uf ? nullptr : side_f, kSideF, st, s)) != hipSuccess)
     return hip_fail(e);
   return SN_OK;
 }
@@ -476,6 +481,8 @@ WsLayout ws_layout(int64_t n, int D, int T, int H) {
   L.wg_start_b = take((size_t)(kMaxWorkers + 1) * 4);
   L.wg_edge = take((size_t)(kMaxWorkers + 1) * 4);
   L.wg_edge_b = take((size_t)(kMaxWorkers + 1) * 4);
+  L.wg_start_b0 = take((size_t)(kMaxWorkers + 1) * 4);
+  L.wg_edge_b0 = take((size_t)(kMaxWorkers + 1) * 4);
   L.side_h = take((size_t)kMaxWorkers * (size_t)D * 4);
   L.side_f = take((size_t)T * kMaxWorkers * 3 * 4);
   L.scan_blocks = take((size_t)(scan_n / kScanChunk + 2) * 8);

@@ -150,6 +150,12 @@ template <int D, int PR, bool BWD>
 constexpr int cf_nw() {
   return BWD ? 8 : 16;
 }
+// The first block's backward (no source sums) fits 168 registers: three waves
+// per SIMD, but for the fp16 pairs (which would spill there).
+template <int D, int PR>
+constexpr int cf_nw_first() {
+  return PR == PREC_F16X2 ? 8 : 12;
+}
 
 int cf_kp(int Dr, int prec) {
   (void)prec;
@@ -812,9 +818,13 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, false>()), 1) void k_cf_fwd(CfPa
   }
 }
 
-template <int D, int KP, int PR>
-__global__ __launch_bounds__((64 * cf_nw<D, PR, true>()), 1) void k_cf_bwd(CfParams p) {
-  using P = Plan<D, KP, PR, cf_nw<D, PR, true>()>;
+// Q: the block's source sums q are wanted (every block but the first, whose
+// input is the embedding). Without them only the tangents are needed: the
+// second product's values, the softplus values and the messages drop out.
+template <int D, int KP, int PR, bool Q>
+__global__ __launch_bounds__((64 * (Q ? cf_nw<D, PR, true>() : cf_nw_first<D, PR>())), 1)
+    void k_cf_bwd(CfParams p) {
+  using P = Plan<D, KP, PR, (Q ? cf_nw<D, PR, true>() : cf_nw_first<D, PR>())>;
   constexpr int NB = D / 16;
   extern __shared__ __align__(16) unsigned char lds[];
   stage_image<P>(p.img, lds);
@@ -829,7 +839,9 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, true>()), 1) void k_cf_bwd(CfPar
   const uint32_t N = (uint32_t)p.n_atoms;
   const __amdgpu_buffer_rsrc_t rx = rsrc(p.x, N * (uint32_t)D * 4u);
   const __amdgpu_buffer_rsrc_t rgh = rsrc(p.gh, N * (uint32_t)D * 4u);
-  const bool want_q = p.q_out != nullptr;
+  // (tested at run time as well: with the branches kept, the fp32 kernel's
+  // schedule stays within its registers)
+  const bool want_q = Q && p.q_out != nullptr;
   const int fcol = col_feature(lane);
   SplitScales ss{};
   if constexpr (PR == PREC_F16X2) ss = split_scales<P>(p);
@@ -857,7 +869,8 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, true>()), 1) void k_cf_bwd(CfPar
     // gathers of the first 64 features (x_j, dE/dh_j, x_i, dE/dh_i); edges
     // that contribute nothing read zeros, as in the forward (their source
     // sums and dE/dd vanish). Issued before the first product where the
-    // registers allow (16-bit filters), else before the second.
+    // registers allow (16-bit filters with source sums), else before the
+    // second.
     const uint32_t jo = g.in > 0.f ? ((uint32_t)th.j * (uint32_t)D + (uint32_t)g4) * 4u
                                    : kMaskedRow;
     const uint32_t io = g.in > 0.f ? ((uint32_t)th.recv * (uint32_t)D + (uint32_t)g4) * 4u
@@ -870,7 +883,7 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, true>()), 1) void k_cf_bwd(CfPar
       Gb[2] = bload4(rx, io + co);
       Gb[3] = bload4(rgh, io + co);
     };
-    if constexpr (kEarlyGather<PR>) {
+    if constexpr (kEarlyGather<PR> && Q) {
 #pragma unroll
       for (int b = 0; b < 4; ++b) gather(b, G[b]);
     }
@@ -912,7 +925,7 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, true>()), 1) void k_cf_bwd(CfPar
     pjy = bload(wk.rpos, (uint32_t)jn * 12u + 4);
     pjz = bload(wk.rpos, (uint32_t)jn * 12u + 8);
 
-    if constexpr (!kEarlyGather<PR>) {
+    if constexpr (!(kEarlyGather<PR> && Q)) {
 #pragma unroll
       for (int b = 0; b < 4; ++b) gather(b, G[b]);
     }
@@ -921,7 +934,7 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, true>()), 1) void k_cf_bwd(CfPar
     // GEMM2: the tangents of all blocks, w' = s' Wf2, and the values w = s Wf2
     // of the first 64 features, as independent product chains; the values of
     // each further 64 features are formed once the previous ones are used
-    const auto os = W2Op<D, PR>::make(av[0], ss.a[2]);
+    const auto os = W2Op<D, PR>::make(av[0], ss.a[2]);   // unused (and dropped) without Q
     f32x4 wt[NB], wv[4];
     {
       const auto ot = W2Op<D, PR>::make(av[1], ss.a[3]);
@@ -929,7 +942,7 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, true>()), 1) void k_cf_bwd(CfPar
       for (int nb = 0; nb < NB; ++nb) {
         wt[nb] = f32x4{};
         gemm2_block<P>(wt[nb], ot, lds, nb, wl);
-        if (nb < 4) {
+        if (Q && nb < 4) {
           wv[nb] = kBiasInit<PR> ? bias4<P>(p, lds, g4, D + 16 * nb) : f32x4{};
           gemm2_block<P>(wv[nb], os, lds, nb, wl);
         }
@@ -947,28 +960,32 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, true>()), 1) void k_cf_bwd(CfPar
         const int nb = 4 * pss + b;
         const f32x4 xj = G[b][0], gj = G[b][1], xi = G[b][2], gi = G[b][3];
         if constexpr (PR == PREC_F16S) {
-          const f32x4 c2 = bias4<P>(p, lds, g4, D + 16 * nb);
           const f32x4 s2 = scale4<P>(p, lds, g4, D + 16 * nb);
+          if constexpr (Q) {
+            const f32x4 c2 = bias4<P>(p, lds, g4, D + 16 * nb);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) wv[b][r] = fmaf(wv[b][r], s2[r], c2[r]);
+            for (int r = 0; r < 4; ++r) wv[b][r] = fmaf(wv[b][r], s2[r], c2[r]);
+          }
           wt[nb] *= s2;
         }
         if constexpr (PR == PREC_F16X2) {
-          const f32x4 c2 = bias4<P>(p, lds, g4, D + 16 * nb);
+          if constexpr (Q) {
+            const f32x4 c2 = bias4<P>(p, lds, g4, D + 16 * nb);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) wv[b][r] = fmaf(wv[b][r], ss.u[2], c2[r]);
+            for (int r = 0; r < 4; ++r) wv[b][r] = fmaf(wv[b][r], ss.u[2], c2[r]);
+          }
           wt[nb] *= ss.u[3];
         }
         f32x4 qv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          qv[r] = gj[r] * wv[b][r];
+          if constexpr (Q) qv[r] = gj[r] * wv[b][r];
           gdd = fmaf(gi[r] * xj[r] + gj[r] * xi[r], wt[nb][r], gdd);
         }
         if (want_q) tile_put(Tb, b, qv, tl);
         if (pss + 1 < NB / 4) gather(nb + 4, G[b]);
       }
-      if (pss + 1 < NB / 4) {
+      if (Q && pss + 1 < NB / 4) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
@@ -1076,15 +1093,17 @@ __device__ __forceinline__ void partition_one(const int32_t* rowptr, int N, int6
   wg_edge[w] = (int32_t)e0;
 }
 
-// Set-up of one evaluation in one launch. The first nbp blocks write both
+// Set-up of one evaluation in one launch. The first nbp blocks write the
 // kernels' partitions (threads 0..G1 the first, the next G2 + 1 threads the
-// second; nbp = 0 when no partition is wanted); the next nbe blocks write
+// second, the next G3 + 1 the third; nbp = 0 when no partition is wanted);
+// the next nbe blocks write
 // the initial features x[i][:] = Emb[types[i]][:] (FlashSchNet §3.2 "SchNet
 // model"), four features per thread; any blocks after them apply the MD
 // build mark (BuildMark), one position component per thread.
 __global__ __launch_bounds__(kThreads) void k_setup(const int32_t* rowptr, int N, int G1,
                                                     int32_t* wg_start1, int32_t* wg_edge1, int G2,
-                                                    int32_t* wg_start2, int32_t* wg_edge2, int nbp,
+                                                    int32_t* wg_start2, int32_t* wg_edge2, int G3,
+                                                    int32_t* wg_start3, int32_t* wg_edge3, int nbp,
                                                     const int32_t* types, const float* emb,
                                                     int log2D, int n_types, float* x, int nbe,
                                                     BuildMark mark, DevStatus* st) {
@@ -1098,6 +1117,8 @@ __global__ __launch_bounds__(kThreads) void k_setup(const int32_t* rowptr, int N
     }
     if (t <= G1) partition_one(rowptr, N, E, G1, t, wg_start1, wg_edge1);
     else if (t <= G1 + 1 + G2) partition_one(rowptr, N, E, G2, t - G1 - 1, wg_start2, wg_edge2);
+    else if (t <= G1 + G2 + 2 + G3)
+      partition_one(rowptr, N, E, G3, t - G1 - G2 - 2, wg_start3, wg_edge3);
     return;
   }
   if ((int)blockIdx.x >= nbp + nbe) {
@@ -1123,9 +1144,10 @@ __global__ __launch_bounds__(kThreads) void k_setup(const int32_t* rowptr, int N
 
 hipError_t launch_setup(const int32_t* rowptr, int n_atoms, int G1, int32_t* wg_start1,
                         int32_t* wg_edge1, int G2, int32_t* wg_start2, int32_t* wg_edge2,
-                        const int32_t* types, const float* emb, int D, int n_types, float* x,
-                        const BuildMark* mark, DevStatus* st, hipStream_t s) {
-  const int nbp = rowptr ? (G1 + 1 + G2 + 1 + kThreads - 1) / kThreads : 0;
+                        int G3, int32_t* wg_start3, int32_t* wg_edge3, const int32_t* types,
+                        const float* emb, int D, int n_types, float* x, const BuildMark* mark,
+                        DevStatus* st, hipStream_t s) {
+  const int nbp = rowptr ? (G1 + 1 + G2 + 1 + G3 + 1 + kThreads - 1) / kThreads : 0;
   const int log2D = D == 128 ? 7 : 6;
   const int64_t n4 = (int64_t)n_atoms * D / 4;
   const int nbe = (int)((n4 + kThreads - 1) / kThreads);
@@ -1134,8 +1156,8 @@ hipError_t launch_setup(const int32_t* rowptr, int n_atoms, int G1, int32_t* wg_
   if (nb == 0) return hipSuccess;
   const BuildMark mk = mark ? *mark : BuildMark{};
   hipLaunchKernelGGL(k_setup, dim3((unsigned)nb), dim3(kThreads), 0, s, rowptr, n_atoms, G1,
-                     wg_start1, wg_edge1, G2, wg_start2, wg_edge2, nbp, types, emb, log2D, n_types,
-                     x, nbe, mk, st);
+                     wg_start1, wg_edge1, G2, wg_start2, wg_edge2, G3, wg_start3, wg_edge3, nbp,
+                     types, emb, log2D, n_types, x, nbe, mk, st);
   return hipGetLastError();
 }
 
@@ -1144,15 +1166,19 @@ template <int D, int KP, int PR>
 struct CfKernels {
   using PF = Plan<D, KP, PR, cf_nw<D, PR, false>()>;
   using PB = Plan<D, KP, PR, cf_nw<D, PR, true>()>;
+  using P0 = Plan<D, KP, PR, cf_nw_first<D, PR>()>;
   static hipError_t prepare() {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_cf_fwd<D, KP, PR>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, PF::TOTAL);
     if (e != hipSuccess) return e;
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_cf_bwd<D, KP, PR>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, PB::TOTAL);
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_cf_bwd<D, KP, PR, true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, PB::TOTAL);
+    if (e != hipSuccess) return e;
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_cf_bwd<D, KP, PR, false>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, P0::TOTAL);
   }
   static size_t image_bytes() { return PF::IMG; }
-  static int workers(int bwd) { return bwd ? PB::NW : PF::NW; }
+  static int workers(int kind) { return kind == 2 ? P0::NW : kind == 1 ? PB::NW : PF::NW; }
   static void fill(int Dr, const float* Wf1, const float* cf1, const float* Wf2, const float* cf2,
                    float rbf_step, float r_cut, unsigned char* out) {
     fill_image<D, KP, PR>(Dr, Wf1, cf1, Wf2, cf2, rbf_step, r_cut, out);
@@ -1162,7 +1188,10 @@ struct CfKernels {
     return hipGetLastError();
   }
   static hipError_t bwd(const CfParams& p, int G, hipStream_t s) {
-    hipLaunchKernelGGL((k_cf_bwd<D, KP, PR>), dim3(G), dim3(PB::NT), PB::TOTAL, s, p);
+    if (p.q_out != nullptr)
+      hipLaunchKernelGGL((k_cf_bwd<D, KP, PR, true>), dim3(G), dim3(PB::NT), PB::TOTAL, s, p);
+    else
+      hipLaunchKernelGGL((k_cf_bwd<D, KP, PR, false>), dim3(G), dim3(P0::NT), P0::TOTAL, s, p);
     return hipGetLastError();
   }
 };
@@ -1182,8 +1211,8 @@ hipError_t cf_prepare(int D, int KP, int prec) {
   return cf_dispatch(D, KP, prec, hipErrorInvalidValue,
                      [](auto k) { return decltype(k)::prepare(); });
 }
-int cf_workers(int D, int KP, int prec, int bwd) {
-  return cf_dispatch(D, KP, prec, 0, [&](auto k) { return decltype(k)::workers(bwd); });
+int cf_workers(int D, int KP, int prec, int kind) {
+  return cf_dispatch(D, KP, prec, 0, [&](auto k) { return decltype(k)::workers(kind); });
 }
 size_t cf_image_bytes(int D, int KP, int prec) {
   return cf_dispatch(D, KP, prec, (size_t)0, [](auto k) { return decltype(k)::image_bytes(); });

@@ -72,7 +72,7 @@ __device__ inline void dev_fail(DevStatus* st, int code, int64_t detail) {
 
 // Offsets (bytes) of everything carved out of a workspace.
 struct WsLayout {
-  size_t status, wg_start, wg_start_b, wg_edge, wg_edge_b, side_h, side_f;
+  size_t status, wg_start, wg_start_b, wg_start_b0, wg_edge, wg_edge_b, wg_edge_b0, side_h, side_f;
   size_t scan_blocks, cell_count, cell_start, cell_atoms, atom_cell;
   size_t x, au, gbuf, tmp, gx, fblk, eps, total;
 };
@@ -137,7 +137,9 @@ struct CfParams {
 // prec: the model's filter_dtype (Prec).
 int cf_kp(int Dr, int prec);               // basis length the LDS images are padded to
 int cf_chunks(int Dr, int prec);           // basis chunks (8 fp32 / 32 16-bit basis functions each)
-int cf_workers(int D, int KP, int prec, int bwd);  // waves (workers) per work-group of a kernel
+// waves (workers) per work-group of a kernel: kind 0 the forward, 1 the
+// backward, 2 the backward of the first block (no source sums)
+int cf_workers(int D, int KP, int prec, int kind);
 hipError_t cf_prepare(int D, int KP, int prec);  // raises the dynamic LDS limit of the kernels
 // Filter-weight image of one interaction block as the CFConv kernels hold it
 // in LDS: cf_image_bytes bytes, filled on the host.
@@ -156,13 +158,15 @@ struct BuildMark {
   const int64_t* gate;
   int64_t gate_val;
 };
-// Both CFConv kernels' worker partitions of the receiver CSR (skipped when
-// rowptr is null), the initial features x = Emb[types] and, with mark, the
-// build mark, in one launch.
+// The CFConv kernels' worker partitions of the receiver CSR (G1 workers of
+// the forward, G2 of the backward, G3 of the first block's backward; skipped
+// when rowptr is null), the initial features x = Emb[types] and, with mark,
+// the build mark, in one launch.
 hipError_t launch_setup(const int32_t* rowptr, int n_atoms, int G1, int32_t* wg_start1,
                         int32_t* wg_edge1, int G2, int32_t* wg_start2, int32_t* wg_edge2,
-                        const int32_t* types, const float* emb, int D, int n_types, float* x,
-                        const BuildMark* mark, DevStatus* st, hipStream_t s);
+                        int G3, int32_t* wg_start3, int32_t* wg_edge3, const int32_t* types,
+                        const float* emb, int D, int n_types, float* x, const BuildMark* mark,
+                        DevStatus* st, hipStream_t s);
 hipError_t launch_cf_forward(int D, int KP, int prec, const CfParams& p, int G, hipStream_t s);
 hipError_t launch_cf_backward(int D, int KP, int prec, const CfParams& p, int G, hipStream_t s);
 
@@ -200,12 +204,13 @@ hipError_t atom_prepare(int D, int H, int prec);   // raises the dynamic LDS lim
 hipError_t launch_atom(const AtomArgs& g, int D, int N1, int prec, int n_cu, hipStream_t s);
 // Per-replica energies (double sums of eps) and F = -(sum over the T blocks
 // of fb), in one launch; with vel, also vel += half_kick F. With side_f,
-// block t's rows of receivers cut by the G workers of its CFConv launch
-// (over the list rowptr) gain their parts side_f[t * side_stride + 3 w].
+// block t's rows of receivers cut by the workers of its CFConv launch (G0
+// for block 0, G for the others, over the list rowptr) gain their parts
+// side_f[t * side_stride + 3 w].
 hipError_t launch_finish(const float* eps, int n_rep, int n_per, float* energy, const float* fb,
                          int T, int64_t n_atoms, float* forces, float* vel, float half_kick,
-                         const int32_t* rowptr, int G, const float* side_f, int64_t side_stride,
-                         DevStatus* st, hipStream_t s);
+                         const int32_t* rowptr, int G0, int G, const float* side_f,
+                         int64_t side_stride, DevStatus* st, hipStream_t s);
 
 // Unfused edge pipeline (unfused.hip): one kernel per step, edge tensors in
 // the workspace, atomic or segmented aggregation.
