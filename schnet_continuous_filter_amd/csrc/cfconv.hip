@@ -358,19 +358,28 @@ __device__ __forceinline__ void gemm1_plain(f32x4 (&acc)[NA][D / 16], const unsi
       // (centres one step apart), and the tangent factor
       // C' - (d - mu_k) C / sigma^2, which grows by step C / sigma^2 per k
       const float z = __builtin_fmaf(-(float)(k0 + CH * c), step, g.d0);
-      float gk = g.in * __builtin_amdgcn_exp2f(coef2 * z * z);
       float q = __builtin_amdgcn_exp2f(__builtin_fmaf(p.rbf_qa, z, p.rbf_qb));
-      float tk = gCp - z * inv_s2 * gC;
-      const float dt = step * inv_s2 * gC;
+      if constexpr (NA == 2) {
+        float gk = g.in * __builtin_amdgcn_exp2f(coef2 * z * z);
+        float tk = gCp - z * inv_s2 * gC;
+        const float dt = step * inv_s2 * gC;
 #pragma unroll
-      for (int t = 0; t < PL; ++t) {
-        b[0][t] = gk * gC;
-        if constexpr (NA == 2) {
+        for (int t = 0; t < PL; ++t) {
+          b[0][t] = gk * gC;
           b[1][t] = gk * tk;
           tk += dt;
+          gk *= q;
+          q *= p.rbf_r;
         }
-        gk *= q;
-        q *= p.rbf_r;
+      } else {
+        // without the tangent the envelope rides along with the Gaussian
+        float gk = g.in * gC * __builtin_amdgcn_exp2f(coef2 * z * z);
+#pragma unroll
+        for (int t = 0; t < PL; ++t) {
+          b[0][t] = gk;
+          gk *= q;
+          q *= p.rbf_r;
+        }
       }
     } else {
 #pragma unroll
