@@ -98,6 +98,12 @@ constexpr bool kBiasInit = PR == PREC_F32 || PR == PREC_BF16;
 // spill and the forward runs no faster, so they request them after it.
 template <int PR>
 constexpr bool kEarlyGather = PR == PREC_BF16 || PR == PREC_F16S;
+// Weight reads of the second product scheduled ahead of their products
+// (pipeline_gemm2_reads) with bf16 filters, where the compiler otherwise
+// makes each product wait on its own read (measured: backward 1-3 % faster;
+// fp32 unchanged).
+template <int PR>
+constexpr bool kPipelineReads = PR == PREC_BF16;
 // A sum over messages (h, q) or a dE/dd leaving the kernel, back in natural units.
 template <int PR>
 __device__ __forceinline__ float out_scale(float v) {
@@ -518,6 +524,24 @@ __device__ __forceinline__ void gemm2_block(f32x4& acc, const Op& op, const unsi
   else gemm_om_block<D, PR>(acc, op, lds + P::W2, nb, wl);
 }
 
+// Schedule of the weight reads of NB output blocks of the second product
+// (each block's bias read first where it starts the accumulator): the reads
+// run LEAD ahead of the products that use them, one read per MFMA_PER_READ
+// products, instead of each product waiting on the read issued just before
+// it. Only the order of the instructions is constrained.
+template <int PR, int NBLK, int K>
+__device__ __forceinline__ void pipeline_gemm2_reads() {
+  constexpr int LEAD = 2;
+  constexpr int READS = PR == PREC_F32 ? NBLK * (K / 16) : NBLK * (K / 32);
+  constexpr int PER = PR == PREC_F32 ? 4 : 1;
+  __builtin_amdgcn_sched_group_barrier(0x100, (kBiasInit<PR> ? NBLK : 0) + LEAD, 0);
+#pragma unroll
+  for (int i = 0; i < READS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+}
+
 // ------------------------------------------------------------------ receiver segments
 // Lane l of a window holds rowptr[cur + 1 + l], the end of receiver cur + l's
 // segment; INT_MAX past the worker's last receiver ib - 1.
@@ -790,6 +814,7 @@ __global__ __launch_bounds__((64 * cf_nw<D, PR, false>()), 1) void k_cf_fwd(CfPa
         w[b] = kBiasInit<PR> ? bias4<P>(p, lds, g4, D + 16 * (4 * pss + b)) : f32x4{};
         gemm2_block<P>(w[b], os, lds, 4 * pss + b, wl);
       }
+      if constexpr (kPipelineReads<PR>) pipeline_gemm2_reads<PR, 4, D>();
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int nb = 4 * pss + b;
@@ -1001,6 +1026,7 @@ __global__ __launch_bounds__((64 * (Q ? cf_nw<D, PR, true>() : cf_nw_first<D, PR
           wv[b] = kBiasInit<PR> ? bias4<P>(p, lds, g4, D + 16 * (4 * (pss + 1) + b)) : f32x4{};
           gemm2_block<P>(wv[b], os, lds, 4 * (pss + 1) + b, wl);
         }
+        if constexpr (kPipelineReads<PR>) pipeline_gemm2_reads<PR, 4, D>();
       }
       if (want_q) {
         wave_sync();
