@@ -411,6 +411,8 @@ bool nbr_geom(const sn_system* sys, float r_list, NbrGeom& g) {
       g.cells_per_axis = nc;
       g.inv_cell = (float)((double)nc / (double)sys->box);
     }
+  } else if (sys->n_replicas == 1 && sys->atoms_per_replica >= kOpenCellMinAtoms) {
+    g.cells_per_axis = -1;   // grid over the bounding box, set on the device
   }
   return true;
 }
@@ -490,6 +492,7 @@ WsLayout ws_layout(int64_t n, int D, int T, int H) {
   L.cell_start = take((size_t)ncell * 4);
   L.cell_atoms = take((size_t)n * 4);
   L.atom_cell = take((size_t)n * 4);
+  L.cell_grid = take(64);
   const size_t ND = (size_t)n * (size_t)D * 4;
   L.x = take((size_t)(T + 1) * ND);
   L.au = take((size_t)T * ND);

@@ -18,6 +18,7 @@ namespace sn {
 constexpr int kThreads = 256;  // every kernel of the library runs 4 wave64 per block
 constexpr int kMaxWorkers = 8192; // upper bound on CFConv workers (partition table size)
 constexpr int kCellsPerAxisMax = 64;
+constexpr int kOpenCellMinAtoms = 8192;   // open single systems this large use a cell list
 constexpr int kScanChunk = 1024; // elements per block of the device scan
 constexpr int kSortRowMax = 1024;
 
@@ -73,7 +74,7 @@ __device__ inline void dev_fail(DevStatus* st, int code, int64_t detail) {
 // Offsets (bytes) of everything carved out of a workspace.
 struct WsLayout {
   size_t status, wg_start, wg_start_b, wg_start_b0, wg_edge, wg_edge_b, wg_edge_b0, side_h, side_f;
-  size_t scan_blocks, cell_count, cell_start, cell_atoms, atom_cell;
+  size_t scan_blocks, cell_count, cell_start, cell_atoms, atom_cell, cell_grid;
   size_t x, au, gbuf, tmp, gx, fblk, eps, total;
 };
 WsLayout ws_layout(int64_t n_atoms, int D, int T, int H);
@@ -84,7 +85,7 @@ struct NbrGeom {
   int n_rep, n_per, periodic;
   float box;
   double L, half, r2;   // IEEE double values used by the exact predicate
-  int cells_per_axis;   // 0 = all-pairs mode
+  int cells_per_axis;   // 0 = all-pairs mode; -1 = cell list over the bounding box (open system)
   float inv_cell;
 };
 hipError_t launch_build_neighbors(const NbrGeom& g, const float* pos, int32_t* rowptr,

@@ -13,8 +13,10 @@
 // Two search modes:
 //  * all pairs inside each replica (chains and small boxes), one wave per
 //    receiver with ballot compaction; senders ascend, so rows come out sorted;
-//  * a cell list for one large periodic cube: cells of edge >= r_list,
-//    27-cell search, then a per-row rank sort in LDS.
+//  * a cell list for one large system: a periodic cube, or an open system
+//    whose bounding box the device finds first; cells of edge >= r_list,
+//    27-cell search (without wrap-around for open systems), then a per-row
+//    rank sort in LDS.
 #include "common.hpp"
 
 namespace sn {
@@ -281,18 +283,93 @@ __device__ __forceinline__ int cell_coord(float x, float inv_cell, int nc) {
   return c < 0 ? 0 : (c >= nc ? nc - 1 : c);
 }
 
+// Cell grid of an open system, found on the device (k_open_grid): cells
+// per axis and, per axis, the lowest coordinate and cells per unit length.
+// The cell-list kernels take either this grid (OPEN) or one periodic cube
+// (nc cells per axis of 1 / inv_cell each, from the origin).
+struct CellGrid {
+  int nx, ny, nz;
+  float lo[3], inv[3];
+  __device__ __forceinline__ int cell_of(float x, float y, float z) const {
+    const int cx = cell_coord(x - lo[0], inv[0], nx);
+    const int cy = cell_coord(y - lo[1], inv[1], ny);
+    const int cz = cell_coord(z - lo[2], inv[2], nz);
+    return (cz * ny + cy) * nx + cx;
+  }
+};
+static_assert(sizeof(CellGrid) <= 64, "the workspace keeps 64 bytes for the grid");
+__device__ __forceinline__ CellGrid cube_grid(float inv_cell, int nc) {
+  CellGrid g;
+  g.nx = g.ny = g.nz = nc;
+  for (int a = 0; a < 3; ++a) {
+    g.lo[a] = 0.f;
+    g.inv[a] = inv_cell;
+  }
+  return g;
+}
+
+// The bounding box of an open system (one work-group; min and max are
+// independent of order) and the grid over it: per axis the largest number of
+// cells, at most kCellsPerAxisMax, whose edge is at least r_list (one cell
+// where the extent is below r_list).
+__global__ __launch_bounds__(1024) void k_open_grid(const float* __restrict__ pos, int N,
+                                                    double r_list, CellGrid* grid,
+                                                    const int64_t* gate, int64_t gate_val) {
+  SN_GATE
+  __shared__ float smin[3][16], smax[3][16];
+  float lo[3] = {INFINITY, INFINITY, INFINITY}, hi[3] = {-INFINITY, -INFINITY, -INFINITY};
+  for (int i = threadIdx.x; i < N; i += 1024)
+    for (int a = 0; a < 3; ++a) {
+      const float v = pos[3 * i + a];
+      lo[a] = fminf(lo[a], v);
+      hi[a] = fmaxf(hi[a], v);
+    }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int a = 0; a < 3; ++a) {
+    for (int o = 32; o > 0; o >>= 1) {
+      lo[a] = fminf(lo[a], __shfl_xor(lo[a], o, 64));
+      hi[a] = fmaxf(hi[a], __shfl_xor(hi[a], o, 64));
+    }
+    if (lane == 0) {
+      smin[a][wave] = lo[a];
+      smax[a][wave] = hi[a];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  CellGrid g;
+  int n[3];
+  for (int a = 0; a < 3; ++a) {
+    float l = smin[a][0], h = smax[a][0];
+    for (int w = 1; w < 16; ++w) {
+      l = fminf(l, smin[a][w]);
+      h = fmaxf(h, smax[a][w]);
+    }
+    const double ext = (double)h - (double)l;
+    double c = ext / (r_list * (1.0 + 1e-5));
+    n[a] = (c >= 1.0 && ext < INFINITY) ? (c >= kCellsPerAxisMax ? kCellsPerAxisMax : (int)c) : 1;
+    g.lo[a] = (ext < INFINITY) ? l : 0.f;
+    g.inv[a] = n[a] > 1 ? (float)((double)n[a] / ext) : 0.f;
+  }
+  g.nx = n[0];
+  g.ny = n[1];
+  g.nz = n[2];
+  *grid = g;
+}
+
+template <bool OPEN>
 __global__ __launch_bounds__(kThreads) void k_cell_assign(const float* __restrict__ pos, int N,
-                                                          float inv_cell, int nc, int32_t* atom_cell,
+                                                          float inv_cell, int nc,
+                                                          const CellGrid* open_grid,
+                                                          int32_t* atom_cell,
                                                           int32_t* cell_count, DevStatus* st,
                                                           const int64_t* gate, int64_t gate_val) {
   SN_GATE
   const int i = blockIdx.x * kThreads + threadIdx.x;
   if (i >= N) return;
   check_position(st, i, pos[3 * i + 0], pos[3 * i + 1], pos[3 * i + 2]);
-  const int cx = cell_coord(pos[3 * i + 0], inv_cell, nc);
-  const int cy = cell_coord(pos[3 * i + 1], inv_cell, nc);
-  const int cz = cell_coord(pos[3 * i + 2], inv_cell, nc);
-  const int c = (cz * nc + cy) * nc + cx;
+  const CellGrid g = OPEN ? *open_grid : cube_grid(inv_cell, nc);
+  const int c = g.cell_of(pos[3 * i + 0], pos[3 * i + 1], pos[3 * i + 2]);
   atom_cell[i] = c;
   atomicAdd(&cell_count[c], 1);
 }
@@ -313,9 +390,12 @@ __global__ __launch_bounds__(kThreads) void k_cell_scatter(int N, const int32_t*
 // one candidate list (cell order, then slot order); lanes take 64 candidates
 // at a time, each finding its cell by a binary search over the cells'
 // offsets, so the loads of a round are independent. Hits are compacted with a
-// ballot; k_sort_rows orders each row afterwards.
-template <bool FILL>
+// ballot; k_sort_rows orders each row afterwards. A periodic cube wraps the
+// neighbouring cells around (27 distinct cells, nc >= 3); an open grid leaves
+// out those past its faces.
+template <bool FILL, bool OPEN>
 __global__ __launch_bounds__(kThreads) void k_nbr_cells(const float* __restrict__ pos, int N, int nc,
+                                                        const CellGrid* open_grid,
                                                         double L, double half, double r2,
                                                         const int32_t* atom_cell,
                                                         const int32_t* cell_start,
@@ -329,14 +409,27 @@ __global__ __launch_bounds__(kThreads) void k_nbr_cells(const float* __restrict_
   if (i >= N) return;
   const float xi = pos[3 * i + 0], yi = pos[3 * i + 1], zi = pos[3 * i + 2];
   const int c = atom_cell[i];
-  const int cx = c % nc, cy = (c / nc) % nc, cz = c / (nc * nc);
-  // lanes 0..26: start and size of one neighbouring cell (27 distinct cells, nc >= 3)
+  const int nx = OPEN ? open_grid->nx : nc, ny = OPEN ? open_grid->ny : nc,
+            nz = OPEN ? open_grid->nz : nc;
+  const int cx = c % nx, cy = (c / nx) % ny, cz = c / (nx * ny);
+  // lanes 0..26: start and size of one neighbouring cell
   int cs = 0, cn = 0;
   if (lane < 27) {
     const int dz = lane / 9 - 1, dy = (lane / 3) % 3 - 1, dx = lane % 3 - 1;
-    const int cc = (((cz + dz + nc) % nc) * nc + (cy + dy + nc) % nc) * nc + (cx + dx + nc) % nc;
-    cs = cell_start[cc];
-    cn = cell_start[cc + 1] - cs;
+    int ax = cx + dx, ay = cy + dy, az = cz + dz;
+    bool ok = true;
+    if (OPEN) {
+      ok = ax >= 0 && ax < nx && ay >= 0 && ay < ny && az >= 0 && az < nz;
+    } else {
+      ax = (ax + nx) % nx;
+      ay = (ay + ny) % ny;
+      az = (az + nz) % nz;
+    }
+    if (ok) {
+      const int cc = (az * ny + ay) * nx + ax;
+      cs = cell_start[cc];
+      cn = cell_start[cc + 1] - cs;
+    }
   }
   int incl = cn;
 #pragma unroll
@@ -363,7 +456,8 @@ __global__ __launch_bounds__(kThreads) void k_nbr_cells(const float* __restrict_
     int j = 0;
     if (f < total) {
       j = cell_atoms[k];
-      in = j != i && pair_in(xi, yi, zi, pos[3 * j], pos[3 * j + 1], pos[3 * j + 2], 1, L, half, r2);
+      in = j != i && pair_in(xi, yi, zi, pos[3 * j], pos[3 * j + 1], pos[3 * j + 2], OPEN ? 0 : 1,
+                             L, half, r2);
     }
     const uint64_t m = __ballot(in);
     if (FILL && in) col[out + __popcll(m & ((1ull << lane) - 1))] = j;
@@ -485,8 +579,13 @@ hipError_t launch_build_neighbors(const NbrGeom& g, const float* pos, int32_t* r
                        g.periodic, g.L, g.half, g.r2, rowptr, col, st, gate, gate_val);
     return hipGetLastError();
   }
-  const int nc = g.cells_per_axis;
-  const int64_t ncell = (int64_t)nc * nc * nc;
+  // a periodic cube of nc^3 cells, or an open grid of up to kCellsPerAxisMax^3
+  // cells whose sizes the device sets (cells past its own count stay empty)
+  const bool open = g.cells_per_axis < 0;
+  const int nc = open ? 0 : g.cells_per_axis;
+  const int64_t ncell = open ? (int64_t)kCellsPerAxisMax * kCellsPerAxisMax * kCellsPerAxisMax
+                             : (int64_t)nc * nc * nc;
+  CellGrid* grid = reinterpret_cast<CellGrid*>(ws + L.cell_grid);
   int32_t* cstart = reinterpret_cast<int32_t*>(ws + L.cell_count);   // counts, then starts
   int32_t* ccur = reinterpret_cast<int32_t*>(ws + L.cell_start);     // scatter cursors
   int32_t* catoms = reinterpret_cast<int32_t*>(ws + L.cell_atoms);
@@ -496,21 +595,40 @@ hipError_t launch_build_neighbors(const NbrGeom& g, const float* pos, int32_t* r
                      ncell + 1, 0, gate, gate_val);
   hipLaunchKernelGGL(k_fill_i32, dim3(blocks_for(ncell)), dim3(kThreads), 0, s, ccur, ncell, 0,
                      gate, gate_val);
-  hipLaunchKernelGGL(k_cell_assign, dim3(blocks_for(N)), dim3(kThreads), 0, s, pos, N, g.inv_cell,
-                     nc, acell, cstart, st, gate, gate_val);
+  if (open) {
+    hipLaunchKernelGGL(k_open_grid, dim3(1), dim3(1024), 0, s, pos, N, std::sqrt(g.r2), grid, gate,
+                       gate_val);
+    hipLaunchKernelGGL(k_cell_assign<true>, dim3(blocks_for(N)), dim3(kThreads), 0, s, pos, N,
+                       0.f, 0, grid, acell, cstart, st, gate, gate_val);
+  } else {
+    hipLaunchKernelGGL(k_cell_assign<false>, dim3(blocks_for(N)), dim3(kThreads), 0, s, pos, N,
+                       g.inv_cell, nc, grid, acell, cstart, st, gate, gate_val);
+  }
   if ((e = launch_exclusive_scan(cstart, ncell, scan_blocks, st, -1, gate, gate_val, s)) !=
       hipSuccess)
     return e;
   hipLaunchKernelGGL(k_cell_scatter, dim3(blocks_for(N)), dim3(kThreads), 0, s, N, acell, cstart,
                      ccur, catoms, gate, gate_val);
   const dim3 wave_grid((unsigned)((N + kThreads / 64 - 1) / (kThreads / 64)));
-  hipLaunchKernelGGL(k_nbr_cells<false>, wave_grid, dim3(kThreads), 0, s, pos, N, nc,
-                     g.L, g.half, g.r2, acell, cstart, catoms, rowptr, col, st, gate, gate_val);
+  if (open)
+    hipLaunchKernelGGL((k_nbr_cells<false, true>), wave_grid, dim3(kThreads), 0, s, pos, N, nc,
+                       grid, g.L, g.half, g.r2, acell, cstart, catoms, rowptr, col, st, gate,
+                       gate_val);
+  else
+    hipLaunchKernelGGL((k_nbr_cells<false, false>), wave_grid, dim3(kThreads), 0, s, pos, N, nc,
+                       grid, g.L, g.half, g.r2, acell, cstart, catoms, rowptr, col, st, gate,
+                       gate_val);
   if ((e = launch_exclusive_scan(rowptr, N, scan_blocks, st, edge_capacity, gate, gate_val, s)) !=
       hipSuccess)
     return e;
-  hipLaunchKernelGGL(k_nbr_cells<true>, wave_grid, dim3(kThreads), 0, s, pos, N, nc, g.L,
-                     g.half, g.r2, acell, cstart, catoms, rowptr, col, st, gate, gate_val);
+  if (open)
+    hipLaunchKernelGGL((k_nbr_cells<true, true>), wave_grid, dim3(kThreads), 0, s, pos, N, nc,
+                       grid, g.L, g.half, g.r2, acell, cstart, catoms, rowptr, col, st, gate,
+                       gate_val);
+  else
+    hipLaunchKernelGGL((k_nbr_cells<true, false>), wave_grid, dim3(kThreads), 0, s, pos, N, nc,
+                       grid, g.L, g.half, g.r2, acell, cstart, catoms, rowptr, col, st, gate,
+                       gate_val);
   hipLaunchKernelGGL(k_sort_rows, dim3((unsigned)((N + 3) / 4)), dim3(kThreads), 0, s, rowptr, col,
                      N, st, gate, gate_val);
   return hipGetLastError();

@@ -125,3 +125,37 @@ def cutout_forces(cfg, pos, types, w, m, centre, radius, inner):
                                  sub_col, n_replicas=1)
     keep = r[sel] < inner
     return sel[keep], Fo[keep]
+
+
+def open_system(shape, seed=5):
+    """One open (non-periodic) system of at least 8192 atoms, the size from
+    which the library builds its list from cells over the bounding box. The
+    density of the bulk workloads (0.0612 per A^3) unless the shape says
+    otherwise; returns float32 positions and the list radius."""
+    rng = np.random.default_rng([seed, 7])
+    rho, r = 0.0612, 5.0
+    if shape == "cube":
+        n = 20000
+        pos = rng.uniform(0.0, (n / rho) ** (1 / 3), (n, 3))
+    elif shape == "ball":           # centred off the origin, negative coordinates too
+        n = 16384
+        v = rng.normal(size=(n, 3))
+        v /= np.linalg.norm(v, axis=1, keepdims=True)
+        R = (3 * n / (4 * np.pi * rho)) ** (1 / 3)
+        pos = v * R * rng.uniform(0.0, 1.0, (n, 1)) ** (1 / 3) - 7.3
+    elif shape == "slab":           # zero thickness: one cell across it
+        n = 10000
+        pos = np.full((n, 3), 3.25)
+        pos[:, :2] = rng.uniform(-200.0, 200.0, (n, 2))
+    elif shape == "outlier":        # one far atom: the cell count capped, cells >> r
+        n = 9001
+        pos = rng.uniform(0.0, ((n - 1) / rho) ** (1 / 3), (n, 3))
+        pos[-1] = (1.0e4, -1.0e4, 5.0e3)
+    elif shape == "lattice":        # spacings within an ulp or two of the radius, and at it
+        inside = float(np.nextafter(np.float32(r), np.float32(0)))
+        i, j, k = np.meshgrid(np.arange(32), np.arange(16), np.arange(16), indexing="ij")
+        pos = np.stack([i * np.float32(inside), j * np.float32(r), k * np.float32(1.5 * r)],
+                       axis=-1).reshape(-1, 3)
+    else:
+        raise ValueError(shape)
+    return np.ascontiguousarray(pos, dtype=np.float32), r

@@ -103,6 +103,21 @@ def test_small_periodic_box_ragged(gpu_lib):
     check(gpu_lib, c2, pos, types, w, what="box389")
 
 
+def test_open_cluster_cell_list(gpu_lib):
+    """Energies and forces of a large open cluster (a ball of 16,384 atoms at
+    the bulk density, the bulk model with biases), whose list the library
+    builds from cells over the bounding box, against the oracle."""
+    from gen.configs import Config, SystemSpec
+    from tests.gpu_helpers import open_system
+    cfg = CONFIGS["bulk4k"]
+    pos, r = open_system("ball", seed=9)
+    n = len(pos)
+    types = np.random.default_rng(12).integers(0, 4, n).astype(np.int32)
+    w = make_weights(cfg.model, 6, bias_scale=0.05)
+    c2 = Config("ball16k", SystemSpec("bulk", 1, n, False, 0.0), cfg.model)
+    check(gpu_lib, c2, pos, types, w, r_list=cfg.model.r_cut, what="open ball")
+
+
 def sparse_clusters(n_iso=100, seed=11):
     """Clusters of 10 atoms (index-contiguous, 4 A apart on a helix) separated
     in index order by runs of isolated atoms 50 A apart: one 16-edge tile

@@ -4,7 +4,7 @@ import pytest
 
 import oracle
 from gen.configs import CONFIGS, make_config
-from tests.gpu_helpers import gpu_neighbors, lib_system
+from tests.gpu_helpers import gpu_neighbors, lib_system, open_system
 
 pytestmark = pytest.mark.gpu
 
@@ -58,6 +58,17 @@ def test_pairs_at_the_radius(gpu_lib):
                     [40, 0, 0], [40 + outside, 0, 0], [60, 60, 60]], dtype=np.float32)
     ne = _compare(gpu_lib, gpu_lib.make_system(1, 7, False, 0.0), pos, float(r))
     assert ne == 2
+
+
+@pytest.mark.parametrize("shape", ["cube", "ball", "slab", "outlier", "lattice"])
+def test_open_system_cell_list_exact(gpu_lib, shape):
+    """A large open system takes the cell list over its bounding box (the
+    grid set on the device, no wrap-around at its faces); the list must
+    equal the oracle's bit for bit."""
+    pos, r = open_system(shape)
+    ne = _compare(gpu_lib, gpu_lib.make_system(1, len(pos), False, 0.0), pos, r)
+    print(f"open {shape}: {len(pos)} atoms, {ne} directed edges")
+    assert ne > 0
 
 
 def test_isolated_atoms_give_empty_rows(gpu_lib):
