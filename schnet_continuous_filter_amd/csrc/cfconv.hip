@@ -157,10 +157,10 @@ constexpr int cf_nw() {
   return BWD ? 8 : 16;
 }
 // The first block's backward (no source sums) fits 168 registers: three waves
-// per SIMD, but for the fp16 pairs (which would spill there).
+// per SIMD.
 template <int D, int PR>
 constexpr int cf_nw_first() {
-  return PR == PREC_F16X2 ? 8 : 12;
+  return 12;
 }
 
 int cf_kp(int Dr, int prec) {
@@ -909,7 +909,9 @@ __global__ __launch_bounds__((64 * (Q ? cf_nw<D, PR, true>() : cf_nw_first<D, PR
                                    : kMaskedRow;
     const uint32_t io = g.in > 0.f ? ((uint32_t)th.recv * (uint32_t)D + (uint32_t)g4) * 4u
                                    : kMaskedRow;
-    f32x4 G[4][4];
+    // fp16 pairs hold two blocks' gathers, refilled two blocks ahead
+    constexpr int GD = PR == PREC_F16X2 ? 2 : 4;
+    f32x4 G[GD][4];
     auto gather = [&](int nb, f32x4 (&Gb)[4]) {
       const uint32_t co = (uint32_t)(64 * nb);
       Gb[0] = bload4(rx, jo + co);
@@ -961,7 +963,7 @@ __global__ __launch_bounds__((64 * (Q ? cf_nw<D, PR, true>() : cf_nw_first<D, PR
 
     if constexpr (!(kEarlyGather<PR> && Q)) {
 #pragma unroll
-      for (int b = 0; b < 4; ++b) gather(b, G[b]);
+      for (int b = 0; b < GD; ++b) gather(b, G[b]);
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -969,8 +971,29 @@ __global__ __launch_bounds__((64 * (Q ? cf_nw<D, PR, true>() : cf_nw_first<D, PR
     // of the first 64 features, as independent product chains; the values of
     // each further 64 features are formed once the previous ones are used
     const auto os = W2Op<D, PR>::make(av[0], ss.a[2]);   // unused (and dropped) without Q
-    f32x4 wt[NB], wv[4];
-    {
+    // fp16 pairs: the values of all features are formed here, so that the
+    // split operand (twice the registers of a 16-bit one) dies before the
+    // messages; otherwise the values of each further 64 features are formed
+    // once the previous ones are used
+    constexpr bool VF = PR == PREC_F16X2;
+    f32x4 wt[NB], wv[VF ? NB : 4];
+    if constexpr (VF) {
+      // values first, then tangents: one split operand live at a time
+      if (Q) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          wv[nb] = f32x4{};
+          gemm2_block<P>(wv[nb], os, lds, nb, wl);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const auto ot = W2Op<D, PR>::make(av[1], ss.a[3]);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        wt[nb] = f32x4{};
+        gemm2_block<P>(wt[nb], ot, lds, nb, wl);
+      }
+    } else {
       const auto ot = W2Op<D, PR>::make(av[1], ss.a[3]);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
@@ -992,13 +1015,14 @@ __global__ __launch_bounds__((64 * (Q ? cf_nw<D, PR, true>() : cf_nw_first<D, PR
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int nb = 4 * pss + b;
-        const f32x4 xj = G[b][0], gj = G[b][1], xi = G[b][2], gi = G[b][3];
+        const int gs = nb % GD;   // this block's gather slot
+        const f32x4 xj = G[gs][0], gj = G[gs][1], xi = G[gs][2], gi = G[gs][3];
         if constexpr (PR == PREC_F16S) {
           const f32x4 s2 = scale4<P>(p, lds, g4, D + 16 * nb);
           if constexpr (Q) {
             const f32x4 c2 = bias4<P>(p, lds, g4, D + 16 * nb);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) wv[b][r] = fmaf(wv[b][r], s2[r], c2[r]);
+            for (int r = 0; r < 4; ++r) wv[VF ? nb : b][r] = fmaf(wv[VF ? nb : b][r], s2[r], c2[r]);
           }
           wt[nb] *= s2;
         }
@@ -1006,20 +1030,20 @@ __global__ __launch_bounds__((64 * (Q ? cf_nw<D, PR, true>() : cf_nw_first<D, PR
           if constexpr (Q) {
             const f32x4 c2 = bias4<P>(p, lds, g4, D + 16 * nb);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) wv[b][r] = fmaf(wv[b][r], ss.u[2], c2[r]);
+            for (int r = 0; r < 4; ++r) wv[VF ? nb : b][r] = fmaf(wv[VF ? nb : b][r], ss.u[2], c2[r]);
           }
           wt[nb] *= ss.u[3];
         }
         f32x4 qv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          if constexpr (Q) qv[r] = gj[r] * wv[b][r];
+          if constexpr (Q) qv[r] = gj[r] * wv[VF ? nb : b][r];
           gdd = fmaf(gi[r] * xj[r] + gj[r] * xi[r], wt[nb][r], gdd);
         }
         if (want_q) tile_put(Tb, b, qv, tl);
-        if (pss + 1 < NB / 4) gather(nb + 4, G[b]);
+        if (nb + GD < NB) gather(nb + GD, G[gs]);
       }
-      if (Q && pss + 1 < NB / 4) {
+      if (Q && !VF && pss + 1 < NB / 4) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
