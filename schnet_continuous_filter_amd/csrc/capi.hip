@@ -159,7 +159,7 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
                              float* energy, float* forces, char* ws, hipStream_t s,
                              const UfMode* uf = nullptr, float* vel_kick = nullptr,
                              float half_kick = 0.f, const BuildMark* mark = nullptr,
-                             bool profile = true) {
+                             bool profile = true, bool x0_ready = false) {
   const sn_model_desc& d = m->desc;
   const int64_t n = n_atoms(sys);
   const int D = d.D, T = d.T, H = d.H;
@@ -187,9 +187,11 @@ sn_status energy_forces_impl(const sn_model* m, const sn_system* sys, const floa
   const int Gf = cf_grid(m, n, wf), Gb = cf_grid(m, n, wb), Gb0 = cf_grid(m, n, wb0);
   hipError_t e;
 
+  // x0_ready: the workspace already holds x0 = Emb[types] for these types
   if ((e = launch_setup(uf ? nullptr : rowptr, (int)n, Gf * wf, wg_start, wg_edge, Gb * wb,
                         wg_start_b, wg_edge_b, Gb0 * wb0, wg_start_b0, wg_edge_b0, types,
-                        m->w + m->off_emb, D, d.n_types, x, mark, st, s)) != hipSuccess)
+                        m->w + m->off_emb, D, d.n_types, x0_ready ? nullptr : x, mark, st,
+                        s)) != hipSuccess)
     return hip_fail(e);
 
   CfParams p{};
@@ -800,8 +802,11 @@ sn_status sn_md_step(const sn_model* m, const sn_system* sys, const int32_t* typ
     // the build mark (when this step rebuilt) runs in the evaluation's set-up
     // launch, the closing half-kick B in the launch that sums the forces
     const BuildMark mark{state->pos, state->pos_at_build, gate, gval};
+    // the types do not change inside the call: from its second step on, the
+    // initial features x0 = Emb[types] in the workspace are still those of
+    // the first
     rc = energy_forces_impl(m, sys, state->pos, types, rp, cl, e_out, state->forces, w, s, nullptr,
-                            state->vel, su.c.half_kick, &mark);
+                            state->vel, su.c.half_kick, &mark, true, k > 0);
     if (rc != SN_OK) return rc;
     state->step = step + 1;
   }

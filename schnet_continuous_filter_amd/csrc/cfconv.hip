@@ -1208,7 +1208,7 @@ hipError_t launch_setup(const int32_t* rowptr, int n_atoms, int G1, int32_t* wg_
                         DevStatus* st, hipStream_t s) {
   const int nbp = rowptr ? (G1 + 1 + G2 + 1 + G3 + 1 + kThreads - 1) / kThreads : 0;
   const int log2D = D == 128 ? 7 : 6;
-  const int64_t n4 = (int64_t)n_atoms * D / 4;
+  const int64_t n4 = x ? (int64_t)n_atoms * D / 4 : 0;   // no x: the features are kept
   const int nbe = (int)((n4 + kThreads - 1) / kThreads);
   const int nbm = mark ? std::max(1, (int)((3 * (int64_t)n_atoms + kThreads - 1) / kThreads)) : 0;
   const int64_t nb = (int64_t)nbp + nbe + nbm;

@@ -162,7 +162,7 @@ struct BuildMark {
 // The CFConv kernels' worker partitions of the receiver CSR (G1 workers of
 // the forward, G2 of the backward, G3 of the first block's backward; skipped
 // when rowptr is null), the initial features x = Emb[types] and, with mark,
-// the build mark, in one launch.
+// the build mark, in one launch (x null: the features are left as they are).
 hipError_t launch_setup(const int32_t* rowptr, int n_atoms, int G1, int32_t* wg_start1,
                         int32_t* wg_edge1, int G2, int32_t* wg_start2, int32_t* wg_edge2,
                         int G3, int32_t* wg_start3, int32_t* wg_edge3, const int32_t* types,
