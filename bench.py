@@ -52,13 +52,21 @@ def counter_record(kind, workload, m):
         if not os.path.exists(path):
             continue
         rec = json.load(open(path))
-        kern = rec.get("kernel", "")   # "void sn::k_cf_bwd<D, KP, precision>(sn::CfParams)"
         if (rec.get("kernel_hash") == profiling.kernel_hash()
-                and kern.startswith(f"void sn::k_cf_{kind}<{m.D}, ")
-                and f", {m.filter_dtype}>(" in kern
+                and kernel_args(rec.get("kernel", ""), kind)[:3:2] == [str(m.D), str(m.filter_dtype)]
                 and rec.get("workload", "").split("_")[0] == workload):
             return rec
     return None
+
+
+def kernel_args(name, kind):
+    """Template arguments of a CFConv kernel name as rocprofv3 reports it,
+    "void sn::k_cf_bwd<D, KP, precision, q>(sn::CfParams)" (the forward has
+    no q), as strings; [] for another kernel."""
+    head = f"void sn::k_cf_{kind}<"
+    if not name.startswith(head) or ">(" not in name:
+        return []
+    return [a.strip() for a in name[len(head):name.index(">(")].split(",")]
 
 
 def utilisation_record(kind, workload, m):
