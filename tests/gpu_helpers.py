@@ -8,13 +8,18 @@ from gen.configs import CONFIGS, make_config
 
 # Parity bars: energy within 1e-5 relative; forces within 1e-4 (max abs) of the
 # oracle's force RMS, for fp32 filters. bf16 filters: the oracle uses the same
-# bf16-rounded weights but exact activations (every activation entering a
-# filter product is rounded to 8 significant bits on the GPU), so the bars
-# widen; they are set at about twice the largest errors measured over the
-# parity cases on MI355X (energy 1.3e-4 relative, forces 9.5e-3 max and
-# 2.6e-3 RMS of the force RMS).
+# bf16-rounded weights but exact activations, while the path rounds four
+# filter activations per edge to 8 significant bits, so the bars are the
+# 16-bit ones that rounding allows: a replica's energy within 1e-3 of
+# sum_i |eps_i| (each atom's rounding error does not cancel when the energies
+# do), forces within 5e-2 max and 5e-3 RMS of the force RMS. The same
+# rounding applied to the oracle's arithmetic, at nine scales across a
+# binade, reaches 4.4e-4, 2.9e-2 and 2.9e-3 on one- and five-block models
+# (test_bf16_bars); the path itself measured 2.3e-4, 2.3e-2 and 2.7e-3 there. The path's own
+# rounding is checked far more tightly against tests.bf16_model
+# (test_gpu_bf16_rounding).
 E_TOL_F32, F_TOL_F32 = 1e-5, 1e-4
-E_TOL_BF16, F_TOL_BF16, F_RMS_TOL_BF16 = 3e-4, 2e-2, 5e-3
+E_TOL_BF16_ABS_SUM, F_TOL_BF16, F_RMS_TOL_BF16 = 1e-3, 5e-2, 5e-3
 # fp16 operands in every MLP (W16A16): every activation entering a product is
 # rounded to 11 significant bits, so a replica's energy error grows with the
 # per-atom energies it sums, not with their (possibly cancelling) total: the
@@ -65,31 +70,31 @@ def oracle_list(system, pos_np, r_list, rp_gpu, col_gpu, what=""):
     return rp, col
 
 
-def assert_energy_forces(E_gpu, F_gpu, E_ref, F_ref, bf16=False, what="", eps_abs_sum=None):
-    """bf16: the 16-bit bars; with eps_abs_sum (per replica sum of |eps_i|
-    from the oracle) the energy bar is the W16A16 one."""
+def assert_energy_forces(E_gpu, F_gpu, E_ref, F_ref, bf16=False, what="", eps_abs_sum=None,
+                         w16=False):
+    """bf16: the 16-bit bars (w16: the tighter W16A16 ones); their energy
+    bar needs eps_abs_sum, the oracle's per-replica sum of |eps_i|."""
     E_gpu = np.asarray(E_gpu, dtype=np.float64)
     F_gpu = np.asarray(F_gpu, dtype=np.float64).reshape(-1, 3)
     rel = np.abs(E_gpu - E_ref) / np.maximum(np.abs(E_ref), 1e-30)
-    if eps_abs_sum is not None:
-        bound = E_TOL_W16_ABS_SUM * np.asarray(eps_abs_sum, dtype=np.float64)
-        err = np.abs(E_gpu - E_ref)
-        assert np.all(err <= bound), \
-            f"{what} energy err {np.max(err / bound) * E_TOL_W16_ABS_SUM:.3e} of sum|eps|"
+    if bf16:
+        assert eps_abs_sum is not None, "16-bit energy bars are taken against sum |eps_i|"
+        e_tol = E_TOL_W16_ABS_SUM if w16 else E_TOL_BF16_ABS_SUM
+        err = np.abs(E_gpu - E_ref) / np.asarray(eps_abs_sum, dtype=np.float64)
+        assert np.all(err <= e_tol), f"{what} energy err {err.max():.3e} of sum|eps| > {e_tol}"
     else:
-        e_tol = E_TOL_BF16 if bf16 else E_TOL_F32
-        assert np.all(rel <= e_tol), f"{what} energy rel err {rel.max():.3e} > {e_tol}"
+        assert np.all(rel <= E_TOL_F32), f"{what} energy rel err {rel.max():.3e} > {E_TOL_F32}"
     rms = np.sqrt(np.mean(F_ref ** 2))
     err = np.abs(F_gpu - F_ref)
     if rms == 0.0:            # no forces at all (isolated atoms): demand exact zeros
         assert err.max() == 0.0, f"{what} forces should vanish"
         return rel.max(), 0.0
-    f_tol = (F_TOL_W16 if eps_abs_sum is not None else F_TOL_BF16) if bf16 else F_TOL_F32
+    f_tol = (F_TOL_W16 if w16 else F_TOL_BF16) if bf16 else F_TOL_F32
     assert err.max() <= f_tol * rms, f"{what} force max err {err.max() / rms:.3e} x rms > {f_tol}"
     if bf16:
         e_rms = np.sqrt(np.mean(err ** 2)) / rms
         print(f"{what}: F err rms/rms {e_rms:.2e}")
-        assert e_rms <= (F_RMS_TOL_W16 if eps_abs_sum is not None else F_RMS_TOL_BF16)
+        assert e_rms <= (F_RMS_TOL_W16 if w16 else F_RMS_TOL_BF16)
     return rel.max(), err.max() / rms
 
 

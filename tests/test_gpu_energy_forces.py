@@ -42,10 +42,10 @@ def check(lib, cfg, pos, types, w, r_list=None, n_replicas=None, what=""):
                                        n_replicas=system.n_replicas,
                                        periodic=bool(system.periodic), box=system.box,
                                        return_eps=True)
-    eps_sum = np.abs(eps).reshape(system.n_replicas, -1).sum(axis=1) if m.filter_dtype == 2 else None
+    eps_sum = np.abs(eps).reshape(system.n_replicas, -1).sum(axis=1)
     re, rf = assert_energy_forces(E, F, Eo, Fo, bf16=m.filter_dtype in (1, 2), what=what,
-                                  eps_abs_sum=eps_sum)
-    if eps_sum is not None:
+                                  eps_abs_sum=eps_sum, w16=m.filter_dtype == 2)
+    if m.filter_dtype in (1, 2):
         print(f"{what}: E err / sum|eps| {np.max(np.abs(E - Eo) / eps_sum):.2e}")
     print(f"{what}: E rel {re:.2e}, F max/rms {rf:.2e}, edges {len(col)}")
     return E, F
@@ -67,6 +67,22 @@ def test_cg32_with_biases_and_skin_list(gpu_lib):
 def test_cg269_four_replicas(gpu_lib):
     cfg, pos, types, w = make_config("cg269x64", n_replicas=4, bias_scale=0.05)
     check(gpu_lib, cfg, pos, types, w, n_replicas=4, what="cg269x4")
+
+
+@pytest.mark.parametrize("T", [1, 5])
+@pytest.mark.parametrize("dtype", [0, 1])
+def test_interaction_block_counts(gpu_lib, T, dtype):
+    """One interaction block (only the first block's backward kernel, on its
+    own worker partition, and the force sum over one block) and five (three
+    blocks with source sums between the first and the last), at fp32 and with
+    a bf16 filter, on four 269-bead chains with biases."""
+    import dataclasses
+    from gen.configs import Config
+    cfg, pos, types, _ = make_config("cg269x64", n_replicas=4)
+    m = dataclasses.replace(cfg.model, T=T, filter_dtype=dtype)
+    w = make_weights(m, 4, bias_scale=0.05)
+    c2 = Config(f"chains-T{T}", cfg.system, m)
+    check(gpu_lib, c2, pos, types, w, n_replicas=4, what=f"T={T} dtype={dtype}")
 
 
 def test_cg269x64_full(gpu_lib):
@@ -255,9 +271,10 @@ def test_md1024_full_sampled_replicas(gpu_lib):
     for r in (0, 377, 1023):
         sl = slice(r * n, (r + 1) * n)
         rp, col = oracle.neighbor_list(pos[sl], 1, n, False, 0.0, m.r_cut)
-        Eo, Fo = oracle.energy_forces(oracle_desc(m), w, pos[sl], types[sl], rp, col,
-                                      n_replicas=1, periodic=False, box=0.0)
-        re, rf = assert_energy_forces(E[r:r + 1], F[sl], Eo, Fo, bf16=True, what=f"md1024 r{r}")
+        Eo, Fo, eps = oracle.energy_forces(oracle_desc(m), w, pos[sl], types[sl], rp, col,
+                                           n_replicas=1, periodic=False, box=0.0, return_eps=True)
+        re, rf = assert_energy_forces(E[r:r + 1], F[sl], Eo, Fo, bf16=True, what=f"md1024 r{r}",
+                                      eps_abs_sum=[np.abs(eps).sum()])
         print(f"md1024 replica {r}: E rel {re:.2e}, F max/rms {rf:.2e}")
 
 
@@ -328,7 +345,7 @@ def test_bulk64k_full_vs_oracle(gpu_lib):
     import dataclasses
     import json
     import os
-    from tests.gpu_helpers import E_TOL_BF16, E_TOL_F32, E_TOL_W16_ABS_SUM
+    from tests.gpu_helpers import E_TOL_BF16_ABS_SUM, E_TOL_F32, E_TOL_W16_ABS_SUM
     gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
                                        "bulk64k_oracle.json")))
     cfg, pos, types, w = make_config("bulk64k")
@@ -344,12 +361,12 @@ def test_bulk64k_full_vs_oracle(gpu_lib):
         Fo = np.asarray(gold["forces"][ref]["F"])
         rms = np.sqrt(np.mean(Fo ** 2))
         ferr = np.max(np.abs(F[atoms] - Fo)) / rms
-        if dtype == 2:
+        if dtype in (1, 2):
             eerr = abs(E[0] - Eo) / gold["energy"][ref]["sum_abs_eps"]
-            ebar = E_TOL_W16_ABS_SUM
+            ebar = E_TOL_W16_ABS_SUM if dtype == 2 else E_TOL_BF16_ABS_SUM
         else:
             eerr = abs(E[0] - Eo) / abs(Eo)
-            ebar = E_TOL_F32 if dtype in (0, 3) else E_TOL_BF16
+            ebar = E_TOL_F32
         print(f"bulk64k dtype {dtype}: E {E[0]:.6f} vs {Eo:.6f} (err {eerr:.2e}), "
               f"{len(atoms)} atoms F max/rms {ferr:.2e}")
         assert eerr <= ebar
@@ -476,9 +493,10 @@ def test_largest_admitted_system(gpu_lib):
         for r in (0, 7777, R - 1):
             sl = slice(r * N, (r + 1) * N)
             rp, cl = oracle.neighbor_list(pos[sl], 1, N, False, 0.0, m.r_cut)
-            Eo, Fo = oracle.energy_forces(oracle_desc(m), w, pos[sl], types[sl], rp, cl,
-                                          n_replicas=1)
+            Eo, Fo, eps = oracle.energy_forces(oracle_desc(m), w, pos[sl], types[sl], rp, cl,
+                                               n_replicas=1, return_eps=True)
             re, rf = assert_energy_forces(E[r:r + 1], F[sl], Eo, Fo, bf16=dtype == 1,
-                                          what=f"max size r{r} dtype {dtype}")
+                                          what=f"max size r{r} dtype {dtype}",
+                                          eps_abs_sum=[np.abs(eps).sum()])
             print(f"largest batch, dtype {dtype}, replica {r}: {len(col)} edges in all, "
                   f"E rel {re:.2e}, F max/rms {rf:.2e}")

@@ -41,10 +41,12 @@ def check(lib, cfg, pos, types, w, mode, r_list=None, n_replicas=None, what=""):
     E, F, rp_gpu, col_gpu, status = run_unfused(lib, m, system, pos, types, w, r_list, MODES[mode])
     assert status[0] == 0, f"device status {status}"
     rp, col = oracle_list(system, pos, r_list, rp_gpu, col_gpu, what)
-    Eo, Fo = oracle.energy_forces(oracle_desc(m), w, pos, types, rp, col,
-                                  n_replicas=system.n_replicas, periodic=bool(system.periodic),
-                                  box=system.box)
-    re, rf = assert_energy_forces(E, F, Eo, Fo, bf16=m.filter_dtype in (1, 2), what=f"{what} {mode}")
+    Eo, Fo, eps = oracle.energy_forces(oracle_desc(m), w, pos, types, rp, col,
+                                       n_replicas=system.n_replicas,
+                                       periodic=bool(system.periodic), box=system.box,
+                                       return_eps=True)
+    re, rf = assert_energy_forces(E, F, Eo, Fo, bf16=m.filter_dtype in (1, 2), what=f"{what} {mode}",
+                                  eps_abs_sum=np.abs(eps).reshape(system.n_replicas, -1).sum(axis=1))
     print(f"{what} {mode}: E rel {re:.2e}, F max/rms {rf:.2e}, edges {len(col)}")
     return E, F
 

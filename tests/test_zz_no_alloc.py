@@ -43,10 +43,13 @@ def _both(lib, cfg, pos, types, w):
         E = e_na.cpu().double().numpy()
         F = f_na.cpu().double().numpy().reshape(-1, 3)
         rp, cl = oracle_list(system, pos, m.r_cut, rowptr.cpu().numpy(), col[:ne].cpu().numpy())
-        Eo, Fo = oracle.energy_forces(oracle_desc(m), w, pos, types, rp, cl,
-                                      n_replicas=system.n_replicas,
-                                      periodic=bool(system.periodic), box=system.box)
-        assert_energy_forces(E, F, Eo, Fo, bf16=m.filter_dtype in (1, 2))
+        Eo, Fo, eps = oracle.energy_forces(oracle_desc(m), w, pos, types, rp, cl,
+                                           n_replicas=system.n_replicas,
+                                           periodic=bool(system.periodic), box=system.box,
+                                           return_eps=True)
+        assert_energy_forces(E, F, Eo, Fo, bf16=m.filter_dtype in (1, 2),
+                             eps_abs_sum=np.abs(eps).reshape(system.n_replicas, -1).sum(axis=1),
+                             w16=m.filter_dtype == 2)
     finally:
         lib.sn_model_destroy(model)
 
