@@ -70,12 +70,13 @@ def test_cg269_four_replicas(gpu_lib):
 
 
 @pytest.mark.parametrize("T", [1, 5])
-@pytest.mark.parametrize("dtype", [0, 1])
+@pytest.mark.parametrize("dtype", [0, 1, 2, 3])
 def test_interaction_block_counts(gpu_lib, T, dtype):
     """One interaction block (only the first block's backward kernel, on its
     own worker partition, and the force sum over one block) and five (three
-    blocks with source sums between the first and the last), at fp32 and with
-    a bf16 filter, on four 269-bead chains with biases."""
+    blocks with source sums between the first and the last), at fp32, with a
+    bf16 filter, W16A16 and fp32 on fp16 pairs, on four 269-bead chains with
+    biases."""
     import dataclasses
     from gen.configs import Config
     cfg, pos, types, _ = make_config("cg269x64", n_replicas=4)
