@@ -658,6 +658,13 @@ def main():
             e = ef_timing(sub)
             e.pop("ms_per_ef_runs")
             line["energy_forces"][sub] = e
+        # the same fp32 models with their filter and atom-wise products on
+        # fp16 hi/lo pairs (fp32-grade: held to the fp32 parity bars)
+        line["energy_forces_f16x2"] = {}
+        for sub in subs:
+            e = ef_timing(sub, "f16x2")
+            e.pop("ms_per_ef_runs")
+            line["energy_forces_f16x2"][sub] = e
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(subs, args.cpu_full)
     print(json.dumps(line))
