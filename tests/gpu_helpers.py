@@ -15,17 +15,19 @@ from gen.configs import CONFIGS, make_config
 # do), forces within 5e-2 max and 5e-3 RMS of the force RMS. The same
 # rounding applied to the oracle's arithmetic, at nine scales across a
 # binade, reaches 4.4e-4, 2.9e-2 and 2.9e-3 on one- and five-block models
-# (test_bf16_bars); the path itself measured 2.3e-4, 2.3e-2 and 2.7e-3 there. The path's own
-# rounding is checked far more tightly against tests.bf16_model
-# (test_gpu_bf16_rounding).
+# (test_16bit_bars); the path itself measured 2.3e-4, 2.3e-2 and 2.7e-3 there. The path's own
+# rounding is checked far more tightly against tests.rounding_model
+# (test_gpu_rounding_model).
 E_TOL_F32, F_TOL_F32 = 1e-5, 1e-4
 E_TOL_BF16_ABS_SUM, F_TOL_BF16, F_RMS_TOL_BF16 = 1e-3, 5e-2, 5e-3
 # fp16 operands in every MLP (W16A16): every activation entering a product is
 # rounded to 11 significant bits, so a replica's energy error grows with the
 # per-atom energies it sums, not with their (possibly cancelling) total: the
 # energy bar is taken relative to sum_i |eps_i|. Bars at about twice the
-# largest measured errors (1.6e-4 of sum |eps_i|, forces 3.2e-3 max and
-# 4.8e-4 RMS of the force RMS).
+# largest measured errors (1.6e-4 of sum |eps_i|, forces 3.6e-3 max and
+# 4.9e-4 RMS of the force RMS); the same rounding applied to the oracle's
+# arithmetic at nine scales reaches 9.0e-5, 5.2e-3 and 5.7e-4 on one- and
+# five-block chain models (test_16bit_bars).
 E_TOL_W16_ABS_SUM = 3.5e-4
 F_TOL_W16, F_RMS_TOL_W16 = 7e-3, 1e-3
 

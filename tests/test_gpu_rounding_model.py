@@ -1,11 +1,17 @@
 """The bf16 filter path against a CPU model of its own rounding, through the C ABI.
 
 Against the exact-activation oracle the bf16 path is only held to the bars
-that bf16 rounding allows. The model in tests.bf16_model rounds the same four
-activations at the same points and in the same units as the path, so what is
-left between the two is fp32 arithmetic (summation order, the hardware's exp2
-and log2) and the rare activation whose rounding that arithmetic tips across a
-tie: the bars here are fp32-grade, far inside the bf16 ones.
+that bf16 rounding allows. The model in tests.rounding_model rounds the same
+four activations at the same points and in the same units as the path, so
+what is left between the two is fp32 arithmetic (summation order, the
+hardware's exp2 and log2) and the rare activation whose rounding that
+arithmetic tips across a tie: the bars here are fp32-grade, far inside the
+bf16 ones. The bf16 path rounds only functions of the pair distance, which
+both sides compute from the same fp32 positions, so such a tie changes one
+value and nothing downstream. W16A16 also rounds the features and their
+gradients: one tie decided differently there shifts later blocks' inputs by
+more than fp32 noise and tips further ties, so that path matches the model
+in distribution (tests/test_16bit_bars.py) but not element by element.
 """
 import dataclasses
 
@@ -13,7 +19,7 @@ import numpy as np
 import pytest
 
 from gen.configs import CONFIGS, Config, SystemSpec, make_config, make_weights
-from tests.bf16_model import rounded_energy_forces
+from tests.rounding_model import rounded_energy_forces
 from tests.gpu_helpers import lib_system, oracle_desc, oracle_list
 from tests.test_gpu_energy_forces import run_gpu
 
