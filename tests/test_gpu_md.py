@@ -25,7 +25,7 @@ def test_philox_words_exact(gpu_lib):
 
 
 def _md_setup(lib, name, R, seed=0, gamma=1.0, skin=1.0, rebuild_every=10, filter_f32=True,
-              dtype=None, active=True):
+              dtype=None, active=True, T=None):
     import torch
     from dataclasses import replace
     cfg, pos, types, w = make_config(name, seed=seed, n_replicas=R)
@@ -34,6 +34,9 @@ def _md_setup(lib, name, R, seed=0, gamma=1.0, skin=1.0, rebuild_every=10, filte
         m = replace(m, filter_dtype=0)
     if dtype is not None:
         m = replace(m, filter_dtype=dtype)
+    if T is not None:   # another block count: weights of that shape (no biases, so that
+        m = replace(m, T=T)   # the energy stays continuous where edges cross the cutoff)
+        w = make_weights(m, seed + 7)
     desc = lib_desc(lib, m)
     system = lib_system(lib, cfg.system, R)
     model = lib.sn_model_create(desc, w)
@@ -46,14 +49,15 @@ def _md_setup(lib, name, R, seed=0, gamma=1.0, skin=1.0, rebuild_every=10, filte
     return cfg, m, pos, types, w, desc, system, model, ws, t, params, state, energy
 
 
-@pytest.mark.parametrize("dtype", [0, 3])
-def test_short_trajectory_matches_oracle(gpu_lib, dtype):
+@pytest.mark.parametrize("dtype,T", [(0, None), (3, None), (0, 1), (0, 5)])
+def test_short_trajectory_matches_oracle(gpu_lib, dtype, T):
     """Ten BAOAB steps of 3 chain replicas with the same Philox stream: the
-    GPU (fp32, or the fp32 model on fp16 pairs) and the oracle (fp64)
-    trajectories agree to fp32 accuracy."""
+    GPU (fp32, or the fp32 model on fp16 pairs; the chain model's three
+    interaction blocks, or one or five) and the oracle (fp64) trajectories
+    agree to fp32 accuracy."""
     lib = gpu_lib
     cfg, m, pos, types, w, desc, system, model, ws, t, params, state, energy = _md_setup(
-        lib, "cg269x64", 3, dtype=dtype)
+        lib, "cg269x64", 3, dtype=dtype, T=T)
     try:
         lib.sn_md_init(model, system, t, params, state, energy, ws)
         v0 = state.vel.cpu().double().numpy().reshape(-1, 3)

@@ -94,6 +94,20 @@ def test_small_periodic_box_ragged(gpu_lib, mode):
 
 
 @pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("T", [1, 5])
+@pytest.mark.parametrize("dtype", [0, 1])
+def test_interaction_block_counts(gpu_lib, dtype, T, mode):
+    """One and five interaction blocks (fp32 and a bf16 filter) on four
+    269-bead chains with biases."""
+    import dataclasses
+    cfg, pos, types, _ = make_config("cg269x64", n_replicas=4)
+    m = dataclasses.replace(cfg.model, T=T, filter_dtype=dtype)
+    w = make_weights(m, 4, bias_scale=0.05)
+    check(gpu_lib, Config(f"chains-T{T}", cfg.system, m), pos, types, w, mode, n_replicas=4,
+          what=f"T={T} dtype={dtype}")
+
+
+@pytest.mark.parametrize("mode", list(MODES))
 def test_bf16_filter(gpu_lib, mode):
     cfg, pos, types, w = make_config("md1024", n_replicas=4)
     check(gpu_lib, cfg, pos, types, w, mode, n_replicas=4, what="bf16 filter, 4 x 269")
