@@ -4,9 +4,9 @@ import pytest
 
 import oracle
 from gen.configs import CONFIGS, ModelSpec, make_config, make_weights
-from tests.gpu_helpers import (assert_energy_forces, cutout_forces, gpu_neighbors, lib_desc,
-                               lib_system, oracle_desc, oracle_list, F_TOL_BF16, F_TOL_F32,
-                               F_TOL_W16)
+from tests.gpu_helpers import (assert_energy_forces, cutout_forces, depth_scale, gpu_neighbors,
+                               lib_desc, lib_system, oracle_desc, oracle_list, F_TOL_BF16,
+                               F_TOL_F32, F_TOL_W16)
 
 pytestmark = pytest.mark.gpu
 
@@ -44,7 +44,8 @@ def check(lib, cfg, pos, types, w, r_list=None, n_replicas=None, what=""):
                                        return_eps=True)
     eps_sum = np.abs(eps).reshape(system.n_replicas, -1).sum(axis=1)
     re, rf = assert_energy_forces(E, F, Eo, Fo, bf16=m.filter_dtype in (1, 2), what=what,
-                                  eps_abs_sum=eps_sum, w16=m.filter_dtype == 2)
+                                  eps_abs_sum=eps_sum, w16=m.filter_dtype == 2,
+                                  depth=depth_scale(m.T))
     if m.filter_dtype in (1, 2):
         print(f"{what}: E err / sum|eps| {np.max(np.abs(E - Eo) / eps_sum):.2e}")
     print(f"{what}: E rel {re:.2e}, F max/rms {rf:.2e}, edges {len(col)}")
@@ -84,6 +85,26 @@ def test_interaction_block_counts(gpu_lib, T, dtype):
     w = make_weights(m, 4, bias_scale=0.05)
     c2 = Config(f"chains-T{T}", cfg.system, m)
     check(gpu_lib, c2, pos, types, w, n_replicas=4, what=f"T={T} dtype={dtype}")
+
+
+# Model shapes the API accepts beyond the workloads' (D, Dr, T, H): a basis of
+# two functions and of one past a 32-wide chunk, a 32-wide readout at D 128,
+# a single block and the largest block count.
+SHAPES = [(64, 2, 1, 32), (64, 33, 2, 64), (128, 7, 2, 32), (128, 31, 1, 64), (128, 63, 8, 64)]
+
+
+@pytest.mark.parametrize("dtype", [0, 1, 2, 3])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "D%d-Dr%d-T%d-H%d" % s)
+def test_model_shapes(gpu_lib, shape, dtype):
+    """Each shape in every precision on four 269-bead chains with biases."""
+    import dataclasses
+    from gen.configs import Config
+    D, Dr, T, H = shape
+    cfg, pos, types, _ = make_config("cg269x64", n_replicas=4)
+    m = dataclasses.replace(cfg.model, D=D, Dr=Dr, T=T, H=H, filter_dtype=dtype)
+    w = make_weights(m, 11, bias_scale=0.05)
+    check(gpu_lib, Config("shape", cfg.system, m), pos, types, w, n_replicas=4,
+          what=f"D{D} Dr{Dr} T{T} H{H} dtype {dtype}")
 
 
 def test_cg269x64_full(gpu_lib):

@@ -33,6 +33,11 @@ E_TOL, F_TOL, F_RMS_TOL = 1e-5, 3e-3, 2e-4
 
 
 def _case(name):
+    if name.startswith("shape-"):   # shape-D-Dr-T-H on four chains with biases
+        D, Dr, T, H = (int(v) for v in name.split("-")[1:])
+        cfg, pos, types, _ = make_config("cg269x64", n_replicas=4)
+        m = dataclasses.replace(cfg.model, D=D, Dr=Dr, T=T, H=H, filter_dtype=1)
+        return Config(name, cfg.system, m), pos, types, make_weights(m, 11, bias_scale=0.05), 4
     if name.startswith("chains-T"):
         T = int(name[8:])
         cfg, pos, types, _ = make_config("cg269x64", n_replicas=4)
@@ -57,7 +62,8 @@ def _case(name):
                    dataclasses.replace(cfg.model, filter_dtype=1)), pos, types, w, None)
 
 
-@pytest.mark.parametrize("name", ["chains-T1", "chains-T5", "md1024x4", "cg32", "box389"])
+@pytest.mark.parametrize("name", ["chains-T1", "chains-T5", "md1024x4", "cg32", "box389",
+                                  "shape-64-2-1-32", "shape-128-63-8-64"])
 def test_bf16_path_matches_its_rounding_model(gpu_lib, name):
     cfg, pos, types, w, nrep = _case(name)
     m = cfg.model
