@@ -314,20 +314,23 @@ def test_nonfinite_position_in_neighbour_build(gpu_lib, periodic):
     assert st == lib.SN_ERR_NONFINITE and det == -(1 + 123), (st, det)
 
 
-def test_short_trajectory_bf16_filter_active_list(gpu_lib):
-    """The MD workload's own precision and path: a bf16 filter, the update
-    and readout layers on fp16 pairs, the per-step active list, ten BAOAB
-    steps of 3 replicas against the oracle with the same bf16-rounded filter
+@pytest.mark.parametrize("dtype", [1, 2])
+def test_short_trajectory_16bit_active_list(gpu_lib, dtype):
+    """The MD workload's own precision and path (a bf16 filter, the update
+    and readout layers on fp16 pairs; or W16A16), the per-step active list,
+    ten BAOAB steps of 3 replicas against the oracle with the same rounded
     weights and exact activations. Bars follow from the 16-bit force bar:
-    a force error of at most F_TOL_BF16 F_rms per step moves velocities by at
+    a force error of at most F_TOL F_rms per step moves velocities by at
     most that times dt kappa / m per step, and positions by dt times that."""
     import torch
-    from tests.gpu_helpers import E_TOL_BF16_ABS_SUM, F_TOL_BF16
+    from tests.gpu_helpers import E_TOL_BF16_ABS_SUM, E_TOL_W16_ABS_SUM, F_TOL_BF16, F_TOL_W16
+    E_TOL, F_TOL = (E_TOL_BF16_ABS_SUM, F_TOL_BF16) if dtype == 1 else (E_TOL_W16_ABS_SUM,
+                                                                        F_TOL_W16)
     lib = gpu_lib
     nsteps = 10
     cfg, m, pos, types, w, desc, system, model, ws, t, params, state, energy = _md_setup(
-        lib, "md1024", 3, filter_f32=False, active=True)
-    assert m.filter_dtype == 1
+        lib, "md1024", 3, filter_f32=False, dtype=dtype, active=True)
+    assert m.filter_dtype == dtype
     try:
         lib.sn_md_init(model, system, t, params, state, energy, ws)
         F0 = state.forces.cpu().double().numpy().reshape(-1, 3)
@@ -354,13 +357,13 @@ def test_short_trajectory_bf16_filter_active_list(gpu_lib):
     rebuild(pos)
     E0, F0o = forces(pos.astype(np.float64))
     f_rms = np.sqrt(np.mean(F0o ** 2))
-    assert np.max(np.abs(F0 - F0o)) <= F_TOL_BF16 * f_rms
+    assert np.max(np.abs(F0 - F0o)) <= F_TOL * f_rms
     p_o, v_o, F_o, E_o, _ = oracle.baoab_run(forces, rebuild, pos, v_init, F0o, dt_fs=2.0,
                                              temperature_K=300.0, gamma_per_ps=1.0,
                                              mass_amu=100.0, skin=1.0, rebuild_every=10, seed=42,
                                              step0=0, n_steps=nsteps)
     kick = 2.0 * oracle.md.KAPPA / 100.0                 # dt kappa / m per step
-    dv_bar = nsteps * kick * F_TOL_BF16 * f_rms + 1e-3 * np.sqrt(np.mean(v_o ** 2))
+    dv_bar = nsteps * kick * F_TOL * f_rms + 1e-3 * np.sqrt(np.mean(v_o ** 2))
     disp = np.max(np.abs(p_o - pos))
     dp_bar = nsteps * 2.0 * dv_bar + 1e-2 * disp + 2e-4
     dv = np.max(np.abs(v_gpu - v_o))
@@ -368,7 +371,7 @@ def test_short_trajectory_bf16_filter_active_list(gpu_lib):
     _, _, eps = oracle.energy_forces(d, None, p_o, types, *nl["l"], n_replicas=3, weights=W,
                                      return_eps=True)
     de = np.max(np.abs(E_gpu - E_o) / np.abs(eps).reshape(3, -1).sum(axis=1))
-    print(f"bf16 trajectory: dv {dv:.2e} (bar {dv_bar:.2e}), dp {dp:.2e} (bar {dp_bar:.2e}), "
+    print(f"dtype {dtype} trajectory: dv {dv:.2e} (bar {dv_bar:.2e}), dp {dp:.2e} (bar {dp_bar:.2e}), "
           f"E err {de:.2e} of sum|eps|")
     assert dv <= dv_bar and dp <= dp_bar
-    assert de <= E_TOL_BF16_ABS_SUM
+    assert de <= E_TOL
