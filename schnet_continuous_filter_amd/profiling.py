@@ -7,6 +7,9 @@
   python -m schnet_continuous_filter_amd.profiling util PMC_CSV OUT_TXT \
       --kernel k_cf_bwd --workload md1024 --cmd "..."
 
+  python -m schnet_continuous_filter_amd.profiling insts OUT_TXT PMC_CSV [PMC_CSV ...] \
+      --edges E --workload md1024 --cmd "..."
+
 ``traffic`` scales FETCH_SIZE and WRITE_SIZE (KiB per dispatch) by what the
 same counters read for a device copy of known size (bench.py
 --copy-calibration copies 256 MiB five times), and records the result with a
@@ -19,6 +22,11 @@ SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE times the SIMD count) and
 VALUBusy (percent of the cycles the vector ALUs issued: SQ_ACTIVE_INST_VALU
 over the CU count times GRBM_GUI_ACTIVE), as rocprofv3 defines them, plus
 any raw counters of the same run, and records them the same way.
+
+``insts`` merges several counter passes over the same command and lists,
+for every CFConv kernel, each counter's mean per dispatch, the instruction
+counts (SQ_INSTS_*) per 16-edge tile of the E-edge list, and the share of
+the waves' cycles spent waiting (SQ_WAIT_ANY over SQ_WAVE_CYCLES).
 """
 from __future__ import annotations
 
@@ -126,6 +134,35 @@ def util(pmc_csv, out_txt, kernel, workload, cmd) -> dict:
     return rec
 
 
+def insts(pmc_csvs, out_txt, edges, workload, cmd, kernel="k_cf_") -> dict:
+    per = collections.defaultdict(dict)
+    for c in pmc_csvs:
+        for name, by_kernel in _per_kernel_counter(c).items():
+            per[name].update(by_kernel)
+    kernels = sorted({k for by_kernel in per.values() for k in by_kernel if kernel in k})
+    tiles = -(-int(edges) // 16)
+    rec = {"workload": workload, "kernel_hash": kernel_hash(), "edges": int(edges),
+           "tiles": tiles, "command": cmd, "kernels": {}}
+    lines = [f"# rocprofv3 --pmc counter passes over one command; {workload}, {edges} edges "
+             f"= {tiles} tiles of 16 per dispatch", f"# command: {cmd}",
+             f"# kernel_hash {rec['kernel_hash']}", ""]
+    for k in kernels:
+        means = {n: sum(v[k]) / len(v[k]) for n, v in per.items() if k in v}
+        rec["kernels"][k] = means
+        lines.append(k)
+        for n in sorted(means):
+            tail = f"  {means[n] / tiles:10.1f} per tile" if n.startswith("SQ_INSTS") else ""
+            lines.append(f"  {n:28s} {means[n]:16.6g}{tail}")
+        if "SQ_WAIT_ANY" in means and means.get("SQ_WAVE_CYCLES"):
+            lines.append(f"  {'waiting share':28s} {means['SQ_WAIT_ANY'] / means['SQ_WAVE_CYCLES']:16.3f}"
+                         "  (SQ_WAIT_ANY / SQ_WAVE_CYCLES)")
+        lines.append("")
+    with open(out_txt, "w") as f:
+        f.write("\n".join(lines))
+        f.write(json.dumps(rec) + "\n")
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -145,9 +182,17 @@ def main():
     u.add_argument("--kernel", default="k_cf_bwd")
     u.add_argument("--workload", default="md1024")
     u.add_argument("--cmd", required=True)
+    n = sub.add_parser("insts")
+    n.add_argument("out")
+    n.add_argument("csvs", nargs="+")
+    n.add_argument("--edges", type=int, required=True)
+    n.add_argument("--workload", default="md1024")
+    n.add_argument("--cmd", required=True)
     a = ap.parse_args()
     if a.what == "stats":
         stats(a.csv, a.out, a.cmd)
+    elif a.what == "insts":
+        insts(a.csvs, a.out, a.edges, a.workload, a.cmd)
     elif a.what == "util":
         print(json.dumps(util(a.csv, a.out, a.kernel, a.workload, a.cmd)))
     else:
