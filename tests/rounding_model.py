@@ -24,9 +24,12 @@ but the treatment of fp16 subnormals.
 
 This module applies exactly those roundings to an fp64 copy of the oracle's
 arithmetic (the oracle keeps every activation exact). With the default
-scales it predicts a path's deviation from the oracle; other scales give
-other samples of the same rounding, which is how the 16-bit parity bars are
-checked against what the rounding itself does. Only tests use it.
+scales it predicts a path's deviation from the oracle: the bf16 filter's to
+within fp32 arithmetic, W16A16's in distribution only (it also rounds the
+features, so a tie decided differently on the GPU tips later ones). Other
+scales give other samples of the same rounding, which is how the 16-bit
+parity bars are checked against what the rounding itself does. Only tests
+use it.
 """
 from __future__ import annotations
 
