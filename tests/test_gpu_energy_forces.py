@@ -189,6 +189,25 @@ def test_sparse_receivers_beyond_the_window(gpu_lib):
           what="sparse clusters x1200")
 
 
+@pytest.mark.parametrize("dtype", [0, 1, 2, 3])
+def test_coincident_atoms(gpu_lib, dtype):
+    """Pairs at distance zero (a bead moved onto its bonded neighbour, and two
+    beads far apart in sequence made to coincide): the energy is defined,
+    and the pair's force term, whose direction u / d is undefined there, is
+    zero on both sides (the oracle divides by 1 where d = 0, the kernels
+    take 1 / d as 0)."""
+    import dataclasses
+    from gen.configs import Config
+    cfg, pos, types, _ = make_config("cg269x64", n_replicas=4)
+    pos = pos.copy()
+    pos[5] = pos[6]
+    pos[269 + 100] = pos[269 + 200]
+    m = dataclasses.replace(cfg.model, filter_dtype=dtype)
+    w = make_weights(m, 4, bias_scale=0.05)
+    check(gpu_lib, Config("coincident", cfg.system, m), pos, types, w, n_replicas=4,
+          what=f"coincident beads dtype {dtype}")
+
+
 def test_isolated_atoms_and_single_atom(gpu_lib):
     cfg = CONFIGS["cg32"]
     w = make_weights(cfg.model, 0, bias_scale=0.1)
