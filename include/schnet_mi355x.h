@@ -164,7 +164,9 @@ sn_status sn_build_neighbors(const sn_system* sys, const float* pos, float r_lis
  * The list must be symmetric, as that call makes it: the force on atom i is
  * gathered from i's own row. fp32 inputs and outputs, fp32 accumulation.
  * A list of 2^30 or more edges sets the device status to SN_ERR_UNSUPPORTED
- * (detail: the edge count) and leaves the outputs invalid. */
+ * (detail: the edge count) and leaves the outputs invalid; a type outside
+ * [0, n_types) sets it to SN_ERR_INVALID_ARG (detail: an offending atom), is
+ * read as type 0, and leaves the outputs invalid. */
 sn_status sn_energy_forces(const sn_model* model, const sn_system* sys, const float* pos,
                            const int32_t* types, const int32_t* rowptr, const int32_t* col,
                            float* energy, float* forces, void* ws, size_t ws_bytes,

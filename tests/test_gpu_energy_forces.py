@@ -208,6 +208,34 @@ def test_coincident_atoms(gpu_lib, dtype):
           what=f"coincident beads dtype {dtype}")
 
 
+def test_out_of_range_types_reported(gpu_lib):
+    """An atom type outside [0, n_types) is reported in the device status
+    word (SN_ERR_INVALID_ARG, detail = an offending atom) instead of being
+    read past the embedding table (the set-up kernel clamps it to 0)."""
+    import torch
+    cfg, pos, types, w = make_config("cg269x64", n_replicas=2)
+    m = cfg.model
+    system = lib_system(gpu_lib, cfg.system, 2)
+    bad = types.copy()
+    bad[17] = m.n_types
+    bad[300] = -1
+    desc = lib_desc(gpu_lib, m)
+    model = gpu_lib.sn_model_create(desc, w)
+    try:
+        ws = gpu_lib.Workspace(gpu_lib.sn_workspace_size(desc, system))
+        p, rowptr, col, ne, ws = gpu_neighbors(gpu_lib, system, pos, m.r_cut, ws=ws)
+        t = torch.from_numpy(np.ascontiguousarray(bad, dtype=np.int32)).cuda()
+        n = 2 * cfg.system.atoms_per_replica
+        energy = torch.empty(2, dtype=torch.float32, device="cuda")
+        forces = torch.empty(3 * n, dtype=torch.float32, device="cuda")
+        gpu_lib.sn_energy_forces(model, system, p, t, rowptr, col, energy, forces, ws)
+        torch.cuda.synchronize()
+        status, detail, _ = gpu_lib.sn_get_device_status(ws)
+        assert status == gpu_lib.SN_ERR_INVALID_ARG and detail in (17, 300), (status, detail)
+    finally:
+        gpu_lib.sn_model_destroy(model)
+
+
 def test_isolated_atoms_and_single_atom(gpu_lib):
     cfg = CONFIGS["cg32"]
     w = make_weights(cfg.model, 0, bias_scale=0.1)
