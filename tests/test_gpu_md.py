@@ -49,15 +49,19 @@ def _md_setup(lib, name, R, seed=0, gamma=1.0, skin=1.0, rebuild_every=10, filte
     return cfg, m, pos, types, w, desc, system, model, ws, t, params, state, energy
 
 
-@pytest.mark.parametrize("dtype,T", [(0, None), (3, None), (0, 1), (0, 5)])
-def test_short_trajectory_matches_oracle(gpu_lib, dtype, T):
+@pytest.mark.parametrize("dtype,T,skin,every", [(0, None, 1.0, 10), (3, None, 1.0, 10),
+                                                (0, 1, 1.0, 10), (0, 5, 1.0, 10),
+                                                (0, None, 0.0, 1000), (0, None, 1.0, 1)])
+def test_short_trajectory_matches_oracle(gpu_lib, dtype, T, skin, every):
     """Ten BAOAB steps of 3 chain replicas with the same Philox stream: the
     GPU (fp32, or the fp32 model on fp16 pairs; the chain model's three
     interaction blocks, or one or five) and the oracle (fp64) trajectories
-    agree to fp32 accuracy."""
+    agree to fp32 accuracy, and the lists are rebuilt on the same steps:
+    every 10, or, with no skin, after every step (any motion trips the
+    displacement guard), or on a schedule of every step."""
     lib = gpu_lib
     cfg, m, pos, types, w, desc, system, model, ws, t, params, state, energy = _md_setup(
-        lib, "cg269x64", 3, dtype=dtype, T=T)
+        lib, "cg269x64", 3, dtype=dtype, T=T, skin=skin, rebuild_every=every)
     try:
         lib.sn_md_init(model, system, t, params, state, energy, ws)
         v0 = state.vel.cpu().double().numpy().reshape(-1, 3)
@@ -71,6 +75,7 @@ def test_short_trajectory_matches_oracle(gpu_lib, dtype, T):
         v_gpu = state.vel.cpu().double().numpy().reshape(-1, 3)
         E_gpu = energy.cpu().double().numpy()
         assert state.step == 10
+        n_builds = st[2]
     finally:
         lib.sn_model_destroy(model)
 
@@ -81,7 +86,7 @@ def test_short_trajectory_matches_oracle(gpu_lib, dtype, T):
     nl = {}
 
     def rebuild(p):
-        nl["l"] = oracle.neighbor_list(np.asarray(p, np.float32), 3, 269, False, 0.0, m.r_cut + 1.0)
+        nl["l"] = oracle.neighbor_list(np.asarray(p, np.float32), 3, 269, False, 0.0, m.r_cut + skin)
 
     def forces(p):
         return oracle.energy_forces(d, None, p, types, *nl["l"], n_replicas=3, weights=W)
@@ -89,10 +94,12 @@ def test_short_trajectory_matches_oracle(gpu_lib, dtype, T):
     rebuild(pos)
     E0, F0o = forces(pos.astype(np.float64))
     assert np.max(np.abs(F0 - F0o)) < 1e-4 * np.sqrt(np.mean(F0o ** 2))
-    p_o, v_o, F_o, E_o, _ = oracle.baoab_run(forces, rebuild, pos, v_init, F0o, dt_fs=2.0,
-                                             temperature_K=300.0, gamma_per_ps=1.0,
-                                             mass_amu=100.0, skin=1.0, rebuild_every=10, seed=42,
-                                             step0=0, n_steps=10)
+    p_o, v_o, F_o, E_o, nrb = oracle.baoab_run(forces, rebuild, pos, v_init, F0o, dt_fs=2.0,
+                                               temperature_K=300.0, gamma_per_ps=1.0,
+                                               mass_amu=100.0, skin=skin, rebuild_every=every,
+                                               seed=42, step0=0, n_steps=10)
+    assert n_builds == 1 + nrb, (n_builds, nrb)       # the GPU count includes the initial build
+    assert nrb == (10 if (skin == 0.0 or every == 1) else 1)
     # displacement over 10 steps is ~ 0.03 A; compare against it
     # fp32 positions of up to ~200 A carry ~1e-5 A rounding per update; the
     # displacement over 10 steps is ~0.03 A
