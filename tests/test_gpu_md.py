@@ -109,6 +109,73 @@ def test_short_trajectory_matches_oracle(gpu_lib, dtype, T, skin, every):
     assert np.all(np.abs(E_gpu - E_o) <= 1e-4 * np.abs(E_o) + 1e-4)
 
 
+def test_periodic_trajectory_matches_oracle(gpu_lib):
+    """Ten BAOAB steps of a 389-atom periodic box (the bulk model, fp32, a
+    rebuild every 5 steps): positions wrap into [0, L) on both sides and are
+    compared by minimum image (a value that rounds to L is 0, as in the
+    generator and the kernels)."""
+    import torch
+    lib = gpu_lib
+    cfg = CONFIGS["bulk4k"]
+    rng = np.random.default_rng(4)
+    n, box = 389, 17.9
+    L = float(np.float32(box))
+    pos = rng.uniform(0, box, (n, 3)).astype(np.float32)
+    pos[pos >= np.float32(box)] = 0
+    types = rng.integers(0, 4, n).astype(np.int32)
+    m = cfg.model
+    w = make_weights(m, 6)
+    system = lib.make_system(1, n, True, box)
+    desc = lib_desc(lib, m)
+    model = lib.sn_model_create(desc, w)
+    try:
+        ws = lib.Workspace(lib.sn_workspace_size(desc, system))
+        p = torch.from_numpy(pos).cuda().reshape(-1)
+        t = torch.from_numpy(types).cuda()
+        params = lib.make_md_params(2.0, 300.0, 1.0, 100.0, 1.0, 5, 42)
+        state = lib.MdState(p, 400 * n, active=True)
+        energy = torch.empty(1, dtype=torch.float32, device="cuda")
+        lib.sn_md_init(model, system, t, params, state, energy, ws)
+        lib.sn_md_step(model, system, t, params, state, 10, energy, ws)
+        torch.cuda.synchronize()
+        st = lib.sn_get_device_status(ws)
+        assert st[0] == 0, st
+        p_gpu = state.pos.cpu().double().numpy().reshape(-1, 3)
+        v_gpu = state.vel.cpu().double().numpy().reshape(-1, 3)
+        E_gpu = energy.cpu().double().numpy()
+    finally:
+        lib.sn_model_destroy(model)
+    assert p_gpu.min() >= 0 and p_gpu.max() < L
+    d = oracle_desc(m)
+    W = oracle.unpack_weights(d, w)
+    v_init = oracle.init_velocities(42, n, 300.0, 100.0)
+    nl = {}
+
+    def rebuild(q):
+        q32 = np.asarray(q, np.float32)
+        q32[q32 >= np.float32(box)] = 0
+        nl["l"] = oracle.neighbor_list(q32, 1, n, True, box, m.r_cut + 1.0)
+
+    def forces(q):
+        return oracle.energy_forces(d, None, q, types, *nl["l"], n_replicas=1, periodic=True,
+                                    box=box, weights=W)
+
+    rebuild(pos)
+    E0, F0 = forces(pos.astype(np.float64))
+    p_o, v_o, F_o, E_o, nrb = oracle.baoab_run(forces, rebuild, pos, v_init, F0, dt_fs=2.0,
+                                               temperature_K=300.0, gamma_per_ps=1.0,
+                                               mass_amu=100.0, skin=1.0, rebuild_every=5, seed=42,
+                                               step0=0, n_steps=10, periodic=True, box=box)
+    assert st[2] == 1 + nrb
+    dp = p_gpu - p_o
+    dp -= L * np.round(dp / L)
+    disp = p_o - pos
+    disp -= L * np.round(disp / L)
+    assert np.max(np.abs(dp)) < 1e-2 * np.max(np.abs(disp)) + 2e-4
+    assert np.max(np.abs(v_gpu - v_o)) < 1e-3 * np.sqrt(np.mean(v_o ** 2))
+    assert np.all(np.abs(E_gpu - E_o) <= 1e-4 * np.abs(E_o) + 1e-4)
+
+
 def test_restore_replays_bitwise(gpu_lib):
     import torch
     lib = gpu_lib
