@@ -20,8 +20,9 @@
  *    except where a call says it synchronises.
  *  - Arguments are validated on the host before anything is launched; an
  *    invalid argument returns SN_ERR_INVALID_ARG and enqueues nothing.
- *  - Errors found on the device (list capacity, non-finite energies or
- *    positions) are recorded in a status word inside the workspace; read it with
+ *  - Errors found on the device (list capacity, non-finite energies,
+ *    positions or velocities, atom types out of range, lists too long) are
+ *    recorded in a status word inside the workspace; read it with
  *    sn_get_device_status. The first error wins until sn_reset_device_status.
  *  - Atoms are numbered replica-major: atom a of replica r is r*N + a, with
  *    N = atoms_per_replica. Positions and forces are float [R*N][3].
