@@ -295,7 +295,9 @@ sn_status sn_md_step(const sn_model* model, const sn_system* sys, const int32_t*
  * status_host gets an sn_status value; detail_host the needed edge count for
  * SN_ERR_CAPACITY; for SN_ERR_NONFINITE the replica r >= 0 whose energy is
  * not finite, or -(1 + i) for atom i whose position or velocity is not
- * finite. n_rebuilds_host (may be
+ * finite; for SN_ERR_INVALID_ARG an atom whose type is out of range; for
+ * SN_ERR_UNSUPPORTED the edge count of a list too long to evaluate.
+ * n_rebuilds_host (may be
  * NULL) gets the number of neighbour-list builds done by the MD calls. */
 sn_status sn_get_device_status(const void* ws, size_t ws_bytes, hipStream_t stream,
                                int32_t* status_host, int64_t* detail_host,
