@@ -921,7 +921,7 @@ __global__ __launch_bounds__((64 * (Q ? cf_nw<D, PR, true>() : cf_nw_first<D, PR
     };
     if constexpr (kEarlyGather<PR> && Q) {
 #pragma unroll
-      for (int b = 0; b < 4; ++b) gather(b, G[b]);
+      for (int b = 0; b < GD; ++b) gather(b, G[b]);
     }
 
     // GEMM1: a = b~ Wf1 + cf1 and its tangent a' = (d b~/dd) Wf1;
