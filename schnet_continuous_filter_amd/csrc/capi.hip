@@ -409,12 +409,14 @@ bool nbr_geom(const sn_system* sys, float r_list, NbrGeom& g) {
     if (!((double)sys->box >= 2.0 * (double)r_list)) return false;
     int nc = (int)std::floor((double)sys->box / ((double)r_list * (1.0 + 1e-5)));
     if (nc > kCellsPerAxisMax) nc = kCellsPerAxisMax;
-    if (sys->n_replicas == 1 && nc >= 3) {
+    // cells hold every replica's atoms (the pair test keeps replicas apart),
+    // so several replicas take them only when each is large
+    if (nc >= 3 && (sys->n_replicas == 1 || sys->atoms_per_replica >= kOpenCellMinAtoms)) {
       g.cells_per_axis = nc;
       g.inv_cell = (float)((double)nc / (double)sys->box);
     }
-  } else if (sys->n_replicas == 1 && sys->atoms_per_replica >= kOpenCellMinAtoms) {
-    g.cells_per_axis = -1;   // grid over the bounding box, set on the device
+  } else if (sys->atoms_per_replica >= kOpenCellMinAtoms) {
+    g.cells_per_axis = -1;   // grid over the bounding box of all replicas, set on the device
   }
   return true;
 }

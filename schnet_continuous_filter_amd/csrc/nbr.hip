@@ -394,7 +394,8 @@ __global__ __launch_bounds__(kThreads) void k_cell_scatter(int N, const int32_t*
 // neighbouring cells around (27 distinct cells, nc >= 3); an open grid leaves
 // out those past its faces.
 template <bool FILL, bool OPEN>
-__global__ __launch_bounds__(kThreads) void k_nbr_cells(const float* __restrict__ pos, int N, int nc,
+__global__ __launch_bounds__(kThreads) void k_nbr_cells(const float* __restrict__ pos, int N,
+                                                        int n_per, int nc,
                                                         const CellGrid* open_grid,
                                                         double L, double half, double r2,
                                                         const int32_t* atom_cell,
@@ -408,6 +409,8 @@ __global__ __launch_bounds__(kThreads) void k_nbr_cells(const float* __restrict_
   const int i = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   if (i >= N) return;
   const float xi = pos[3 * i + 0], yi = pos[3 * i + 1], zi = pos[3 * i + 2];
+  // the receiver's replica: atoms [rlo, rlo + n_per) (cells hold every replica's atoms)
+  const int rlo = i - i % n_per;
   const int c = atom_cell[i];
   const int nx = OPEN ? open_grid->nx : nc, ny = OPEN ? open_grid->ny : nc,
             nz = OPEN ? open_grid->nz : nc;
@@ -456,8 +459,9 @@ __global__ __launch_bounds__(kThreads) void k_nbr_cells(const float* __restrict_
     int j = 0;
     if (f < total) {
       j = cell_atoms[k];
-      in = j != i && pair_in(xi, yi, zi, pos[3 * j], pos[3 * j + 1], pos[3 * j + 2], OPEN ? 0 : 1,
-                             L, half, r2);
+      in = j != i && (unsigned)(j - rlo) < (unsigned)n_per &&
+           pair_in(xi, yi, zi, pos[3 * j], pos[3 * j + 1], pos[3 * j + 2], OPEN ? 0 : 1, L, half,
+                   r2);
     }
     const uint64_t m = __ballot(in);
     if (FILL && in) col[out + __popcll(m & ((1ull << lane) - 1))] = j;
@@ -590,7 +594,7 @@ hipError_t launch_build_neighbors(const NbrGeom& g, const float* pos, int32_t* r
   int32_t* ccur = reinterpret_cast<int32_t*>(ws + L.cell_start);     // scatter cursors
   int32_t* catoms = reinterpret_cast<int32_t*>(ws + L.cell_atoms);
   int32_t* acell = reinterpret_cast<int32_t*>(ws + L.atom_cell);
-  const int N = g.n_per;
+  const int N = g.n_rep * g.n_per;   // every replica's atoms share the cells
   hipLaunchKernelGGL(k_fill_i32, dim3(blocks_for(ncell + 1)), dim3(kThreads), 0, s, cstart,
                      ncell + 1, 0, gate, gate_val);
   hipLaunchKernelGGL(k_fill_i32, dim3(blocks_for(ncell)), dim3(kThreads), 0, s, ccur, ncell, 0,
@@ -611,23 +615,23 @@ hipError_t launch_build_neighbors(const NbrGeom& g, const float* pos, int32_t* r
                      ccur, catoms, gate, gate_val);
   const dim3 wave_grid((unsigned)((N + kThreads / 64 - 1) / (kThreads / 64)));
   if (open)
-    hipLaunchKernelGGL((k_nbr_cells<false, true>), wave_grid, dim3(kThreads), 0, s, pos, N, nc,
-                       grid, g.L, g.half, g.r2, acell, cstart, catoms, rowptr, col, st, gate,
+    hipLaunchKernelGGL((k_nbr_cells<false, true>), wave_grid, dim3(kThreads), 0, s, pos, N,
+                       g.n_per, nc, grid, g.L, g.half, g.r2, acell, cstart, catoms, rowptr, col, st, gate,
                        gate_val);
   else
-    hipLaunchKernelGGL((k_nbr_cells<false, false>), wave_grid, dim3(kThreads), 0, s, pos, N, nc,
-                       grid, g.L, g.half, g.r2, acell, cstart, catoms, rowptr, col, st, gate,
+    hipLaunchKernelGGL((k_nbr_cells<false, false>), wave_grid, dim3(kThreads), 0, s, pos, N,
+                       g.n_per, nc, grid, g.L, g.half, g.r2, acell, cstart, catoms, rowptr, col, st, gate,
                        gate_val);
   if ((e = launch_exclusive_scan(rowptr, N, scan_blocks, st, edge_capacity, gate, gate_val, s)) !=
       hipSuccess)
     return e;
   if (open)
-    hipLaunchKernelGGL((k_nbr_cells<true, true>), wave_grid, dim3(kThreads), 0, s, pos, N, nc,
-                       grid, g.L, g.half, g.r2, acell, cstart, catoms, rowptr, col, st, gate,
+    hipLaunchKernelGGL((k_nbr_cells<true, true>), wave_grid, dim3(kThreads), 0, s, pos, N,
+                       g.n_per, nc, grid, g.L, g.half, g.r2, acell, cstart, catoms, rowptr, col, st, gate,
                        gate_val);
   else
-    hipLaunchKernelGGL((k_nbr_cells<true, false>), wave_grid, dim3(kThreads), 0, s, pos, N, nc,
-                       grid, g.L, g.half, g.r2, acell, cstart, catoms, rowptr, col, st, gate,
+    hipLaunchKernelGGL((k_nbr_cells<true, false>), wave_grid, dim3(kThreads), 0, s, pos, N,
+                       g.n_per, nc, grid, g.L, g.half, g.r2, acell, cstart, catoms, rowptr, col, st, gate,
                        gate_val);
   hipLaunchKernelGGL(k_sort_rows, dim3((unsigned)((N + 3) / 4)), dim3(kThreads), 0, s, rowptr, col,
                      N, st, gate, gate_val);

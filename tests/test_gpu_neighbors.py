@@ -71,6 +71,32 @@ def test_open_system_cell_list_exact(gpu_lib, shape):
     assert ne > 0
 
 
+@pytest.mark.parametrize("layout", ["overlapping", "offset", "periodic"])
+def test_large_replicas_cell_list_exact(gpu_lib, layout):
+    """Several replicas of 8,192 atoms or more share one cell list (open: over
+    the bounding box of all of them; periodic: the cube), the pair test
+    keeping replicas apart; the list must equal the oracle's bit for bit."""
+    rng = np.random.default_rng([11, 7])
+    rho, r = 0.0612, 5.0
+    if layout == "periodic":
+        R, n = 2, 8192
+        box = float(np.float32((n / rho) ** (1 / 3)))
+        pos = rng.uniform(0.0, box, (R * n, 3)).astype(np.float32)
+        pos[pos >= np.float32(box)] = 0
+        system = gpu_lib.make_system(R, n, True, box)
+    else:
+        R, n = 3, 9000
+        side = (n / rho) ** (1 / 3)
+        pos = rng.uniform(0.0, side, (R, n, 3))
+        if layout == "offset":      # replicas side by side, one partly overlapping the next
+            pos += np.array([0.7 * side, 0.0, -0.3 * side])[None, None, :] * np.arange(R)[:, None, None]
+        pos = pos.reshape(-1, 3).astype(np.float32)
+        system = gpu_lib.make_system(R, n, False, 0.0)
+    ne = _compare(gpu_lib, system, pos, r)
+    print(f"{layout}: {R} x {n} atoms, {ne} directed edges")
+    assert ne > 0
+
+
 def test_isolated_atoms_give_empty_rows(gpu_lib):
     pos = (np.arange(30, dtype=np.float32)[:, None] * np.float32(50.0)).repeat(3, 1)
     ne = _compare(gpu_lib, gpu_lib.make_system(3, 10, False, 0.0), pos, 5.0)
